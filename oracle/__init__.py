@@ -1,0 +1,142 @@
+"""fp64 CPU oracle for the Gated DeltaNet-2 forward recurrence.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path never does. It shares
+no code with the HIP library (``gated_delta_rule_83_amd``), and neither side
+imports the other.
+
+The arithmetic lives in ``gdn2_oracle.c`` (plain sequential double-precision
+recurrence, one token at a time; see the header of that file for the steps
+and the passages they follow). This module only builds it with gcc, loads it
+with ctypes and marshals numpy arrays.
+
+Pins (checked by ``tests/test_oracle_pins.py`` against things other than the
+oracle itself): the delta-rule tutorial's worked 2x2 example and its printed
+variants, the linear-attention closed form, the "difference is zero"
+invariant, the query-change identity, a per-step key-read identity for
+channel-wise gates, the decay-only closed form, the reductions to the delta
+rule, a chunked fp64 evaluation, column separability and split prefill.
+Parity unpinned: the exact placement of channel-wise erase and write gates
+when b and w are not uniform (the pages state it only in prose); the oracle
+takes erase (b * k) r^T and write k (w * v)^T.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn2_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn2_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-D_POSIX_C_SOURCE=200809L",
+                               "-o", tmp, _SRC, "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def bind(path: str):
+    """Load an oracle shared library from `path` (the tests also bind mutated copies)."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.gdn2_oracle_forward.restype = ctypes.c_int
+    lib.gdn2_oracle_forward.argtypes = [ctypes.c_int] * 6 + [dp] * 9 + [ctypes.c_int, dp]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = bind(_LIB)
+    return _lib
+
+
+def _f64(x) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor: upcast exactly via float32
+        x = x.detach().cpu().float().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    if x is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def forward(q, k, v, a, b, w, S0=None, nthreads: Optional[int] = None,
+            want_o: bool = True, timing: bool = False, lib=None):
+    """Run the recurrence in fp64.
+
+    Shapes: q, k [B, T, H_qk, d_k]; v, w [B, T, H_v, d_v]; a, b [B, T, H_v, d_k];
+    S0 [B, H_v, d_k, d_v] or None. Returns (o [B, T, H_v, d_v], S_T), plus the
+    recurrence's wall time in seconds if `timing`.
+    """
+    lib = _load() if lib is None else lib
+    q, k, v, a, b, w, S0 = (_f64(x) for x in (q, k, v, a, b, w, S0))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    assert k.shape == q.shape and v.shape == (B, T, Hv, dv)
+    assert a.shape == (B, T, Hv, dk) and b.shape == a.shape and w.shape == v.shape
+    if S0 is not None:
+        assert S0.shape == (B, Hv, dk, dv)
+    o = np.empty((B, T, Hv, dv), dtype=np.float64) if want_o else None
+    ST = np.empty((B, Hv, dk, dv), dtype=np.float64)
+    el = ctypes.c_double(0.0)
+    nt = cores() if nthreads is None else int(nthreads)
+    rc = lib.gdn2_oracle_forward(B, T, Hqk, Hv, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                 _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), nt, ctypes.byref(el))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    if timing:
+        return o, ST, el.value
+    return o, ST
+
+
+def forward_heads(inputs: dict, heads, nthreads: Optional[int] = None) -> Tuple[dict, dict]:
+    """Run the oracle only on selected (n, h_v) pairs of a prefill input dict.
+
+    `inputs` holds q, k, v, a, b, w, S0 (numpy or torch, full shapes). Returns
+    ({(n, h): o[T, d_v]}, {(n, h): S_T[d_k, d_v]}).
+    """
+    heads = list(heads)
+    q, k = inputs["q"], inputs["k"]
+    Hqk = q.shape[2]
+    Hv = inputs["v"].shape[2]
+    G = Hv // Hqk
+    S0 = inputs.get("S0")
+
+    def gather(x, per_qk):
+        rows = [_f64(x[n:n + 1, :, (h // G if per_qk else h):(h // G if per_qk else h) + 1])
+                for (n, h) in heads]
+        return np.concatenate(rows, axis=0)
+
+    s0 = None
+    if S0 is not None:
+        s0 = np.concatenate([_f64(S0[n:n + 1, h:h + 1]) for (n, h) in heads], axis=0)
+    o, ST = forward(gather(q, True), gather(k, True), gather(inputs["v"], False),
+                    gather(inputs["a"], False), gather(inputs["b"], False),
+                    gather(inputs["w"], False), s0, nthreads=nthreads)
+    outs = {hd: o[i, :, 0] for i, hd in enumerate(heads)}
+    states = {hd: ST[i, 0] for i, hd in enumerate(heads)}
+    return outs, states
