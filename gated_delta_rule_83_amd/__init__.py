@@ -1,1 +1,189 @@
-"""libgdn2: Gated DeltaNet-2 forward sequence mixing on MI355X (gfx950)."""
+"""libgdn2: Gated DeltaNet-2 forward sequence mixing on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/gdn2.h``. Every step of
+the computation runs in the HIP kernels of ``libgdn2.so``; this module only
+marshals arguments. PyTorch supplies device memory and the stream.
+
+Raw entry points (same names and arguments as the C ABI; pointers are ints):
+    gdn2_chunk_forward, gdn2_decode_step, gdn2_chunk_forward_workspace_bytes,
+    gdn2_status_string, gdn2_version
+Torch conveniences:
+    chunk_forward(q, k, v, a, b, w, S0=None, chunk=64) -> (o, S_T)
+    decode_step(q, k, v, a, b, w, S) -> o        (S updated in place)
+
+If ``libgdn2.so`` has not been built, loading fails loudly: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+
+GDN2_OK = 0
+GDN2_ERR_NULL_POINTER = 1
+GDN2_ERR_BAD_SHAPE = 2
+GDN2_ERR_UNSUPPORTED = 3
+GDN2_ERR_BAD_DTYPE = 4
+GDN2_ERR_WORKSPACE = 5
+GDN2_ERR_HIP = 6
+GDN2_ERR_ALIAS = 7
+
+GDN2_F32 = 0
+GDN2_BF16 = 1
+
+EXPORTED = ("gdn2_chunk_forward", "gdn2_decode_step", "gdn2_chunk_forward_workspace_bytes",
+            "gdn2_status_string", "gdn2_version")
+
+
+class gdn2_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H_qk", ctypes.c_int32),
+                ("H_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libgdn2 status {status}: {gdn2_status_string(status)}")
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libgdn2.so (raises if it is missing: build it with gated_delta_rule_83_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libgdn2.so not found at {p}; run `python -m gated_delta_rule_83_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(gdn2_desc)
+    lib.gdn2_chunk_forward.restype = ctypes.c_int
+    lib.gdn2_chunk_forward.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
+    lib.gdn2_decode_step.restype = ctypes.c_int
+    lib.gdn2_decode_step.argtypes = [dp] + [vp] * 8 + [vp]
+    lib.gdn2_chunk_forward_workspace_bytes.restype = sz
+    lib.gdn2_chunk_forward_workspace_bytes.argtypes = [dp]
+    lib.gdn2_status_string.restype = ctypes.c_char_p
+    lib.gdn2_status_string.argtypes = [ctypes.c_int]
+    lib.gdn2_version.restype = ctypes.c_int
+    lib.gdn2_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_desc(B, T, H_qk, H_v, d_k, d_v, chunk=64, dtype=GDN2_BF16) -> gdn2_desc:
+    return gdn2_desc(B, T, H_qk, H_v, d_k, d_v, chunk, dtype)
+
+
+# ------------------------------------------------------------------ raw C ABI
+def gdn2_version() -> int:
+    return load().gdn2_version()
+
+
+def gdn2_status_string(status: int) -> str:
+    return load().gdn2_status_string(int(status)).decode()
+
+
+def gdn2_chunk_forward_workspace_bytes(desc) -> int:
+    return load().gdn2_chunk_forward_workspace_bytes(None if desc is None else ctypes.byref(desc))
+
+
+def gdn2_chunk_forward(desc, q, k, v, a, b, w, S0, o, S_T, workspace=0, workspace_bytes=0,
+                       stream=0) -> int:
+    return load().gdn2_chunk_forward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w,
+                                     S0, o, S_T, workspace, workspace_bytes, stream)
+
+
+def gdn2_decode_step(desc, q, k, v, a, b, w, S, o, stream=0) -> int:
+    return load().gdn2_decode_step(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w, S,
+                                   o, stream)
+
+
+# ------------------------------------------------------------------ torch conveniences
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN2_BF16
+    if t.dtype == torch.float32:
+        return GDN2_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, dtype=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a torch tensor on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def chunk_forward(q, k, v, a, b, w, S0=None, chunk: int = 64, o=None, S_T=None,
+                  want_state: bool = True, stream=None):
+    """Prefill. q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v]; a, b [B,T,H_v,d_k] fp32;
+    w [B,T,H_v,d_v] fp32; S0 [B,H_v,d_k,d_v] fp32 or None. Returns (o, S_T)."""
+    import torch
+    B, T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, q.dtype)
+    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0")):
+        _check(t, nm, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    _check(o, "o", q.dtype)
+    _check(S_T, "S_T", torch.float32)
+    desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
+    ws = gdn2_chunk_forward_workspace_bytes(desc)
+    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    st = gdn2_chunk_forward(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0),
+                            _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st)
+    return o, S_T
+
+
+def decode_step(q, k, v, a, b, w, S, o=None, stream=None):
+    """One decode token. q, k [N,1,H_qk,d_k] (or [N,H_qk,d_k]); v [N,1,H_v,d_v];
+    a, b [N,1,H_v,d_k]; w [N,1,H_v,d_v]; S [N,H_v,d_k,d_v] fp32, updated in place.
+    Returns o shaped like v."""
+    import torch
+    N, H_v, d_k, d_v = S.shape
+    H_qk = q.shape[-2]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, q.dtype)
+    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S, "S")):
+        _check(t, nm, torch.float32)
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    _check(o, "o", q.dtype)
+    desc = make_desc(N, 1, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
+    st = gdn2_decode_step(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S),
+                          _ptr(o), _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st)
+    return o

@@ -1,0 +1,140 @@
+// gdn2_api.cpp -- the C ABI of libgdn2 (include/gdn2.h): argument checks,
+// then a launch on the caller's stream. Nothing here allocates device memory
+// or keeps state between calls.
+#include "gdn2.h"
+
+#include <stdint.h>
+
+#include "gdn2_internal.hpp"
+
+namespace {
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+bool overlaps(Range x, Range y) {
+  return x.lo != x.hi && y.lo != y.hi && x.lo < y.hi && y.lo < x.hi;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common description checks; `decode` additionally requires T == 1.
+gdn2_status check_desc(const gdn2_desc *d, bool decode) {
+  if (!d) return GDN2_ERR_NULL_POINTER;
+  if (d->dtype != GDN2_F32 && d->dtype != GDN2_BF16) return GDN2_ERR_BAD_DTYPE;
+  if (d->B < 0 || d->T < 0 || d->H_qk < 1 || d->H_v < 1 || d->d_k < 1 || d->d_v < 1 ||
+      d->chunk < 1)
+    return GDN2_ERR_BAD_SHAPE;
+  if (d->H_v % d->H_qk != 0) return GDN2_ERR_BAD_SHAPE;
+  if (decode && d->T != 1) return GDN2_ERR_BAD_SHAPE;
+  if (!supported_dim(d->d_k) || !supported_dim(d->d_v)) return GDN2_ERR_UNSUPPORTED;
+  if (!decode && !supported_chunk(d->chunk)) return GDN2_ERR_UNSUPPORTED;
+  return GDN2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn2_version(void) { return 10000; }
+
+const char *gdn2_status_string(gdn2_status s) {
+  switch (s) {
+    case GDN2_OK: return "ok";
+    case GDN2_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case GDN2_ERR_BAD_SHAPE: return "invalid shape, or a tensor pointer not 16-byte aligned";
+    case GDN2_ERR_UNSUPPORTED: return "unsupported head dimension or chunk length";
+    case GDN2_ERR_BAD_DTYPE: return "unknown dtype";
+    case GDN2_ERR_WORKSPACE: return "workspace too small";
+    case GDN2_ERR_HIP: return "HIP runtime error at launch";
+    case GDN2_ERR_ALIAS: return "output overlaps an input or the state";
+  }
+  return "unknown status";
+}
+
+size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc) {
+  (void)desc;
+  return 0;  // the prefill keeps every intermediate on chip
+}
+
+gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                               const float *a, const float *b, const float *w, const float *S0,
+                               void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  gdn2_status st = check_desc(d, false);
+  if (st != GDN2_OK) return st;
+  (void)workspace;
+  if (workspace_bytes < gdn2_chunk_forward_workspace_bytes(d)) return GDN2_ERR_WORKSPACE;
+  const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
+  const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
+  const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
+  if (B == 0) return GDN2_OK;
+  const bool tokens = T > 0;
+  if (tokens && (!q || !k || !v || !a || !b || !w || !o)) return GDN2_ERR_NULL_POINTER;
+  const void *ptrs[] = {q, k, v, a, b, w, S0, o, S_T};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+
+  const Range rq = range_of(q, B * T * Hqk * dk * es), rk = range_of(k, B * T * Hqk * dk * es);
+  const Range rv = range_of(v, B * T * Hv * dv * es);
+  const Range ra = range_of(a, B * T * Hv * dk * 4), rb = range_of(b, B * T * Hv * dk * 4);
+  const Range rw = range_of(w, B * T * Hv * dv * 4);
+  const Range ro = range_of(o, B * T * Hv * dv * es);
+  const Range rs0 = range_of(S0, S0 ? B * Hv * dk * dv * 4 : 0);
+  const Range rst = range_of(S_T, S_T ? B * Hv * dk * dv * 4 : 0);
+  const Range ins[] = {rq, rk, rv, ra, rb, rw, rs0, rst};
+  if (tokens)
+    for (const Range &r : ins)
+      if (overlaps(ro, r)) return GDN2_ERR_ALIAS;
+  // S_T may alias S0 exactly (in-place), but not partially.
+  if (S0 && S_T && overlaps(rs0, rst) && S0 != S_T) return GDN2_ERR_ALIAS;
+
+  gdn2::PrefillArgs p;
+  p.B = d->B; p.T = d->T; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
+  p.chunk = d->chunk;
+  p.bf16 = d->dtype == GDN2_BF16;
+  p.nct = gdn2::prefill_pick_nct(d->B, d->H_v, d->d_v);
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.o = o; p.S_T = S_T;
+  const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status gdn2_decode_step(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                             const float *a, const float *b, const float *w, float *S, void *o,
+                             void *stream) {
+  gdn2_status st = check_desc(d, true);
+  if (st != GDN2_OK) return st;
+  const size_t B = (size_t)d->B, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
+  const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
+  const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
+  if (B == 0) return GDN2_OK;
+  if (!q || !k || !v || !a || !b || !w || !S || !o) return GDN2_ERR_NULL_POINTER;
+  const void *ptrs[] = {q, k, v, a, b, w, S, o};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+  const Range ro = range_of(o, B * Hv * dv * es);
+  const Range ins[] = {range_of(q, B * Hqk * dk * es), range_of(k, B * Hqk * dk * es),
+                       range_of(v, B * Hv * dv * es),  range_of(a, B * Hv * dk * 4),
+                       range_of(b, B * Hv * dk * 4),   range_of(w, B * Hv * dv * 4),
+                       range_of(S, B * Hv * dk * dv * 4)};
+  for (const Range &r : ins)
+    if (overlaps(ro, r)) return GDN2_ERR_ALIAS;
+
+  gdn2::DecodeArgs p;
+  p.B = d->B; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
+  p.bf16 = d->dtype == GDN2_BF16;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S = S; p.o = o;
+  const hipError_t e = gdn2::launch_decode(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// gdn2_internal.hpp -- launch interface between the C ABI layer and the
+// kernels. Not installed; the public interface is include/gdn2.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+struct DecodeArgs {
+  int B, H_qk, H_v, d_k, d_v;
+  bool bf16;
+  const void *q, *k, *v;
+  const float *a, *b, *w;
+  float *S;
+  void *o;
+};
+
+struct PrefillArgs {
+  int B, T, H_qk, H_v, d_k, d_v, chunk;
+  bool bf16;
+  int nct;  // 16-column state tiles per workgroup (one wave each): 1, 4 or 8
+  const void *q, *k, *v;
+  const float *a, *b, *w, *S0;
+  void *o;
+  float *S_T;
+};
+
+// Threshold on the chunk's total decay per key channel above which the
+// chunk-parallel form is used. Below it the chunk is stepped token by token
+// (exact for any decay). The chunk form scales key-side operands by the
+// inverse cumulative decay, so this bounds every such factor by e^60.
+constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
+
+hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream);
+// Workgroup column width the prefill would use (for tests and tuning).
+int prefill_pick_nct(int B, int H_v, int d_v);
+
+}  // namespace gdn2

@@ -1,0 +1,119 @@
+/*
+ * gdn2.h -- C ABI of libgdn2: the Gated DeltaNet-2 forward sequence-mixing
+ * hot path on AMD MI355X (gfx950).
+ *
+ * The method (Gated DeltaNet-2 post on tilnote.io, section on the GDN-2
+ * design; news.hamidun.com item, section on the architecture) keeps one
+ * fixed-size state S (d_k x d_v, rows = key channels, columns = value
+ * channels) per sequence and value head. For each token t, in this order:
+ *
+ *   S~  = diag(a_t) S                       decay, channel-wise on the key axis
+ *   r_t = S~^T k_t                          key read of the decayed state
+ *   S   = S~ - (b_t * k_t) r_t^T + k_t (w_t * v_t)^T
+ *                                           erase (gate b on the key axis),
+ *                                           write (gate w on the value axis)
+ *   o_t = S^T q_t                           the query reads the updated state
+ *
+ * The read/update/read order and the state orientation follow the delta-rule
+ * tutorial on ai-systems-engineering.com ("write with KV, read with Q" and
+ * "record the difference" sections). The pages describe the decoupled erase
+ * and write only in prose; the placement above is the plainest reading, and
+ * it reduces to the delta rule S + beta k (v - S^T k)^T when a = 1 and
+ * b = w = beta (tutorial, beta section).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or retains device memory and keeps no state
+ *    between calls; calls are thread-safe.
+ *  - Tensors are contiguous, row-major, in these layouts:
+ *      q, k : [B, T, H_qk, d_k]      dtype of desc (fp32 or bf16)
+ *      v    : [B, T, H_v,  d_v]      dtype of desc
+ *      a, b : [B, T, H_v,  d_k]      fp32 (decay in (0,1], erase gate)
+ *      w    : [B, T, H_v,  d_v]      fp32 (write gate)
+ *      o    : [B, T, H_v,  d_v]      dtype of desc (fp32 -> bf16 rounds to nearest even)
+ *      S0, S_T, S : [B, H_v, d_k, d_v]  fp32
+ *    Value head h uses query/key head h / (H_v / H_qk) (contiguous groups,
+ *    as in the grouped 16 QK / 32 V head layout of the aiki wiki entry on
+ *    Gated DeltaNet, "how it works").
+ *  - Preconditions that are documented, not checked (checking would cost
+ *    bandwidth): a in (0, 1]; finite inputs (NaN/Inf propagate). Keys and
+ *    queries are used as given: the library never normalises them.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work and returns; device faults surface on the stream.
+ *  - Argument errors return a status before anything is enqueued.
+ */
+#ifndef GDN2_H_
+#define GDN2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN2_OK = 0,
+  GDN2_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  GDN2_ERR_BAD_SHAPE = 2,    /* negative size, H_v % H_qk != 0, decode with T != 1,
+                                a tensor pointer not 16-byte aligned */
+  GDN2_ERR_UNSUPPORTED = 3,  /* valid but not built: d_k, d_v not in {16,32,64,128}, chunk not in {16,32,64} */
+  GDN2_ERR_BAD_DTYPE = 4,    /* dtype is neither GDN2_F32 nor GDN2_BF16 */
+  GDN2_ERR_WORKSPACE = 5,    /* workspace smaller than gdn2_chunk_forward_workspace_bytes() */
+  GDN2_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
+  GDN2_ERR_ALIAS = 7         /* o overlaps an input or the state */
+} gdn2_status;
+
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
+
+/* Problem description. B: sequences; T: tokens per sequence; H_qk / H_v:
+ * query-key heads / value heads (H_v % H_qk == 0); d_k, d_v: head dims;
+ * chunk: tokens per chunk of the prefill (a performance knob only: results
+ * agree at every supported chunk); dtype: a gdn2_dtype for q, k, v, o. */
+typedef struct {
+  int32_t B, T, H_qk, H_v, d_k, d_v, chunk;
+  int32_t dtype;
+} gdn2_desc;
+
+/* Bytes of device workspace gdn2_chunk_forward needs for `desc` (0 if none).
+ * Returns 0 for an invalid description as well; the forward call reports
+ * the error. */
+size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc);
+
+/* Prefill: run T tokens of every (sequence, value head) through the
+ * recurrence above, starting from S0, writing every output o_t and the final
+ * state S_T. Computed chunk-parallel: within each chunk of `chunk` tokens
+ * the key reads come from one triangular solve and the outputs from dense
+ * products, with the state carried across chunks in fp32. The result equals
+ * the token-by-token recurrence up to rounding.
+ *   S0  : may be NULL (zero state).
+ *   S_T : may be NULL (not written); may alias S0 exactly (in-place update).
+ *   o   : must not overlap any input or S_T (GDN2_ERR_ALIAS).
+ *   workspace / workspace_bytes: device scratch of at least
+ *         gdn2_chunk_forward_workspace_bytes(desc) bytes (may be NULL if 0).
+ * T == 0 is valid: S_T = S0 (or zeros). Any T >= 0 is accepted; a last
+ * partial chunk is stepped token by token. */
+gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                               const float *a, const float *b, const float *w, const float *S0,
+                               void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Decode: one token per sequence (desc->T must be 1). Reads the state S,
+ * applies the step above and writes S back in place, and writes o.
+ * Inputs are shaped as for the prefill with T = 1 (B = number of sequences).
+ * S streams through HBM once: read once, written once. */
+gdn2_status gdn2_decode_step(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                             const float *a, const float *b, const float *w, float *S, void *o,
+                             void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *gdn2_status_string(gdn2_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int gdn2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H_ */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads, exports everything the
+header declares, and rejects bad arguments with a status before touching the
+GPU (every call here returns before any HIP call, so it runs without a GPU)."""
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_83_amd as g
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gdn2.h")
+
+FAKE = 1 << 40  # a 16-byte aligned address that is never dereferenced by argument checks
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = g.load()
+    names = declared_functions()
+    assert set(names) == set(g.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert g.gdn2_version() == 10000
+    for s in range(8):
+        assert g.gdn2_status_string(s)
+    assert g.gdn2_status_string(99) == "unknown status"
+
+
+def _ptrs(n_bytes_each=1 << 30):
+    # nine distinct, non-overlapping fake buffers (q, k, v, a, b, w, S0, o, S_T)
+    return [FAKE + i * n_bytes_each for i in range(9)]
+
+
+def fwd(desc, ptrs=None, **kw):
+    p = ptrs or _ptrs()
+    return g.gdn2_chunk_forward(desc, *p, kw.get("ws", 0), kw.get("ws_bytes", 0), 0)
+
+
+def test_chunk_forward_argument_errors():
+    d = g.make_desc(2, 64, 2, 4, 128, 128, 64, g.GDN2_BF16)
+    assert fwd(None) == g.GDN2_ERR_NULL_POINTER
+    assert fwd(g.make_desc(2, 64, 2, 4, 128, 128, 64, 7)) == g.GDN2_ERR_BAD_DTYPE
+    assert fwd(g.make_desc(-1, 64, 2, 4, 128, 128, 64, 1)) == g.GDN2_ERR_BAD_SHAPE
+    assert fwd(g.make_desc(2, -3, 2, 4, 128, 128, 64, 1)) == g.GDN2_ERR_BAD_SHAPE
+    assert fwd(g.make_desc(2, 64, 3, 4, 128, 128, 64, 1)) == g.GDN2_ERR_BAD_SHAPE  # H_v % H_qk
+    assert fwd(g.make_desc(2, 64, 0, 4, 128, 128, 64, 1)) == g.GDN2_ERR_BAD_SHAPE
+    assert fwd(g.make_desc(2, 64, 2, 4, 96, 128, 64, 1)) == g.GDN2_ERR_UNSUPPORTED
+    assert fwd(g.make_desc(2, 64, 2, 4, 128, 256, 64, 1)) == g.GDN2_ERR_UNSUPPORTED
+    assert fwd(g.make_desc(2, 64, 2, 4, 128, 128, 48, 1)) == g.GDN2_ERR_UNSUPPORTED
+    assert fwd(g.make_desc(2, 64, 2, 4, 128, 128, 128, 1)) == g.GDN2_ERR_UNSUPPORTED
+    # required pointers
+    for i in range(6):
+        p = _ptrs()
+        p[i] = 0
+        assert fwd(d, p) == g.GDN2_ERR_NULL_POINTER, i
+    p = _ptrs()
+    p[7] = 0  # o
+    assert fwd(d, p) == g.GDN2_ERR_NULL_POINTER
+    # misaligned
+    p = _ptrs()
+    p[3] += 4
+    assert fwd(d, p) == g.GDN2_ERR_BAD_SHAPE
+    # o overlapping an input, or the state
+    for i in (0, 1, 2, 3, 4, 5, 6, 8):
+        p = _ptrs()
+        p[7] = p[i] + 16
+        assert fwd(d, p) == g.GDN2_ERR_ALIAS, i
+    # S_T partially overlapping S0
+    p = _ptrs()
+    p[8] = p[6] + 64
+    assert fwd(d, p) == g.GDN2_ERR_ALIAS
+
+
+def test_chunk_forward_empty_batch_is_ok_without_gpu():
+    # B == 0: nothing to do, returns before any launch
+    assert fwd(g.make_desc(0, 64, 2, 4, 128, 128, 64, 1), [0] * 9) == g.GDN2_OK
+
+
+def test_workspace_query():
+    assert g.gdn2_chunk_forward_workspace_bytes(g.make_desc(8, 4096, 16, 16, 128, 128, 64, 1)) == 0
+    assert g.gdn2_chunk_forward_workspace_bytes(None) == 0
+
+
+def test_decode_argument_errors():
+    def dec(desc, p=None):
+        p = p or _ptrs()[:8]
+        return g.gdn2_decode_step(desc, *p, 0)
+
+    d = g.make_desc(256, 1, 16, 16, 128, 128, 64, g.GDN2_BF16)
+    assert dec(None) == g.GDN2_ERR_NULL_POINTER
+    assert dec(g.make_desc(256, 2, 16, 16, 128, 128, 64, 1)) == g.GDN2_ERR_BAD_SHAPE  # T != 1
+    assert dec(g.make_desc(256, 1, 16, 16, 128, 128, 64, 5)) == g.GDN2_ERR_BAD_DTYPE
+    assert dec(g.make_desc(256, 1, 16, 16, 80, 128, 64, 1)) == g.GDN2_ERR_UNSUPPORTED
+    assert dec(g.make_desc(0, 1, 16, 16, 128, 128, 64, 1), [0] * 8) == g.GDN2_OK
+    for i in range(8):
+        p = _ptrs()[:8]
+        p[i] = 0
+        assert dec(d, p) == g.GDN2_ERR_NULL_POINTER, i
+    p = _ptrs()[:8]
+    p[6] += 8
+    assert dec(d, p) == g.GDN2_ERR_BAD_SHAPE
+    for i in range(7):
+        p = _ptrs()[:8]
+        p[7] = p[i]
+        assert dec(d, p) == g.GDN2_ERR_ALIAS, i
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        g.load(str(tmp_path / "nope.so"))
