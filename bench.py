@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet-2 forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over one batch of synthetic
+input: a prefill (gdn2_chunk_forward) over the 1.3B-class layer shape
+(B=8, T=4096, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates and state)
+followed by one decode step (gdn2_decode_step) over the batched-decode shape
+(256 sequences x 16 heads, fp32 128x128 state). Inputs are resident in HBM
+before the timed region. Per-kernel durations come from HIP events recorded
+on the stream the kernels are launched on.
+
+After the timed steps, the decode workload as stated (1024 successive decode
+steps from a random state) runs once for the decode bandwidth figure, and
+the fp64 oracle runs on the host over the prefill batch for the CPU baseline.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PREFILL_KERNEL_SOURCES = ["gated_delta_rule_83_amd/csrc/gdn2_prefill.hpp",
+                          "gated_delta_rule_83_amd/csrc/gdn2_device.hpp",
+                          "gated_delta_rule_83_amd/csrc/gdn2_prefill_inst.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c1_hbm_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_algorithmic(c):
+    """Bytes and flops the method itself must move / compute for one prefill call.
+
+    Bytes: q, k (H_qk heads) and v, o in the input dtype; a, b, w in fp32; the
+    final state S_T in fp32 (S0 is null). Flops per (token, value head):
+    4*C*d_k (four Gram triangles) + 4*C*d_v (Akk U, T Z, Mqk U, Mqb R) +
+    8*d_k*d_v (gamma*K S0, gamma*Q S0, two carry products) + C^2/3 (solve)
+    + d_k*d_v/C (carry scaling)."""
+    es = 2 if c.dtype == "bf16" else 4
+    toks = c.B * c.T
+    by = toks * (c.H_qk * c.d_k * es * 2 + c.H_v * c.d_v * es * 2 + c.H_v * c.d_k * 4 * 2
+                 + c.H_v * c.d_v * 4) + c.B * c.H_v * c.d_k * c.d_v * 4
+    C = c.chunk
+    fl_th = 4 * C * c.d_k + 4 * C * c.d_v + 8 * c.d_k * c.d_v + C * C / 3 + c.d_k * c.d_v / C
+    return by, fl_th * toks * c.H_v
+
+
+def decode_algorithmic(c):
+    """Bytes per decode step: state read + write, q, k, v, o, a, b, w."""
+    es = 2 if c.dtype == "bf16" else 4
+    per_head = c.d_k * c.d_v * 4 * 2 + c.d_v * es * 2 + c.d_k * 4 * 2 + c.d_v * 4
+    qk = c.B * c.H_qk * c.d_k * es * 2
+    return c.B * c.H_v * per_head + qk
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(digest):
+    """HBM bytes per prefill launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_digest") != digest:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="length of the decode workload leg (default: the workload's 1024)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_83_amd as g
+    from gated_delta_rule_83_amd import inputs as gi
+
+    g.load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    cp = gi.config(1)
+    if args.chunk:
+        cp = cp.replace(chunk=args.chunk)
+    cd = gi.config(4)
+    dec_steps = args.decode_steps or cd.decode_steps
+
+    log(f"[bench] drawing prefill inputs {cp.name}")
+    t0 = time.time()
+    dp = gi.make_inputs(cp)
+    tp = gi.to_torch(dp, cp.dtype, dev)
+    o = torch.empty((cp.B, cp.T, cp.H_v, cp.d_v), dtype=tp["q"].dtype, device=dev)
+    S_T = torch.empty((cp.B, cp.H_v, cp.d_k, cp.d_v), dtype=torch.float32, device=dev)
+    log(f"[bench] drawing {dec_steps} decode steps {cd.name} ({time.time() - t0:.1f}s so far)")
+    S_dec0 = torch.from_numpy(gi.make_decode_state(cd)).to(dev)
+    dsteps = [gi.to_torch(gi.make_decode_step(cd, s), cd.dtype, dev) for s in range(dec_steps)]
+    o_dec = torch.empty((cd.B, 1, cd.H_v, cd.d_v), dtype=dsteps[0]["q"].dtype, device=dev)
+    S_dec = S_dec0.clone()
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident ({time.time() - t0:.1f}s)")
+
+    def prefill():
+        g.chunk_forward(tp["q"], tp["k"], tp["v"], tp["a"], tp["b"], tp["w"], None, chunk=cp.chunk,
+                        o=o, S_T=S_T, stream=stream)
+
+    def decode(i):
+        x = dsteps[i % dec_steps]
+        g.decode_step(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], S_dec, o=o_dec, stream=stream)
+
+    for i in range(args.warmup):
+        prefill()
+        decode(i)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        e[2].record(stream)
+        decode(i)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    pre_avg = float(np.mean(pre_ms)) / 1e3
+    log(f"[bench] {K} steps: prefill avg {pre_avg * 1e6:.1f} us (min {min(pre_ms) * 1e3:.1f}), "
+        f"decode avg {np.mean(dec_ms) * 1e3:.1f} us; wall {wall * 1e3:.1f} ms")
+
+    tokens = cp.B * cp.T
+    pbytes, pflops = prefill_algorithmic(cp)
+    value = tokens / pre_avg
+    digest = source_digest(PREFILL_KERNEL_SOURCES)
+    traffic = read_traffic(digest)
+
+    # ---------------------------------------------------------------- decode workload leg
+    S_dec.copy_(S_dec0)
+    torch.cuda.synchronize()
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(dec_steps)]
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    l0.record(stream)
+    for s in range(dec_steps):
+        dev_ev[s][0].record(stream)
+        decode(s)
+        dev_ev[s][1].record(stream)
+    l1.record(stream)
+    torch.cuda.synchronize()
+    dk_ms = [a.elapsed_time(b) for a, b in dev_ev]
+    loop_ms = l0.elapsed_time(l1)
+    dbytes = decode_algorithmic(cd)
+    d_avg = float(np.mean(dk_ms)) / 1e3
+    d_gbs = dbytes / d_avg / 1e9
+    log(f"[bench] decode workload: {dec_steps} steps in {loop_ms:.1f} ms; kernel avg {d_avg * 1e6:.1f} us "
+        f"= {d_gbs:.0f} GB/s algorithmic")
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = min(16, oracle.cores())
+        log(f"[bench] oracle on the host, {nthreads} threads, full prefill batch")
+        _, _, el = oracle.forward(dp["q"] if cp.dtype == "f32" else tp["q"].cpu(),
+                                  dp["k"] if cp.dtype == "f32" else tp["k"].cpu(),
+                                  dp["v"] if cp.dtype == "f32" else tp["v"].cpu(),
+                                  dp["a"], dp["b"], dp["w"], None, nthreads=nthreads, timing=True)
+        cpu = {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+               "sample": f"the whole prefill batch once (B={cp.B}, T={cp.T}, {cp.H_v} heads, "
+                         f"d={cp.d_k}), fp64 recurrence, {el:.1f} s"}
+        log(f"[bench] oracle {el:.1f} s -> {tokens / el:.0f} tokens/s")
+
+    out = {
+        "metric": "prefill tokens/s (T=4096,H=16,d=128) + decode HBM GB/s, % of roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"prefill B{cp.B} T{cp.T} H_qk{cp.H_qk} H_v{cp.H_v} d_k{cp.d_k} d_v{cp.d_v} "
+                         f"chunk{cp.chunk} {cp.dtype} + decode step N{cd.B} H{cd.H_v} d{cd.d_k} fp32 state"),
+            "prefill_kernel_us": pre_avg * 1e6,
+            "decode_kernel_us": float(np.mean(dec_ms)) * 1e3,
+        },
+        "roofline": {
+            "kernel": "prefill",
+            "bound": "hbm",
+            "achieved": pbytes / pre_avg / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": pbytes / pre_avg / 1e9 / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes": pbytes,
+            "mfma_frac_algorithmic": pflops / pre_avg / 1e12 / MFMA_BF16_PEAK_TFS,
+            "kernel_source_digest": digest,
+        },
+        "decode": {
+            "steps": dec_steps,
+            "kernel_us": d_avg * 1e6,
+            "loop_us_per_step": loop_ms * 1e3 / dec_steps,
+            "achieved": d_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": d_gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": dbytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,7 +34,7 @@ int prefill_pick_nct(int B, int H_v, int d_v) {
 hipError_t launch_prefill(const PrefillArgs &in, hipStream_t st) {
   PrefillArgs a = in;
   if (a.B == 0 || a.H_v == 0) return hipSuccess;
-  if (!a.bf16 && a.d_k >= 128 && a.chunk > 32) a.chunk = 32;  // fp32 operands: LDS bound
+  if (!a.bf16 && a.d_k >= 64 && a.chunk > 32) a.chunk = 32;  // fp32 operands: LDS bound
   if (a.bf16) {
     switch (a.d_k) {
       case 16: return launch_prefill_bf16_dk16(a, st);

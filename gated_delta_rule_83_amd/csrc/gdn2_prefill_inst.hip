@@ -14,7 +14,7 @@ namespace gdn2 {
 // are twice as wide as bf16 ones).
 template <int DK, bool BF16>
 constexpr int max_chunk() {
-  return (!BF16 && DK >= 128) ? 32 : 64;
+  return (!BF16 && DK >= 64) ? 32 : 64;
 }
 
 hipError_t GDN2_INST_FN(const PrefillArgs &a, hipStream_t st) {
