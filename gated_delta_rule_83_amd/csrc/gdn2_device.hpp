@@ -159,11 +159,43 @@ template <> __device__ __forceinline__ uint16_t bload<uint16_t>(rsrc_t r, uint32
 template <> __device__ __forceinline__ floatx2 bload<floatx2>(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(floatx2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
+template <> __device__ __forceinline__ uint2 bload<uint2>(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <> __device__ __forceinline__ floatx4 bload<floatx4>(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 __device__ __forceinline__ void bstore(uint16_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b16(x, r, voff, soff, 0);
 }
 __device__ __forceinline__ void bstore(float x, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------- lane shifts
+// x from lane (l - D) of the same 16-lane row (DPP row_shr:D); lanes whose
+// source is outside the row get `fill`. The empty asm keeps each component's
+// shift a separate instruction: when shifts of the components of one vector
+// were left to the optimizer, a single shifted component was reused for all
+// of them (wrong results).
+template <int D>
+__device__ __forceinline__ float row_shr(float x, float fill) {
+  static_assert(D >= 1 && D < 16, "row shift");
+  asm volatile("" : "+v"(x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                               __builtin_bit_cast(int, x),
+                                                               0x110 + D, 0xf, 0xf, false));
+}
+
+// x from lane S of this lane's group of 4 (DPP quad_perm [S,S,S,S]); same
+// empty-asm guard as row_shr.
+template <int S>
+__device__ __forceinline__ float quad_bcast(float x) {
+  static_assert(S >= 0 && S < 4, "quad lane");
+  asm volatile("" : "+v"(x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                       S | (S << 2) | (S << 4) | (S << 6), 0xf, 0xf, false));
 }
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.

@@ -10,24 +10,14 @@
 
 namespace gdn2 {
 
-// Largest chunk whose LDS working set fits one workgroup (fp32 operands
-// are twice as wide as bf16 ones).
-template <int DK, bool BF16>
-constexpr int max_chunk() {
-  return (!BF16 && DK >= 64) ? 32 : 64;
-}
-
 hipError_t GDN2_INST_FN(const PrefillArgs &a, hipStream_t st) {
-  constexpr int DK = GDN2_INST_DK;
-  constexpr bool BF16 = GDN2_INST_BF16 != 0;
-  switch (a.chunk) {
-    case 16: return dispatch_prefill_nct<DK, 16, BF16>(a, st);
-    case 32: return dispatch_prefill_nct<DK, 32, BF16>(a, st);
-    case 64:
-      if constexpr (max_chunk<DK, BF16>() >= 64) return dispatch_prefill_nct<DK, 64, BF16>(a, st);
-      else return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch_prefill<GDN2_INST_DK, GDN2_INST_BF16 != 0>(a, st);
 }
 
 }  // namespace gdn2
+
+#ifdef GDN2_PHASE_TIMING
+extern "C" int gdn2_phase_cycles_read(unsigned long long *host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn2::gdn2_phase_cycles), sizeof(gdn2::gdn2_phase_cycles));
+}
+#endif
