@@ -27,32 +27,107 @@
 // blocks are the prefill's chunks.
 //
 // Everything that does not depend on the entering state (scaled operands,
-// the Gram matrices, the inverses of the diagonal blocks of I + Akb) is
-// computed one chunk ahead by four producer waves, while four consumer
-// waves run the state-dependent part of the previous chunk. A workgroup of
-// 8 waves handles one (sequence, value head, block of 16*NCT value columns,
-// NCT = 1, 2 or 4); consumer wave w < NCT owns the 16-column state tile w.
-// Value columns of S evolve independently, so the column split is exact.
-// Step s of the pipeline (chunk s produced into LDS buffer s%2, chunk s-1
-// consumed from buffer (s-1)%2), with one workgroup barrier after each phase:
+// the Gram matrices) is computed one chunk ahead by four producer waves,
+// while four consumer waves run the state-dependent part of the previous
+// chunk. A workgroup of 8 waves handles one (sequence, value head, block of
+// 16*NCT value columns, NCT = 1, 2 or 4); consumer wave w < NCT owns the
+// 16-column state tile w and reads U = w*v for its columns straight from
+// memory into MFMA operand registers. Value columns of S evolve
+// independently, so the column split is exact. Step s of the pipeline
+// (chunk s produced into LDS buffer s%2, chunk s-1 consumed from buffer
+// (s-1)%2), with one workgroup barrier after each phase:
 //   A. producers: decay scan (wave-local, across lanes), scaled operands
-//      K*gamma | Q*gamma, K/gamma | beta/gamma (also transposed), U = w*v;
-//      then the next chunk's raw inputs are requested into registers.
-//      consumers: X = (gamma*K) S0, Y = (gamma*Q) S0.
-//   B. producer wave q: Gram quadrant q (Akk, Akb, Mqk, Mqb), lower tiles.
-//      consumers: Z = X + Akk U and the blocked forward solve for R.
-//   C. producer wave 0: inverses of the 16x16 diagonal blocks of I + Akb.
-//      consumers: outputs O and the state carry.
+//      K*gamma | Q*gamma, K/gamma | beta/gamma (also transposed); then the
+//      next chunk's decay and erase gates are requested into registers.
+//      consumers: inverses of the 16x16 diagonal blocks of I + Akb (one
+//      block per wave), X = (gamma*K) S0, Y = (gamma*Q) S0.
+//   B. producer wave q: Gram quadrant q (Akk, Akb, Mqk, Mqb), lower tiles;
+//      then the next chunk's keys and queries are requested.
+//      consumers: Z = X + Akk U, the blocked forward solve for R, the
+//      outputs O and the state carry.
 // Consumer products are chained through MFMA accumulators: an accumulator
 // tile is already the next product's B operand.
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "gdn2_device.hpp"
 #include "gdn2_internal.hpp"
 
 namespace gdn2 {
+
+// LDS row layout of an MFMA operand array. A row holds W elements of the
+// contraction index k; a lane's K16 fragment is k = 16kb + 4g .. +3 (lane
+// group g). For bf16 the two K16 blocks of a K32 step are interleaved so
+// that a lane's whole K32 fragment is one 16-byte unit: unit 4P + g of a row
+// holds k = 32P + 4g .. +3 in its first 8 bytes and k = 32P + 16 + 4g .. +3
+// in its second. For fp32 one unit is one K16 fragment (unit 4kb + g).
+// The units of row R are XOR-permuted by (R >> 2) & SW and rows are NU + 2
+// units apart. With the LDS serving 16-byte reads of 16 lanes as one 64-bank
+// pass and 8-byte accesses of 16 consecutive lanes as one 32-bank pass,
+// this keeps the kernel's patterns free of bank conflicts: operand reads
+// (16 lanes on 16 consecutive rows, one unit) and the build's writes (lanes
+// on 8 rows 4 apart, both halves of one unit).
+template <bool BF16, int W>
+struct RowLayout {
+  static constexpr int EPU = BF16 ? 8 : 4;                 // elements per unit
+  static constexpr int NU = (W / EPU) < 4 ? 4 : (W / EPU);  // units per row
+  static constexpr int SW = (NU < 8 ? NU : 8) - 1;
+  static constexpr int STRIDE = 16 * (NU + 2);             // bytes per row
+  static __device__ __forceinline__ uint32_t off(int row, int k) {
+    const int unit = BF16 ? (((k >> 5) << 2) | ((k >> 2) & 3)) : (k >> 2);
+    const int sub = BF16 ? ((((k >> 4) & 1) << 3) | ((k & 3) << 1)) : ((k & 3) << 2);
+    return (uint32_t)(row * STRIDE + ((unit ^ ((row >> 2) & SW)) << 4) + sub);
+  }
+};
+
+// K32 operand: the fragments of two consecutive K16 blocks.
+template <bool BF16>
+struct Pair {
+  typename Op<BF16>::Frag lo, hi;
+};
+
+// Fragment loads and stores in RowLayout L (O = Op<BF16>).
+template <class L, bool BF16>
+__device__ __forceinline__ typename Op<BF16>::Frag frag16(const char *base, int row, int kb, int g) {
+  return *reinterpret_cast<const typename Op<BF16>::Frag *>(base + L::off(row, 16 * kb + 4 * g));
+}
+// K32 step p (K16 blocks 2p, 2p+1); `single` = only block 2p exists
+template <class L, bool BF16, bool single = false>
+__device__ __forceinline__ Pair<BF16> frag32(const char *base, int row, int p, int g) {
+  using O = Op<BF16>;
+  if constexpr (single) {
+    return Pair<BF16>{frag16<L, BF16>(base, row, 2 * p, g), O::zero()};
+  } else if constexpr (BF16) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(base + L::off(row, 32 * p + 4 * g));
+    return Pair<BF16>{__builtin_shufflevector(x, x, 0, 1, 2, 3), __builtin_shufflevector(x, x, 4, 5, 6, 7)};
+  } else {
+    return Pair<BF16>{frag16<L, BF16>(base, row, 2 * p, g), frag16<L, BF16>(base, row, 2 * p + 1, g)};
+  }
+}
+template <class L, bool BF16>
+__device__ __forceinline__ void st4(char *base, int row, int k, floatx4 v) {
+  *reinterpret_cast<typename Op<BF16>::Frag *>(base + L::off(row, k)) = Op<BF16>::from_acc(v);
+}
+template <class L, bool BF16>
+__device__ __forceinline__ void st2(char *base, int row, int k, float x0, float x1) {
+  Op<BF16>::st2(reinterpret_cast<typename Op<BF16>::T *>(base + L::off(row, k)), x0, x1);
+}
+template <class L, bool BF16>
+__device__ __forceinline__ void st1(char *base, int row, int k, float x) {
+  *reinterpret_cast<typename Op<BF16>::T *>(base + L::off(row, k)) = Op<BF16>::cvt(x);
+}
+// acc += a * b over one K32 step; a zero upper half costs nothing extra on
+// the fp32 path (one K16 step), and keeps one MFMA shape on the bf16 path.
+template <bool BF16, bool single = false>
+__device__ __forceinline__ floatx4 mma(floatx4 acc, const Pair<BF16> &a, const Pair<BF16> &b) {
+  using O = Op<BF16>;
+  if constexpr (single && !O::kK32Only)
+    return O::mma16(acc, a.lo, b.lo);
+  else
+    return O::mma32(acc, a.lo, a.hi, b.lo, b.hi);
+}
 
 template <int DK_, int C_, int NCT_, bool BF16_>
 struct PrefillCfg {
@@ -65,14 +140,10 @@ struct PrefillCfg {
   static constexpr int NRT = DK / 16;      // 16-row tiles of the state
   static constexpr int NCH = C / 16;       // 16-token tiles of a chunk
   static constexpr int NTRI = NCH * (NCH + 1) / 2;  // lower 16x16 tiles of a C x C matrix
-  static constexpr int PAD = BF16 ? 8 : 4; // 16 bytes of row padding
-  static constexpr int PADT = BF16 ? 4 : 2;// 8 bytes of row padding
-  static constexpr int LDK = DK + PAD;     // row stride of kqg / kbi
-  static constexpr int LDT = 2 * C + PADT; // row stride of kbiT
-  static constexpr int LDC = C + PAD;      // row stride of akk / akbn
-  static constexpr int LDM = 2 * C + PAD;  // row stride of m = [Mqk | Mqb]
-  static constexpr int LDD = 16 + PAD;     // row stride of the diagonal inverses
-  static constexpr int LDU = C + PADT;     // row stride of uT
+  static constexpr int NKP = (NRT + 1) / 2;          // K32 steps over the key channels
+  typedef RowLayout<BF16, DK> LK;                     // kqg / kbi rows (channels)
+  typedef RowLayout<BF16, 2 * C> LT;                  // kbiT / ab / m rows (tokens)
+  static constexpr int LDD = 20;           // row stride (elements) of the diagonal inverses
   // producer build: wave pw owns key channels [pw*DK/4, (pw+1)*DK/4); a lane
   // owns 4 adjacent channels (quad cq) on RPG consecutive tokens (group rg)
   static constexpr int QPW = DK / 16;              // channel quads per producer wave
@@ -80,37 +151,39 @@ struct PrefillCfg {
   static constexpr int RGE = RGW < C ? RGW : C;    // row groups used
   static constexpr int RPG = C / RGE;              // tokens per row group
   static constexpr int RGL = 64 / QPW;             // lanes per channel quad (>= RGE)
-  // U staging over the 256 producer threads: 4 value columns x TPT tokens
-  static constexpr int UCQ = DVB / 4;
-  static constexpr int UTG = (256 / UCQ) < C ? (256 / UCQ) : C;
-  static constexpr int TPT = C / UTG;
+  // lane -> channel quad: with 8 quads per wave, the two quads that share a
+  // 16-byte operand unit (q and q + 4) are written by the same 16-lane pass
   static_assert(NCT == 1 || NCT == 2 || NCT == 4, "one to four column waves");
   static_assert(DK % 16 == 0 && C % 16 == 0, "16-aligned tiles");
-  static_assert(C % RGE == 0 && C % UTG == 0, "build layout");
-  static_assert(TPT == 1 || TPT == 2 || TPT == 4, "U staging layout");
+  static_assert(C % RGE == 0, "build layout");
 };
 
 // Operands of one chunk (double-buffered: produced for chunk s while chunk
-// s-1 is consumed).
+// s-1 is consumed). Operand arrays are byte arrays in RowLayout order.
 template <class Cf>
 struct ChunkBuf {
-  typedef typename Op<Cf::BF16>::T OT;
-  OT kqg[2 * Cf::C * Cf::LDK];   // rows 0..C-1: k*gamma; rows C..2C-1: q*gamma
-  OT kbi[2 * Cf::C * Cf::LDK];   // rows 0..C-1: k/gamma; rows C..2C-1: (b*k)/gamma
-  OT kbiT[Cf::DK * Cf::LDT];     // kbi transposed: [channel][token (K part | beta part)]
-  OT akk[Cf::C * Cf::LDC];       // Akk, lower blocks (strictly lower inside diagonal blocks)
-  OT akbn[Cf::C * Cf::LDC];      // -Akb, off-diagonal lower blocks
-  OT m[Cf::C * Cf::LDM];         // [Mqk | Mqb], lower blocks incl. diagonal
-  OT dinv[Cf::NCH * 16 * Cf::LDD];   // (I + Akb_rr)^-1 per diagonal block
-  OT uT[Cf::DVB * Cf::LDU];          // U = w * v, transposed: [value column][token]
-  float gamc[Cf::DK];                // gamma_C per key channel
-  int bad[Cf::NP];                   // per producer wave: chunk must be stepped token by token
+  typedef typename Cf::LK LK;
+  typedef typename Cf::LT LT;
+  alignas(16) char kqg[2 * Cf::C * LK::STRIDE];  // rows 0..C-1: k*gamma; rows C..2C-1: q*gamma
+  alignas(16) char kbi[2 * Cf::C * LK::STRIDE];  // rows 0..C-1: k/gamma; rows C..2C-1: (b*k)/gamma
+  alignas(16) char kbiT[Cf::DK * LT::STRIDE];    // kbi transposed: [channel][token (K part | beta part)]
+  // ab: row t, 16-column block 2c = Akk block (t, c) (strictly lower inside
+  // diagonal blocks), block 2c + 1 = -Akb block (t, c) (off-diagonal only);
+  // m: block 2c = Mqk block, 2c + 1 = Mqb block (lower incl. diagonal)
+  alignas(16) char ab[Cf::C * LT::STRIDE];
+  alignas(16) char m[Cf::C * LT::STRIDE];
+  alignas(16) float gamc[Cf::DK];                // gamma_C per key channel
+  alignas(16) int bad[Cf::NP];                   // per producer wave: chunk must be stepped token by token
 };
 
 template <class Cf>
 struct PrefillSmem {
   ChunkBuf<Cf> buf[2];
-  float akbd[Cf::NCH * 16 * 20];     // Akb diagonal blocks (fp32, 16-byte rows), Gram -> inverses
+  // Akb diagonal blocks (fp32, 80-byte rows), Gram -> inverses; row i of a
+  // block is stored at position 4 (i % 4) + i / 4 so that the inverse's
+  // reads of rows 4qq + j (qq = 0..3) fall on distinct banks
+  alignas(16) float akbd[Cf::NCH * 16 * 20];
+  alignas(16) typename Op<Cf::BF16>::T dinv[Cf::NCH * 16 * Cf::LDD];  // (I + Akb_rr)^-1, inverses -> solve
 };
 
 template <class Cf>
@@ -147,82 +220,65 @@ struct PrefillParams {
   int B, T, H_qk, H_v, d_v;
 };
 
-// Chain a contraction over 16-deep blocks kb0..kb1-1 into acc, pairing blocks
-// into K32 steps (see the operand convention in gdn2_device.hpp). An odd
-// last block is padded with a zero half where the chain must keep one shape.
-template <class O, int KB0, int KB1, class FA, class FB>
-__device__ __forceinline__ floatx4 chain(floatx4 acc, FA fa, FB fb) {
-#pragma unroll
-  for (int kb = KB0; kb + 1 < KB1; kb += 2) acc = O::mma32(acc, fa(kb), fa(kb + 1), fb(kb), fb(kb + 1));
-  if constexpr (((KB1 - KB0) & 1) != 0) {
-    if constexpr (O::kK32Only)
-      acc = O::mma32(acc, fa(KB1 - 1), O::zero(), fb(KB1 - 1), O::zero());
-    else
-      acc = O::mma16(acc, fa(KB1 - 1), fb(KB1 - 1));
-  }
-  return acc;
-}
-
-// One quadrant of the chunk's Gram matrix (q = 0 Akk, 1 Akb, 2 Mqk, 3 Mqb):
-// rows of kqg times rows of kbi over the key channels. Per K32 step the wave
-// loads each row block's and each column block's fragments once and reuses
-// them across the quadrant's lower tiles.
+// One quadrant of the chunk's Gram matrix (q = 0 Akk, 1 Akb, 2 Mqk, 3 Mqb)
+// over the key channels, computed transposed: the A operand is rows of kbi
+// (column index s), the B operand rows of kqg (row index t), so that
+// acc[j] = G[t = 16r + lc][s = 16c + 4g + j] and each lane stores four
+// consecutive columns of one row. Per K32 step the wave loads each row
+// block's and each column block's fragments once and reuses them across the
+// quadrant's lower tiles.
 template <class Cf, int q>
 __device__ __forceinline__ void gram_quadrant(ChunkBuf<Cf> &cb, float *akbd, int lg, int lc) {
-  using O = Op<Cf::BF16>;
-  using Frag = typename O::Frag;
-  constexpr int C = Cf::C, NRT = Cf::NRT, NCH = Cf::NCH, LDK = Cf::LDK, LDC = Cf::LDC,
-                LDM = Cf::LDM;
-  const int arow0 = (q >= 2) ? C : 0, brow0 = (q & 1) ? C : 0;
+  constexpr bool BF16 = Cf::BF16;
+  using LK = typename Cf::LK;
+  using LT = typename Cf::LT;
+  constexpr int C = Cf::C, NCH = Cf::NCH, NKP = Cf::NKP, NRT = Cf::NRT;
+  const int trow0 = (q >= 2) ? C : 0, srow0 = (q & 1) ? C : 0;
   floatx4 acc[Cf::NTRI];
 #pragma unroll
   for (int i = 0; i < Cf::NTRI; ++i) acc[i] = zero4();
-  auto frag = [&](const typename O::T *base, int row, int kb) -> Frag {
-    return O::ld(base + (row + lc) * LDK + 16 * kb + 4 * lg);
-  };
-#pragma unroll
-  for (int kb = 0; kb < NRT; kb += 2) {
-    Frag a0[NCH], a1[NCH], b0[NCH], b1[NCH];
+  // all fragments are read before the first product so that the LDS
+  // latencies overlap
+  Pair<BF16> a[NKP][NCH], b[NKP][NCH];
+  static_for<NKP>([&](auto pc) {
+    constexpr int pp = decltype(pc)::value;
+    constexpr bool single = 2 * pp + 1 >= NRT;
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
-      a0[r] = frag(cb.kqg, arow0 + 16 * r, kb);
-      a1[r] = (kb + 1 < NRT) ? frag(cb.kqg, arow0 + 16 * r, kb + 1) : O::zero();
-      b0[r] = frag(cb.kbi, brow0 + 16 * r, kb);
-      b1[r] = (kb + 1 < NRT) ? frag(cb.kbi, brow0 + 16 * r, kb + 1) : O::zero();
+      a[pp][r] = frag32<LK, BF16, single>(cb.kbi, srow0 + 16 * r + lc, pp, lg);
+      b[pp][r] = frag32<LK, BF16, single>(cb.kqg, trow0 + 16 * r + lc, pp, lg);
     }
+  });
+  static_for<NKP>([&](auto pc) {
+    constexpr int pp = decltype(pc)::value;
+    constexpr bool single = 2 * pp + 1 >= NRT;
 #pragma unroll
     for (int r = 0, ti = 0; r < NCH; ++r)
 #pragma unroll
-      for (int c = 0; c <= r; ++c, ++ti) {
-        if constexpr (O::kK32Only || NRT % 2 == 0)
-          acc[ti] = O::mma32(acc[ti], a0[r], a1[r], b0[c], b1[c]);
-        else if (kb + 1 < NRT)
-          acc[ti] = O::mma32(acc[ti], a0[r], a1[r], b0[c], b1[c]);
-        else
-          acc[ti] = O::mma16(acc[ti], a0[r], b0[c]);
-      }
-  }
+      for (int c = 0; c <= r; ++c, ++ti) acc[ti] = mma<BF16, single>(acc[ti], a[pp][c], b[pp][r]);
+  });
 #pragma unroll
   for (int r = 0, ti = 0; r < NCH; ++r)
 #pragma unroll
     for (int c = 0; c <= r; ++c, ++ti) {
-      const int s = 16 * c + lc;
+      const int t = 16 * r + lc, s0 = 16 * c + 4 * lg;
+      floatx4 x = acc[ti];
+      if constexpr (q == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * r + 4 * lg + j;
-        const float x = acc[ti][j];
-        if constexpr (q == 0) {
-          cb.akk[t * LDC + s] = O::cvt(t > s ? x : 0.f);
-        } else if constexpr (q == 1) {
-          if (c != r)
-            cb.akbn[t * LDC + s] = O::cvt(-x);
-          else  // diagonal block, strictly lower part, fp32 for the inverse
-            akbd[r * 16 * 20 + (4 * lg + j) * 20 + lc] = (t > s) ? x : 0.f;
-        } else if constexpr (q == 2) {
-          cb.m[t * LDM + s] = O::cvt(t >= s ? x : 0.f);
-        } else {
-          cb.m[t * LDM + C + s] = O::cvt(t >= s ? x : 0.f);
+        for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
+        st4<LT, BF16>(cb.ab, t, 32 * c + 4 * lg, x);
+      } else if constexpr (q == 1) {
+        if (c != r) {
+          st4<LT, BF16>(cb.ab, t, 32 * c + 16 + 4 * lg, -x);
+        } else {  // diagonal block, strictly lower part, fp32 for the inverse
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
+          *reinterpret_cast<floatx4 *>(&akbd[r * 16 * 20 + (4 * (lc & 3) + (lc >> 2)) * 20 + 4 * lg]) = x;
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = t >= s0 + j ? x[j] : 0.f;
+        st4<LT, BF16>(cb.m, t, 32 * c + (q == 3 ? 16 : 0) + 4 * lg, x);
       }
     }
 }
@@ -262,9 +318,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   using Frag = typename O::Frag;
   // four q/k (or v) elements in their stored type
   using Quad = typename std::conditional<BF16, uint2, floatx4>::type;
-  constexpr int NRT = Cf::NRT, NCH = Cf::NCH, LDK = Cf::LDK, LDT = Cf::LDT, LDC = Cf::LDC,
-                LDM = Cf::LDM, LDD = Cf::LDD, LDU = Cf::LDU, RPG = Cf::RPG, TPT = Cf::TPT,
-                QPW = Cf::QPW, RGE = Cf::RGE;
+  using LK = typename Cf::LK;
+  using LT = typename Cf::LT;
+  constexpr int NRT = Cf::NRT, NCH = Cf::NCH, NKP = Cf::NKP, LDD = Cf::LDD, RPG = Cf::RPG,
+                RGE = Cf::RGE;
   static_assert(sizeof(PrefillSmem<Cf>) <= 160 * 1024, "LDS working set exceeds one CU");
 
   __shared__ PrefillSmem<Cf> sm;
@@ -301,25 +358,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // ---------------------------------------------------------------- producer layout
   // build: lane = (row group rg, channel quad cq) of producer wave `wave`,
   // row group fastest so that a quad's prefix product runs across adjacent lanes
-  const int rg = lane % Cf::RGL, cq = lane / Cf::RGL;
+  const int rg = lane % Cf::RGL;
+  const int cq = Cf::QPW == 8 ? (((lane / Cf::RGL) >> 1) | (((lane / Cf::RGL) & 1) << 2)) : lane / Cf::RGL;
   const bool brow = (RGE == Cf::RGL) || rg < RGE;  // lane holds build rows
   const int ch0 = wave * (DK / 4) + 4 * cq;
   const uint32_t ab_off = (uint32_t)(rg * RPG) * ab_tb + (uint32_t)ch0 * 4u;
   const uint32_t qk_off = (uint32_t)(rg * RPG) * qk_tb + (uint32_t)ch0 * sizeof(ET);
-  // U staging: producer thread tid = (token group utq, column quad ucq)
-  const int ucq = tid % Cf::UCQ, utq = tid / Cf::UCQ, ucol = 4 * ucq;
-  const bool ustager = (Cf::UTG * Cf::UCQ == 256) || utq < Cf::UTG;
-  const uint32_t v_off = (uint32_t)(utq * TPT) * v_tb + (uint32_t)(cb * Cf::DVB + ucol) * sizeof(ET);
-  const uint32_t w_off = (uint32_t)(utq * TPT) * w_tb + (uint32_t)(cb * Cf::DVB + ucol) * 4u;
 
   // Raw inputs of the next chunk to build, held in producer registers.
   floatx4 ra[RPG], rb[RPG];
   Quad rk[RPG], rq[RPG];
-  floatx4 uw[TPT];
-  Quad uv[TPT];
   // The next chunk's inputs are requested in two parts (decay and erase gate
-  // after the build; keys, queries, values and write gate after the Gram
-  // tiles) so that no single phase waits for the whole request to issue.
+  // after the build; keys and queries after the Gram tiles) so that no
+  // single phase waits for the whole request to issue.
   auto load_raw_ab = [&](int t0) {
     if (brow) {
       const rsrc_t ra_ = make_rsrc((const char *)ah + (size_t)t0 * ab_tb, rows_left(t0, ab_tb));
@@ -331,7 +382,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
     }
   };
-  auto load_raw_kqvw = [&](int t0) {
+  auto load_raw_kq = [&](int t0) {
     if (brow) {
       const rsrc_t rk_ = make_rsrc((const char *)kh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb));
       const rsrc_t rq_ = make_rsrc((const char *)qh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb));
@@ -339,15 +390,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       for (int r = 0; r < RPG; ++r) {
         rk[r] = bload<Quad>(rk_, qk_off, r * qk_tb);
         rq[r] = bload<Quad>(rq_, qk_off, r * qk_tb);
-      }
-    }
-    if (ustager) {
-      const rsrc_t rv_ = make_rsrc((const char *)vh + (size_t)t0 * v_tb, rows_left(t0, v_tb));
-      const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * w_tb, rows_left(t0, w_tb));
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        uv[i] = bload<Quad>(rv_, v_off, i * v_tb);
-        uw[i] = bload<floatx4>(rw_, w_off, i * w_tb);
       }
     }
   };
@@ -417,10 +459,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const floatx4 qv = quad_f(rq[r]);
         const floatx4 kb = kv * gi;
         const floatx4 bk = rb[r] * kb;
-        *reinterpret_cast<Frag *>(&cbuf.kqg[tl * LDK + ch0]) = O::from_acc(kv * gm);
-        *reinterpret_cast<Frag *>(&cbuf.kqg[(C + tl) * LDK + ch0]) = O::from_acc(qv * gm);
-        *reinterpret_cast<Frag *>(&cbuf.kbi[tl * LDK + ch0]) = O::from_acc(kb);
-        *reinterpret_cast<Frag *>(&cbuf.kbi[(C + tl) * LDK + ch0]) = O::from_acc(bk);
+        st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * gm);
+        st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * gm);
+        st4<LK, BF16>(cbuf.kbi, tl, ch0, kb);
+        st4<LK, BF16>(cbuf.kbi, C + tl, ch0, bk);
         // transposed copy: 4 (or 2) consecutive tokens per channel at once
         if constexpr (RPG % 4 == 0) {
           kbq[r & 3] = kb;
@@ -428,18 +470,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           if ((r & 3) == 3) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              *reinterpret_cast<Frag *>(&cbuf.kbiT[(ch0 + c) * LDT + tl - 3]) =
-                  O::from_acc(floatx4{kbq[0][c], kbq[1][c], kbq[2][c], kbq[3][c]});
-              *reinterpret_cast<Frag *>(&cbuf.kbiT[(ch0 + c) * LDT + C + tl - 3]) =
-                  O::from_acc(floatx4{bkq[0][c], bkq[1][c], bkq[2][c], bkq[3][c]});
+              st4<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 3, floatx4{kbq[0][c], kbq[1][c], kbq[2][c], kbq[3][c]});
+              st4<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 3, floatx4{bkq[0][c], bkq[1][c], bkq[2][c], bkq[3][c]});
             }
           }
         } else if constexpr (RPG % 2 == 0) {
           if (r & 1) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              O::st2(&cbuf.kbiT[(ch0 + c) * LDT + tl - 1], kbq[0][c], kb[c]);
-              O::st2(&cbuf.kbiT[(ch0 + c) * LDT + C + tl - 1], bkq[0][c], bk[c]);
+              st2<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 1, kbq[0][c], kb[c]);
+              st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bk[c]);
             }
           }
           kbq[0] = kb;
@@ -447,25 +487,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            cbuf.kbiT[(ch0 + c) * LDT + tl] = O::cvt(kb[c]);
-            cbuf.kbiT[(ch0 + c) * LDT + C + tl] = O::cvt(bk[c]);
+            st1<LT, BF16>(cbuf.kbiT, ch0 + c, tl, kb[c]);
+            st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bk[c]);
           }
-        }
-      }
-    }
-    if (ustager) {  // U = w * v, stored transposed for the consumers' B fragments
-      floatx4 u[TPT];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) u[i] = uw[i] * quad_f(uv[i]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        OT *dst = &cbuf.uT[(ucol + c) * LDU + utq * TPT];
-        if constexpr (TPT == 4) {
-          *reinterpret_cast<Frag *>(dst) = O::from_acc(floatx4{u[0][c], u[1][c], u[2][c], u[3][c]});
-        } else if constexpr (TPT == 2) {
-          O::st2(dst, u[0][c], u[1][c]);
-        } else {
-          dst[0] = O::cvt(u[0][c]);
         }
       }
     }
@@ -474,12 +498,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const int nfull = p.T / C;
 
   // The two roles run separate loops (the branch is wave-uniform); each loop
-  // step executes exactly three workgroup barriers, so the barrier counts of
-  // producer and consumer waves always match.
+  // step executes exactly two workgroup barriers, so the barrier counts of
+  // producer and consumer waves always match (a producer wave that has
+  // returned no longer takes part in barriers).
   if (producer) {
     if (nfull > 0) {
       load_raw_ab(0);
-      load_raw_kqvw(0);
+      load_raw_kq(0);
     }
     for (int s = 0; s <= nfull; ++s) {
       ChunkBuf<Cf> &pb = sm.buf[s & 1];  // produced this step (chunk s)
@@ -500,38 +525,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           case 2: gram_quadrant<Cf, 2>(pb, sm.akbd, lg, lc); break;
           default: gram_quadrant<Cf, 3>(pb, sm.akbd, lg, lc); break;
         }
-        if (s + 1 < nfull) load_raw_kqvw((s + 1) * C);
+        if (s + 1 < nfull) load_raw_kq((s + 1) * C);
       }
       GDN2_MARK(2);
-      __syncthreads();
-      GDN2_MARK(7);
-      // phase C: inverses of the diagonal blocks of I + Akb, one block per
-      // producer wave. Lane = (column c, row quarter qq): it holds rows
-      // 4qq..4qq+3 of column c of (I + Akb_rr)^-1 and of Akb_rr. Forward
-      // substitution: at step i the lane owning row i passes the final x_i to
-      // its quad by DPP, and every lane updates its rows below i.
-      for (int r = wave; r < NCH && produce; r += Cf::NP) {
-        const int c = lane >> 2, qq = lane & 3;
-        floatx4 arow[4][4];  // arow[j][k4] = Akb_rr[4qq + j][4k4 .. 4k4+3]
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4)
-            arow[j][k4] = *reinterpret_cast<const floatx4 *>(&sm.akbd[r * 16 * 20 + (4 * qq + j) * 20 + 4 * k4]);
-        floatx4 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = (4 * qq + j == c) ? 1.f : 0.f;
-        static_for<15>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          const float xi = quad_bcast<i / 4>(x[i % 4]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (4 * qq + j > i) x[j] -= arow[j][i / 4][i % 4] * xi;
-        });
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pb.dinv[r * 16 * LDD + (4 * qq + j) * LDD + c] = O::cvt(x[j]);
-      }
-      GDN2_MARK(4);
       __syncthreads();  // buffer s&1 is now complete for the consumers
       GDN2_MARK(7);
     }
@@ -547,6 +543,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       S[rt][j] = (p.S0 && consumer) ? p.S0[s_off + (size_t)(16 * rt + 4 * lg + j) * d_v] : 0.f;
+  // The entering state is complete before the chunk loop: otherwise the
+  // compiler, merging loop entry and back edge, waits for every outstanding
+  // load (including the next chunk's prefetch) at each first use of S.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Token-by-token steps on this wave's columns (exact for any decay).
   auto token_steps = [&](int tb, int te) {
@@ -581,35 +581,116 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       po += __shfl_xor(po, 32, 64);
       if (lg == 0) E::st(oh + (size_t)t * (v_tb / sizeof(ET)) + col, po);
     }
+    // Drain every memory operation of this path here: the fast path reuses
+    // these registers, and an operation left in flight across the merge would
+    // make the compiler wait for all outstanding loads (including the next
+    // chunk's prefetch) at the first such reuse.
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  // U = w * v for this wave's columns as MFMA B fragments: for each 16-token
+  // block c, lane (lc, lg) holds tokens 16c + 4lg + j (j < 4) of column
+  // `col`. Chunk s's raw values are requested during step s and used in
+  // step s+1.
+  using UV = std::conditional_t<BF16, uint16_t, float>;
+  UV rv[NCH][4];
+  float rw[NCH][4];
+  const uint32_t uv_off = (uint32_t)(4 * lg) * v_tb + (uint32_t)col * sizeof(ET);
+  const uint32_t uw_off = (uint32_t)(4 * lg) * w_tb + (uint32_t)col * 4u;
+  auto load_u = [&](int t0) {
+    const rsrc_t rv_ = make_rsrc((const char *)vh + (size_t)t0 * v_tb, rows_left(t0, v_tb));
+    const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * w_tb, rows_left(t0, w_tb));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rv[c][j] = bload<UV>(rv_, uv_off, (uint32_t)(16 * c + j) * v_tb);
+        rw[c][j] = bload<float>(rw_, uw_off, (uint32_t)(16 * c + j) * w_tb);
+      }
+  };
+  auto vf = [](UV x) -> float {
+    if constexpr (BF16)
+      return bf16_to_f32(x);
+    else
+      return x;
+  };
+
+  // Inverse of the diagonal block r of I + Akb (strictly lower Akb_rr from
+  // the Gram step). Lane = (column c, row quarter qq): it holds rows
+  // 4qq..4qq+3 of column c of (I + Akb_rr)^-1 and of Akb_rr. Forward
+  // substitution: at step i the lane owning row i passes the final x_i to
+  // its quad by DPP, and every lane updates its rows; the coefficients
+  // Akb_rr[row][i] of rows <= i are zero, so no row needs masking.
+  auto invert_diag = [&](int r) {
+    const int c = lane >> 2, qq = lane & 3;
+    floatx4 arow[4][4];  // arow[j][k4] = Akb_rr[4qq + j][4k4 .. 4k4+3]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+        arow[j][k4] = *reinterpret_cast<const floatx4 *>(&sm.akbd[r * 16 * 20 + (4 * j + qq) * 20 + 4 * k4]);
+    floatx4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (4 * qq + j == c) ? 1.f : 0.f;
+    static_for<15>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const float xi = quad_bcast<i / 4>(x[i % 4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] -= arow[j][i / 4][i % 4] * xi;
+    });
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.dinv[r * 16 * LDD + (4 * qq + j) * LDD + c] = O::cvt(x[j]);
   };
 
   // consumer registers carried across the phases of one step
   Frag Uf[NCH], Rf[NCH], Rn[NCH];
   floatx4 X[NCH], Y[NCH];
-  auto rowfrag = [&](const OT *base, int ld, int row, int colblk) -> Frag {
-    return O::ld(base + (row + lc) * ld + 16 * colblk + 4 * lg);
-  };
   for (int s = 0; s <= nfull; ++s) {
     ChunkBuf<Cf> &cbf = sm.buf[(s + 1) & 1];  // consumed this step (chunk s-1)
-    const bool work = consumer && s >= 1;
     const int tc = (s - 1) * C;               // first token of the consumed chunk
-    const bool cbad = work && (cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3]) != 0;
-    const bool fast = work && !cbad;
+    // the same flags are read by every wave: the chunk's path is workgroup-uniform
+    const bool chunk_bad = s >= 1 && (cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3]) != 0;
+    const bool cbad = consumer && s >= 1 && chunk_bad;
+    const bool fast = consumer && s >= 1 && !chunk_bad;
     // ---------------------------------------------------------------- phase A
+    if (s >= 1 && !chunk_bad)
+      for (int r = cw; r < NCH; r += 4) invert_diag(r);
+    if (fast) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        Uf[c] = O::from_acc(floatx4{rw[c][0] * vf(rv[c][0]), rw[c][1] * vf(rv[c][1]),
+                                    rw[c][2] * vf(rv[c][2]), rw[c][3] * vf(rv[c][3])});
+    }
+    if (consumer && s < nfull) load_u(s * C);
     if (cbad) {
       token_steps(tc, tc + C);
     } else if (fast) {
-      // X = (gamma * K) S0, Y = (gamma * Q) S0
-      Frag Sf[NRT];
+      // X = (gamma * K) S0, Y = (gamma * Q) S0; all operand reads are issued
+      // before the first product so that their LDS latencies overlap
+      Pair<BF16> kf[NCH][NKP], qf[NCH][NKP];
+      static_for<NKP>([&](auto pc) {
+        constexpr int pp = decltype(pc)::value;
+        constexpr bool single = 2 * pp + 1 >= NRT;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) Sf[rt] = O::from_acc(S[rt]);
+        for (int r = 0; r < NCH; ++r) {
+          kf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, 16 * r + lc, pp, lg);
+          qf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, C + 16 * r + lc, pp, lg);
+        }
+      });
+      Pair<BF16> Sp[NKP];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) Uf[c] = O::ld(&cbf.uT[(cw * 16 + lc) * LDU + 16 * c + 4 * lg]);
-      auto sfrag = [&](int kb) { return Sf[kb]; };
+      for (int pp = 0; pp < NKP; ++pp)
+        Sp[pp] = Pair<BF16>{O::from_acc(S[2 * pp]), 2 * pp + 1 < NRT ? O::from_acc(S[(2 * pp + 1) % NRT]) : O::zero()};
 #pragma unroll
       for (int r = 0; r < NCH; ++r) {
-        X[r] = chain<O, 0, NRT>(zero4(), [&](int kb) { return rowfrag(cbf.kqg, LDK, 16 * r, kb); }, sfrag);
-        Y[r] = chain<O, 0, NRT>(zero4(), [&](int kb) { return rowfrag(cbf.kqg, LDK, C + 16 * r, kb); }, sfrag);
+        X[r] = zero4();
+        Y[r] = zero4();
+        static_for<NKP>([&](auto pc) {
+          constexpr int pp = decltype(pc)::value;
+          constexpr bool single = 2 * pp + 1 >= NRT;
+          X[r] = mma<BF16, single>(X[r], kf[r][pp], Sp[pp]);
+          Y[r] = mma<BF16, single>(Y[r], qf[r][pp], Sp[pp]);
+        });
       }
     }
     GDN2_MARK(1);
@@ -617,38 +698,51 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     GDN2_MARK(7);
     // ---------------------------------------------------------------- phase B
     if (fast) {
+      // All of this phase's LDS operands are read up front: the diagonal
+      // inverses and Gram blocks of the solve and the outputs, then the
+      // transposed keys and gamma_C of the carry.
+      Frag df[NCH];
+      Pair<BF16> af[NCH][NCH], mf[NCH][NCH], tf[NRT][NCH];
+      floatx4 gc[NRT];
+#pragma unroll
+      for (int r = 0; r < NCH; ++r) {
+        df[r] = O::ld(reinterpret_cast<const OT *>(sm.dinv) + r * 16 * LDD + lc * LDD + 4 * lg);
+#pragma unroll
+        for (int c = 0; c <= r; ++c) {
+          // pair c: [Akk block c | -Akb block c]; the last pair only has Akk
+          af[r][c] = c < r ? frag32<LT, BF16>(cbf.ab, 16 * r + lc, c, lg)
+                           : frag32<LT, BF16, true>(cbf.ab, 16 * r + lc, c, lg);
+          mf[r][c] = frag32<LT, BF16>(cbf.m, 16 * r + lc, c, lg);  // [Mqk block c | Mqb block c]
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+        for (int pp = 0; pp < NCH; ++pp) tf[rt][pp] = frag32<LT, BF16>(cbf.kbiT, 16 * rt + lc, pp, lg);
+        gc[rt] = *reinterpret_cast<const floatx4 *>(&cbf.gamc[16 * rt + 4 * lg]);
+      }
       // Z = X + Akk U, then (I + Akb) R = Z by blocked forward substitution:
-      // R_r = D_r (Z_r - sum_{c<r} Akb_rc R_c), one chain over
-      // [Akk blocks 0..r with U] ++ [-Akb blocks 0..r-1 with R].
+      // R_r = D_r (Z_r - sum_{c<r} Akb_rc R_c), one chain over the pairs
+      // ([Akk_rc | -Akb_rc], [U_c ; R_c]) for c < r and (Akk_rr, U_r).
       static_for<NCH>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        auto fa = [&](int kb) {
-          return kb <= r ? rowfrag(cbf.akk, LDC, 16 * r, kb) : rowfrag(cbf.akbn, LDC, 16 * r, kb - r - 1);
-        };
-        auto fb = [&](int kb) { return kb <= r ? Uf[kb] : Rf[kb - r - 1]; };
-        const floatx4 acc = chain<O, 0, 2 * r + 1>(X[r], fa, fb);
-        const floatx4 R = chain<O, 0, 1>(
-            zero4(), [&](int) { return rowfrag(cbf.dinv + r * 16 * LDD, LDD, 0, 0); },
-            [&](int) { return O::from_acc(acc); });
+        floatx4 acc = X[r];
+#pragma unroll
+        for (int c = 0; c < r; ++c) acc = mma<BF16>(acc, af[r][c], Pair<BF16>{Uf[c], Rf[c]});
+        acc = mma<BF16, true>(acc, af[r][r], Pair<BF16>{Uf[r], O::zero()});
+        const floatx4 R = mma<BF16, true>(zero4(), Pair<BF16>{df[r], O::zero()}, Pair<BF16>{O::from_acc(acc), O::zero()});
         Rf[r] = O::from_acc(R);
         Rn[r] = O::from_acc(-R);
       });
-    }
-    GDN2_MARK(3);
-    __syncthreads();
-    GDN2_MARK(7);
-    // ---------------------------------------------------------------- phase C
-    if (fast) {
-      // O = Y + Mqk U - Mqb R, one chain over [Mqk blocks 0..r | Mqb blocks 0..r]
+      GDN2_MARK(3);
+      // O = Y + Mqk U - Mqb R, one chain over the pairs ([Mqk_rc | Mqb_rc], [U_c ; -R_c])
       const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)tc * v_tb, rows_left(tc, v_tb));
       const uint32_t o_off = (uint32_t)(4 * lg) * v_tb + (uint32_t)col * sizeof(ET);
       static_for<NCH>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        auto fa = [&](int kb) {
-          return kb <= r ? rowfrag(cbf.m, LDM, 16 * r, kb) : rowfrag(cbf.m, LDM, 16 * r, NCH + kb - r - 1);
-        };
-        auto fb = [&](int kb) { return kb <= r ? Uf[kb] : Rn[kb - r - 1]; };
-        const floatx4 acc = chain<O, 0, 2 * r + 2>(Y[r], fa, fb);
+        floatx4 acc = Y[r];
+#pragma unroll
+        for (int c = 0; c <= r; ++c) acc = mma<BF16>(acc, mf[r][c], Pair<BF16>{Uf[c], Rn[c]});
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (BF16)
@@ -657,14 +751,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             bstore(acc[j], ro_, o_off, (16 * r + j) * v_tb);
         }
       });
-      // S_C = diag(gamma_C) (S0 + (K/gamma)^T U - (beta/gamma)^T R)
+      // S_C = diag(gamma_C) (S0 + (K/gamma)^T U - (beta/gamma)^T R): kbiT
+      // columns are [K part | beta part], K16 block kb pairs with U_kb or
+      // -R_(kb - NCH)
+      auto ub = [&](int kb) { return kb < NCH ? Uf[kb % NCH] : Rn[(kb - NCH) % NCH]; };
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        auto fa = [&](int kb) { return rowfrag(cbf.kbiT, LDT, 16 * rt, kb); };
-        auto fb = [&](int kb) { return kb < NCH ? Uf[kb] : Rn[kb - NCH]; };
-        const floatx4 acc = chain<O, 0, 2 * NCH>(S[rt], fa, fb);
-        const floatx4 gc = *reinterpret_cast<const floatx4 *>(&cbf.gamc[16 * rt + 4 * lg]);
-        S[rt] = acc * gc;
+        floatx4 acc = S[rt];
+#pragma unroll
+        for (int pp = 0; pp < NCH; ++pp) acc = mma<BF16>(acc, tf[rt][pp], Pair<BF16>{ub(2 * pp), ub(2 * pp + 1)});
+        S[rt] = acc * gc[rt];
       }
     }
     GDN2_MARK(5);
@@ -684,13 +780,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   }
 }
 
-// Largest chunk (<= the requested one) whose double-buffered working set
-// fits one CU's LDS.
+// A chunk size is usable when its double-buffered working set fits one CU's
+// LDS and the K32 operand pairs a consumer wave prefetches for its second
+// phase (solve and output blocks, transposed keys) fit its registers.
+template <int DK, int C, int NCT, bool BF16>
+constexpr bool chunk_fits() {
+  using Cf = PrefillCfg<DK, C, NCT, BF16>;
+  return prefill_smem_bytes<Cf>() <= 160 * 1024 && Cf::NCH * (Cf::NCH + 1) + Cf::NRT * Cf::NCH <= 24;
+}
+
+// Largest usable chunk <= the requested one.
 template <int DK, int NCT, bool BF16>
 constexpr int fitting_chunk(int requested) {
-  return (requested >= 64 && prefill_smem_bytes<PrefillCfg<DK, 64, NCT, BF16>>() <= 160 * 1024) ? 64
-         : (requested >= 32 && prefill_smem_bytes<PrefillCfg<DK, 32, NCT, BF16>>() <= 160 * 1024) ? 32
-                                                                                                  : 16;
+  return (requested >= 64 && chunk_fits<DK, 64, NCT, BF16>()) ? 64
+         : (requested >= 32 && chunk_fits<DK, 32, NCT, BF16>()) ? 32
+                                                                 : 16;
 }
 
 template <int DK, int C, int NCT, bool BF16>
@@ -708,12 +812,12 @@ template <int DK, int NCT, bool BF16>
 hipError_t dispatch_prefill_chunk(const PrefillArgs &a, hipStream_t st) {
   switch (fitting_chunk<DK, NCT, BF16>(a.chunk)) {
     case 64:
-      if constexpr (prefill_smem_bytes<PrefillCfg<DK, 64, NCT, BF16>>() <= 160 * 1024)
+      if constexpr (chunk_fits<DK, 64, NCT, BF16>())
         return launch_prefill_t<DK, 64, NCT, BF16>(a, st);
       else
         return hipErrorInvalidValue;
     case 32:
-      if constexpr (prefill_smem_bytes<PrefillCfg<DK, 32, NCT, BF16>>() <= 160 * 1024)
+      if constexpr (chunk_fits<DK, 32, NCT, BF16>())
         return launch_prefill_t<DK, 32, NCT, BF16>(a, st);
       else
         return hipErrorInvalidValue;
