@@ -171,6 +171,12 @@ __device__ __forceinline__ void bstore(uint16_t x, rsrc_t r, uint32_t voff, uint
 __device__ __forceinline__ void bstore(float x, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
 }
+__device__ __forceinline__ void bstore(uint2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void bstore(floatx4 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), x), r, voff, soff, 0);
+}
 
 // ---------------------------------------------------------------- lane shifts
 // x from lane (l - D) of the same 16-lane row (DPP row_shr:D); lanes whose

@@ -172,6 +172,7 @@ struct ChunkBuf {
   // m: block 2c = Mqk block, 2c + 1 = Mqb block (lower incl. diagonal)
   alignas(16) char ab[Cf::C * LT::STRIDE];
   alignas(16) char m[Cf::C * LT::STRIDE];
+  alignas(16) typename Op<Cf::BF16>::T dinv[Cf::NCH * 16 * Cf::LDD];  // (I + Akb_rr)^-1 per diagonal block
   alignas(16) float gamc[Cf::DK];                // gamma_C per key channel
   alignas(16) int bad[Cf::NP];                   // per producer wave: chunk must be stepped token by token
 };
@@ -183,7 +184,6 @@ struct PrefillSmem {
   // block is stored at position 4 (i % 4) + i / 4 so that the inverse's
   // reads of rows 4qq + j (qq = 0..3) fall on distinct banks
   alignas(16) float akbd[Cf::NCH * 16 * 20];
-  alignas(16) typename Op<Cf::BF16>::T dinv[Cf::NCH * 16 * Cf::LDD];  // (I + Akb_rr)^-1, inverses -> solve
 };
 
 template <class Cf>
@@ -220,67 +220,138 @@ struct PrefillParams {
   int B, T, H_qk, H_v, d_v;
 };
 
-// One quadrant of the chunk's Gram matrix (q = 0 Akk, 1 Akb, 2 Mqk, 3 Mqb)
-// over the key channels, computed transposed: the A operand is rows of kbi
-// (column index s), the B operand rows of kqg (row index t), so that
-// acc[j] = G[t = 16r + lc][s = 16c + 4g + j] and each lane stores four
-// consecutive columns of one row. Per K32 step the wave loads each row
-// block's and each column block's fragments once and reuses them across the
-// quadrant's lower tiles.
-template <class Cf, int q>
-__device__ __forceinline__ void gram_quadrant(ChunkBuf<Cf> &cb, float *akbd, int lg, int lc) {
+// Lower 16x16 tiles (r, c), c <= r, of the chunk's Gram matrices over the
+// key channels; tile (r, c) has index r (r + 1) / 2 + c in the bit masks
+// KK (Akk), KB (Akb), QK (Mqk), QB (Mqb). Tiles are computed transposed: the
+// A operand is rows of kbi (column index s), the B operand rows of kqg (row
+// index t), so acc[j] = G[t = 16r + lc][s = 16c + 4g + j] and each lane
+// stores four consecutive columns of one row. Every fragment the tiles need
+// is read once, before the first product, so that the LDS latencies overlap.
+constexpr bool tile_in(unsigned m, int r, int c) { return ((m >> (r * (r + 1) / 2 + c)) & 1u) != 0; }
+constexpr bool tile_row_used(unsigned m, int r) {
+  bool u = false;
+  for (int c = 0; c <= r; ++c) u = u || tile_in(m, r, c);
+  return u;
+}
+constexpr bool tile_col_used(unsigned m, int c, int nch) {
+  bool u = false;
+  for (int r = c; r < nch; ++r) u = u || tile_in(m, r, c);
+  return u;
+}
+template <class Cf, unsigned KK, unsigned KB, unsigned QK, unsigned QB>
+__device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, float *akbd, int lg, int lc) {
   constexpr bool BF16 = Cf::BF16;
   using LK = typename Cf::LK;
   using LT = typename Cf::LT;
   constexpr int C = Cf::C, NCH = Cf::NCH, NKP = Cf::NKP, NRT = Cf::NRT;
-  const int trow0 = (q >= 2) ? C : 0, srow0 = (q & 1) ? C : 0;
-  floatx4 acc[Cf::NTRI];
-#pragma unroll
-  for (int i = 0; i < Cf::NTRI; ++i) acc[i] = zero4();
-  // all fragments are read before the first product so that the LDS
-  // latencies overlap
-  Pair<BF16> a[NKP][NCH], b[NKP][NCH];
+  constexpr unsigned ALL = KK | KB | QK | QB;
+  Pair<BF16> tk[NKP][NCH], tq[NKP][NCH], sk[NKP][NCH], sb[NKP][NCH];
   static_for<NKP>([&](auto pc) {
     constexpr int pp = decltype(pc)::value;
     constexpr bool single = 2 * pp + 1 >= NRT;
-#pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      a[pp][r] = frag32<LK, BF16, single>(cb.kbi, srow0 + 16 * r + lc, pp, lg);
-      b[pp][r] = frag32<LK, BF16, single>(cb.kqg, trow0 + 16 * r + lc, pp, lg);
-    }
+    static_for<NCH>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (tile_row_used(KK | KB, i)) tk[pp][i] = frag32<LK, BF16, single>(cb.kqg, 16 * i + lc, pp, lg);
+      if constexpr (tile_row_used(QK | QB, i)) tq[pp][i] = frag32<LK, BF16, single>(cb.kqg, C + 16 * i + lc, pp, lg);
+      if constexpr (tile_col_used(KK | QK, i, NCH)) sk[pp][i] = frag32<LK, BF16, single>(cb.kbi, 16 * i + lc, pp, lg);
+      if constexpr (tile_col_used(KB | QB, i, NCH)) sb[pp][i] = frag32<LK, BF16, single>(cb.kbi, C + 16 * i + lc, pp, lg);
+    });
   });
-  static_for<NKP>([&](auto pc) {
-    constexpr int pp = decltype(pc)::value;
-    constexpr bool single = 2 * pp + 1 >= NRT;
+  static_for<NCH>([&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    static_for<r + 1>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      static_for<4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        constexpr unsigned M = q == 0 ? KK : q == 1 ? KB : q == 2 ? QK : QB;
+        if constexpr (tile_in(M, r, c)) {
+          floatx4 x = zero4();
+          static_for<NKP>([&](auto pc) {
+            constexpr int pp = decltype(pc)::value;
+            constexpr bool single = 2 * pp + 1 >= NRT;
+            const Pair<BF16> &a = (q & 1) ? sb[pp][c] : sk[pp][c];
+            const Pair<BF16> &b = (q >= 2) ? tq[pp][r] : tk[pp][r];
+            x = mma<BF16, single>(x, a, b);
+          });
+          const int t = 16 * r + lc, s0 = 16 * c + 4 * lg;
+          if constexpr (q == 0) {
 #pragma unroll
-    for (int r = 0, ti = 0; r < NCH; ++r)
+            for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
+            st4<LT, BF16>(cb.ab, t, 32 * c + 4 * lg, x);
+          } else if constexpr (q == 1) {
+            if constexpr (c != r) {
+              st4<LT, BF16>(cb.ab, t, 32 * c + 16 + 4 * lg, -x);
+            } else {  // diagonal block, strictly lower part, fp32 for the inverse
 #pragma unroll
-      for (int c = 0; c <= r; ++c, ++ti) acc[ti] = mma<BF16, single>(acc[ti], a[pp][c], b[pp][r]);
-  });
+              for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
+              *reinterpret_cast<floatx4 *>(&akbd[r * 16 * 20 + (4 * (lc & 3) + (lc >> 2)) * 20 + 4 * lg]) = x;
+            }
+          } else {
 #pragma unroll
-  for (int r = 0, ti = 0; r < NCH; ++r)
-#pragma unroll
-    for (int c = 0; c <= r; ++c, ++ti) {
-      const int t = 16 * r + lc, s0 = 16 * c + 4 * lg;
-      floatx4 x = acc[ti];
-      if constexpr (q == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
-        st4<LT, BF16>(cb.ab, t, 32 * c + 4 * lg, x);
-      } else if constexpr (q == 1) {
-        if (c != r) {
-          st4<LT, BF16>(cb.ab, t, 32 * c + 16 + 4 * lg, -x);
-        } else {  // diagonal block, strictly lower part, fp32 for the inverse
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
-          *reinterpret_cast<floatx4 *>(&akbd[r * 16 * 20 + (4 * (lc & 3) + (lc >> 2)) * 20 + 4 * lg]) = x;
+            for (int j = 0; j < 4; ++j) x[j] = t >= s0 + j ? x[j] : 0.f;
+            st4<LT, BF16>(cb.m, t, 32 * c + (q == 3 ? 16 : 0) + 4 * lg, x);
+          }
         }
-      } else {
+      });
+    });
+  });
+  (void)ALL;
+}
+
+// Work split of the Gram tiles and diagonal inverses over the 4 producer
+// waves: waves 2 and 3 take Mqk and Mqb; waves 0 and 1 share Akk and Akb so
+// that the wave which computes the diagonal Akb tile of row block r also
+// inverts it, with about equal work on both.
+template <int NCH>
+struct GramSplit {
+  static constexpr unsigned FULL = (1u << (NCH * (NCH + 1) / 2)) - 1u;
+  // NCH = 1: one tile per quadrant; NCH = 2: tiles 0 = (0,0), 1 = (1,0), 2 = (1,1)
+  static constexpr unsigned KK0 = NCH == 1 ? 1u : NCH == 2 ? 3u : FULL;
+  static constexpr unsigned KB0 = NCH == 1 ? 0u : NCH == 2 ? 1u : 0u;
+  static constexpr unsigned INV0 = NCH == 1 ? 0u : NCH == 2 ? 1u : 0u;  // diagonal blocks wave 0 inverts
+  static constexpr unsigned KK1 = FULL & ~KK0;
+  static constexpr unsigned KB1 = FULL & ~KB0;
+  static constexpr unsigned INV1 = ((1u << NCH) - 1u) & ~INV0;
+};
+
+// Inverses of the diagonal blocks r0 .. r0+NB-1 of I + Akb (strictly lower
+// Akb_rr, fp32, from the Gram step) into dinv; the NB independent
+// substitutions run interleaved. Lane = (column c, row quarter qq): it holds
+// rows 4qq..4qq+3 of column c of (I + Akb_rr)^-1 and of Akb_rr. Forward
+// substitution: at step i the lane owning row i passes the final x_i to its
+// quad by DPP, and every lane updates its rows; the coefficients
+// Akb_rr[row][i] of rows <= i are zero, so no row needs masking.
+template <class Cf, int NB>
+__device__ __forceinline__ void invert_diag(const float *akbd, typename Op<Cf::BF16>::T *dinv, int r0, int lane) {
+  using O = Op<Cf::BF16>;
+  constexpr int LDD = Cf::LDD;
+  const int c = lane >> 2, qq = lane & 3;
+  floatx4 arow[NB][4][4];  // arow[b][j][k4] = Akb_rr[4qq + j][4k4 .. 4k4+3], r = r0 + b
+  floatx4 x[NB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = t >= s0 + j ? x[j] : 0.f;
-        st4<LT, BF16>(cb.m, t, 32 * c + (q == 3 ? 16 : 0) + 4 * lg, x);
-      }
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+        arow[b][j][k4] = *reinterpret_cast<const floatx4 *>(&akbd[(r0 + b) * 16 * 20 + (4 * j + qq) * 20 + 4 * k4]);
+      x[b][j] = (4 * qq + j == c) ? 1.f : 0.f;
     }
+  }
+  static_for<15>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    float xi[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xi[b] = quad_bcast<i / 4>(x[b][i % 4]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[b][j] -= arow[b][j][i / 4][i % 4] * xi[b];
+  });
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dinv[(r0 + b) * 16 * LDD + (4 * qq + j) * LDD + c] = O::cvt(x[b][j]);
 }
 
 // Block -> (sequence, value head, column block). Workgroups are dealt
@@ -353,7 +424,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const float *wh = p.w + tok0 * p.H_v * d_v + (size_t)h * d_v;
   ET *oh = (ET *)p.o + tok0 * p.H_v * d_v + (size_t)h * d_v;
   const size_t s_off = ((size_t)n * p.H_v + h) * (size_t)DK * d_v + col;
-  auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return (uint32_t)(p.T - t0) * tb; };
+  // bytes from token t0 to the end of the sequence (0 past the end: a
+  // buffer access beyond the range returns 0 without touching memory)
+  auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return t0 < p.T ? (uint32_t)(p.T - t0) * tb : 0u; };
 
   // ---------------------------------------------------------------- producer layout
   // build: lane = (row group rg, channel quad cq) of producer wave `wave`,
@@ -365,31 +438,37 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const uint32_t ab_off = (uint32_t)(rg * RPG) * ab_tb + (uint32_t)ch0 * 4u;
   const uint32_t qk_off = (uint32_t)(rg * RPG) * qk_tb + (uint32_t)ch0 * sizeof(ET);
 
-  // Raw inputs of the next chunk to build, held in producer registers.
-  floatx4 ra[RPG], rb[RPG];
-  Quad rk[RPG], rq[RPG];
-  // The next chunk's inputs are requested in two parts (decay and erase gate
-  // after the build; keys and queries after the Gram tiles) so that no
-  // single phase waits for the whole request to issue.
-  auto load_raw_ab = [&](int t0) {
+  // Raw inputs of the chunks to build, held in two register sets (chunk s
+  // in set s % 2) and requested two chunks ahead so that a request has more
+  // than a full step to complete: decay and erase gate after the build,
+  // keys and queries after the Gram tiles, so that neither burst of
+  // requests delays the other phase's work.
+  floatx4 ra[2][RPG], rb[2][RPG];
+  Quad rk[2][RPG], rq[2][RPG];
+  struct RawSrc {
+    rsrc_t a, b, k, q;
+  };
+  auto raw_src = [&](int t0) {
+    return RawSrc{make_rsrc((const char *)ah + (size_t)t0 * ab_tb, rows_left(t0, ab_tb)),
+                  make_rsrc((const char *)bh + (size_t)t0 * ab_tb, rows_left(t0, ab_tb)),
+                  make_rsrc((const char *)kh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb)),
+                  make_rsrc((const char *)qh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb))};
+  };
+  auto load_ab = [&](auto P, const RawSrc &src) {
     if (brow) {
-      const rsrc_t ra_ = make_rsrc((const char *)ah + (size_t)t0 * ab_tb, rows_left(t0, ab_tb));
-      const rsrc_t rb_ = make_rsrc((const char *)bh + (size_t)t0 * ab_tb, rows_left(t0, ab_tb));
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
-        ra[r] = bload<floatx4>(ra_, ab_off, r * ab_tb);
-        rb[r] = bload<floatx4>(rb_, ab_off, r * ab_tb);
+        ra[P][r] = bload<floatx4>(src.a, ab_off, r * ab_tb);
+        rb[P][r] = bload<floatx4>(src.b, ab_off, r * ab_tb);
       }
     }
   };
-  auto load_raw_kq = [&](int t0) {
+  auto load_kq = [&](auto P, const RawSrc &src) {
     if (brow) {
-      const rsrc_t rk_ = make_rsrc((const char *)kh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb));
-      const rsrc_t rq_ = make_rsrc((const char *)qh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb));
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
-        rk[r] = bload<Quad>(rk_, qk_off, r * qk_tb);
-        rq[r] = bload<Quad>(rq_, qk_off, r * qk_tb);
+        rk[P][r] = bload<Quad>(src.k, qk_off, r * qk_tb);
+        rq[P][r] = bload<Quad>(src.q, qk_off, r * qk_tb);
       }
     }
   };
@@ -407,15 +486,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 
   // Build chunk operands into buffer cbuf (producer waves; no workgroup sync
   // inside: the decay scan runs across the lanes of one wave).
-  auto build = [&](ChunkBuf<Cf> &cbuf) {
+  auto build = [&](auto P, ChunkBuf<Cf> &cbuf) {
     // cumulative decay within the lane's RPG tokens
     floatx4 gl[RPG];
     floatx4 pr = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
-      if (brow) pr *= ra[r];
+      if (brow) pr *= ra[P][r];
       gl[r] = pr;
     }
+
     // inclusive prefix product over the row groups (adjacent lanes): DPP row
     // shifts when a quad's groups fit in one 16-lane row, lane shuffles else
     floatx4 inc = pr, pre;
@@ -455,10 +535,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const floatx4 gm = pre * gl[r];
         const floatx4 gi = {__builtin_amdgcn_rcpf(gm[0]), __builtin_amdgcn_rcpf(gm[1]),
                             __builtin_amdgcn_rcpf(gm[2]), __builtin_amdgcn_rcpf(gm[3])};
-        const floatx4 kv = quad_f(rk[r]);
-        const floatx4 qv = quad_f(rq[r]);
+        const floatx4 kv = quad_f(rk[P][r]);
+        const floatx4 qv = quad_f(rq[P][r]);
         const floatx4 kb = kv * gi;
-        const floatx4 bk = rb[r] * kb;
+        const floatx4 bk = rb[P][r] * kb;
         st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * gm);
         st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * gm);
         st4<LK, BF16>(cbuf.kbi, tl, ch0, kb);
@@ -496,40 +576,78 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   };
 
   const int nfull = p.T / C;
+  // pipeline steps: chunk s is produced in step s and consumed in step s+1;
+  // the count is rounded up to even so that the producers' two-step loop
+  // body has no conditional part (the extra step only passes the barriers)
+  const int nsteps = (nfull + 2) & ~1;
 
-  // The two roles run separate loops (the branch is wave-uniform); each loop
-  // step executes exactly two workgroup barriers, so the barrier counts of
-  // producer and consumer waves always match (a producer wave that has
-  // returned no longer takes part in barriers).
+  // The two roles run separate loops (the branch is wave-uniform) of nsteps
+  // steps each; every step executes exactly two workgroup barriers, so the
+  // barrier counts of producer and consumer waves always match.
   if (producer) {
-    if (nfull > 0) {
-      load_raw_ab(0);
-      load_raw_kq(0);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    {  // chunks 0 and 1, unconditional and in the loop's request order
+       // (the scheduling barriers keep that order)
+      const RawSrc src0 = raw_src(nfull > 0 ? 0 : p.T);
+      const RawSrc src1 = raw_src(nfull > 1 ? C : p.T);
+      load_ab(I0(), src0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_kq(I0(), src0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_ab(I1(), src1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_kq(I1(), src1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    for (int s = 0; s <= nfull; ++s) {
-      ChunkBuf<Cf> &pb = sm.buf[s & 1];  // produced this step (chunk s)
+    // One pipeline step; chunk s uses raw register set P = s % 2. The
+    // requests for chunk s+2 are issued unconditionally (past the last
+    // chunk they read nothing): every path through the loop then has the
+    // same request order, so the compiler's waits before the build only
+    // cover set P.
+    auto pstep = [&](auto P, int s) {
+      ChunkBuf<Cf> &pb = sm.buf[P];  // produced this step (chunk s)
       const bool produce = s < nfull;
-      // phase A: operands of chunk s, then request chunk s+1's inputs
-      if (produce) {
-        build(pb);
-        if (s + 1 < nfull) load_raw_ab((s + 1) * C);
-      }
+      const int tn = s + 2 < nfull ? (s + 2) * C : p.T;
+      // phase A: operands of chunk s, then request chunk s+2's gates
+      if (produce) build(P, pb);
+      load_ab(P, raw_src(tn));
       GDN2_MARK(0);
       __syncthreads();
       GDN2_MARK(7);
-      // phase B: Gram quadrant `wave`
+      // phase B: Gram tiles (and diagonal inverses), then chunk s+2's keys
+      // and queries
       if (produce) {
+        using GS = GramSplit<NCH>;
+        // each of waves 0 and 1 inverts the diagonal blocks whose Akb tile it
+        // has just written (same wave: no synchronisation needed)
+        auto invert_set = [&](auto mask) {
+          static_for<NCH>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            if constexpr (((decltype(mask)::value >> r) & 1u) != 0) invert_diag<Cf, 1>(sm.akbd, pb.dinv, r, lane);
+          });
+        };
         switch (wave) {
-          case 0: gram_quadrant<Cf, 0>(pb, sm.akbd, lg, lc); break;
-          case 1: gram_quadrant<Cf, 1>(pb, sm.akbd, lg, lc); break;
-          case 2: gram_quadrant<Cf, 2>(pb, sm.akbd, lg, lc); break;
-          default: gram_quadrant<Cf, 3>(pb, sm.akbd, lg, lc); break;
+          case 0:
+            gram_tiles<Cf, GS::KK0, GS::KB0, 0u, 0u>(pb, sm.akbd, lg, lc);
+            invert_set(std::integral_constant<unsigned, GS::INV0>());
+            break;
+          case 1:
+            gram_tiles<Cf, GS::KK1, GS::KB1, 0u, 0u>(pb, sm.akbd, lg, lc);
+            invert_set(std::integral_constant<unsigned, GS::INV1>());
+            break;
+          case 2: gram_tiles<Cf, 0u, 0u, GS::FULL, 0u>(pb, sm.akbd, lg, lc); break;
+          default: gram_tiles<Cf, 0u, 0u, 0u, GS::FULL>(pb, sm.akbd, lg, lc); break;
         }
-        if (s + 1 < nfull) load_raw_kq((s + 1) * C);
       }
+      load_kq(P, raw_src(tn));
       GDN2_MARK(2);
-      __syncthreads();  // buffer s&1 is now complete for the consumers
+      __syncthreads();  // buffer P is now complete for the consumers
       GDN2_MARK(7);
+    };
+    for (int s = 0; s < nsteps; s += 2) {
+      pstep(I0(), s);
+      pstep(I1(), s + 1);
     }
     GDN2_TIMER_STORE
     return;
@@ -615,58 +733,52 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       return x;
   };
 
-  // Inverse of the diagonal block r of I + Akb (strictly lower Akb_rr from
-  // the Gram step). Lane = (column c, row quarter qq): it holds rows
-  // 4qq..4qq+3 of column c of (I + Akb_rr)^-1 and of Akb_rr. Forward
-  // substitution: at step i the lane owning row i passes the final x_i to
-  // its quad by DPP, and every lane updates its rows; the coefficients
-  // Akb_rr[row][i] of rows <= i are zero, so no row needs masking.
-  auto invert_diag = [&](int r) {
-    const int c = lane >> 2, qq = lane & 3;
-    floatx4 arow[4][4];  // arow[j][k4] = Akb_rr[4qq + j][4k4 .. 4k4+3]
+  // Outputs of the last chunk, held until the next step's loads of U have
+  // been consumed (a store issued before them would make that wait include
+  // the store): lane (lc, lg) holds token otc + 16r + lc, columns
+  // col0 + 4lg .. +3.
+  using OS = std::conditional_t<BF16, uint2, floatx4>;
+  OS opend[NCH];
+  int otc = -1;
+  const uint32_t o_off = (uint32_t)lc * v_tb + (uint32_t)(cb * Cf::DVB + cw * 16 + 4 * lg) * sizeof(ET);
+  auto flush_o = [&]() {
+    if (otc >= 0) {
+      const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)otc * v_tb, rows_left(otc, v_tb));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-        arow[j][k4] = *reinterpret_cast<const floatx4 *>(&sm.akbd[r * 16 * 20 + (4 * j + qq) * 20 + 4 * k4]);
-    floatx4 x;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = (4 * qq + j == c) ? 1.f : 0.f;
-    static_for<15>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const float xi = quad_bcast<i / 4>(x[i % 4]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] -= arow[j][i / 4][i % 4] * xi;
-    });
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm.dinv[r * 16 * LDD + (4 * qq + j) * LDD + c] = O::cvt(x[j]);
+      for (int r = 0; r < NCH; ++r) bstore(opend[r], ro_, o_off, (uint32_t)(16 * r) * v_tb);
+      otc = -1;
+    }
   };
 
   // consumer registers carried across the phases of one step
   Frag Uf[NCH], Rf[NCH], Rn[NCH];
   floatx4 X[NCH], Y[NCH];
-  for (int s = 0; s <= nfull; ++s) {
+  for (int s = 0; s < nsteps; ++s) {
     ChunkBuf<Cf> &cbf = sm.buf[(s + 1) & 1];  // consumed this step (chunk s-1)
     const int tc = (s - 1) * C;               // first token of the consumed chunk
+    const bool live = s >= 1 && s <= nfull;   // a chunk is consumed this step
     // the same flags are read by every wave: the chunk's path is workgroup-uniform
-    const bool chunk_bad = s >= 1 && (cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3]) != 0;
-    const bool cbad = consumer && s >= 1 && chunk_bad;
-    const bool fast = consumer && s >= 1 && !chunk_bad;
+    const bool chunk_bad = live && (cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3]) != 0;
+    const bool cbad = consumer && live && chunk_bad;
+    const bool fast = consumer && live && !chunk_bad;
     // ---------------------------------------------------------------- phase A
-    if (s >= 1 && !chunk_bad)
-      for (int r = cw; r < NCH; r += 4) invert_diag(r);
     if (fast) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         Uf[c] = O::from_acc(floatx4{rw[c][0] * vf(rv[c][0]), rw[c][1] * vf(rv[c][1]),
                                     rw[c][2] * vf(rv[c][2]), rw[c][3] * vf(rv[c][3])});
     }
-    if (consumer && s < nfull) load_u(s * C);
+    flush_o();
+    // unconditional (reads nothing past the last chunk): one request order on
+    // every path keeps the compiler's waits exact
+    load_u(s < nfull ? s * C : p.T);
     if (cbad) {
       token_steps(tc, tc + C);
     } else if (fast) {
       // X = (gamma * K) S0, Y = (gamma * Q) S0; all operand reads are issued
-      // before the first product so that their LDS latencies overlap
+      // before the first product so that their LDS latencies overlap. Y is
+      // formed transposed (operands swapped): lane (lc, lg) holds Y[t = lc]
+      // at columns 4lg..4lg+3, the layout of the output store.
       Pair<BF16> kf[NCH][NKP], qf[NCH][NKP];
       static_for<NKP>([&](auto pc) {
         constexpr int pp = decltype(pc)::value;
@@ -689,7 +801,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           constexpr int pp = decltype(pc)::value;
           constexpr bool single = 2 * pp + 1 >= NRT;
           X[r] = mma<BF16, single>(X[r], kf[r][pp], Sp[pp]);
-          Y[r] = mma<BF16, single>(Y[r], qf[r][pp], Sp[pp]);
+          Y[r] = mma<BF16, single>(Y[r], Sp[pp], qf[r][pp]);  // transposed
         });
       }
     }
@@ -706,7 +818,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       floatx4 gc[NRT];
 #pragma unroll
       for (int r = 0; r < NCH; ++r) {
-        df[r] = O::ld(reinterpret_cast<const OT *>(sm.dinv) + r * 16 * LDD + lc * LDD + 4 * lg);
+        df[r] = O::ld(cbf.dinv + r * 16 * LDD + lc * LDD + 4 * lg);
 #pragma unroll
         for (int c = 0; c <= r; ++c) {
           // pair c: [Akk block c | -Akb block c]; the last pair only has Akk
@@ -735,22 +847,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         Rn[r] = O::from_acc(-R);
       });
       GDN2_MARK(3);
-      // O = Y + Mqk U - Mqb R, one chain over the pairs ([Mqk_rc | Mqb_rc], [U_c ; -R_c])
-      const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)tc * v_tb, rows_left(tc, v_tb));
-      const uint32_t o_off = (uint32_t)(4 * lg) * v_tb + (uint32_t)col * sizeof(ET);
+      // O^T = Y^T + U^T Mqk^T - R^T Mqb^T, one chain over the pairs
+      // ([U_c ; -R_c]^T, [Mqk_rc | Mqb_rc]); U and R tiles are already A
+      // operands of the transposed product. The outputs are stored at the
+      // start of the next step.
       static_for<NCH>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         floatx4 acc = Y[r];
 #pragma unroll
-        for (int c = 0; c <= r; ++c) acc = mma<BF16>(acc, mf[r][c], Pair<BF16>{Uf[c], Rn[c]});
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (BF16)
-            bstore(f32_to_bf16(acc[j]), ro_, o_off, (16 * r + j) * v_tb);
-          else
-            bstore(acc[j], ro_, o_off, (16 * r + j) * v_tb);
-        }
+        for (int c = 0; c <= r; ++c) acc = mma<BF16>(acc, Pair<BF16>{Uf[c], Rn[c]}, mf[r][c]);
+        if constexpr (BF16)
+          opend[r] = __builtin_bit_cast(uint2, __builtin_convertvector(acc, bf16x4));
+        else
+          opend[r] = acc;
       });
+      otc = tc;
       // S_C = diag(gamma_C) (S0 + (K/gamma)^T U - (beta/gamma)^T R): kbiT
       // columns are [K part | beta part], K16 block kb pairs with U_kb or
       // -R_(kb - NCH)
@@ -770,6 +881,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   GDN2_TIMER_STORE
 
   if (consumer) {
+    flush_o();
     if (nfull * C < p.T) token_steps(nfull * C, p.T);
     if (p.S_T) {
 #pragma unroll
