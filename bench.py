@@ -34,7 +34,7 @@ MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 PREFILL_KERNEL_SOURCES = ["gated_delta_rule_83_amd/csrc/gdn2_prefill.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_device.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_prefill_inst.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c1_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_B8_T4096_H16_d128_bf16_hbm_traffic.txt")
 
 
 def log(*a):
@@ -100,6 +100,9 @@ def main():
                     help="length of the decode workload leg (default: the workload's 1024)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
+    ap.add_argument("--counters", action="store_true",
+                    help="for hardware-counter runs: launch the prefill and the decode kernel twice each "
+                         "and a plain 256 MiB device copy twice (counter calibration), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -145,6 +148,17 @@ def main():
     def decode(i):
         x = dsteps[i % dec_steps]
         g.decode_step(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], S_dec, o=o_dec, stream=stream)
+
+    if args.counters:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for i in range(2):
+            prefill()
+            decode(i)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] counter launches done: 2 x prefill, 2 x decode, 2 x copy of 256 MiB")
+        return
 
     for i in range(args.warmup):
         prefill()
