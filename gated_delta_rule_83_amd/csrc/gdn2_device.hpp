@@ -204,6 +204,18 @@ __device__ __forceinline__ float quad_bcast(float x) {
                                        S | (S << 2) | (S << 4) | (S << 6), 0xf, 0xf, false));
 }
 
+// Empty asm on every 32-bit part of x: the value counts as used and
+// redefined here, so its computation cannot move past this point.
+template <class V>
+__device__ __forceinline__ void pin_regs(V &x) {
+  static_assert(sizeof(V) % 4 == 0, "32-bit parts");
+  uint32_t w[sizeof(V) / 4];
+  __builtin_memcpy(w, &x, sizeof(V));
+#pragma unroll
+  for (unsigned i = 0; i < sizeof(V) / 4; ++i) asm volatile("" : "+v"(w[i]));
+  __builtin_memcpy(&x, w, sizeof(V));
+}
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
 template <class F, int... Is>
 __device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, Is...>) {

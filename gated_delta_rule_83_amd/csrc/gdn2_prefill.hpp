@@ -711,19 +711,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // `col`. Chunk s's raw values are requested during step s and used in
   // step s+1.
   using UV = std::conditional_t<BF16, uint16_t, float>;
-  UV rv[NCH][4];
-  float rw[NCH][4];
+  // two register sets: chunk s's raw values in set s % 2
+  UV rv[2][NCH][4];
+  float rw[2][NCH][4];
   const uint32_t uv_off = (uint32_t)(4 * lg) * v_tb + (uint32_t)col * sizeof(ET);
   const uint32_t uw_off = (uint32_t)(4 * lg) * w_tb + (uint32_t)col * 4u;
-  auto load_u = [&](int t0) {
+  auto load_u = [&](auto P, int t0) {
     const rsrc_t rv_ = make_rsrc((const char *)vh + (size_t)t0 * v_tb, rows_left(t0, v_tb));
     const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * w_tb, rows_left(t0, w_tb));
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        rv[c][j] = bload<UV>(rv_, uv_off, (uint32_t)(16 * c + j) * v_tb);
-        rw[c][j] = bload<float>(rw_, uw_off, (uint32_t)(16 * c + j) * w_tb);
+        rv[P][c][j] = bload<UV>(rv_, uv_off, (uint32_t)(16 * c + j) * v_tb);
+        rw[P][c][j] = bload<float>(rw_, uw_off, (uint32_t)(16 * c + j) * w_tb);
       }
   };
   auto vf = [](UV x) -> float {
@@ -753,42 +754,55 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // consumer registers carried across the phases of one step
   Frag Uf[NCH], Rf[NCH], Rn[NCH];
   floatx4 X[NCH], Y[NCH];
-  for (int s = 0; s < nsteps; ++s) {
+  // One pipeline step (chunk s-1 consumed, set P = s % 2 requested); the
+  // loop runs two steps per iteration so that both U register sets have
+  // fixed registers (no copies that would wait for the requests).
+  auto cstep = [&](auto P, int s) {
+    constexpr int PP = decltype(P)::value ^ 1;  // set of the consumed chunk
     ChunkBuf<Cf> &cbf = sm.buf[(s + 1) & 1];  // consumed this step (chunk s-1)
     const int tc = (s - 1) * C;               // first token of the consumed chunk
     const bool live = s >= 1 && s <= nfull;   // a chunk is consumed this step
-    // the same flags are read by every wave: the chunk's path is workgroup-uniform
-    const bool chunk_bad = live && (cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3]) != 0;
-    const bool cbad = consumer && live && chunk_bad;
-    const bool fast = consumer && live && !chunk_bad;
     // ---------------------------------------------------------------- phase A
-    if (fast) {
+    // The operand reads of X and Y and the chunk's flags are issued first
+    // (reading a buffer that holds no chunk is harmless), so that their LDS
+    // latency overlaps the U conversion, the output stores and the U requests;
+    // the scheduling barriers keep that order.
+    Pair<BF16> kf[NCH][NKP], qf[NCH][NKP];
+    static_for<NKP>([&](auto pc) {
+      constexpr int pp = decltype(pc)::value;
+      constexpr bool single = 2 * pp + 1 >= NRT;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        Uf[c] = O::from_acc(floatx4{rw[c][0] * vf(rv[c][0]), rw[c][1] * vf(rv[c][1]),
-                                    rw[c][2] * vf(rv[c][2]), rw[c][3] * vf(rv[c][3])});
+      for (int r = 0; r < NCH; ++r) {
+        kf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, 16 * r + lc, pp, lg);
+        qf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, C + 16 * r + lc, pp, lg);
+      }
+    });
+    const int flags = cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3];
+    __builtin_amdgcn_sched_barrier(0);
+    // raw U of the consumed chunk (requested last step) -> MFMA operands;
+    // the empty asm keeps the conversion (and its wait for the requests)
+    // here instead of letting the compiler sink it into the next phase
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      Uf[c] = O::from_acc(floatx4{rw[PP][c][0] * vf(rv[PP][c][0]), rw[PP][c][1] * vf(rv[PP][c][1]),
+                                  rw[PP][c][2] * vf(rv[PP][c][2]), rw[PP][c][3] * vf(rv[PP][c][3])});
+      pin_regs(Uf[c]);
     }
     flush_o();
     // unconditional (reads nothing past the last chunk): one request order on
     // every path keeps the compiler's waits exact
-    load_u(s < nfull ? s * C : p.T);
+    load_u(P, s < nfull ? s * C : p.T);
+    __builtin_amdgcn_sched_barrier(0);
+    // the same flags are read by every wave: the chunk's path is workgroup-uniform
+    const bool chunk_bad = live && flags != 0;
+    const bool cbad = consumer && live && chunk_bad;
+    const bool fast = consumer && live && !chunk_bad;
     if (cbad) {
       token_steps(tc, tc + C);
     } else if (fast) {
-      // X = (gamma * K) S0, Y = (gamma * Q) S0; all operand reads are issued
-      // before the first product so that their LDS latencies overlap. Y is
-      // formed transposed (operands swapped): lane (lc, lg) holds Y[t = lc]
-      // at columns 4lg..4lg+3, the layout of the output store.
-      Pair<BF16> kf[NCH][NKP], qf[NCH][NKP];
-      static_for<NKP>([&](auto pc) {
-        constexpr int pp = decltype(pc)::value;
-        constexpr bool single = 2 * pp + 1 >= NRT;
-#pragma unroll
-        for (int r = 0; r < NCH; ++r) {
-          kf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, 16 * r + lc, pp, lg);
-          qf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, C + 16 * r + lc, pp, lg);
-        }
-      });
+      // X = (gamma * K) S0, Y = (gamma * Q) S0. Y is formed transposed
+      // (operands swapped): lane (lc, lg) holds Y[t = lc] at columns
+      // 4lg..4lg+3, the layout of the output store.
       Pair<BF16> Sp[NKP];
 #pragma unroll
       for (int pp = 0; pp < NKP; ++pp)
@@ -877,6 +891,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     GDN2_MARK(5);
     __syncthreads();  // buffer (s+1)&1 may now be rebuilt by the producers
     GDN2_MARK(7);
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    cstep(std::integral_constant<int, 0>(), s);
+    cstep(std::integral_constant<int, 1>(), s + 1);
   }
   GDN2_TIMER_STORE
 
