@@ -193,15 +193,15 @@ __device__ __forceinline__ float row_shr(float x, float fill) {
                                                                0x110 + D, 0xf, 0xf, false));
 }
 
-// x from lane S of this lane's group of 4 (DPP quad_perm [S,S,S,S]); same
-// empty-asm guard as row_shr.
+// x from lane S of this lane's group of 4 (DPP quad_perm [S,S,S,S]). One
+// scalar per call, so there is nothing for the compiler to merge (unlike
+// the per-component shifts of row_shr).
 template <int S>
 __device__ __forceinline__ float quad_bcast(float x) {
   static_assert(S >= 0 && S < 4, "quad lane");
-  asm volatile("" : "+v"(x));
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                       __builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                       S | (S << 2) | (S << 4) | (S << 6), 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            S | (S << 2) | (S << 4) | (S << 6),
+                                                            0xf, 0xf, false));
 }
 
 // Empty asm on every 32-bit part of x: the value counts as used and

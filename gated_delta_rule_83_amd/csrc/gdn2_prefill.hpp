@@ -153,6 +153,15 @@ struct PrefillCfg {
   static constexpr int RGL = 64 / QPW;             // lanes per channel quad (>= RGE)
   // lane -> channel quad: with 8 quads per wave, the two quads that share a
   // 16-byte operand unit (q and q + 4) are written by the same 16-lane pass
+  // U = w * v staging: the column waves share the chunk's tokens; a lane
+  // loads 8 adjacent columns of one token
+  static constexpr int ULPT = DVB / 8;                  // lanes per token
+  static constexpr int UTPI = 64 / ULPT;                // tokens per load
+  static constexpr int UTPW = C / NCT;                  // tokens per column wave
+  static constexpr int UNI = (UTPW + UTPI - 1) / UTPI;  // loads per wave and array
+  // row stride (bytes) of the staged U: rows 4 apart in banks for the
+  // transposing reads (4 consecutive rows per 16-lane pass)
+  static constexpr int UROW = DVB * (BF16 ? 2 : 4) + (DVB * (BF16 ? 2 : 4) >= 64 ? 32 : 0);
   static_assert(NCT == 1 || NCT == 2 || NCT == 4, "one to four column waves");
   static_assert(DK % 16 == 0 && C % 16 == 0, "16-aligned tiles");
   static_assert(C % RGE == 0, "build layout");
@@ -184,6 +193,10 @@ struct PrefillSmem {
   // block is stored at position 4 (i % 4) + i / 4 so that the inverse's
   // reads of rows 4qq + j (qq = 0..3) fall on distinct banks
   alignas(16) float akbd[Cf::NCH * 16 * 20];
+  // U = w * v of the chunk being consumed, [token][column of the workgroup]
+  // in the operand type (written in the first phase of a step, read in the
+  // second)
+  alignas(16) char ubuf[Cf::C * Cf::UROW];
 };
 
 template <class Cf>
@@ -343,10 +356,15 @@ __device__ __forceinline__ void invert_diag(const float *akbd, typename Op<Cf::B
     float xi[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) xi[b] = quad_bcast<i / 4>(x[b][i % 4]);
+    // the element the next step broadcasts is updated first: it is the only
+    // one on the dependency chain
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[b][j] -= arow[b][j][i / 4][i % 4] * xi[b];
+      for (int jj = 1; jj <= 4; ++jj) {
+        const int j = (i + jj) & 3;
+        x[b][j] -= arow[b][j][i / 4][i % 4] * xi[b];
+      }
   });
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -528,13 +546,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     if (lane == 0) cbuf.bad[wave] = any_bad ? 1 : 0;
     if (last) *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = inc;
     if (brow) {
+      // 1/gamma on the lane's tokens from one reciprocal per channel: the
+      // lane's last cumulative decay (inc) times the decays after each token
+      const floatx4 ginc = {__builtin_amdgcn_rcpf(inc[0]), __builtin_amdgcn_rcpf(inc[1]),
+                            __builtin_amdgcn_rcpf(inc[2]), __builtin_amdgcn_rcpf(inc[3])};
+      floatx4 gis[RPG];
+      gis[RPG - 1] = ginc;
+#pragma unroll
+      for (int r = RPG - 2; r >= 0; --r) gis[r] = gis[r + 1] * ra[P][r + 1];
       floatx4 kbq[4], bkq[4];
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
         const int tl = rg * RPG + r;
         const floatx4 gm = pre * gl[r];
-        const floatx4 gi = {__builtin_amdgcn_rcpf(gm[0]), __builtin_amdgcn_rcpf(gm[1]),
-                            __builtin_amdgcn_rcpf(gm[2]), __builtin_amdgcn_rcpf(gm[3])};
+        const floatx4 gi = gis[r];
         const floatx4 kv = quad_f(rk[P][r]);
         const floatx4 qv = quad_f(rq[P][r]);
         const floatx4 kb = kv * gi;
@@ -706,32 +731,78 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     __builtin_amdgcn_s_waitcnt(0);
   };
 
-  // U = w * v for this wave's columns as MFMA B fragments: for each 16-token
-  // block c, lane (lc, lg) holds tokens 16c + 4lg + j (j < 4) of column
-  // `col`. Chunk s's raw values are requested during step s and used in
-  // step s+1.
-  using UV = std::conditional_t<BF16, uint16_t, float>;
-  // two register sets: chunk s's raw values in set s % 2
-  UV rv[2][NCH][4];
-  float rw[2][NCH][4];
-  const uint32_t uv_off = (uint32_t)(4 * lg) * v_tb + (uint32_t)col * sizeof(ET);
-  const uint32_t uw_off = (uint32_t)(4 * lg) * w_tb + (uint32_t)col * 4u;
+  // U = w * v. The column waves split the chunk's tokens: lane (ut, uc) of
+  // column wave cw requests token cw * UTPW + i * UTPI + ut, columns
+  // 8 uc .. 8 uc + 7 of the workgroup's block, as 16-byte loads. Chunk s's
+  // raw values are requested during step s (register set s % 2); in step
+  // s+1 their products are staged in LDS ([token][column], operand type)
+  // and each wave reads its own columns back as MFMA fragments.
+  constexpr int UNI = Cf::UNI, UTPI = Cf::UTPI, UTPW = Cf::UTPW, UROW = Cf::UROW;
+  constexpr int NVL = BF16 ? 1 : 2;  // 16-byte loads of v per 8 columns
+  floatx4 rv[2][UNI][NVL], rw[2][UNI][2];
+  const int ut = lane / Cf::ULPT, uc = lane % Cf::ULPT;
+  const int utok = cw * UTPW + ut;  // first token of this lane (i = 0)
+  const uint32_t uv_off = (uint32_t)utok * v_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * sizeof(ET);
+  const uint32_t uw_off = (uint32_t)utok * w_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * 4u;
   auto load_u = [&](auto P, int t0) {
     const rsrc_t rv_ = make_rsrc((const char *)vh + (size_t)t0 * v_tb, rows_left(t0, v_tb));
     const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * w_tb, rows_left(t0, w_tb));
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+    for (int i = 0; i < UNI; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rv[P][c][j] = bload<UV>(rv_, uv_off, (uint32_t)(16 * c + j) * v_tb);
-        rw[P][c][j] = bload<float>(rw_, uw_off, (uint32_t)(16 * c + j) * w_tb);
-      }
+      for (int e = 0; e < NVL; ++e)
+        rv[P][i][e] = bload<floatx4>(rv_, uv_off + 16u * e, (uint32_t)(i * UTPI) * v_tb);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        rw[P][i][e] = bload<floatx4>(rw_, uw_off + 16u * e, (uint32_t)(i * UTPI) * w_tb);
+    }
   };
-  auto vf = [](UV x) -> float {
-    if constexpr (BF16)
-      return bf16_to_f32(x);
-    else
-      return x;
+  // products of register set PP into the staging rows (lanes past the
+  // wave's share of tokens hold duplicates and write nothing)
+  auto stage_u = [&](auto PP) {
+#pragma unroll
+    for (int i = 0; i < UNI; ++i) {
+      if (UTPW % UTPI == 0 || i * UTPI + ut < UTPW) {
+        floatx4 v8[2];
+        if constexpr (BF16) {
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 raw = __builtin_bit_cast(u32x4, rv[PP][i][0]);
+          v8[0] = floatx4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                          __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+          v8[1] = floatx4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
+                          __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
+        } else {
+          v8[0] = rv[PP][i][0];
+          v8[1] = rv[PP][i][NVL - 1];
+        }
+        char *dst = sm.ubuf + (utok + i * UTPI) * UROW + 8 * uc * (int)sizeof(OT);
+        if constexpr (BF16) {
+          const bf16x4 lo = __builtin_convertvector(rw[PP][i][0] * v8[0], bf16x4);
+          const bf16x4 hi = __builtin_convertvector(rw[PP][i][1] * v8[1], bf16x4);
+          *reinterpret_cast<bf16x8 *>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          *reinterpret_cast<floatx4 *>(dst) = rw[PP][i][0] * v8[0];
+          *reinterpret_cast<floatx4 *>(dst + 16) = rw[PP][i][1] * v8[1];
+        }
+      }
+    }
+  };
+  // this wave's U fragment of 16-token block c: lane (lc, lg) gets tokens
+  // 16c + 4lg .. +3 of column lc. bf16: one transposing read per fragment
+  // (within a 16-lane group, lane 4a + b receives element b of the 8-byte
+  // rows addressed by lanes a, a + 4, a + 8, a + 12; lane j addresses token
+  // 16c + 4lg + j / 4, columns 4 (j % 4) .. +3); fp32: four element reads.
+  auto read_u = [&](int c) -> Frag {
+    if constexpr (BF16) {
+      const char *src = sm.ubuf + (16 * c + 4 * lg + (lc >> 2)) * UROW + (cw * 16 + 4 * (lc & 3)) * 2;
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(__attribute__((address_space(3))) const char *)src);
+      return __builtin_bit_cast(Frag, r);
+    } else {
+      const float *src = reinterpret_cast<const float *>(sm.ubuf + (16 * c + 4 * lg) * UROW) + cw * 16 + lc;
+      return Frag{src[0], src[UROW / 4], src[2 * (UROW / 4)], src[3 * (UROW / 4)]};
+    }
   };
 
   // Outputs of the last chunk, held until the next step's loads of U have
@@ -779,19 +850,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     });
     const int flags = cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3];
     __builtin_amdgcn_sched_barrier(0);
-    // raw U of the consumed chunk (requested last step) -> MFMA operands;
-    // the empty asm keeps the conversion (and its wait for the requests)
-    // here instead of letting the compiler sink it into the next phase
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      Uf[c] = O::from_acc(floatx4{rw[PP][c][0] * vf(rv[PP][c][0]), rw[PP][c][1] * vf(rv[PP][c][1]),
-                                  rw[PP][c][2] * vf(rv[PP][c][2]), rw[PP][c][3] * vf(rv[PP][c][3])});
-      pin_regs(Uf[c]);
-    }
+    // U of the consumed chunk (requested last step) into the staging rows
+    if (consumer) stage_u(std::integral_constant<int, PP>());
     flush_o();
     // unconditional (reads nothing past the last chunk): one request order on
     // every path keeps the compiler's waits exact
-    load_u(P, s < nfull ? s * C : p.T);
+    load_u(P, consumer && s < nfull ? s * C : p.T);
     __builtin_amdgcn_sched_barrier(0);
     // the same flags are read by every wave: the chunk's path is workgroup-uniform
     const bool chunk_bad = live && flags != 0;
@@ -824,7 +888,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     GDN2_MARK(7);
     // ---------------------------------------------------------------- phase B
     if (fast) {
-      // All of this phase's LDS operands are read up front: the diagonal
+      // All of this phase's LDS operands are read up front: U, the diagonal
       // inverses and Gram blocks of the solve and the outputs, then the
       // transposed keys and gamma_C of the carry.
       Frag df[NCH];
@@ -832,6 +896,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       floatx4 gc[NRT];
 #pragma unroll
       for (int r = 0; r < NCH; ++r) {
+        Uf[r] = read_u(r);
         df[r] = O::ld(cbf.dinv + r * 16 * LDD + lc * LDD + 4 * lg);
 #pragma unroll
         for (int c = 0; c <= r; ++c) {
