@@ -56,14 +56,28 @@ const char *gdn2_status_string(gdn2_status s) {
     case GDN2_ERR_BAD_DTYPE: return "unknown dtype";
     case GDN2_ERR_WORKSPACE: return "workspace too small";
     case GDN2_ERR_HIP: return "HIP runtime error at launch";
-    case GDN2_ERR_ALIAS: return "output overlaps an input or the state";
+    case GDN2_ERR_ALIAS: return "output or workspace overlaps an input, the state or each other";
   }
   return "unknown status";
 }
 
+namespace {
+
+gdn2::PrefillArgs prefill_args(const gdn2_desc *d) {
+  gdn2::PrefillArgs p{};
+  p.B = d->B; p.T = d->T; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
+  p.chunk = d->chunk;
+  p.bf16 = d->dtype == GDN2_BF16;
+  p.nct = gdn2::prefill_pick_nct(d->B, d->H_v, d->d_v);
+  return p;
+}
+
+}  // namespace
+
 size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc) {
-  (void)desc;
-  return 0;  // the prefill keeps every intermediate on chip
+  if (check_desc(desc, false) != GDN2_OK) return 0;
+  // nonzero only when long sequences are split across workgroups
+  return gdn2::prefill_plan(prefill_args(desc)).ws_bytes;
 }
 
 gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k, const void *v,
@@ -72,8 +86,8 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
                                void *stream) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
-  (void)workspace;
-  if (workspace_bytes < gdn2_chunk_forward_workspace_bytes(d)) return GDN2_ERR_WORKSPACE;
+  const size_t ws_need = gdn2_chunk_forward_workspace_bytes(d);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
   const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
   const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
   const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
@@ -95,15 +109,20 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
   if (tokens)
     for (const Range &r : ins)
       if (overlaps(ro, r)) return GDN2_ERR_ALIAS;
+  if (ws_need > 0) {
+    if (!aligned16(workspace)) return GDN2_ERR_BAD_SHAPE;
+    const Range rws = range_of(workspace, ws_need);
+    for (const Range &r : ins)
+      if (overlaps(rws, r)) return GDN2_ERR_ALIAS;
+    if (overlaps(rws, ro)) return GDN2_ERR_ALIAS;
+  }
   // S_T may alias S0 exactly (in-place), but not partially.
   if (S0 && S_T && overlaps(rs0, rst) && S0 != S_T) return GDN2_ERR_ALIAS;
 
-  gdn2::PrefillArgs p;
-  p.B = d->B; p.T = d->T; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
-  p.chunk = d->chunk;
-  p.bf16 = d->dtype == GDN2_BF16;
-  p.nct = gdn2::prefill_pick_nct(d->B, d->H_v, d->d_v);
+  gdn2::PrefillArgs p = prefill_args(d);
   p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
   const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }

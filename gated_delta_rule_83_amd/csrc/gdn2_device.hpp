@@ -193,15 +193,19 @@ __device__ __forceinline__ float row_shr(float x, float fill) {
                                                                0x110 + D, 0xf, 0xf, false));
 }
 
-// x from lane S of this lane's group of 4 (DPP quad_perm [S,S,S,S]). One
-// scalar per call, so there is nothing for the compiler to merge (unlike
-// the per-component shifts of row_shr).
+// x from lane S of this lane's group of 4 (DPP quad_perm [S,S,S,S]), as one
+// asm statement: independent broadcasts issued together cannot be merged by
+// the optimizer (see row_shr), and the asm costs no copy of x. The leading
+// s_nop covers the wait a DPP read needs after a VALU write of its source,
+// which the compiler does not see through the asm.
 template <int S>
 __device__ __forceinline__ float quad_bcast(float x) {
   static_assert(S >= 0 && S < 4, "quad lane");
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
-                                                            S | (S << 2) | (S << 4) | (S << 6),
-                                                            0xf, 0xf, false));
+  float y;
+  asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 quad_perm:[%2,%2,%2,%2] row_mask:0xf bank_mask:0xf"
+               : "=v"(y)
+               : "v"(x), "i"(S));
+  return y;
 }
 
 // Empty asm on every 32-bit part of x: the value counts as used and

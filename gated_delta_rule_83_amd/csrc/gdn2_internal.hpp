@@ -25,6 +25,17 @@ struct PrefillArgs {
   const float *a, *b, *w, *S0;
   void *o;
   float *S_T;
+  void *workspace;  // split-sequence scratch (see PrefillPlan), may be null
+  size_t workspace_bytes;
+};
+
+// How a prefill call runs: the chunk length used (the largest supported one
+// not above the requested one), and whether sequences are split into nseg
+// segments of seg_len tokens processed in parallel (nseg = 1: unsplit), which
+// needs ws_bytes of workspace.
+struct PrefillPlan {
+  int chunk, nseg, seg_len;
+  size_t ws_bytes;
 };
 
 // Threshold on the chunk's total decay per key channel above which the
@@ -35,6 +46,12 @@ constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream);
+PrefillPlan prefill_plan(const PrefillArgs &p);
+// Split-sequence hand-off: for j = 1 .. nseg - 2 in order,
+// state[j] = trans[j] * state[j - 1] + state[j] per (sequence, head), where
+// state is [nseg][BH][d_k][d_v] and trans [nseg][BH][d_k][d_k], fp32.
+hipError_t launch_split_combine(float *state, const float *trans, int nseg, int BH, int d_k, int d_v,
+                                hipStream_t stream);
 // Workgroup column width the prefill would use (for tests and tuning).
 int prefill_pick_nct(int B, int H_v, int d_v);
 

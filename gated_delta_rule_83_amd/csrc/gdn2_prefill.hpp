@@ -49,6 +49,8 @@
 // tile is already the next product's B operand.
 #pragma once
 
+#include <stdlib.h>
+
 #include <type_traits>
 #include <utility>
 
@@ -231,6 +233,22 @@ struct PrefillParams {
   void *o;
   float *S_T;
   int B, T, H_qk, H_v, d_v;
+  // Split sequences. Segment s of a sequence is tokens [s * seg_len,
+  // min((s + 1) * seg_len, T)) (seg_len a multiple of the chunk, >= T when
+  // unsplit); the launch runs segments seg_first .. seg_first + nseg - 1,
+  // the r-th of them (r = s - seg_first) as its own workgroups. Per head
+  // there are ncb_val value column blocks and ncb_id identity column blocks:
+  // an identity block runs the recurrence on the key-axis identity (entering
+  // state I restricted to its columns, no writes, no outputs), so that its
+  // final state is the segment's transition matrix, stored in M_T.
+  int seg_len, seg_first, nseg, ncb_val, ncb_id;
+  // Per-segment strides (elements) of S0, S_T and M_T. S0 with stride 0 is
+  // the entering state of the launch's first segment only (later segments
+  // start from zero).
+  size_t s0_stride, sT_stride, m_stride;
+  float *M_T;
+  bool o_first_only;   // only the launch's first segment writes outputs
+  bool sT_last_only;   // only the launch's last segment writes S_T
 };
 
 // Lower 16x16 tiles (r, c), c <= r, of the chunk's Gram matrices over the
@@ -416,8 +434,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   __shared__ PrefillSmem<Cf> sm;
   GDN2_TIMER_INIT
 
+  // workgroup -> (segment, sequence, value head, column block)
+  const int ncbt = p.ncb_val + p.ncb_id;
+  const int per_seg = p.B * p.H_v * ncbt;
+  const int rel = blockIdx.x / per_seg;  // segment within the launch
   int n, h, cb;
-  map_block(blockIdx.x, p.B, p.H_qk, p.H_v, p.d_v / Cf::DVB, n, h, cb);
+  map_block(blockIdx.x - rel * per_seg, p.B, p.H_qk, p.H_v, ncbt, n, h, cb);
+  const int tseg = (p.seg_first + rel) * p.seg_len;  // first token of the segment
+  const int Tl = min(p.seg_len, p.T - tseg);        // tokens in the segment
+  const bool ident = cb >= p.ncb_val;                // identity column block
+  // (uniform over the workgroup) nothing to do past the end of the
+  // sequence, nor for the transition of a sequence's first segment, whose
+  // entering state is known
+  if ((p.T > 0 && Tl <= 0) || (ident && p.seg_first + rel == 0)) return;
   const int g = h / (p.H_v / p.H_qk);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -426,14 +455,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const bool producer = wave < Cf::NP;
   const int cw = wave - Cf::NP;                 // consumer index
   const bool consumer = !producer && cw < NCT;  // owns a 16-column state tile
-  const int col = cb * Cf::DVB + (consumer ? cw : 0) * 16 + lc;  // consumer lane's value column
+  // consumer lane's column: a value column, or for an identity block the
+  // key channel whose unit vector the column starts from
+  const int col = (ident ? cb - p.ncb_val : cb) * Cf::DVB + (consumer ? cw : 0) * 16 + lc;
+  const bool write_o = !ident && !(p.o_first_only && rel > 0);
 
   // Token strides in bytes, and this (sequence, head)'s token-0 bases.
   const uint32_t qk_tb = (uint32_t)(p.H_qk * DK) * sizeof(ET);
   const uint32_t ab_tb = (uint32_t)(p.H_v * DK) * 4u;
   const uint32_t v_tb = (uint32_t)(p.H_v * d_v) * sizeof(ET);
   const uint32_t w_tb = (uint32_t)(p.H_v * d_v) * 4u;
-  const size_t tok0 = (size_t)n * p.T;
+  const size_t tok0 = (size_t)n * p.T + tseg;
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v;
@@ -441,10 +473,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const float *bh = p.b + tok0 * p.H_v * DK + (size_t)h * DK;
   const float *wh = p.w + tok0 * p.H_v * d_v + (size_t)h * d_v;
   ET *oh = (ET *)p.o + tok0 * p.H_v * d_v + (size_t)h * d_v;
-  const size_t s_off = ((size_t)n * p.H_v + h) * (size_t)DK * d_v + col;
-  // bytes from token t0 to the end of the sequence (0 past the end: a
+  // entering and final state of this lane's column: value blocks use S0 /
+  // S_T ([B][H_v][d_k][d_v] per segment), identity blocks start from the
+  // unit vector and end in M_T ([B][H_v][d_k][d_k] per segment)
+  const int ld_s = ident ? DK : d_v;
+  const size_t s_off = ((size_t)n * p.H_v + h) * (size_t)DK * ld_s + col;
+  const float *S0p = (ident || !p.S0 || (rel > 0 && p.s0_stride == 0)) ? nullptr : p.S0 + rel * p.s0_stride;
+  float *STp = ident ? p.M_T + rel * p.m_stride
+               : (!p.S_T || (p.sT_last_only && rel != p.nseg - 1)) ? nullptr : p.S_T + rel * p.sT_stride;
+  // bytes from token t0 to the end of the segment (0 past the end: a
   // buffer access beyond the range returns 0 without touching memory)
-  auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return t0 < p.T ? (uint32_t)(p.T - t0) * tb : 0u; };
+  auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return t0 < Tl ? (uint32_t)(Tl - t0) * tb : 0u; };
 
   // ---------------------------------------------------------------- producer layout
   // build: lane = (row group rg, channel quad cq) of producer wave `wave`,
@@ -600,7 +639,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  const int nfull = p.T / C;
+  const int nfull = Tl / C;
   // pipeline steps: chunk s is produced in step s and consumed in step s+1;
   // the count is rounded up to even so that the producers' two-step loop
   // body has no conditional part (the extra step only passes the barriers)
@@ -614,8 +653,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     using I1 = std::integral_constant<int, 1>;
     {  // chunks 0 and 1, unconditional and in the loop's request order
        // (the scheduling barriers keep that order)
-      const RawSrc src0 = raw_src(nfull > 0 ? 0 : p.T);
-      const RawSrc src1 = raw_src(nfull > 1 ? C : p.T);
+      const RawSrc src0 = raw_src(nfull > 0 ? 0 : Tl);
+      const RawSrc src1 = raw_src(nfull > 1 ? C : Tl);
       load_ab(I0(), src0);
       __builtin_amdgcn_sched_barrier(0);
       load_kq(I0(), src0);
@@ -633,7 +672,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     auto pstep = [&](auto P, int s) {
       ChunkBuf<Cf> &pb = sm.buf[P];  // produced this step (chunk s)
       const bool produce = s < nfull;
-      const int tn = s + 2 < nfull ? (s + 2) * C : p.T;
+      const int tn = s + 2 < nfull ? (s + 2) * C : Tl;
       // phase A: operands of chunk s, then request chunk s+2's gates
       if (produce) build(P, pb);
       load_ab(P, raw_src(tn));
@@ -685,7 +724,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      S[rt][j] = (p.S0 && consumer) ? p.S0[s_off + (size_t)(16 * rt + 4 * lg + j) * d_v] : 0.f;
+      S[rt][j] = !consumer ? 0.f
+                 : ident  ? (16 * rt + 4 * lg + j == col ? 1.f : 0.f)
+                 : S0p    ? S0p[s_off + (size_t)(16 * rt + 4 * lg + j) * d_v]
+                          : 0.f;
   // The entering state is complete before the chunk loop: otherwise the
   // compiler, merging loop entry and back edge, waits for every outstanding
   // load (including the next chunk's prefetch) at each first use of S.
@@ -709,7 +751,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);  // key read r for this column
-      const float u = wh[(size_t)t * (w_tb / 4) + col] * E::ld(vh + (size_t)t * (v_tb / sizeof(ET)) + col);
+      const float u = ident ? 0.f : wh[(size_t)t * (w_tb / 4) + col] * E::ld(vh + (size_t)t * (v_tb / sizeof(ET)) + col);
       float po = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
@@ -722,7 +764,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
       po += __shfl_xor(po, 16, 64);
       po += __shfl_xor(po, 32, 64);
-      if (lg == 0) E::st(oh + (size_t)t * (v_tb / sizeof(ET)) + col, po);
+      if (lg == 0 && write_o) E::st(oh + (size_t)t * (v_tb / sizeof(ET)) + col, po);
     }
     // Drain every memory operation of this path here: the fast path reuses
     // these registers, and an operation left in flight across the merge would
@@ -814,7 +856,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   int otc = -1;
   const uint32_t o_off = (uint32_t)lc * v_tb + (uint32_t)(cb * Cf::DVB + cw * 16 + 4 * lg) * sizeof(ET);
   auto flush_o = [&]() {
-    if (otc >= 0) {
+    if (otc >= 0 && write_o) {
       const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)otc * v_tb, rows_left(otc, v_tb));
 #pragma unroll
       for (int r = 0; r < NCH; ++r) bstore(opend[r], ro_, o_off, (uint32_t)(16 * r) * v_tb);
@@ -855,7 +897,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     flush_o();
     // unconditional (reads nothing past the last chunk): one request order on
     // every path keeps the compiler's waits exact
-    load_u(P, consumer && s < nfull ? s * C : p.T);
+    load_u(P, consumer && !ident && s < nfull ? s * C : Tl);
     __builtin_amdgcn_sched_barrier(0);
     // the same flags are read by every wave: the chunk's path is workgroup-uniform
     const bool chunk_bad = live && flags != 0;
@@ -965,12 +1007,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 
   if (consumer) {
     flush_o();
-    if (nfull * C < p.T) token_steps(nfull * C, p.T);
-    if (p.S_T) {
+    if (nfull * C < Tl) token_steps(nfull * C, Tl);
+    if (STp) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p.S_T[s_off + (size_t)(16 * rt + 4 * lg + j) * d_v] = S[rt][j];
+        for (int j = 0; j < 4; ++j) STp[s_off + (size_t)(16 * rt + 4 * lg + j) * ld_s] = S[rt][j];
     }
   }
 }
@@ -992,41 +1034,127 @@ constexpr int fitting_chunk(int requested) {
                                                                  : 16;
 }
 
+// Split plan. Sequences are cut into segments when an unsplit launch would
+// occupy few workgroups (few sequences and heads) and the sequence is long:
+// segments of at least 16 chunks, about two rounds of 256 workgroups in the
+// first pass. GDN2_PREFILL_SPLIT=<n> forces n segments (1: never split).
 template <int DK, int C, int NCT, bool BF16>
-hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st) {
+PrefillPlan plan_t(const PrefillArgs &a) {
+  constexpr int DVB = 16 * NCT;
+  PrefillPlan pl{C, 1, a.T, 0};
+  const int ncb = a.d_v / DVB;
+  const int nfull = a.T / C;
+  if (DK % DVB != 0 || nfull < 2) return pl;
+  long P = 1;
+  if (const char *env = getenv("GDN2_PREFILL_SPLIT")) {
+    P = atol(env);
+  } else if ((long)a.B * a.H_v * ncb < 128) {
+    const long per_seg = (long)a.B * a.H_v * (ncb + DK / DVB);
+    while (P * 2 * per_seg <= 512) P *= 2;
+    P = P < nfull / 16 ? P : nfull / 16;
+  }
+  P = P < nfull ? P : nfull;
+  if (P < 2) return pl;
+  const int seg_chunks = (int)((nfull + P - 1) / P);
+  const int seg_len = seg_chunks * C;
+  const int nseg = (a.T + seg_len - 1) / seg_len;
+  if (nseg < 2) return pl;
+  pl.nseg = nseg;
+  pl.seg_len = seg_len;
+  pl.ws_bytes = (size_t)nseg * a.B * a.H_v * DK * (size_t)(a.d_v + DK) * sizeof(float);
+  return pl;
+}
+
+// Unsplit: one launch over whole sequences. Split (nseg segments):
+//  1. every segment from a zero entering state (the first from S0), value
+//     blocks ending in state[s] and identity blocks in trans[s]: the
+//     segment maps an entering state X to trans[s] X + state[s]; only the
+//     first segment, whose entering state is exact, writes outputs;
+//  2. state[s] = trans[s] state[s - 1] + state[s] in order: the exact state
+//     after each segment;
+//  3. segments 1 .. nseg - 1 again from the exact entering states, writing
+//     their outputs and the last one S_T.
+// The chunk boundaries of every segment are those of the unsplit run.
+template <int DK, int C, int NCT, bool BF16>
+hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
+  const PrefillPlan pl = plan_t<DK, C, NCT, BF16>(a);
+  if (plan_only) {
+    *plan_only = pl;
+    return hipSuccess;
+  }
+  constexpr int DVB = 16 * NCT;
+  const int ncb = a.d_v / DVB;
   PrefillParams p;
-  p.q = a.q; p.k = a.k; p.v = a.v; p.a = a.a; p.b = a.b; p.w = a.w; p.S0 = a.S0;
-  p.o = a.o; p.S_T = a.S_T;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.a = a.a; p.b = a.b; p.w = a.w;
   p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
-  const int blocks = (a.d_v / (16 * NCT)) * a.H_v * a.B;
-  hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(blocks), dim3(512), 0, st, p);
+  p.o = a.o;
+  p.seg_len = pl.seg_len;
+  p.seg_first = 0;
+  p.nseg = pl.nseg;
+  p.ncb_val = ncb;
+  p.ncb_id = 0;
+  p.S0 = a.S0; p.s0_stride = 0;
+  p.S_T = a.S_T; p.sT_stride = 0;
+  p.M_T = nullptr; p.m_stride = 0;
+  p.o_first_only = false;
+  p.sT_last_only = false;
+  const int units = a.B * a.H_v;
+  if (pl.nseg <= 1) {
+    hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(units * ncb), dim3(512), 0, st, p);
+    return hipGetLastError();
+  }
+  if (!a.workspace || a.workspace_bytes < pl.ws_bytes) return hipErrorInvalidValue;
+  const size_t sstate = (size_t)units * DK * a.d_v, strans = (size_t)units * DK * DK;
+  float *state = static_cast<float *>(a.workspace);
+  float *trans = state + (size_t)pl.nseg * sstate;
+  // 1.
+  p.ncb_id = DK / DVB;
+  p.S_T = state; p.sT_stride = sstate;
+  p.M_T = trans; p.m_stride = strans;
+  p.o_first_only = true;
+  hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(pl.nseg * units * (ncb + p.ncb_id)), dim3(512), 0,
+                     st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 2.
+  e = launch_split_combine(state, trans, pl.nseg, units, DK, a.d_v, st);
+  if (e != hipSuccess) return e;
+  // 3.
+  p.seg_first = 1;
+  p.nseg = pl.nseg - 1;
+  p.ncb_id = 0;
+  p.S0 = state; p.s0_stride = sstate;
+  p.S_T = a.S_T; p.sT_stride = 0; p.sT_last_only = true;
+  p.M_T = nullptr; p.m_stride = 0;
+  p.o_first_only = false;
+  hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(p.nseg * units * ncb), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
 template <int DK, int NCT, bool BF16>
-hipError_t dispatch_prefill_chunk(const PrefillArgs &a, hipStream_t st) {
+hipError_t dispatch_prefill_chunk(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   switch (fitting_chunk<DK, NCT, BF16>(a.chunk)) {
     case 64:
       if constexpr (chunk_fits<DK, 64, NCT, BF16>())
-        return launch_prefill_t<DK, 64, NCT, BF16>(a, st);
+        return launch_prefill_t<DK, 64, NCT, BF16>(a, st, plan_only);
       else
         return hipErrorInvalidValue;
     case 32:
       if constexpr (chunk_fits<DK, 32, NCT, BF16>())
-        return launch_prefill_t<DK, 32, NCT, BF16>(a, st);
+        return launch_prefill_t<DK, 32, NCT, BF16>(a, st, plan_only);
       else
         return hipErrorInvalidValue;
     default:
-      return launch_prefill_t<DK, 16, NCT, BF16>(a, st);
+      return launch_prefill_t<DK, 16, NCT, BF16>(a, st, plan_only);
   }
 }
 
 template <int DK, bool BF16>
-hipError_t dispatch_prefill(const PrefillArgs &a, hipStream_t st) {
+hipError_t dispatch_prefill(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   switch (a.nct) {
-    case 1: return dispatch_prefill_chunk<DK, 1, BF16>(a, st);
-    case 2: return dispatch_prefill_chunk<DK, 2, BF16>(a, st);
-    case 4: return dispatch_prefill_chunk<DK, 4, BF16>(a, st);
+    case 1: return dispatch_prefill_chunk<DK, 1, BF16>(a, st, plan_only);
+    case 2: return dispatch_prefill_chunk<DK, 2, BF16>(a, st, plan_only);
+    case 4: return dispatch_prefill_chunk<DK, 4, BF16>(a, st, plan_only);
     default: return hipErrorInvalidValue;
   }
 }

@@ -10,8 +10,8 @@
 
 namespace gdn2 {
 
-hipError_t GDN2_INST_FN(const PrefillArgs &a, hipStream_t st) {
-  return dispatch_prefill<GDN2_INST_DK, GDN2_INST_BF16 != 0>(a, st);
+hipError_t GDN2_INST_FN(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
+  return dispatch_prefill<GDN2_INST_DK, GDN2_INST_BF16 != 0>(a, st, plan_only);
 }
 
 }  // namespace gdn2

@@ -61,7 +61,7 @@ typedef enum {
   GDN2_ERR_BAD_DTYPE = 4,    /* dtype is neither GDN2_F32 nor GDN2_BF16 */
   GDN2_ERR_WORKSPACE = 5,    /* workspace smaller than gdn2_chunk_forward_workspace_bytes() */
   GDN2_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
-  GDN2_ERR_ALIAS = 7         /* o overlaps an input or the state */
+  GDN2_ERR_ALIAS = 7         /* o or the workspace overlaps an input, the state or each other */
 } gdn2_status;
 
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
@@ -76,6 +76,13 @@ typedef struct {
 } gdn2_desc;
 
 /* Bytes of device workspace gdn2_chunk_forward needs for `desc` (0 if none).
+ * Nonzero when the prefill splits long sequences into segments processed in
+ * parallel: that happens when the unsplit call would occupy few workgroups
+ * (few sequences x value heads) and T spans many chunks; the environment
+ * variable GDN2_PREFILL_SPLIT=<n>, read at each call, forces n segments
+ * (1: never split). The split computes the same recurrence: each segment's
+ * entering state is obtained exactly (up to rounding) from the previous
+ * segments' states and transition matrices, then the segment is run from it.
  * Returns 0 for an invalid description as well; the forward call reports
  * the error. */
 size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc);
@@ -90,7 +97,10 @@ size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc);
  *   S_T : may be NULL (not written); may alias S0 exactly (in-place update).
  *   o   : must not overlap any input or S_T (GDN2_ERR_ALIAS).
  *   workspace / workspace_bytes: device scratch of at least
- *         gdn2_chunk_forward_workspace_bytes(desc) bytes (may be NULL if 0).
+ *         gdn2_chunk_forward_workspace_bytes(desc) bytes, 16-byte aligned,
+ *         not overlapping any tensor (may be NULL if that is 0). Smaller:
+ *         GDN2_ERR_WORKSPACE; overlapping: GDN2_ERR_ALIAS. Its contents are
+ *         scratch on entry and exit, owned by the caller.
  * T == 0 is valid: S_T = S0 (or zeros). Any T >= 0 is accepted; a last
  * partial chunk is stepped token by token. */
 gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void *k, const void *v,

@@ -87,6 +87,30 @@ def test_chunk_forward_empty_batch_is_ok_without_gpu():
 def test_workspace_query():
     assert g.gdn2_chunk_forward_workspace_bytes(g.make_desc(8, 4096, 16, 16, 128, 128, 64, 1)) == 0
     assert g.gdn2_chunk_forward_workspace_bytes(None) == 0
+    assert g.gdn2_chunk_forward_workspace_bytes(g.make_desc(1, 64, 2, 2, 96, 16, 16, 0)) == 0
+
+
+def test_split_workspace_query_and_errors(monkeypatch):
+    """Few heads over a long sequence: the prefill splits the sequence and asks
+    for workspace (segments x (d_k x d_v state + d_k x d_k transition) fp32 per
+    head); too little or an overlapping workspace is rejected before any launch."""
+    d2 = g.make_desc(1, 65536, 16, 16, 128, 128, 64, g.GDN2_BF16)
+    per_seg = 16 * 128 * (128 + 128) * 4
+    monkeypatch.delenv("GDN2_PREFILL_SPLIT", raising=False)
+    need = g.gdn2_chunk_forward_workspace_bytes(d2)
+    assert need == 8 * per_seg
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
+    assert g.gdn2_chunk_forward_workspace_bytes(d2) == 0
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "4")
+    assert g.gdn2_chunk_forward_workspace_bytes(d2) == 4 * per_seg
+    monkeypatch.delenv("GDN2_PREFILL_SPLIT")
+    ws = FAKE + 20 * (1 << 30)
+    assert fwd(d2) == g.GDN2_ERR_WORKSPACE
+    assert fwd(d2, ws=ws, ws_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
+    assert fwd(d2, ws=ws + 4, ws_bytes=need) == g.GDN2_ERR_BAD_SHAPE  # misaligned
+    for i in (0, 3, 6, 7, 8):
+        p = _ptrs()
+        assert fwd(d2, p, ws=p[i] + 256, ws_bytes=need) == g.GDN2_ERR_ALIAS, i
 
 
 def test_decode_argument_errors():

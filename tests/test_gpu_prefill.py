@@ -114,6 +114,56 @@ def test_state_in_place_and_split_prefill():
     assert torch.equal(S, S_full)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("nseg", [2, 3, 7])
+def test_split_sequence_matches_oracle(monkeypatch, dtype, nseg):
+    """Sequences cut into nseg segments run in parallel (forced): GQA, random S0,
+    a ragged tail, against the oracle."""
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", str(nseg))
+    rng = np.random.default_rng(90 + nseg)
+    d = rand_inputs(rng, 2, 7 * 64 + 19, 1, 2, 128, 128)
+    run_and_compare(d, dtype, 64, label=f"split{nseg}")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 32), (16, 16), (32, 128), (128, 16)])
+def test_split_sequence_head_sizes(monkeypatch, dk, dv):
+    """Forced split at other head sizes (where the column blocks do not tile
+    d_k the call runs unsplit; the result is the same either way)."""
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "4")
+    rng = np.random.default_rng(100 + dk + dv)
+    d = rand_inputs(rng, 1, 300, 1, 2, dk, dv)
+    run_and_compare(d, "f32", 32, label=f"split4 dk{dk} dv{dv}")
+
+
+def test_split_equals_unsplit_with_strong_decay_and_in_place_state(monkeypatch):
+    """Split and unsplit agree to rounding, also with a token-stepped chunk
+    inside a segment, a null S0 and S_T updated in place; the split is
+    deterministic."""
+    import gated_delta_rule_83_amd as g
+    rng = np.random.default_rng(95)
+    d = rand_inputs(rng, 1, 1000, 1, 2, 128, 128)
+    d["a"][0, 300:310, 1, :] = 1e-5  # a chunk of segment 1 (of 5) decays below e^-60
+    td = gi.to_torch(d, "f32", DEV)
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
+    o1, S1 = gpu_prefill(td, 64)
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "5")
+    o2, S2 = gpu_prefill(td, 64)
+    o3, S3 = gpu_prefill(td, 64)
+    S = td["S0"].clone()
+    o4, _ = g.chunk_forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], S, chunk=64, S_T=S)
+    td0 = dict(td, S0=None)
+    o5, S5 = gpu_prefill(td0, 64)
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
+    o6, S6 = gpu_prefill(td0, 64)
+    torch.cuda.synchronize()
+    assert normwise(to_np(o2), to_np(o1)) < 1e-5 and normwise(to_np(S2), to_np(S1)) < 1e-5
+    assert torch.equal(o2, o3) and torch.equal(S2, S3)
+    assert torch.equal(o4, o2) and torch.equal(S, S2)
+    assert normwise(to_np(o5), to_np(o6)) < 1e-5 and normwise(to_np(S5), to_np(S6)) < 1e-5
+    ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
+    assert normwise(to_np(o2), ref_o) <= TOL["f32"] and normwise(to_np(S2), ref_S) <= TOL["f32"]
+
+
 def test_chunk_length_invariance():
     c = gi.scaled(1, B=1, T=256, H_qk=2, H_v=2)
     d = gi.make_inputs(c)
