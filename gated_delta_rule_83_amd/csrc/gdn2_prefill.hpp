@@ -775,10 +775,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 
   // U = w * v. The column waves split the chunk's tokens: lane (ut, uc) of
   // column wave cw requests token cw * UTPW + i * UTPI + ut, columns
-  // 8 uc .. 8 uc + 7 of the workgroup's block, as 16-byte loads. Chunk s's
-  // raw values are requested during step s (register set s % 2); in step
-  // s+1 their products are staged in LDS ([token][column], operand type)
-  // and each wave reads its own columns back as MFMA fragments.
+  // 8 uc .. 8 uc + 7 of the workgroup's block, as 16-byte loads. Chunk c's
+  // raw values (register set c % 2) are requested two steps before they are
+  // used: in step c - 1 (chunk 0 before the loop); in step c + 1 their
+  // products are staged in LDS ([token][column], operand type) and each wave
+  // reads its own columns back as MFMA fragments.
   constexpr int UNI = Cf::UNI, UTPI = Cf::UTPI, UTPW = Cf::UTPW, UROW = Cf::UROW;
   constexpr int NVL = BF16 ? 1 : 2;  // 16-byte loads of v per 8 columns
   floatx4 rv[2][UNI][NVL], rw[2][UNI][2];
@@ -852,24 +853,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // the store): lane (lc, lg) holds token otc + 16r + lc, columns
   // col0 + 4lg .. +3.
   using OS = std::conditional_t<BF16, uint2, floatx4>;
-  OS opend[NCH];
+  OS opend[NCH] = {};
   int otc = -1;
   const uint32_t o_off = (uint32_t)lc * v_tb + (uint32_t)(cb * Cf::DVB + cw * 16 + 4 * lg) * sizeof(ET);
+  // The stores are issued on every call (with nothing pending, into an empty
+  // range: dropped without a memory access) so that the number of memory
+  // operations between a request and its use is the same on every path,
+  // which keeps the compiler's waits for the U requests exact.
   auto flush_o = [&]() {
-    if (otc >= 0 && write_o) {
-      const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)otc * v_tb, rows_left(otc, v_tb));
+    const bool pend = otc >= 0 && write_o;
+    const int t = pend ? otc : 0;
+    const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)t * v_tb, pend ? rows_left(t, v_tb) : 0u);
 #pragma unroll
-      for (int r = 0; r < NCH; ++r) bstore(opend[r], ro_, o_off, (uint32_t)(16 * r) * v_tb);
-      otc = -1;
-    }
+    for (int r = 0; r < NCH; ++r) bstore(opend[r], ro_, o_off, (uint32_t)(16 * r) * v_tb);
+    otc = -1;
   };
 
   // consumer registers carried across the phases of one step
   Frag Uf[NCH], Rf[NCH], Rn[NCH];
   floatx4 X[NCH], Y[NCH];
-  // One pipeline step (chunk s-1 consumed, set P = s % 2 requested); the
-  // loop runs two steps per iteration so that both U register sets have
-  // fixed registers (no copies that would wait for the requests).
+  // One pipeline step (chunk s-1 consumed from set PP, which then receives
+  // chunk s+1); the loop runs two steps per iteration so that both U
+  // register sets have fixed registers (no copies that would wait for the
+  // requests).
   auto cstep = [&](auto P, int s) {
     constexpr int PP = decltype(P)::value ^ 1;  // set of the consumed chunk
     ChunkBuf<Cf> &cbf = sm.buf[(s + 1) & 1];  // consumed this step (chunk s-1)
@@ -892,12 +898,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     });
     const int flags = cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3];
     __builtin_amdgcn_sched_barrier(0);
-    // U of the consumed chunk (requested last step) into the staging rows
+    // U of the consumed chunk (requested two steps ago) into the staging rows
     if (consumer) stage_u(std::integral_constant<int, PP>());
     flush_o();
     // unconditional (reads nothing past the last chunk): one request order on
     // every path keeps the compiler's waits exact
-    load_u(P, consumer && !ident && s < nfull ? s * C : Tl);
+    load_u(std::integral_constant<int, PP>(), consumer && !ident && s + 1 < nfull ? (s + 1) * C : Tl);
     __builtin_amdgcn_sched_barrier(0);
     // the same flags are read by every wave: the chunk's path is workgroup-uniform
     const bool chunk_bad = live && flags != 0;
@@ -999,6 +1005,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     __syncthreads();  // buffer (s+1)&1 may now be rebuilt by the producers
     GDN2_MARK(7);
   };
+  load_u(std::integral_constant<int, 0>(), consumer && !ident && nfull > 0 ? 0 : Tl);
   for (int s = 0; s < nsteps; s += 2) {
     cstep(std::integral_constant<int, 0>(), s);
     cstep(std::integral_constant<int, 1>(), s + 1);
