@@ -27,24 +27,27 @@
 // blocks are the prefill's chunks.
 //
 // Everything that does not depend on the entering state (scaled operands,
-// the Gram matrices) is computed one chunk ahead by four producer waves,
-// while four consumer waves run the state-dependent part of the previous
-// chunk. A workgroup of 8 waves handles one (sequence, value head, block of
-// 16*NCT value columns, NCT = 1, 2 or 4); consumer wave w < NCT owns the
-// 16-column state tile w and reads U = w*v for its columns straight from
-// memory into MFMA operand registers. Value columns of S evolve
+// the Gram matrices, the diagonal inverses) is computed one chunk ahead by
+// four producer waves, while four consumer waves run the state-dependent
+// part of the previous chunk. A workgroup of 8 waves handles one (sequence,
+// value head, block of 16*NCT value columns, NCT = 1, 2 or 4); consumer wave
+// w < NCT owns the 16-column state tile w. Value columns of S evolve
 // independently, so the column split is exact. Step s of the pipeline
 // (chunk s produced into LDS buffer s%2, chunk s-1 consumed from buffer
 // (s-1)%2), with one workgroup barrier after each phase:
 //   A. producers: decay scan (wave-local, across lanes), scaled operands
 //      K*gamma | Q*gamma, K/gamma | beta/gamma (also transposed); then the
-//      next chunk's decay and erase gates are requested into registers.
-//      consumers: inverses of the 16x16 diagonal blocks of I + Akb (one
-//      block per wave), X = (gamma*K) S0, Y = (gamma*Q) S0.
-//   B. producer wave q: Gram quadrant q (Akk, Akb, Mqk, Mqb), lower tiles;
-//      then the next chunk's keys and queries are requested.
-//      consumers: Z = X + Akk U, the blocked forward solve for R, the
-//      outputs O and the state carry.
+//      decay and erase gates of chunk s+2 are requested into registers.
+//      consumers: U = w*v of chunk s-1 (requested two steps earlier) into an
+//      LDS staging array, the previous chunk's outputs stored, v and w of
+//      chunk s+1 requested, X = (gamma*K) S0, Y = (gamma*Q) S0.
+//   B. producers: the Gram tiles (Akk, Akb, Mqk, Mqb, lower tiles) split
+//      over the waves, the inverses of the 16x16 diagonal blocks of I + Akb;
+//      then the keys and queries of chunk s+2 are requested.
+//      consumers: U fragments from the staging array, Z = X + Akk U, the
+//      blocked forward solve for R, the outputs O and the state carry.
+// A launch may also run segments of the sequences (split sequences): see
+// PrefillParams and launch_prefill_t.
 // Consumer products are chained through MFMA accumulators: an accumulator
 // tile is already the next product's B operand.
 #pragma once
