@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -67,10 +68,16 @@ def decode_algorithmic(c):
 
 
 def source_digest(paths):
+    """sha256 of the kernel sources without comments and blank lines, so that
+    an edit of a comment does not invalidate counters taken on the code."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
