@@ -167,6 +167,16 @@ struct PrefillCfg {
   // row stride (bytes) of the staged U: rows 4 apart in banks for the
   // transposing reads (4 consecutive rows per 16-lane pass)
   static constexpr int UROW = DVB * (BF16 ? 2 : 4) + (DVB * (BF16 ? 2 : 4) >= 64 ? 32 : 0);
+  // output staging: rows of DVB output elements plus 8 bytes, so that the
+  // 16 rows of one 8-byte column slice written together fall on distinct
+  // bank pairs; the stores then write whole rows, 8 bytes per lane
+  static constexpr int OES = BF16 ? 2 : 4;               // output element bytes
+  static constexpr int OROW = DVB * OES + 8;             // row stride (bytes)
+  static constexpr int OLPR = DVB * OES / 8;             // lanes per row in a store
+  static constexpr int ORPI = 64 / OLPR;                 // rows per store instruction
+  static constexpr int ORPW = C / NCT;                   // rows stored by each column wave
+  static constexpr int ONI = ORPW / ORPI;                // store instructions per wave
+  static_assert(ORPW % ORPI == 0, "whole store instructions");
   static_assert(NCT == 1 || NCT == 2 || NCT == 4, "one to four column waves");
   static_assert(DK % 16 == 0 && C % 16 == 0, "16-aligned tiles");
   static_assert(C % RGE == 0, "build layout");
@@ -202,6 +212,10 @@ struct PrefillSmem {
   // in the operand type (written in the first phase of a step, read in the
   // second)
   alignas(16) char ubuf[Cf::C * Cf::UROW];
+  // outputs of the chunk consumed last, [token][column of the workgroup] in
+  // the output type (written in the second phase of a step, stored to memory
+  // in the first phase of the next)
+  alignas(16) char obuf[Cf::C * Cf::OROW];
 };
 
 template <class Cf>
@@ -851,24 +865,31 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  // Outputs of the last chunk, held until the next step's loads of U have
-  // been consumed (a store issued before them would make that wait include
-  // the store): lane (lc, lg) holds token otc + 16r + lc, columns
-  // col0 + 4lg .. +3.
-  using OS = std::conditional_t<BF16, uint2, floatx4>;
-  OS opend[NCH] = {};
-  int otc = -1;
-  const uint32_t o_off = (uint32_t)lc * v_tb + (uint32_t)(cb * Cf::DVB + cw * 16 + 4 * lg) * sizeof(ET);
+  // Outputs. Each column wave writes its 16-column tile of the chunk's
+  // outputs to the staging rows; in the next step the waves store whole rows
+  // (the workgroup's DVB columns of a token, 8 bytes per lane), so every
+  // output line is written by one instruction. Column wave cw stores rows
+  // cw * ORPW + i * ORPI + lane / OLPR, bytes 8 (lane % OLPR) .. +7.
+  constexpr int OROW = Cf::OROW, OLPR = Cf::OLPR, ORPI = Cf::ORPI, ORPW = Cf::ORPW, ONI = Cf::ONI;
+  int otc = -1;  // first token of the staged outputs (-1: none)
+  const int orow0 = (consumer ? cw : 0) * ORPW + lane / OLPR;
+  const uint32_t o_off = (uint32_t)orow0 * v_tb + (uint32_t)(cb * Cf::DVB * Cf::OES + 8 * (lane % OLPR));
+  uint2 ox[ONI];
+  auto read_o = [&]() {
+#pragma unroll
+    for (int i = 0; i < ONI; ++i)
+      ox[i] = *reinterpret_cast<const uint2 *>(sm.obuf + (orow0 + i * ORPI) * OROW + 8 * (lane % OLPR));
+  };
   // The stores are issued on every call (with nothing pending, into an empty
   // range: dropped without a memory access) so that the number of memory
   // operations between a request and its use is the same on every path,
   // which keeps the compiler's waits for the U requests exact.
-  auto flush_o = [&]() {
+  auto store_o = [&]() {
     const bool pend = otc >= 0 && write_o;
     const int t = pend ? otc : 0;
     const rsrc_t ro_ = make_rsrc((const char *)oh + (size_t)t * v_tb, pend ? rows_left(t, v_tb) : 0u);
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) bstore(opend[r], ro_, o_off, (uint32_t)(16 * r) * v_tb);
+    for (int i = 0; i < ONI; ++i) bstore(ox[i], ro_, o_off, (uint32_t)(i * ORPI) * v_tb);
     otc = -1;
   };
 
@@ -889,6 +910,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     // (reading a buffer that holds no chunk is harmless), so that their LDS
     // latency overlaps the U conversion, the output stores and the U requests;
     // the scheduling barriers keep that order.
+    read_o();  // first: its wait then covers only these reads
     Pair<BF16> kf[NCH][NKP], qf[NCH][NKP];
     static_for<NKP>([&](auto pc) {
       constexpr int pp = decltype(pc)::value;
@@ -903,7 +925,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     __builtin_amdgcn_sched_barrier(0);
     // U of the consumed chunk (requested two steps ago) into the staging rows
     if (consumer) stage_u(std::integral_constant<int, PP>());
-    flush_o();
+    store_o();
     // unconditional (reads nothing past the last chunk): one request order on
     // every path keeps the compiler's waits exact
     load_u(std::integral_constant<int, PP>(), consumer && !ident && s + 1 < nfull ? (s + 1) * C : Tl);
@@ -979,17 +1001,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       GDN2_MARK(3);
       // O^T = Y^T + U^T Mqk^T - R^T Mqb^T, one chain over the pairs
       // ([U_c ; -R_c]^T, [Mqk_rc | Mqb_rc]); U and R tiles are already A
-      // operands of the transposed product. The outputs are stored at the
-      // start of the next step.
+      // operands of the transposed product. The outputs go to the staging
+      // rows and are stored to memory in the next step.
       static_for<NCH>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         floatx4 acc = Y[r];
 #pragma unroll
         for (int c = 0; c <= r; ++c) acc = mma<BF16>(acc, Pair<BF16>{Uf[c], Rn[c]}, mf[r][c]);
-        if constexpr (BF16)
-          opend[r] = __builtin_bit_cast(uint2, __builtin_convertvector(acc, bf16x4));
-        else
-          opend[r] = acc;
+        char *dst = sm.obuf + (16 * r + lc) * OROW + (cw * 16 + 4 * lg) * Cf::OES;
+        if constexpr (BF16) {
+          *reinterpret_cast<bf16x4 *>(dst) = __builtin_convertvector(acc, bf16x4);
+        } else {
+          *reinterpret_cast<floatx2 *>(dst) = floatx2{acc[0], acc[1]};
+          *reinterpret_cast<floatx2 *>(dst + 8) = floatx2{acc[2], acc[3]};
+        }
       });
       otc = tc;
       // S_C = diag(gamma_C) (S0 + (K/gamma)^T U - (beta/gamma)^T R): kbiT
@@ -1016,7 +1041,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   GDN2_TIMER_STORE
 
   if (consumer) {
-    flush_o();
+    read_o();
+    store_o();
     if (nfull * C < Tl) token_steps(nfull * C, Tl);
     if (STp) {
 #pragma unroll
