@@ -167,6 +167,11 @@ struct PrefillCfg {
   // row stride (bytes) of the staged U: rows 4 apart in banks for the
   // transposing reads (4 consecutive rows per 16-lane pass)
   static constexpr int UROW = DVB * (BF16 ? 2 : 4) + (DVB * (BF16 ? 2 : 4) >= 64 ? 32 : 0);
+  // keys and queries requested as whole token rows and redistributed through
+  // LDS (bf16, d_k = 128: a row is 256 bytes = two full lines): producer wave
+  // w requests tokens w * C/4 .. +C/4, 16 bytes per lane, four rows per load
+  static constexpr bool KQS = BF16 && DK == 128;
+  static constexpr int KQNI = C / 16;  // loads per lane and array
   // output staging: rows of DVB output elements plus 8 bytes, so that the
   // 16 rows of one 8-byte column slice written together fall on distinct
   // bank pairs; the stores then write whole rows, 8 bytes per lane
@@ -189,7 +194,6 @@ struct ChunkBuf {
   typedef typename Cf::LK LK;
   typedef typename Cf::LT LT;
   alignas(16) char kqg[2 * Cf::C * LK::STRIDE];  // rows 0..C-1: k*gamma; rows C..2C-1: q*gamma
-  alignas(16) char kbi[2 * Cf::C * LK::STRIDE];  // rows 0..C-1: k/gamma; rows C..2C-1: (b*k)/gamma
   alignas(16) char kbiT[Cf::DK * LT::STRIDE];    // kbi transposed: [channel][token (K part | beta part)]
   // ab: row t, 16-column block 2c = Akk block (t, c) (strictly lower inside
   // diagonal blocks), block 2c + 1 = -Akb block (t, c) (off-diagonal only);
@@ -204,6 +208,10 @@ struct ChunkBuf {
 template <class Cf>
 struct PrefillSmem {
   ChunkBuf<Cf> buf[2];
+  // rows 0..C-1: k/gamma; rows C..2C-1: (b*k)/gamma of the chunk being
+  // produced (written by the build, read by the Gram tiles of the same step:
+  // one buffer)
+  alignas(16) char kbi[2 * Cf::C * Cf::LK::STRIDE];
   // Akb diagonal blocks (fp32, 80-byte rows), Gram -> inverses; row i of a
   // block is stored at position 4 (i % 4) + i / 4 so that the inverse's
   // reads of rows 4qq + j (qq = 0..3) fall on distinct banks
@@ -216,6 +224,9 @@ struct PrefillSmem {
   // the output type (written in the second phase of a step, stored to memory
   // in the first phase of the next)
   alignas(16) char obuf[Cf::C * Cf::OROW];
+  // raw keys (rows 0 .. C-1) and queries (rows C .. 2C-1) of the next chunk
+  // to build, 8-byte units XOR-swizzled per row (only with KQS)
+  alignas(16) char kqs[Cf::KQS ? 2 * Cf::C * Cf::DK * 2 : 16];
 };
 
 template <class Cf>
@@ -287,7 +298,7 @@ constexpr bool tile_col_used(unsigned m, int c, int nch) {
   return u;
 }
 template <class Cf, unsigned KK, unsigned KB, unsigned QK, unsigned QB>
-__device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, float *akbd, int lg, int lc) {
+__device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, float *akbd, int lg, int lc) {
   constexpr bool BF16 = Cf::BF16;
   using LK = typename Cf::LK;
   using LT = typename Cf::LT;
@@ -301,8 +312,8 @@ __device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, float *akbd, int lg
       constexpr int i = decltype(ic)::value;
       if constexpr (tile_row_used(KK | KB, i)) tk[pp][i] = frag32<LK, BF16, single>(cb.kqg, 16 * i + lc, pp, lg);
       if constexpr (tile_row_used(QK | QB, i)) tq[pp][i] = frag32<LK, BF16, single>(cb.kqg, C + 16 * i + lc, pp, lg);
-      if constexpr (tile_col_used(KK | QK, i, NCH)) sk[pp][i] = frag32<LK, BF16, single>(cb.kbi, 16 * i + lc, pp, lg);
-      if constexpr (tile_col_used(KB | QB, i, NCH)) sb[pp][i] = frag32<LK, BF16, single>(cb.kbi, C + 16 * i + lc, pp, lg);
+      if constexpr (tile_col_used(KK | QK, i, NCH)) sk[pp][i] = frag32<LK, BF16, single>(kbi, 16 * i + lc, pp, lg);
+      if constexpr (tile_col_used(KB | QB, i, NCH)) sb[pp][i] = frag32<LK, BF16, single>(kbi, C + 16 * i + lc, pp, lg);
     });
   });
   static_for<NCH>([&](auto rc) {
@@ -519,6 +530,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // requests delays the other phase's work.
   floatx4 ra[2][RPG], rb[2][RPG];
   Quad rk[2][RPG], rq[2][RPG];
+  floatx4 rkf[2][2][Cf::KQNI > 0 ? Cf::KQNI : 1];  // KQS: [set][keys, queries][load]
   struct RawSrc {
     rsrc_t a, b, k, q;
   };
@@ -538,13 +550,38 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
   };
   auto load_kq = [&](auto P, const RawSrc &src) {
-    if (brow) {
+    if constexpr (Cf::KQS) {
+#pragma unroll
+      for (int i = 0; i < Cf::KQNI; ++i) {
+        const uint32_t fo = (uint32_t)((C / 4) * wave + 4 * i + (lane >> 4)) * qk_tb + 16u * (uint32_t)(lane & 15);
+        rkf[P][0][i] = bload<floatx4>(src.k, fo, 0);
+        rkf[P][1][i] = bload<floatx4>(src.q, fo, 0);
+      }
+    } else if (brow) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
         rk[P][r] = bload<Quad>(src.k, qk_off, r * qk_tb);
         rq[P][r] = bload<Quad>(src.q, qk_off, r * qk_tb);
       }
     }
+  };
+  // KQS staging: row t of array x at x * C + t, 8-byte unit u of the row at
+  // u ^ kq_sw(t). The swizzle makes the build's reads (16 lanes: 8 rows 4
+  // apart, two units 4 apart) hit distinct banks.
+  auto kq_sw = [](int t) { return ((t >> 2) & 3) ^ (((t >> 3) & 3) << 2); };
+  auto kq_addr = [&](int x, int t, int u) -> char * {
+    return sm.kqs + (x * C + t) * (DK * 2) + 8 * (u ^ kq_sw(t));
+  };
+  auto stage_kq = [&](auto P) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int i = 0; i < Cf::KQNI; ++i) {
+        const int t = (C / 4) * wave + 4 * i + (lane >> 4);
+        const uint4 v = __builtin_bit_cast(uint4, rkf[P][x][i]);
+        *reinterpret_cast<uint2 *>(kq_addr(x, t, 2 * (lane & 15))) = uint2{v.x, v.y};
+        *reinterpret_cast<uint2 *>(kq_addr(x, t, 2 * (lane & 15) + 1)) = uint2{v.z, v.w};
+      }
   };
   auto quad_f = [](Quad x) -> floatx4 {
     if constexpr (BF16)
@@ -562,6 +599,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // inside: the decay scan runs across the lanes of one wave).
   auto build = [&](auto P, ChunkBuf<Cf> &cbuf) {
     // cumulative decay within the lane's RPG tokens
+    Quad kst[RPG], qst[RPG];  // KQS: this lane's keys and queries from the staging rows
+    if constexpr (Cf::KQS) {
+#pragma unroll
+      for (int r = 0; r < RPG; ++r) {
+        kst[r] = *reinterpret_cast<const Quad *>(kq_addr(0, rg * RPG + r, ch0 / 4));
+        qst[r] = *reinterpret_cast<const Quad *>(kq_addr(1, rg * RPG + r, ch0 / 4));
+      }
+    }
     floatx4 gl[RPG];
     floatx4 pr = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
@@ -616,14 +661,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const int tl = rg * RPG + r;
         const floatx4 gm = pre * gl[r];
         const floatx4 gi = gis[r];
-        const floatx4 kv = quad_f(rk[P][r]);
-        const floatx4 qv = quad_f(rq[P][r]);
+        const floatx4 kv = quad_f(Cf::KQS ? kst[r] : rk[P][r]);
+        const floatx4 qv = quad_f(Cf::KQS ? qst[r] : rq[P][r]);
         const floatx4 kb = kv * gi;
         const floatx4 bk = rb[P][r] * kb;
         st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * gm);
         st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * gm);
-        st4<LK, BF16>(cbuf.kbi, tl, ch0, kb);
-        st4<LK, BF16>(cbuf.kbi, C + tl, ch0, bk);
+        st4<LK, BF16>(sm.kbi, tl, ch0, kb);
+        st4<LK, BF16>(sm.kbi, C + tl, ch0, bk);
         // transposed copy: 4 (or 2) consecutive tokens per channel at once
         if constexpr (RPG % 4 == 0) {
           kbq[r & 3] = kb;
@@ -676,10 +721,25 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_barrier(0);
       load_kq(I0(), src0);
       __builtin_amdgcn_sched_barrier(0);
-      load_ab(I1(), src1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_kq(I1(), src1);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (Cf::KQS) {  // the loop requests keys and queries one chunk earlier
+        load_kq(I1(), src1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_ab(I1(), src1);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        load_ab(I1(), src1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_kq(I1(), src1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (Cf::KQS) {
+        // chunk 0's keys and queries into the staging rows, chunk 2's
+        // requested into the freed set; the barrier publishes the rows (the
+        // other waves execute a matching one before their loop)
+        stage_kq(I0());
+        load_kq(I0(), raw_src(nfull > 2 ? 2 * C : Tl));
+        __syncthreads();
+      }
     }
     // One pipeline step; chunk s uses raw register set P = s % 2. The
     // requests for chunk s+2 are issued unconditionally (past the last
@@ -710,18 +770,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         };
         switch (wave) {
           case 0:
-            gram_tiles<Cf, GS::KK0, GS::KB0, 0u, 0u>(pb, sm.akbd, lg, lc);
+            gram_tiles<Cf, GS::KK0, GS::KB0, 0u, 0u>(pb, sm.kbi, sm.akbd, lg, lc);
             invert_set(std::integral_constant<unsigned, GS::INV0>());
             break;
           case 1:
-            gram_tiles<Cf, GS::KK1, GS::KB1, 0u, 0u>(pb, sm.akbd, lg, lc);
+            gram_tiles<Cf, GS::KK1, GS::KB1, 0u, 0u>(pb, sm.kbi, sm.akbd, lg, lc);
             invert_set(std::integral_constant<unsigned, GS::INV1>());
             break;
-          case 2: gram_tiles<Cf, 0u, 0u, GS::FULL, 0u>(pb, sm.akbd, lg, lc); break;
-          default: gram_tiles<Cf, 0u, 0u, 0u, GS::FULL>(pb, sm.akbd, lg, lc); break;
+          case 2: gram_tiles<Cf, 0u, 0u, GS::FULL, 0u>(pb, sm.kbi, sm.akbd, lg, lc); break;
+          default: gram_tiles<Cf, 0u, 0u, 0u, GS::FULL>(pb, sm.kbi, sm.akbd, lg, lc); break;
         }
       }
-      load_kq(P, raw_src(tn));
+      if constexpr (Cf::KQS) {
+        // keys and queries of chunk s+1 (requested three steps ago) into the
+        // staging rows for the next build, chunk s+3's requested into the
+        // freed set
+        constexpr int PN = decltype(P)::value ^ 1;
+        stage_kq(std::integral_constant<int, PN>());
+        load_kq(std::integral_constant<int, PN>(), raw_src(s + 3 < nfull ? (s + 3) * C : Tl));
+      } else {
+        load_kq(P, raw_src(tn));
+      }
       GDN2_MARK(2);
       __syncthreads();  // buffer P is now complete for the consumers
       GDN2_MARK(7);
@@ -1034,6 +1103,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     GDN2_MARK(7);
   };
   load_u(std::integral_constant<int, 0>(), consumer && !ident && nfull > 0 ? 0 : Tl);
+  if constexpr (Cf::KQS) __syncthreads();  // matches the producers' staging barrier
   for (int s = 0; s < nsteps; s += 2) {
     cstep(std::integral_constant<int, 0>(), s);
     cstep(std::integral_constant<int, 1>(), s + 1);
