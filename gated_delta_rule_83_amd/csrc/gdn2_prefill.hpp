@@ -167,11 +167,10 @@ struct PrefillCfg {
   // row stride (bytes) of the staged U: rows 4 apart in banks for the
   // transposing reads (4 consecutive rows per 16-lane pass)
   static constexpr int UROW = DVB * (BF16 ? 2 : 4) + (DVB * (BF16 ? 2 : 4) >= 64 ? 32 : 0);
-  // keys and queries requested as whole token rows and redistributed through
-  // LDS (bf16, d_k = 128: a row is 256 bytes = two full lines): producer wave
-  // w requests tokens w * C/4 .. +C/4, 16 bytes per lane, four rows per load
-  static constexpr bool KQS = BF16 && DK == 128;
-  static constexpr int KQNI = C / 16;  // loads per lane and array
+  // token-major build (d_k = 128): producer wave w builds tokens
+  // w*C/4 .. +C/4 for all key channels, so that every raw request covers
+  // whole token rows (see the kernel's producer layout)
+  static constexpr bool TOKM = DK == 128;
   // output staging: rows of DVB output elements plus 8 bytes, so that the
   // 16 rows of one 8-byte column slice written together fall on distinct
   // bank pairs; the stores then write whole rows, 8 bytes per lane
@@ -224,9 +223,9 @@ struct PrefillSmem {
   // the output type (written in the second phase of a step, stored to memory
   // in the first phase of the next)
   alignas(16) char obuf[Cf::C * Cf::OROW];
-  // raw keys (rows 0 .. C-1) and queries (rows C .. 2C-1) of the next chunk
-  // to build, 8-byte units XOR-swizzled per row (only with KQS)
-  alignas(16) char kqs[Cf::KQS ? 2 * Cf::C * Cf::DK * 2 : 16];
+  // token-major build: per producer wave, the product of the decays of its
+  // tokens per key channel, for the next chunk to build
+  alignas(16) float tot[Cf::NP][Cf::TOKM ? Cf::DK : 4];
 };
 
 template <class Cf>
@@ -514,14 +513,25 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return t0 < Tl ? (uint32_t)(Tl - t0) * tb : 0u; };
 
   // ---------------------------------------------------------------- producer layout
-  // build: lane = (row group rg, channel quad cq) of producer wave `wave`,
-  // row group fastest so that a quad's prefix product runs across adjacent lanes
-  const int rg = lane % Cf::RGL;
-  const int cq = Cf::QPW == 8 ? (((lane / Cf::RGL) >> 1) | (((lane / Cf::RGL) & 1) << 2)) : lane / Cf::RGL;
-  const bool brow = (RGE == Cf::RGL) || rg < RGE;  // lane holds build rows
-  const int ch0 = wave * (DK / 4) + 4 * cq;
-  const uint32_t ab_off = (uint32_t)(rg * RPG) * ab_tb + (uint32_t)ch0 * 4u;
-  const uint32_t qk_off = (uint32_t)(rg * RPG) * qk_tb + (uint32_t)ch0 * sizeof(ET);
+  // Token-major (d_k = 128): producer wave w builds tokens w*C/4 .. +C/4 of
+  // the chunk for all key channels; lane = (half rg, channel quad cq) holds
+  // tokens w*C/4 + rg*RPG + r (r < RPG) of channels 4cq .. 4cq+3, so every
+  // raw request covers two whole token rows. The decay's cumulative product
+  // runs within the lane, across the halves by a lane exchange, and across
+  // the waves through per-wave totals in LDS computed one step ahead.
+  // Channel-major (d_k < 128): lane = (row group rg, channel quad cq) of the
+  // wave's d_k/4 channels, row group fastest so that a quad's prefix product
+  // runs across adjacent lanes.
+  constexpr bool TOKM = Cf::TOKM;
+  const int rg = TOKM ? lane >> 5 : lane % Cf::RGL;
+  const int cq = TOKM ? lane & 31
+                      : Cf::QPW == 8 ? (((lane / Cf::RGL) >> 1) | (((lane / Cf::RGL) & 1) << 2)) : lane / Cf::RGL;
+  const bool brow = TOKM || (RGE == Cf::RGL) || rg < RGE;  // lane holds build rows
+  const int ch0 = TOKM ? 4 * cq : wave * (DK / 4) + 4 * cq;
+  const int tb0 = TOKM ? wave * (C / 4) + rg * RPG : rg * RPG;  // the lane's first token
+  static_assert(!TOKM || RPG * 8 == C, "token-major: C/8 tokens per lane");
+  const uint32_t ab_off = (uint32_t)tb0 * ab_tb + (uint32_t)ch0 * 4u;
+  const uint32_t qk_off = (uint32_t)tb0 * qk_tb + (uint32_t)ch0 * sizeof(ET);
 
   // Raw inputs of the chunks to build, held in two register sets (chunk s
   // in set s % 2) and requested two chunks ahead so that a request has more
@@ -530,7 +540,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // requests delays the other phase's work.
   floatx4 ra[2][RPG], rb[2][RPG];
   Quad rk[2][RPG], rq[2][RPG];
-  floatx4 rkf[2][2][Cf::KQNI > 0 ? Cf::KQNI : 1];  // KQS: [set][keys, queries][load]
   struct RawSrc {
     rsrc_t a, b, k, q;
   };
@@ -550,38 +559,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
   };
   auto load_kq = [&](auto P, const RawSrc &src) {
-    if constexpr (Cf::KQS) {
-#pragma unroll
-      for (int i = 0; i < Cf::KQNI; ++i) {
-        const uint32_t fo = (uint32_t)((C / 4) * wave + 4 * i + (lane >> 4)) * qk_tb + 16u * (uint32_t)(lane & 15);
-        rkf[P][0][i] = bload<floatx4>(src.k, fo, 0);
-        rkf[P][1][i] = bload<floatx4>(src.q, fo, 0);
-      }
-    } else if (brow) {
+    if (brow) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
         rk[P][r] = bload<Quad>(src.k, qk_off, r * qk_tb);
         rq[P][r] = bload<Quad>(src.q, qk_off, r * qk_tb);
       }
     }
-  };
-  // KQS staging: row t of array x at x * C + t, 8-byte unit u of the row at
-  // u ^ kq_sw(t). The swizzle makes the build's reads (16 lanes: 8 rows 4
-  // apart, two units 4 apart) hit distinct banks.
-  auto kq_sw = [](int t) { return ((t >> 2) & 3) ^ (((t >> 3) & 3) << 2); };
-  auto kq_addr = [&](int x, int t, int u) -> char * {
-    return sm.kqs + (x * C + t) * (DK * 2) + 8 * (u ^ kq_sw(t));
-  };
-  auto stage_kq = [&](auto P) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int i = 0; i < Cf::KQNI; ++i) {
-        const int t = (C / 4) * wave + 4 * i + (lane >> 4);
-        const uint4 v = __builtin_bit_cast(uint4, rkf[P][x][i]);
-        *reinterpret_cast<uint2 *>(kq_addr(x, t, 2 * (lane & 15))) = uint2{v.x, v.y};
-        *reinterpret_cast<uint2 *>(kq_addr(x, t, 2 * (lane & 15) + 1)) = uint2{v.z, v.w};
-      }
   };
   auto quad_f = [](Quad x) -> floatx4 {
     if constexpr (BF16)
@@ -595,18 +579,22 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                    __shfl(x[3], src, 64)};
   };
 
+  // Token-major: this wave's total decay per channel for the chunk in raw
+  // set P, for the next build (published by the barrier before it).
+  auto wave_totals = [&](auto P) {
+    if constexpr (TOKM) {
+      floatx4 pr = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int r = 0; r < RPG; ++r) pr *= ra[P][r];
+      const floatx4 lo = shfl4(pr, lane ^ 32);
+      if (rg == 0) *reinterpret_cast<floatx4 *>(&sm.tot[wave][ch0]) = pr * lo;
+    }
+  };
+
   // Build chunk operands into buffer cbuf (producer waves; no workgroup sync
   // inside: the decay scan runs across the lanes of one wave).
   auto build = [&](auto P, ChunkBuf<Cf> &cbuf) {
     // cumulative decay within the lane's RPG tokens
-    Quad kst[RPG], qst[RPG];  // KQS: this lane's keys and queries from the staging rows
-    if constexpr (Cf::KQS) {
-#pragma unroll
-      for (int r = 0; r < RPG; ++r) {
-        kst[r] = *reinterpret_cast<const Quad *>(kq_addr(0, rg * RPG + r, ch0 / 4));
-        qst[r] = *reinterpret_cast<const Quad *>(kq_addr(1, rg * RPG + r, ch0 / 4));
-      }
-    }
     floatx4 gl[RPG];
     floatx4 pr = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
@@ -615,10 +603,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       gl[r] = pr;
     }
 
-    // inclusive prefix product over the row groups (adjacent lanes): DPP row
-    // shifts when a quad's groups fit in one 16-lane row, lane shuffles else
     floatx4 inc = pr, pre;
-    if constexpr (RGE <= 16) {
+    if constexpr (TOKM) {
+      // earlier waves' totals (LDS, one step ahead), then the lower half's
+      // product for the upper half (lane exchange across the halves)
+      floatx4 pw = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int w2 = 0; w2 < Cf::NP - 1; ++w2)
+        if (w2 < wave) pw *= *reinterpret_cast<const floatx4 *>(&sm.tot[w2][ch0]);
+      const floatx4 lo = shfl4(pr, lane ^ 32);
+      pre = rg ? pw * lo : pw;
+      inc = pre * pr;
+    } else if constexpr (RGE <= 16) {
+      // inclusive prefix product over the row groups (adjacent lanes): DPP
+      // row shifts when a quad's groups fit in one 16-lane row
+
       static_for<4>([&](auto li) {
         constexpr int d = 1 << decltype(li)::value;
         if constexpr (d < RGE) {
@@ -638,9 +637,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
       pre = shfl4(inc, lane - 1);
     }
-    if (rg == 0) pre = floatx4{1.f, 1.f, 1.f, 1.f};
-    // the last row group holds gamma_C of the lane's 4 channels
-    const bool last = rg == RGE - 1;
+    if (!TOKM && rg == 0) pre = floatx4{1.f, 1.f, 1.f, 1.f};
+    // the lanes holding the chunk's last token hold gamma_C of their 4 channels
+    const bool last = TOKM ? (wave == Cf::NP - 1 && rg == 1) : rg == RGE - 1;
     const bool lane_bad = last && (!(inc[0] >= kMinChunkDecay) || !(inc[1] >= kMinChunkDecay) ||
                                    !(inc[2] >= kMinChunkDecay) || !(inc[3] >= kMinChunkDecay));
     const bool any_bad = __any(lane_bad);
@@ -658,11 +657,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       floatx4 kbq[4], bkq[4];
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
-        const int tl = rg * RPG + r;
+        const int tl = tb0 + r;
         const floatx4 gm = pre * gl[r];
         const floatx4 gi = gis[r];
-        const floatx4 kv = quad_f(Cf::KQS ? kst[r] : rk[P][r]);
-        const floatx4 qv = quad_f(Cf::KQS ? qst[r] : rq[P][r]);
+        const floatx4 kv = quad_f(rk[P][r]);
+        const floatx4 qv = quad_f(rq[P][r]);
         const floatx4 kb = kv * gi;
         const floatx4 bk = rb[P][r] * kb;
         st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * gm);
@@ -721,23 +720,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_barrier(0);
       load_kq(I0(), src0);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (Cf::KQS) {  // the loop requests keys and queries one chunk earlier
-        load_kq(I1(), src1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_ab(I1(), src1);
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        load_ab(I1(), src1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_kq(I1(), src1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (Cf::KQS) {
-        // chunk 0's keys and queries into the staging rows, chunk 2's
-        // requested into the freed set; the barrier publishes the rows (the
-        // other waves execute a matching one before their loop)
-        stage_kq(I0());
-        load_kq(I0(), raw_src(nfull > 2 ? 2 * C : Tl));
+      load_ab(I1(), src1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_kq(I1(), src1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (TOKM) {
+        // chunk 0's wave totals; the barrier publishes them (the other waves
+        // execute a matching one before their loop)
+        wave_totals(I0());
         __syncthreads();
       }
     }
@@ -781,16 +771,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           default: gram_tiles<Cf, 0u, 0u, 0u, GS::FULL>(pb, sm.kbi, sm.akbd, lg, lc); break;
         }
       }
-      if constexpr (Cf::KQS) {
-        // keys and queries of chunk s+1 (requested three steps ago) into the
-        // staging rows for the next build, chunk s+3's requested into the
-        // freed set
-        constexpr int PN = decltype(P)::value ^ 1;
-        stage_kq(std::integral_constant<int, PN>());
-        load_kq(std::integral_constant<int, PN>(), raw_src(s + 3 < nfull ? (s + 3) * C : Tl));
-      } else {
-        load_kq(P, raw_src(tn));
-      }
+      wave_totals(std::integral_constant<int, decltype(P)::value ^ 1>());  // chunk s+1
+      load_kq(P, raw_src(tn));
       GDN2_MARK(2);
       __syncthreads();  // buffer P is now complete for the consumers
       GDN2_MARK(7);
@@ -1103,7 +1085,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     GDN2_MARK(7);
   };
   load_u(std::integral_constant<int, 0>(), consumer && !ident && nfull > 0 ? 0 : Tl);
-  if constexpr (Cf::KQS) __syncthreads();  // matches the producers' staging barrier
+  if constexpr (Cf::TOKM) __syncthreads();  // matches the producers' barrier before their loop
   for (int s = 0; s < nsteps; s += 2) {
     cstep(std::integral_constant<int, 0>(), s);
     cstep(std::integral_constant<int, 1>(), s + 1);
