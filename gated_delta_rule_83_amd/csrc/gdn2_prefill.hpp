@@ -357,19 +357,22 @@ __device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, fl
 }
 
 // Work split of the Gram tiles and diagonal inverses over the 4 producer
-// waves: waves 2 and 3 take Mqk and Mqb; waves 0 and 1 share Akk and Akb so
-// that the wave which computes the diagonal Akb tile of row block r also
-// inverts it, with about equal work on both.
+// waves (masks of lower tiles per wave; INV: diagonal blocks the wave
+// inverts, always blocks whose Akb tile the same wave computes, so no
+// synchronisation is needed). The inverses are the longest serial part, so
+// with two row blocks the waves that invert compute only the diagonal Akb
+// tile they need and the other two waves take the remaining ten tiles. With
+// one block waves 0 and 1 take Akk and Akb, 2 and 3 Mqk and Mqb; with more
+// blocks wave 0 takes all of Akk, wave 1 all of Akb and the inverses.
 template <int NCH>
 struct GramSplit {
   static constexpr unsigned FULL = (1u << (NCH * (NCH + 1) / 2)) - 1u;
-  // NCH = 1: one tile per quadrant; NCH = 2: tiles 0 = (0,0), 1 = (1,0), 2 = (1,1)
-  static constexpr unsigned KK0 = NCH == 1 ? 1u : NCH == 2 ? 3u : FULL;
-  static constexpr unsigned KB0 = NCH == 1 ? 0u : NCH == 2 ? 1u : 0u;
-  static constexpr unsigned INV0 = NCH == 1 ? 0u : NCH == 2 ? 1u : 0u;  // diagonal blocks wave 0 inverts
-  static constexpr unsigned KK1 = FULL & ~KK0;
-  static constexpr unsigned KB1 = FULL & ~KB0;
-  static constexpr unsigned INV1 = ((1u << NCH) - 1u) & ~INV0;
+  static constexpr bool TWO = NCH == 2;  // tiles 0 = (0,0), 1 = (1,0), 2 = (1,1)
+  static constexpr unsigned KK[4] = {TWO ? 0u : NCH == 1 ? 1u : FULL, 0u, TWO ? 3u : 0u, TWO ? 4u : 0u};
+  static constexpr unsigned KB[4] = {TWO ? 1u : 0u, TWO ? 4u : NCH == 1 ? 1u : FULL, TWO ? 2u : 0u, 0u};
+  static constexpr unsigned QK[4] = {0u, 0u, TWO ? 3u : FULL, TWO ? 4u : 0u};
+  static constexpr unsigned QB[4] = {0u, 0u, 0u, FULL};
+  static constexpr unsigned INV[4] = {TWO ? 1u : 0u, TWO ? 2u : (1u << NCH) - 1u, 0u, 0u};
 };
 
 // Inverses of the diagonal blocks r0 .. r0+NB-1 of I + Akb (strictly lower
@@ -750,25 +753,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       // and queries
       if (produce) {
         using GS = GramSplit<NCH>;
-        // each of waves 0 and 1 inverts the diagonal blocks whose Akb tile it
-        // has just written (same wave: no synchronisation needed)
+        // the diagonal blocks whose Akb tile this wave has just written
         auto invert_set = [&](auto mask) {
           static_for<NCH>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
             if constexpr (((decltype(mask)::value >> r) & 1u) != 0) invert_diag<Cf, 1>(sm.akbd, pb.dinv, r, lane);
           });
         };
+        auto gram_wave = [&](auto wc) {
+          constexpr int w = decltype(wc)::value;
+          gram_tiles<Cf, GS::KK[w], GS::KB[w], GS::QK[w], GS::QB[w]>(pb, sm.kbi, sm.akbd, lg, lc);
+          invert_set(std::integral_constant<unsigned, GS::INV[w]>());
+        };
         switch (wave) {
-          case 0:
-            gram_tiles<Cf, GS::KK0, GS::KB0, 0u, 0u>(pb, sm.kbi, sm.akbd, lg, lc);
-            invert_set(std::integral_constant<unsigned, GS::INV0>());
-            break;
-          case 1:
-            gram_tiles<Cf, GS::KK1, GS::KB1, 0u, 0u>(pb, sm.kbi, sm.akbd, lg, lc);
-            invert_set(std::integral_constant<unsigned, GS::INV1>());
-            break;
-          case 2: gram_tiles<Cf, 0u, 0u, GS::FULL, 0u>(pb, sm.kbi, sm.akbd, lg, lc); break;
-          default: gram_tiles<Cf, 0u, 0u, 0u, GS::FULL>(pb, sm.kbi, sm.akbd, lg, lc); break;
+          case 0: gram_wave(std::integral_constant<int, 0>()); break;
+          case 1: gram_wave(std::integral_constant<int, 1>()); break;
+          case 2: gram_wave(std::integral_constant<int, 2>()); break;
+          default: gram_wave(std::integral_constant<int, 3>()); break;
         }
       }
       wave_totals(std::integral_constant<int, decltype(P)::value ^ 1>());  // chunk s+1
