@@ -5,10 +5,11 @@ the computation runs in the HIP kernels of ``libgdn2.so``; this module only
 marshals arguments. PyTorch supplies device memory and the stream.
 
 Raw entry points (same names and arguments as the C ABI; pointers are ints):
-    gdn2_chunk_forward, gdn2_decode_step, gdn2_chunk_forward_workspace_bytes,
-    gdn2_status_string, gdn2_version
+    gdn2_chunk_forward, gdn2_chunk_forward_varlen, gdn2_decode_step,
+    gdn2_chunk_forward_workspace_bytes, gdn2_status_string, gdn2_version
 Torch conveniences:
     chunk_forward(q, k, v, a, b, w, S0=None, chunk=64) -> (o, S_T)
+    chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk=64) -> (o, S_T)
     decode_step(q, k, v, a, b, w, S) -> o        (S updated in place)
 
 If ``libgdn2.so`` has not been built, loading fails loudly: there is no
@@ -35,8 +36,8 @@ GDN2_ERR_ALIAS = 7
 GDN2_F32 = 0
 GDN2_BF16 = 1
 
-EXPORTED = ("gdn2_chunk_forward", "gdn2_decode_step", "gdn2_chunk_forward_workspace_bytes",
-            "gdn2_status_string", "gdn2_version")
+EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_varlen", "gdn2_decode_step",
+            "gdn2_chunk_forward_workspace_bytes", "gdn2_status_string", "gdn2_version")
 
 
 class gdn2_desc(ctypes.Structure):
@@ -66,6 +67,8 @@ def load(path: Optional[str] = None):
     vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(gdn2_desc)
     lib.gdn2_chunk_forward.restype = ctypes.c_int
     lib.gdn2_chunk_forward.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
+    lib.gdn2_chunk_forward_varlen.restype = ctypes.c_int
+    lib.gdn2_chunk_forward_varlen.argtypes = [dp] + [vp] * 10 + [vp]
     lib.gdn2_decode_step.restype = ctypes.c_int
     lib.gdn2_decode_step.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn2_chunk_forward_workspace_bytes.restype = sz
@@ -100,6 +103,11 @@ def gdn2_chunk_forward(desc, q, k, v, a, b, w, S0, o, S_T, workspace=0, workspac
                        stream=0) -> int:
     return load().gdn2_chunk_forward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w,
                                      S0, o, S_T, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_forward_varlen(desc, cu_seqlens, q, k, v, a, b, w, S0, o, S_T, stream=0) -> int:
+    return load().gdn2_chunk_forward_varlen(None if desc is None else ctypes.byref(desc), cu_seqlens, q, k,
+                                            v, a, b, w, S0, o, S_T, stream)
 
 
 def gdn2_decode_step(desc, q, k, v, a, b, w, S, o, stream=0) -> int:
@@ -162,6 +170,35 @@ def chunk_forward(q, k, v, a, b, w, S0=None, chunk: int = 64, o=None, S_T=None,
     work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
     st = gdn2_chunk_forward(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0),
                             _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st)
+    return o, S_T
+
+
+def chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64, o=None, S_T=None,
+                         want_state: bool = True, stream=None):
+    """Prefill of packed sequences of different lengths. q, k [T,H_qk,d_k] (or
+    [1,T,H_qk,d_k]); v [T,H_v,d_v]; a, b [T,H_v,d_k] fp32; w [T,H_v,d_v] fp32;
+    cu_seqlens int32 [N+1] on the device (sequence n = tokens cu[n]..cu[n+1]-1);
+    S0 [N,H_v,d_k,d_v] fp32 or None. Returns (o shaped like v, S_T [N,H_v,d_k,d_v])."""
+    import torch
+    T, H_qk, d_k = q.shape[-3:]
+    H_v, d_v = v.shape[-2], v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, q.dtype)
+    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0")):
+        _check(t, nm, torch.float32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    _check(o, "o", q.dtype)
+    _check(S_T, "S_T", torch.float32)
+    desc = make_desc(N, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
+    st = gdn2_chunk_forward_varlen(desc, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                   _ptr(w), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return o, S_T

@@ -27,6 +27,9 @@ struct PrefillArgs {
   float *S_T;
   void *workspace;  // split-sequence scratch (see PrefillPlan), may be null
   size_t workspace_bytes;
+  // packed sequences of different lengths: B + 1 token offsets (device), or
+  // null for B sequences of T tokens each
+  const int32_t *cu_seqlens;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one

@@ -276,6 +276,9 @@ struct PrefillParams {
   float *M_T;
   bool o_first_only;   // only the launch's first segment writes outputs
   bool sT_last_only;   // only the launch's last segment writes S_T
+  // packed sequences: sequence n is tokens cu[n] .. cu[n+1]-1 of T (one
+  // segment each); null: sequence n is tokens n*T .. n*T + T-1
+  const int32_t *cu;
 };
 
 // Lower 16x16 tiles (r, c), c <= r, of the chunk's Gram matrices over the
@@ -470,13 +473,22 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const int rel = blockIdx.x / per_seg;  // segment within the launch
   int n, h, cb;
   map_block(blockIdx.x - rel * per_seg, p.B, p.H_qk, p.H_v, ncbt, n, h, cb);
-  const int tseg = (p.seg_first + rel) * p.seg_len;  // first token of the segment
-  const int Tl = min(p.seg_len, p.T - tseg);        // tokens in the segment
-  const bool ident = cb >= p.ncb_val;                // identity column block
+  size_t tok0;  // first token of the segment in the token axis of the inputs
+  int Tl;       // tokens in the segment
+  if (p.cu) {
+    const int t0 = min(max(p.cu[n], 0), p.T), t1 = min(max(p.cu[n + 1], t0), p.T);
+    tok0 = (size_t)t0;
+    Tl = t1 - t0;
+  } else {
+    const int tseg = (p.seg_first + rel) * p.seg_len;  // first token of the segment
+    tok0 = (size_t)n * p.T + tseg;
+    Tl = min(p.seg_len, p.T - tseg);
+  }
+  const bool ident = cb >= p.ncb_val;  // identity column block
   // (uniform over the workgroup) nothing to do past the end of the
   // sequence, nor for the transition of a sequence's first segment, whose
   // entering state is known
-  if ((p.T > 0 && Tl <= 0) || (ident && p.seg_first + rel == 0)) return;
+  if ((!p.cu && p.T > 0 && Tl <= 0) || (ident && p.seg_first + rel == 0)) return;
   const int g = h / (p.H_v / p.H_qk);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -495,7 +507,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const uint32_t ab_tb = (uint32_t)(p.H_v * DK) * 4u;
   const uint32_t v_tb = (uint32_t)(p.H_v * d_v) * sizeof(ET);
   const uint32_t w_tb = (uint32_t)(p.H_v * d_v) * 4u;
-  const size_t tok0 = (size_t)n * p.T + tseg;
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v;
@@ -1133,7 +1144,7 @@ PrefillPlan plan_t(const PrefillArgs &a) {
   PrefillPlan pl{C, 1, a.T, 0};
   const int ncb = a.d_v / DVB;
   const int nfull = a.T / C;
-  if (DK % DVB != 0 || nfull < 2) return pl;
+  if (a.cu_seqlens || DK % DVB != 0 || nfull < 2) return pl;
   long P = 1;
   if (const char *env = getenv("GDN2_PREFILL_SPLIT")) {
     P = atol(env);
@@ -1187,6 +1198,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.M_T = nullptr; p.m_stride = 0;
   p.o_first_only = false;
   p.sT_last_only = false;
+  p.cu = a.cu_seqlens;
   const int units = a.B * a.H_v;
   if (pl.nseg <= 1) {
     hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(units * ncb), dim3(512), 0, st, p);

@@ -108,6 +108,28 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void 
                                void *o, float *S_T, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Prefill of a batch of sequences of different lengths packed along the
+ * token axis (the serving layout; GDN-2 note and wiki describe the layer's
+ * use in serving long and short requests alike). desc->B is the number of
+ * sequences and desc->T the total number of tokens; q, k are
+ * [T, H_qk, d_k], v, w, o [T, H_v, d_v], a, b [T, H_v, d_k] (a leading batch
+ * dimension of 1 is the same memory); sequence n is tokens
+ * cu_seqlens[n] .. cu_seqlens[n+1]-1.
+ *   cu_seqlens: device pointer to B+1 int32 offsets, cu_seqlens[0] = 0,
+ *         non-decreasing, cu_seqlens[B] = T (a precondition: device memory
+ *         is not read by the host; offsets outside [0, T] are clamped to it).
+ *         Required when B > 0 (GDN2_ERR_NULL_POINTER).
+ *   S0, S_T: [B, H_v, d_k, d_v] fp32, one state per sequence, as for
+ *         gdn2_chunk_forward (S0 may be NULL, S_T may be NULL or alias S0).
+ * Each sequence is computed exactly as gdn2_chunk_forward computes it alone
+ * (the same chunk boundaries from its first token, a ragged last chunk
+ * stepped token by token); an empty sequence gives S_T = S0. Sequences are
+ * never split into segments: no workspace is used. Errors as for
+ * gdn2_chunk_forward. */
+gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *desc, const int32_t *cu_seqlens, const void *q,
+                                      const void *k, const void *v, const float *a, const float *b,
+                                      const float *w, const float *S0, void *o, float *S_T, void *stream);
+
 /* Decode: one token per sequence (desc->T must be 1). Reads the state S,
  * applies the step above and writes S back in place, and writes o.
  * Inputs are shaped as for the prefill with T = 1 (B = number of sequences).

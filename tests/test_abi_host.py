@@ -113,6 +113,32 @@ def test_split_workspace_query_and_errors(monkeypatch):
         assert fwd(d2, p, ws=p[i] + 256, ws_bytes=need) == g.GDN2_ERR_ALIAS, i
 
 
+def test_varlen_argument_errors():
+    def fv(desc, cu=FAKE + 30 * (1 << 30), p=None):
+        p = p or _ptrs()
+        return g.gdn2_chunk_forward_varlen(desc, cu, *p, 0)
+
+    d = g.make_desc(4, 640, 2, 4, 128, 128, 64, g.GDN2_BF16)
+    assert fv(None) == g.GDN2_ERR_NULL_POINTER
+    assert fv(g.make_desc(4, 640, 2, 4, 128, 128, 64, 9)) == g.GDN2_ERR_BAD_DTYPE
+    assert fv(g.make_desc(4, 640, 3, 4, 128, 128, 64, 1)) == g.GDN2_ERR_BAD_SHAPE
+    assert fv(g.make_desc(0, 640, 2, 4, 128, 128, 64, 1), cu=0) == g.GDN2_OK  # no sequences: nothing to do
+    assert fv(d, cu=0) == g.GDN2_ERR_NULL_POINTER
+    p = _ptrs()
+    p[1] = 0
+    assert fv(d, p=p) == g.GDN2_ERR_NULL_POINTER
+    p = _ptrs()
+    p[0] += 8
+    assert fv(d, p=p) == g.GDN2_ERR_BAD_SHAPE
+    for i in (0, 2, 3, 6, 8):
+        p = _ptrs()
+        p[7] = p[i] + 16
+        assert fv(d, p=p) == g.GDN2_ERR_ALIAS, i
+    p = _ptrs()
+    assert fv(d, cu=p[7] + 64, p=p) == g.GDN2_ERR_ALIAS  # o over the offsets
+    assert fv(d, cu=p[8] + 64, p=p) == g.GDN2_ERR_ALIAS  # S_T over the offsets
+
+
 def test_decode_argument_errors():
     def dec(desc, p=None):
         p = p or _ptrs()[:8]

@@ -164,6 +164,60 @@ def test_split_equals_unsplit_with_strong_decay_and_in_place_state(monkeypatch):
     assert normwise(to_np(o2), ref_o) <= TOL["f32"] and normwise(to_np(S2), ref_S) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("dtype,dk,dv,chunk", [("f32", 128, 128, 64), ("bf16", 128, 128, 64),
+                                                ("f32", 64, 32, 32), ("bf16", 16, 64, 16)])
+def test_varlen_matches_oracle_and_separate_calls(dtype, dk, dv, chunk):
+    """Packed sequences of different lengths (empty, one token, below / at /
+    above a chunk, ragged), grouped heads, one random S0 per sequence: each
+    sequence matches the oracle, and bit for bit the same sequence run alone."""
+    import gated_delta_rule_83_amd as g
+    rng = np.random.default_rng(110 + dk + dv)
+    lens = [0, 1, 31, 64, 100, 5, 257]
+    T = sum(lens)
+    d = rand_inputs(rng, 1, T, 1, 2, dk, dv)
+    S0 = (rng.standard_normal((len(lens), 2, dk, dv)) * 0.5).astype(np.float32)
+    d["S0"] = None
+    td = gi.to_torch(d, dtype, DEV)
+    S0t = torch.from_numpy(S0).to(DEV)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cut = torch.from_numpy(cu).to(DEV)
+    o, ST = g.chunk_forward_varlen(td["q"][0], td["k"][0], td["v"][0], td["a"][0], td["b"][0], td["w"][0],
+                                   cut, S0t, chunk=chunk)
+    torch.cuda.synchronize()
+    assert o.shape == (T, 2, dv) and ST.shape == (len(lens), 2, dk, dv)
+    for n, (t0, t1) in enumerate(zip(cu[:-1], cu[1:])):
+        sl = lambda x: x[:, t0:t1].contiguous()
+        o1, S1 = g.chunk_forward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]),
+                                 S0t[n:n + 1].contiguous(), chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(o[t0:t1], o1[0]) and torch.equal(ST[n], S1[0]), n
+        if t1 == t0:
+            assert torch.equal(ST[n], S0t[n])  # an empty sequence keeps its state
+            continue
+        ref_o, ref_S = oracle.forward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]),
+                                      sl(td["w"]), S0t[n:n + 1])
+        eo = normwise(to_np(o[t0:t1]), ref_o[0])
+        es = normwise(to_np(ST[n]), ref_S[0])
+        print(f"[varlen {dtype} dk{dk} dv{dv} seq {n} len {t1 - t0}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
+        assert eo <= TOL[dtype] and es <= TOL[dtype], (n, eo, es)
+
+
+def test_varlen_null_state_and_in_place():
+    import gated_delta_rule_83_amd as g
+    rng = np.random.default_rng(120)
+    lens = [40, 0, 70]
+    d = rand_inputs(rng, 1, sum(lens), 2, 2, 128, 128)
+    td = gi.to_torch(d, "bf16", DEV)
+    cut = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    args = [td[x][0] for x in ("q", "k", "v", "a", "b", "w")]
+    o0, S_zero = g.chunk_forward_varlen(*args, cut, None, chunk=64)
+    S = torch.zeros((3, 2, 128, 128), dtype=torch.float32, device=DEV)
+    o1, _ = g.chunk_forward_varlen(*args, cut, S, chunk=64, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(S, S_zero)
+    assert float(S_zero[1].abs().max()) == 0.0  # the empty sequence keeps its (zero) state
+
+
 def test_chunk_length_invariance():
     c = gi.scaled(1, B=1, T=256, H_qk=2, H_v=2)
     d = gi.make_inputs(c)
