@@ -127,6 +127,49 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                       const float *a, const float *beta, const float *S0, void *o,
+                                       float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  gdn2_status st = check_desc(d, false);
+  if (st != GDN2_OK) return st;
+  const size_t ws_need = gdn2_chunk_forward_workspace_bytes(d);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
+  const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
+  const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
+  const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
+  if (B == 0) return GDN2_OK;
+  const bool tokens = T > 0;
+  if (tokens && (!q || !k || !v || !a || !beta || !o)) return GDN2_ERR_NULL_POINTER;
+  const void *ptrs[] = {q, k, v, a, beta, S0, o, S_T};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+  const Range rq = range_of(q, B * T * Hqk * dk * es), rk = range_of(k, B * T * Hqk * dk * es);
+  const Range rv = range_of(v, B * T * Hv * dv * es);
+  const Range ra = range_of(a, B * T * Hv * dk * 4), rbeta = range_of(beta, B * T * Hv * 4);
+  const Range ro = range_of(o, B * T * Hv * dv * es);
+  const Range rs0 = range_of(S0, S0 ? B * Hv * dk * dv * 4 : 0);
+  const Range rst = range_of(S_T, S_T ? B * Hv * dk * dv * 4 : 0);
+  const Range ins[] = {rq, rk, rv, ra, rbeta, rs0, rst};
+  if (tokens)
+    for (const Range &r : ins)
+      if (overlaps(ro, r)) return GDN2_ERR_ALIAS;
+  if (S0 && S_T && overlaps(rs0, rst) && S0 != S_T) return GDN2_ERR_ALIAS;
+  if (ws_need > 0) {
+    if (!aligned16(workspace)) return GDN2_ERR_BAD_SHAPE;
+    const Range rws = range_of(workspace, ws_need);
+    for (const Range &r : ins)
+      if (overlaps(rws, r)) return GDN2_ERR_ALIAS;
+    if (overlaps(rws, ro)) return GDN2_ERR_ALIAS;
+  }
+  gdn2::PrefillArgs p = prefill_args(d);
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = beta; p.w = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  p.coupled = true;
+  const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q,
                                       const void *k, const void *v, const float *a, const float *b,
                                       const float *w, const float *S0, void *o, float *S_T, void *stream) {

@@ -30,6 +30,9 @@ struct PrefillArgs {
   // packed sequences of different lengths: B + 1 token offsets (device), or
   // null for B sequences of T tokens each
   const int32_t *cu_seqlens;
+  // coupled gates: b and w both point to beta [.., T, H_v] (one scalar per
+  // token and value head, b = w = beta * ones)
+  bool coupled;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one

@@ -448,7 +448,10 @@ __device__ __forceinline__ void map_block(int L, int B, int H_qk, int H_v, int n
   cb = u % ncb;
 }
 
-template <int DK, int C, int NCT, bool BF16>
+// CPL: coupled gates (b = w = beta, one scalar per token and value head,
+// passed as both p.b and p.w, [.., T, H_v]); otherwise b is per key channel
+// and w per value channel.
+template <int DK, int C, int NCT, bool BF16, bool CPL>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   using Cf = PrefillCfg<DK, C, NCT, BF16>;
   using E = Elem<BF16>;
@@ -507,12 +510,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const uint32_t ab_tb = (uint32_t)(p.H_v * DK) * 4u;
   const uint32_t v_tb = (uint32_t)(p.H_v * d_v) * sizeof(ET);
   const uint32_t w_tb = (uint32_t)(p.H_v * d_v) * 4u;
+  const uint32_t bt_tb = CPL ? (uint32_t)p.H_v * 4u : ab_tb;  // token strides of b and w
+  const uint32_t wt_tb = CPL ? (uint32_t)p.H_v * 4u : w_tb;
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v;
   const float *ah = p.a + tok0 * p.H_v * DK + (size_t)h * DK;
-  const float *bh = p.b + tok0 * p.H_v * DK + (size_t)h * DK;
-  const float *wh = p.w + tok0 * p.H_v * d_v + (size_t)h * d_v;
+  const float *bh = CPL ? p.b + tok0 * p.H_v + h : p.b + tok0 * p.H_v * DK + (size_t)h * DK;
+  const float *wh = CPL ? p.w + tok0 * p.H_v + h : p.w + tok0 * p.H_v * d_v + (size_t)h * d_v;
   ET *oh = (ET *)p.o + tok0 * p.H_v * d_v + (size_t)h * d_v;
   // entering and final state of this lane's column: value blocks use S0 /
   // S_T ([B][H_v][d_k][d_v] per segment), identity blocks start from the
@@ -559,7 +564,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   };
   auto raw_src = [&](int t0) {
     return RawSrc{make_rsrc((const char *)ah + (size_t)t0 * ab_tb, rows_left(t0, ab_tb)),
-                  make_rsrc((const char *)bh + (size_t)t0 * ab_tb, rows_left(t0, ab_tb)),
+                  make_rsrc((const char *)bh + (size_t)t0 * bt_tb, rows_left(t0, bt_tb)),
                   make_rsrc((const char *)kh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb)),
                   make_rsrc((const char *)qh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb))};
   };
@@ -568,7 +573,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
         ra[P][r] = bload<floatx4>(src.a, ab_off, r * ab_tb);
-        rb[P][r] = bload<floatx4>(src.b, ab_off, r * ab_tb);
+        if constexpr (CPL) {
+          const float bb = bload<float>(src.b, (uint32_t)tb0 * bt_tb, r * bt_tb);
+          rb[P][r] = floatx4{bb, bb, bb, bb};
+        } else {
+          rb[P][r] = bload<floatx4>(src.b, ab_off, r * ab_tb);
+        }
       }
     }
   };
@@ -817,7 +827,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   auto token_steps = [&](int tb, int te) {
     for (int t = tb; t < te; ++t) {
       const float *at = ah + (size_t)t * (ab_tb / 4);
-      const float *bt = bh + (size_t)t * (ab_tb / 4);
+      const float *bt = bh + (size_t)t * (bt_tb / 4);
       const ET *kt = kh + (size_t)t * (qk_tb / sizeof(ET));
       const ET *qt = qh + (size_t)t * (qk_tb / sizeof(ET));
       float part = 0.f;
@@ -831,12 +841,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);  // key read r for this column
-      const float u = ident ? 0.f : wh[(size_t)t * (w_tb / 4) + col] * E::ld(vh + (size_t)t * (v_tb / sizeof(ET)) + col);
+      const float u = ident ? 0.f : wh[(size_t)t * (wt_tb / 4) + (CPL ? 0 : col)] * E::ld(vh + (size_t)t * (v_tb / sizeof(ET)) + col);
       float po = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         const int i0 = 16 * rt + 4 * lg;
-        const floatx4 bv = *reinterpret_cast<const floatx4 *>(bt + i0);
+        const floatx4 bv = CPL ? floatx4{bt[0], bt[0], bt[0], bt[0]} : *reinterpret_cast<const floatx4 *>(bt + i0);
         const floatx4 kv = E::ld4(kt + i0);
         const floatx4 qv = E::ld4(qt + i0);
         S[rt] = S[rt] - (bv * kv) * part + kv * u;
@@ -866,10 +876,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const int ut = lane / Cf::ULPT, uc = lane % Cf::ULPT;
   const int utok = cw * UTPW + ut;  // first token of this lane (i = 0)
   const uint32_t uv_off = (uint32_t)utok * v_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * sizeof(ET);
-  const uint32_t uw_off = (uint32_t)utok * w_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * 4u;
+  const uint32_t uw_off = CPL ? (uint32_t)utok * wt_tb : (uint32_t)utok * w_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * 4u;
   auto load_u = [&](auto P, int t0) {
     const rsrc_t rv_ = make_rsrc((const char *)vh + (size_t)t0 * v_tb, rows_left(t0, v_tb));
-    const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * w_tb, rows_left(t0, w_tb));
+    const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * wt_tb, rows_left(t0, wt_tb));
 #pragma unroll
     for (int i = 0; i < UNI; ++i) {
 #pragma unroll
@@ -877,7 +887,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         rv[P][i][e] = bload<floatx4>(rv_, uv_off + 16u * e, (uint32_t)(i * UTPI) * v_tb);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        rw[P][i][e] = bload<floatx4>(rw_, uw_off + 16u * e, (uint32_t)(i * UTPI) * w_tb);
+        if constexpr (CPL) {  // one gate per token, for all 8 columns
+          if (e == 0) {
+            const float bb = bload<float>(rw_, uw_off, (uint32_t)(i * UTPI) * wt_tb);
+            rw[P][i][0] = rw[P][i][1] = floatx4{bb, bb, bb, bb};
+          }
+        } else {
+          rw[P][i][e] = bload<floatx4>(rw_, uw_off + 16u * e, (uint32_t)(i * UTPI) * w_tb);
+        }
     }
   };
   // products of register set PP into the staging rows (lanes past the
@@ -1177,6 +1194,12 @@ PrefillPlan plan_t(const PrefillArgs &a) {
 // The chunk boundaries of every segment are those of the unsplit run.
 template <int DK, int C, int NCT, bool BF16>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
+  auto kernel = [&](int blocks, const PrefillParams &kp) {
+    if (a.coupled)
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true>), dim3(blocks), dim3(512), 0, st, kp);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false>), dim3(blocks), dim3(512), 0, st, kp);
+  };
   const PrefillPlan pl = plan_t<DK, C, NCT, BF16>(a);
   if (plan_only) {
     *plan_only = pl;
@@ -1201,7 +1224,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.cu = a.cu_seqlens;
   const int units = a.B * a.H_v;
   if (pl.nseg <= 1) {
-    hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(units * ncb), dim3(512), 0, st, p);
+    kernel(units * ncb, p);
     return hipGetLastError();
   }
   if (!a.workspace || a.workspace_bytes < pl.ws_bytes) return hipErrorInvalidValue;
@@ -1213,8 +1236,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.S_T = state; p.sT_stride = sstate;
   p.M_T = trans; p.m_stride = strans;
   p.o_first_only = true;
-  hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(pl.nseg * units * (ncb + p.ncb_id)), dim3(512), 0,
-                     st, p);
+  kernel(pl.nseg * units * (ncb + p.ncb_id), p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 2.
@@ -1228,7 +1250,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.S_T = a.S_T; p.sT_stride = 0; p.sT_last_only = true;
   p.M_T = nullptr; p.m_stride = 0;
   p.o_first_only = false;
-  hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16>), dim3(p.nseg * units * ncb), dim3(512), 0, st, p);
+  kernel(p.nseg * units * ncb, p);
   return hipGetLastError();
 }
 

@@ -108,6 +108,23 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void 
                                void *o, float *S_T, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Prefill with coupled gates: the erase gate and the write gate are one
+ * scalar per token and value head, b_t = w_t = beta_t (all channels): the
+ * form of the earlier Gated DeltaNet and Kimi Delta Attention, whose erase
+ * and write share one scalar gate (GDN-2 note, section on the delta rule's
+ * basic idea and its limits), with GDN-2's channel-wise decay kept. The
+ * update is then S = S~ + beta_t k_t (v_t - r_t)^T. Same arguments as
+ * gdn2_chunk_forward with b, w replaced by
+ *   beta: [B, T, H_v] fp32.
+ * The result equals gdn2_chunk_forward with b = beta * ones(d_k) and
+ * w = beta * ones(d_v) (bit for bit: the kernels are the same up to how the
+ * gates are read); the two per-channel gate arrays are not read, which
+ * removes about 40% of the prefill's memory traffic at d = 128. The same
+ * workspace rules apply (gdn2_chunk_forward_workspace_bytes). */
+gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                       const float *a, const float *beta, const float *S0, void *o,
+                                       float *S_T, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Prefill of a batch of sequences of different lengths packed along the
  * token axis (the serving layout; GDN-2 note and wiki describe the layer's
  * use in serving long and short requests alike). desc->B is the number of

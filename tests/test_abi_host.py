@@ -113,6 +113,31 @@ def test_split_workspace_query_and_errors(monkeypatch):
         assert fwd(d2, p, ws=p[i] + 256, ws_bytes=need) == g.GDN2_ERR_ALIAS, i
 
 
+def test_coupled_argument_errors():
+    def fc(desc, p=None, ws=0, ws_bytes=0):
+        p = p or _ptrs()[:8]  # q, k, v, a, beta, S0, o, S_T
+        return g.gdn2_chunk_forward_coupled(desc, *p, ws, ws_bytes, 0)
+
+    d = g.make_desc(2, 64, 2, 4, 128, 128, 64, g.GDN2_BF16)
+    assert fc(None) == g.GDN2_ERR_NULL_POINTER
+    assert fc(g.make_desc(2, 64, 2, 4, 128, 128, 64, 3)) == g.GDN2_ERR_BAD_DTYPE
+    assert fc(g.make_desc(2, 64, 2, 4, 128, 128, 48, 1)) == g.GDN2_ERR_UNSUPPORTED
+    for i in range(5):
+        p = _ptrs()[:8]
+        p[i] = 0
+        assert fc(d, p) == g.GDN2_ERR_NULL_POINTER, i
+    p = _ptrs()[:8]
+    p[4] += 4
+    assert fc(d, p) == g.GDN2_ERR_BAD_SHAPE
+    for i in (0, 3, 4, 5, 7):
+        p = _ptrs()[:8]
+        p[6] = p[i] + 16
+        assert fc(d, p) == g.GDN2_ERR_ALIAS, i
+    # the long-context shape needs the split workspace, as for gdn2_chunk_forward
+    d2 = g.make_desc(1, 65536, 16, 16, 128, 128, 64, g.GDN2_BF16)
+    assert fc(d2) == g.GDN2_ERR_WORKSPACE
+
+
 def test_varlen_argument_errors():
     def fv(desc, cu=FAKE + 30 * (1 << 30), p=None):
         p = p or _ptrs()

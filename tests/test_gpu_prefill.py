@@ -218,6 +218,46 @@ def test_varlen_null_state_and_in_place():
     assert float(S_zero[1].abs().max()) == 0.0  # the empty sequence keeps its (zero) state
 
 
+@pytest.mark.parametrize("dtype,dk,dv,chunk,T", [("f32", 128, 128, 64, 200), ("bf16", 128, 128, 64, 300),
+                                                  ("f32", 32, 64, 32, 133), ("bf16", 64, 16, 16, 70)])
+def test_coupled_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
+    """b = w = beta (one scalar per token and value head): bit for bit the
+    general path fed the expanded gates, and the oracle within tolerance."""
+    import gated_delta_rule_83_amd as g
+    rng = np.random.default_rng(130 + dk + dv)
+    d = rand_inputs(rng, 2, T, 1, 2, dk, dv)
+    beta = rng.uniform(0.0, 1.0, (2, T, 2)).astype(np.float32)
+    d["b"] = np.ascontiguousarray(np.broadcast_to(beta[..., None], (2, T, 2, dk)))
+    d["w"] = np.ascontiguousarray(np.broadcast_to(beta[..., None], (2, T, 2, dv)))
+    td = gi.to_torch(d, dtype, DEV)
+    bt = torch.from_numpy(beta).to(DEV)
+    oc, Sc = g.chunk_forward_coupled(td["q"], td["k"], td["v"], td["a"], bt, td["S0"], chunk=chunk)
+    og, Sg = gpu_prefill(td, chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, og) and torch.equal(Sc, Sg)
+    ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
+    eo, es = normwise(to_np(oc), ref_o), normwise(to_np(Sc), ref_S)
+    print(f"[coupled {dtype} dk{dk} dv{dv}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_coupled_gates_split_sequence(monkeypatch):
+    """Coupled gates through the split-sequence path (forced 3 segments)."""
+    import gated_delta_rule_83_amd as g
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "3")
+    rng = np.random.default_rng(140)
+    d = rand_inputs(rng, 1, 500, 1, 2, 128, 128)
+    beta = rng.uniform(0.0, 1.0, (1, 500, 2)).astype(np.float32)
+    d["b"] = np.ascontiguousarray(np.broadcast_to(beta[..., None], (1, 500, 2, 128)))
+    d["w"] = np.ascontiguousarray(np.broadcast_to(beta[..., None], (1, 500, 2, 128)))
+    td = gi.to_torch(d, "bf16", DEV)
+    oc, Sc = g.chunk_forward_coupled(td["q"], td["k"], td["v"], td["a"], torch.from_numpy(beta).to(DEV), td["S0"],
+                                     chunk=64)
+    og, Sg = gpu_prefill(td, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, og) and torch.equal(Sc, Sg)
+
+
 def test_chunk_length_invariance():
     c = gi.scaled(1, B=1, T=256, H_qk=2, H_v=2)
     d = gi.make_inputs(c)
