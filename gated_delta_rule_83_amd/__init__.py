@@ -5,11 +5,13 @@ the computation runs in the HIP kernels of ``libgdn2.so``; this module only
 marshals arguments. PyTorch supplies device memory and the stream.
 
 Raw entry points (same names and arguments as the C ABI; pointers are ints):
-    gdn2_chunk_forward, gdn2_chunk_forward_coupled, gdn2_chunk_forward_varlen, gdn2_decode_step,
+    gdn2_chunk_forward, gdn2_chunk_forward_coupled, gdn2_chunk_forward_scalar,
+    gdn2_chunk_forward_varlen, gdn2_decode_step,
     gdn2_chunk_forward_workspace_bytes, gdn2_status_string, gdn2_version
 Torch conveniences:
     chunk_forward(q, k, v, a, b, w, S0=None, chunk=64) -> (o, S_T)
     chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk=64) -> (o, S_T)
+    chunk_forward_scalar(q, k, v, alpha, beta, S0=None, chunk=64) -> (o, S_T)
     chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk=64) -> (o, S_T)
     decode_step(q, k, v, a, b, w, S) -> o        (S updated in place)
 
@@ -37,7 +39,8 @@ GDN2_ERR_ALIAS = 7
 GDN2_F32 = 0
 GDN2_BF16 = 1
 
-EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forward_varlen", "gdn2_decode_step",
+EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forward_scalar",
+            "gdn2_chunk_forward_varlen", "gdn2_decode_step",
             "gdn2_chunk_forward_workspace_bytes", "gdn2_status_string", "gdn2_version")
 
 
@@ -70,6 +73,8 @@ def load(path: Optional[str] = None):
     lib.gdn2_chunk_forward.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
     lib.gdn2_chunk_forward_coupled.restype = ctypes.c_int
     lib.gdn2_chunk_forward_coupled.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
+    lib.gdn2_chunk_forward_scalar.restype = ctypes.c_int
+    lib.gdn2_chunk_forward_scalar.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
     lib.gdn2_chunk_forward_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_forward_varlen.argtypes = [dp] + [vp] * 10 + [vp]
     lib.gdn2_decode_step.restype = ctypes.c_int
@@ -112,6 +117,12 @@ def gdn2_chunk_forward_coupled(desc, q, k, v, a, beta, S0, o, S_T, workspace=0, 
                                stream=0) -> int:
     return load().gdn2_chunk_forward_coupled(None if desc is None else ctypes.byref(desc), q, k, v, a, beta,
                                              S0, o, S_T, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_forward_scalar(desc, q, k, v, a, beta, S0, o, S_T, workspace=0, workspace_bytes=0,
+                              stream=0) -> int:
+    return load().gdn2_chunk_forward_scalar(None if desc is None else ctypes.byref(desc), q, k, v, a, beta,
+                                            S0, o, S_T, workspace, workspace_bytes, stream)
 
 
 def gdn2_chunk_forward_varlen(desc, cu_seqlens, q, k, v, a, b, w, S0, o, S_T, stream=0) -> int:
@@ -189,6 +200,19 @@ def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_
     """Prefill with coupled gates b = w = beta (one scalar per token and value
     head). q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v]; a [B,T,H_v,d_k] fp32;
     beta [B,T,H_v] fp32; S0 [B,H_v,d_k,d_v] fp32 or None. Returns (o, S_T)."""
+    return _forward_scalar_gates(gdn2_chunk_forward_coupled, q, k, v, a, beta, S0, chunk, o, S_T, want_state,
+                                 stream)
+
+
+def chunk_forward_scalar(q, k, v, alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
+                         want_state: bool = True, stream=None):
+    """Prefill with scalar gates (Gated DeltaNet form): decay alpha and coupled
+    erase/write gate beta, each [B,T,H_v] fp32. Other arguments as chunk_forward."""
+    return _forward_scalar_gates(gdn2_chunk_forward_scalar, q, k, v, alpha, beta, S0, chunk, o, S_T, want_state,
+                                 stream)
+
+
+def _forward_scalar_gates(entry, q, k, v, a, beta, S0, chunk, o, S_T, want_state, stream):
     import torch
     B, T, H_qk, d_k = q.shape
     H_v, d_v = v.shape[2], v.shape[3]
@@ -205,8 +229,8 @@ def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
     ws = gdn2_chunk_forward_workspace_bytes(desc)
     work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
-    st = gdn2_chunk_forward_coupled(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0), _ptr(o),
-                                    _ptr(S_T), _ptr(work), ws, _stream(stream))
+    st = entry(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(work), ws,
+               _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return o, S_T

@@ -127,9 +127,15 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *d, const void *q, const void *k, const void *v,
-                                       const float *a, const float *beta, const float *S0, void *o,
-                                       float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Coupled gates (beta [B, T, H_v]); a is [B, T, H_v, d_k], or [B, T, H_v]
+// with scalar_decay.
+gdn2_status forward_scalar_gates(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                 const float *a, const float *beta, const float *S0, void *o, float *S_T,
+                                 void *workspace, size_t workspace_bytes, void *stream, bool scalar_decay) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
   const size_t ws_need = gdn2_chunk_forward_workspace_bytes(d);
@@ -145,7 +151,7 @@ gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *d, const void *q, const 
     if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
   const Range rq = range_of(q, B * T * Hqk * dk * es), rk = range_of(k, B * T * Hqk * dk * es);
   const Range rv = range_of(v, B * T * Hv * dv * es);
-  const Range ra = range_of(a, B * T * Hv * dk * 4), rbeta = range_of(beta, B * T * Hv * 4);
+  const Range ra = range_of(a, B * T * Hv * (scalar_decay ? 1 : dk) * 4), rbeta = range_of(beta, B * T * Hv * 4);
   const Range ro = range_of(o, B * T * Hv * dv * es);
   const Range rs0 = range_of(S0, S0 ? B * Hv * dk * dv * 4 : 0);
   const Range rst = range_of(S_T, S_T ? B * Hv * dk * dv * 4 : 0);
@@ -166,8 +172,25 @@ gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *d, const void *q, const 
   p.workspace = workspace;
   p.workspace_bytes = workspace_bytes;
   p.coupled = true;
+  p.scalar_decay = scalar_decay;
   const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                       const float *a, const float *beta, const float *S0, void *o,
+                                       float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_scalar_gates(d, q, k, v, a, beta, S0, o, S_T, workspace, workspace_bytes, stream, false);
+}
+
+gdn2_status gdn2_chunk_forward_scalar(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                      const float *a, const float *beta, const float *S0, void *o,
+                                      float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_scalar_gates(d, q, k, v, a, beta, S0, o, S_T, workspace, workspace_bytes, stream, true);
 }
 
 gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q,

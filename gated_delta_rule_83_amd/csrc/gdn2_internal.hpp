@@ -33,6 +33,9 @@ struct PrefillArgs {
   // coupled gates: b and w both point to beta [.., T, H_v] (one scalar per
   // token and value head, b = w = beta * ones)
   bool coupled;
+  // scalar decay (with coupled gates): a points to [.., T, H_v], one decay
+  // per token and value head for all key channels
+  bool scalar_decay;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one

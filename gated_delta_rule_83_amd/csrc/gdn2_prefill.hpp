@@ -450,8 +450,9 @@ __device__ __forceinline__ void map_block(int L, int B, int H_qk, int H_v, int n
 
 // CPL: coupled gates (b = w = beta, one scalar per token and value head,
 // passed as both p.b and p.w, [.., T, H_v]); otherwise b is per key channel
-// and w per value channel.
-template <int DK, int C, int NCT, bool BF16, bool CPL>
+// and w per value channel. SCA: scalar decay (a one scalar per token and
+// value head, [.., T, H_v]); otherwise a is per key channel.
+template <int DK, int C, int NCT, bool BF16, bool CPL, bool SCA>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   using Cf = PrefillCfg<DK, C, NCT, BF16>;
   using E = Elem<BF16>;
@@ -510,12 +511,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const uint32_t ab_tb = (uint32_t)(p.H_v * DK) * 4u;
   const uint32_t v_tb = (uint32_t)(p.H_v * d_v) * sizeof(ET);
   const uint32_t w_tb = (uint32_t)(p.H_v * d_v) * 4u;
-  const uint32_t bt_tb = CPL ? (uint32_t)p.H_v * 4u : ab_tb;  // token strides of b and w
+  const uint32_t at_tb = SCA ? (uint32_t)p.H_v * 4u : ab_tb;  // token strides of a, b and w
+  const uint32_t bt_tb = CPL ? (uint32_t)p.H_v * 4u : ab_tb;
   const uint32_t wt_tb = CPL ? (uint32_t)p.H_v * 4u : w_tb;
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v;
-  const float *ah = p.a + tok0 * p.H_v * DK + (size_t)h * DK;
+  const float *ah = SCA ? p.a + tok0 * p.H_v + h : p.a + tok0 * p.H_v * DK + (size_t)h * DK;
   const float *bh = CPL ? p.b + tok0 * p.H_v + h : p.b + tok0 * p.H_v * DK + (size_t)h * DK;
   const float *wh = CPL ? p.w + tok0 * p.H_v + h : p.w + tok0 * p.H_v * d_v + (size_t)h * d_v;
   ET *oh = (ET *)p.o + tok0 * p.H_v * d_v + (size_t)h * d_v;
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     rsrc_t a, b, k, q;
   };
   auto raw_src = [&](int t0) {
-    return RawSrc{make_rsrc((const char *)ah + (size_t)t0 * ab_tb, rows_left(t0, ab_tb)),
+    return RawSrc{make_rsrc((const char *)ah + (size_t)t0 * at_tb, rows_left(t0, at_tb)),
                   make_rsrc((const char *)bh + (size_t)t0 * bt_tb, rows_left(t0, bt_tb)),
                   make_rsrc((const char *)kh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb)),
                   make_rsrc((const char *)qh + (size_t)t0 * qk_tb, rows_left(t0, qk_tb))};
@@ -572,7 +574,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     if (brow) {
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
-        ra[P][r] = bload<floatx4>(src.a, ab_off, r * ab_tb);
+        if constexpr (SCA) {
+          const float aa = bload<float>(src.a, (uint32_t)tb0 * at_tb, r * at_tb);
+          ra[P][r] = floatx4{aa, aa, aa, aa};
+        } else {
+          ra[P][r] = bload<floatx4>(src.a, ab_off, r * ab_tb);
+        }
         if constexpr (CPL) {
           const float bb = bload<float>(src.b, (uint32_t)tb0 * bt_tb, r * bt_tb);
           rb[P][r] = floatx4{bb, bb, bb, bb};
@@ -826,7 +833,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // Token-by-token steps on this wave's columns (exact for any decay).
   auto token_steps = [&](int tb, int te) {
     for (int t = tb; t < te; ++t) {
-      const float *at = ah + (size_t)t * (ab_tb / 4);
+      const float *at = ah + (size_t)t * (at_tb / 4);
       const float *bt = bh + (size_t)t * (bt_tb / 4);
       const ET *kt = kh + (size_t)t * (qk_tb / sizeof(ET));
       const ET *qt = qh + (size_t)t * (qk_tb / sizeof(ET));
@@ -834,7 +841,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         const int i0 = 16 * rt + 4 * lg;
-        const floatx4 av = *reinterpret_cast<const floatx4 *>(at + i0);
+        const floatx4 av = SCA ? floatx4{at[0], at[0], at[0], at[0]} : *reinterpret_cast<const floatx4 *>(at + i0);
         const floatx4 kv = E::ld4(kt + i0);
         S[rt] *= av;
         part += S[rt][0] * kv[0] + S[rt][1] * kv[1] + S[rt][2] * kv[2] + S[rt][3] * kv[3];
@@ -1195,10 +1202,12 @@ PrefillPlan plan_t(const PrefillArgs &a) {
 template <int DK, int C, int NCT, bool BF16>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   auto kernel = [&](int blocks, const PrefillParams &kp) {
-    if (a.coupled)
-      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true>), dim3(blocks), dim3(512), 0, st, kp);
+    if (a.scalar_decay)  // scalar decay comes with coupled gates (Gated DeltaNet)
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, true>), dim3(blocks), dim3(512), 0, st, kp);
+    else if (a.coupled)
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, false>), dim3(blocks), dim3(512), 0, st, kp);
     else
-      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false>), dim3(blocks), dim3(512), 0, st, kp);
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false>), dim3(blocks), dim3(512), 0, st, kp);
   };
   const PrefillPlan pl = plan_t<DK, C, NCT, BF16>(a);
   if (plan_only) {

@@ -125,6 +125,19 @@ gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *desc, const void *q, con
                                        const float *a, const float *beta, const float *S0, void *o,
                                        float *S_T, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Prefill with scalar gates: the decay is also one scalar per token and
+ * value head (all key channels), a_t = alpha_t, with coupled erase/write
+ * gates b_t = w_t = beta_t: the form of the earlier Gated DeltaNet (GDN-2
+ * note, section on the delta rule's basic idea and its limits; wiki, how it
+ * works). Same arguments as gdn2_chunk_forward_coupled with
+ *   a: [B, T, H_v] fp32 (one decay per token and value head).
+ * The result equals gdn2_chunk_forward with a = alpha * ones(d_k),
+ * b = beta * ones(d_k), w = beta * ones(d_v), bit for bit; no per-channel
+ * gate array is read. */
+gdn2_status gdn2_chunk_forward_scalar(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                      const float *a, const float *beta, const float *S0, void *o,
+                                      float *S_T, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Prefill of a batch of sequences of different lengths packed along the
  * token axis (the serving layout; GDN-2 note and wiki describe the layer's
  * use in serving long and short requests alike). desc->B is the number of

@@ -138,6 +138,17 @@ def test_coupled_argument_errors():
     assert fc(d2) == g.GDN2_ERR_WORKSPACE
 
 
+def test_scalar_argument_errors():
+    d = g.make_desc(2, 64, 2, 4, 128, 128, 64, g.GDN2_BF16)
+    p = _ptrs()[:8]
+    assert g.gdn2_chunk_forward_scalar(None, *p, 0, 0, 0) == g.GDN2_ERR_NULL_POINTER
+    p[3] = 0
+    assert g.gdn2_chunk_forward_scalar(d, *p, 0, 0, 0) == g.GDN2_ERR_NULL_POINTER
+    p = _ptrs()[:8]
+    p[6] = p[3] + 16
+    assert g.gdn2_chunk_forward_scalar(d, *p, 0, 0, 0) == g.GDN2_ERR_ALIAS
+
+
 def test_varlen_argument_errors():
     def fv(desc, cu=FAKE + 30 * (1 << 30), p=None):
         p = p or _ptrs()

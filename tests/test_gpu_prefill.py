@@ -241,6 +241,32 @@ def test_coupled_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,dk,dv,chunk,T", [("f32", 128, 128, 64, 150), ("bf16", 128, 128, 64, 330),
+                                                  ("bf16", 32, 32, 32, 97)])
+def test_scalar_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
+    """Gated DeltaNet form (scalar decay alpha, coupled gate beta, one scalar
+    each per token and value head): bit for bit the general path fed the
+    expanded gates, and the oracle within tolerance."""
+    import gated_delta_rule_83_amd as g
+    rng = np.random.default_rng(150 + dk + dv)
+    d = rand_inputs(rng, 2, T, 1, 2, dk, dv)
+    alpha = rng.uniform(0.5, 1.0, (2, T, 2)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (2, T, 2)).astype(np.float32)
+    d["a"] = np.ascontiguousarray(np.broadcast_to(alpha[..., None], (2, T, 2, dk)))
+    d["b"] = np.ascontiguousarray(np.broadcast_to(beta[..., None], (2, T, 2, dk)))
+    d["w"] = np.ascontiguousarray(np.broadcast_to(beta[..., None], (2, T, 2, dv)))
+    td = gi.to_torch(d, dtype, DEV)
+    os_, Ss = g.chunk_forward_scalar(td["q"], td["k"], td["v"], torch.from_numpy(alpha).to(DEV),
+                                     torch.from_numpy(beta).to(DEV), td["S0"], chunk=chunk)
+    og, Sg = gpu_prefill(td, chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(os_, og) and torch.equal(Ss, Sg)
+    ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
+    eo, es = normwise(to_np(os_), ref_o), normwise(to_np(Ss), ref_S)
+    print(f"[scalar {dtype} dk{dk} dv{dv}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
 def test_coupled_gates_split_sequence(monkeypatch):
     """Coupled gates through the split-sequence path (forced 3 segments)."""
     import gated_delta_rule_83_amd as g
