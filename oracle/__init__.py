@@ -16,6 +16,11 @@ variants, the linear-attention closed form, the "difference is zero"
 invariant, the query-change identity, a per-step key-read identity for
 channel-wise gates, the decay-only closed form, the reductions to the delta
 rule, a chunked fp64 evaluation, column separability and split prefill.
+The backward pass (``backward``: reverse-mode gradients of the same
+recurrence, every state kept) is pinned by ``tests/test_oracle_backward.py``:
+central finite differences of the forward, closed-form linear-attention
+gradients, the decay and erase-gate gradients at a = 1, b = 0, and the
+grouped-head sum.
 Parity unpinned: the exact placement of channel-wise erase and write gates
 when b and w are not uniform (the pages state it only in prose); the oracle
 takes erase (b * k) r^T and write k (w * v)^T.
@@ -51,6 +56,8 @@ def bind(path: str):
     dp = ctypes.POINTER(ctypes.c_double)
     lib.gdn2_oracle_forward.restype = ctypes.c_int
     lib.gdn2_oracle_forward.argtypes = [ctypes.c_int] * 6 + [dp] * 9 + [ctypes.c_int, dp]
+    lib.gdn2_oracle_backward.restype = ctypes.c_int
+    lib.gdn2_oracle_backward.argtypes = [ctypes.c_int] * 6 + [dp] * 16 + [ctypes.c_int]
     return lib
 
 
@@ -111,6 +118,38 @@ def forward(q, k, v, a, b, w, S0=None, nthreads: Optional[int] = None,
     if timing:
         return o, ST, el.value
     return o, ST
+
+
+def backward(q, k, v, a, b, w, S0, dO, dS_T=None, nthreads: Optional[int] = None, lib=None) -> dict:
+    """Gradients of the recurrence in fp64 (reverse mode, every state kept).
+
+    Shapes as :func:`forward`, plus dO like o and dS_T like S_T (None: zero).
+    Returns a dict with dq, dk [B, T, H_qk, d_k] (summed over the value heads
+    that share a query/key head), dv, dw [B, T, H_v, d_v], da, db
+    [B, T, H_v, d_k] and dS0 [B, H_v, d_k, d_v].
+    """
+    lib = _load() if lib is None else lib
+    q, k, v, a, b, w, S0, dO, dS_T = (_f64(x) for x in (q, k, v, a, b, w, S0, dO, dS_T))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    assert k.shape == q.shape and v.shape == (B, T, Hv, dv) and dO.shape == v.shape
+    assert a.shape == (B, T, Hv, dk) and b.shape == a.shape and w.shape == v.shape
+    for s in (S0, dS_T):
+        if s is not None:
+            assert s.shape == (B, Hv, dk, dv)
+    dq_h = np.empty((B, T, Hv, dk)); dk_h = np.empty((B, T, Hv, dk))
+    out = {"dv": np.empty((B, T, Hv, dv)), "dw": np.empty((B, T, Hv, dv)), "da": np.empty((B, T, Hv, dk)),
+           "db": np.empty((B, T, Hv, dk)), "dS0": np.empty((B, Hv, dk, dv))}
+    nt = cores() if nthreads is None else int(nthreads)
+    rc = lib.gdn2_oracle_backward(B, T, Hqk, Hv, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w),
+                                  _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dq_h), _ptr(dk_h), _ptr(out["dv"]),
+                                  _ptr(out["da"]), _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dS0"]), nt)
+    if rc != 0:
+        raise RuntimeError(f"oracle backward failed with code {rc}")
+    G = Hv // Hqk
+    out["dq"] = dq_h.reshape(B, T, Hqk, G, dk).sum(axis=3)
+    out["dk"] = dk_h.reshape(B, T, Hqk, G, dk).sum(axis=3)
+    return out
 
 
 def forward_heads(inputs: dict, heads, nthreads: Optional[int] = None) -> Tuple[dict, dict]:

@@ -179,3 +179,220 @@ int gdn2_oracle_forward(int B, int T, int Hqk, int Hv, int dk, int dv,
     *elapsed_s = (double)(t1.tv_sec - t0.tv_sec) + 1e-9 * (double)(t1.tv_nsec - t0.tv_nsec);
   return J.fail ? -2 : 0;
 }
+
+/*
+ * Backward pass (gradients of the same recurrence), fp64.
+ *
+ * The pages define no backward pass; training the layer (the GDN-2 post on
+ * tilnote.io reports a 1.3B-parameter model trained on 100B tokens) needs
+ * the derivative of the forward map above. This is reverse-mode
+ * differentiation of steps 1-5, one token at a time from the last token to
+ * the first, with every state S_t kept from a forward run (no recomputation
+ * tricks). Given upstream gradients dO = dL/do and dS_T = dL/dS_T (NULL:
+ * zero), with L the running adjoint dL/dS of the state after token t:
+ *
+ *   5. read:   dq_t[i] = sum_j S_t[i][j] dO_t[j];   L[i][j] += q_t[i] dO_t[j]
+ *   4./3. with e = b_t*k_t, u = w_t*v_t and r the k-read of step 2:
+ *              du[j] = sum_i L[i][j] k_t[i]  -> dv_t[j] = du[j] w_t[j], dw_t[j] = du[j] v_t[j]
+ *              de[i] = -sum_j L[i][j] r[j]   -> db_t[i] = de[i] k_t[i],  dk_t[i] += de[i] b_t[i]
+ *              dk_t[i] += sum_j L[i][j] u[j]
+ *              dr[j] = -sum_i L[i][j] e[i]
+ *   2. k-read (r = Sd^T k, Sd the decayed state):
+ *              dk_t[i] += sum_j Sd[i][j] dr[j];  L[i][j] += k_t[i] dr[j]   (L is now dL/dSd)
+ *   1. decay (Sd = diag(a_t) S_{t-1}):
+ *              da_t[i] = sum_j L[i][j] S_{t-1}[i][j];  L[i][j] *= a_t[i]
+ *
+ * and finally dS0 = L. dq and dk are returned per value head
+ * ([B, T, H_v, d_k]); the QK-head gradient is their sum over the value heads
+ * that share the QK head (done by the caller).
+ */
+typedef struct {
+  int B, T, Hqk, Hv, dk, dv;
+  const double *q, *k, *v, *a, *b, *w, *S0, *dO, *dST;
+  double *dq, *dk_, *dv_, *da, *db, *dw, *dS0;
+  int next_unit;
+  pthread_mutex_t lock;
+  int fail;
+} bjob_t;
+
+static void run_unit_bwd(const bjob_t *J, int unit, double *hist, double *rs, double *L, double *du,
+                         double *dr) {
+  const int n = unit / J->Hv, h = unit % J->Hv;
+  const int G = J->Hv / J->Hqk, g = h / G;
+  const int dk = J->dk, dv = J->dv, T = J->T;
+  const size_t qk_tok = (size_t)J->Hqk * dk, ab_tok = (size_t)J->Hv * dk, vw_tok = (size_t)J->Hv * dv;
+  const size_t ssz = (size_t)dk * dv;
+  const size_t s_off = ((size_t)n * J->Hv + h) * ssz;
+
+  /* forward: hist[t + 1] = S after token t, hist[0] = S0; rs[t] = k-read */
+  if (J->S0)
+    memcpy(hist, J->S0 + s_off, sizeof(double) * ssz);
+  else
+    memset(hist, 0, sizeof(double) * ssz);
+  for (int t = 0; t < T; ++t) {
+    const size_t tok = (size_t)n * T + t;
+    const double *kt = J->k + tok * qk_tok + (size_t)g * dk;
+    const double *at = J->a + tok * ab_tok + (size_t)h * dk;
+    const double *bt = J->b + tok * ab_tok + (size_t)h * dk;
+    const double *vt = J->v + tok * vw_tok + (size_t)h * dv;
+    const double *wt = J->w + tok * vw_tok + (size_t)h * dv;
+    const double *Sp = hist + (size_t)t * ssz;
+    double *S = hist + (size_t)(t + 1) * ssz;
+    double *r = rs + (size_t)t * dv;
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = Sp[(size_t)i * dv + j] * at[i];
+    for (int j = 0; j < dv; ++j) r[j] = 0.0;
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) r[j] += S[(size_t)i * dv + j] * kt[i];
+    for (int i = 0; i < dk; ++i) {
+      const double e = bt[i] * kt[i];
+      for (int j = 0; j < dv; ++j) {
+        S[(size_t)i * dv + j] -= e * r[j];
+        S[(size_t)i * dv + j] += kt[i] * (wt[j] * vt[j]);
+      }
+    }
+  }
+
+  /* backward */
+  if (J->dST)
+    memcpy(L, J->dST + s_off, sizeof(double) * ssz);
+  else
+    memset(L, 0, sizeof(double) * ssz);
+  for (int t = T - 1; t >= 0; --t) {
+    const size_t tok = (size_t)n * T + t;
+    const double *qt = J->q + tok * qk_tok + (size_t)g * dk;
+    const double *kt = J->k + tok * qk_tok + (size_t)g * dk;
+    const double *at = J->a + tok * ab_tok + (size_t)h * dk;
+    const double *bt = J->b + tok * ab_tok + (size_t)h * dk;
+    const double *vt = J->v + tok * vw_tok + (size_t)h * dv;
+    const double *wt = J->w + tok * vw_tok + (size_t)h * dv;
+    const double *dOt = J->dO + tok * vw_tok + (size_t)h * dv;
+    const double *St = hist + (size_t)(t + 1) * ssz;
+    const double *Sp = hist + (size_t)t * ssz;
+    const double *r = rs + (size_t)t * dv;
+    double *dqt = J->dq + tok * ab_tok + (size_t)h * dk;
+    double *dkt = J->dk_ + tok * ab_tok + (size_t)h * dk;
+    double *dat = J->da + tok * ab_tok + (size_t)h * dk;
+    double *dbt = J->db + tok * ab_tok + (size_t)h * dk;
+    double *dvt = J->dv_ + tok * vw_tok + (size_t)h * dv;
+    double *dwt = J->dw + tok * vw_tok + (size_t)h * dv;
+
+    /* 5. the query read o_t = S_t^T q_t */
+    for (int i = 0; i < dk; ++i) {
+      double s = 0.0;
+      for (int j = 0; j < dv; ++j) s += St[(size_t)i * dv + j] * dOt[j];
+      dqt[i] = s;
+    }
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] += qt[i] * dOt[j];
+    /* 4. write k u^T and 3. erase e r^T */
+    for (int j = 0; j < dv; ++j) {
+      du[j] = 0.0;
+      dr[j] = 0.0;
+    }
+    for (int i = 0; i < dk; ++i) {
+      const double e = bt[i] * kt[i];
+      for (int j = 0; j < dv; ++j) {
+        du[j] += L[(size_t)i * dv + j] * kt[i];
+        dr[j] -= L[(size_t)i * dv + j] * e;
+      }
+    }
+    for (int j = 0; j < dv; ++j) {
+      dvt[j] = du[j] * wt[j];
+      dwt[j] = du[j] * vt[j];
+    }
+    for (int i = 0; i < dk; ++i) {
+      double de = 0.0, kw = 0.0;
+      for (int j = 0; j < dv; ++j) {
+        de -= L[(size_t)i * dv + j] * r[j];
+        kw += L[(size_t)i * dv + j] * (wt[j] * vt[j]);
+      }
+      dbt[i] = de * kt[i];
+      dkt[i] = kw + de * bt[i];
+    }
+    /* 2. the k-read r = Sd^T k, Sd = diag(a_t) S_{t-1} */
+    for (int i = 0; i < dk; ++i) {
+      double s = 0.0;
+      for (int j = 0; j < dv; ++j) s += at[i] * Sp[(size_t)i * dv + j] * dr[j];
+      dkt[i] += s;
+      for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] += kt[i] * dr[j];
+    }
+    /* 1. the decay */
+    for (int i = 0; i < dk; ++i) {
+      double s = 0.0;
+      for (int j = 0; j < dv; ++j) s += L[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
+      dat[i] = s;
+      for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] *= at[i];
+    }
+  }
+  if (J->dS0) memcpy(J->dS0 + s_off, L, sizeof(double) * ssz);
+}
+
+static void *worker_bwd(void *arg) {
+  bjob_t *J = (bjob_t *)arg;
+  const size_t ssz = (size_t)J->dk * J->dv;
+  double *hist = (double *)malloc(sizeof(double) * ssz * ((size_t)J->T + 1));
+  double *rs = (double *)malloc(sizeof(double) * (size_t)J->dv * ((size_t)J->T + 1));
+  double *L = (double *)malloc(sizeof(double) * ssz);
+  double *du = (double *)malloc(sizeof(double) * (size_t)J->dv);
+  double *dr = (double *)malloc(sizeof(double) * (size_t)J->dv);
+  if (!hist || !rs || !L || !du || !dr) {
+    pthread_mutex_lock(&J->lock);
+    J->fail = 1;
+    pthread_mutex_unlock(&J->lock);
+  } else {
+    const int units = J->B * J->Hv;
+    for (;;) {
+      pthread_mutex_lock(&J->lock);
+      const int u = J->next_unit++;
+      pthread_mutex_unlock(&J->lock);
+      if (u >= units) break;
+      run_unit_bwd(J, u, hist, rs, L, du, dr);
+    }
+  }
+  free(hist);
+  free(rs);
+  free(L);
+  free(du);
+  free(dr);
+  return NULL;
+}
+
+/* Gradients of the forward map. Layouts as the forward, plus dO like o and
+ * dS_T like S_T (NULL: zero). Outputs: dq, dk per value head [B, T, H_v, d_k];
+ * dv, dw [B, T, H_v, d_v]; da, db [B, T, H_v, d_k]; dS0 [B, H_v, d_k, d_v]
+ * (NULL: not written). Each worker thread holds T + 1 states of one head.
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
+int gdn2_oracle_backward(int B, int T, int Hqk, int Hv, int dk, int dv,
+                         const double *q, const double *k, const double *v,
+                         const double *a, const double *b, const double *w,
+                         const double *S0, const double *dO, const double *dST,
+                         double *dq, double *dk_out, double *dv_out, double *da, double *db,
+                         double *dw, double *dS0, int nthreads) {
+  if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (Hv % Hqk != 0) return -1;
+  if (T > 0 && (!q || !k || !v || !a || !b || !w || !dO || !dq || !dk_out || !dv_out || !da || !db || !dw))
+    return -1;
+  bjob_t J;
+  J.B = B; J.T = T; J.Hqk = Hqk; J.Hv = Hv; J.dk = dk; J.dv = dv;
+  J.q = q; J.k = k; J.v = v; J.a = a; J.b = b; J.w = w; J.S0 = S0; J.dO = dO; J.dST = dST;
+  J.dq = dq; J.dk_ = dk_out; J.dv_ = dv_out; J.da = da; J.db = db; J.dw = dw; J.dS0 = dS0;
+  J.next_unit = 0;
+  J.fail = 0;
+  pthread_mutex_init(&J.lock, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > B * Hv) nthreads = B * Hv > 0 ? B * Hv : 1;
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  int started = 0;
+  if (th) {
+    for (int i = 0; i < nthreads; ++i) {
+      if (pthread_create(&th[i], NULL, worker_bwd, &J) != 0) break;
+      ++started;
+    }
+  }
+  if (started == 0) worker_bwd(&J);
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.lock);
+  return J.fail ? -2 : 0;
+}
