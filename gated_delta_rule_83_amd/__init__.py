@@ -41,7 +41,8 @@ GDN2_BF16 = 1
 
 EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forward_scalar",
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
-            "gdn2_chunk_forward_workspace_bytes", "gdn2_status_string", "gdn2_version")
+            "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
+            "gdn2_status_string", "gdn2_version")
 
 
 class gdn2_desc(ctypes.Structure):
@@ -81,6 +82,10 @@ def load(path: Optional[str] = None):
     lib.gdn2_decode_step.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn2_chunk_forward_workspace_bytes.restype = sz
     lib.gdn2_chunk_forward_workspace_bytes.argtypes = [dp]
+    lib.gdn2_chunk_backward.restype = ctypes.c_int
+    lib.gdn2_chunk_backward.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+    lib.gdn2_chunk_backward_workspace_bytes.restype = sz
+    lib.gdn2_chunk_backward_workspace_bytes.argtypes = [dp]
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_status_string.argtypes = [ctypes.c_int]
     lib.gdn2_version.restype = ctypes.c_int
@@ -128,6 +133,16 @@ def gdn2_chunk_forward_scalar(desc, q, k, v, a, beta, S0, o, S_T, workspace=0, w
 def gdn2_chunk_forward_varlen(desc, cu_seqlens, q, k, v, a, b, w, S0, o, S_T, stream=0) -> int:
     return load().gdn2_chunk_forward_varlen(None if desc is None else ctypes.byref(desc), cu_seqlens, q, k,
                                             v, a, b, w, S0, o, S_T, stream)
+
+
+def gdn2_chunk_backward_workspace_bytes(desc) -> int:
+    return load().gdn2_chunk_backward_workspace_bytes(None if desc is None else ctypes.byref(desc))
+
+
+def gdn2_chunk_backward(desc, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace=0,
+                        workspace_bytes=0, stream=0) -> int:
+    return load().gdn2_chunk_backward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w, S0, dO,
+                                      dS_T, dq, dk, dv, da, db, dw, dS0, workspace, workspace_bytes, stream)
 
 
 def gdn2_decode_step(desc, q, k, v, a, b, w, S, o, stream=0) -> int:
@@ -193,6 +208,45 @@ def chunk_forward(q, k, v, a, b, w, S0=None, chunk: int = 64, o=None, S_T=None,
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return o, S_T
+
+
+def chunk_backward(q, k, v, a, b, w, S0, dO, dS_T=None, want_dS0: bool = True, grads=None, workspace=None,
+                   stream=None) -> dict:
+    """Gradients of chunk_forward. Inputs as chunk_forward, plus dO (like o)
+    and dS_T (like S_T, or None for zero). Returns a dict with dq, dk, dv (the
+    input dtype), da, db, dw (fp32) and dS0 (fp32, or None without want_dS0).
+    `grads` may hold preallocated outputs under those names, and `workspace`
+    a uint8 device tensor of at least gdn2_chunk_backward_workspace_bytes."""
+    import torch
+    B, T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
+        _check(t, nm, q.dtype)
+    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0"), (dS_T, "dS_T")):
+        _check(t, nm, torch.float32)
+    g = dict(grads or {})
+    dev = q.device
+    shapes = {"dq": ((B, T, H_qk, d_k), q.dtype), "dk": ((B, T, H_qk, d_k), q.dtype),
+              "dv": ((B, T, H_v, d_v), q.dtype), "da": ((B, T, H_v, d_k), torch.float32),
+              "db": ((B, T, H_v, d_k), torch.float32), "dw": ((B, T, H_v, d_v), torch.float32)}
+    if want_dS0:
+        shapes["dS0"] = ((B, H_v, d_k, d_v), torch.float32)
+    for nm, (shape, dt) in shapes.items():
+        if g.get(nm) is None:
+            g[nm] = torch.empty(shape, dtype=dt, device=dev)
+        _check(g[nm], nm, dt)
+    g.setdefault("dS0", None)
+    desc = make_desc(B, T, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
+    ws = gdn2_chunk_backward_workspace_bytes(desc)
+    if workspace is None and ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() if workspace is not None else 0
+    st = gdn2_chunk_backward(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO),
+                             _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]),
+                             _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), wbytes, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st)
+    return g
 
 
 def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_T=None,

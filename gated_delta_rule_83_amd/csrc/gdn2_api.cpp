@@ -261,3 +261,63 @@ gdn2_status gdn2_decode_step(const gdn2_desc *d, const void *q, const void *k, c
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t gdn2_chunk_backward_workspace_bytes(const gdn2_desc *d) {
+  if (check_desc(d, false) != GDN2_OK) return 0;
+  return gdn2::backward_workspace_bytes(d->B, d->T, d->H_v, d->d_k, d->d_v);
+}
+
+gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                const float *a, const float *b, const float *w, const float *S0,
+                                const void *dO, const float *dS_T, void *dq, void *dk, void *dv, float *da,
+                                float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  gdn2_status st = check_desc(d, false);
+  if (st != GDN2_OK) return st;
+  const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
+  const size_t dkk = (size_t)d->d_k, dvv = (size_t)d->d_v;
+  const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
+  if (B == 0) return GDN2_OK;
+  const size_t ws_need = gdn2_chunk_backward_workspace_bytes(d);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
+  const bool tokens = T > 0;
+  if (tokens && (!q || !k || !v || !a || !b || !w || !dO || !dq || !dk || !dv || !da || !db || !dw))
+    return GDN2_ERR_NULL_POINTER;
+  const void *ptrs[] = {q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+  if (ws_need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_BAD_SHAPE;
+
+  const size_t nqk = tokens ? B * T * Hqk * dkk : 0, nab = tokens ? B * T * Hv * dkk : 0;
+  const size_t nvw = tokens ? B * T * Hv * dvv : 0, ns = B * Hv * dkk * dvv;
+  const Range ins[] = {range_of(q, nqk * es),  range_of(k, nqk * es), range_of(v, nvw * es),
+                       range_of(a, nab * 4),   range_of(b, nab * 4),  range_of(w, nvw * 4),
+                       range_of(S0, S0 ? ns * 4 : 0), range_of(dO, nvw * es),
+                       range_of(dS_T, dS_T ? ns * 4 : 0)};
+  const Range outs[] = {range_of(dq, nqk * es), range_of(dk, nqk * es), range_of(dv, nvw * es),
+                        range_of(da, nab * 4),  range_of(db, nab * 4),  range_of(dw, nvw * 4),
+                        range_of(dS0, dS0 ? ns * 4 : 0), range_of(workspace, ws_need)};
+  constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < NO; ++i) {
+    for (const Range &r : ins) {
+      // dS0 may replace dS_T exactly (each element is read before it is written)
+      if (i == 6 && dS0 && dS0 == dS_T && r.lo == reinterpret_cast<uintptr_t>(dS_T)) continue;
+      if (overlaps(outs[i], r)) return GDN2_ERR_ALIAS;
+    }
+    for (int j = i + 1; j < NO; ++j)
+      if (overlaps(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+  }
+
+  gdn2::BackwardArgs p{};
+  p.B = d->B; p.T = d->T; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
+  p.bf16 = d->dtype == GDN2_BF16;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.dO = dO; p.dST = dS_T;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.da = da; p.db = db; p.dw = dw; p.dS0 = dS0;
+  p.workspace = workspace;
+  const hipError_t e = gdn2::launch_backward(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,489 @@
+// gdn2_backward.hip -- gradients of the Gated DeltaNet-2 recurrence (the
+// backward pass of gdn2_chunk_forward, for training).
+//
+// Forward step per (sequence n, value head h), for every value column j
+// (Gated DeltaNet-2 post on tilnote.io, GDN-2 design section; delta-rule
+// tutorial on ai-systems-engineering.com, "record the difference" and
+// key-versus-query sections):
+//   Sd = diag(a_t) S_{t-1};  r_j = k_t . Sd[:, j];
+//   S_t[:, j] = Sd[:, j] - r_j e_t + u_j k_t   (e = b*k, u = w*v);
+//   o_t[j] = q_t . S_t[:, j].
+// Value columns never mix, so each column's d_k-vector state, and its
+// adjoint L = dLoss/dS[:, j], can be run alone; key-side gradients (dq, dk,
+// da, db) sum over the columns. Reverse mode, from the last token to the
+// first (L starts at dS_T):
+//   dq_t += S_t[:, j] dO_t[j];                L += q_t dO_t[j]
+//   du_j = k_t . L  -> dv = du w, dw = du v;  dr_j = -(e_t . L)
+//   de -= L r_j  -> db = de*k, dk += de*b;    dk += u_j L + dr_j Sd[:, j]
+//   L += dr_j k_t;  da_t += L * S_{t-1}[:, j];  L = a_t * L
+// and dS0[:, j] = L at the end.
+//
+// MI355X design: this is a per-token recurrence with two 16-lane key
+// reductions per token and column, so it runs on the vector ALUs, not the
+// matrix cores. One workgroup per (n, h, block of CB value columns): four
+// waves (two for CB = 16), each holding 8 columns; lane = (column pair c4,
+// key group kg) holds columns 2*c4, 2*c4+1 of its wave on the key channels
+// kg*KPL .. +KPL. Key sums (k-read, du, dr) are DPP rotations within a
+// 16-lane row; key-side gradient sums over the wave's columns are a
+// two-step reduce-scatter across the four column pairs, then a fixed-order
+// sum over the waves in LDS (deterministic, no atomics).
+//
+// Memory: phase 1 runs the recurrence forward and stores the state at the
+// start of every kSub-token sub-segment (fp32, in the workspace); phase 2
+// walks the sub-segments backward, recomputes a sub-segment's kSub + 1
+// states into registers from its checkpoint, and runs the adjoint over it.
+// Inputs of a sub-segment are staged in LDS (one set of loads per
+// workgroup, requested one sub-segment ahead). Key-side sums go to the
+// workspace per column block and are added up by backward_reduce_kernel,
+// which also sums the value heads that share a query/key head.
+#include "gdn2_device.hpp"
+#include "gdn2_internal.hpp"
+
+#ifndef GDN2_BWD_BF16
+#error "build with -DGDN2_BWD_BF16=0 or 1"
+#endif
+
+namespace gdn2 {
+
+hipError_t launch_backward_bf16(const BackwardParams &p, int d_k, hipStream_t st);
+
+namespace {
+
+constexpr int kSub = 8;  // tokens per sub-segment (the register history)
+
+template <int DK, int CB>
+struct BwdCfg {
+  static constexpr int NWV = CB / 8;   // waves, 8 value columns each
+  static constexpr int NT = 64 * NWV;  // threads
+  static constexpr int KPL = DK / 16;  // key channels per lane
+  static constexpr int L = kSub;
+  static constexpr int NKS = L * DK / 4;                  // key quads staged per sub-segment
+  static constexpr int KIT = (NKS + NT - 1) / NT;         // ... per thread
+  static constexpr int NCS = L * CB / 4;                  // column quads staged per sub-segment
+  static_assert(NCS <= NT, "one column quad per thread at most");
+  static_assert(CB == 16 || CB == 32, "column block");
+};
+
+template <int DK, int CB>
+struct BwdSmem {
+  using Cf = BwdCfg<DK, CB>;
+  alignas(16) float kqae[Cf::L][4][DK];         // k, q, a, e = b*k of the sub-segment's tokens
+  alignas(16) float col[Cf::L][4][CB];          // u = w*v, v, w, dO of the workgroup's columns
+  alignas(16) float red[Cf::NWV][Cf::L][4][DK]; // per-wave key-side sums (dq, dk part, e part, da)
+  alignas(16) float du[Cf::L][CB];              // du per token and column
+};
+
+// x from lane (l + R) mod 16 of this lane's 16-lane row (DPP row_ror:R). The
+// empty asm keeps separate rotations separate instructions.
+template <int R>
+__device__ __forceinline__ float row_ror(float x) {
+  asm volatile("" : "+v"(x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xf,
+                                                               0xf, false));
+}
+// Sum over the 16 lanes of the row; every lane gets the same value (each
+// step adds two values that are equal in both lanes of a rotation pair).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  return x;
+}
+
+// Raw inputs of one sub-segment, held by a thread between its request and
+// its LDS store.
+template <int DK, int CB>
+struct Stage {
+  floatx4 k[BwdCfg<DK, CB>::KIT], q[BwdCfg<DK, CB>::KIT], a[BwdCfg<DK, CB>::KIT], b[BwdCfg<DK, CB>::KIT];
+  floatx4 v, w, d;
+};
+
+}  // namespace
+
+template <int DK, int CB, bool BF16>
+__global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(BackwardParams p) {
+  using Cf = BwdCfg<DK, CB>;
+  using E = Elem<BF16>;
+  using ET = typename E::T;
+  constexpr int KPL = Cf::KPL, L = Cf::L;
+  __shared__ BwdSmem<DK, CB> sm;
+
+  const int ncb = p.d_v / CB;
+  const int cb = blockIdx.x % ncb, unit = blockIdx.x / ncb;  // unit = n * H_v + h
+  const int n = unit / p.H_v, h = unit - n * p.H_v;
+  const int g = h / (p.H_v / p.H_qk);
+  const int T = p.T, d_v = p.d_v;
+  const int nsub = (T + L - 1) / L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c4 = lane >> 4, kg = lane & 15;
+  const int lcol = wave * 8 + 2 * c4;  // the lane's first column within the block
+  const int col = cb * CB + lcol;      // ... within the head
+  const int key0 = kg * KPL;
+
+  const size_t tok0 = (size_t)n * T;  // first token of the sequence
+  const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
+  const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
+  const float *ah = p.a + tok0 * p.H_v * DK + (size_t)h * DK;
+  const float *bh = p.b + tok0 * p.H_v * DK + (size_t)h * DK;
+  const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  const float *wh = p.w + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  const ET *dOh = (const ET *)p.dO + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  const size_t qk_t = (size_t)p.H_qk * DK, ab_t = (size_t)p.H_v * DK, vw_t = (size_t)p.H_v * d_v;
+  const size_t s_off = (size_t)unit * DK * d_v;
+  float *ckp = p.ck + ((size_t)unit * ncb + cb) * (size_t)nsub * (DK * CB) + (size_t)tid * (2 * KPL);
+
+  // Request sub-segment `sub`'s inputs into registers; tokens past the end
+  // are identity steps (a = 1, everything else 0).
+  auto request = [&](int sub, Stage<DK, CB> &st, bool backward) {
+#pragma unroll
+    for (int it = 0; it < Cf::KIT; ++it) {
+      const int idx = tid + it * Cf::NT;
+      const int tt = idx / (DK / 4), kq = idx % (DK / 4);
+      const int t = sub * L + tt;
+      const bool ok = idx < Cf::NKS && t < T;
+      st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
+      st.q[it] = ok && backward ? E::ld4(qh + t * qk_t + 4 * kq) : zero4();
+      st.a[it] = ok ? *reinterpret_cast<const floatx4 *>(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
+      st.b[it] = ok ? *reinterpret_cast<const floatx4 *>(bh + t * ab_t + 4 * kq) : zero4();
+    }
+    {
+      const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+      const int t = sub * L + tt;
+      const bool ok = tid < Cf::NCS && t < T;
+      st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
+      st.w = ok ? *reinterpret_cast<const floatx4 *>(wh + t * vw_t + 4 * cq) : zero4();
+      st.d = ok && backward ? E::ld4(dOh + t * vw_t + 4 * cq) : zero4();
+    }
+  };
+  auto stash = [&](const Stage<DK, CB> &st) {
+#pragma unroll
+    for (int it = 0; it < Cf::KIT; ++it) {
+      const int idx = tid + it * Cf::NT;
+      if (idx < Cf::NKS) {
+        const int tt = idx / (DK / 4), kq = idx % (DK / 4);
+        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][0][4 * kq]) = st.k[it];
+        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][1][4 * kq]) = st.q[it];
+        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][2][4 * kq]) = st.a[it];
+        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][3][4 * kq]) = st.b[it] * st.k[it];
+      }
+    }
+    if (tid < Cf::NCS) {
+      const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+      *reinterpret_cast<floatx4 *>(&sm.col[tt][0][4 * cq]) = st.w * st.v;
+      *reinterpret_cast<floatx4 *>(&sm.col[tt][1][4 * cq]) = st.v;
+      *reinterpret_cast<floatx4 *>(&sm.col[tt][2][4 * cq]) = st.w;
+      *reinterpret_cast<floatx4 *>(&sm.col[tt][3][4 * cq]) = st.d;
+    }
+  };
+  auto lds_keys = [&](int tt, int which, float (&x)[KPL]) {
+#pragma unroll
+    for (int e = 0; e < KPL; e += (KPL >= 4 ? 4 : KPL)) {
+      if constexpr (KPL >= 4) {
+        const floatx4 y = *reinterpret_cast<const floatx4 *>(&sm.kqae[tt][which][key0 + e]);
+        x[e] = y[0]; x[e + 1] = y[1]; x[e + 2] = y[2]; x[e + 3] = y[3];
+      } else if constexpr (KPL == 2) {
+        const floatx2 y = *reinterpret_cast<const floatx2 *>(&sm.kqae[tt][which][key0 + e]);
+        x[e] = y[0]; x[e + 1] = y[1];
+      } else {
+        x[e] = sm.kqae[tt][which][key0 + e];
+      }
+    }
+  };
+  // One forward step on the lane's two columns: s <- step(s); returns the k-reads.
+  auto fwd_step = [&](int tt, float (&s)[KPL][2], float &r0, float &r1) {
+    float kk[KPL], aa[KPL], ee[KPL];
+    lds_keys(tt, 0, kk);
+    lds_keys(tt, 2, aa);
+    lds_keys(tt, 3, ee);
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+      s[e][0] *= aa[e];
+      s[e][1] *= aa[e];
+      x0 = fmaf(kk[e], s[e][0], x0);
+      x1 = fmaf(kk[e], s[e][1], x1);
+    }
+    r0 = row_sum16(x0);
+    r1 = row_sum16(x1);
+    const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+      s[e][0] = fmaf(kk[e], u0, fmaf(-ee[e], r0, s[e][0]));
+      s[e][1] = fmaf(kk[e], u1, fmaf(-ee[e], r1, s[e][1]));
+    }
+  };
+
+  // ---------------------------------------------------------------- phase 1: forward, checkpoints
+  float s[KPL][2];
+#pragma unroll
+  for (int e = 0; e < KPL; ++e) {
+    if (p.S0) {
+      const floatx2 x = *reinterpret_cast<const floatx2 *>(p.S0 + s_off + (size_t)(key0 + e) * d_v + col);
+      s[e][0] = x[0];
+      s[e][1] = x[1];
+    } else {
+      s[e][0] = s[e][1] = 0.f;
+    }
+  }
+  Stage<DK, CB> st;
+  if (nsub > 0) request(0, st, false);
+  for (int sub = 0; sub < nsub; ++sub) {
+    __syncthreads();  // the previous sub-segment's readers are done
+    stash(st);
+    __syncthreads();
+    if (sub + 1 < nsub) request(sub + 1, st, false);
+    float *ck = ckp + (size_t)sub * (DK * CB);
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) *reinterpret_cast<floatx2 *>(ck + 2 * e) = floatx2{s[e][0], s[e][1]};
+#pragma unroll
+    for (int tt = 0; tt < L; ++tt) {
+      float r0, r1;
+      fwd_step(tt, s, r0, r1);
+    }
+  }
+
+  // ---------------------------------------------------------------- phase 2: backward
+  float lam[KPL][2];
+#pragma unroll
+  for (int e = 0; e < KPL; ++e) {
+    if (p.dST) {
+      const floatx2 x = *reinterpret_cast<const floatx2 *>(p.dST + s_off + (size_t)(key0 + e) * d_v + col);
+      lam[e][0] = x[0];
+      lam[e][1] = x[1];
+    } else {
+      lam[e][0] = lam[e][1] = 0.f;
+    }
+  }
+  if (nsub > 0) request(nsub - 1, st, true);
+  for (int sub = nsub - 1; sub >= 0; --sub) {
+    __syncthreads();  // the previous sub-segment's readers (and the sums below) are done
+    stash(st);
+    __syncthreads();
+    if (sub > 0) request(sub - 1, st, true);
+
+    // the sub-segment's states: hs[tt] = S before token tt, hs[L] = S after the last
+    float hs[L + 1][KPL][2], rr[L][2];
+    {
+      const float *ck = ckp + (size_t)sub * (DK * CB);
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        const floatx2 x = *reinterpret_cast<const floatx2 *>(ck + 2 * e);
+        hs[0][e][0] = x[0];
+        hs[0][e][1] = x[1];
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < L; ++tt) {
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        hs[tt + 1][e][0] = hs[tt][e][0];
+        hs[tt + 1][e][1] = hs[tt][e][1];
+      }
+      fwd_step(tt, hs[tt + 1], rr[tt][0], rr[tt][1]);
+    }
+
+#pragma unroll
+    for (int tt = L - 1; tt >= 0; --tt) {
+      float kk[KPL], qq[KPL], aa[KPL], ee[KPL];
+      lds_keys(tt, 0, kk);
+      lds_keys(tt, 1, qq);
+      lds_keys(tt, 2, aa);
+      lds_keys(tt, 3, ee);
+      const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
+      const float d0 = sm.col[tt][3][lcol], d1 = sm.col[tt][3][lcol + 1];
+      // x[0] dq part, x[1] dk part (u L + a * dr S_{t-1}), x[2] sum_j r_j L (de = -x[2]), x[3] da
+      float x[4][KPL];
+      float pu0 = 0.f, pu1 = 0.f, pe0 = 0.f, pe1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        x[0][e] = fmaf(hs[tt + 1][e][0], d0, hs[tt + 1][e][1] * d1);
+        lam[e][0] = fmaf(qq[e], d0, lam[e][0]);
+        lam[e][1] = fmaf(qq[e], d1, lam[e][1]);
+        pu0 = fmaf(lam[e][0], kk[e], pu0);
+        pu1 = fmaf(lam[e][1], kk[e], pu1);
+        pe0 = fmaf(lam[e][0], ee[e], pe0);
+        pe1 = fmaf(lam[e][1], ee[e], pe1);
+      }
+      const float du0 = row_sum16(pu0), du1 = row_sum16(pu1);
+      const float dr0 = -row_sum16(pe0), dr1 = -row_sum16(pe1);
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        x[2][e] = fmaf(lam[e][0], rr[tt][0], lam[e][1] * rr[tt][1]);
+        const float p2 = fmaf(lam[e][0], u0, lam[e][1] * u1);
+        lam[e][0] = fmaf(kk[e], dr0, lam[e][0]);
+        lam[e][1] = fmaf(kk[e], dr1, lam[e][1]);
+        const float p4 = fmaf(hs[tt][e][0], dr0, hs[tt][e][1] * dr1);
+        x[3][e] = fmaf(lam[e][0], hs[tt][e][0], lam[e][1] * hs[tt][e][1]);
+        x[1][e] = fmaf(aa[e], p4, p2);
+        lam[e][0] *= aa[e];
+        lam[e][1] *= aa[e];
+      }
+      // reduce-scatter over the four column pairs: lane group c4 ends with
+      // sum x[c4][.] of the wave's 8 columns
+      const bool hi1 = (c4 & 2) != 0, hi0 = (c4 & 1) != 0;
+      float y[2][KPL];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          const float send = hi1 ? x[m][e] : x[2 + m][e];
+          const float keep = hi1 ? x[2 + m][e] : x[m][e];
+          y[m][e] = keep + __shfl_xor(send, 32, 64);
+        }
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        const float send = hi0 ? y[0][e] : y[1][e];
+        const float keep = hi0 ? y[1][e] : y[0][e];
+        sm.red[wave][tt][c4][key0 + e] = keep + __shfl_xor(send, 16, 64);
+      }
+      if (kg == 0) {
+        sm.du[tt][lcol] = du0;
+        sm.du[tt][lcol + 1] = du1;
+      }
+    }
+    __syncthreads();
+
+    // key-side sums of the block (fixed wave order) -> workspace
+    constexpr int NQ = L * 4 * DK / 4;
+    for (int idx = tid; idx < NQ; idx += Cf::NT) {
+      const int tt = idx / DK, rem = idx % DK;  // rem = vector * (DK / 4) + key quad
+      const int vec = rem / (DK / 4), kq = rem % (DK / 4);
+      const int t = sub * L + tt;
+      if (t < T) {
+        floatx4 acc = *reinterpret_cast<const floatx4 *>(&sm.red[0][tt][vec][4 * kq]);
+#pragma unroll
+        for (int w2 = 1; w2 < Cf::NWV; ++w2) acc += *reinterpret_cast<const floatx4 *>(&sm.red[w2][tt][vec][4 * kq]);
+        float *dst = p.part + (((size_t)cb * p.B * T + tok0 + t) * p.H_v + h) * (4 * DK) + vec * DK + 4 * kq;
+        *reinterpret_cast<floatx4 *>(dst) = acc;
+      }
+    }
+    // dv = du * w, dw = du * v
+    for (int idx = tid; idx < L * CB; idx += Cf::NT) {
+      const int tt = idx / CB, c = idx % CB;
+      const int t = sub * L + tt;
+      if (t < T) {
+        const float du = sm.du[tt][c];
+        const size_t o = (tok0 + t) * vw_t + (size_t)h * d_v + cb * CB + c;
+        E::st((ET *)p.dv + o, du * sm.col[tt][2][c]);
+        p.dw[o] = du * sm.col[tt][1][c];
+      }
+    }
+  }
+  if (p.dS0) {
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+      *reinterpret_cast<floatx2 *>(p.dS0 + s_off + (size_t)(key0 + e) * d_v + col) = floatx2{lam[e][0], lam[e][1]};
+  }
+}
+
+// Key-side gradients: per (token, query/key head g), sum the column blocks'
+// partial sums of every value head h that shares g:
+//   dq = sum x0;  dk = sum (x1 - b*x2);  per h: da = x3, db = -k*x2.
+template <int DK, bool BF16>
+__global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) {
+  using E = Elem<BF16>;
+  using ET = typename E::T;
+  constexpr int TPR = DK / 4;  // threads per (token, g) row, 4 keys each
+  const int ncb = p.d_v / (p.d_v >= 32 ? 32 : 16);
+  const size_t BT = (size_t)p.B * p.T;
+  const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (row >= BT * p.H_qk) return;
+  const int kq = threadIdx.x % TPR;
+  const size_t tok = row / p.H_qk;
+  const int g = (int)(row % p.H_qk), G = p.H_v / p.H_qk;
+  const floatx4 kk = E::ld4((const ET *)p.k + row * DK + 4 * kq);
+  floatx4 dq = zero4(), dk = zero4();
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    floatx4 x[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int c = 0; c < ncb; ++c) {
+      const float *src = p.part + (((size_t)c * BT + tok) * p.H_v + h) * (4 * DK) + 4 * kq;
+#pragma unroll
+      for (int vec = 0; vec < 4; ++vec) x[vec] += *reinterpret_cast<const floatx4 *>(src + vec * DK);
+    }
+    const size_t o = (tok * p.H_v + h) * DK + 4 * kq;
+    const floatx4 bb = *reinterpret_cast<const floatx4 *>(p.b + o);
+    *reinterpret_cast<floatx4 *>(p.da + o) = x[3];
+    *reinterpret_cast<floatx4 *>(p.db + o) = -(kk * x[2]);
+    dq += x[0];
+    dk += x[1] - bb * x[2];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    E::st((ET *)p.dq + row * DK + 4 * kq + e, dq[e]);
+    E::st((ET *)p.dk + row * DK + 4 * kq + e, dk[e]);
+  }
+}
+
+namespace {
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int bwd_cb(int d_v) { return d_v >= 32 ? 32 : 16; }
+
+template <int DK, int CB, bool BF16>
+hipError_t launch_t(const BackwardParams &p, hipStream_t st) {
+  const int ncb = p.d_v / CB;
+  hipLaunchKernelGGL((backward_kernel<DK, CB, BF16>), dim3(p.B * p.H_v * ncb), dim3(BwdCfg<DK, CB>::NT), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.T == 0) return e;
+  const size_t rows = (size_t)p.B * p.T * p.H_qk;
+  const size_t rpb = 256 / (DK / 4);
+  hipLaunchKernelGGL((backward_reduce_kernel<DK, BF16>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+                     p);
+  return hipGetLastError();
+}
+
+template <int DK, bool BF16>
+hipError_t launch_dk(const BackwardParams &p, hipStream_t st) {
+  return bwd_cb(p.d_v) == 32 ? launch_t<DK, 32, BF16>(p, st) : launch_t<DK, 16, BF16>(p, st);
+}
+
+}  // namespace
+
+// This translation unit holds the instances of one dtype (GDN2_BWD_BF16).
+#if GDN2_BWD_BF16
+hipError_t launch_backward_bf16(const BackwardParams &p, int d_k, hipStream_t st) {
+  constexpr bool BF16 = true;
+#else
+hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st) {
+  constexpr bool BF16 = false;
+#endif
+  switch (d_k) {
+    case 16: return launch_dk<16, BF16>(p, st);
+    case 32: return launch_dk<32, BF16>(p, st);
+    case 64: return launch_dk<64, BF16>(p, st);
+    case 128: return launch_dk<128, BF16>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+#if GDN2_BWD_BF16
+hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st);
+
+size_t backward_workspace_bytes(int B, int T, int H_v, int d_k, int d_v) {
+  const size_t nsub = ((size_t)T + kSub - 1) / kSub;
+  const size_t ncb = (size_t)d_v / bwd_cb(d_v);
+  const size_t ck = (size_t)B * H_v * nsub * d_k * d_v * 4;
+  const size_t part = ncb * (size_t)B * T * H_v * 4 * d_k * 4;
+  return align256(ck) + align256(part);
+}
+
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  BackwardParams p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.a = a.a; p.b = a.b; p.w = a.w; p.S0 = a.S0;
+  p.dO = a.dO; p.dST = a.dST;
+  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.da = a.da; p.db = a.db; p.dw = a.dw; p.dS0 = a.dS0;
+  p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
+  const size_t nsub = ((size_t)a.T + kSub - 1) / kSub;
+  const size_t ck = (size_t)a.B * a.H_v * nsub * a.d_k * a.d_v * 4;
+  p.ck = reinterpret_cast<float *>(a.workspace);
+  p.part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck));
+  return a.bf16 ? launch_backward_bf16(p, a.d_k, st) : launch_backward_f32(p, a.d_k, st);
+}
+#endif
+
+}  // namespace gdn2

@@ -53,6 +53,35 @@ struct PrefillPlan {
 // inverse cumulative decay, so this bounds every such factor by e^60.
 constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
 
+// Backward pass (gradients of the recurrence); see gdn2_chunk_backward.
+struct BackwardArgs {
+  int B, T, H_qk, H_v, d_k, d_v;
+  bool bf16;
+  const void *q, *k, *v;
+  const float *a, *b, *w, *S0;
+  const void *dO;
+  const float *dST;
+  void *dq, *dk, *dv;
+  float *da, *db, *dw, *dS0;
+  void *workspace;  // backward_workspace_bytes() bytes, 256-byte aligned
+};
+
+// Kernel parameters: the arguments plus the two workspace regions (state
+// checkpoints, and per column block key-side partial sums).
+struct BackwardParams {
+  const void *q, *k, *v;
+  const float *a, *b, *w, *S0;
+  const void *dO;
+  const float *dST;
+  void *dq, *dk, *dv;
+  float *da, *db, *dw, *dS0;
+  float *ck, *part;
+  int B, T, H_qk, H_v, d_v;
+};
+
+size_t backward_workspace_bytes(int B, int T, int H_v, int d_k, int d_v);
+hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream);
 PrefillPlan prefill_plan(const PrefillArgs &p);

@@ -168,6 +168,43 @@ gdn2_status gdn2_decode_step(const gdn2_desc *desc, const void *q, const void *k
                              const float *a, const float *b, const float *w, float *S, void *o,
                              void *stream);
 
+/* Backward pass of gdn2_chunk_forward: the gradients of a loss with respect
+ * to every input, given its gradients dO = dLoss/do and dS_T = dLoss/dS_T.
+ * The pages define no backward pass; training the layer (the Gated
+ * DeltaNet-2 post on tilnote.io reports a 1.3B-parameter model trained on
+ * 100B tokens) needs the exact derivative of the forward map above, which
+ * is what this computes (reverse mode through the per-token recurrence).
+ *
+ * Arguments (all device pointers, caller-owned, contiguous row-major):
+ *   desc : as for gdn2_chunk_forward. The chunk length is checked as there
+ *          but does not change the method or the result.
+ *   q, k, v, a, b, w, S0 : the forward call's inputs (S0 may be NULL: zero).
+ *   dO   : [B, T, H_v, d_v] in the input dtype.
+ *   dS_T : [B, H_v, d_k, d_v] fp32, or NULL (zero: S_T unused by the loss).
+ *   dq, dk : [B, T, H_qk, d_k] in the input dtype; a query/key head shared by
+ *          several value heads gets the sum of their gradients.
+ *   dv   : [B, T, H_v, d_v] in the input dtype.
+ *   da, db : [B, T, H_v, d_k] fp32.   dw : [B, T, H_v, d_v] fp32.
+ *   dS0  : [B, H_v, d_k, d_v] fp32, or NULL (not written). It may be the
+ *          same pointer as dS_T (in place), but not a partial overlap.
+ *   workspace : gdn2_chunk_backward_workspace_bytes(desc) bytes (fp32 state
+ *          checkpoints every 8 tokens and per 32-column block key-side
+ *          partial sums: about (d_k * d_v / 8 + 16 * d_k * d_v / 32) * 4 bytes
+ *          per token and value head), 256-byte aligned; NULL only when that
+ *          size is 0. Contents on return are unspecified.
+ * Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums; all
+ * arithmetic is fp32. The result is deterministic (no atomics).
+ * Errors: as for gdn2_chunk_forward; a missing required pointer is
+ * GDN2_ERR_NULL_POINTER, a small or misaligned workspace GDN2_ERR_WORKSPACE /
+ * GDN2_ERR_BAD_SHAPE, and an output or the workspace overlapping an input,
+ * another output or each other GDN2_ERR_ALIAS. */
+size_t gdn2_chunk_backward_workspace_bytes(const gdn2_desc *desc);
+gdn2_status gdn2_chunk_backward(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                const float *a, const float *b, const float *w, const float *S0,
+                                const void *dO, const float *dS_T, void *dq, void *dk, void *dv, float *da,
+                                float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *gdn2_status_string(gdn2_status status);
 

@@ -202,3 +202,58 @@ def test_decode_argument_errors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         g.load(str(tmp_path / "nope.so"))
+
+
+def bwd(desc, ptrs=None, ws=0, ws_bytes=0):
+    # q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0
+    p = ptrs or [FAKE + i * (1 << 30) for i in range(16)]
+    return g.gdn2_chunk_backward(desc, *p, ws, ws_bytes, 0)
+
+
+def test_backward_workspace_query_and_argument_errors():
+    """Workspace: fp32 checkpoints every 8 tokens (d_k x d_v per head) plus four
+    d_k-vectors per token, head and 32-column block; errors before any launch."""
+    d = g.make_desc(2, 20, 1, 2, 64, 64, 64, g.GDN2_BF16)
+    nsub, ncb = 3, 2
+    ck = 2 * 2 * nsub * 64 * 64 * 4
+    part = ncb * 2 * 20 * 2 * 4 * 64 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    need = g.gdn2_chunk_backward_workspace_bytes(d)
+    assert need == up(ck) + up(part)
+    assert g.gdn2_chunk_backward_workspace_bytes(None) == 0
+    assert g.gdn2_chunk_backward_workspace_bytes(g.make_desc(1, 0, 1, 1, 16, 16, 16, 0)) == 0
+    ws = FAKE + 40 * (1 << 30)
+    assert bwd(None) == g.GDN2_ERR_NULL_POINTER
+    assert bwd(g.make_desc(2, 20, 1, 2, 96, 64, 64, 1), ws=ws, ws_bytes=need) == g.GDN2_ERR_UNSUPPORTED
+    assert bwd(d) == g.GDN2_ERR_WORKSPACE
+    assert bwd(d, ws=ws, ws_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
+    assert bwd(d, ws=ws + 16, ws_bytes=need) == g.GDN2_ERR_BAD_SHAPE  # workspace needs 256-byte alignment
+    assert bwd(g.make_desc(0, 20, 1, 2, 64, 64, 64, 1), [0] * 16) == g.GDN2_OK  # empty batch
+    base = [FAKE + i * (1 << 30) for i in range(16)]
+    for i in (0, 1, 2, 3, 4, 5, 7, 9, 10, 11, 12, 13, 14):  # required pointers
+        p = list(base)
+        p[i] = 0
+        assert bwd(d, p, ws, need) == g.GDN2_ERR_NULL_POINTER, i
+    for i in (6, 8, 15):  # S0, dS_T, dS0 are optional
+        p = list(base)
+        p[i] = 0
+        # the call would launch; only check that the pointer checks pass by
+        # making a later check fail (misaligned dq)
+        p[9] += 4
+        assert bwd(d, p, ws, need) == g.GDN2_ERR_BAD_SHAPE, i
+    p = list(base)
+    p[12] += 8
+    assert bwd(d, p, ws, need) == g.GDN2_ERR_BAD_SHAPE
+    for i in range(9):  # an output over an input
+        for o in (9, 11, 12, 15):
+            p = list(base)
+            p[o] = p[i] + 16
+            assert bwd(d, p, ws, need) == g.GDN2_ERR_ALIAS, (i, o)
+    p = list(base)
+    p[10] = p[9] + 256  # two outputs overlapping
+    assert bwd(d, p, ws, need) == g.GDN2_ERR_ALIAS
+    assert bwd(d, base, base[3] + 256, need) == g.GDN2_ERR_ALIAS  # workspace over an input
+    assert bwd(d, base, base[13] + 256, need) == g.GDN2_ERR_ALIAS  # ... over an output
+    p = list(base)
+    p[15] = p[8] + 64  # dS0 partially over dS_T
+    assert bwd(d, p, ws, need) == g.GDN2_ERR_ALIAS

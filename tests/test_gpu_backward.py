@@ -1,0 +1,135 @@
+"""Parity of the HIP backward pass (gdn2_chunk_backward) with the fp64 oracle's
+gradients (oracle.backward, pinned in test_oracle_backward.py).
+
+Every gradient tensor is compared normwise (max|x - ref| / max|ref|) against
+the oracle fed the exact values the GPU sees, at the forward's tolerances:
+1e-4 for fp32 inputs, 2e-2 for bf16 inputs (whose dq, dk, dv are rounded to
+bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_83_amd as g
+import oracle
+from gated_delta_rule_83_amd import inputs as gi
+from tests.parity import TOL, normwise, rand_inputs, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "da", "db", "dw", "dS0")
+
+
+def upstream(rng, d, dtype, with_dst=True):
+    B, T, Hv, dv = d["v"].shape
+    dk = d["a"].shape[3]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dO = torch.from_numpy(rng.standard_normal((B, T, Hv, dv)).astype(np.float32)).to(tdt).to(DEV)
+    dST = (torch.from_numpy(rng.standard_normal((B, Hv, dk, dv)).astype(np.float32)).to(DEV)
+           if with_dst else None)
+    return dO, dST
+
+
+def compare(td, dO, dST, dtype, label, tol=None, grads=None):
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    ref = oracle.backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    tol = TOL[dtype] if tol is None else tol
+    errs = {nm: normwise(to_np(gg[nm]), ref[nm]) for nm in NAMES}
+    print(f"[backward {label} {dtype}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f" tol {tol:g}",
+          flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+    return gg
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)])
+def test_fp32_shapes_ragged_gqa(dk, dv):
+    """fp32 at every head size: several 8-token sub-segments plus a ragged
+    tail, two value heads per query/key head, random S0 and dS_T."""
+    rng = np.random.default_rng(3000 + dk + 7 * dv)
+    d = rand_inputs(rng, 2, 21, 1, 2, dk, dv)
+    td = gi.to_torch(d, "f32", DEV)
+    dO, dST = upstream(rng, d, "f32")
+    compare(td, dO, dST, "f32", f"dk{dk} dv{dv} T21")
+
+
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 64])
+def test_fp32_lengths_null_state(T):
+    """Sequence lengths around the 8-token sub-segment, S0 and dS_T absent."""
+    rng = np.random.default_rng(3100 + T)
+    d = rand_inputs(rng, 1, T, 2, 2, 32, 32, with_s0=False)
+    td = gi.to_torch(d, "f32", DEV)
+    dO, _ = upstream(rng, d, "f32", with_dst=False)
+    compare(td, dO, None, "f32", f"T{T} no S0/dS_T")
+
+
+def test_bf16_layer_shape_scaled():
+    """The 1.3B-class layer's distributions (decay pre-activation N(-4,1)) at B2 H4 T520."""
+    c = gi.scaled(1, B=2, T=520, H_qk=4, H_v=4)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(3200)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    compare(td, dO, dST, "bf16", "c1-scaled")
+
+
+def test_bf16_grouped_heads_hard_erases():
+    """Grouped heads (2 value heads per query/key head) and 1% hard erases."""
+    c = gi.scaled(3, B=1, T=300, H_qk=2, H_v=4)
+    d = gi.make_inputs(c)
+    c2 = gi.scaled(2, B=1, T=300, H_qk=2, H_v=4)
+    d["b"] = gi.make_inputs(c2)["b"]  # b with the hard-erase positions
+    rng = np.random.default_rng(3300)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    compare(td, dO, dST, "bf16", "grouped+hard-erase")
+
+
+def test_zero_length_passes_state_gradient():
+    rng = np.random.default_rng(3400)
+    d = rand_inputs(rng, 2, 0, 1, 2, 64, 64)
+    td = gi.to_torch(d, "f32", DEV)
+    dST = torch.from_numpy(rng.standard_normal((2, 2, 64, 64)).astype(np.float32)).to(DEV)
+    dO = torch.empty((2, 0, 2, 64), device=DEV)
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    assert torch.equal(gg["dS0"], dST)
+
+
+def test_deterministic_and_in_place_state_gradient():
+    """Two runs are bitwise equal; dS0 written over dS_T gives the same values."""
+    rng = np.random.default_rng(3500)
+    d = rand_inputs(rng, 2, 40, 2, 2, 128, 128)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    g1 = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    g2 = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    buf = dST.clone()
+    g3 = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, buf,
+                          grads={"dS0": buf})
+    torch.cuda.synchronize()
+    for nm in NAMES:
+        assert torch.equal(g1[nm], g2[nm]), nm
+        assert torch.equal(g1[nm], g3[nm]), nm
+    assert g3["dS0"].data_ptr() == buf.data_ptr()
+
+
+def test_full_layer_shape_sampled_heads():
+    """B8 T4096 H16 d128 bf16 (the layer workload's prefill shape): the whole
+    backward on the GPU, two (sequence, head) pairs against the oracle."""
+    c = gi.config(1)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(3600)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    for (n, h) in ((0, 0), (7, 13)):
+        sl = lambda x: None if x is None else x[n:n + 1, :, h:h + 1]
+        ref = oracle.backward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]), None,
+                              sl(dO), dST[n:n + 1, h:h + 1], nthreads=1)
+        errs = {nm: normwise(to_np(gg[nm][n:n + 1, :, h:h + 1] if nm != "dS0" else gg[nm][n:n + 1, h:h + 1]),
+                             ref[nm]) for nm in NAMES}
+        print(f"[backward full n{n} h{h}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+        bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+        assert not bad, bad
