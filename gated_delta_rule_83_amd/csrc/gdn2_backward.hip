@@ -29,9 +29,10 @@
 // sum over the waves in LDS (deterministic, no atomics).
 //
 // Memory: phase 1 runs the recurrence forward and stores the state at the
-// start of every kSub-token sub-segment (fp32, in the workspace); phase 2
-// walks the sub-segments backward, recomputes a sub-segment's kSub + 1
-// states into registers from its checkpoint, and runs the adjoint over it.
+// start of every kSub-token sub-segment and every token's k-read (fp32, in
+// the workspace); phase 2 walks the sub-segments backward, rebuilds a
+// sub-segment's kSub + 1 states into registers from its checkpoint and the
+// stored k-reads (no key sums), and runs the adjoint over it.
 // Inputs of a sub-segment are staged in LDS (one set of loads per
 // workgroup, requested one sub-segment ahead). Key-side sums go to the
 // workspace per column block and are added up by backward_reduce_kernel,
@@ -49,7 +50,7 @@ hipError_t launch_backward_bf16(const BackwardParams &p, int d_k, hipStream_t st
 
 namespace {
 
-constexpr int kSub = 8;  // tokens per sub-segment (the register history)
+constexpr int kSub = 4;  // tokens per sub-segment (the register history)
 
 template <int DK, int CB>
 struct BwdCfg {
@@ -68,7 +69,7 @@ template <int DK, int CB>
 struct BwdSmem {
   using Cf = BwdCfg<DK, CB>;
   alignas(16) float kqae[Cf::L][4][DK];         // k, q, a, e = b*k of the sub-segment's tokens
-  alignas(16) float col[Cf::L][4][CB];          // u = w*v, v, w, dO of the workgroup's columns
+  alignas(16) float col[Cf::L][5][CB];          // u = w*v, v, w, dO, k-read r of the workgroup's columns
   alignas(16) float red[Cf::NWV][Cf::L][4][DK]; // per-wave key-side sums (dq, dk part, e part, da)
   alignas(16) float du[Cf::L][CB];              // du per token and column
 };
@@ -91,12 +92,27 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// Lane exchange of the column reduce-scatter (gfx950 v_permlane32_swap /
+// v_permlane16_swap): the sum of the two swapped registers. Written as asm
+// with both registers read and written: with the compiler builtins, the
+// second result was taken from the first register (the sum came out as
+// twice the first). The leading s_nop covers the wait after a VALU write of
+// the operands, which the compiler does not see through the asm.
+template <int W>
+__device__ __forceinline__ float swap_sum(float a, float b) {
+  if constexpr (W == 32)
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
 // Raw inputs of one sub-segment, held by a thread between its request and
 // its LDS store.
 template <int DK, int CB>
 struct Stage {
   floatx4 k[BwdCfg<DK, CB>::KIT], q[BwdCfg<DK, CB>::KIT], a[BwdCfg<DK, CB>::KIT], b[BwdCfg<DK, CB>::KIT];
-  floatx4 v, w, d;
+  floatx4 v, w, d, r;
 };
 
 }  // namespace
@@ -133,6 +149,8 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   const size_t qk_t = (size_t)p.H_qk * DK, ab_t = (size_t)p.H_v * DK, vw_t = (size_t)p.H_v * d_v;
   const size_t s_off = (size_t)unit * DK * d_v;
   float *ckp = p.ck + ((size_t)unit * ncb + cb) * (size_t)nsub * (DK * CB) + (size_t)tid * (2 * KPL);
+  // k-reads of the block's columns, [token][d_v] per (n, h)
+  float *rh = p.rk + (size_t)unit * T * d_v + cb * CB;
 
   // Request sub-segment `sub`'s inputs into registers; tokens past the end
   // are identity steps (a = 1, everything else 0).
@@ -155,6 +173,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
       st.w = ok ? *reinterpret_cast<const floatx4 *>(wh + t * vw_t + 4 * cq) : zero4();
       st.d = ok && backward ? E::ld4(dOh + t * vw_t + 4 * cq) : zero4();
+      st.r = ok && backward ? *reinterpret_cast<const floatx4 *>(rh + (size_t)t * d_v + 4 * cq) : zero4();
     }
   };
   auto stash = [&](const Stage<DK, CB> &st) {
@@ -175,6 +194,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       *reinterpret_cast<floatx4 *>(&sm.col[tt][1][4 * cq]) = st.v;
       *reinterpret_cast<floatx4 *>(&sm.col[tt][2][4 * cq]) = st.w;
       *reinterpret_cast<floatx4 *>(&sm.col[tt][3][4 * cq]) = st.d;
+      *reinterpret_cast<floatx4 *>(&sm.col[tt][4][4 * cq]) = st.r;
     }
   };
   auto lds_keys = [&](int tt, int which, float (&x)[KPL]) {
@@ -241,6 +261,8 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
     for (int tt = 0; tt < L; ++tt) {
       float r0, r1;
       fwd_step(tt, s, r0, r1);
+      if (kg == 0 && sub * L + tt < T)
+        *reinterpret_cast<floatx2 *>(rh + (size_t)(sub * L + tt) * d_v + lcol) = floatx2{r0, r1};
     }
   }
 
@@ -256,32 +278,49 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       lam[e][0] = lam[e][1] = 0.f;
     }
   }
-  if (nsub > 0) request(nsub - 1, st, true);
+  // the checkpoint of the next sub-segment to process, requested one ahead
+  floatx2 ckn[KPL];
+  auto request_ck = [&](int sub) {
+    const float *ck = ckp + (size_t)sub * (DK * CB);
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) ckn[e] = *reinterpret_cast<const floatx2 *>(ck + 2 * e);
+  };
+  // the k-reads of phase 1 were stored by other waves of the workgroup: the
+  // barrier (workgroup-scope release and acquire) makes them visible
+  __syncthreads();
+  if (nsub > 0) {
+    request(nsub - 1, st, true);
+    request_ck(nsub - 1);
+  }
   for (int sub = nsub - 1; sub >= 0; --sub) {
     __syncthreads();  // the previous sub-segment's readers (and the sums below) are done
     stash(st);
     __syncthreads();
-    if (sub > 0) request(sub - 1, st, true);
-
     // the sub-segment's states: hs[tt] = S before token tt, hs[L] = S after the last
-    float hs[L + 1][KPL][2], rr[L][2];
-    {
-      const float *ck = ckp + (size_t)sub * (DK * CB);
+    float hs[L + 1][KPL][2];
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const floatx2 x = *reinterpret_cast<const floatx2 *>(ck + 2 * e);
-        hs[0][e][0] = x[0];
-        hs[0][e][1] = x[1];
-      }
+    for (int e = 0; e < KPL; ++e) {
+      hs[0][e][0] = ckn[e][0];
+      hs[0][e][1] = ckn[e][1];
     }
+    if (sub > 0) {
+      request(sub - 1, st, true);
+      request_ck(sub - 1);
+    }
+    // (the k-reads come from phase 1: no key sums here)
 #pragma unroll
     for (int tt = 0; tt < L; ++tt) {
+      float kk[KPL], aa[KPL], ee[KPL];
+      lds_keys(tt, 0, kk);
+      lds_keys(tt, 2, aa);
+      lds_keys(tt, 3, ee);
+      const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
+      const float r0 = sm.col[tt][4][lcol], r1 = sm.col[tt][4][lcol + 1];
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
-        hs[tt + 1][e][0] = hs[tt][e][0];
-        hs[tt + 1][e][1] = hs[tt][e][1];
+        hs[tt + 1][e][0] = fmaf(kk[e], u0, fmaf(-ee[e], r0, hs[tt][e][0] * aa[e]));
+        hs[tt + 1][e][1] = fmaf(kk[e], u1, fmaf(-ee[e], r1, hs[tt][e][1] * aa[e]));
       }
-      fwd_step(tt, hs[tt + 1], rr[tt][0], rr[tt][1]);
     }
 
 #pragma unroll
@@ -293,6 +332,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       lds_keys(tt, 3, ee);
       const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
       const float d0 = sm.col[tt][3][lcol], d1 = sm.col[tt][3][lcol + 1];
+      const float r0 = sm.col[tt][4][lcol], r1 = sm.col[tt][4][lcol + 1];
       // x[0] dq part, x[1] dk part (u L + a * dr S_{t-1}), x[2] sum_j r_j L (de = -x[2]), x[3] da
       float x[4][KPL];
       float pu0 = 0.f, pu1 = 0.f, pe0 = 0.f, pe1 = 0.f;
@@ -310,7 +350,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const float dr0 = -row_sum16(pe0), dr1 = -row_sum16(pe1);
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
-        x[2][e] = fmaf(lam[e][0], rr[tt][0], lam[e][1] * rr[tt][1]);
+        x[2][e] = fmaf(lam[e][0], r0, lam[e][1] * r1);
         const float p2 = fmaf(lam[e][0], u0, lam[e][1] * u1);
         lam[e][0] = fmaf(kk[e], dr0, lam[e][0]);
         lam[e][1] = fmaf(kk[e], dr1, lam[e][1]);
@@ -321,23 +361,18 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         lam[e][1] *= aa[e];
       }
       // reduce-scatter over the four column pairs: lane group c4 ends with
-      // sum x[c4][.] of the wave's 8 columns
-      const bool hi1 = (c4 & 2) != 0, hi0 = (c4 & 1) != 0;
+      // sum x[c4][.] of the wave's 8 columns. swap32(A, B) gives
+      // [A lanes 0-31, B lanes 0-31] and [A lanes 32-63, B lanes 32-63], so
+      // their sum is, in the lower half, A plus the upper half's A, and in
+      // the upper half, B plus the lower half's B; swap16 does the same
+      // between rows 0/1 and 2/3.
       float y[2][KPL];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          const float send = hi1 ? x[m][e] : x[2 + m][e];
-          const float keep = hi1 ? x[2 + m][e] : x[m][e];
-          y[m][e] = keep + __shfl_xor(send, 32, 64);
-        }
+        for (int e = 0; e < KPL; ++e) y[m][e] = swap_sum<32>(x[m][e], x[2 + m][e]);
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const float send = hi0 ? y[0][e] : y[1][e];
-        const float keep = hi0 ? y[1][e] : y[0][e];
-        sm.red[wave][tt][c4][key0 + e] = keep + __shfl_xor(send, 16, 64);
-      }
+      for (int e = 0; e < KPL; ++e) sm.red[wave][tt][c4][key0 + e] = swap_sum<16>(y[0][e], y[1][e]);
       if (kg == 0) {
         sm.du[tt][lcol] = du0;
         sm.du[tt][lcol + 1] = du1;
@@ -468,7 +503,8 @@ size_t backward_workspace_bytes(int B, int T, int H_v, int d_k, int d_v) {
   const size_t ncb = (size_t)d_v / bwd_cb(d_v);
   const size_t ck = (size_t)B * H_v * nsub * d_k * d_v * 4;
   const size_t part = ncb * (size_t)B * T * H_v * 4 * d_k * 4;
-  return align256(ck) + align256(part);
+  const size_t rk = (size_t)B * H_v * T * d_v * 4;
+  return align256(ck) + align256(part) + align256(rk);
 }
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
@@ -481,7 +517,9 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   const size_t nsub = ((size_t)a.T + kSub - 1) / kSub;
   const size_t ck = (size_t)a.B * a.H_v * nsub * a.d_k * a.d_v * 4;
   p.ck = reinterpret_cast<float *>(a.workspace);
+  const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * a.B * a.T * a.H_v * 4 * a.d_k * 4;
   p.part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck));
+  p.rk = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck) + align256(part));
   return a.bf16 ? launch_backward_bf16(p, a.d_k, st) : launch_backward_f32(p, a.d_k, st);
 }
 #endif

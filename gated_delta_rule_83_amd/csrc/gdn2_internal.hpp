@@ -66,8 +66,8 @@ struct BackwardArgs {
   void *workspace;  // backward_workspace_bytes() bytes, 256-byte aligned
 };
 
-// Kernel parameters: the arguments plus the two workspace regions (state
-// checkpoints, and per column block key-side partial sums).
+// Kernel parameters: the arguments plus the three workspace regions (state
+// checkpoints, per column block key-side partial sums, per-token k-reads).
 struct BackwardParams {
   const void *q, *k, *v;
   const float *a, *b, *w, *S0;
@@ -75,7 +75,7 @@ struct BackwardParams {
   const float *dST;
   void *dq, *dk, *dv;
   float *da, *db, *dw, *dS0;
-  float *ck, *part;
+  float *ck, *part, *rk;
   int B, T, H_qk, H_v, d_v;
 };
 

@@ -211,15 +211,17 @@ def bwd(desc, ptrs=None, ws=0, ws_bytes=0):
 
 
 def test_backward_workspace_query_and_argument_errors():
-    """Workspace: fp32 checkpoints every 8 tokens (d_k x d_v per head) plus four
-    d_k-vectors per token, head and 32-column block; errors before any launch."""
+    """Workspace: fp32 checkpoints every 4 tokens (d_k x d_v per head), four
+    d_k-vectors per token, head and 32-column block, and one d_v-vector of
+    k-reads per token and head; errors before any launch."""
     d = g.make_desc(2, 20, 1, 2, 64, 64, 64, g.GDN2_BF16)
-    nsub, ncb = 3, 2
+    nsub, ncb = 5, 2  # checkpoints every 4 tokens
     ck = 2 * 2 * nsub * 64 * 64 * 4
     part = ncb * 2 * 20 * 2 * 4 * 64 * 4
+    rk = 2 * 2 * 20 * 64 * 4
     up = lambda x: (x + 255) // 256 * 256
     need = g.gdn2_chunk_backward_workspace_bytes(d)
-    assert need == up(ck) + up(part)
+    assert need == up(ck) + up(part) + up(rk)
     assert g.gdn2_chunk_backward_workspace_bytes(None) == 0
     assert g.gdn2_chunk_backward_workspace_bytes(g.make_desc(1, 0, 1, 1, 16, 16, 16, 0)) == 0
     ws = FAKE + 40 * (1 << 30)
