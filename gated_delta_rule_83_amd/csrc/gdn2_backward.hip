@@ -74,37 +74,94 @@ struct BwdSmem {
   alignas(16) float du[Cf::L][CB];              // du per token and column
 };
 
-// x from lane (l + R) mod 16 of this lane's 16-lane row (DPP row_ror:R). The
-// empty asm keeps separate rotations separate instructions.
-template <int R>
-__device__ __forceinline__ float row_ror(float x) {
-  asm volatile("" : "+v"(x));
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xf,
-                                                               0xf, false));
+// Sums over the 16 lanes of the row, of two or four independent values at
+// once: x += (x from lane (l + R) mod 16) for R = 8, 4, 2, 1 (DPP row_ror),
+// every lane ending with the same value (each step adds two values that are
+// equal in both lanes of a rotation pair). One asm block interleaves the
+// chains, so that the wait a DPP read needs after the VALU write of its
+// source is filled by the other chains (four chains: three instructions
+// apart; two chains: one s_nop per round); the leading s_nop covers the
+// writes before the block, which the compiler does not see through it.
+__device__ __forceinline__ void row_sum16x4(float &x0, float &x1, float &x2, float &x3) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %3, %3 row_ror:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
 }
-// Sum over the 16 lanes of the row; every lane gets the same value (each
-// step adds two values that are equal in both lanes of a rotation pair).
-__device__ __forceinline__ float row_sum16(float x) {
-  x += row_ror<8>(x);
-  x += row_ror<4>(x);
-  x += row_ror<2>(x);
-  x += row_ror<1>(x);
-  return x;
+__device__ __forceinline__ void row_sum16x2(float &x0, float &x1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(x0), "+v"(x1));
 }
 
 // Lane exchange of the column reduce-scatter (gfx950 v_permlane32_swap /
-// v_permlane16_swap): the sum of the two swapped registers. Written as asm
-// with both registers read and written: with the compiler builtins, the
-// second result was taken from the first register (the sum came out as
-// twice the first). The leading s_nop covers the wait after a VALU write of
-// the operands, which the compiler does not see through the asm.
+// v_permlane16_swap), N pairs at once: after swap32(A, B), A holds
+// [A lanes 0-31, B lanes 0-31] and B [A lanes 32-63, B lanes 32-63] (swap16
+// likewise between rows 0/1 and 2/3), so A + B is, in the lower half, A plus
+// the upper half's A, and in the upper half B plus the lower half's B.
+// Written as asm with both registers read and written: with the compiler
+// builtins, the second result was taken from the first register (the sum
+// came out as twice the first). One leading s_nop per block covers the wait
+// after a VALU write of the operands.
 template <int W>
-__device__ __forceinline__ float swap_sum(float a, float b) {
+__device__ __forceinline__ void swap1(float &a, float &b) {
   if constexpr (W == 32)
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   else
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  return a + b;
+}
+template <int W>
+__device__ __forceinline__ void swap4(float &a0, float &b0, float &a1, float &b1, float &a2, float &b2, float &a3,
+                                      float &b3) {
+  if constexpr (W == 32)
+    asm volatile(
+        "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\t"
+        "v_permlane32_swap_b32 %4, %5\n\tv_permlane32_swap_b32 %6, %7"
+        : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2), "+v"(a3), "+v"(b3));
+  else
+    asm volatile(
+        "s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\t"
+        "v_permlane16_swap_b32 %4, %5\n\tv_permlane16_swap_b32 %6, %7"
+        : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2), "+v"(a3), "+v"(b3));
+}
+// a[i] <- a[i] + b[i] summed across the exchange above, for N values.
+template <int W, int N>
+__device__ __forceinline__ void swap_sum_n(float (&a)[N], float (&b)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) swap4<W>(a[i], b[i], a[i + 1], b[i + 1], a[i + 2], b[i + 2], a[i + 3], b[i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) swap1<W>(a[i], b[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] += b[i];
 }
 
 // Raw inputs of one sub-segment, held by a thread between its request and
@@ -225,8 +282,9 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       x0 = fmaf(kk[e], s[e][0], x0);
       x1 = fmaf(kk[e], s[e][1], x1);
     }
-    r0 = row_sum16(x0);
-    r1 = row_sum16(x1);
+    row_sum16x2(x0, x1);
+    r0 = x0;
+    r1 = x1;
     const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
@@ -346,8 +404,8 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         pe0 = fmaf(lam[e][0], ee[e], pe0);
         pe1 = fmaf(lam[e][1], ee[e], pe1);
       }
-      const float du0 = row_sum16(pu0), du1 = row_sum16(pu1);
-      const float dr0 = -row_sum16(pe0), dr1 = -row_sum16(pe1);
+      row_sum16x4(pu0, pu1, pe0, pe1);
+      const float du0 = pu0, du1 = pu1, dr0 = -pe0, dr1 = -pe1;
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         x[2][e] = fmaf(lam[e][0], r0, lam[e][1] * r1);
@@ -366,13 +424,19 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       // their sum is, in the lower half, A plus the upper half's A, and in
       // the upper half, B plus the lower half's B; swap16 does the same
       // between rows 0/1 and 2/3.
-      float y[2][KPL];
+      swap_sum_n<32, KPL>(x[0], x[2]);
+      swap_sum_n<32, KPL>(x[1], x[3]);
+      swap_sum_n<16, KPL>(x[0], x[1]);
+      // x[0] now holds the lane group's vector c4 on keys key0 .. key0 + KPL - 1
+      float *dst = &sm.red[wave][tt][c4][key0];
+      if constexpr (KPL >= 4) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int e = 0; e < KPL; e += 4)
+          *reinterpret_cast<floatx4 *>(dst + e) = floatx4{x[0][e], x[0][e + 1], x[0][e + 2], x[0][e + 3]};
+      } else {
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) y[m][e] = swap_sum<32>(x[m][e], x[2 + m][e]);
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) sm.red[wave][tt][c4][key0 + e] = swap_sum<16>(y[0][e], y[1][e]);
+        for (int e = 0; e < KPL; ++e) dst[e] = x[0][e];
+      }
       if (kg == 0) {
         sm.du[tt][lcol] = du0;
         sm.du[tt][lcol + 1] = du1;
