@@ -12,8 +12,10 @@ before the timed region. Per-kernel durations come from HIP events recorded
 on the stream the kernels are launched on.
 
 After the timed steps, the decode workload as stated (1024 successive decode
-steps from a random state) runs once for the decode bandwidth figure, and
-the fp64 oracle runs on the host over the prefill batch for the CPU baseline.
+steps from a random state) runs once for the decode bandwidth figure, the
+backward pass (gdn2_chunk_backward) of the prefill runs a few times for its
+own figure, and the fp64 oracle runs on the host over the prefill batch for
+the CPU baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector ALUs, TFLOP/s
 PREFILL_KERNEL_SOURCES = ["gated_delta_rule_83_amd/csrc/gdn2_prefill.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_device.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_prefill_inst.hip"]
@@ -65,6 +68,20 @@ def decode_algorithmic(c):
     per_head = c.d_k * c.d_v * 4 * 2 + c.d_v * es * 2 + c.d_k * 4 * 2 + c.d_v * 4
     qk = c.B * c.H_qk * c.d_k * es * 2
     return c.B * c.H_v * per_head + qk
+
+
+def backward_algorithmic(c):
+    """Flops of the gradient by the recurrence, per state element and token:
+    the forward states (decay 1, k-read 2, erase 2, write 2) and the adjoint
+    (query read 2+2, du 2, dr 2, erase-gate sum 2, write-gate sum 2, read
+    adjoint 2+3, decay sum 2, decay 1): 27 * d_k * d_v per token and value
+    head. Bytes: inputs, dO and every gradient once."""
+    es = 2 if c.dtype == "bf16" else 4
+    toks = c.B * c.T
+    fl = 27.0 * c.d_k * c.d_v * toks * c.H_v
+    by = toks * (c.H_qk * c.d_k * es * 4 + c.H_v * c.d_v * es * 3 + c.H_v * c.d_k * 4 * 4
+                 + c.H_v * c.d_v * 4 * 2) + 2 * c.B * c.H_v * c.d_k * c.d_v * 4
+    return fl, by
 
 
 def source_digest(paths):
@@ -101,11 +118,13 @@ def read_traffic(digest):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="length of the decode workload leg (default: the workload's 1024)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5,
+                    help="timed launches of the backward pass over the prefill shape (0: skip)")
     ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
     ap.add_argument("--counters", action="store_true",
                     help="for hardware-counter runs: launch the prefill and the decode kernel twice each "
@@ -224,6 +243,42 @@ def main():
     log(f"[bench] decode workload: {dec_steps} steps in {loop_ms:.1f} ms; kernel avg {d_avg * 1e6:.1f} us "
         f"= {d_gbs:.0f} GB/s algorithmic")
 
+    # ---------------------------------------------------------------- backward leg
+    bwd = None
+    if args.backward_steps > 0:
+        gen = torch.Generator(device=dev).manual_seed(5)
+        dO = torch.randn(o.shape, generator=gen, device=dev, dtype=torch.float32).to(o.dtype)
+        dST = torch.randn(S_T.shape, generator=gen, device=dev, dtype=torch.float32)
+        desc = g.make_desc(cp.B, cp.T, cp.H_qk, cp.H_v, cp.d_k, cp.d_v, cp.chunk,
+                           g.GDN2_BF16 if cp.dtype == "bf16" else g.GDN2_F32)
+        bws = torch.empty(g.gdn2_chunk_backward_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+
+        def backward(grads=None):
+            return g.chunk_backward(tp["q"], tp["k"], tp["v"], tp["a"], tp["b"], tp["w"], None, dO, dST,
+                                    grads=grads, workspace=bws, stream=stream)
+
+        grads = backward()
+        backward(grads)
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.backward_steps)]
+        for e0, e1 in bev:
+            e0.record(stream)
+            backward(grads)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        b_ms = [a.elapsed_time(b) for a, b in bev]
+        b_avg = float(np.mean(b_ms)) / 1e3
+        bfl, bby = backward_algorithmic(cp)
+        bwd = {"launches": args.backward_steps, "ms": b_avg * 1e3, "min_ms": min(b_ms),
+               "tokens_per_s": tokens / b_avg, "bound": "alu",
+               "achieved": bfl / b_avg / 1e12, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
+               "frac": bfl / b_avg / 1e12 / FP32_VECTOR_PEAK_TFS, "algorithmic_flops": bfl,
+               "algorithmic_bytes": bby, "workspace_bytes": bws.numel()}
+        log(f"[bench] backward: {b_avg * 1e3:.2f} ms per launch (min {min(b_ms):.2f}), "
+            f"{bfl / b_avg / 1e12:.1f} TFLOP/s algorithmic")
+        del grads, bws
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -256,6 +311,8 @@ def main():
             "workload": (f"prefill B{cp.B} T{cp.T} H_qk{cp.H_qk} H_v{cp.H_v} d_k{cp.d_k} d_v{cp.d_v} "
                          f"chunk{cp.chunk} {cp.dtype} + decode step N{cd.B} H{cd.H_v} d{cd.d_k} fp32 state"),
             "prefill_kernel_us": pre_avg * 1e6,
+            "prefill_kernel_us_median": float(np.median(pre_ms)) * 1e3,
+            "prefill_kernel_us_min": float(min(pre_ms)) * 1e3,
             "decode_kernel_us": float(np.mean(dec_ms)) * 1e3,
         },
         "roofline": {
@@ -280,6 +337,7 @@ def main():
             "frac": d_gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": dbytes,
         },
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

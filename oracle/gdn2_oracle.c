@@ -218,7 +218,7 @@ typedef struct {
 static void run_unit_bwd(const bjob_t *J, int unit, double *hist, double *rs, double *L, double *du,
                          double *dr) {
   const int n = unit / J->Hv, h = unit % J->Hv;
-  const int G = J->Hv / J->Hqk, g = h / G;
+  const int grp = J->Hv / J->Hqk, g = h / grp;
   const int dk = J->dk, dv = J->dv, T = J->T;
   const size_t qk_tok = (size_t)J->Hqk * dk, ab_tok = (size_t)J->Hv * dk, vw_tok = (size_t)J->Hv * dv;
   const size_t ssz = (size_t)dk * dv;
@@ -237,18 +237,18 @@ static void run_unit_bwd(const bjob_t *J, int unit, double *hist, double *rs, do
     const double *vt = J->v + tok * vw_tok + (size_t)h * dv;
     const double *wt = J->w + tok * vw_tok + (size_t)h * dv;
     const double *Sp = hist + (size_t)t * ssz;
-    double *S = hist + (size_t)(t + 1) * ssz;
-    double *r = rs + (size_t)t * dv;
+    double *Sn = hist + (size_t)(t + 1) * ssz;
+    double *rt = rs + (size_t)t * dv;
     for (int i = 0; i < dk; ++i)
-      for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = Sp[(size_t)i * dv + j] * at[i];
-    for (int j = 0; j < dv; ++j) r[j] = 0.0;
+      for (int j = 0; j < dv; ++j) Sn[(size_t)i * dv + j] = Sp[(size_t)i * dv + j] * at[i];
+    for (int j = 0; j < dv; ++j) rt[j] = 0.0;
     for (int i = 0; i < dk; ++i)
-      for (int j = 0; j < dv; ++j) r[j] += S[(size_t)i * dv + j] * kt[i];
+      for (int j = 0; j < dv; ++j) rt[j] += Sn[(size_t)i * dv + j] * kt[i];
     for (int i = 0; i < dk; ++i) {
-      const double e = bt[i] * kt[i];
+      const double eb = bt[i] * kt[i];
       for (int j = 0; j < dv; ++j) {
-        S[(size_t)i * dv + j] -= e * r[j];
-        S[(size_t)i * dv + j] += kt[i] * (wt[j] * vt[j]);
+        Sn[(size_t)i * dv + j] -= eb * rt[j];
+        Sn[(size_t)i * dv + j] += (wt[j] * vt[j]) * kt[i];
       }
     }
   }
@@ -291,10 +291,10 @@ static void run_unit_bwd(const bjob_t *J, int unit, double *hist, double *rs, do
       dr[j] = 0.0;
     }
     for (int i = 0; i < dk; ++i) {
-      const double e = bt[i] * kt[i];
+      const double eb = bt[i] * kt[i];
       for (int j = 0; j < dv; ++j) {
         du[j] += L[(size_t)i * dv + j] * kt[i];
-        dr[j] -= L[(size_t)i * dv + j] * e;
+        dr[j] -= L[(size_t)i * dv + j] * eb;
       }
     }
     for (int j = 0; j < dv; ++j) {

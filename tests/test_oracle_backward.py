@@ -155,7 +155,7 @@ BWD_MUTANTS = [
      "for (int j = 0; j < dv; ++j) s += Sp[(size_t)i * dv + j] * dOt[j];"),
     ("bwd_no_query_adjoint", "for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] += qt[i] * dOt[j];",
      "for (int j = 0; j < dv; ++j) L[(size_t)i * dv + j] += 0.0 * qt[i] * dOt[j];"),
-    ("bwd_erase_read_sign", "dr[j] -= L[(size_t)i * dv + j] * e;", "dr[j] += L[(size_t)i * dv + j] * e;"),
+    ("bwd_erase_read_sign", "dr[j] -= L[(size_t)i * dv + j] * eb;", "dr[j] += L[(size_t)i * dv + j] * eb;"),
     ("bwd_dv_ungated", "dvt[j] = du[j] * wt[j];", "dvt[j] = du[j];"),
     ("bwd_db_without_key", "dbt[i] = de * kt[i];", "dbt[i] = de;"),
     ("bwd_dk_no_erase_term", "dkt[i] = kw + de * bt[i];", "dkt[i] = kw;"),
