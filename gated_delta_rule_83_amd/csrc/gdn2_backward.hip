@@ -58,20 +58,34 @@ struct BwdCfg {
   static constexpr int NT = 64 * NWV;  // threads
   static constexpr int KPL = DK / 16;  // key channels per lane
   static constexpr int L = kSub;
+  static constexpr int L1 = 16;                           // tokens per forward-phase stage
   static constexpr int NKS = L * DK / 4;                  // key quads staged per sub-segment
   static constexpr int KIT = (NKS + NT - 1) / NT;         // ... per thread
   static constexpr int NCS = L * CB / 4;                  // column quads staged per sub-segment
-  static_assert(NCS <= NT, "one column quad per thread at most");
+  static constexpr int NKS1 = L1 * DK / 4;                // ... per forward-phase stage
+  static constexpr int KIT1 = (NKS1 + NT - 1) / NT;
+  static constexpr int NCS1 = L1 * CB / 4;
+  static_assert(NCS <= NT && NCS1 <= NT, "one column quad per thread at most");
+  static_assert(L1 % L == 0, "checkpoints at sub-segment starts");
   static_assert(CB == 16 || CB == 32, "column block");
 };
 
 template <int DK, int CB>
 struct BwdSmem {
   using Cf = BwdCfg<DK, CB>;
-  alignas(16) float kqae[Cf::L][4][DK];         // k, q, a, e = b*k of the sub-segment's tokens
-  alignas(16) float col[Cf::L][5][CB];          // u = w*v, v, w, dO, k-read r of the workgroup's columns
-  alignas(16) float red[Cf::NWV][Cf::L][4][DK]; // per-wave key-side sums (dq, dk part, e part, da)
-  alignas(16) float du[Cf::L][CB];              // du per token and column
+  union {
+    struct {  // forward phase: one L1-token stage
+      alignas(16) float kae[Cf::L1][3][DK];         // k, a, e = b*k
+      alignas(16) float u[Cf::L1][CB];              // u = w*v of the workgroup's columns
+      alignas(16) float r[Cf::L1][CB];              // k-reads of the stage, written out as rows
+    } f;
+    struct {  // backward phase: one sub-segment
+      alignas(16) float kqae[Cf::L][4][DK];         // k, q, a, e = b*k of the sub-segment's tokens
+      alignas(16) float col[Cf::L][5][CB];          // u = w*v, v, w, dO, k-read r of the block's columns
+      alignas(16) float red[Cf::NWV][Cf::L][4][DK]; // per-wave key-side sums (dq, dk part, e part, da)
+      alignas(16) float du[Cf::L][CB];              // du per token and column
+    } b;
+  };
 };
 
 // Sums over the 16 lanes of the row, of two or four independent values at
@@ -167,6 +181,11 @@ __device__ __forceinline__ void swap_sum_n(float (&a)[N], float (&b)[N]) {
 // Raw inputs of one sub-segment, held by a thread between its request and
 // its LDS store.
 template <int DK, int CB>
+struct Stage1 {
+  floatx4 k[BwdCfg<DK, CB>::KIT1], a[BwdCfg<DK, CB>::KIT1], b[BwdCfg<DK, CB>::KIT1];
+  floatx4 v, w;
+};
+template <int DK, int CB>
 struct Stage {
   floatx4 k[BwdCfg<DK, CB>::KIT], q[BwdCfg<DK, CB>::KIT], a[BwdCfg<DK, CB>::KIT], b[BwdCfg<DK, CB>::KIT];
   floatx4 v, w, d, r;
@@ -205,7 +224,22 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   const ET *dOh = (const ET *)p.dO + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
   const size_t qk_t = (size_t)p.H_qk * DK, ab_t = (size_t)p.H_v * DK, vw_t = (size_t)p.H_v * d_v;
   const size_t s_off = (size_t)unit * DK * d_v;
-  float *ckp = p.ck + ((size_t)unit * ncb + cb) * (size_t)nsub * (DK * CB) + (size_t)tid * (2 * KPL);
+  // checkpoints: per (n, h, column block, sub-segment) DK * CB floats; the
+  // thread's 2 * KPL values s[e][c] (flat 2e + c) in pieces of CW floats,
+  // piece q of every thread contiguous (each store instruction writes one
+  // contiguous range)
+  constexpr int CW = 2 * KPL < 4 ? 2 * KPL : 4;
+  float *ckp = p.ck + ((size_t)unit * ncb + cb) * (size_t)nsub * (DK * CB) + (size_t)tid * CW;
+  auto store_ck = [&](float *ck, const float (&x)[KPL][2]) {
+#pragma unroll
+    for (int q = 0; q < 2 * KPL / CW; ++q) {
+      if constexpr (CW == 4)
+        *reinterpret_cast<floatx4 *>(ck + q * (Cf::NT * CW)) =
+            floatx4{x[2 * q][0], x[2 * q][1], x[2 * q + 1][0], x[2 * q + 1][1]};
+      else
+        *reinterpret_cast<floatx2 *>(ck + q * (Cf::NT * CW)) = floatx2{x[q][0], x[q][1]};
+    }
+  };
   // k-reads of the block's columns, [token][d_v] per (n, h)
   float *rh = p.rk + (size_t)unit * T * d_v + cb * CB;
 
@@ -239,41 +273,78 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const int idx = tid + it * Cf::NT;
       if (idx < Cf::NKS) {
         const int tt = idx / (DK / 4), kq = idx % (DK / 4);
-        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][0][4 * kq]) = st.k[it];
-        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][1][4 * kq]) = st.q[it];
-        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][2][4 * kq]) = st.a[it];
-        *reinterpret_cast<floatx4 *>(&sm.kqae[tt][3][4 * kq]) = st.b[it] * st.k[it];
+        *reinterpret_cast<floatx4 *>(&sm.b.kqae[tt][0][4 * kq]) = st.k[it];
+        *reinterpret_cast<floatx4 *>(&sm.b.kqae[tt][1][4 * kq]) = st.q[it];
+        *reinterpret_cast<floatx4 *>(&sm.b.kqae[tt][2][4 * kq]) = st.a[it];
+        *reinterpret_cast<floatx4 *>(&sm.b.kqae[tt][3][4 * kq]) = st.b[it] * st.k[it];
       }
     }
     if (tid < Cf::NCS) {
       const int tt = tid / (CB / 4), cq = tid % (CB / 4);
-      *reinterpret_cast<floatx4 *>(&sm.col[tt][0][4 * cq]) = st.w * st.v;
-      *reinterpret_cast<floatx4 *>(&sm.col[tt][1][4 * cq]) = st.v;
-      *reinterpret_cast<floatx4 *>(&sm.col[tt][2][4 * cq]) = st.w;
-      *reinterpret_cast<floatx4 *>(&sm.col[tt][3][4 * cq]) = st.d;
-      *reinterpret_cast<floatx4 *>(&sm.col[tt][4][4 * cq]) = st.r;
+      *reinterpret_cast<floatx4 *>(&sm.b.col[tt][0][4 * cq]) = st.w * st.v;
+      *reinterpret_cast<floatx4 *>(&sm.b.col[tt][1][4 * cq]) = st.v;
+      *reinterpret_cast<floatx4 *>(&sm.b.col[tt][2][4 * cq]) = st.w;
+      *reinterpret_cast<floatx4 *>(&sm.b.col[tt][3][4 * cq]) = st.d;
+      *reinterpret_cast<floatx4 *>(&sm.b.col[tt][4][4 * cq]) = st.r;
     }
   };
-  auto lds_keys = [&](int tt, int which, float (&x)[KPL]) {
+  // x[e] = row[key0 + e]: the lane's key channels of one staged row
+  auto lds_row = [&](const float *row, float (&x)[KPL]) {
 #pragma unroll
     for (int e = 0; e < KPL; e += (KPL >= 4 ? 4 : KPL)) {
       if constexpr (KPL >= 4) {
-        const floatx4 y = *reinterpret_cast<const floatx4 *>(&sm.kqae[tt][which][key0 + e]);
+        const floatx4 y = *reinterpret_cast<const floatx4 *>(row + key0 + e);
         x[e] = y[0]; x[e + 1] = y[1]; x[e + 2] = y[2]; x[e + 3] = y[3];
       } else if constexpr (KPL == 2) {
-        const floatx2 y = *reinterpret_cast<const floatx2 *>(&sm.kqae[tt][which][key0 + e]);
+        const floatx2 y = *reinterpret_cast<const floatx2 *>(row + key0 + e);
         x[e] = y[0]; x[e + 1] = y[1];
       } else {
-        x[e] = sm.kqae[tt][which][key0 + e];
+        x[e] = row[key0 + e];
       }
     }
   };
-  // One forward step on the lane's two columns: s <- step(s); returns the k-reads.
+  auto lds_keys = [&](int tt, int which, float (&x)[KPL]) { lds_row(sm.b.kqae[tt][which], x); };
+  // Forward phase: request stage sb's inputs (k, a, b of every key channel,
+  // v, w of the block's columns; tokens past the end are identity steps),
+  // stage them in LDS, and run one token on the lane's two columns.
+  auto request1 = [&](int sb, Stage1<DK, CB> &st) {
+#pragma unroll
+    for (int it = 0; it < Cf::KIT1; ++it) {
+      const int idx = tid + it * Cf::NT;
+      const int tt = idx / (DK / 4), kq = idx % (DK / 4);
+      const int t = sb * Cf::L1 + tt;
+      const bool ok = idx < Cf::NKS1 && t < T;
+      st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
+      st.a[it] = ok ? *reinterpret_cast<const floatx4 *>(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
+      st.b[it] = ok ? *reinterpret_cast<const floatx4 *>(bh + t * ab_t + 4 * kq) : zero4();
+    }
+    const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+    const int t = sb * Cf::L1 + tt;
+    const bool ok = tid < Cf::NCS1 && t < T;
+    st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
+    st.w = ok ? *reinterpret_cast<const floatx4 *>(wh + t * vw_t + 4 * cq) : zero4();
+  };
+  auto stash1 = [&](const Stage1<DK, CB> &st) {
+#pragma unroll
+    for (int it = 0; it < Cf::KIT1; ++it) {
+      const int idx = tid + it * Cf::NT;
+      if (idx < Cf::NKS1) {
+        const int tt = idx / (DK / 4), kq = idx % (DK / 4);
+        *reinterpret_cast<floatx4 *>(&sm.f.kae[tt][0][4 * kq]) = st.k[it];
+        *reinterpret_cast<floatx4 *>(&sm.f.kae[tt][1][4 * kq]) = st.a[it];
+        *reinterpret_cast<floatx4 *>(&sm.f.kae[tt][2][4 * kq]) = st.b[it] * st.k[it];
+      }
+    }
+    if (tid < Cf::NCS1) {
+      const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+      *reinterpret_cast<floatx4 *>(&sm.f.u[tt][4 * cq]) = st.w * st.v;
+    }
+  };
   auto fwd_step = [&](int tt, float (&s)[KPL][2], float &r0, float &r1) {
     float kk[KPL], aa[KPL], ee[KPL];
-    lds_keys(tt, 0, kk);
-    lds_keys(tt, 2, aa);
-    lds_keys(tt, 3, ee);
+    lds_row(sm.f.kae[tt][0], kk);
+    lds_row(sm.f.kae[tt][1], aa);
+    lds_row(sm.f.kae[tt][2], ee);
     float x0 = 0.f, x1 = 0.f;
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
@@ -285,7 +356,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
     row_sum16x2(x0, x1);
     r0 = x0;
     r1 = x1;
-    const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
+    const float u0 = sm.f.u[tt][lcol], u1 = sm.f.u[tt][lcol + 1];
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
       s[e][0] = fmaf(kk[e], u0, fmaf(-ee[e], r0, s[e][0]));
@@ -305,22 +376,34 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       s[e][0] = s[e][1] = 0.f;
     }
   }
-  Stage<DK, CB> st;
-  if (nsub > 0) request(0, st, false);
-  for (int sub = 0; sub < nsub; ++sub) {
-    __syncthreads();  // the previous sub-segment's readers are done
-    stash(st);
-    __syncthreads();
-    if (sub + 1 < nsub) request(sub + 1, st, false);
-    float *ck = ckp + (size_t)sub * (DK * CB);
+  // (stages of L1 tokens: each request covers enough work to hide its latency)
+  {
+    const int nst = (T + Cf::L1 - 1) / Cf::L1;
+    Stage1<DK, CB> st1;
+    if (nst > 0) request1(0, st1);
+    for (int sb = 0; sb < nst; ++sb) {
+      __syncthreads();  // the previous stage's readers are done
+      stash1(st1);
+      __syncthreads();
+      if (sb + 1 < nst) request1(sb + 1, st1);
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) *reinterpret_cast<floatx2 *>(ck + 2 * e) = floatx2{s[e][0], s[e][1]};
-#pragma unroll
-    for (int tt = 0; tt < L; ++tt) {
-      float r0, r1;
-      fwd_step(tt, s, r0, r1);
-      if (kg == 0 && sub * L + tt < T)
-        *reinterpret_cast<floatx2 *>(rh + (size_t)(sub * L + tt) * d_v + lcol) = floatx2{r0, r1};
+      for (int tt = 0; tt < Cf::L1; ++tt) {
+        const int t = sb * Cf::L1 + tt;
+        if (tt % L == 0 && t < T)  // checkpoint: the state before sub-segment t / L
+          store_ck(ckp + (size_t)(t / L) * (DK * CB), s);
+        float r0, r1;
+        fwd_step(tt, s, r0, r1);
+        if (kg == 0) *reinterpret_cast<floatx2 *>(&sm.f.r[tt][lcol]) = floatx2{r0, r1};
+      }
+      __syncthreads();
+      // the stage's k-reads as whole rows of the block's columns
+      if (tid < Cf::NCS1) {
+        const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+        const int t = sb * Cf::L1 + tt;
+        if (t < T)
+          *reinterpret_cast<floatx4 *>(rh + (size_t)t * d_v + 4 * cq) =
+              *reinterpret_cast<const floatx4 *>(&sm.f.r[tt][4 * cq]);
+      }
     }
   }
 
@@ -341,11 +424,20 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   auto request_ck = [&](int sub) {
     const float *ck = ckp + (size_t)sub * (DK * CB);
 #pragma unroll
-    for (int e = 0; e < KPL; ++e) ckn[e] = *reinterpret_cast<const floatx2 *>(ck + 2 * e);
+    for (int q = 0; q < 2 * KPL / CW; ++q) {
+      if constexpr (CW == 4) {
+        const floatx4 x = *reinterpret_cast<const floatx4 *>(ck + q * (Cf::NT * CW));
+        ckn[2 * q] = floatx2{x[0], x[1]};
+        ckn[2 * q + 1] = floatx2{x[2], x[3]};
+      } else {
+        ckn[q] = *reinterpret_cast<const floatx2 *>(ck + q * (Cf::NT * CW));
+      }
+    }
   };
   // the k-reads of phase 1 were stored by other waves of the workgroup: the
   // barrier (workgroup-scope release and acquire) makes them visible
   __syncthreads();
+  Stage<DK, CB> st;
   if (nsub > 0) {
     request(nsub - 1, st, true);
     request_ck(nsub - 1);
@@ -372,8 +464,8 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       lds_keys(tt, 0, kk);
       lds_keys(tt, 2, aa);
       lds_keys(tt, 3, ee);
-      const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
-      const float r0 = sm.col[tt][4][lcol], r1 = sm.col[tt][4][lcol + 1];
+      const float u0 = sm.b.col[tt][0][lcol], u1 = sm.b.col[tt][0][lcol + 1];
+      const float r0 = sm.b.col[tt][4][lcol], r1 = sm.b.col[tt][4][lcol + 1];
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         hs[tt + 1][e][0] = fmaf(kk[e], u0, fmaf(-ee[e], r0, hs[tt][e][0] * aa[e]));
@@ -388,9 +480,9 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       lds_keys(tt, 1, qq);
       lds_keys(tt, 2, aa);
       lds_keys(tt, 3, ee);
-      const float u0 = sm.col[tt][0][lcol], u1 = sm.col[tt][0][lcol + 1];
-      const float d0 = sm.col[tt][3][lcol], d1 = sm.col[tt][3][lcol + 1];
-      const float r0 = sm.col[tt][4][lcol], r1 = sm.col[tt][4][lcol + 1];
+      const float u0 = sm.b.col[tt][0][lcol], u1 = sm.b.col[tt][0][lcol + 1];
+      const float d0 = sm.b.col[tt][3][lcol], d1 = sm.b.col[tt][3][lcol + 1];
+      const float r0 = sm.b.col[tt][4][lcol], r1 = sm.b.col[tt][4][lcol + 1];
       // x[0] dq part, x[1] dk part (u L + a * dr S_{t-1}), x[2] sum_j r_j L (de = -x[2]), x[3] da
       float x[4][KPL];
       float pu0 = 0.f, pu1 = 0.f, pe0 = 0.f, pe1 = 0.f;
@@ -428,7 +520,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       swap_sum_n<32, KPL>(x[1], x[3]);
       swap_sum_n<16, KPL>(x[0], x[1]);
       // x[0] now holds the lane group's vector c4 on keys key0 .. key0 + KPL - 1
-      float *dst = &sm.red[wave][tt][c4][key0];
+      float *dst = &sm.b.red[wave][tt][c4][key0];
       if constexpr (KPL >= 4) {
 #pragma unroll
         for (int e = 0; e < KPL; e += 4)
@@ -438,8 +530,8 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         for (int e = 0; e < KPL; ++e) dst[e] = x[0][e];
       }
       if (kg == 0) {
-        sm.du[tt][lcol] = du0;
-        sm.du[tt][lcol + 1] = du1;
+        sm.b.du[tt][lcol] = du0;
+        sm.b.du[tt][lcol + 1] = du1;
       }
     }
     __syncthreads();
@@ -451,9 +543,9 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const int vec = rem / (DK / 4), kq = rem % (DK / 4);
       const int t = sub * L + tt;
       if (t < T) {
-        floatx4 acc = *reinterpret_cast<const floatx4 *>(&sm.red[0][tt][vec][4 * kq]);
+        floatx4 acc = *reinterpret_cast<const floatx4 *>(&sm.b.red[0][tt][vec][4 * kq]);
 #pragma unroll
-        for (int w2 = 1; w2 < Cf::NWV; ++w2) acc += *reinterpret_cast<const floatx4 *>(&sm.red[w2][tt][vec][4 * kq]);
+        for (int w2 = 1; w2 < Cf::NWV; ++w2) acc += *reinterpret_cast<const floatx4 *>(&sm.b.red[w2][tt][vec][4 * kq]);
         float *dst = p.part + (((size_t)cb * p.B * T + tok0 + t) * p.H_v + h) * (4 * DK) + vec * DK + 4 * kq;
         *reinterpret_cast<floatx4 *>(dst) = acc;
       }
@@ -463,10 +555,10 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const int tt = idx / CB, c = idx % CB;
       const int t = sub * L + tt;
       if (t < T) {
-        const float du = sm.du[tt][c];
+        const float du = sm.b.du[tt][c];
         const size_t o = (tok0 + t) * vw_t + (size_t)h * d_v + cb * CB + c;
-        E::st((ET *)p.dv + o, du * sm.col[tt][2][c]);
-        p.dw[o] = du * sm.col[tt][1][c];
+        E::st((ET *)p.dv + o, du * sm.b.col[tt][2][c]);
+        p.dw[o] = du * sm.b.col[tt][1][c];
       }
     }
   }
