@@ -20,8 +20,8 @@
 //
 // MI355X design: this is a per-token recurrence with two 16-lane key
 // reductions per token and column, so it runs on the vector ALUs, not the
-// matrix cores. One workgroup per (n, h, block of CB value columns): four
-// waves (two for CB = 16), each holding 8 columns; lane = (column pair c4,
+// matrix cores. One workgroup per (n, h, block of CB value columns, 64
+// when d_v allows): one wave per 8 columns; lane = (column pair c4,
 // key group kg) holds columns 2*c4, 2*c4+1 of its wave on the key channels
 // kg*KPL .. +KPL. Key sums (k-read, du, dr) are DPP rotations within a
 // 16-lane row; key-side gradient sums over the wave's columns are a
@@ -52,6 +52,9 @@ namespace {
 
 constexpr int kSub = 4;  // tokens per sub-segment (the register history)
 
+// Value columns per workgroup (one wave per 8): 64 when d_v allows.
+__host__ __device__ constexpr int bwd_cb(int d_v) { return d_v >= 64 ? 64 : d_v >= 32 ? 32 : 16; }
+
 template <int DK, int CB>
 struct BwdCfg {
   static constexpr int NWV = CB / 8;   // waves, 8 value columns each
@@ -67,7 +70,7 @@ struct BwdCfg {
   static constexpr int NCS1 = L1 * CB / 4;
   static_assert(NCS <= NT && NCS1 <= NT, "one column quad per thread at most");
   static_assert(L1 % L == 0, "checkpoints at sub-segment starts");
-  static_assert(CB == 16 || CB == 32, "column block");
+  static_assert(CB == 16 || CB == 32 || CB == 64, "column block");
 };
 
 template <int DK, int CB>
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) 
   using E = Elem<BF16>;
   using ET = typename E::T;
   constexpr int TPR = DK / 4;  // threads per (token, g) row, 4 keys each
-  const int ncb = p.d_v / (p.d_v >= 32 ? 32 : 16);
+  const int ncb = p.d_v / bwd_cb(p.d_v);
   const size_t BT = (size_t)p.B * p.T;
   const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= BT * p.H_qk) return;
@@ -612,7 +615,6 @@ namespace {
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int bwd_cb(int d_v) { return d_v >= 32 ? 32 : 16; }
 
 template <int DK, int CB, bool BF16>
 hipError_t launch_t(const BackwardParams &p, hipStream_t st) {
@@ -629,7 +631,11 @@ hipError_t launch_t(const BackwardParams &p, hipStream_t st) {
 
 template <int DK, bool BF16>
 hipError_t launch_dk(const BackwardParams &p, hipStream_t st) {
-  return bwd_cb(p.d_v) == 32 ? launch_t<DK, 32, BF16>(p, st) : launch_t<DK, 16, BF16>(p, st);
+  switch (bwd_cb(p.d_v)) {
+    case 64: return launch_t<DK, 64, BF16>(p, st);
+    case 32: return launch_t<DK, 32, BF16>(p, st);
+  }
+  return launch_t<DK, 16, BF16>(p, st);
 }
 
 }  // namespace

@@ -188,9 +188,9 @@ gdn2_status gdn2_decode_step(const gdn2_desc *desc, const void *q, const void *k
  *   dS0  : [B, H_v, d_k, d_v] fp32, or NULL (not written). It may be the
  *          same pointer as dS_T (in place), but not a partial overlap.
  *   workspace : gdn2_chunk_backward_workspace_bytes(desc) bytes (fp32 state
- *          checkpoints every 4 tokens, per 32-column block key-side partial
+ *          checkpoints every 4 tokens, per 64-column block key-side partial
  *          sums and every token's k-read: about
- *          (d_k * d_v / 4 + 4 * d_k * ceil(d_v / 32) + d_v) * 4 bytes per
+ *          (d_k * d_v / 4 + 4 * d_k * ceil(d_v / 64) + d_v) * 4 bytes per
  *          token and value head), 256-byte aligned; NULL only when that size
  *          is 0. Contents on return are unspecified.
  * Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums; all

@@ -212,10 +212,10 @@ def bwd(desc, ptrs=None, ws=0, ws_bytes=0):
 
 def test_backward_workspace_query_and_argument_errors():
     """Workspace: fp32 checkpoints every 4 tokens (d_k x d_v per head), four
-    d_k-vectors per token, head and 32-column block, and one d_v-vector of
+    d_k-vectors per token, head and 64-column block, and one d_v-vector of
     k-reads per token and head; errors before any launch."""
     d = g.make_desc(2, 20, 1, 2, 64, 64, 64, g.GDN2_BF16)
-    nsub, ncb = 5, 2  # checkpoints every 4 tokens
+    nsub, ncb = 5, 1  # checkpoints every 4 tokens; one 64-column block
     ck = 2 * 2 * nsub * 64 * 64 * 4
     part = ncb * 2 * 20 * 2 * 4 * 64 * 4
     rk = 2 * 2 * 20 * 64 * 4
