@@ -13,8 +13,9 @@ on the stream the kernels are launched on.
 
 After the timed steps, the decode workload as stated (1024 successive decode
 steps from a random state) runs once for the decode bandwidth figure, the
-backward pass (gdn2_chunk_backward) of the prefill runs a few times for its
-own figure, and the fp64 oracle runs on the host over the prefill batch for
+prefill with the gates as bf16 pre-activations (gdn2_chunk_forward_preact)
+and the backward pass (gdn2_chunk_backward) of the prefill run a few times
+for their own figures, and the fp64 oracle runs on the host over the prefill batch for
 the CPU baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -70,6 +71,15 @@ def decode_algorithmic(c):
     return c.B * c.H_v * per_head + qk
 
 
+def preact_algorithmic(c):
+    """Bytes of one prefill launch with the gates as pre-activations in the
+    input dtype (a, b, w at es bytes instead of 4)."""
+    es = 2 if c.dtype == "bf16" else 4
+    toks = c.B * c.T
+    return (toks * (c.H_qk * c.d_k * es * 2 + c.H_v * c.d_v * es * 2 + c.H_v * c.d_k * es * 2
+                    + c.H_v * c.d_v * es) + c.B * c.H_v * c.d_k * c.d_v * 4)
+
+
 def backward_algorithmic(c):
     """Flops of the gradient by the recurrence, per state element and token:
     the forward states (decay 1, k-read 2, erase 2, write 2) and the adjoint
@@ -123,6 +133,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="length of the decode workload leg (default: the workload's 1024)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--preact-steps", type=int, default=50,
+                    help="timed launches of the prefill with gate pre-activations (0: skip)")
     ap.add_argument("--backward-steps", type=int, default=5,
                     help="timed launches of the backward pass over the prefill shape (0: skip)")
     ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
@@ -243,6 +255,34 @@ def main():
     log(f"[bench] decode workload: {dec_steps} steps in {loop_ms:.1f} ms; kernel avg {d_avg * 1e6:.1f} us "
         f"= {d_gbs:.0f} GB/s algorithmic")
 
+    # ---------------------------------------------------------------- gate pre-activation leg
+    pre_leg = None
+    if args.preact_steps > 0:
+        tpp = gi.to_torch_preact(gi.make_preact_inputs(cp), cp.dtype, dev)
+
+        def prefill_preact():
+            g.chunk_forward_preact(tpp["q"], tpp["k"], tpp["v"], tpp["a"], tpp["b"], tpp["w"], None, chunk=cp.chunk,
+                                   o=o, S_T=S_T, stream=stream)
+
+        for _ in range(20):
+            prefill_preact()
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.preact_steps)]
+        for e0, e1 in pev:
+            e0.record(stream)
+            prefill_preact()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        p_ms = [a.elapsed_time(b) for a, b in pev]
+        p_avg = float(np.mean(p_ms)) / 1e3
+        pby = preact_algorithmic(cp)
+        pre_leg = {"launches": args.preact_steps, "kernel_us": p_avg * 1e6, "min_us": min(p_ms) * 1e3,
+                   "tokens_per_s": tokens / p_avg, "achieved": pby / p_avg / 1e9, "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": pby / p_avg / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": pby}
+        log(f"[bench] prefill with gate pre-activations: {p_avg * 1e6:.1f} us per launch")
+        del tpp
+
     # ---------------------------------------------------------------- backward leg
     bwd = None
     if args.backward_steps > 0:
@@ -337,6 +377,7 @@ def main():
             "frac": d_gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": dbytes,
         },
+        "preact": pre_leg,
         "backward": bwd,
         "cpu_baseline": cpu,
     }

@@ -40,6 +40,7 @@ GDN2_F32 = 0
 GDN2_BF16 = 1
 
 EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forward_scalar",
+            "gdn2_chunk_forward_preact",
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
             "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
             "gdn2_status_string", "gdn2_version")
@@ -72,6 +73,8 @@ def load(path: Optional[str] = None):
     vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(gdn2_desc)
     lib.gdn2_chunk_forward.restype = ctypes.c_int
     lib.gdn2_chunk_forward.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
+    lib.gdn2_chunk_forward_preact.restype = ctypes.c_int
+    lib.gdn2_chunk_forward_preact.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
     lib.gdn2_chunk_forward_coupled.restype = ctypes.c_int
     lib.gdn2_chunk_forward_coupled.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
     lib.gdn2_chunk_forward_scalar.restype = ctypes.c_int
@@ -116,6 +119,12 @@ def gdn2_chunk_forward(desc, q, k, v, a, b, w, S0, o, S_T, workspace=0, workspac
                        stream=0) -> int:
     return load().gdn2_chunk_forward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w,
                                      S0, o, S_T, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_forward_preact(desc, q, k, v, a_pre, b_pre, w_pre, S0, o, S_T, workspace=0, workspace_bytes=0,
+                              stream=0) -> int:
+    return load().gdn2_chunk_forward_preact(None if desc is None else ctypes.byref(desc), q, k, v, a_pre, b_pre,
+                                            w_pre, S0, o, S_T, workspace, workspace_bytes, stream)
 
 
 def gdn2_chunk_forward_coupled(desc, q, k, v, a, beta, S0, o, S_T, workspace=0, workspace_bytes=0,
@@ -247,6 +256,33 @@ def chunk_backward(q, k, v, a, b, w, S0, dO, dS_T=None, want_dS0: bool = True, g
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return g
+
+
+def chunk_forward_preact(q, k, v, a_pre, b_pre, w_pre, S0=None, chunk: int = 64, o=None, S_T=None,
+                         want_state: bool = True, stream=None):
+    """Prefill with the per-channel gates given as pre-activations in the
+    input dtype (decay a = exp(-softplus(a_pre)), b = sigmoid(b_pre),
+    w = sigmoid(w_pre)), activated in the kernel. Shapes as chunk_forward."""
+    import torch
+    B, T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (a_pre, "a_pre"), (b_pre, "b_pre"), (w_pre, "w_pre")):
+        _check(t, nm, q.dtype)
+    _check(S0, "S0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    _check(o, "o", q.dtype)
+    _check(S_T, "S_T", torch.float32)
+    desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
+    ws = gdn2_chunk_forward_workspace_bytes(desc)
+    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    st = gdn2_chunk_forward_preact(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a_pre), _ptr(b_pre), _ptr(w_pre),
+                                   _ptr(S0), _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st)
+    return o, S_T
 
 
 def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_T=None,

@@ -72,6 +72,12 @@ gdn2::PrefillArgs prefill_args(const gdn2_desc *d) {
   return p;
 }
 
+// gdn2_chunk_forward and gdn2_chunk_forward_preact: per-channel gates, fp32
+// activated values or pre-activations in the input dtype.
+gdn2_status forward_general(const gdn2_desc *d, const void *q, const void *k, const void *v, const void *a,
+                            const void *b, const void *w, const float *S0, void *o, float *S_T, void *workspace,
+                            size_t workspace_bytes, void *stream, bool preact);
+
 }  // namespace
 
 size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc) {
@@ -84,6 +90,23 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
                                const float *a, const float *b, const float *w, const float *S0,
                                void *o, float *S_T, void *workspace, size_t workspace_bytes,
                                void *stream) {
+  return forward_general(d, q, k, v, a, b, w, S0, o, S_T, workspace, workspace_bytes, stream, false);
+}
+
+gdn2_status gdn2_chunk_forward_preact(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                      const void *a_pre, const void *b_pre, const void *w_pre, const float *S0,
+                                      void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  return forward_general(d, q, k, v, a_pre, b_pre, w_pre, S0, o, S_T, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn2_status forward_general(const gdn2_desc *d, const void *q, const void *k, const void *v, const void *a,
+                            const void *b, const void *w, const float *S0, void *o, float *S_T, void *workspace,
+                            size_t workspace_bytes, void *stream, bool preact) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
   const size_t ws_need = gdn2_chunk_forward_workspace_bytes(d);
@@ -100,8 +123,9 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
 
   const Range rq = range_of(q, B * T * Hqk * dk * es), rk = range_of(k, B * T * Hqk * dk * es);
   const Range rv = range_of(v, B * T * Hv * dv * es);
-  const Range ra = range_of(a, B * T * Hv * dk * 4), rb = range_of(b, B * T * Hv * dk * 4);
-  const Range rw = range_of(w, B * T * Hv * dv * 4);
+  const size_t gs = preact ? es : 4;  // gate element bytes
+  const Range ra = range_of(a, B * T * Hv * dk * gs), rb = range_of(b, B * T * Hv * dk * gs);
+  const Range rw = range_of(w, B * T * Hv * dv * gs);
   const Range ro = range_of(o, B * T * Hv * dv * es);
   const Range rs0 = range_of(S0, S0 ? B * Hv * dk * dv * 4 : 0);
   const Range rst = range_of(S_T, S_T ? B * Hv * dk * dv * 4 : 0);
@@ -120,14 +144,19 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k,
   if (S0 && S_T && overlaps(rs0, rst) && S0 != S_T) return GDN2_ERR_ALIAS;
 
   gdn2::PrefillArgs p = prefill_args(d);
-  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.q = q; p.k = k; p.v = v; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.a = static_cast<const float *>(a);  // pre-activations in the input dtype when preact
+  p.b = static_cast<const float *>(b);
+  p.w = static_cast<const float *>(w);
+  p.preact = preact;
   p.workspace = workspace;
   p.workspace_bytes = workspace_bytes;
   const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace
+
 
 namespace {
 

@@ -178,6 +178,18 @@ __device__ __forceinline__ void bstore(floatx4 x, rsrc_t r, uint32_t voff, uint3
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), x), r, voff, soff, 0);
 }
 
+// ---------------------------------------------------------------- gate activations
+// Decay from its pre-activation: exp(-softplus(x)) = 1 / (1 + e^x); erase and
+// write gates: sigmoid(x) = 1 / (1 + e^-x). e^x as 2^(x log2 e) (v_exp_f32),
+// then one reciprocal: relative error a few ulp; e^x overflowing to infinity
+// gives 0, underflowing gives 1.
+__device__ __forceinline__ float decay_from_pre(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * 1.44269504088896341f));
+}
+__device__ __forceinline__ float gate_from_pre(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+
 // ---------------------------------------------------------------- lane shifts
 // x from lane (l - D) of the same 16-lane row (DPP row_shr:D); lanes whose
 // source is outside the row get `fill`. The empty asm keeps each component's

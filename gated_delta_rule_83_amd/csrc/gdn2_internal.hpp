@@ -36,6 +36,9 @@ struct PrefillArgs {
   // scalar decay (with coupled gates): a points to [.., T, H_v], one decay
   // per token and value head for all key channels
   bool scalar_decay;
+  // per-channel gates given as pre-activations in the input dtype (a, b, w
+  // point to them), activated in the kernel
+  bool preact;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one

@@ -451,8 +451,11 @@ __device__ __forceinline__ void map_block(int L, int B, int H_qk, int H_v, int n
 // CPL: coupled gates (b = w = beta, one scalar per token and value head,
 // passed as both p.b and p.w, [.., T, H_v]); otherwise b is per key channel
 // and w per value channel. SCA: scalar decay (a one scalar per token and
-// value head, [.., T, H_v]); otherwise a is per key channel.
-template <int DK, int C, int NCT, bool BF16, bool CPL, bool SCA>
+// value head, [.., T, H_v]); otherwise a is per key channel. PRE: per-channel
+// gates given as pre-activations x in the input dtype, activated here
+// (decay a = exp(-softplus(x)) = 1 / (1 + e^x), erase and write gates
+// b, w = sigmoid(x)).
+template <int DK, int C, int NCT, bool BF16, bool CPL, bool SCA, bool PRE>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   using Cf = PrefillCfg<DK, C, NCT, BF16>;
   using E = Elem<BF16>;
@@ -506,20 +509,42 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const int col = (ident ? cb - p.ncb_val : cb) * Cf::DVB + (consumer ? cw : 0) * 16 + lc;
   const bool write_o = !ident && !(p.o_first_only && rel > 0);
 
-  // Token strides in bytes, and this (sequence, head)'s token-0 bases.
+  // Token strides in bytes, and this (sequence, head)'s token-0 bases. GT:
+  // the stored type of the per-channel gates.
+  static_assert(!PRE || (!CPL && !SCA), "pre-activations for per-channel gates");
+  using GT = typename std::conditional<PRE, ET, float>::type;
+  constexpr uint32_t GS = sizeof(GT);
   const uint32_t qk_tb = (uint32_t)(p.H_qk * DK) * sizeof(ET);
-  const uint32_t ab_tb = (uint32_t)(p.H_v * DK) * 4u;
+  const uint32_t ab_tb = (uint32_t)(p.H_v * DK) * GS;
   const uint32_t v_tb = (uint32_t)(p.H_v * d_v) * sizeof(ET);
-  const uint32_t w_tb = (uint32_t)(p.H_v * d_v) * 4u;
+  const uint32_t w_tb = (uint32_t)(p.H_v * d_v) * GS;
   const uint32_t at_tb = SCA ? (uint32_t)p.H_v * 4u : ab_tb;  // token strides of a, b and w
   const uint32_t bt_tb = CPL ? (uint32_t)p.H_v * 4u : ab_tb;
   const uint32_t wt_tb = CPL ? (uint32_t)p.H_v * 4u : w_tb;
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v;
-  const float *ah = SCA ? p.a + tok0 * p.H_v + h : p.a + tok0 * p.H_v * DK + (size_t)h * DK;
-  const float *bh = CPL ? p.b + tok0 * p.H_v + h : p.b + tok0 * p.H_v * DK + (size_t)h * DK;
-  const float *wh = CPL ? p.w + tok0 * p.H_v + h : p.w + tok0 * p.H_v * d_v + (size_t)h * d_v;
+  const GT *ga = (const GT *)p.a, *gb = (const GT *)p.b, *gw = (const GT *)p.w;
+  const GT *ah = SCA ? ga + tok0 * p.H_v + h : ga + tok0 * p.H_v * DK + (size_t)h * DK;
+  const GT *bh = CPL ? gb + tok0 * p.H_v + h : gb + tok0 * p.H_v * DK + (size_t)h * DK;
+  const GT *wh = CPL ? gw + tok0 * p.H_v + h : gw + tok0 * p.H_v * d_v + (size_t)h * d_v;
+  // activated gates from pre-activations (four channels: the raw values are
+  // the register's first two words as bf16 pairs, or all four as fp32)
+  auto gate_unpack = [](floatx4 raw) -> floatx4 {
+    if constexpr (BF16) {
+      const uint32_t x = __float_as_uint(raw[0]), y = __float_as_uint(raw[1]);
+      return floatx4{__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u), __uint_as_float(y << 16),
+                     __uint_as_float(y & 0xffff0000u)};
+    } else {
+      return raw;
+    }
+  };
+  auto decay4 = [](floatx4 x) {
+    return floatx4{decay_from_pre(x[0]), decay_from_pre(x[1]), decay_from_pre(x[2]), decay_from_pre(x[3])};
+  };
+  auto gate4 = [](floatx4 x) {
+    return floatx4{gate_from_pre(x[0]), gate_from_pre(x[1]), gate_from_pre(x[2]), gate_from_pre(x[3])};
+  };
   ET *oh = (ET *)p.o + tok0 * p.H_v * d_v + (size_t)h * d_v;
   // entering and final state of this lane's column: value blocks use S0 /
   // S_T ([B][H_v][d_k][d_v] per segment), identity blocks start from the
@@ -551,7 +576,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const int ch0 = TOKM ? 4 * cq : wave * (DK / 4) + 4 * cq;
   const int tb0 = TOKM ? wave * (C / 4) + rg * RPG : rg * RPG;  // the lane's first token
   static_assert(!TOKM || RPG * 8 == C, "token-major: C/8 tokens per lane");
-  const uint32_t ab_off = (uint32_t)tb0 * ab_tb + (uint32_t)ch0 * 4u;
+  const uint32_t ab_off = (uint32_t)tb0 * ab_tb + (uint32_t)ch0 * GS;
   const uint32_t qk_off = (uint32_t)tb0 * qk_tb + (uint32_t)ch0 * sizeof(ET);
 
   // Raw inputs of the chunks to build, held in two register sets (chunk s
@@ -577,12 +602,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         if constexpr (SCA) {
           const float aa = bload<float>(src.a, (uint32_t)tb0 * at_tb, r * at_tb);
           ra[P][r] = floatx4{aa, aa, aa, aa};
+        } else if constexpr (PRE && BF16) {  // raw bf16 quads in the first two words
+          const uint2 u = bload<uint2>(src.a, ab_off, r * ab_tb);
+          ra[P][r] = floatx4{__uint_as_float(u.x), __uint_as_float(u.y), 0.f, 0.f};
         } else {
           ra[P][r] = bload<floatx4>(src.a, ab_off, r * ab_tb);
         }
         if constexpr (CPL) {
           const float bb = bload<float>(src.b, (uint32_t)tb0 * bt_tb, r * bt_tb);
           rb[P][r] = floatx4{bb, bb, bb, bb};
+        } else if constexpr (PRE && BF16) {
+          const uint2 u = bload<uint2>(src.b, ab_off, r * ab_tb);
+          rb[P][r] = floatx4{__uint_as_float(u.x), __uint_as_float(u.y), 0.f, 0.f};
         } else {
           rb[P][r] = bload<floatx4>(src.b, ab_off, r * ab_tb);
         }
@@ -608,6 +639,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   auto shfl4 = [](floatx4 x, int src) {
     return floatx4{__shfl(x[0], src, 64), __shfl(x[1], src, 64), __shfl(x[2], src, 64),
                    __shfl(x[3], src, 64)};
+  };
+
+  // Pre-activations of register set P -> activated decay and erase gate, in
+  // place (before the set's first use: its wave totals, then its build).
+  auto activate_ab = [&](auto P) {
+    if constexpr (PRE) {
+      if (brow) {
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+          ra[P][r] = decay4(gate_unpack(ra[P][r]));
+          rb[P][r] = gate4(gate_unpack(rb[P][r]));
+        }
+      }
+    }
   };
 
   // Token-major: this wave's total decay per channel for the chunk in raw
@@ -755,6 +800,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_barrier(0);
       load_kq(I1(), src1);
       __builtin_amdgcn_sched_barrier(0);
+      activate_ab(I0());
       if constexpr (TOKM) {
         // chunk 0's wave totals; the barrier publishes them (the other waves
         // execute a matching one before their loop)
@@ -800,6 +846,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           default: gram_wave(std::integral_constant<int, 3>()); break;
         }
       }
+      activate_ab(std::integral_constant<int, decltype(P)::value ^ 1>());
       wave_totals(std::integral_constant<int, decltype(P)::value ^ 1>());  // chunk s+1
       load_kq(P, raw_src(tn));
       GDN2_MARK(2);
@@ -831,29 +878,42 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // Token-by-token steps on this wave's columns (exact for any decay).
-  auto token_steps = [&](int tb, int te) {
+  auto token_steps = [&](int tb, int te) __attribute__((always_inline)) {
     for (int t = tb; t < te; ++t) {
-      const float *at = ah + (size_t)t * (at_tb / 4);
-      const float *bt = bh + (size_t)t * (bt_tb / 4);
+      const GT *at = ah + (size_t)t * (at_tb / GS);
+      const GT *bt = bh + (size_t)t * (bt_tb / GS);
       const ET *kt = kh + (size_t)t * (qk_tb / sizeof(ET));
       const ET *qt = qh + (size_t)t * (qk_tb / sizeof(ET));
       float part = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         const int i0 = 16 * rt + 4 * lg;
-        const floatx4 av = SCA ? floatx4{at[0], at[0], at[0], at[0]} : *reinterpret_cast<const floatx4 *>(at + i0);
+        floatx4 av;
+        if constexpr (PRE)
+          av = decay4(E::ld4(at + i0));
+        else
+          av = SCA ? floatx4{at[0], at[0], at[0], at[0]} : *reinterpret_cast<const floatx4 *>(at + i0);
         const floatx4 kv = E::ld4(kt + i0);
         S[rt] *= av;
         part += S[rt][0] * kv[0] + S[rt][1] * kv[1] + S[rt][2] * kv[2] + S[rt][3] * kv[3];
       }
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);  // key read r for this column
-      const float u = ident ? 0.f : wh[(size_t)t * (wt_tb / 4) + (CPL ? 0 : col)] * E::ld(vh + (size_t)t * (v_tb / sizeof(ET)) + col);
+      float wg;
+      if constexpr (PRE)
+        wg = gate_from_pre(E::ld(wh + (size_t)t * (wt_tb / GS) + col));
+      else
+        wg = wh[(size_t)t * (wt_tb / GS) + (CPL ? 0 : col)];
+      const float u = ident ? 0.f : wg * E::ld(vh + (size_t)t * (v_tb / sizeof(ET)) + col);
       float po = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         const int i0 = 16 * rt + 4 * lg;
-        const floatx4 bv = CPL ? floatx4{bt[0], bt[0], bt[0], bt[0]} : *reinterpret_cast<const floatx4 *>(bt + i0);
+        floatx4 bv;
+        if constexpr (PRE)
+          bv = gate4(E::ld4(bt + i0));
+        else
+          bv = CPL ? floatx4{bt[0], bt[0], bt[0], bt[0]} : *reinterpret_cast<const floatx4 *>(bt + i0);
         const floatx4 kv = E::ld4(kt + i0);
         const floatx4 qv = E::ld4(qt + i0);
         S[rt] = S[rt] - (bv * kv) * part + kv * u;
@@ -883,7 +943,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const int ut = lane / Cf::ULPT, uc = lane % Cf::ULPT;
   const int utok = cw * UTPW + ut;  // first token of this lane (i = 0)
   const uint32_t uv_off = (uint32_t)utok * v_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * sizeof(ET);
-  const uint32_t uw_off = CPL ? (uint32_t)utok * wt_tb : (uint32_t)utok * w_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * 4u;
+  const uint32_t uw_off = CPL ? (uint32_t)utok * wt_tb : (uint32_t)utok * w_tb + (uint32_t)(cb * Cf::DVB + 8 * uc) * GS;
   auto load_u = [&](auto P, int t0) {
     const rsrc_t rv_ = make_rsrc((const char *)vh + (size_t)t0 * v_tb, rows_left(t0, v_tb));
     const rsrc_t rw_ = make_rsrc((const char *)wh + (size_t)t0 * wt_tb, rows_left(t0, wt_tb));
@@ -898,6 +958,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           if (e == 0) {
             const float bb = bload<float>(rw_, uw_off, (uint32_t)(i * UTPI) * wt_tb);
             rw[P][i][0] = rw[P][i][1] = floatx4{bb, bb, bb, bb};
+          }
+        } else if constexpr (PRE && BF16) {  // 8 bf16 pre-activations in one 16-byte load
+          if (e == 0) {
+            rw[P][i][0] = bload<floatx4>(rw_, uw_off, (uint32_t)(i * UTPI) * w_tb);
+            rw[P][i][1] = zero4();
           }
         } else {
           rw[P][i][e] = bload<floatx4>(rw_, uw_off + 16u * e, (uint32_t)(i * UTPI) * w_tb);
@@ -922,14 +987,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           v8[0] = rv[PP][i][0];
           v8[1] = rv[PP][i][NVL - 1];
         }
+        floatx4 w8[2] = {rw[PP][i][0], rw[PP][i][1]};
+        if constexpr (PRE && BF16) {  // 8 bf16 pre-activations -> write gates
+          const floatx4 raw = rw[PP][i][0];
+          w8[0] = gate4(gate_unpack(floatx4{raw[0], raw[1], 0.f, 0.f}));
+          w8[1] = gate4(gate_unpack(floatx4{raw[2], raw[3], 0.f, 0.f}));
+        } else if constexpr (PRE) {
+          w8[0] = gate4(w8[0]);
+          w8[1] = gate4(w8[1]);
+        }
         char *dst = sm.ubuf + (utok + i * UTPI) * UROW + 8 * uc * (int)sizeof(OT);
         if constexpr (BF16) {
-          const bf16x4 lo = __builtin_convertvector(rw[PP][i][0] * v8[0], bf16x4);
-          const bf16x4 hi = __builtin_convertvector(rw[PP][i][1] * v8[1], bf16x4);
+          const bf16x4 lo = __builtin_convertvector(w8[0] * v8[0], bf16x4);
+          const bf16x4 hi = __builtin_convertvector(w8[1] * v8[1], bf16x4);
           *reinterpret_cast<bf16x8 *>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
-          *reinterpret_cast<floatx4 *>(dst) = rw[PP][i][0] * v8[0];
-          *reinterpret_cast<floatx4 *>(dst + 16) = rw[PP][i][1] * v8[1];
+          *reinterpret_cast<floatx4 *>(dst) = w8[0] * v8[0];
+          *reinterpret_cast<floatx4 *>(dst + 16) = w8[1] * v8[1];
         }
       }
     }
@@ -1203,11 +1277,13 @@ template <int DK, int C, int NCT, bool BF16>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   auto kernel = [&](int blocks, const PrefillParams &kp) {
     if (a.scalar_decay)  // scalar decay comes with coupled gates (Gated DeltaNet)
-      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, true>), dim3(blocks), dim3(512), 0, st, kp);
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, true, false>), dim3(blocks), dim3(512), 0, st, kp);
     else if (a.coupled)
-      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, false>), dim3(blocks), dim3(512), 0, st, kp);
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, false, false>), dim3(blocks), dim3(512), 0, st, kp);
+    else if (a.preact)
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false, true>), dim3(blocks), dim3(512), 0, st, kp);
     else
-      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false>), dim3(blocks), dim3(512), 0, st, kp);
+      hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false, false>), dim3(blocks), dim3(512), 0, st, kp);
   };
   const PrefillPlan pl = plan_t<DK, C, NCT, BF16>(a);
   if (plan_only) {

@@ -103,7 +103,7 @@ def _decay(x: np.ndarray) -> np.ndarray:
     return (1.0 / (1.0 + np.exp(x.astype(np.float64)))).astype(np.float32)
 
 
-def _draw(rng: np.random.Generator, c: Config, B: int, T: int, with_s0: bool):
+def _draw(rng: np.random.Generator, c: Config, B: int, T: int, with_s0: bool, preact: bool = False):
     f32 = np.float32
     q = _l2_normalise(rng.standard_normal((B, T, c.H_qk, c.d_k), dtype=f32))
     k = _l2_normalise(rng.standard_normal((B, T, c.H_qk, c.d_k), dtype=f32))
@@ -111,15 +111,16 @@ def _draw(rng: np.random.Generator, c: Config, B: int, T: int, with_s0: bool):
     a_pre = rng.standard_normal((B, T, c.H_v, c.d_k), dtype=f32)
     if c.a_mu != 0.0:
         a_pre += f32(c.a_mu)
-    a = _decay(a_pre)
-    del a_pre
     b_pre = rng.standard_normal((B, T, c.H_v, c.d_k), dtype=f32)
-    w = _sigmoid(rng.standard_normal((B, T, c.H_v, c.d_v), dtype=f32))
+    w_pre = rng.standard_normal((B, T, c.H_v, c.d_v), dtype=f32)
     if c.hard_erase_p > 0.0:
         mask = rng.random((B, T), dtype=np.float64) < c.hard_erase_p
         b_pre[mask] = f32(6.0)
-    b = _sigmoid(b_pre)
-    del b_pre
+    if preact:
+        a, b, w = a_pre, b_pre, w_pre
+    else:
+        a, b, w = _decay(a_pre), _sigmoid(b_pre), _sigmoid(w_pre)
+    del a_pre, b_pre, w_pre
     S0 = None
     if with_s0 and c.s0_std is not None:
         S0 = (rng.standard_normal((B, c.H_v, c.d_k, c.d_v), dtype=f32) * f32(c.s0_std)).astype(f32)
@@ -134,6 +135,25 @@ def make_inputs(c: Config) -> dict:
     """
     rng = np.random.default_rng(c.seed)
     return _draw(rng, c, c.B, c.T, with_s0=True)
+
+
+def make_preact_inputs(c: Config) -> dict:
+    """The same draws as :func:`make_inputs`, with the gates left as their
+    float32 pre-activations (a: decay, b, w: erase and write gates). Use
+    :func:`to_torch_preact` to store them in the input dtype."""
+    rng = np.random.default_rng(c.seed)
+    return _draw(rng, c, c.B, c.T, with_s0=True, preact=True)
+
+
+def to_torch_preact(d: dict, dtype: str, device=None):
+    """Like :func:`to_torch`, with the gate pre-activations a, b, w also cast
+    to `dtype` (round-to-nearest-even for bf16)."""
+    import torch
+    out = to_torch(d, dtype, device)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for name in ("a", "b", "w"):
+        out[name] = out[name].to(tdt)
+    return out
 
 
 def make_decode_state(c: Config) -> Optional[np.ndarray]:

@@ -160,6 +160,22 @@ gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *desc, const int32_t *cu_s
                                       const void *k, const void *v, const float *a, const float *b,
                                       const float *w, const float *S0, void *o, float *S_T, void *stream);
 
+/* Prefill with the per-channel gates given as pre-activations: a_pre, b_pre
+ * ([B, T, H_v, d_k]) and w_pre ([B, T, H_v, d_v]) in the input dtype
+ * (desc->dtype, bf16 or fp32) instead of fp32 activated values. The kernel
+ * activates them in fp32: decay a = exp(-softplus(a_pre)) = 1 / (1 + e^a_pre),
+ * erase gate b = sigmoid(b_pre), write gate w = sigmoid(w_pre) (values in
+ * (0, 1) as the step above needs; the pages describe the gates only as
+ * channel-wise values, and this is the usual parameterisation of such
+ * gates). With bf16 inputs the gates cross HBM at half the bytes. Everything
+ * else (layouts, S0/S_T, workspace, splitting, errors) is as for
+ * gdn2_chunk_forward; the gate tensors are checked for overlap with the
+ * output at their input-dtype size. */
+gdn2_status gdn2_chunk_forward_preact(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                      const void *a_pre, const void *b_pre, const void *w_pre, const float *S0,
+                                      void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
 /* Decode: one token per sequence (desc->T must be 1). Reads the state S,
  * applies the step above and writes S back in place, and writes o.
  * Inputs are shaped as for the prefill with T = 1 (B = number of sequences).

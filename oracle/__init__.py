@@ -21,6 +21,10 @@ recurrence, every state kept) is pinned by ``tests/test_oracle_backward.py``:
 central finite differences of the forward, closed-form linear-attention
 gradients, the decay and erase-gate gradients at a = 1, b = 0, and the
 grouped-head sum.
+Gate activations from pre-activations (``activate_gates``, the
+parameterisation of the gates in the synthetic workloads: softplus decay,
+sigmoid gates) are pinned by ``tests/test_oracle_preact.py`` against
+closed-form values, identities and scipy's logistic function.
 Parity unpinned: the exact placement of channel-wise erase and write gates
 when b and w are not uniform (the pages state it only in prose); the oracle
 takes erase (b * k) r^T and write k (w * v)^T.
@@ -118,6 +122,23 @@ def forward(q, k, v, a, b, w, S0=None, nthreads: Optional[int] = None,
     if timing:
         return o, ST, el.value
     return o, ST
+
+
+def activate_gates(a_pre, b_pre, w_pre):
+    """Gates from their pre-activations, in fp64: decay a = exp(-softplus(x)),
+    erase and write gates b, w = sigmoid(x) = exp(-softplus(-x)), with
+    softplus(x) = log(1 + e^x) evaluated as logaddexp(0, x)."""
+    a = np.exp(-np.logaddexp(0.0, _f64(a_pre)))
+    b = np.exp(-np.logaddexp(0.0, -_f64(b_pre)))
+    w = np.exp(-np.logaddexp(0.0, -_f64(w_pre)))
+    return a, b, w
+
+
+def forward_preact(q, k, v, a_pre, b_pre, w_pre, S0=None, **kw):
+    """The recurrence with its gates given as pre-activations (see
+    :func:`activate_gates`); other arguments as :func:`forward`."""
+    a, b, w = activate_gates(a_pre, b_pre, w_pre)
+    return forward(q, k, v, a, b, w, S0, **kw)
 
 
 def backward(q, k, v, a, b, w, S0, dO, dS_T=None, nthreads: Optional[int] = None, lib=None) -> dict:

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+import gated_delta_rule_83_amd as g
 import oracle
 from gated_delta_rule_83_amd import inputs as gi
 from tests.parity import TOL, gpu_prefill, normwise, rand_inputs, to_np
@@ -356,3 +357,74 @@ def test_full_config2_sampled_heads():
 
 def test_full_config3_sampled_heads():
     _full_size(3, [(0, 0), (1, 1), (3, 30)])
+
+
+# ------------------------------------------------------------------ gate pre-activations (fused activation)
+def _preact_compare(d, dtype, chunk, label, tol=None):
+    td = gi.to_torch_preact(d, dtype, DEV)
+    o, ST = g.chunk_forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    ref_o, ref_S = oracle.forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
+    eo, es = normwise(to_np(o), ref_o), normwise(to_np(ST), ref_S)
+    tol = TOL[dtype] if tol is None else tol
+    print(f"[preact {label} {dtype} C={chunk}] o err {eo:.3e}  S_T err {es:.3e}  tol {tol:g}", flush=True)
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+def _rand_preact(rng, B, T, Hqk, Hv, dk, dv, a_mu=0.0):
+    d = rand_inputs(rng, B, T, Hqk, Hv, dk, dv)
+    f = np.float32
+    d["a"] = (rng.standard_normal((B, T, Hv, dk)) + a_mu).astype(f)
+    d["b"] = rng.standard_normal((B, T, Hv, dk)).astype(f)
+    d["w"] = rng.standard_normal((B, T, Hv, dv)).astype(f)
+    return d
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 32), ("f32", 128, 128), ("bf16", 32, 64),
+                                      ("bf16", 128, 128)])
+def test_preact_gates_match_oracle(dt, dk, dv):
+    """Pre-activation gates in the input dtype, activated in the kernel: several
+    chunks plus a ragged tail, grouped heads, random S0."""
+    rng = np.random.default_rng(4000 + dk + dv)
+    _preact_compare(_rand_preact(rng, 2, 2 * 32 + 5, 1, 2, dk, dv), dt, 32, f"dk{dk} dv{dv}")
+
+
+def test_preact_layer_shape_scaled():
+    """The 1.3B layer's gate distributions (decay pre-activation N(-4,1)) as pre-activations, B2 H4 T520."""
+    c = gi.scaled(1, B=2, T=520, H_qk=4, H_v=4)
+    _preact_compare(gi.make_preact_inputs(c), "bf16", 64, "c1-scaled")
+
+
+def test_preact_strong_decay_takes_token_steps():
+    """Decay pre-activations of +40 (a ~ 4e-18) on some tokens: the chunks whose
+    total decay falls below e^-60 are stepped token by token, activating
+    their gates there."""
+    rng = np.random.default_rng(4100)
+    d = _rand_preact(rng, 1, 100, 1, 1, 128, 128)
+    d["a"][0, 40:43] = 40.0
+    _preact_compare(d, "bf16", 32, "strong decay")
+    _preact_compare(d, "f32", 32, "strong decay")
+
+
+def test_preact_split_sequence(monkeypatch):
+    """Through the split path (3 segments) with hard erases."""
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "3")
+    c = gi.scaled(2, T=1024, H_qk=2, H_v=2)
+    _preact_compare(gi.make_preact_inputs(c), "bf16", 64, "split3")
+
+
+def test_preact_full_layer_shape_sampled_heads():
+    """B8 T4096 H16 d128 bf16 with pre-activation gates: two sampled heads."""
+    c = gi.config(1)
+    d = gi.make_preact_inputs(c)
+    td = gi.to_torch_preact(d, "bf16", DEV)
+    o, ST = g.chunk_forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], None, chunk=64)
+    torch.cuda.synchronize()
+    for (n, h) in ((0, 0), (5, 11)):
+        sl = lambda x: x[n:n + 1, :, h:h + 1]
+        ref_o, ref_S = oracle.forward_preact(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]),
+                                             sl(td["w"]), None)
+        eo = normwise(to_np(sl(o)), ref_o)
+        es = normwise(to_np(ST[n:n + 1, h:h + 1]), ref_S)
+        print(f"[preact full n{n} h{h}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
