@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.test_oracle_mutants import _build_mutant
+from tests.mutant_build import build_mutant
 from tests.test_oracle_pins import rand_inputs
 
 
@@ -173,7 +173,7 @@ BWD_MUTANTS = [
 def test_pins_catch_backward_mutant(mut, tmp_path_factory):
     name, old, new = mut
     d = str(tmp_path_factory.mktemp("bwd_mutants"))
-    lib = oracle.bind(_build_mutant(name, old, new, d))
+    lib = oracle.bind(build_mutant(name, old, new, d))
     fwd = functools.partial(oracle.forward, lib=lib)
     bwd = functools.partial(oracle.backward, lib=lib)
     caught = []

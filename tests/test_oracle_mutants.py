@@ -1,15 +1,12 @@
 """Plant one mistake at a time in a copy of the oracle (CPU only) and check that
 the pins catch every one of them. The real oracle is never modified."""
 import functools
-import os
-import subprocess
 
 import pytest
 
 import oracle
+from tests.mutant_build import build_mutant
 from tests.test_oracle_pins import PINS
-
-SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn2_oracle.c")
 
 # (name, text in the oracle, replacement)
 MUTANTS = [
@@ -28,24 +25,11 @@ MUTANTS = [
 ]
 
 
-@functools.lru_cache(maxsize=None)
-def _build_mutant(name, old, new, tmpdir):
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
-    path_c = os.path.join(tmpdir, f"mut_{name}.c")
-    path_so = os.path.join(tmpdir, f"mut_{name}.so")
-    with open(path_c, "w") as f:
-        f.write(src.replace(old, new))
-    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-D_POSIX_C_SOURCE=200809L",
-                           "-o", path_so, path_c, "-lpthread"])
-    return path_so
-
-
 @pytest.mark.parametrize("mut", MUTANTS, ids=lambda m: m[0])
 def test_pins_catch_mutant(mut, tmp_path_factory):
     name, old, new = mut
     d = str(tmp_path_factory.mktemp("mutants"))
-    lib = oracle.bind(_build_mutant(name, old, new, d))
+    lib = oracle.bind(build_mutant(name, old, new, d))
     fwd = functools.partial(oracle.forward, lib=lib)
     caught = []
     for pin in PINS:
