@@ -264,7 +264,7 @@ def main():
             g.chunk_forward_preact(tpp["q"], tpp["k"], tpp["v"], tpp["a"], tpp["b"], tpp["w"], None, chunk=cp.chunk,
                                    o=o, S_T=S_T, stream=stream)
 
-        for _ in range(20):
+        for _ in range(100):
             prefill_preact()
         torch.cuda.synchronize()
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
