@@ -375,3 +375,40 @@ def decode_step(q, k, v, a, b, w, S, o=None, stream=None):
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return o
+
+
+# ------------------------------------------------------------------ autograd
+def _autograd_function():
+    import torch
+
+    class GatedDeltaRule2(torch.autograd.Function):
+        """o, S_T = prefill(q, k, v, a, b, w, S0); backward through
+        gdn2_chunk_backward. The saved tensors are the inputs themselves."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, a, b, w, S0, chunk):
+            o, S_T = chunk_forward(q, k, v, a, b, w, S0, chunk=chunk)
+            ctx.save_for_backward(q, k, v, a, b, w, S0)
+            return o, S_T
+
+        @staticmethod
+        def backward(ctx, dO, dS_T):
+            q, k, v, a, b, w, S0 = ctx.saved_tensors
+            g = chunk_backward(q, k, v, a, b, w, S0, dO.contiguous(),
+                               None if dS_T is None else dS_T.contiguous(), want_dS0=S0 is not None)
+            return g["dq"], g["dk"], g["dv"], g["da"], g["db"], g["dw"], g["dS0"], None
+
+    return GatedDeltaRule2
+
+
+_GDR2 = None
+
+
+def gated_delta_rule(q, k, v, a, b, w, S0=None, chunk: int = 64):
+    """Differentiable prefill for PyTorch training: returns (o, S_T) like
+    chunk_forward; gradients of q, k, v, a, b, w and S0 come from
+    gdn2_chunk_backward."""
+    global _GDR2
+    if _GDR2 is None:
+        _GDR2 = _autograd_function()
+    return _GDR2.apply(q, k, v, a, b, w, S0, chunk)

@@ -44,8 +44,9 @@ def compare(td, dO, dST, dtype, label, tol=None, grads=None):
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)])
 def test_fp32_shapes_ragged_gqa(dk, dv):
-    """fp32 at every head size: several 8-token sub-segments plus a ragged
-    tail, two value heads per query/key head, random S0 and dS_T."""
+    """fp32 at every head size: several 4-token sub-segments and 16-token
+    forward stages plus a ragged tail, two value heads per query/key head,
+    random S0 and dS_T."""
     rng = np.random.default_rng(3000 + dk + 7 * dv)
     d = rand_inputs(rng, 2, 21, 1, 2, dk, dv)
     td = gi.to_torch(d, "f32", DEV)
@@ -53,9 +54,10 @@ def test_fp32_shapes_ragged_gqa(dk, dv):
     compare(td, dO, dST, "f32", f"dk{dk} dv{dv} T21")
 
 
-@pytest.mark.parametrize("T", [1, 7, 8, 9, 64])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 15, 16, 17, 64])
 def test_fp32_lengths_null_state(T):
-    """Sequence lengths around the 8-token sub-segment, S0 and dS_T absent."""
+    """Sequence lengths around the 4-token sub-segment and the 16-token
+    forward stage, S0 and dS_T absent."""
     rng = np.random.default_rng(3100 + T)
     d = rand_inputs(rng, 1, T, 2, 2, 32, 32, with_s0=False)
     td = gi.to_torch(d, "f32", DEV)
@@ -133,3 +135,46 @@ def test_full_layer_shape_sampled_heads():
         print(f"[backward full n{n} h{h}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
         bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
         assert not bad, bad
+
+
+def test_autograd_wrapper_gradients():
+    """gated_delta_rule under torch.autograd: the loss <dO, o> + <dS_T, S_T>
+    back-propagates to the oracle's gradients."""
+    rng = np.random.default_rng(3700)
+    d = rand_inputs(rng, 2, 45, 1, 2, 64, 64)
+    td = gi.to_torch(d, "f32", DEV)
+    leaves = {nm: td[nm].clone().requires_grad_(True) for nm in ("q", "k", "v", "a", "b", "w", "S0")}
+    dO, dST = upstream(rng, d, "f32")
+    o, ST = g.gated_delta_rule(*(leaves[nm] for nm in ("q", "k", "v", "a", "b", "w", "S0")), chunk=32)
+    ((o * dO).sum() + (ST * dST).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle.backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    for nm in ("q", "k", "v", "a", "b", "w", "S0"):
+        err = normwise(to_np(leaves[nm].grad), ref["d" + nm])
+        print(f"[autograd d{nm}] {err:.2e}", flush=True)
+        assert err <= TOL["f32"], (nm, err)
+
+
+def test_grouped_heads_full_size_sampled():
+    """B4 T16384 H_qk16 H_v32 d128 bf16 (the grouped-head layout): the whole
+    backward on the GPU; one query/key head's pair of value heads against the
+    oracle, so that dq, dk are the sums over the two."""
+    c = gi.config(3)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(3800)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    n, qk = 3, 9
+    hs = slice(2 * qk, 2 * qk + 2)
+    sv = lambda x: x[n:n + 1, :, hs]
+    ref = oracle.backward(td["q"][n:n + 1, :, qk:qk + 1], td["k"][n:n + 1, :, qk:qk + 1], sv(td["v"]), sv(td["a"]),
+                          sv(td["b"]), sv(td["w"]), None if td["S0"] is None else td["S0"][n:n + 1, hs],
+                          sv(dO), dST[n:n + 1, hs], nthreads=2)
+    got = {"dq": gg["dq"][n:n + 1, :, qk:qk + 1], "dk": gg["dk"][n:n + 1, :, qk:qk + 1], "dv": sv(gg["dv"]),
+           "da": sv(gg["da"]), "db": sv(gg["db"]), "dw": sv(gg["dw"]), "dS0": gg["dS0"][n:n + 1, hs]}
+    errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in NAMES}
+    print("[backward grouped full] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, bad
