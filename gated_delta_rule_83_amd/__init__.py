@@ -43,6 +43,7 @@ EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forw
             "gdn2_chunk_forward_preact",
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
             "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
+            "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes",
             "gdn2_status_string", "gdn2_version")
 
 
@@ -89,6 +90,10 @@ def load(path: Optional[str] = None):
     lib.gdn2_chunk_backward.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
     lib.gdn2_chunk_backward_workspace_bytes.restype = sz
     lib.gdn2_chunk_backward_workspace_bytes.argtypes = [dp]
+    lib.gdn2_chunk_backward_varlen.restype = ctypes.c_int
+    lib.gdn2_chunk_backward_varlen.argtypes = [dp] + [vp] * 17 + [vp, sz, vp]
+    lib.gdn2_chunk_backward_varlen_workspace_bytes.restype = sz
+    lib.gdn2_chunk_backward_varlen_workspace_bytes.argtypes = [dp]
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_status_string.argtypes = [ctypes.c_int]
     lib.gdn2_version.restype = ctypes.c_int
@@ -152,6 +157,17 @@ def gdn2_chunk_backward(desc, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db
                         workspace_bytes=0, stream=0) -> int:
     return load().gdn2_chunk_backward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w, S0, dO,
                                       dS_T, dq, dk, dv, da, db, dw, dS0, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_backward_varlen_workspace_bytes(desc) -> int:
+    return load().gdn2_chunk_backward_varlen_workspace_bytes(None if desc is None else ctypes.byref(desc))
+
+
+def gdn2_chunk_backward_varlen(desc, cu_seqlens, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0,
+                               workspace=0, workspace_bytes=0, stream=0) -> int:
+    return load().gdn2_chunk_backward_varlen(None if desc is None else ctypes.byref(desc), cu_seqlens, q, k, v, a,
+                                             b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
+                                             workspace_bytes, stream)
 
 
 def gdn2_decode_step(desc, q, k, v, a, b, w, S, o, stream=0) -> int:
@@ -226,18 +242,34 @@ def chunk_backward(q, k, v, a, b, w, S0, dO, dS_T=None, want_dS0: bool = True, g
     input dtype), da, db, dw (fp32) and dS0 (fp32, or None without want_dS0).
     `grads` may hold preallocated outputs under those names, and `workspace`
     a uint8 device tensor of at least gdn2_chunk_backward_workspace_bytes."""
+    return _backward(q, k, v, a, b, w, S0, dO, dS_T, None, want_dS0, grads, workspace, stream)
+
+
+def chunk_backward_varlen(q, k, v, a, b, w, cu_seqlens, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
+                          workspace=None, stream=None) -> dict:
+    """Gradients of chunk_forward_varlen (packed sequences; shapes as there,
+    dO like v, dS_T [N,H_v,d_k,d_v] or None). Returns the dict of chunk_backward,
+    token gradients shaped like their inputs."""
+    return _backward(q, k, v, a, b, w, S0, dO, dS_T, cu_seqlens, want_dS0, grads, workspace, stream)
+
+
+def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, stream) -> dict:
     import torch
-    B, T, H_qk, d_k = q.shape
-    H_v, d_v = v.shape[2], v.shape[3]
+    T, H_qk, d_k = q.shape[-3:]
+    H_v, d_v = v.shape[-2], v.shape[-1]
+    if cu is None:
+        B = q.shape[0]
+    else:
+        _check(cu, "cu_seqlens", torch.int32)
+        B = cu.numel() - 1
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
         _check(t, nm, q.dtype)
     for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0"), (dS_T, "dS_T")):
         _check(t, nm, torch.float32)
     g = dict(grads or {})
     dev = q.device
-    shapes = {"dq": ((B, T, H_qk, d_k), q.dtype), "dk": ((B, T, H_qk, d_k), q.dtype),
-              "dv": ((B, T, H_v, d_v), q.dtype), "da": ((B, T, H_v, d_k), torch.float32),
-              "db": ((B, T, H_v, d_k), torch.float32), "dw": ((B, T, H_v, d_v), torch.float32)}
+    shapes = {"dq": (q.shape, q.dtype), "dk": (k.shape, q.dtype), "dv": (v.shape, q.dtype),
+              "da": (a.shape, torch.float32), "db": (b.shape, torch.float32), "dw": (w.shape, torch.float32)}
     if want_dS0:
         shapes["dS0"] = ((B, H_v, d_k, d_v), torch.float32)
     for nm, (shape, dt) in shapes.items():
@@ -246,43 +278,21 @@ def chunk_backward(q, k, v, a, b, w, S0, dO, dS_T=None, want_dS0: bool = True, g
         _check(g[nm], nm, dt)
     g.setdefault("dS0", None)
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
-    ws = gdn2_chunk_backward_workspace_bytes(desc)
+    ws = (gdn2_chunk_backward_workspace_bytes(desc) if cu is None
+          else gdn2_chunk_backward_varlen_workspace_bytes(desc))
     if workspace is None and ws:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
     wbytes = workspace.numel() if workspace is not None else 0
-    st = gdn2_chunk_backward(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO),
-                             _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]),
-                             _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), wbytes, _stream(stream))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
+            _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
+            _ptr(workspace), wbytes, _stream(stream))
+    if cu is None:
+        st = gdn2_chunk_backward(desc, *ptrs)
+    else:
+        st = gdn2_chunk_backward_varlen(desc, _ptr(cu), *ptrs)
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return g
-
-
-def chunk_forward_preact(q, k, v, a_pre, b_pre, w_pre, S0=None, chunk: int = 64, o=None, S_T=None,
-                         want_state: bool = True, stream=None):
-    """Prefill with the per-channel gates given as pre-activations in the
-    input dtype (decay a = exp(-softplus(a_pre)), b = sigmoid(b_pre),
-    w = sigmoid(w_pre)), activated in the kernel. Shapes as chunk_forward."""
-    import torch
-    B, T, H_qk, d_k = q.shape
-    H_v, d_v = v.shape[2], v.shape[3]
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (a_pre, "a_pre"), (b_pre, "b_pre"), (w_pre, "w_pre")):
-        _check(t, nm, q.dtype)
-    _check(S0, "S0", torch.float32)
-    if o is None:
-        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
-    if S_T is None and want_state:
-        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
-    _check(o, "o", q.dtype)
-    _check(S_T, "S_T", torch.float32)
-    desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
-    ws = gdn2_chunk_forward_workspace_bytes(desc)
-    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
-    st = gdn2_chunk_forward_preact(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a_pre), _ptr(b_pre), _ptr(w_pre),
-                                   _ptr(S0), _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
-    if st != GDN2_OK:
-        raise Gdn2Error(st)
-    return o, S_T
 
 
 def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_T=None,

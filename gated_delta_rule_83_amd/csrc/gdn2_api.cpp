@@ -72,6 +72,11 @@ gdn2::PrefillArgs prefill_args(const gdn2_desc *d) {
   return p;
 }
 
+gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *q, const void *k, const void *v,
+                             const float *a, const float *b, const float *w, const float *S0, const void *dO,
+                             const float *dS_T, void *dq, void *dk, void *dv, float *da, float *db, float *dw,
+                             float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen);
+
 // gdn2_chunk_forward and gdn2_chunk_forward_preact: per-channel gates, fp32
 // activated values or pre-activations in the input dtype.
 gdn2_status forward_general(const gdn2_desc *d, const void *q, const void *k, const void *v, const void *a,
@@ -295,7 +300,12 @@ extern "C" {
 
 size_t gdn2_chunk_backward_workspace_bytes(const gdn2_desc *d) {
   if (check_desc(d, false) != GDN2_OK) return 0;
-  return gdn2::backward_workspace_bytes(d->B, d->T, d->H_v, d->d_k, d->d_v);
+  return gdn2::backward_workspace_bytes(d->B, (size_t)d->B * d->T, d->H_v, d->d_k, d->d_v);
+}
+
+size_t gdn2_chunk_backward_varlen_workspace_bytes(const gdn2_desc *d) {
+  if (check_desc(d, false) != GDN2_OK) return 0;
+  return gdn2::backward_workspace_bytes(d->B, (size_t)d->T, d->H_v, d->d_k, d->d_v);
 }
 
 gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k, const void *v,
@@ -303,15 +313,40 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k
                                 const void *dO, const float *dS_T, void *dq, void *dk, void *dv, float *da,
                                 float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
                                 void *stream) {
+  return backward_general(d, nullptr, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
+                          workspace_bytes, stream, false);
+}
+
+gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                                       const void *v, const float *a, const float *b, const float *w,
+                                       const float *S0, const void *dO, const float *dS_T, void *dq, void *dk,
+                                       void *dv, float *da, float *db, float *dw, float *dS0, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  return backward_general(d, cu_seqlens, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
+                          workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// gdn2_chunk_backward and gdn2_chunk_backward_varlen (cu_seqlens non-null:
+// B sequences packed along T tokens).
+gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *q, const void *k, const void *v,
+                             const float *a, const float *b, const float *w, const float *S0, const void *dO,
+                             const float *dS_T, void *dq, void *dk, void *dv, float *da, float *db, float *dw,
+                             float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
   const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
   const size_t dkk = (size_t)d->d_k, dvv = (size_t)d->d_v;
   const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
   if (B == 0) return GDN2_OK;
-  const size_t ws_need = gdn2_chunk_backward_workspace_bytes(d);
+  if (varlen && !cu) return GDN2_ERR_NULL_POINTER;
+  const size_t BT = varlen ? T : B * T;  // tokens in all
+  const size_t ws_need = gdn2::backward_workspace_bytes(d->B, BT, d->H_v, d->d_k, d->d_v);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
-  const bool tokens = T > 0;
+  const bool tokens = BT > 0;
   if (tokens && (!q || !k || !v || !a || !b || !w || !dO || !dq || !dk || !dv || !da || !db || !dw))
     return GDN2_ERR_NULL_POINTER;
   const void *ptrs[] = {q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0};
@@ -319,12 +354,11 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k
     if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
   if (ws_need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_BAD_SHAPE;
 
-  const size_t nqk = tokens ? B * T * Hqk * dkk : 0, nab = tokens ? B * T * Hv * dkk : 0;
-  const size_t nvw = tokens ? B * T * Hv * dvv : 0, ns = B * Hv * dkk * dvv;
+  const size_t nqk = BT * Hqk * dkk, nab = BT * Hv * dkk, nvw = BT * Hv * dvv, ns = B * Hv * dkk * dvv;
   const Range ins[] = {range_of(q, nqk * es),  range_of(k, nqk * es), range_of(v, nvw * es),
                        range_of(a, nab * 4),   range_of(b, nab * 4),  range_of(w, nvw * 4),
                        range_of(S0, S0 ? ns * 4 : 0), range_of(dO, nvw * es),
-                       range_of(dS_T, dS_T ? ns * 4 : 0)};
+                       range_of(dS_T, dS_T ? ns * 4 : 0), range_of(cu, varlen ? (B + 1) * sizeof(int32_t) : 0)};
   const Range outs[] = {range_of(dq, nqk * es), range_of(dk, nqk * es), range_of(dv, nvw * es),
                         range_of(da, nab * 4),  range_of(db, nab * 4),  range_of(dw, nvw * 4),
                         range_of(dS0, dS0 ? ns * 4 : 0), range_of(workspace, ws_need)};
@@ -345,8 +379,9 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k
   p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.dO = dO; p.dST = dS_T;
   p.dq = dq; p.dk = dk; p.dv = dv; p.da = da; p.db = db; p.dw = dw; p.dS0 = dS0;
   p.workspace = workspace;
+  p.cu_seqlens = varlen ? cu : nullptr;
   const hipError_t e = gdn2::launch_backward(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace

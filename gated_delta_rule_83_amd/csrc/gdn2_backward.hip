@@ -28,13 +28,13 @@
 // two-step reduce-scatter across the four column pairs, then a fixed-order
 // sum over the waves in LDS (deterministic, no atomics).
 //
-// Memory: phase 1 runs the recurrence forward and stores the state at the
-// start of every kSub-token sub-segment and every token's k-read (fp32, in
-// the workspace); phase 2 walks the sub-segments backward, rebuilds a
-// sub-segment's kSub + 1 states into registers from its checkpoint and the
-// stored k-reads (no key sums), and runs the adjoint over it.
-// Inputs of a sub-segment are staged in LDS (one set of loads per
-// workgroup, requested one sub-segment ahead). Key-side sums go to the
+// Memory: phase 1 runs the recurrence forward in 16-token stages and stores
+// the state at the start of every kSub-token sub-segment and every token's
+// k-read (fp32, in the workspace); phase 2 walks the sub-segments backward,
+// rebuilds a sub-segment's kSub + 1 states into registers from its
+// checkpoint and the stored k-reads (no key sums), and runs the adjoint over
+// it. Inputs of a stage or sub-segment are staged in LDS (one set of loads
+// per workgroup, requested one stage or sub-segment ahead). Key-side sums go to the
 // workspace per column block and are added up by backward_reduce_kernel,
 // which also sums the value heads that share a query/key head.
 #include "gdn2_device.hpp"
@@ -208,7 +208,20 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   const int cb = blockIdx.x % ncb, unit = blockIdx.x / ncb;  // unit = n * H_v + h
   const int n = unit / p.H_v, h = unit - n * p.H_v;
   const int g = h / (p.H_v / p.H_qk);
-  const int T = p.T, d_v = p.d_v;
+  const int d_v = p.d_v;
+  // the sequence's tokens: packed sequences take theirs from cu (offsets
+  // clamped to [0, p.T]); otherwise sequence n is tokens n*T .. n*T + T-1
+  size_t tok0;  // first token of the sequence in the token axis
+  int T;        // its length
+  if (p.cu) {
+    const int t0 = min(max(p.cu[n], 0), p.T), t1 = min(max(p.cu[n + 1], t0), p.T);
+    tok0 = (size_t)t0;
+    T = t1 - t0;
+  } else {
+    tok0 = (size_t)n * p.T;
+    T = p.T;
+  }
+  const size_t BT = p.cu ? (size_t)p.T : (size_t)p.B * p.T;  // tokens in all
   const int nsub = (T + L - 1) / L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -217,7 +230,6 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   const int col = cb * CB + lcol;      // ... within the head
   const int key0 = kg * KPL;
 
-  const size_t tok0 = (size_t)n * T;  // first token of the sequence
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
   const float *ah = p.a + tok0 * p.H_v * DK + (size_t)h * DK;
@@ -232,7 +244,10 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   // piece q of every thread contiguous (each store instruction writes one
   // contiguous range)
   constexpr int CW = 2 * KPL < 4 ? 2 * KPL : 4;
-  float *ckp = p.ck + ((size_t)unit * ncb + cb) * (size_t)nsub * (DK * CB) + (size_t)tid * CW;
+  // a sequence's checkpoints start at slot tok0 / L + n of its (head, column
+  // block) range of BT / L + B slots: room for its ceil(T / L) sub-segments
+  const size_t nslot = BT / L + p.B;
+  float *ckp = p.ck + (((size_t)h * ncb + cb) * nslot + tok0 / L + n) * (DK * CB) + (size_t)tid * CW;
   auto store_ck = [&](float *ck, const float (&x)[KPL][2]) {
 #pragma unroll
     for (int q = 0; q < 2 * KPL / CW; ++q) {
@@ -243,12 +258,12 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         *reinterpret_cast<floatx2 *>(ck + q * (Cf::NT * CW)) = floatx2{x[q][0], x[q][1]};
     }
   };
-  // k-reads of the block's columns, [token][d_v] per (n, h)
-  float *rh = p.rk + (size_t)unit * T * d_v + cb * CB;
+  // k-reads of the block's columns ([token][H_v][d_v], like v)
+  float *rh = p.rk + tok0 * vw_t + (size_t)h * d_v + cb * CB;
 
   // Request sub-segment `sub`'s inputs into registers; tokens past the end
   // are identity steps (a = 1, everything else 0).
-  auto request = [&](int sub, Stage<DK, CB> &st, bool backward) {
+  auto request = [&](int sub, Stage<DK, CB> &st) {
 #pragma unroll
     for (int it = 0; it < Cf::KIT; ++it) {
       const int idx = tid + it * Cf::NT;
@@ -256,7 +271,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const int t = sub * L + tt;
       const bool ok = idx < Cf::NKS && t < T;
       st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
-      st.q[it] = ok && backward ? E::ld4(qh + t * qk_t + 4 * kq) : zero4();
+      st.q[it] = ok ? E::ld4(qh + t * qk_t + 4 * kq) : zero4();
       st.a[it] = ok ? *reinterpret_cast<const floatx4 *>(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
       st.b[it] = ok ? *reinterpret_cast<const floatx4 *>(bh + t * ab_t + 4 * kq) : zero4();
     }
@@ -266,8 +281,8 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const bool ok = tid < Cf::NCS && t < T;
       st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
       st.w = ok ? *reinterpret_cast<const floatx4 *>(wh + t * vw_t + 4 * cq) : zero4();
-      st.d = ok && backward ? E::ld4(dOh + t * vw_t + 4 * cq) : zero4();
-      st.r = ok && backward ? *reinterpret_cast<const floatx4 *>(rh + (size_t)t * d_v + 4 * cq) : zero4();
+      st.d = ok ? E::ld4(dOh + t * vw_t + 4 * cq) : zero4();
+      st.r = ok ? *reinterpret_cast<const floatx4 *>(rh + (size_t)t * vw_t + 4 * cq) : zero4();
     }
   };
   auto stash = [&](const Stage<DK, CB> &st) {
@@ -404,7 +419,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         const int tt = tid / (CB / 4), cq = tid % (CB / 4);
         const int t = sb * Cf::L1 + tt;
         if (t < T)
-          *reinterpret_cast<floatx4 *>(rh + (size_t)t * d_v + 4 * cq) =
+          *reinterpret_cast<floatx4 *>(rh + (size_t)t * vw_t + 4 * cq) =
               *reinterpret_cast<const floatx4 *>(&sm.f.r[tt][4 * cq]);
       }
     }
@@ -442,7 +457,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   __syncthreads();
   Stage<DK, CB> st;
   if (nsub > 0) {
-    request(nsub - 1, st, true);
+    request(nsub - 1, st);
     request_ck(nsub - 1);
   }
   for (int sub = nsub - 1; sub >= 0; --sub) {
@@ -457,7 +472,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       hs[0][e][1] = ckn[e][1];
     }
     if (sub > 0) {
-      request(sub - 1, st, true);
+      request(sub - 1, st);
       request_ck(sub - 1);
     }
     // (the k-reads come from phase 1: no key sums here)
@@ -549,7 +564,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         floatx4 acc = *reinterpret_cast<const floatx4 *>(&sm.b.red[0][tt][vec][4 * kq]);
 #pragma unroll
         for (int w2 = 1; w2 < Cf::NWV; ++w2) acc += *reinterpret_cast<const floatx4 *>(&sm.b.red[w2][tt][vec][4 * kq]);
-        float *dst = p.part + (((size_t)cb * p.B * T + tok0 + t) * p.H_v + h) * (4 * DK) + vec * DK + 4 * kq;
+        float *dst = p.part + (((size_t)cb * BT + tok0 + t) * p.H_v + h) * (4 * DK) + vec * DK + 4 * kq;
         *reinterpret_cast<floatx4 *>(dst) = acc;
       }
     }
@@ -581,7 +596,7 @@ __global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) 
   using ET = typename E::T;
   constexpr int TPR = DK / 4;  // threads per (token, g) row, 4 keys each
   const int ncb = p.d_v / bwd_cb(p.d_v);
-  const size_t BT = (size_t)p.B * p.T;
+  const size_t BT = p.cu ? (size_t)p.T : (size_t)p.B * p.T;
   const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= BT * p.H_qk) return;
   const int kq = threadIdx.x % TPR;
@@ -621,8 +636,9 @@ hipError_t launch_t(const BackwardParams &p, hipStream_t st) {
   const int ncb = p.d_v / CB;
   hipLaunchKernelGGL((backward_kernel<DK, CB, BF16>), dim3(p.B * p.H_v * ncb), dim3(BwdCfg<DK, CB>::NT), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.T == 0) return e;
-  const size_t rows = (size_t)p.B * p.T * p.H_qk;
+  const size_t BT = p.cu ? (size_t)p.T : (size_t)p.B * p.T;
+  if (e != hipSuccess || BT == 0) return e;
+  const size_t rows = BT * p.H_qk;
   const size_t rpb = 256 / (DK / 4);
   hipLaunchKernelGGL((backward_reduce_kernel<DK, BF16>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
                      p);
@@ -660,12 +676,16 @@ hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st)
 #if GDN2_BWD_BF16
 hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st);
 
-size_t backward_workspace_bytes(int B, int T, int H_v, int d_k, int d_v) {
-  const size_t nsub = ((size_t)T + kSub - 1) / kSub;
+// Checkpoints: per (head, column block) BT / kSub + B slots of d_k x CB fp32
+// (each sequence needs at most ceil(T_n / kSub) <= T_n / kSub + 1 of them);
+// key-side sums: ncb x BT x H_v x 4 x d_k fp32; k-reads: BT x H_v x d_v fp32.
+// BT = B * T, or T for packed sequences.
+size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v) {
+  if (BT == 0) return 0;  // no tokens: only dS0 = dS_T, no scratch
   const size_t ncb = (size_t)d_v / bwd_cb(d_v);
-  const size_t ck = (size_t)B * H_v * nsub * d_k * d_v * 4;
-  const size_t part = ncb * (size_t)B * T * H_v * 4 * d_k * 4;
-  const size_t rk = (size_t)B * H_v * T * d_v * 4;
+  const size_t ck = (BT / kSub + B) * (size_t)H_v * d_k * d_v * 4;
+  const size_t part = ncb * BT * H_v * 4 * d_k * 4;
+  const size_t rk = BT * H_v * d_v * 4;
   return align256(ck) + align256(part) + align256(rk);
 }
 
@@ -676,10 +696,11 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   p.dO = a.dO; p.dST = a.dST;
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.da = a.da; p.db = a.db; p.dw = a.dw; p.dS0 = a.dS0;
   p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
-  const size_t nsub = ((size_t)a.T + kSub - 1) / kSub;
-  const size_t ck = (size_t)a.B * a.H_v * nsub * a.d_k * a.d_v * 4;
+  p.cu = a.cu_seqlens;
+  const size_t BT = a.cu_seqlens ? (size_t)a.T : (size_t)a.B * a.T;
+  const size_t ck = (BT / kSub + a.B) * (size_t)a.H_v * a.d_k * a.d_v * 4;
+  const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * BT * a.H_v * 4 * a.d_k * 4;
   p.ck = reinterpret_cast<float *>(a.workspace);
-  const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * a.B * a.T * a.H_v * 4 * a.d_k * 4;
   p.part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck));
   p.rk = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck) + align256(part));
   return a.bf16 ? launch_backward_bf16(p, a.d_k, st) : launch_backward_f32(p, a.d_k, st);

@@ -67,6 +67,9 @@ struct BackwardArgs {
   void *dq, *dk, *dv;
   float *da, *db, *dw, *dS0;
   void *workspace;  // backward_workspace_bytes() bytes, 256-byte aligned
+  // packed sequences: B + 1 token offsets (device), or null for B sequences
+  // of T tokens each
+  const int32_t *cu_seqlens;
 };
 
 // Kernel parameters: the arguments plus the three workspace regions (state
@@ -79,10 +82,11 @@ struct BackwardParams {
   void *dq, *dk, *dv;
   float *da, *db, *dw, *dS0;
   float *ck, *part, *rk;
+  const int32_t *cu;
   int B, T, H_qk, H_v, d_v;
 };
 
-size_t backward_workspace_bytes(int B, int T, int H_v, int d_k, int d_v);
+size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v);
 hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);

@@ -207,8 +207,9 @@ gdn2_status gdn2_decode_step(const gdn2_desc *desc, const void *q, const void *k
  *          checkpoints every 4 tokens, per 64-column block key-side partial
  *          sums and every token's k-read: about
  *          (d_k * d_v / 4 + 4 * d_k * ceil(d_v / 64) + d_v) * 4 bytes per
- *          token and value head), 256-byte aligned; NULL only when that size
- *          is 0. Contents on return are unspecified.
+ *          token and value head, plus d_k * d_v * 4 per sequence and value
+ *          head), 256-byte aligned; NULL only when that size is 0. Contents
+ *          on return are unspecified.
  * Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums; all
  * arithmetic is fp32. The result is deterministic (no atomics).
  * Errors: as for gdn2_chunk_forward; a missing required pointer is
@@ -221,6 +222,24 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *desc, const void *q, const void
                                 const void *dO, const float *dS_T, void *dq, void *dk, void *dv, float *da,
                                 float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/* Backward pass of gdn2_chunk_forward_varlen: desc->B sequences packed along
+ * desc->T tokens, sequence n = tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
+ * (cu_seqlens: B + 1 non-decreasing int32 device offsets; offsets outside
+ * [0, T] are clamped). The token tensors (q, k, v, a, b, w, dO and the token
+ * gradients) hold desc->T tokens; S0, dS_T and dS0 hold one state per
+ * sequence. Each sequence's gradients are computed exactly as
+ * gdn2_chunk_backward computes them for that sequence alone. The workspace
+ * is gdn2_chunk_backward_varlen_workspace_bytes(desc) bytes (the same
+ * regions as gdn2_chunk_backward's, over T tokens in all). Errors as for
+ * gdn2_chunk_backward, plus GDN2_ERR_NULL_POINTER for a null cu_seqlens when
+ * B > 0. */
+size_t gdn2_chunk_backward_varlen_workspace_bytes(const gdn2_desc *desc);
+gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *desc, const int32_t *cu_seqlens, const void *q,
+                                       const void *k, const void *v, const float *a, const float *b, const float *w,
+                                       const float *S0, const void *dO, const float *dS_T, void *dq, void *dk,
+                                       void *dv, float *da, float *db, float *dw, float *dS0, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *gdn2_status_string(gdn2_status status);

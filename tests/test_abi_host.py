@@ -215,8 +215,8 @@ def test_backward_workspace_query_and_argument_errors():
     d_k-vectors per token, head and 64-column block, and one d_v-vector of
     k-reads per token and head; errors before any launch."""
     d = g.make_desc(2, 20, 1, 2, 64, 64, 64, g.GDN2_BF16)
-    nsub, ncb = 5, 1  # checkpoints every 4 tokens; one 64-column block
-    ck = 2 * 2 * nsub * 64 * 64 * 4
+    nslot, ncb = 2 * 20 // 4 + 2, 1  # checkpoint slots: B*T/4 + B; one 64-column block
+    ck = 2 * nslot * 64 * 64 * 4
     part = ncb * 2 * 20 * 2 * 4 * 64 * 4
     rk = 2 * 2 * 20 * 64 * 4
     up = lambda x: (x + 255) // 256 * 256
@@ -259,3 +259,22 @@ def test_backward_workspace_query_and_argument_errors():
     p = list(base)
     p[15] = p[8] + 64  # dS0 partially over dS_T
     assert bwd(d, p, ws, need) == g.GDN2_ERR_ALIAS
+
+
+def test_backward_varlen_workspace_and_errors():
+    """Packed sequences: the workspace counts desc.T tokens in all; a null
+    cu_seqlens and overlaps with it are rejected before any launch."""
+    d = g.make_desc(3, 50, 1, 2, 64, 64, 64, g.GDN2_BF16)
+    up = lambda x: (x + 255) // 256 * 256
+    need = g.gdn2_chunk_backward_varlen_workspace_bytes(d)
+    assert need == up((50 // 4 + 3) * 2 * 64 * 64 * 4) + up(1 * 50 * 2 * 4 * 64 * 4) + up(50 * 2 * 64 * 4)
+    ws = FAKE + 40 * (1 << 30)
+    base = [FAKE + i * (1 << 30) for i in range(16)]
+    cu = FAKE + 50 * (1 << 30)
+    call = lambda cu_, p, w=ws, nb=need: g.gdn2_chunk_backward_varlen(d, cu_, *p, w, nb, 0)
+    assert call(0, base) == g.GDN2_ERR_NULL_POINTER
+    assert call(cu, base, 0, 0) == g.GDN2_ERR_WORKSPACE
+    p = list(base)
+    p[9] = cu  # dq over cu_seqlens
+    assert call(cu, p) == g.GDN2_ERR_ALIAS
+    assert g.gdn2_chunk_backward_varlen(g.make_desc(0, 50, 1, 2, 64, 64, 64, 1), 0, *([0] * 16), 0, 0, 0) == g.GDN2_OK

@@ -178,3 +178,43 @@ def test_grouped_heads_full_size_sampled():
     print("[backward grouped full] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 64, 64), ("bf16", 128, 128), ("f32", 16, 128)])
+def test_varlen_matches_oracle_and_separate_calls(dt, dk, dv):
+    """Packed sequences of lengths 0, 1, 5, 17, 64, 3 (ragged against the
+    4-token sub-segments and 16-token stages), grouped heads, per-sequence S0
+    and dS_T: each sequence's gradients equal the oracle's and, bit for bit,
+    those of gdn2_chunk_backward on the sequence alone."""
+    rng = np.random.default_rng(3900 + dk + dv)
+    lens = [0, 1, 5, 17, 64, 3]
+    N, T = len(lens), sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = rand_inputs(rng, 1, T, 1, 2, dk, dv)
+    S0 = (rng.standard_normal((N, 2, dk, dv)) * 0.5).astype(np.float32)
+    td = gi.to_torch(d, dt, DEV)
+    tdt = td["q"].dtype
+    dO = torch.from_numpy(rng.standard_normal((1, T, 2, dv)).astype(np.float32)).to(tdt).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((N, 2, dk, dv)).astype(np.float32)).to(DEV)
+    S0t = torch.from_numpy(S0).to(DEV)
+    cut = torch.from_numpy(cu).to(DEV)
+    gv = g.chunk_backward_varlen(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], cut, S0t, dO, dST)
+    torch.cuda.synchronize()
+    for n in range(N):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: x[:, t0:t1].contiguous()
+        if t1 > t0:
+            ref = oracle.backward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]),
+                                  S0t[n:n + 1], sl(dO), dST[n:n + 1])
+            errs = {nm: normwise(to_np(gv[nm][:, t0:t1] if nm != "dS0" else gv[nm][n:n + 1]), ref[nm])
+                    for nm in NAMES}
+            print(f"[backward varlen {dt} seq{n} len{t1 - t0}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()),
+                  flush=True)
+            bad = {k: v for k, v in errs.items() if not v <= TOL[dt]}
+            assert not bad, (n, bad)
+        alone = g.chunk_backward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]),
+                                 S0t[n:n + 1].contiguous(), sl(dO), dST[n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        for nm in ("dq", "dk", "dv", "da", "db", "dw"):
+            assert torch.equal(gv[nm][:, t0:t1], alone[nm]), (n, nm)
+        assert torch.equal(gv["dS0"][n:n + 1], alone["dS0"]), n
