@@ -43,7 +43,7 @@ EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forw
             "gdn2_chunk_forward_preact",
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
             "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
-            "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes",
+            "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes", "gdn2_chunk_backward_preact",
             "gdn2_status_string", "gdn2_version")
 
 
@@ -90,6 +90,8 @@ def load(path: Optional[str] = None):
     lib.gdn2_chunk_backward.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
     lib.gdn2_chunk_backward_workspace_bytes.restype = sz
     lib.gdn2_chunk_backward_workspace_bytes.argtypes = [dp]
+    lib.gdn2_chunk_backward_preact.restype = ctypes.c_int
+    lib.gdn2_chunk_backward_preact.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
     lib.gdn2_chunk_backward_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_backward_varlen.argtypes = [dp] + [vp] * 17 + [vp, sz, vp]
     lib.gdn2_chunk_backward_varlen_workspace_bytes.restype = sz
@@ -157,6 +159,13 @@ def gdn2_chunk_backward(desc, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db
                         workspace_bytes=0, stream=0) -> int:
     return load().gdn2_chunk_backward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w, S0, dO,
                                       dS_T, dq, dk, dv, da, db, dw, dS0, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_backward_preact(desc, q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T, dq, dk, dv, da_pre, db_pre,
+                               dw_pre, dS0, workspace=0, workspace_bytes=0, stream=0) -> int:
+    return load().gdn2_chunk_backward_preact(None if desc is None else ctypes.byref(desc), q, k, v, a_pre, b_pre,
+                                             w_pre, S0, dO, dS_T, dq, dk, dv, da_pre, db_pre, dw_pre, dS0, workspace,
+                                             workspace_bytes, stream)
 
 
 def gdn2_chunk_backward_varlen_workspace_bytes(desc) -> int:
@@ -245,6 +254,14 @@ def chunk_backward(q, k, v, a, b, w, S0, dO, dS_T=None, want_dS0: bool = True, g
     return _backward(q, k, v, a, b, w, S0, dO, dS_T, None, want_dS0, grads, workspace, stream)
 
 
+def chunk_backward_preact(q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
+                          workspace=None, stream=None) -> dict:
+    """Gradients of chunk_forward_preact: as chunk_backward, with da, db, dw
+    the gradients of the gate pre-activations, in the input dtype."""
+    return _backward(q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T, None, want_dS0, grads, workspace, stream,
+                     preact=True)
+
+
 def chunk_backward_varlen(q, k, v, a, b, w, cu_seqlens, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
                           workspace=None, stream=None) -> dict:
     """Gradients of chunk_forward_varlen (packed sequences; shapes as there,
@@ -253,7 +270,7 @@ def chunk_backward_varlen(q, k, v, a, b, w, cu_seqlens, S0, dO, dS_T=None, want_
     return _backward(q, k, v, a, b, w, S0, dO, dS_T, cu_seqlens, want_dS0, grads, workspace, stream)
 
 
-def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, stream) -> dict:
+def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, stream, preact=False) -> dict:
     import torch
     T, H_qk, d_k = q.shape[-3:]
     H_v, d_v = v.shape[-2], v.shape[-1]
@@ -264,12 +281,15 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
         B = cu.numel() - 1
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
         _check(t, nm, q.dtype)
-    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0"), (dS_T, "dS_T")):
+    gdt = q.dtype if preact else torch.float32  # gates (and their gradients)
+    for t, nm in ((a, "a"), (b, "b"), (w, "w")):
+        _check(t, nm, gdt)
+    for t, nm in ((S0, "S0"), (dS_T, "dS_T")):
         _check(t, nm, torch.float32)
     g = dict(grads or {})
     dev = q.device
     shapes = {"dq": (q.shape, q.dtype), "dk": (k.shape, q.dtype), "dv": (v.shape, q.dtype),
-              "da": (a.shape, torch.float32), "db": (b.shape, torch.float32), "dw": (w.shape, torch.float32)}
+              "da": (a.shape, gdt), "db": (b.shape, gdt), "dw": (w.shape, gdt)}
     if want_dS0:
         shapes["dS0"] = ((B, H_v, d_k, d_v), torch.float32)
     for nm, (shape, dt) in shapes.items():
@@ -286,13 +306,42 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
             _ptr(workspace), wbytes, _stream(stream))
-    if cu is None:
+    if preact:
+        st = gdn2_chunk_backward_preact(desc, *ptrs)
+    elif cu is None:
         st = gdn2_chunk_backward(desc, *ptrs)
     else:
         st = gdn2_chunk_backward_varlen(desc, _ptr(cu), *ptrs)
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return g
+
+
+def chunk_forward_preact(q, k, v, a_pre, b_pre, w_pre, S0=None, chunk: int = 64, o=None, S_T=None,
+                         want_state: bool = True, stream=None):
+    """Prefill with the per-channel gates given as pre-activations in the
+    input dtype (decay a = exp(-softplus(a_pre)), b = sigmoid(b_pre),
+    w = sigmoid(w_pre)), activated in the kernel. Shapes as chunk_forward."""
+    import torch
+    B, T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (a_pre, "a_pre"), (b_pre, "b_pre"), (w_pre, "w_pre")):
+        _check(t, nm, q.dtype)
+    _check(S0, "S0", torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
+    _check(o, "o", q.dtype)
+    _check(S_T, "S_T", torch.float32)
+    desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
+    ws = gdn2_chunk_forward_workspace_bytes(desc)
+    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    st = gdn2_chunk_forward_preact(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a_pre), _ptr(b_pre), _ptr(w_pre),
+                                   _ptr(S0), _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st)
+    return o, S_T
 
 
 def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_T=None,
@@ -412,6 +461,40 @@ def _autograd_function():
 
 
 _GDR2 = None
+_GDR2P = None
+
+
+def _autograd_function_preact():
+    import torch
+
+    class GatedDeltaRule2Preact(torch.autograd.Function):
+        """gated_delta_rule with the gates as pre-activations (chunk_forward_preact
+        / gdn2_chunk_backward_preact)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, a_pre, b_pre, w_pre, S0, chunk):
+            o, S_T = chunk_forward_preact(q, k, v, a_pre, b_pre, w_pre, S0, chunk=chunk)
+            ctx.save_for_backward(q, k, v, a_pre, b_pre, w_pre, S0)
+            return o, S_T
+
+        @staticmethod
+        def backward(ctx, dO, dS_T):
+            q, k, v, a_pre, b_pre, w_pre, S0 = ctx.saved_tensors
+            g = chunk_backward_preact(q, k, v, a_pre, b_pre, w_pre, S0, dO.contiguous(),
+                                      None if dS_T is None else dS_T.contiguous(), want_dS0=S0 is not None)
+            return g["dq"], g["dk"], g["dv"], g["da"], g["db"], g["dw"], g["dS0"], None
+
+    return GatedDeltaRule2Preact
+
+
+def gated_delta_rule_preact(q, k, v, a_pre, b_pre, w_pre, S0=None, chunk: int = 64):
+    """Differentiable prefill with the gates as pre-activations in the input
+    dtype (decay a = exp(-softplus(a_pre)), b = sigmoid(b_pre),
+    w = sigmoid(w_pre)); gradients reach the pre-activations."""
+    global _GDR2P
+    if _GDR2P is None:
+        _GDR2P = _autograd_function_preact()
+    return _GDR2P.apply(q, k, v, a_pre, b_pre, w_pre, S0, chunk)
 
 
 def gated_delta_rule(q, k, v, a, b, w, S0=None, chunk: int = 64):

@@ -73,9 +73,10 @@ gdn2::PrefillArgs prefill_args(const gdn2_desc *d) {
 }
 
 gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *q, const void *k, const void *v,
-                             const float *a, const float *b, const float *w, const float *S0, const void *dO,
-                             const float *dS_T, void *dq, void *dk, void *dv, float *da, float *db, float *dw,
-                             float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen);
+                             const void *a, const void *b, const void *w, const float *S0, const void *dO,
+                             const float *dS_T, void *dq, void *dk, void *dv, void *da, void *db, void *dw,
+                             float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen,
+                             bool preact);
 
 // gdn2_chunk_forward and gdn2_chunk_forward_preact: per-channel gates, fp32
 // activated values or pre-activations in the input dtype.
@@ -314,7 +315,16 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k
                                 float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
                                 void *stream) {
   return backward_general(d, nullptr, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
-                          workspace_bytes, stream, false);
+                          workspace_bytes, stream, false, false);
+}
+
+gdn2_status gdn2_chunk_backward_preact(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                       const void *a_pre, const void *b_pre, const void *w_pre, const float *S0,
+                                       const void *dO, const float *dS_T, void *dq, void *dk, void *dv,
+                                       void *da_pre, void *db_pre, void *dw_pre, float *dS0, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  return backward_general(d, nullptr, q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T, dq, dk, dv, da_pre, db_pre, dw_pre,
+                          dS0, workspace, workspace_bytes, stream, false, true);
 }
 
 gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
@@ -323,7 +333,7 @@ gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *d, const int32_t *cu_seq
                                        void *dv, float *da, float *db, float *dw, float *dS0, void *workspace,
                                        size_t workspace_bytes, void *stream) {
   return backward_general(d, cu_seqlens, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
-                          workspace_bytes, stream, true);
+                          workspace_bytes, stream, true, false);
 }
 
 }  // extern "C"
@@ -333,9 +343,10 @@ namespace {
 // gdn2_chunk_backward and gdn2_chunk_backward_varlen (cu_seqlens non-null:
 // B sequences packed along T tokens).
 gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *q, const void *k, const void *v,
-                             const float *a, const float *b, const float *w, const float *S0, const void *dO,
-                             const float *dS_T, void *dq, void *dk, void *dv, float *da, float *db, float *dw,
-                             float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen) {
+                             const void *a, const void *b, const void *w, const float *S0, const void *dO,
+                             const float *dS_T, void *dq, void *dk, void *dv, void *da, void *db, void *dw,
+                             float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen,
+                             bool preact) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
   const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
@@ -355,12 +366,13 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
   if (ws_need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_BAD_SHAPE;
 
   const size_t nqk = BT * Hqk * dkk, nab = BT * Hv * dkk, nvw = BT * Hv * dvv, ns = B * Hv * dkk * dvv;
+  const size_t gs = preact ? es : 4;  // gate (and gate gradient) element bytes
   const Range ins[] = {range_of(q, nqk * es),  range_of(k, nqk * es), range_of(v, nvw * es),
-                       range_of(a, nab * 4),   range_of(b, nab * 4),  range_of(w, nvw * 4),
+                       range_of(a, nab * gs),  range_of(b, nab * gs), range_of(w, nvw * gs),
                        range_of(S0, S0 ? ns * 4 : 0), range_of(dO, nvw * es),
                        range_of(dS_T, dS_T ? ns * 4 : 0), range_of(cu, varlen ? (B + 1) * sizeof(int32_t) : 0)};
   const Range outs[] = {range_of(dq, nqk * es), range_of(dk, nqk * es), range_of(dv, nvw * es),
-                        range_of(da, nab * 4),  range_of(db, nab * 4),  range_of(dw, nvw * 4),
+                        range_of(da, nab * gs), range_of(db, nab * gs), range_of(dw, nvw * gs),
                         range_of(dS0, dS0 ? ns * 4 : 0), range_of(workspace, ws_need)};
   constexpr int NO = sizeof(outs) / sizeof(outs[0]);
   for (int i = 0; i < NO; ++i) {
@@ -376,8 +388,15 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
   gdn2::BackwardArgs p{};
   p.B = d->B; p.T = d->T; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
   p.bf16 = d->dtype == GDN2_BF16;
-  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.dO = dO; p.dST = dS_T;
-  p.dq = dq; p.dk = dk; p.dv = dv; p.da = da; p.db = db; p.dw = dw; p.dS0 = dS0;
+  p.q = q; p.k = k; p.v = v; p.S0 = S0; p.dO = dO; p.dST = dS_T;
+  p.a = static_cast<const float *>(a);  // pre-activations in the input dtype when preact
+  p.b = static_cast<const float *>(b);
+  p.w = static_cast<const float *>(w);
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dS0 = dS0;
+  p.da = static_cast<float *>(da);
+  p.db = static_cast<float *>(db);
+  p.dw = static_cast<float *>(dw);
+  p.preact = preact;
   p.workspace = workspace;
   p.cu_seqlens = varlen ? cu : nullptr;
   const hipError_t e = gdn2::launch_backward(p, reinterpret_cast<hipStream_t>(stream));

@@ -196,7 +196,10 @@ struct Stage {
 
 }  // namespace
 
-template <int DK, int CB, bool BF16>
+// PRE: the per-channel gates are pre-activations in the input dtype (decay
+// a = exp(-softplus(x)), b, w = sigmoid(x)), activated as they are staged;
+// dw is then the gradient of the write gate's pre-activation.
+template <int DK, int CB, bool BF16, bool PRE>
 __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(BackwardParams p) {
   using Cf = BwdCfg<DK, CB>;
   using E = Elem<BF16>;
@@ -232,10 +235,28 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
 
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
-  const float *ah = p.a + tok0 * p.H_v * DK + (size_t)h * DK;
-  const float *bh = p.b + tok0 * p.H_v * DK + (size_t)h * DK;
+  using GT = typename std::conditional<PRE, ET, float>::type;  // stored gate type
+  const GT *ah = (const GT *)p.a + tok0 * p.H_v * DK + (size_t)h * DK;
+  const GT *bh = (const GT *)p.b + tok0 * p.H_v * DK + (size_t)h * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
-  const float *wh = p.w + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  const GT *wh = (const GT *)p.w + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  // four gates (activated) from their stored form
+  auto decay_q = [&](const GT *x) -> floatx4 {
+    if constexpr (PRE) {
+      const floatx4 y = E::ld4(x);
+      return floatx4{decay_from_pre(y[0]), decay_from_pre(y[1]), decay_from_pre(y[2]), decay_from_pre(y[3])};
+    } else {
+      return *reinterpret_cast<const floatx4 *>(x);
+    }
+  };
+  auto gate_q = [&](const GT *x) -> floatx4 {
+    if constexpr (PRE) {
+      const floatx4 y = E::ld4(x);
+      return floatx4{gate_from_pre(y[0]), gate_from_pre(y[1]), gate_from_pre(y[2]), gate_from_pre(y[3])};
+    } else {
+      return *reinterpret_cast<const floatx4 *>(x);
+    }
+  };
   const ET *dOh = (const ET *)p.dO + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
   const size_t qk_t = (size_t)p.H_qk * DK, ab_t = (size_t)p.H_v * DK, vw_t = (size_t)p.H_v * d_v;
   const size_t s_off = (size_t)unit * DK * d_v;
@@ -272,15 +293,15 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const bool ok = idx < Cf::NKS && t < T;
       st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
       st.q[it] = ok ? E::ld4(qh + t * qk_t + 4 * kq) : zero4();
-      st.a[it] = ok ? *reinterpret_cast<const floatx4 *>(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
-      st.b[it] = ok ? *reinterpret_cast<const floatx4 *>(bh + t * ab_t + 4 * kq) : zero4();
+      st.a[it] = ok ? decay_q(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
+      st.b[it] = ok ? gate_q(bh + t * ab_t + 4 * kq) : zero4();
     }
     {
       const int tt = tid / (CB / 4), cq = tid % (CB / 4);
       const int t = sub * L + tt;
       const bool ok = tid < Cf::NCS && t < T;
       st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
-      st.w = ok ? *reinterpret_cast<const floatx4 *>(wh + t * vw_t + 4 * cq) : zero4();
+      st.w = ok ? gate_q(wh + t * vw_t + 4 * cq) : zero4();
       st.d = ok ? E::ld4(dOh + t * vw_t + 4 * cq) : zero4();
       st.r = ok ? *reinterpret_cast<const floatx4 *>(rh + (size_t)t * vw_t + 4 * cq) : zero4();
     }
@@ -333,14 +354,14 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const int t = sb * Cf::L1 + tt;
       const bool ok = idx < Cf::NKS1 && t < T;
       st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
-      st.a[it] = ok ? *reinterpret_cast<const floatx4 *>(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
-      st.b[it] = ok ? *reinterpret_cast<const floatx4 *>(bh + t * ab_t + 4 * kq) : zero4();
+      st.a[it] = ok ? decay_q(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
+      st.b[it] = ok ? gate_q(bh + t * ab_t + 4 * kq) : zero4();
     }
     const int tt = tid / (CB / 4), cq = tid % (CB / 4);
     const int t = sb * Cf::L1 + tt;
     const bool ok = tid < Cf::NCS1 && t < T;
     st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
-    st.w = ok ? *reinterpret_cast<const floatx4 *>(wh + t * vw_t + 4 * cq) : zero4();
+    st.w = ok ? gate_q(wh + t * vw_t + 4 * cq) : zero4();
   };
   auto stash1 = [&](const Stage1<DK, CB> &st) {
 #pragma unroll
@@ -576,7 +597,12 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         const float du = sm.b.du[tt][c];
         const size_t o = (tok0 + t) * vw_t + (size_t)h * d_v + cb * CB + c;
         E::st((ET *)p.dv + o, du * sm.b.col[tt][2][c]);
-        p.dw[o] = du * sm.b.col[tt][1][c];
+        if constexpr (PRE) {  // through w = sigmoid(x): dw/dx = w (1 - w)
+          const float wg = sm.b.col[tt][2][c];
+          E::st((ET *)p.dw + o, du * sm.b.col[tt][1][c] * (wg * (1.f - wg)));
+        } else {
+          p.dw[o] = du * sm.b.col[tt][1][c];
+        }
       }
     }
   }
@@ -590,7 +616,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
 // Key-side gradients: per (token, query/key head g), sum the column blocks'
 // partial sums of every value head h that shares g:
 //   dq = sum x0;  dk = sum (x1 - b*x2);  per h: da = x3, db = -k*x2.
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool PRE>
 __global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) {
   using E = Elem<BF16>;
   using ET = typename E::T;
@@ -613,9 +639,21 @@ __global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) 
       for (int vec = 0; vec < 4; ++vec) x[vec] += *reinterpret_cast<const floatx4 *>(src + vec * DK);
     }
     const size_t o = (tok * p.H_v + h) * DK + 4 * kq;
-    const floatx4 bb = *reinterpret_cast<const floatx4 *>(p.b + o);
-    *reinterpret_cast<floatx4 *>(p.da + o) = x[3];
-    *reinterpret_cast<floatx4 *>(p.db + o) = -(kk * x[2]);
+    floatx4 bb;
+    if constexpr (PRE) {  // gradients of the pre-activations: da/dx = -a (1 - a), db/dx = b (1 - b)
+      const floatx4 xa = E::ld4((const ET *)p.a + o), xb = E::ld4((const ET *)p.b + o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float aa = decay_from_pre(xa[e]);
+        bb[e] = gate_from_pre(xb[e]);
+        E::st((ET *)p.da + o + e, x[3][e] * (-aa * (1.f - aa)));
+        E::st((ET *)p.db + o + e, -(kk[e] * x[2][e]) * (bb[e] * (1.f - bb[e])));
+      }
+    } else {
+      bb = *reinterpret_cast<const floatx4 *>(p.b + o);
+      *reinterpret_cast<floatx4 *>(p.da + o) = x[3];
+      *reinterpret_cast<floatx4 *>(p.db + o) = -(kk * x[2]);
+    }
     dq += x[0];
     dk += x[1] - bb * x[2];
   }
@@ -631,27 +669,33 @@ namespace {
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 
-template <int DK, int CB, bool BF16>
+template <int DK, int CB, bool BF16, bool PRE>
 hipError_t launch_t(const BackwardParams &p, hipStream_t st) {
   const int ncb = p.d_v / CB;
-  hipLaunchKernelGGL((backward_kernel<DK, CB, BF16>), dim3(p.B * p.H_v * ncb), dim3(BwdCfg<DK, CB>::NT), 0, st, p);
+  hipLaunchKernelGGL((backward_kernel<DK, CB, BF16, PRE>), dim3(p.B * p.H_v * ncb), dim3(BwdCfg<DK, CB>::NT), 0, st,
+                     p);
   hipError_t e = hipGetLastError();
   const size_t BT = p.cu ? (size_t)p.T : (size_t)p.B * p.T;
   if (e != hipSuccess || BT == 0) return e;
   const size_t rows = BT * p.H_qk;
   const size_t rpb = 256 / (DK / 4);
-  hipLaunchKernelGGL((backward_reduce_kernel<DK, BF16>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+  hipLaunchKernelGGL((backward_reduce_kernel<DK, BF16, PRE>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
                      p);
   return hipGetLastError();
 }
 
+template <int DK, bool BF16, bool PRE>
+hipError_t launch_cb(const BackwardParams &p, hipStream_t st) {
+  switch (bwd_cb(p.d_v)) {
+    case 64: return launch_t<DK, 64, BF16, PRE>(p, st);
+    case 32: return launch_t<DK, 32, BF16, PRE>(p, st);
+  }
+  return launch_t<DK, 16, BF16, PRE>(p, st);
+}
+
 template <int DK, bool BF16>
 hipError_t launch_dk(const BackwardParams &p, hipStream_t st) {
-  switch (bwd_cb(p.d_v)) {
-    case 64: return launch_t<DK, 64, BF16>(p, st);
-    case 32: return launch_t<DK, 32, BF16>(p, st);
-  }
-  return launch_t<DK, 16, BF16>(p, st);
+  return p.preact ? launch_cb<DK, BF16, true>(p, st) : launch_cb<DK, BF16, false>(p, st);
 }
 
 }  // namespace
@@ -697,6 +741,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.da = a.da; p.db = a.db; p.dw = a.dw; p.dS0 = a.dS0;
   p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
   p.cu = a.cu_seqlens;
+  p.preact = a.preact;
   const size_t BT = a.cu_seqlens ? (size_t)a.T : (size_t)a.B * a.T;
   const size_t ck = (BT / kSub + a.B) * (size_t)a.H_v * a.d_k * a.d_v * 4;
   const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * BT * a.H_v * 4 * a.d_k * 4;

@@ -70,6 +70,8 @@ struct BackwardArgs {
   // packed sequences: B + 1 token offsets (device), or null for B sequences
   // of T tokens each
   const int32_t *cu_seqlens;
+  // a, b, w (and da, db, dw) are gate pre-activations in the input dtype
+  bool preact;
 };
 
 // Kernel parameters: the arguments plus the three workspace regions (state
@@ -84,6 +86,7 @@ struct BackwardParams {
   float *ck, *part, *rk;
   const int32_t *cu;
   int B, T, H_qk, H_v, d_v;
+  bool preact;
 };
 
 size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v);

@@ -223,6 +223,18 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *desc, const void *q, const void
                                 float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/* Backward pass of gdn2_chunk_forward_preact: arguments as for
+ * gdn2_chunk_backward with a_pre, b_pre, w_pre the forward call's gate
+ * pre-activations (input dtype), and da_pre, db_pre, dw_pre the gradients
+ * with respect to them, in the input dtype (through the activations:
+ * d exp(-softplus(x))/dx = -a (1 - a), d sigmoid(x)/dx = s (1 - s)). The
+ * workspace is gdn2_chunk_backward_workspace_bytes(desc) bytes. */
+gdn2_status gdn2_chunk_backward_preact(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                       const void *a_pre, const void *b_pre, const void *w_pre, const float *S0,
+                                       const void *dO, const float *dS_T, void *dq, void *dk, void *dv,
+                                       void *da_pre, void *db_pre, void *dw_pre, float *dS0, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* Backward pass of gdn2_chunk_forward_varlen: desc->B sequences packed along
  * desc->T tokens, sequence n = tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
  * (cu_seqlens: B + 1 non-decreasing int32 device offsets; offsets outside

@@ -173,6 +173,21 @@ def backward(q, k, v, a, b, w, S0, dO, dS_T=None, nthreads: Optional[int] = None
     return out
 
 
+def backward_preact(q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T=None, nthreads: Optional[int] = None,
+                    lib=None) -> dict:
+    """Gradients of :func:`forward_preact`: the recurrence's gradients
+    (:func:`backward`) on the activated gates, then through the activations
+    by the chain rule, d/dx exp(-softplus(x)) = -a (1 - a) and
+    d/dx sigmoid(x) = s (1 - s). Returns dq, dk, dv, dS0 as :func:`backward`
+    and da, db, dw with respect to the pre-activations."""
+    a, b, w = activate_gates(a_pre, b_pre, w_pre)
+    g = backward(q, k, v, a, b, w, S0, dO, dS_T, nthreads=nthreads, lib=lib)
+    g["da"] = g["da"] * (-a * (1.0 - a))
+    g["db"] = g["db"] * (b * (1.0 - b))
+    g["dw"] = g["dw"] * (w * (1.0 - w))
+    return g
+
+
 def forward_heads(inputs: dict, heads, nthreads: Optional[int] = None) -> Tuple[dict, dict]:
     """Run the oracle only on selected (n, h_v) pairs of a prefill input dict.
 

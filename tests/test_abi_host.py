@@ -278,3 +278,12 @@ def test_backward_varlen_workspace_and_errors():
     p[9] = cu  # dq over cu_seqlens
     assert call(cu, p) == g.GDN2_ERR_ALIAS
     assert g.gdn2_chunk_backward_varlen(g.make_desc(0, 50, 1, 2, 64, 64, 64, 1), 0, *([0] * 16), 0, 0, 0) == g.GDN2_OK
+
+
+def test_binding_exposes_every_entry_point_wrapper():
+    """The torch-level wrappers of every entry point exist (import-time check;
+    the GPU tests exercise them)."""
+    for name in ("chunk_forward", "chunk_forward_preact", "chunk_forward_coupled", "chunk_forward_scalar",
+                 "chunk_forward_varlen", "decode_step", "chunk_backward", "chunk_backward_preact",
+                 "chunk_backward_varlen", "gated_delta_rule", "gated_delta_rule_preact"):
+        assert callable(getattr(g, name, None)), name

@@ -218,3 +218,28 @@ def test_varlen_matches_oracle_and_separate_calls(dt, dk, dv):
         for nm in ("dq", "dk", "dv", "da", "db", "dw"):
             assert torch.equal(gv[nm][:, t0:t1], alone[nm]), (n, nm)
         assert torch.equal(gv["dS0"][n:n + 1], alone["dS0"]), n
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 64, 64), ("f32", 128, 16), ("bf16", 128, 128)])
+def test_preact_backward_matches_oracle(dt, dk, dv):
+    """Gradients with the gates as pre-activations (the kernel activates them
+    and returns the pre-activation gradients) against the oracle's chain rule,
+    through the autograd wrapper."""
+    rng = np.random.default_rng(4200 + dk + dv)
+    B, T = 2, 37
+    d = rand_inputs(rng, B, T, 1, 2, dk, dv)
+    f = np.float32
+    d["a"] = (rng.standard_normal((B, T, 2, dk)) - 2.0).astype(f)
+    d["b"] = rng.standard_normal((B, T, 2, dk)).astype(f)
+    d["w"] = rng.standard_normal((B, T, 2, dv)).astype(f)
+    td = gi.to_torch_preact(d, dt, DEV)
+    leaves = {nm: td[nm].clone().requires_grad_(True) for nm in ("q", "k", "v", "a", "b", "w", "S0")}
+    dO, dST = upstream(rng, d, dt)
+    o, ST = g.gated_delta_rule_preact(*(leaves[nm] for nm in ("q", "k", "v", "a", "b", "w", "S0")), chunk=32)
+    ((o.float() * dO.float()).sum() + (ST * dST).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle.backward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    for nm in ("q", "k", "v", "a", "b", "w", "S0"):
+        err = normwise(to_np(leaves[nm].grad), ref["d" + nm])
+        print(f"[preact backward {dt} dk{dk} dv{dv} d{nm}] {err:.2e}", flush=True)
+        assert err <= TOL[dt], (nm, err)

@@ -43,3 +43,32 @@ def test_forward_preact_is_forward_of_activated_gates():
     o2, s2 = oracle.forward(q, k, v, expit(-xa), expit(xb), expit(xw), S0)
     np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(s1, s2, rtol=1e-13, atol=1e-14)
+
+
+def test_backward_preact_finite_differences():
+    """The pre-activation gradients against central differences of
+    L = <dO, o> + <dS_T, S_T> through forward_preact."""
+    rng = np.random.default_rng(22)
+    B, T, Hv, dk, dv = 1, 5, 2, 3, 2
+    q, k, v, _, _, _, S0 = rand_inputs(rng, B, T, 1, Hv, dk, dv)
+    X = {"a": rng.standard_normal((B, T, Hv, dk)) - 1.0, "b": rng.standard_normal((B, T, Hv, dk)),
+         "w": rng.standard_normal((B, T, Hv, dv))}
+    dO = rng.standard_normal((B, T, Hv, dv)); dST = rng.standard_normal((B, Hv, dk, dv))
+    g = oracle.backward_preact(q, k, v, X["a"], X["b"], X["w"], S0, dO, dST)
+
+    def loss(**Y):
+        o, ST = oracle.forward_preact(q, k, v, Y["a"], Y["b"], Y["w"], S0, nthreads=1)
+        return float((o * dO).sum() + (ST * dST).sum())
+
+    h = 1e-6
+    for name, x in X.items():
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            Y = dict(X)
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            Y[name] = xp; lp = loss(**Y)
+            Y[name] = xm; lm = loss(**Y)
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(fd - g["d" + name]).max() / np.abs(fd).max()
+        assert err < 1e-7, (name, err)
