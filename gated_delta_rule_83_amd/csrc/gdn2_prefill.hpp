@@ -226,6 +226,9 @@ struct PrefillSmem {
   // token-major build: per producer wave, the product of the decays of its
   // tokens per key channel, for the next chunk to build
   alignas(16) float tot[Cf::NP][Cf::TOKM ? Cf::DK : 4];
+  // coupled gates: beta per token of the chunk in buffer b (last, so that
+  // the other members keep their offsets)
+  alignas(16) float beta[2][Cf::C];
 };
 
 template <class Cf>
@@ -299,8 +302,12 @@ constexpr bool tile_col_used(unsigned m, int c, int nch) {
   for (int r = c; r < nch; ++r) u = u || tile_in(m, r, c);
   return u;
 }
-template <class Cf, unsigned KK, unsigned KB, unsigned QK, unsigned QB>
-__device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, float *akbd, int lg, int lc) {
+// CPLT (coupled gates, b = beta per token): B = diag(beta) K, so Akb and
+// Mqb are Akk and Mqk with column s scaled by beta_s; each Akk and Mqk tile
+// is then also written, scaled, as the Akb / Mqb tile (KB and QB are empty).
+template <class Cf, unsigned KK, unsigned KB, unsigned QK, unsigned QB, bool CPLT = false>
+__device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, float *akbd, const float *beta, int lg,
+                                           int lc) {
   constexpr bool BF16 = Cf::BF16;
   using LK = typename Cf::LK;
   using LT = typename Cf::LT;
@@ -339,6 +346,13 @@ __device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, fl
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] = t > s0 + j ? x[j] : 0.f;
             st4<LT, BF16>(cb.ab, t, 32 * c + 4 * lg, x);
+            if constexpr (CPLT) {
+              const floatx4 y = x * *reinterpret_cast<const floatx4 *>(&beta[s0]);
+              if constexpr (c != r)
+                st4<LT, BF16>(cb.ab, t, 32 * c + 16 + 4 * lg, -y);
+              else
+                *reinterpret_cast<floatx4 *>(&akbd[r * 16 * 20 + (4 * (lc & 3) + (lc >> 2)) * 20 + 4 * lg]) = y;
+            }
           } else if constexpr (q == 1) {
             if constexpr (c != r) {
               st4<LT, BF16>(cb.ab, t, 32 * c + 16 + 4 * lg, -x);
@@ -351,6 +365,8 @@ __device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, fl
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] = t >= s0 + j ? x[j] : 0.f;
             st4<LT, BF16>(cb.m, t, 32 * c + (q == 3 ? 16 : 0) + 4 * lg, x);
+            if constexpr (CPLT && q == 2)
+              st4<LT, BF16>(cb.m, t, 32 * c + 16 + 4 * lg, x * *reinterpret_cast<const floatx4 *>(&beta[s0]));
           }
         }
       });
@@ -367,6 +383,21 @@ __device__ __forceinline__ void gram_tiles(ChunkBuf<Cf> &cb, const char *kbi, fl
 // tile they need and the other two waves take the remaining ten tiles. With
 // one block waves 0 and 1 take Akk and Akb, 2 and 3 Mqk and Mqb; with more
 // blocks wave 0 takes all of Akk, wave 1 all of Akb and the inverses.
+// Coupled gates (Akb and Mqb as scaled Akk and Mqk): with two row blocks
+// waves 0 and 1 compute the diagonal Akk tile they invert, wave 2 the
+// off-diagonal Akk tile and Mqk (0,0), wave 3 the other two Mqk tiles; with
+// one block, or more, wave 0 takes Akk (and the inverses) and wave 2 Mqk.
+template <int NCH>
+struct GramSplitCpl {
+  static constexpr unsigned FULL = (1u << (NCH * (NCH + 1) / 2)) - 1u;
+  static constexpr bool TWO = NCH == 2;  // tiles 0 = (0,0), 1 = (1,0), 2 = (1,1)
+  static constexpr unsigned KK[4] = {TWO ? 1u : FULL, TWO ? 4u : 0u, TWO ? 2u : 0u, 0u};
+  static constexpr unsigned KB[4] = {0u, 0u, 0u, 0u};
+  static constexpr unsigned QK[4] = {0u, 0u, TWO ? 1u : FULL, TWO ? 6u : 0u};
+  static constexpr unsigned QB[4] = {0u, 0u, 0u, 0u};
+  static constexpr unsigned INV[4] = {TWO ? 1u : (1u << NCH) - 1u, TWO ? 2u : 0u, 0u, 0u};
+};
+
 template <int NCH>
 struct GramSplit {
   static constexpr unsigned FULL = (1u << (NCH * (NCH + 1) / 2)) - 1u;
@@ -721,6 +752,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     const bool any_bad = __any(lane_bad);
     if (lane == 0) cbuf.bad[wave] = any_bad ? 1 : 0;
     if (last) *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = inc;
+    if constexpr (CPL) {  // beta of the lane's tokens, for the Gram tiles
+      if (brow && cq == 0 && (TOKM || wave == 0)) {
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) sm.beta[P][tb0 + r] = rb[P][r][0];
+      }
+    }
     if (brow) {
       // 1/gamma on the lane's tokens from one reciprocal per channel: the
       // lane's last cumulative decay (inc) times the decays after each token
@@ -826,7 +863,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       // phase B: Gram tiles (and diagonal inverses), then chunk s+2's keys
       // and queries
       if (produce) {
-        using GS = GramSplit<NCH>;
+        using GS = typename std::conditional<CPL, GramSplitCpl<NCH>, GramSplit<NCH>>::type;
         // the diagonal blocks whose Akb tile this wave has just written
         auto invert_set = [&](auto mask) {
           static_for<NCH>([&](auto rc) {
@@ -836,7 +873,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         };
         auto gram_wave = [&](auto wc) {
           constexpr int w = decltype(wc)::value;
-          gram_tiles<Cf, GS::KK[w], GS::KB[w], GS::QK[w], GS::QB[w]>(pb, sm.kbi, sm.akbd, lg, lc);
+          gram_tiles<Cf, GS::KK[w], GS::KB[w], GS::QK[w], GS::QB[w], CPL>(pb, sm.kbi, sm.akbd, sm.beta[P], lg, lc);
           invert_set(std::integral_constant<unsigned, GS::INV[w]>());
         };
         switch (wave) {

@@ -117,10 +117,12 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void 
  * gdn2_chunk_forward with b, w replaced by
  *   beta: [B, T, H_v] fp32.
  * The result equals gdn2_chunk_forward with b = beta * ones(d_k) and
- * w = beta * ones(d_v) (bit for bit: the kernels are the same up to how the
- * gates are read); the two per-channel gate arrays are not read, which
- * removes about 40% of the prefill's memory traffic at d = 128. The same
- * workspace rules apply (gdn2_chunk_forward_workspace_bytes). */
+ * w = beta * ones(d_v) up to rounding: with b = beta the erase-side Gram
+ * matrices are the key-side ones with column s scaled by beta_s, so only two
+ * of the four are formed as products (scaled in fp32). The two per-channel
+ * gate arrays are not read, which removes about 40% of the prefill's memory
+ * traffic at d = 128. The same workspace rules apply
+ * (gdn2_chunk_forward_workspace_bytes). */
 gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *desc, const void *q, const void *k, const void *v,
                                        const float *a, const float *beta, const float *S0, void *o,
                                        float *S_T, void *workspace, size_t workspace_bytes, void *stream);
@@ -132,8 +134,9 @@ gdn2_status gdn2_chunk_forward_coupled(const gdn2_desc *desc, const void *q, con
  * works). Same arguments as gdn2_chunk_forward_coupled with
  *   a: [B, T, H_v] fp32 (one decay per token and value head).
  * The result equals gdn2_chunk_forward with a = alpha * ones(d_k),
- * b = beta * ones(d_k), w = beta * ones(d_v), bit for bit; no per-channel
- * gate array is read. */
+ * b = beta * ones(d_k), w = beta * ones(d_v) up to rounding (two Gram
+ * matrices formed, as for gdn2_chunk_forward_coupled); no per-channel gate
+ * array is read. */
 gdn2_status gdn2_chunk_forward_scalar(const gdn2_desc *desc, const void *q, const void *k, const void *v,
                                       const float *a, const float *beta, const float *S0, void *o,
                                       float *S_T, void *workspace, size_t workspace_bytes, void *stream);
