@@ -44,6 +44,7 @@ EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forw
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
             "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
             "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes", "gdn2_chunk_backward_preact",
+            "gdn2_chunk_backward_coupled", "gdn2_chunk_backward_scalar",
             "gdn2_status_string", "gdn2_version")
 
 
@@ -92,6 +93,10 @@ def load(path: Optional[str] = None):
     lib.gdn2_chunk_backward_workspace_bytes.argtypes = [dp]
     lib.gdn2_chunk_backward_preact.restype = ctypes.c_int
     lib.gdn2_chunk_backward_preact.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+    lib.gdn2_chunk_backward_coupled.restype = ctypes.c_int
+    lib.gdn2_chunk_backward_coupled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
+    lib.gdn2_chunk_backward_scalar.restype = ctypes.c_int
+    lib.gdn2_chunk_backward_scalar.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
     lib.gdn2_chunk_backward_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_backward_varlen.argtypes = [dp] + [vp] * 17 + [vp, sz, vp]
     lib.gdn2_chunk_backward_varlen_workspace_bytes.restype = sz
@@ -165,6 +170,20 @@ def gdn2_chunk_backward_preact(desc, q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T,
                                dw_pre, dS0, workspace=0, workspace_bytes=0, stream=0) -> int:
     return load().gdn2_chunk_backward_preact(None if desc is None else ctypes.byref(desc), q, k, v, a_pre, b_pre,
                                              w_pre, S0, dO, dS_T, dq, dk, dv, da_pre, db_pre, dw_pre, dS0, workspace,
+                                             workspace_bytes, stream)
+
+
+def gdn2_chunk_backward_coupled(desc, q, k, v, a, beta, S0, dO, dS_T, dq, dk, dv, da, dbeta, dS0, workspace=0,
+                                workspace_bytes=0, stream=0) -> int:
+    return load().gdn2_chunk_backward_coupled(None if desc is None else ctypes.byref(desc), q, k, v, a, beta, S0,
+                                              dO, dS_T, dq, dk, dv, da, dbeta, dS0, workspace, workspace_bytes,
+                                              stream)
+
+
+def gdn2_chunk_backward_scalar(desc, q, k, v, alpha, beta, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0,
+                               workspace=0, workspace_bytes=0, stream=0) -> int:
+    return load().gdn2_chunk_backward_scalar(None if desc is None else ctypes.byref(desc), q, k, v, alpha, beta,
+                                             S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0, workspace,
                                              workspace_bytes, stream)
 
 
@@ -259,7 +278,24 @@ def chunk_backward_preact(q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T=None, want_
     """Gradients of chunk_forward_preact: as chunk_backward, with da, db, dw
     the gradients of the gate pre-activations, in the input dtype."""
     return _backward(q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T, None, want_dS0, grads, workspace, stream,
-                     preact=True)
+                     form="preact")
+
+
+def chunk_backward_coupled(q, k, v, a, beta, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
+                           workspace=None, stream=None) -> dict:
+    """Gradients of chunk_forward_coupled: dq, dk, dv, da (like a), db (the
+    gradient of beta, [B,T,H_v] fp32: erase and write uses together) and dS0;
+    no dw."""
+    return _backward(q, k, v, a, beta, None, S0, dO, dS_T, None, want_dS0, grads, workspace, stream,
+                     form="coupled")
+
+
+def chunk_backward_scalar(q, k, v, alpha, beta, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
+                          workspace=None, stream=None) -> dict:
+    """Gradients of chunk_forward_scalar: as chunk_backward_coupled, with da
+    the gradient of alpha ([B,T,H_v] fp32)."""
+    return _backward(q, k, v, alpha, beta, None, S0, dO, dS_T, None, want_dS0, grads, workspace, stream,
+                     form="scalar")
 
 
 def chunk_backward_varlen(q, k, v, a, b, w, cu_seqlens, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
@@ -270,7 +306,7 @@ def chunk_backward_varlen(q, k, v, a, b, w, cu_seqlens, S0, dO, dS_T=None, want_
     return _backward(q, k, v, a, b, w, S0, dO, dS_T, cu_seqlens, want_dS0, grads, workspace, stream)
 
 
-def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, stream, preact=False) -> dict:
+def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, stream, form="general") -> dict:
     import torch
     T, H_qk, d_k = q.shape[-3:]
     H_v, d_v = v.shape[-2], v.shape[-1]
@@ -281,15 +317,20 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
         B = cu.numel() - 1
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
         _check(t, nm, q.dtype)
+    preact, coupled = form == "preact", form in ("coupled", "scalar")
     gdt = q.dtype if preact else torch.float32  # gates (and their gradients)
     for t, nm in ((a, "a"), (b, "b"), (w, "w")):
         _check(t, nm, gdt)
+    if coupled and (b.dim() != q.dim() - 1 or (form == "scalar" and a.dim() != q.dim() - 1)):
+        raise ValueError("scalar gates are [.., T, H_v]")
     for t, nm in ((S0, "S0"), (dS_T, "dS_T")):
         _check(t, nm, torch.float32)
     g = dict(grads or {})
     dev = q.device
     shapes = {"dq": (q.shape, q.dtype), "dk": (k.shape, q.dtype), "dv": (v.shape, q.dtype),
-              "da": (a.shape, gdt), "db": (b.shape, gdt), "dw": (w.shape, gdt)}
+              "da": (a.shape, gdt), "db": (b.shape, gdt)}
+    if not coupled:
+        shapes["dw"] = (w.shape, gdt)
     if want_dS0:
         shapes["dS0"] = ((B, H_v, d_k, d_v), torch.float32)
     for nm, (shape, dt) in shapes.items():
@@ -297,6 +338,7 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
             g[nm] = torch.empty(shape, dtype=dt, device=dev)
         _check(g[nm], nm, dt)
     g.setdefault("dS0", None)
+    g.setdefault("dw", None)
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
     ws = (gdn2_chunk_backward_workspace_bytes(desc) if cu is None
           else gdn2_chunk_backward_varlen_workspace_bytes(desc))
@@ -306,7 +348,10 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
             _ptr(workspace), wbytes, _stream(stream))
-    if preact:
+    if coupled:
+        entry = gdn2_chunk_backward_coupled if form == "coupled" else gdn2_chunk_backward_scalar
+        st = entry(desc, *(ptrs[:5] + ptrs[6:14] + ptrs[15:]))
+    elif preact:
         st = gdn2_chunk_backward_preact(desc, *ptrs)
     elif cu is None:
         st = gdn2_chunk_backward(desc, *ptrs)
@@ -505,3 +550,49 @@ def gated_delta_rule(q, k, v, a, b, w, S0=None, chunk: int = 64):
     if _GDR2 is None:
         _GDR2 = _autograd_function()
     return _GDR2.apply(q, k, v, a, b, w, S0, chunk)
+
+
+_GDR2C = {}
+
+
+def _autograd_function_scalar_gates(form: str):
+    import torch
+    fwd = chunk_forward_coupled if form == "coupled" else chunk_forward_scalar
+    bwd = chunk_backward_coupled if form == "coupled" else chunk_backward_scalar
+
+    class GatedDeltaRule2ScalarGates(torch.autograd.Function):
+        """gated_delta_rule with the coupled gate beta (and, in the scalar form,
+        the scalar decay alpha): chunk_forward_coupled / chunk_forward_scalar
+        and their backward passes."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, a, beta, S0, chunk):
+            o, S_T = fwd(q, k, v, a, beta, S0, chunk=chunk)
+            ctx.save_for_backward(q, k, v, a, beta, S0)
+            return o, S_T
+
+        @staticmethod
+        def backward(ctx, dO, dS_T):
+            q, k, v, a, beta, S0 = ctx.saved_tensors
+            g = bwd(q, k, v, a, beta, S0, dO.contiguous(), None if dS_T is None else dS_T.contiguous(),
+                    want_dS0=S0 is not None)
+            return g["dq"], g["dk"], g["dv"], g["da"], g["db"], g["dS0"], None
+
+    return GatedDeltaRule2ScalarGates
+
+
+def gated_delta_rule_coupled(q, k, v, a, beta, S0=None, chunk: int = 64):
+    """Differentiable prefill with coupled erase/write gates b = w = beta
+    ([B,T,H_v] fp32) and a per-channel decay a; gradients reach beta through
+    both of its uses."""
+    if "coupled" not in _GDR2C:
+        _GDR2C["coupled"] = _autograd_function_scalar_gates("coupled")
+    return _GDR2C["coupled"].apply(q, k, v, a, beta, S0, chunk)
+
+
+def gated_delta_rule_scalar(q, k, v, alpha, beta, S0=None, chunk: int = 64):
+    """Differentiable prefill in the Gated DeltaNet form: scalar decay alpha
+    and coupled gate beta, each [B,T,H_v] fp32."""
+    if "scalar" not in _GDR2C:
+        _GDR2C["scalar"] = _autograd_function_scalar_gates("scalar")
+    return _GDR2C["scalar"].apply(q, k, v, alpha, beta, S0, chunk)

@@ -76,7 +76,7 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
                              const void *a, const void *b, const void *w, const float *S0, const void *dO,
                              const float *dS_T, void *dq, void *dk, void *dv, void *da, void *db, void *dw,
                              float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen,
-                             bool preact);
+                             int form);
 
 // gdn2_chunk_forward and gdn2_chunk_forward_preact: per-channel gates, fp32
 // activated values or pre-activations in the input dtype.
@@ -315,7 +315,7 @@ gdn2_status gdn2_chunk_backward(const gdn2_desc *d, const void *q, const void *k
                                 float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes,
                                 void *stream) {
   return backward_general(d, nullptr, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
-                          workspace_bytes, stream, false, false);
+                          workspace_bytes, stream, false, gdn2::kGateGeneral);
 }
 
 gdn2_status gdn2_chunk_backward_preact(const gdn2_desc *d, const void *q, const void *k, const void *v,
@@ -324,7 +324,23 @@ gdn2_status gdn2_chunk_backward_preact(const gdn2_desc *d, const void *q, const 
                                        void *da_pre, void *db_pre, void *dw_pre, float *dS0, void *workspace,
                                        size_t workspace_bytes, void *stream) {
   return backward_general(d, nullptr, q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T, dq, dk, dv, da_pre, db_pre, dw_pre,
-                          dS0, workspace, workspace_bytes, stream, false, true);
+                          dS0, workspace, workspace_bytes, stream, false, gdn2::kGatePre);
+}
+
+gdn2_status gdn2_chunk_backward_coupled(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                        const float *a, const float *beta, const float *S0, const void *dO,
+                                        const float *dS_T, void *dq, void *dk, void *dv, float *da, float *dbeta,
+                                        float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+  return backward_general(d, nullptr, q, k, v, a, beta, nullptr, S0, dO, dS_T, dq, dk, dv, da, dbeta, nullptr, dS0,
+                          workspace, workspace_bytes, stream, false, gdn2::kGateCoupled);
+}
+
+gdn2_status gdn2_chunk_backward_scalar(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                       const float *alpha, const float *beta, const float *S0, const void *dO,
+                                       const float *dS_T, void *dq, void *dk, void *dv, float *dalpha, float *dbeta,
+                                       float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+  return backward_general(d, nullptr, q, k, v, alpha, beta, nullptr, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta,
+                          nullptr, dS0, workspace, workspace_bytes, stream, false, gdn2::kGateScalar);
 }
 
 gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
@@ -333,7 +349,7 @@ gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *d, const int32_t *cu_seq
                                        void *dv, float *da, float *db, float *dw, float *dS0, void *workspace,
                                        size_t workspace_bytes, void *stream) {
   return backward_general(d, cu_seqlens, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
-                          workspace_bytes, stream, true, false);
+                          workspace_bytes, stream, true, gdn2::kGateGeneral);
 }
 
 }  // extern "C"
@@ -346,7 +362,8 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
                              const void *a, const void *b, const void *w, const float *S0, const void *dO,
                              const float *dS_T, void *dq, void *dk, void *dv, void *da, void *db, void *dw,
                              float *dS0, void *workspace, size_t workspace_bytes, void *stream, bool varlen,
-                             bool preact) {
+                             int form) {
+  const bool preact = form == gdn2::kGatePre, coupled = form == gdn2::kGateCoupled || form == gdn2::kGateScalar;
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
   const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
@@ -358,8 +375,10 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
   const size_t ws_need = gdn2::backward_workspace_bytes(d->B, BT, d->H_v, d->d_k, d->d_v);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
   const bool tokens = BT > 0;
-  if (tokens && (!q || !k || !v || !a || !b || !w || !dO || !dq || !dk || !dv || !da || !db || !dw))
+  if (tokens && (!q || !k || !v || !a || !b || !dO || !dq || !dk || !dv || !da || !db))
     return GDN2_ERR_NULL_POINTER;
+  if (tokens && !coupled && (!w || !dw)) return GDN2_ERR_NULL_POINTER;
+  if (coupled) w = dw = nullptr;  // the write gate is beta
   const void *ptrs[] = {q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
@@ -367,12 +386,15 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
 
   const size_t nqk = BT * Hqk * dkk, nab = BT * Hv * dkk, nvw = BT * Hv * dvv, ns = B * Hv * dkk * dvv;
   const size_t gs = preact ? es : 4;  // gate (and gate gradient) element bytes
+  // gate elements: per channel, or one per token and value head (beta; alpha in the scalar form)
+  const size_t na = form == gdn2::kGateScalar ? BT * Hv : nab, nb = coupled ? BT * Hv : nab;
+  const size_t nw = coupled ? 0 : nvw;
   const Range ins[] = {range_of(q, nqk * es),  range_of(k, nqk * es), range_of(v, nvw * es),
-                       range_of(a, nab * gs),  range_of(b, nab * gs), range_of(w, nvw * gs),
+                       range_of(a, na * gs),  range_of(b, nb * gs), range_of(w, nw * gs),
                        range_of(S0, S0 ? ns * 4 : 0), range_of(dO, nvw * es),
                        range_of(dS_T, dS_T ? ns * 4 : 0), range_of(cu, varlen ? (B + 1) * sizeof(int32_t) : 0)};
   const Range outs[] = {range_of(dq, nqk * es), range_of(dk, nqk * es), range_of(dv, nvw * es),
-                        range_of(da, nab * gs), range_of(db, nab * gs), range_of(dw, nvw * gs),
+                        range_of(da, na * gs), range_of(db, nb * gs), range_of(dw, nw * gs),
                         range_of(dS0, dS0 ? ns * 4 : 0), range_of(workspace, ws_need)};
   constexpr int NO = sizeof(outs) / sizeof(outs[0]);
   for (int i = 0; i < NO; ++i) {
@@ -396,7 +418,7 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
   p.da = static_cast<float *>(da);
   p.db = static_cast<float *>(db);
   p.dw = static_cast<float *>(dw);
-  p.preact = preact;
+  p.gate_form = form;
   p.workspace = workspace;
   p.cu_seqlens = varlen ? cu : nullptr;
   const hipError_t e = gdn2::launch_backward(p, reinterpret_cast<hipStream_t>(stream));

@@ -196,11 +196,16 @@ struct Stage {
 
 }  // namespace
 
-// PRE: the per-channel gates are pre-activations in the input dtype (decay
-// a = exp(-softplus(x)), b, w = sigmoid(x)), activated as they are staged;
-// dw is then the gradient of the write gate's pre-activation.
-template <int DK, int CB, bool BF16, bool PRE>
+// Gate forms (GF): kGateGeneral, fp32 per-channel gates; kGatePre, the
+// per-channel gates as pre-activations in the input dtype (decay
+// a = exp(-softplus(x)), b, w = sigmoid(x)), activated as they are staged,
+// dw being then the gradient of the write gate's pre-activation; kGateCoupled,
+// b = w = beta one scalar per token and value head ([.., T, H_v]), the value
+// side of d(beta) summed per column block into p.wsum; kGateScalar, also the
+// decay a = alpha one scalar per token and value head.
+template <int DK, int CB, bool BF16, int GF>
 __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(BackwardParams p) {
+  constexpr bool PRE = GF == kGatePre, CPL = GF == kGateCoupled || GF == kGateScalar, SCA = GF == kGateScalar;
   using Cf = BwdCfg<DK, CB>;
   using E = Elem<BF16>;
   using ET = typename E::T;
@@ -240,6 +245,9 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   const GT *bh = (const GT *)p.b + tok0 * p.H_v * DK + (size_t)h * DK;
   const ET *vh = (const ET *)p.v + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
   const GT *wh = (const GT *)p.w + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  // scalar gates: one value per token and value head (token stride H_v)
+  const float *alpha_h = p.a + tok0 * p.H_v + h, *beta_h = p.b + tok0 * p.H_v + h;
+  auto bcast = [](float x) { return floatx4{x, x, x, x}; };
   // four gates (activated) from their stored form
   auto decay_q = [&](const GT *x) -> floatx4 {
     if constexpr (PRE) {
@@ -293,15 +301,24 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const bool ok = idx < Cf::NKS && t < T;
       st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
       st.q[it] = ok ? E::ld4(qh + t * qk_t + 4 * kq) : zero4();
-      st.a[it] = ok ? decay_q(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
-      st.b[it] = ok ? gate_q(bh + t * ab_t + 4 * kq) : zero4();
+      if constexpr (SCA)
+        st.a[it] = ok ? bcast(alpha_h[(size_t)t * p.H_v]) : floatx4{1.f, 1.f, 1.f, 1.f};
+      else
+        st.a[it] = ok ? decay_q(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (CPL)
+        st.b[it] = ok ? bcast(beta_h[(size_t)t * p.H_v]) : zero4();
+      else
+        st.b[it] = ok ? gate_q(bh + t * ab_t + 4 * kq) : zero4();
     }
     {
       const int tt = tid / (CB / 4), cq = tid % (CB / 4);
       const int t = sub * L + tt;
       const bool ok = tid < Cf::NCS && t < T;
       st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
-      st.w = ok ? gate_q(wh + t * vw_t + 4 * cq) : zero4();
+      if constexpr (CPL)
+        st.w = ok ? bcast(beta_h[(size_t)t * p.H_v]) : zero4();
+      else
+        st.w = ok ? gate_q(wh + t * vw_t + 4 * cq) : zero4();
       st.d = ok ? E::ld4(dOh + t * vw_t + 4 * cq) : zero4();
       st.r = ok ? *reinterpret_cast<const floatx4 *>(rh + (size_t)t * vw_t + 4 * cq) : zero4();
     }
@@ -354,14 +371,23 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       const int t = sb * Cf::L1 + tt;
       const bool ok = idx < Cf::NKS1 && t < T;
       st.k[it] = ok ? E::ld4(kh + t * qk_t + 4 * kq) : zero4();
-      st.a[it] = ok ? decay_q(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
-      st.b[it] = ok ? gate_q(bh + t * ab_t + 4 * kq) : zero4();
+      if constexpr (SCA)
+        st.a[it] = ok ? bcast(alpha_h[(size_t)t * p.H_v]) : floatx4{1.f, 1.f, 1.f, 1.f};
+      else
+        st.a[it] = ok ? decay_q(ah + t * ab_t + 4 * kq) : floatx4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (CPL)
+        st.b[it] = ok ? bcast(beta_h[(size_t)t * p.H_v]) : zero4();
+      else
+        st.b[it] = ok ? gate_q(bh + t * ab_t + 4 * kq) : zero4();
     }
     const int tt = tid / (CB / 4), cq = tid % (CB / 4);
     const int t = sb * Cf::L1 + tt;
     const bool ok = tid < Cf::NCS1 && t < T;
     st.v = ok ? E::ld4(vh + t * vw_t + 4 * cq) : zero4();
-    st.w = ok ? gate_q(wh + t * vw_t + 4 * cq) : zero4();
+    if constexpr (CPL)
+      st.w = ok ? bcast(beta_h[(size_t)t * p.H_v]) : zero4();
+    else
+      st.w = ok ? gate_q(wh + t * vw_t + 4 * cq) : zero4();
   };
   auto stash1 = [&](const Stage1<DK, CB> &st) {
 #pragma unroll
@@ -600,8 +626,18 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
         if constexpr (PRE) {  // through w = sigmoid(x): dw/dx = w (1 - w)
           const float wg = sm.b.col[tt][2][c];
           E::st((ET *)p.dw + o, du * sm.b.col[tt][1][c] * (wg * (1.f - wg)));
-        } else {
+        } else if constexpr (!CPL) {
           p.dw[o] = du * sm.b.col[tt][1][c];
+        }
+      }
+    }
+    if constexpr (CPL) {  // value side of d(beta): sum over the block's columns of du * v
+      if (tid < L) {
+        const int t = sub * L + tid;
+        if (t < T) {
+          float acc = 0.f;
+          for (int c = 0; c < CB; ++c) acc = fmaf(sm.b.du[tid][c], sm.b.col[tid][1][c], acc);
+          p.wsum[((size_t)cb * BT + tok0 + t) * p.H_v + h] = acc;
         }
       }
     }
@@ -616,8 +652,9 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
 // Key-side gradients: per (token, query/key head g), sum the column blocks'
 // partial sums of every value head h that shares g:
 //   dq = sum x0;  dk = sum (x1 - b*x2);  per h: da = x3, db = -k*x2.
-template <int DK, bool BF16, bool PRE>
+template <int DK, bool BF16, int GF>
 __global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) {
+  constexpr bool PRE = GF == kGatePre, CPL = GF == kGateCoupled || GF == kGateScalar, SCA = GF == kGateScalar;
   using E = Elem<BF16>;
   using ET = typename E::T;
   constexpr int TPR = DK / 4;  // threads per (token, g) row, 4 keys each
@@ -640,7 +677,25 @@ __global__ __launch_bounds__(256) void backward_reduce_kernel(BackwardParams p) 
     }
     const size_t o = (tok * p.H_v + h) * DK + 4 * kq;
     floatx4 bb;
-    if constexpr (PRE) {  // gradients of the pre-activations: da/dx = -a (1 - a), db/dx = b (1 - b)
+    if constexpr (CPL) {  // scalar beta (and alpha): sums over the key channels of the row
+      const size_t so = tok * p.H_v + h;
+      const float beta = p.b[so];
+      bb = floatx4{beta, beta, beta, beta};
+      const floatx4 dbk = -(kk * x[2]);
+      float sdb = dbk[0] + dbk[1] + dbk[2] + dbk[3];
+      float sda = x[3][0] + x[3][1] + x[3][2] + x[3][3];
+#pragma unroll
+      for (int m = TPR / 2; m >= 1; m /= 2) {
+        sdb += __shfl_xor(sdb, m, 64);
+        if constexpr (SCA) sda += __shfl_xor(sda, m, 64);
+      }
+      if constexpr (!SCA) *reinterpret_cast<floatx4 *>(p.da + o) = x[3];
+      if (kq == 0) {
+        for (int c = 0; c < ncb; ++c) sdb += p.wsum[((size_t)c * BT + tok) * p.H_v + h];
+        p.db[so] = sdb;
+        if constexpr (SCA) p.da[so] = sda;
+      }
+    } else if constexpr (PRE) {  // gradients of the pre-activations: da/dx = -a (1 - a), db/dx = b (1 - b)
       const floatx4 xa = E::ld4((const ET *)p.a + o), xb = E::ld4((const ET *)p.b + o);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -669,33 +724,38 @@ namespace {
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 
-template <int DK, int CB, bool BF16, bool PRE>
+template <int DK, int CB, bool BF16, int GF>
 hipError_t launch_t(const BackwardParams &p, hipStream_t st) {
   const int ncb = p.d_v / CB;
-  hipLaunchKernelGGL((backward_kernel<DK, CB, BF16, PRE>), dim3(p.B * p.H_v * ncb), dim3(BwdCfg<DK, CB>::NT), 0, st,
+  hipLaunchKernelGGL((backward_kernel<DK, CB, BF16, GF>), dim3(p.B * p.H_v * ncb), dim3(BwdCfg<DK, CB>::NT), 0, st,
                      p);
   hipError_t e = hipGetLastError();
   const size_t BT = p.cu ? (size_t)p.T : (size_t)p.B * p.T;
   if (e != hipSuccess || BT == 0) return e;
   const size_t rows = BT * p.H_qk;
   const size_t rpb = 256 / (DK / 4);
-  hipLaunchKernelGGL((backward_reduce_kernel<DK, BF16, PRE>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+  hipLaunchKernelGGL((backward_reduce_kernel<DK, BF16, GF>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
                      p);
   return hipGetLastError();
 }
 
-template <int DK, bool BF16, bool PRE>
+template <int DK, bool BF16, int GF>
 hipError_t launch_cb(const BackwardParams &p, hipStream_t st) {
   switch (bwd_cb(p.d_v)) {
-    case 64: return launch_t<DK, 64, BF16, PRE>(p, st);
-    case 32: return launch_t<DK, 32, BF16, PRE>(p, st);
+    case 64: return launch_t<DK, 64, BF16, GF>(p, st);
+    case 32: return launch_t<DK, 32, BF16, GF>(p, st);
   }
-  return launch_t<DK, 16, BF16, PRE>(p, st);
+  return launch_t<DK, 16, BF16, GF>(p, st);
 }
 
 template <int DK, bool BF16>
 hipError_t launch_dk(const BackwardParams &p, hipStream_t st) {
-  return p.preact ? launch_cb<DK, BF16, true>(p, st) : launch_cb<DK, BF16, false>(p, st);
+  switch (p.gate_form) {
+    case kGatePre: return launch_cb<DK, BF16, kGatePre>(p, st);
+    case kGateCoupled: return launch_cb<DK, BF16, kGateCoupled>(p, st);
+    case kGateScalar: return launch_cb<DK, BF16, kGateScalar>(p, st);
+  }
+  return launch_cb<DK, BF16, kGateGeneral>(p, st);
 }
 
 }  // namespace
@@ -722,7 +782,8 @@ hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st)
 
 // Checkpoints: per (head, column block) BT / kSub + B slots of d_k x CB fp32
 // (each sequence needs at most ceil(T_n / kSub) <= T_n / kSub + 1 of them);
-// key-side sums: ncb x BT x H_v x 4 x d_k fp32; k-reads: BT x H_v x d_v fp32.
+// key-side sums: ncb x BT x H_v x 4 x d_k fp32; k-reads: BT x H_v x d_v fp32;
+// coupled gates' value-side sums: ncb x BT x H_v fp32.
 // BT = B * T, or T for packed sequences.
 size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v) {
   if (BT == 0) return 0;  // no tokens: only dS0 = dS_T, no scratch
@@ -730,7 +791,8 @@ size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v) {
   const size_t ck = (BT / kSub + B) * (size_t)H_v * d_k * d_v * 4;
   const size_t part = ncb * BT * H_v * 4 * d_k * 4;
   const size_t rk = BT * H_v * d_v * 4;
-  return align256(ck) + align256(part) + align256(rk);
+  const size_t ws = ncb * BT * H_v * 4;
+  return align256(ck) + align256(part) + align256(rk) + align256(ws);
 }
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
@@ -741,13 +803,14 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.da = a.da; p.db = a.db; p.dw = a.dw; p.dS0 = a.dS0;
   p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
   p.cu = a.cu_seqlens;
-  p.preact = a.preact;
+  p.gate_form = a.gate_form;
   const size_t BT = a.cu_seqlens ? (size_t)a.T : (size_t)a.B * a.T;
   const size_t ck = (BT / kSub + a.B) * (size_t)a.H_v * a.d_k * a.d_v * 4;
   const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * BT * a.H_v * 4 * a.d_k * 4;
   p.ck = reinterpret_cast<float *>(a.workspace);
   p.part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck));
   p.rk = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck) + align256(part));
+  p.wsum = reinterpret_cast<float *>(reinterpret_cast<char *>(p.rk) + align256(BT * a.H_v * a.d_v * 4));
   return a.bf16 ? launch_backward_bf16(p, a.d_k, st) : launch_backward_f32(p, a.d_k, st);
 }
 #endif

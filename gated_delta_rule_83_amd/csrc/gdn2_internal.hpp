@@ -57,6 +57,7 @@ struct PrefillPlan {
 constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
 
 // Backward pass (gradients of the recurrence); see gdn2_chunk_backward.
+enum { kGateGeneral = 0, kGatePre = 1, kGateCoupled = 2, kGateScalar = 3 };
 struct BackwardArgs {
   int B, T, H_qk, H_v, d_k, d_v;
   bool bf16;
@@ -70,8 +71,11 @@ struct BackwardArgs {
   // packed sequences: B + 1 token offsets (device), or null for B sequences
   // of T tokens each
   const int32_t *cu_seqlens;
-  // a, b, w (and da, db, dw) are gate pre-activations in the input dtype
-  bool preact;
+  // gate form (kGate*): general fp32 per-channel gates; pre-activations in
+  // the input dtype (a, b, w and da, db, dw); coupled b = w = beta
+  // ([.., T, H_v], db is then d(beta), dw unused); scalar, also a = alpha
+  // ([.., T, H_v], da is then d(alpha))
+  int gate_form;
 };
 
 // Kernel parameters: the arguments plus the three workspace regions (state
@@ -84,9 +88,10 @@ struct BackwardParams {
   void *dq, *dk, *dv;
   float *da, *db, *dw, *dS0;
   float *ck, *part, *rk;
+  float *wsum;
   const int32_t *cu;
   int B, T, H_qk, H_v, d_v;
-  bool preact;
+  int gate_form;
 };
 
 size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v);

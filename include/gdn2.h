@@ -209,8 +209,8 @@ gdn2_status gdn2_decode_step(const gdn2_desc *desc, const void *q, const void *k
  *   workspace : gdn2_chunk_backward_workspace_bytes(desc) bytes (fp32 state
  *          checkpoints every 4 tokens, per 64-column block key-side partial
  *          sums and every token's k-read: about
- *          (d_k * d_v / 4 + 4 * d_k * ceil(d_v / 64) + d_v) * 4 bytes per
- *          token and value head, plus d_k * d_v * 4 per sequence and value
+ *          (d_k * d_v / 4 + (4 * d_k + 1) * ceil(d_v / 64) + d_v) * 4 bytes
+ *          per token and value head, plus d_k * d_v * 4 per sequence and value
  *          head), 256-byte aligned; NULL only when that size is 0. Contents
  *          on return are unspecified.
  * Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums; all
@@ -237,6 +237,30 @@ gdn2_status gdn2_chunk_backward_preact(const gdn2_desc *desc, const void *q, con
                                        const void *dO, const float *dS_T, void *dq, void *dk, void *dv,
                                        void *da_pre, void *db_pre, void *dw_pre, float *dS0, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/* Backward pass of gdn2_chunk_forward_coupled (erase and write gate one
+ * scalar beta per token and value head, b = beta * ones(d_k),
+ * w = beta * ones(d_v)). Arguments as for gdn2_chunk_backward, with
+ *   a     : [B, T, H_v, d_k] fp32 per-channel decay, da its gradient (same shape);
+ *   beta  : [B, T, H_v] fp32; dbeta : [B, T, H_v] fp32, the gradient of beta
+ *           through both of its uses: the sum over the key channels of the
+ *           erase gate's gradient plus the sum over the value columns of the
+ *           write gate's gradient (chain rule through the broadcasts).
+ * No write-gate gradient is written. The workspace is
+ * gdn2_chunk_backward_workspace_bytes(desc) bytes; errors as there. */
+gdn2_status gdn2_chunk_backward_coupled(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                        const float *a, const float *beta, const float *S0, const void *dO,
+                                        const float *dS_T, void *dq, void *dk, void *dv, float *da, float *dbeta,
+                                        float *dS0, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward pass of gdn2_chunk_forward_scalar (a = alpha * ones(d_k) as well):
+ * as gdn2_chunk_backward_coupled with alpha : [B, T, H_v] fp32 and
+ * dalpha : [B, T, H_v] fp32, the sum over the key channels of the decay's
+ * gradient. */
+gdn2_status gdn2_chunk_backward_scalar(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                       const float *alpha, const float *beta, const float *S0, const void *dO,
+                                       const float *dS_T, void *dq, void *dk, void *dv, float *dalpha, float *dbeta,
+                                       float *dS0, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Backward pass of gdn2_chunk_forward_varlen: desc->B sequences packed along
  * desc->T tokens, sequence n = tokens cu_seqlens[n] .. cu_seqlens[n+1]-1

@@ -188,6 +188,35 @@ def backward_preact(q, k, v, a_pre, b_pre, w_pre, S0, dO, dS_T=None, nthreads: O
     return g
 
 
+def expand_scalar_gates(a, beta, d_k: int, d_v: int, scalar_decay: bool):
+    """Per-channel gates of the coupled form (GDN-2 note, section on the delta
+    rule's basic idea and its limits; wiki, how it works): erase and write
+    gate both the scalar beta per token and value head, b = beta * ones(d_k),
+    w = beta * ones(d_v); with scalar_decay the decay is alpha * ones(d_k)."""
+    beta = _f64(beta)
+    a = _f64(a)
+    if scalar_decay:
+        a = np.repeat(a[..., None], d_k, axis=-1)
+    return a, np.repeat(beta[..., None], d_k, axis=-1), np.repeat(beta[..., None], d_v, axis=-1)
+
+
+def backward_coupled(q, k, v, a, beta, S0, dO, dS_T=None, scalar_decay: bool = False,
+                     nthreads: Optional[int] = None, lib=None) -> dict:
+    """Gradients of the coupled (and, with scalar_decay, scalar) gate form:
+    the recurrence's gradients (:func:`backward`) on the expanded gates, then
+    through the broadcasts by the chain rule: dbeta = sum over the key
+    channels of db plus sum over the value columns of dw; with scalar_decay
+    da = sum over the key channels of da. Returns dq, dk, dv, da, db (= dbeta)
+    and dS0."""
+    d_k, d_v = q.shape[-1], v.shape[-1]
+    A, Bg, W = expand_scalar_gates(a, beta, d_k, d_v, scalar_decay)
+    g = backward(q, k, v, A, Bg, W, S0, dO, dS_T, nthreads=nthreads, lib=lib)
+    g["db"] = g["db"].sum(axis=-1) + g.pop("dw").sum(axis=-1)
+    if scalar_decay:
+        g["da"] = g["da"].sum(axis=-1)
+    return g
+
+
 def forward_heads(inputs: dict, heads, nthreads: Optional[int] = None) -> Tuple[dict, dict]:
     """Run the oracle only on selected (n, h_v) pairs of a prefill input dict.
 

@@ -212,16 +212,18 @@ def bwd(desc, ptrs=None, ws=0, ws_bytes=0):
 
 def test_backward_workspace_query_and_argument_errors():
     """Workspace: fp32 checkpoints every 4 tokens (d_k x d_v per head), four
-    d_k-vectors per token, head and 64-column block, and one d_v-vector of
-    k-reads per token and head; errors before any launch."""
+    d_k-vectors per token, head and 64-column block, one d_v-vector of
+    k-reads per token and head, and one value per token, head and column
+    block (the coupled gate's value-side sums); errors before any launch."""
     d = g.make_desc(2, 20, 1, 2, 64, 64, 64, g.GDN2_BF16)
     nslot, ncb = 2 * 20 // 4 + 2, 1  # checkpoint slots: B*T/4 + B; one 64-column block
     ck = 2 * nslot * 64 * 64 * 4
     part = ncb * 2 * 20 * 2 * 4 * 64 * 4
     rk = 2 * 2 * 20 * 64 * 4
+    wsum = ncb * 2 * 20 * 2 * 4
     up = lambda x: (x + 255) // 256 * 256
     need = g.gdn2_chunk_backward_workspace_bytes(d)
-    assert need == up(ck) + up(part) + up(rk)
+    assert need == up(ck) + up(part) + up(rk) + up(wsum)
     assert g.gdn2_chunk_backward_workspace_bytes(None) == 0
     assert g.gdn2_chunk_backward_workspace_bytes(g.make_desc(1, 0, 1, 1, 16, 16, 16, 0)) == 0
     ws = FAKE + 40 * (1 << 30)
@@ -267,7 +269,8 @@ def test_backward_varlen_workspace_and_errors():
     d = g.make_desc(3, 50, 1, 2, 64, 64, 64, g.GDN2_BF16)
     up = lambda x: (x + 255) // 256 * 256
     need = g.gdn2_chunk_backward_varlen_workspace_bytes(d)
-    assert need == up((50 // 4 + 3) * 2 * 64 * 64 * 4) + up(1 * 50 * 2 * 4 * 64 * 4) + up(50 * 2 * 64 * 4)
+    assert need == (up((50 // 4 + 3) * 2 * 64 * 64 * 4) + up(1 * 50 * 2 * 4 * 64 * 4) + up(50 * 2 * 64 * 4)
+                    + up(1 * 50 * 2 * 4))
     ws = FAKE + 40 * (1 << 30)
     base = [FAKE + i * (1 << 30) for i in range(16)]
     cu = FAKE + 50 * (1 << 30)
@@ -280,10 +283,45 @@ def test_backward_varlen_workspace_and_errors():
     assert g.gdn2_chunk_backward_varlen(g.make_desc(0, 50, 1, 2, 64, 64, 64, 1), 0, *([0] * 16), 0, 0, 0) == g.GDN2_OK
 
 
+def test_backward_coupled_scalar_errors():
+    """Coupled and scalar gate forms: beta (and alpha) one fp32 per token and
+    value head, no write gate; required pointers, alignment and overlaps at
+    those sizes are checked before any launch."""
+    d = g.make_desc(2, 20, 1, 2, 64, 64, 64, g.GDN2_BF16)
+    need = g.gdn2_chunk_backward_workspace_bytes(d)
+    ws = FAKE + 40 * (1 << 30)
+    # q, k, v, a, beta, S0, dO, dS_T, dq, dk, dv, da, dbeta, dS0
+    base = [FAKE + i * (1 << 30) for i in range(14)]
+    for entry in (g.gdn2_chunk_backward_coupled, g.gdn2_chunk_backward_scalar):
+        call = lambda p, w=ws, nb=need: entry(d, *p, w, nb, 0)
+        assert call(base, 0, 0) == g.GDN2_ERR_WORKSPACE
+        for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):  # required pointers
+            p = list(base)
+            p[i] = 0
+            assert call(p) == g.GDN2_ERR_NULL_POINTER, i
+        p = list(base)
+        p[12] += 8
+        assert call(p) == g.GDN2_ERR_BAD_SHAPE
+        p = list(base)
+        p[12] = p[4] + 16  # dbeta over beta
+        assert call(p) == g.GDN2_ERR_ALIAS
+        assert entry(g.make_desc(0, 20, 1, 2, 64, 64, 64, 1), *([0] * 14), 0, 0, 0) == g.GDN2_OK
+    # beta holds B*T*H_v floats: dbeta just past it is no overlap (so the
+    # call gets as far as the alignment check of a misaligned dq)
+    p = list(base)
+    p[12] = p[4] + 2 * 20 * 2 * 4
+    p[8] += 4
+    assert g.gdn2_chunk_backward_scalar(d, *p, ws, need, 0) == g.GDN2_ERR_BAD_SHAPE
+    p[12] -= 16  # ... and 16 bytes earlier it is
+    p[8] -= 4
+    assert g.gdn2_chunk_backward_scalar(d, *p, ws, need, 0) == g.GDN2_ERR_ALIAS
+
+
 def test_binding_exposes_every_entry_point_wrapper():
     """The torch-level wrappers of every entry point exist (import-time check;
     the GPU tests exercise them)."""
     for name in ("chunk_forward", "chunk_forward_preact", "chunk_forward_coupled", "chunk_forward_scalar",
                  "chunk_forward_varlen", "decode_step", "chunk_backward", "chunk_backward_preact",
-                 "chunk_backward_varlen", "gated_delta_rule", "gated_delta_rule_preact"):
+                 "chunk_backward_varlen", "chunk_backward_coupled", "chunk_backward_scalar", "gated_delta_rule",
+                 "gated_delta_rule_preact", "gated_delta_rule_coupled", "gated_delta_rule_scalar"):
         assert callable(getattr(g, name, None)), name

@@ -243,3 +243,67 @@ def test_preact_backward_matches_oracle(dt, dk, dv):
         err = normwise(to_np(leaves[nm].grad), ref["d" + nm])
         print(f"[preact backward {dt} dk{dk} dv{dv} d{nm}] {err:.2e}", flush=True)
         assert err <= TOL[dt], (nm, err)
+
+
+@pytest.mark.parametrize("form,dt,dk,dv,T", [("coupled", "f32", 64, 64, 37), ("coupled", "bf16", 128, 128, 37),
+                                             ("coupled", "f32", 16, 128, 5), ("scalar", "f32", 128, 16, 21),
+                                             ("scalar", "bf16", 128, 128, 50), ("scalar", "f32", 32, 32, 1)])
+def test_coupled_scalar_backward_matches_oracle(form, dt, dk, dv, T):
+    """Coupled gate beta (b = w = beta), and the scalar form (decay alpha as
+    well): dbeta sums the erase and write gradients, dalpha the decay's, and
+    every gradient matches the oracle's chain rule through the broadcasts.
+    dbeta and dalpha also match the general path's gradients on the broadcast
+    gates, summed. Through the autograd wrapper."""
+    rng = np.random.default_rng(4300 + dk + dv + T + (form == "scalar"))
+    B, Hv, scalar = 2, 2, form == "scalar"
+    d = rand_inputs(rng, B, T, 1, Hv, dk, dv)
+    f = np.float32
+    beta = rng.uniform(0.0, 1.0, (B, T, Hv)).astype(f)
+    a = rng.uniform(0.5, 1.0, (B, T, Hv)).astype(f) if scalar else d["a"]
+    td = gi.to_torch(d, dt, DEV)
+    leaves = {nm: td[nm].clone().requires_grad_(True) for nm in ("q", "k", "v", "S0")}
+    leaves["a"] = torch.from_numpy(a).to(DEV).requires_grad_(True)
+    leaves["b"] = torch.from_numpy(beta).to(DEV).requires_grad_(True)
+    dO, dST = upstream(rng, d, dt)
+    fn = g.gated_delta_rule_scalar if scalar else g.gated_delta_rule_coupled
+    o, ST = fn(*(leaves[nm] for nm in ("q", "k", "v", "a", "b", "S0")), chunk=32)
+    ((o.float() * dO.float()).sum() + (ST * dST).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle.backward_coupled(td["q"], td["k"], td["v"], a, beta, td["S0"], dO, dST, scalar_decay=scalar)
+    for nm in ("q", "k", "v", "a", "b", "S0"):
+        err = normwise(to_np(leaves[nm].grad), ref["d" + nm])
+        print(f"[{form} backward {dt} dk{dk} dv{dv} T{T} d{nm}] {err:.2e}", flush=True)
+        assert err <= TOL[dt], (nm, err)
+    # the general path on the broadcast gates, its gate gradients summed
+    A = leaves["a"].detach()
+    A = A[..., None].expand(B, T, Hv, dk).contiguous() if scalar else A
+    bt = leaves["b"].detach()
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], A, bt[..., None].expand(B, T, Hv, dk).contiguous(),
+                          bt[..., None].expand(B, T, Hv, dv).contiguous(), td["S0"], dO, dST)
+    dbeta = gg["db"].sum(-1) + gg["dw"].sum(-1)
+    err = normwise(to_np(leaves["b"].grad), to_np(dbeta))
+    assert err <= TOL["f32"], ("dbeta vs general", err)
+    if scalar:
+        err = normwise(to_np(leaves["a"].grad), to_np(gg["da"].sum(-1)))
+        assert err <= TOL["f32"], ("dalpha vs general", err)
+
+
+def test_scalar_backward_layer_shape_scaled():
+    """The Gated DeltaNet form at the 1.3B-class layer's distributions
+    (B2 T520 H4, d 128, bf16): every gradient against the oracle."""
+    c = gi.scaled(1, B=2, T=520, H_qk=4, H_v=4)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(4400)
+    B, T, Hv = d["v"].shape[:3]
+    alpha = d["a"].mean(-1).astype(np.float32)
+    beta = d["b"].mean(-1).astype(np.float32)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    ta, tb = torch.from_numpy(alpha).to(DEV), torch.from_numpy(beta).to(DEV)
+    gg = g.chunk_backward_scalar(td["q"], td["k"], td["v"], ta, tb, td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    ref = oracle.backward_coupled(td["q"], td["k"], td["v"], alpha, beta, td["S0"], dO, dST, scalar_decay=True)
+    for nm in ("dq", "dk", "dv", "da", "db", "dS0"):
+        err = normwise(to_np(gg[nm]), ref[nm])
+        print(f"[scalar backward c1-scaled {nm}] {err:.2e}", flush=True)
+        assert err <= TOL["bf16"], (nm, err)
