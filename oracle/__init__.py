@@ -25,6 +25,11 @@ Gate activations from pre-activations (``activate_gates``, the
 parameterisation of the gates in the synthetic workloads: softplus decay,
 sigmoid gates) are pinned by ``tests/test_oracle_preact.py`` against
 closed-form values, identities and scipy's logistic function.
+The coupled and scalar gate forms (``expand_scalar_gates``,
+``backward_coupled``: one beta, and alpha, per token and value head,
+broadcast to the channels) are pinned by ``tests/test_oracle_coupled.py``:
+the broadcast itself, finite differences of the forward on the broadcast
+gates, and the closed form at alpha = beta = 1 with unit keys.
 Parity unpinned: the exact placement of channel-wise erase and write gates
 when b and w are not uniform (the pages state it only in prose); the oracle
 takes erase (b * k) r^T and write k (w * v)^T.
