@@ -44,7 +44,8 @@ EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forw
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
             "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
             "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes", "gdn2_chunk_backward_preact",
-            "gdn2_chunk_backward_coupled", "gdn2_chunk_backward_scalar",
+            "gdn2_chunk_backward_coupled", "gdn2_chunk_backward_scalar", "gdn2_chunk_forward_varlen_gates",
+            "gdn2_chunk_backward_varlen_gates",
             "gdn2_status_string", "gdn2_version")
 
 
@@ -81,6 +82,10 @@ def load(path: Optional[str] = None):
     lib.gdn2_chunk_forward_coupled.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
     lib.gdn2_chunk_forward_scalar.restype = ctypes.c_int
     lib.gdn2_chunk_forward_scalar.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
+    lib.gdn2_chunk_forward_varlen_gates.restype = ctypes.c_int
+    lib.gdn2_chunk_forward_varlen_gates.argtypes = [dp, vp, ctypes.c_int] + [vp] * 9 + [vp]
+    lib.gdn2_chunk_backward_varlen_gates.restype = ctypes.c_int
+    lib.gdn2_chunk_backward_varlen_gates.argtypes = [dp, vp, ctypes.c_int] + [vp] * 16 + [vp, sz, vp]
     lib.gdn2_chunk_forward_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_forward_varlen.argtypes = [dp] + [vp] * 10 + [vp]
     lib.gdn2_decode_step.restype = ctypes.c_int
@@ -154,6 +159,18 @@ def gdn2_chunk_forward_scalar(desc, q, k, v, a, beta, S0, o, S_T, workspace=0, w
 def gdn2_chunk_forward_varlen(desc, cu_seqlens, q, k, v, a, b, w, S0, o, S_T, stream=0) -> int:
     return load().gdn2_chunk_forward_varlen(None if desc is None else ctypes.byref(desc), cu_seqlens, q, k,
                                             v, a, b, w, S0, o, S_T, stream)
+
+
+def gdn2_chunk_forward_varlen_gates(desc, cu_seqlens, gates, q, k, v, a, b, w, S0, o, S_T, stream=0) -> int:
+    return load().gdn2_chunk_forward_varlen_gates(None if desc is None else ctypes.byref(desc), cu_seqlens, gates,
+                                                  q, k, v, a, b, w, S0, o, S_T, stream)
+
+
+def gdn2_chunk_backward_varlen_gates(desc, cu_seqlens, gates, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db,
+                                     dw, dS0, workspace=0, workspace_bytes=0, stream=0) -> int:
+    return load().gdn2_chunk_backward_varlen_gates(None if desc is None else ctypes.byref(desc), cu_seqlens, gates,
+                                                   q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0,
+                                                   workspace, workspace_bytes, stream)
 
 
 def gdn2_chunk_backward_workspace_bytes(desc) -> int:
@@ -299,11 +316,15 @@ def chunk_backward_scalar(q, k, v, alpha, beta, S0, dO, dS_T=None, want_dS0: boo
 
 
 def chunk_backward_varlen(q, k, v, a, b, w, cu_seqlens, S0, dO, dS_T=None, want_dS0: bool = True, grads=None,
-                          workspace=None, stream=None) -> dict:
-    """Gradients of chunk_forward_varlen (packed sequences; shapes as there,
-    dO like v, dS_T [N,H_v,d_k,d_v] or None). Returns the dict of chunk_backward,
-    token gradients shaped like their inputs."""
-    return _backward(q, k, v, a, b, w, S0, dO, dS_T, cu_seqlens, want_dS0, grads, workspace, stream)
+                          workspace=None, stream=None, gates: str = "channel") -> dict:
+    """Gradients of chunk_forward_varlen (packed sequences; shapes and `gates`
+    as there, dO like v, dS_T [N,H_v,d_k,d_v] or None). Returns the dict of
+    chunk_backward, token gradients shaped like their inputs (no dw for the
+    coupled and scalar forms, whose db is the gradient of beta)."""
+    form = {"channel": "general"}.get(gates, gates)
+    if form not in ("general", "preact", "coupled", "scalar"):
+        raise ValueError(f"unknown gate form {gates}")
+    return _backward(q, k, v, a, b, w, S0, dO, dS_T, cu_seqlens, want_dS0, grads, workspace, stream, form=form)
 
 
 def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, stream, form="general") -> dict:
@@ -348,7 +369,10 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
             _ptr(workspace), wbytes, _stream(stream))
-    if coupled:
+    if cu is not None and form != "general":
+        st = gdn2_chunk_backward_varlen_gates(desc, _ptr(cu), GDN2_GATES["channel" if form == "general" else form],
+                                              *ptrs)
+    elif coupled:
         entry = gdn2_chunk_backward_coupled if form == "coupled" else gdn2_chunk_backward_scalar
         st = entry(desc, *(ptrs[:5] + ptrs[6:14] + ptrs[15:]))
     elif preact:
@@ -430,20 +454,29 @@ def _forward_scalar_gates(entry, q, k, v, a, beta, S0, chunk, o, S_T, want_state
     return o, S_T
 
 
+GDN2_GATES = {"channel": 0, "preact": 1, "coupled": 2, "scalar": 3}
+
+
 def chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64, o=None, S_T=None,
-                         want_state: bool = True, stream=None):
+                         want_state: bool = True, stream=None, gates: str = "channel"):
     """Prefill of packed sequences of different lengths. q, k [T,H_qk,d_k] (or
     [1,T,H_qk,d_k]); v [T,H_v,d_v]; a, b [T,H_v,d_k] fp32; w [T,H_v,d_v] fp32;
     cu_seqlens int32 [N+1] on the device (sequence n = tokens cu[n]..cu[n+1]-1);
-    S0 [N,H_v,d_k,d_v] fp32 or None. Returns (o shaped like v, S_T [N,H_v,d_k,d_v])."""
+    S0 [N,H_v,d_k,d_v] fp32 or None. Returns (o shaped like v, S_T [N,H_v,d_k,d_v]).
+    `gates` selects the gate form: "channel" (as above), "preact" (a, b, w as
+    pre-activations in the input dtype), "coupled" (b = beta [T,H_v] fp32,
+    w None), "scalar" (a = alpha and b = beta, each [T,H_v] fp32, w None)."""
     import torch
     T, H_qk, d_k = q.shape[-3:]
     H_v, d_v = v.shape[-2], v.shape[-1]
     N = cu_seqlens.numel() - 1
+    form = GDN2_GATES[gates]
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, nm, q.dtype)
-    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0")):
-        _check(t, nm, torch.float32)
+    gdt = q.dtype if gates == "preact" else torch.float32
+    for t, nm in ((a, "a"), (b, "b"), (w, "w")):
+        _check(t, nm, gdt)
+    _check(S0, "S0", torch.float32)
     _check(cu_seqlens, "cu_seqlens", torch.int32)
     if o is None:
         o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
@@ -452,8 +485,8 @@ def chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64,
     _check(o, "o", q.dtype)
     _check(S_T, "S_T", torch.float32)
     desc = make_desc(N, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
-    st = gdn2_chunk_forward_varlen(desc, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
-                                   _ptr(w), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
+    st = gdn2_chunk_forward_varlen_gates(desc, _ptr(cu_seqlens), form, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                         _ptr(w), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return o, S_T

@@ -26,6 +26,10 @@ bool overlaps(Range x, Range y) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// One fp32 per token and value head (beta, alpha and their gradients) is read
+// and written as single floats: 4-byte alignment, so that a view starting at
+// any token of a [T, H_v] tensor is accepted.
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Common description checks; `decode` additionally requires T == 1.
 gdn2_status check_desc(const gdn2_desc *d, bool decode) {
@@ -181,9 +185,10 @@ gdn2_status forward_scalar_gates(const gdn2_desc *d, const void *q, const void *
   if (B == 0) return GDN2_OK;
   const bool tokens = T > 0;
   if (tokens && (!q || !k || !v || !a || !beta || !o)) return GDN2_ERR_NULL_POINTER;
-  const void *ptrs[] = {q, k, v, a, beta, S0, o, S_T};
+  const void *ptrs[] = {q, k, v, scalar_decay ? nullptr : a, S0, o, S_T};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+  if ((scalar_decay && a && !aligned4(a)) || (beta && !aligned4(beta))) return GDN2_ERR_BAD_SHAPE;
   const Range rq = range_of(q, B * T * Hqk * dk * es), rk = range_of(k, B * T * Hqk * dk * es);
   const Range rv = range_of(v, B * T * Hv * dv * es);
   const Range ra = range_of(a, B * T * Hv * (scalar_decay ? 1 : dk) * 4), rbeta = range_of(beta, B * T * Hv * 4);
@@ -231,23 +236,42 @@ gdn2_status gdn2_chunk_forward_scalar(const gdn2_desc *d, const void *q, const v
 gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q,
                                       const void *k, const void *v, const float *a, const float *b,
                                       const float *w, const float *S0, void *o, float *S_T, void *stream) {
+  return gdn2_chunk_forward_varlen_gates(d, cu_seqlens, GDN2_GATES_CHANNEL, q, k, v, a, b, w, S0, o, S_T, stream);
+}
+
+gdn2_status gdn2_chunk_forward_varlen_gates(const gdn2_desc *d, const int32_t *cu_seqlens, gdn2_gates gates,
+                                            const void *q, const void *k, const void *v, const void *a,
+                                            const void *b, const void *w, const float *S0, void *o, float *S_T,
+                                            void *stream) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
+  if (gates != GDN2_GATES_CHANNEL && gates != GDN2_GATES_PREACT && gates != GDN2_GATES_COUPLED &&
+      gates != GDN2_GATES_SCALAR)
+    return GDN2_ERR_UNSUPPORTED;
+  const bool preact = gates == GDN2_GATES_PREACT;
+  const bool coupled = gates == GDN2_GATES_COUPLED || gates == GDN2_GATES_SCALAR;
   const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
   const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
   const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
   if (B == 0) return GDN2_OK;
   if (!cu_seqlens) return GDN2_ERR_NULL_POINTER;
   const bool tokens = T > 0;
-  if (tokens && (!q || !k || !v || !a || !b || !w || !o)) return GDN2_ERR_NULL_POINTER;
-  const void *ptrs[] = {q, k, v, a, b, w, S0, o, S_T};
+  if (tokens && (!q || !k || !v || !a || !b || !o)) return GDN2_ERR_NULL_POINTER;
+  if (tokens && !coupled && !w) return GDN2_ERR_NULL_POINTER;
+  if (coupled) w = nullptr;  // the write gate is beta
+  const bool sa = gates == GDN2_GATES_SCALAR;  // a is one scalar per token and value head
+  const void *ptrs[] = {q, k, v, sa ? nullptr : a, coupled ? nullptr : b, w, S0, o, S_T};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
-  // token tensors hold T tokens in all (packed sequences)
+  if ((sa && a && !aligned4(a)) || (coupled && b && !aligned4(b))) return GDN2_ERR_BAD_SHAPE;
+  // token tensors hold T tokens in all (packed sequences); gate elements per
+  // channel, or one per token and value head (beta; alpha in the scalar form)
+  const size_t gs = preact ? es : 4;
+  const size_t na = gates == GDN2_GATES_SCALAR ? T * Hv : T * Hv * dk, nb = coupled ? T * Hv : T * Hv * dk;
   const Range rq = range_of(q, T * Hqk * dk * es), rk = range_of(k, T * Hqk * dk * es);
   const Range rv = range_of(v, T * Hv * dv * es);
-  const Range ra = range_of(a, T * Hv * dk * 4), rb = range_of(b, T * Hv * dk * 4);
-  const Range rw = range_of(w, T * Hv * dv * 4);
+  const Range ra = range_of(a, na * gs), rb = range_of(b, nb * gs);
+  const Range rw = range_of(w, coupled ? 0 : T * Hv * dv * gs);
   const Range ro = range_of(o, T * Hv * dv * es);
   const Range rs0 = range_of(S0, S0 ? B * Hv * dk * dv * 4 : 0);
   const Range rst = range_of(S_T, S_T ? B * Hv * dk * dv * 4 : 0);
@@ -260,7 +284,13 @@ gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *d, const int32_t *cu_seql
   if (S0 && S_T && overlaps(rs0, rst) && S0 != S_T) return GDN2_ERR_ALIAS;
 
   gdn2::PrefillArgs p = prefill_args(d);
-  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.q = q; p.k = k; p.v = v; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.a = static_cast<const float *>(a);  // input dtype when preact
+  p.b = static_cast<const float *>(b);
+  p.w = static_cast<const float *>(coupled ? b : w);
+  p.coupled = coupled;
+  p.scalar_decay = gates == GDN2_GATES_SCALAR;
+  p.preact = preact;
   p.cu_seqlens = cu_seqlens;
   const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
@@ -352,6 +382,27 @@ gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *d, const int32_t *cu_seq
                           workspace_bytes, stream, true, gdn2::kGateGeneral);
 }
 
+gdn2_status gdn2_chunk_backward_varlen_gates(const gdn2_desc *d, const int32_t *cu_seqlens, gdn2_gates gates,
+                                             const void *q, const void *k, const void *v, const void *a,
+                                             const void *b, const void *w, const float *S0, const void *dO,
+                                             const float *dS_T, void *dq, void *dk, void *dv, void *da, void *db,
+                                             void *dw, float *dS0, void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+  int form;
+  switch (gates) {
+    case GDN2_GATES_CHANNEL: form = gdn2::kGateGeneral; break;
+    case GDN2_GATES_PREACT: form = gdn2::kGatePre; break;
+    case GDN2_GATES_COUPLED: form = gdn2::kGateCoupled; break;
+    case GDN2_GATES_SCALAR: form = gdn2::kGateScalar; break;
+    default: {
+      const gdn2_status sd = check_desc(d, false);
+      return sd != GDN2_OK ? sd : GDN2_ERR_UNSUPPORTED;
+    }
+  }
+  return backward_general(d, cu_seqlens, q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0, workspace,
+                          workspace_bytes, stream, true, form);
+}
+
 }  // extern "C"
 
 namespace {
@@ -379,9 +430,14 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
     return GDN2_ERR_NULL_POINTER;
   if (tokens && !coupled && (!w || !dw)) return GDN2_ERR_NULL_POINTER;
   if (coupled) w = dw = nullptr;  // the write gate is beta
-  const void *ptrs[] = {q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0};
+  const bool sa = form == gdn2::kGateScalar;  // a, da one scalar per token and value head
+  const void *ptrs[] = {q, k, v, sa ? nullptr : a, coupled ? nullptr : b, w, S0, dO, dS_T, dq, dk, dv,
+                        sa ? nullptr : da, coupled ? nullptr : db, dw, dS0};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+  const void *scalars[] = {sa ? a : nullptr, sa ? da : nullptr, coupled ? b : nullptr, coupled ? db : nullptr};
+  for (const void *p : scalars)
+    if (p && !aligned4(p)) return GDN2_ERR_BAD_SHAPE;
   if (ws_need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_BAD_SHAPE;
 
   const size_t nqk = BT * Hqk * dkk, nab = BT * Hv * dkk, nvw = BT * Hv * dvv, ns = B * Hv * dkk * dvv;

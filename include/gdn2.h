@@ -56,7 +56,9 @@ typedef enum {
   GDN2_OK = 0,
   GDN2_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   GDN2_ERR_BAD_SHAPE = 2,    /* negative size, H_v % H_qk != 0, decode with T != 1,
-                                a tensor pointer not 16-byte aligned */
+                                a tensor pointer not 16-byte aligned (4-byte for the
+                                tensors of one fp32 per token and value head:
+                                beta, alpha and their gradients) */
   GDN2_ERR_UNSUPPORTED = 3,  /* valid but not built: d_k, d_v not in {16,32,64,128}, chunk not in {16,32,64} */
   GDN2_ERR_BAD_DTYPE = 4,    /* dtype is neither GDN2_F32 nor GDN2_BF16 */
   GDN2_ERR_WORKSPACE = 5,    /* workspace smaller than gdn2_chunk_forward_workspace_bytes() */
@@ -115,7 +117,8 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void 
  * basic idea and its limits), with GDN-2's channel-wise decay kept. The
  * update is then S = S~ + beta_t k_t (v_t - r_t)^T. Same arguments as
  * gdn2_chunk_forward with b, w replaced by
- *   beta: [B, T, H_v] fp32.
+ *   beta: [B, T, H_v] fp32 (4-byte alignment suffices: a view starting at
+ *         any token of a larger tensor is accepted).
  * The result equals gdn2_chunk_forward with b = beta * ones(d_k) and
  * w = beta * ones(d_v) up to rounding: with b = beta the erase-side Gram
  * matrices are the key-side ones with column s scaled by beta_s, so only two
@@ -162,6 +165,35 @@ gdn2_status gdn2_chunk_forward_scalar(const gdn2_desc *desc, const void *q, cons
 gdn2_status gdn2_chunk_forward_varlen(const gdn2_desc *desc, const int32_t *cu_seqlens, const void *q,
                                       const void *k, const void *v, const float *a, const float *b,
                                       const float *w, const float *S0, void *o, float *S_T, void *stream);
+
+/* Gate forms of the packed-sequence calls below (each as the unpacked entry
+ * point of the same form describes it):
+ *   GDN2_GATES_CHANNEL: a, b [T, H_v, d_k], w [T, H_v, d_v] fp32 (gdn2_chunk_forward);
+ *   GDN2_GATES_PREACT : the same shapes, pre-activations in the input dtype
+ *                       (gdn2_chunk_forward_preact);
+ *   GDN2_GATES_COUPLED: a [T, H_v, d_k] fp32, b = beta [T, H_v] fp32, w unused
+ *                       (may be NULL) (gdn2_chunk_forward_coupled);
+ *   GDN2_GATES_SCALAR : a = alpha [T, H_v], b = beta [T, H_v] fp32, w unused
+ *                       (gdn2_chunk_forward_scalar).
+ * Any other value is GDN2_ERR_UNSUPPORTED. */
+typedef enum {
+  GDN2_GATES_CHANNEL = 0,
+  GDN2_GATES_PREACT = 1,
+  GDN2_GATES_COUPLED = 2,
+  GDN2_GATES_SCALAR = 3
+} gdn2_gates;
+
+/* gdn2_chunk_forward_varlen for any gate form: packed sequences exactly as
+ * there (cu_seqlens, one state per sequence, no workspace, each sequence
+ * computed as the unpacked call of the same gate form computes it alone),
+ * with the gates of `gates` (token axis of T tokens in all). Serving a model
+ * of the Gated DeltaNet form over a packed batch is GDN2_GATES_SCALAR.
+ * Errors as for gdn2_chunk_forward_varlen, the gate tensors checked for
+ * overlap with the output at their own sizes. */
+gdn2_status gdn2_chunk_forward_varlen_gates(const gdn2_desc *desc, const int32_t *cu_seqlens, gdn2_gates gates,
+                                            const void *q, const void *k, const void *v, const void *a,
+                                            const void *b, const void *w, const float *S0, void *o, float *S_T,
+                                            void *stream);
 
 /* Prefill with the per-channel gates given as pre-activations: a_pre, b_pre
  * ([B, T, H_v, d_k]) and w_pre ([B, T, H_v, d_v]) in the input dtype
@@ -279,6 +311,21 @@ gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *desc, const int32_t *cu_
                                        const float *S0, const void *dO, const float *dS_T, void *dq, void *dk,
                                        void *dv, float *da, float *db, float *dw, float *dS0, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/* gdn2_chunk_backward_varlen for any gate form (gdn2_gates): the gradients of
+ * gdn2_chunk_forward_varlen_gates. Gate gradients take the shapes and types
+ * of the gates, as in the unpacked backward of the same form: da, db, dw
+ * (CHANNEL, fp32; PREACT, input dtype, gradients of the pre-activations);
+ * da and db = dbeta (COUPLED; SCALAR: da = dalpha [T, H_v]), dw unused (may
+ * be NULL). Workspace: gdn2_chunk_backward_varlen_workspace_bytes(desc);
+ * each sequence's gradients are those of the unpacked call on it alone.
+ * Errors as for gdn2_chunk_backward_varlen. */
+gdn2_status gdn2_chunk_backward_varlen_gates(const gdn2_desc *desc, const int32_t *cu_seqlens, gdn2_gates gates,
+                                             const void *q, const void *k, const void *v, const void *a,
+                                             const void *b, const void *w, const float *S0, const void *dO,
+                                             const float *dS_T, void *dq, void *dk, void *dv, void *da, void *db,
+                                             void *dw, float *dS0, void *workspace, size_t workspace_bytes,
+                                             void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *gdn2_status_string(gdn2_status status);

@@ -127,7 +127,13 @@ def test_coupled_argument_errors():
         p[i] = 0
         assert fc(d, p) == g.GDN2_ERR_NULL_POINTER, i
     p = _ptrs()[:8]
-    p[4] += 4
+    p[4] += 2
+    assert fc(d, p) == g.GDN2_ERR_BAD_SHAPE
+    p[4] += 2  # beta needs 4-byte alignment only: the call gets to the overlap check
+    p[6] = p[4] + 12  # o (16-byte aligned) inside beta
+    assert fc(d, p) == g.GDN2_ERR_ALIAS
+    p = _ptrs()[:8]
+    p[3] += 4  # the per-channel decay keeps 16
     assert fc(d, p) == g.GDN2_ERR_BAD_SHAPE
     for i in (0, 3, 4, 5, 7):
         p = _ptrs()[:8]
@@ -300,8 +306,11 @@ def test_backward_coupled_scalar_errors():
             p[i] = 0
             assert call(p) == g.GDN2_ERR_NULL_POINTER, i
         p = list(base)
-        p[12] += 8
+        p[12] += 2  # dbeta needs 4-byte alignment
         assert call(p) == g.GDN2_ERR_BAD_SHAPE
+        p[12] += 2
+        p[11] = p[12] + 12  # ... and passes with it: the overlap of da with it is found next
+        assert call(p) == g.GDN2_ERR_ALIAS
         p = list(base)
         p[12] = p[4] + 16  # dbeta over beta
         assert call(p) == g.GDN2_ERR_ALIAS
@@ -315,6 +324,55 @@ def test_backward_coupled_scalar_errors():
     p[12] -= 16  # ... and 16 bytes earlier it is
     p[8] -= 4
     assert g.gdn2_chunk_backward_scalar(d, *p, ws, need, 0) == g.GDN2_ERR_ALIAS
+
+
+def test_varlen_gate_forms_errors():
+    """Packed sequences in the other gate forms: an unknown form is
+    unsupported, w may be null for the coupled forms (and is required
+    otherwise), a null cu_seqlens is rejected, and the gates are checked for
+    overlap at their own sizes; all before any launch."""
+    d = g.make_desc(3, 50, 1, 2, 64, 64, 64, g.GDN2_BF16)
+    cu = FAKE + 50 * (1 << 30)
+    base = [FAKE + i * (1 << 30) for i in range(8)]  # q, k, v, a, b, w, S0, o (S_T last, none)
+    fwd = lambda form, p, cu_=cu: g.gdn2_chunk_forward_varlen_gates(d, cu_, form, *p, 0, 0)
+    for form in (4, -1, 100):
+        assert fwd(form, base) == g.GDN2_ERR_UNSUPPORTED, form
+    assert fwd(2, base, 0) == g.GDN2_ERR_NULL_POINTER
+    for form in (0, 1):
+        p = list(base)
+        p[5] = 0
+        assert fwd(form, p) == g.GDN2_ERR_NULL_POINTER, form
+    for form in (2, 3):
+        p = list(base)
+        p[5] = 0
+        p[7] = p[4] + 16  # o over beta
+        assert fwd(form, p) == g.GDN2_ERR_ALIAS, form
+        p[7] = p[4] + 50 * 2 * 4  # o just past beta (T * H_v floats): no overlap, fails later on alignment
+        p[0] += 4
+        assert fwd(form, p) == g.GDN2_ERR_BAD_SHAPE, form
+    # scalar alpha holds T * H_v floats; the coupled per-channel decay T * H_v * d_k
+    p = list(base)
+    p[7] = p[3] + 50 * 2 * 4
+    p[0] += 4
+    assert fwd(3, p) == g.GDN2_ERR_BAD_SHAPE
+    p[0] -= 4
+    assert fwd(2, p) == g.GDN2_ERR_ALIAS
+    # backward: unknown form, null dw allowed for the coupled forms
+    need = g.gdn2_chunk_backward_varlen_workspace_bytes(d)
+    ws = FAKE + 40 * (1 << 30)
+    bb = [FAKE + i * (1 << 30) for i in range(16)]
+    bwd = lambda form, p: g.gdn2_chunk_backward_varlen_gates(d, cu, form, *p, ws, need, 0)
+    assert bwd(7, bb) == g.GDN2_ERR_UNSUPPORTED
+    assert g.gdn2_chunk_backward_varlen_gates(None, cu, 7, *bb, ws, need, 0) == g.GDN2_ERR_NULL_POINTER
+    for form in (0, 1):
+        p = list(bb)
+        p[14] = 0  # dw
+        assert bwd(form, p) == g.GDN2_ERR_NULL_POINTER, form
+    for form in (2, 3):
+        p = list(bb)
+        p[5] = p[14] = 0
+        p[9] += 4  # misaligned dq: the pointer checks passed
+        assert bwd(form, p) == g.GDN2_ERR_BAD_SHAPE, form
 
 
 def test_binding_exposes_every_entry_point_wrapper():

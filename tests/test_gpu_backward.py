@@ -307,3 +307,43 @@ def test_scalar_backward_layer_shape_scaled():
         err = normwise(to_np(gg[nm]), ref[nm])
         print(f"[scalar backward c1-scaled {nm}] {err:.2e}", flush=True)
         assert err <= TOL["bf16"], (nm, err)
+
+
+@pytest.mark.parametrize("form,dt", [("preact", "bf16"), ("preact", "f32"), ("coupled", "bf16"), ("coupled", "f32"),
+                                     ("scalar", "bf16"), ("scalar", "f32")])
+def test_varlen_gate_forms_backward_match_separate_calls(form, dt):
+    """Backward of packed sequences in each gate form
+    (gdn2_chunk_backward_varlen_gates): every sequence's gradients bit for bit
+    those of the unpacked backward of the same form on it alone, and the
+    longer sequences against the oracle of the form."""
+    from tests.gate_forms import backward_alone, form_inputs, oracle_backward, sl
+    rng = np.random.default_rng(4500 + len(form) + (dt == "bf16"))
+    lens = [0, 1, 5, 17, 64, 3]
+    N, T, Hv, dk, dv = len(lens), sum(lens), 2, 128, 64
+    x = form_inputs(rng, form, T, Hv, dk, dv, dt, DEV)
+    tdt = x["q"].dtype
+    S0 = torch.from_numpy((rng.standard_normal((N, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
+    dO = torch.from_numpy(rng.standard_normal((1, T, Hv, dv)).astype(np.float32)).to(tdt).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((N, Hv, dk, dv)).astype(np.float32)).to(DEV)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cut = torch.from_numpy(cu).to(DEV)
+    gv = g.chunk_backward_varlen(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], cut, S0, dO, dST, gates=form)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "da", "db") + (("dw",) if form in ("channel", "preact") else ())
+    assert form in ("channel", "preact") or gv["dw"] is None
+    for n in range(N):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        xs = {nm: sl(t, t0, t1) for nm, t in x.items()}
+        alone = backward_alone(form, xs, S0[n:n + 1].contiguous(), sl(dO, t0, t1), dST[n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        for nm in names:
+            assert torch.equal(gv[nm][:, t0:t1], alone[nm]), (n, nm)
+        assert torch.equal(gv["dS0"][n:n + 1], alone["dS0"]), n
+        if t1 - t0 >= 17:
+            ref = oracle_backward(form, xs, S0[n:n + 1], sl(dO, t0, t1), dST[n:n + 1])
+            errs = {nm: normwise(to_np(gv[nm][:, t0:t1]), ref[nm]) for nm in names}
+            errs["dS0"] = normwise(to_np(gv["dS0"][n:n + 1]), ref["dS0"])
+            print(f"[backward varlen {form} {dt} seq{n} len{t1 - t0}] " +
+                  " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+            bad = {k: v for k, v in errs.items() if not v <= TOL[dt]}
+            assert not bad, (n, bad)

@@ -436,3 +436,35 @@ def test_preact_full_layer_shape_sampled_heads():
         es = normwise(to_np(ST[n:n + 1, h:h + 1]), ref_S)
         print(f"[preact full n{n} h{h}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
         assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+
+
+@pytest.mark.parametrize("form,dtype", [("preact", "bf16"), ("preact", "f32"), ("coupled", "bf16"),
+                                        ("coupled", "f32"), ("scalar", "bf16"), ("scalar", "f32")])
+def test_varlen_gate_forms_match_separate_calls(form, dtype):
+    """Packed sequences in each gate form (gdn2_chunk_forward_varlen_gates):
+    every sequence bit for bit the unpacked call of the same form on it alone
+    (empty, one-token, ragged and multi-chunk sequences, per-sequence S0), and
+    the longer sequences against the oracle of the form."""
+    from tests.gate_forms import form_inputs, forward_alone, oracle_forward, sl
+    rng = np.random.default_rng(150 + len(form) + (dtype == "bf16"))
+    lens = [0, 1, 31, 64, 100, 5, 130]
+    N, T, Hv, dk, dv = len(lens), sum(lens), 2, 128, 128
+    x = form_inputs(rng, form, T, Hv, dk, dv, dtype, DEV)
+    S0 = torch.from_numpy((rng.standard_normal((N, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cut = torch.from_numpy(cu).to(DEV)
+    sq = lambda t: None if t is None else t[0]
+    o, ST = g.chunk_forward_varlen(sq(x["q"]), sq(x["k"]), sq(x["v"]), sq(x["a"]), sq(x["b"]), sq(x["w"]), cut, S0,
+                                   chunk=64, gates=form)
+    torch.cuda.synchronize()
+    for n in range(N):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        xs = {nm: sl(t, t0, t1) for nm, t in x.items()}
+        o1, S1 = forward_alone(form, xs, S0[n:n + 1].contiguous(), 64)
+        torch.cuda.synchronize()
+        assert torch.equal(o[t0:t1], o1[0]) and torch.equal(ST[n], S1[0]), n
+        if t1 - t0 >= 64:
+            ref_o, ref_S = oracle_forward(form, xs, S0[n:n + 1])
+            eo, es = normwise(to_np(o[t0:t1]), ref_o[0]), normwise(to_np(ST[n]), ref_S[0])
+            print(f"[varlen {form} {dtype} seq {n} len {t1 - t0}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
+            assert eo <= TOL[dtype] and es <= TOL[dtype], (n, eo, es)
