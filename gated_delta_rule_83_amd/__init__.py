@@ -45,7 +45,7 @@ EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forw
             "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
             "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes", "gdn2_chunk_backward_preact",
             "gdn2_chunk_backward_coupled", "gdn2_chunk_backward_scalar", "gdn2_chunk_forward_varlen_gates",
-            "gdn2_chunk_backward_varlen_gates",
+            "gdn2_chunk_backward_varlen_gates", "gdn2_decode_step_gates",
             "gdn2_status_string", "gdn2_version")
 
 
@@ -88,6 +88,8 @@ def load(path: Optional[str] = None):
     lib.gdn2_chunk_backward_varlen_gates.argtypes = [dp, vp, ctypes.c_int] + [vp] * 16 + [vp, sz, vp]
     lib.gdn2_chunk_forward_varlen.restype = ctypes.c_int
     lib.gdn2_chunk_forward_varlen.argtypes = [dp] + [vp] * 10 + [vp]
+    lib.gdn2_decode_step_gates.restype = ctypes.c_int
+    lib.gdn2_decode_step_gates.argtypes = [dp, ctypes.c_int] + [vp] * 8 + [vp]
     lib.gdn2_decode_step.restype = ctypes.c_int
     lib.gdn2_decode_step.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn2_chunk_forward_workspace_bytes.restype = sz
@@ -171,6 +173,11 @@ def gdn2_chunk_backward_varlen_gates(desc, cu_seqlens, gates, q, k, v, a, b, w, 
     return load().gdn2_chunk_backward_varlen_gates(None if desc is None else ctypes.byref(desc), cu_seqlens, gates,
                                                    q, k, v, a, b, w, S0, dO, dS_T, dq, dk, dv, da, db, dw, dS0,
                                                    workspace, workspace_bytes, stream)
+
+
+def gdn2_decode_step_gates(desc, gates, q, k, v, a, b, w, S, o, stream=0) -> int:
+    return load().gdn2_decode_step_gates(None if desc is None else ctypes.byref(desc), gates, q, k, v, a, b, w, S, o,
+                                         stream)
 
 
 def gdn2_chunk_backward_workspace_bytes(desc) -> int:
@@ -492,23 +499,28 @@ def chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64,
     return o, S_T
 
 
-def decode_step(q, k, v, a, b, w, S, o=None, stream=None):
+def decode_step(q, k, v, a, b, w, S, o=None, stream=None, gates: str = "channel"):
     """One decode token. q, k [N,1,H_qk,d_k] (or [N,H_qk,d_k]); v [N,1,H_v,d_v];
     a, b [N,1,H_v,d_k]; w [N,1,H_v,d_v]; S [N,H_v,d_k,d_v] fp32, updated in place.
-    Returns o shaped like v."""
+    Returns o shaped like v. `gates` as for chunk_forward_varlen: "preact"
+    (a, b, w pre-activations in the input dtype), "coupled" (b = beta
+    [N,1,H_v] fp32, w None), "scalar" (a = alpha, b = beta, each [N,1,H_v])."""
     import torch
     N, H_v, d_k, d_v = S.shape
     H_qk = q.shape[-2]
+    form = GDN2_GATES[gates]
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, nm, q.dtype)
-    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S, "S")):
-        _check(t, nm, torch.float32)
+    gdt = q.dtype if gates == "preact" else torch.float32
+    for t, nm in ((a, "a"), (b, "b"), (w, "w")):
+        _check(t, nm, gdt)
+    _check(S, "S", torch.float32)
     if o is None:
         o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     _check(o, "o", q.dtype)
     desc = make_desc(N, 1, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
-    st = gdn2_decode_step(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S),
-                          _ptr(o), _stream(stream))
+    st = gdn2_decode_step_gates(desc, form, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S),
+                                _ptr(o), _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st)
     return o

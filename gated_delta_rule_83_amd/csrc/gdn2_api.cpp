@@ -299,20 +299,40 @@ gdn2_status gdn2_chunk_forward_varlen_gates(const gdn2_desc *d, const int32_t *c
 gdn2_status gdn2_decode_step(const gdn2_desc *d, const void *q, const void *k, const void *v,
                              const float *a, const float *b, const float *w, float *S, void *o,
                              void *stream) {
+  return gdn2_decode_step_gates(d, GDN2_GATES_CHANNEL, q, k, v, a, b, w, S, o, stream);
+}
+
+gdn2_status gdn2_decode_step_gates(const gdn2_desc *d, gdn2_gates gates, const void *q, const void *k,
+                                   const void *v, const void *a, const void *b, const void *w, float *S, void *o,
+                                   void *stream) {
   gdn2_status st = check_desc(d, true);
   if (st != GDN2_OK) return st;
+  int form;
+  switch (gates) {
+    case GDN2_GATES_CHANNEL: form = gdn2::kGateGeneral; break;
+    case GDN2_GATES_PREACT: form = gdn2::kGatePre; break;
+    case GDN2_GATES_COUPLED: form = gdn2::kGateCoupled; break;
+    case GDN2_GATES_SCALAR: form = gdn2::kGateScalar; break;
+    default: return GDN2_ERR_UNSUPPORTED;
+  }
+  const bool coupled = form == gdn2::kGateCoupled || form == gdn2::kGateScalar;
+  const bool sa = form == gdn2::kGateScalar;
   const size_t B = (size_t)d->B, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
   const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
   const size_t es = d->dtype == GDN2_BF16 ? 2 : 4;
   if (B == 0) return GDN2_OK;
-  if (!q || !k || !v || !a || !b || !w || !S || !o) return GDN2_ERR_NULL_POINTER;
-  const void *ptrs[] = {q, k, v, a, b, w, S, o};
+  if (!q || !k || !v || !a || !b || !S || !o) return GDN2_ERR_NULL_POINTER;
+  if (!coupled && !w) return GDN2_ERR_NULL_POINTER;
+  if (coupled) w = nullptr;  // the write gate is beta
+  const void *ptrs[] = {q, k, v, sa ? nullptr : a, coupled ? nullptr : b, w, S, o};
   for (const void *p : ptrs)
-    if (!aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+    if (p && !aligned16(p)) return GDN2_ERR_BAD_SHAPE;
+  if ((sa && !aligned4(a)) || (coupled && !aligned4(b))) return GDN2_ERR_BAD_SHAPE;
+  const size_t gs = form == gdn2::kGatePre ? es : 4;  // gate element bytes
   const Range ro = range_of(o, B * Hv * dv * es);
   const Range ins[] = {range_of(q, B * Hqk * dk * es), range_of(k, B * Hqk * dk * es),
-                       range_of(v, B * Hv * dv * es),  range_of(a, B * Hv * dk * 4),
-                       range_of(b, B * Hv * dk * 4),   range_of(w, B * Hv * dv * 4),
+                       range_of(v, B * Hv * dv * es),  range_of(a, B * Hv * (sa ? 1 : dk) * gs),
+                       range_of(b, B * Hv * (coupled ? 1 : dk) * gs), range_of(w, coupled ? 0 : B * Hv * dv * gs),
                        range_of(S, B * Hv * dk * dv * 4)};
   for (const Range &r : ins)
     if (overlaps(ro, r)) return GDN2_ERR_ALIAS;
@@ -320,7 +340,7 @@ gdn2_status gdn2_decode_step(const gdn2_desc *d, const void *q, const void *k, c
   gdn2::DecodeArgs p;
   p.B = d->B; p.H_qk = d->H_qk; p.H_v = d->H_v; p.d_k = d->d_k; p.d_v = d->d_v;
   p.bf16 = d->dtype == GDN2_BF16;
-  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.S = S; p.o = o;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.w = w; p.gate_form = form; p.S = S; p.o = o;
   const hipError_t e = gdn2::launch_decode(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }

@@ -1,6 +1,9 @@
 // gdn2_decode.hip -- single-token decode step of the Gated DeltaNet-2
 // recurrence: one streaming pass over the fp32 state.
 //
+// Gate forms as for the prefill: per-channel gates, their pre-activations,
+// the coupled erase/write gate beta, and the scalar decay alpha with it.
+//
 // Per (sequence n, value head h) the step is (Gated DeltaNet-2 post on
 // tilnote.io, GDN-2 design section; delta-rule tutorial on
 // ai-systems-engineering.com, "record the difference" and key-versus-query
@@ -54,14 +57,15 @@ __device__ __forceinline__ floatx4 column_sum(floatx4 x, float (*red)[DV], int t
   return s;
 }
 
-template <int DK, int DV, bool BF16>
+template <int DK, int DV, bool BF16, int GF>
 __global__ __launch_bounds__((DecodeCfg<DK, DV>::NT)) void decode_step_kernel(
     const typename Elem<BF16>::T *__restrict__ q, const typename Elem<BF16>::T *__restrict__ k,
-    const typename Elem<BF16>::T *__restrict__ v, const float *__restrict__ a,
-    const float *__restrict__ b, const float *__restrict__ w, float *__restrict__ S,
+    const typename Elem<BF16>::T *__restrict__ v, const void *__restrict__ a,
+    const void *__restrict__ b, const void *__restrict__ w, float *__restrict__ S,
     typename Elem<BF16>::T *__restrict__ o, int H_qk, int H_v) {
   using Cf = DecodeCfg<DK, DV>;
   using E = Elem<BF16>;
+  using ET = typename E::T;
   __shared__ float s_a[DK], s_bk[DK], s_k[DK], s_q[DK], s_u[DV];
   __shared__ float s_red1[Cf::NW][DV], s_red2[Cf::NW][DV];
 
@@ -79,18 +83,38 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::NT)) void decode_step_kernel(
     const int row = r * Cf::RG + rg;
     s[r] = *reinterpret_cast<const floatx4 *>(Sh + row * DV + 4 * c4);
   }
-  // Per-row gates and per-column values through LDS (tiny).
+  // Per-row gates and per-column values through LDS (tiny), in the gate form
+  // GF: per-channel fp32; per-channel pre-activations in the input dtype,
+  // activated here; coupled beta (b = w, one fp32 per head); scalar alpha
+  // and beta.
   const size_t qk_off = ((size_t)n * H_qk + g) * DK;
   const size_t ab_off = (size_t)unit * DK;
   const size_t vw_off = (size_t)unit * DV;
+  const float *af = static_cast<const float *>(a), *bf = static_cast<const float *>(b);
+  const float *wf = static_cast<const float *>(w);
   for (int i = tid; i < DK; i += Cf::NT) {
     const float kk = E::ld(k + qk_off + i);
     s_k[i] = kk;
     s_q[i] = E::ld(q + qk_off + i);
-    s_a[i] = a[ab_off + i];
-    s_bk[i] = b[ab_off + i] * kk;
+    float ai, bi;
+    if constexpr (GF == kGatePre) {
+      ai = decay_from_pre(E::ld(static_cast<const ET *>(a) + ab_off + i));
+      bi = gate_from_pre(E::ld(static_cast<const ET *>(b) + ab_off + i));
+    } else {
+      ai = GF == kGateScalar ? af[unit] : af[ab_off + i];
+      bi = GF >= kGateCoupled ? bf[unit] : bf[ab_off + i];
+    }
+    s_a[i] = ai;
+    s_bk[i] = bi * kk;
   }
-  for (int j = tid; j < DV; j += Cf::NT) s_u[j] = w[vw_off + j] * E::ld(v + vw_off + j);
+  for (int j = tid; j < DV; j += Cf::NT) {
+    float wj;
+    if constexpr (GF == kGatePre)
+      wj = gate_from_pre(E::ld(static_cast<const ET *>(w) + vw_off + j));
+    else
+      wj = GF >= kGateCoupled ? bf[unit] : wf[vw_off + j];
+    s_u[j] = wj * E::ld(v + vw_off + j);
+  }
   __syncthreads();
 
   // Decay the key-axis rows, then the key read of the decayed state.
@@ -121,15 +145,23 @@ __global__ __launch_bounds__((DecodeCfg<DK, DV>::NT)) void decode_step_kernel(
   }
 }
 
+template <int DK, int DV, bool BF16, int GF>
+static void launch_decode_form(const DecodeArgs &p, hipStream_t st) {
+  using T = typename Elem<BF16>::T;
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, BF16, GF>), dim3(p.B * p.H_v), dim3(DecodeCfg<DK, DV>::NT), 0,
+                     st, (const T *)p.q, (const T *)p.k, (const T *)p.v, p.a, p.b, p.w, p.S, (T *)p.o, p.H_qk,
+                     p.H_v);
+}
+
 template <int DK, int DV, bool BF16>
 static hipError_t launch_decode_t(const DecodeArgs &p, hipStream_t st) {
-  using E = Elem<BF16>;
-  using T = typename E::T;
-  const int units = p.B * p.H_v;
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, BF16>), dim3(units), dim3(DecodeCfg<DK, DV>::NT), 0,
-                     st, (const T *)p.q, (const T *)p.k, (const T *)p.v, p.a, p.b, p.w, p.S,
-                     (T *)p.o, p.H_qk, p.H_v);
+  if (p.B * p.H_v == 0) return hipSuccess;
+  switch (p.gate_form) {
+    case kGatePre: launch_decode_form<DK, DV, BF16, kGatePre>(p, st); break;
+    case kGateCoupled: launch_decode_form<DK, DV, BF16, kGateCoupled>(p, st); break;
+    case kGateScalar: launch_decode_form<DK, DV, BF16, kGateScalar>(p, st); break;
+    default: launch_decode_form<DK, DV, BF16, kGateGeneral>(p, st); break;
+  }
   return hipGetLastError();
 }
 

@@ -8,11 +8,17 @@
 
 namespace gdn2 {
 
+// Gate forms: per-channel fp32 gates; per-channel pre-activations in the
+// input dtype; coupled b = w = beta (one fp32 per token and value head);
+// scalar, also a = alpha (one fp32 per token and value head).
+enum { kGateGeneral = 0, kGatePre = 1, kGateCoupled = 2, kGateScalar = 3 };
+
 struct DecodeArgs {
   int B, H_qk, H_v, d_k, d_v;
   bool bf16;
   const void *q, *k, *v;
-  const float *a, *b, *w;
+  const void *a, *b, *w;  // layout and type by gate_form
+  int gate_form;
   float *S;
   void *o;
 };
@@ -57,7 +63,6 @@ struct PrefillPlan {
 constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
 
 // Backward pass (gradients of the recurrence); see gdn2_chunk_backward.
-enum { kGateGeneral = 0, kGatePre = 1, kGateCoupled = 2, kGateScalar = 3 };
 struct BackwardArgs {
   int B, T, H_qk, H_v, d_k, d_v;
   bool bf16;

@@ -219,6 +219,18 @@ gdn2_status gdn2_decode_step(const gdn2_desc *desc, const void *q, const void *k
                              const float *a, const float *b, const float *w, float *S, void *o,
                              void *stream);
 
+/* gdn2_decode_step in any gate form (gdn2_gates): a, b, w shaped as for
+ * gdn2_chunk_forward_varlen_gates with one token per sequence ([B, 1, H_v, d_k]
+ * per-channel gates or their pre-activations in the input dtype; beta and
+ * alpha [B, 1, H_v] fp32, 4-byte alignment; w unused, may be NULL, for the
+ * coupled and scalar forms), i.e. the decode of gdn2_chunk_forward_preact,
+ * _coupled and _scalar. The gates are staged once per head before the state
+ * streams through, so every form moves the same state bytes. Errors as for
+ * gdn2_decode_step; an unknown form is GDN2_ERR_UNSUPPORTED. */
+gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, const void *q, const void *k,
+                                   const void *v, const void *a, const void *b, const void *w, float *S, void *o,
+                                   void *stream);
+
 /* Backward pass of gdn2_chunk_forward: the gradients of a loss with respect
  * to every input, given its gradients dO = dLoss/do and dS_T = dLoss/dS_T.
  * The pages define no backward pass; training the layer (the Gated

@@ -12,23 +12,23 @@ from tests.parity import rand_inputs
 FORMS = ("channel", "preact", "coupled", "scalar")
 
 
-def form_inputs(rng, form, T, Hv, dk, dv, dtype, dev):
-    """Torch inputs [1, T, ...] of one gate form (grouped heads: H_qk = 1)."""
+def form_inputs(rng, form, T, Hv, dk, dv, dtype, dev, B=1, Hqk=1):
+    """Torch inputs [B, T, ...] of one gate form (grouped heads when Hqk < Hv)."""
     f = np.float32
-    d = rand_inputs(rng, 1, T, 1, Hv, dk, dv, with_s0=False)
+    d = rand_inputs(rng, B, T, Hqk, Hv, dk, dv, with_s0=False)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     x = {nm: torch.from_numpy(d[nm]).to(tdt).to(dev) for nm in ("q", "k", "v")}
     if form == "channel":
         for nm in ("a", "b", "w"):
             x[nm] = torch.from_numpy(d[nm]).to(dev)
     elif form == "preact":
-        x["a"] = torch.from_numpy((rng.standard_normal((1, T, Hv, dk)) - 2.0).astype(f)).to(tdt).to(dev)
-        x["b"] = torch.from_numpy(rng.standard_normal((1, T, Hv, dk)).astype(f)).to(tdt).to(dev)
-        x["w"] = torch.from_numpy(rng.standard_normal((1, T, Hv, dv)).astype(f)).to(tdt).to(dev)
+        x["a"] = torch.from_numpy((rng.standard_normal((B, T, Hv, dk)) - 2.0).astype(f)).to(tdt).to(dev)
+        x["b"] = torch.from_numpy(rng.standard_normal((B, T, Hv, dk)).astype(f)).to(tdt).to(dev)
+        x["w"] = torch.from_numpy(rng.standard_normal((B, T, Hv, dv)).astype(f)).to(tdt).to(dev)
     else:
-        a = rng.uniform(0.5, 1.0, (1, T, Hv)).astype(f) if form == "scalar" else d["a"]
+        a = rng.uniform(0.5, 1.0, (B, T, Hv)).astype(f) if form == "scalar" else d["a"]
         x["a"] = torch.from_numpy(a).to(dev)
-        x["b"] = torch.from_numpy(rng.uniform(0.0, 1.0, (1, T, Hv)).astype(f)).to(dev)
+        x["b"] = torch.from_numpy(rng.uniform(0.0, 1.0, (B, T, Hv)).astype(f)).to(dev)
         x["w"] = None
     return x
 

@@ -375,6 +375,32 @@ def test_varlen_gate_forms_errors():
         assert bwd(form, p) == g.GDN2_ERR_BAD_SHAPE, form
 
 
+def test_decode_gate_forms_errors():
+    """Decode in the other gate forms: unknown form, w optional only for the
+    coupled forms, 4-byte alignment for beta and alpha, overlaps at the gate
+    sizes; all before any launch."""
+    d = g.make_desc(4, 1, 2, 2, 64, 64, 64, g.GDN2_BF16)
+    base = [FAKE + i * (1 << 30) for i in range(9)]  # q, k, v, a, b, w, S, o (stream last)
+    dec = lambda form, p: g.gdn2_decode_step_gates(d, form, *p[:8], 0)
+    assert dec(9, base) == g.GDN2_ERR_UNSUPPORTED
+    assert g.gdn2_decode_step_gates(g.make_desc(4, 2, 2, 2, 64, 64, 64, 1), 2, *base[:8], 0) == g.GDN2_ERR_BAD_SHAPE
+    for form in (0, 1):
+        p = list(base)
+        p[5] = 0
+        assert dec(form, p) == g.GDN2_ERR_NULL_POINTER, form
+    for form in (2, 3):
+        p = list(base)
+        p[5] = 0
+        p[4] += 2
+        assert dec(form, p) == g.GDN2_ERR_BAD_SHAPE, form  # beta not 4-byte aligned
+        p[4] += 2
+        p[7] = p[4] + 12  # o over beta: found after the alignment checks pass
+        assert dec(form, p) == g.GDN2_ERR_ALIAS, form
+        p[7] = p[4] + 4 * 2 * 4 + 12  # o just past beta's B * H_v floats
+        p[0] += 4
+        assert dec(form, p) == g.GDN2_ERR_BAD_SHAPE, form
+
+
 def test_binding_exposes_every_entry_point_wrapper():
     """The torch-level wrappers of every entry point exist (import-time check;
     the GPU tests exercise them)."""

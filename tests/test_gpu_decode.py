@@ -91,3 +91,36 @@ def test_decode_workload_full_1024_steps():
     """Workload c4 as stated: 256 sequences x 16 heads, 1024 steps; sampled heads."""
     c = gi.config(4)
     _decode_workload(c, c.decode_steps, [(0, 0), (100, 7), (255, 15)])
+
+
+@pytest.mark.parametrize("form,dtype,dk,dv", [("preact", "bf16", 128, 128), ("preact", "f32", 64, 32),
+                                              ("coupled", "bf16", 128, 128), ("coupled", "f32", 32, 64),
+                                              ("scalar", "bf16", 128, 128), ("scalar", "f32", 16, 128)])
+def test_decode_gate_forms(form, dtype, dk, dv):
+    """gdn2_decode_step_gates: T successive decode steps of each gate form from
+    a random state equal the oracle's recurrence of that form over T tokens
+    (every output and the final state); the coupled and scalar forms equal,
+    bit for bit, the per-channel decode fed the broadcast gates."""
+    from tests.gate_forms import form_inputs, oracle_forward
+    rng = np.random.default_rng(230 + dk + dv + len(form))
+    N, T, Hv = 3, 6, 4
+    x = form_inputs(rng, form, T, Hv, dk, dv, dtype, DEV, B=N, Hqk=2)
+    S0 = torch.from_numpy((rng.standard_normal((N, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
+    S, S_ch = S0.clone(), S0.clone()
+    outs = []
+    for t in range(T):
+        st = {nm: None if v is None else v[:, t:t + 1].contiguous() for nm, v in x.items()}
+        outs.append(g.decode_step(st["q"], st["k"], st["v"], st["a"], st["b"], st["w"], S, gates=form))
+        if form in ("coupled", "scalar"):
+            a = st["a"][..., None].expand(N, 1, Hv, dk).contiguous() if form == "scalar" else st["a"]
+            bb = st["b"][..., None]
+            o_ch = g.decode_step(st["q"], st["k"], st["v"], a, bb.expand(N, 1, Hv, dk).contiguous(),
+                                 bb.expand(N, 1, Hv, dv).contiguous(), S_ch)
+            torch.cuda.synchronize()
+            assert torch.equal(outs[-1], o_ch) and torch.equal(S, S_ch), t
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1)
+    ref_o, ref_S = oracle_forward(form, x, S0)
+    eo, es = normwise(to_np(o), ref_o), normwise(to_np(S), ref_S)
+    print(f"[decode {form} {dtype} dk{dk} dv{dv}] o err {eo:.3e} S err {es:.3e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
