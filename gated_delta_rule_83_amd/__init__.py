@@ -641,3 +641,41 @@ def gated_delta_rule_scalar(q, k, v, alpha, beta, S0=None, chunk: int = 64):
     if "scalar" not in _GDR2C:
         _GDR2C["scalar"] = _autograd_function_scalar_gates("scalar")
     return _GDR2C["scalar"].apply(q, k, v, alpha, beta, S0, chunk)
+
+
+_GDR2V = None
+
+
+def _autograd_function_varlen():
+    import torch
+
+    class GatedDeltaRule2Varlen(torch.autograd.Function):
+        """Packed sequences in any gate form: chunk_forward_varlen /
+        chunk_backward_varlen with the same `gates`."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, a, b, w, cu_seqlens, S0, chunk, gates):
+            o, S_T = chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0, chunk=chunk, gates=gates)
+            ctx.save_for_backward(q, k, v, a, b, w, cu_seqlens, S0)
+            ctx.gates = gates
+            return o, S_T
+
+        @staticmethod
+        def backward(ctx, dO, dS_T):
+            q, k, v, a, b, w, cu, S0 = ctx.saved_tensors
+            g = chunk_backward_varlen(q, k, v, a, b, w, cu, S0, dO.contiguous(),
+                                      None if dS_T is None else dS_T.contiguous(), want_dS0=S0 is not None,
+                                      gates=ctx.gates)
+            return g["dq"], g["dk"], g["dv"], g["da"], g["db"], g.get("dw"), None, g["dS0"], None, None
+
+    return GatedDeltaRule2Varlen
+
+
+def gated_delta_rule_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64, gates: str = "channel"):
+    """Differentiable prefill of packed sequences (cu_seqlens, one state per
+    sequence) in any gate form (`gates` as for chunk_forward_varlen; w is None
+    for "coupled" and "scalar"); returns (o, S_T [N,H_v,d_k,d_v])."""
+    global _GDR2V
+    if _GDR2V is None:
+        _GDR2V = _autograd_function_varlen()
+    return _GDR2V.apply(q, k, v, a, b, w, cu_seqlens, S0, chunk, gates)

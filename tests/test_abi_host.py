@@ -407,5 +407,6 @@ def test_binding_exposes_every_entry_point_wrapper():
     for name in ("chunk_forward", "chunk_forward_preact", "chunk_forward_coupled", "chunk_forward_scalar",
                  "chunk_forward_varlen", "decode_step", "chunk_backward", "chunk_backward_preact",
                  "chunk_backward_varlen", "chunk_backward_coupled", "chunk_backward_scalar", "gated_delta_rule",
-                 "gated_delta_rule_preact", "gated_delta_rule_coupled", "gated_delta_rule_scalar"):
+                 "gated_delta_rule_preact", "gated_delta_rule_coupled", "gated_delta_rule_scalar",
+                 "gated_delta_rule_varlen", "decode_step"):
         assert callable(getattr(g, name, None)), name

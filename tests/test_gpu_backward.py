@@ -347,3 +347,30 @@ def test_varlen_gate_forms_backward_match_separate_calls(form, dt):
                   " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
             bad = {k: v for k, v in errs.items() if not v <= TOL[dt]}
             assert not bad, (n, bad)
+
+
+@pytest.mark.parametrize("form", ["channel", "scalar"])
+def test_varlen_autograd_wrapper(form):
+    """gated_delta_rule_varlen: the gradients autograd returns for packed
+    sequences equal chunk_backward_varlen's for the same upstream gradients
+    (bit for bit), in the per-channel and the scalar gate forms."""
+    from tests.gate_forms import form_inputs
+    rng = np.random.default_rng(4600 + len(form))
+    lens = [7, 0, 40, 21]
+    N, T, Hv, dk, dv = len(lens), sum(lens), 2, 64, 64
+    x = form_inputs(rng, form, T, Hv, dk, dv, "bf16", DEV)
+    S0 = torch.from_numpy((rng.standard_normal((N, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
+    cut = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    names = [nm for nm in ("q", "k", "v", "a", "b", "w") if x[nm] is not None]
+    leaves = {nm: x[nm].clone().requires_grad_(True) for nm in names}
+    leaves["S0"] = S0.clone().requires_grad_(True)
+    dO = torch.from_numpy(rng.standard_normal((1, T, Hv, dv)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((N, Hv, dk, dv)).astype(np.float32)).to(DEV)
+    o, ST = g.gated_delta_rule_varlen(leaves["q"], leaves["k"], leaves["v"], leaves["a"], leaves["b"],
+                                      leaves.get("w"), cut, leaves["S0"], gates=form)
+    torch.autograd.backward([o, ST], [dO, dST])
+    torch.cuda.synchronize()
+    ref = g.chunk_backward_varlen(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], cut, S0, dO, dST, gates=form)
+    torch.cuda.synchronize()
+    for nm in names + ["S0"]:
+        assert torch.equal(leaves[nm].grad, ref["d" + nm]), nm
