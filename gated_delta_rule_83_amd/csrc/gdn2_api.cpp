@@ -351,7 +351,7 @@ extern "C" {
 
 size_t gdn2_chunk_backward_workspace_bytes(const gdn2_desc *d) {
   if (check_desc(d, false) != GDN2_OK) return 0;
-  return gdn2::backward_workspace_bytes(d->B, (size_t)d->B * d->T, d->H_v, d->d_k, d->d_v);
+  return gdn2::backward_workspace_bytes_split(d->B, d->T, d->H_qk, d->H_v, d->d_k, d->d_v, d->dtype == GDN2_BF16);
 }
 
 size_t gdn2_chunk_backward_varlen_workspace_bytes(const gdn2_desc *d) {
@@ -443,7 +443,9 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
   if (B == 0) return GDN2_OK;
   if (varlen && !cu) return GDN2_ERR_NULL_POINTER;
   const size_t BT = varlen ? T : B * T;  // tokens in all
-  const size_t ws_need = gdn2::backward_workspace_bytes(d->B, BT, d->H_v, d->d_k, d->d_v);
+  const size_t ws_need = varlen ? gdn2::backward_workspace_bytes(d->B, BT, d->H_v, d->d_k, d->d_v)
+                                : gdn2::backward_workspace_bytes_split(d->B, d->T, d->H_qk, d->H_v, d->d_k, d->d_v,
+                                                                        d->dtype == GDN2_BF16);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
   const bool tokens = BT > 0;
   if (tokens && (!q || !k || !v || !a || !b || !dO || !dq || !dk || !dv || !da || !db))

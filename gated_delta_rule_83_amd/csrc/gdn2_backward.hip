@@ -48,6 +48,15 @@ namespace gdn2 {
 
 hipError_t launch_backward_bf16(const BackwardParams &p, int d_k, hipStream_t st);
 
+// Adjoint-only sweep of a split backward (see adjoint_sweep_kernel).
+struct SweepParams {
+  const void *q, *k, *a, *b, *dO;
+  const float *dST;  // [B][H_v][d_k][d_v] or null (zero)
+  float *Lout;       // [B * nseg][H_v][d_k][d_v]: exiting adjoint of segment j of sequence n at n * nseg + j
+  int B, T, H_qk, H_v, d_v, nseg, seg_len;
+};
+hipError_t launch_sweep_bf16(const SweepParams &p, int d_k, int form, hipStream_t st);
+
 namespace {
 
 constexpr int kSub = 4;  // tokens per sub-segment (the register history)
@@ -758,6 +767,239 @@ hipError_t launch_dk(const BackwardParams &p, hipStream_t st) {
   return launch_cb<DK, BF16, kGateGeneral>(p, st);
 }
 
+// ---------------------------------------------------------------- split sequences
+// Few long sequences run as segments in parallel: the packed-sequence
+// backward over the segments, each from its exact entering state and with
+// its exact exiting adjoint. The entering states come from the prefill's
+// split passes; the exiting adjoints from one sequential adjoint-only sweep
+// per sequence. The adjoint of the state does not depend on the state:
+// L_{t-1} = diag(a_t) (I - k_t e_t^T) (L_t + q_t dO_t^T), e = b * k, so the
+// sweep needs no forward states and four operations per state element and
+// token (the full backward needs about twenty).
+
+constexpr int kSweepL = 16;  // tokens per staged block of the sweep
+
+template <int DK, int CB>
+struct SweepSmem {
+  alignas(16) float kqae[2][kSweepL][4][DK];  // k, q, a, e = b*k per token (double-buffered)
+  alignas(16) float dO[2][kSweepL][CB];
+};
+
+// One workgroup per (sequence, value head, CB columns), lanes as in
+// backward_kernel (2 columns x DK/16 keys, key sums over 16-lane rows). From
+// the last token to the first; after each block that starts a segment j > 0
+// the adjoint of the state entering it, i.e. the exiting adjoint of segment
+// j - 1, goes to Lout[n * nseg + j - 1]; Lout[n * nseg + nseg - 1] gets dS_T
+// (or zero).
+template <int DK, int CB, bool BF16, int GF>
+__global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void adjoint_sweep_kernel(SweepParams p) {
+  constexpr bool PRE = GF == kGatePre, CPL = GF == kGateCoupled || GF == kGateScalar, SCA = GF == kGateScalar;
+  using Cf = BwdCfg<DK, CB>;
+  using E = Elem<BF16>;
+  using ET = typename E::T;
+  constexpr int KPL = Cf::KPL, NT = Cf::NT, LS = kSweepL;
+  constexpr int NKQ = LS * DK / 4;  // key quads per block and array
+  constexpr int KIT = (NKQ + NT - 1) / NT;
+  constexpr int NCQ = LS * CB / 4;  // dO quads per block
+  static_assert(NCQ <= NT, "one dO quad per thread at most");
+  __shared__ SweepSmem<DK, CB> sm;
+
+  const int ncb = p.d_v / CB;
+  const int cb = blockIdx.x % ncb, unit = blockIdx.x / ncb;  // unit = n * H_v + h
+  const int n = unit / p.H_v, h = unit - n * p.H_v;
+  const int g = h / (p.H_v / p.H_qk);
+  const int d_v = p.d_v, T = p.T;
+  const size_t tok0 = (size_t)n * T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c4 = lane >> 4, kg = lane & 15;
+  const int lcol = wave * 8 + 2 * c4;  // the lane's first column within the block
+  const int col = cb * CB + lcol;      // ... within the head
+  const int key0 = kg * KPL;
+  using GT = typename std::conditional<PRE, ET, float>::type;
+  const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
+  const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
+  // per-channel gates [token][H_v][DK]; scalar ones [token][H_v]
+  const size_t a_t = (size_t)p.H_v * (SCA ? 1 : DK), b_t = (size_t)p.H_v * (CPL ? 1 : DK);
+  const GT *ah = (const GT *)p.a + tok0 * a_t + (size_t)h * (SCA ? 1 : DK);
+  const GT *bh = (const GT *)p.b + tok0 * b_t + (size_t)h * (CPL ? 1 : DK);
+  const ET *dOh = (const ET *)p.dO + tok0 * p.H_v * d_v + (size_t)h * d_v + cb * CB;
+  const size_t qk_t = (size_t)p.H_qk * DK, vw_t = (size_t)p.H_v * d_v;
+
+  struct Raw {
+    floatx4 k[KIT], q[KIT], a[KIT], e[KIT], d;
+  };
+  // block bi's inputs into registers (tokens past the end are never read)
+  auto request = [&](int bi, Raw &r) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = tid + it * NT;
+      const int tt = idx / (DK / 4), kq = idx % (DK / 4);
+      const int t = bi * LS + tt;
+      const bool ok = idx < NKQ && t < T;
+      floatx4 kv = zero4(), qv = zero4(), av = floatx4{1.f, 1.f, 1.f, 1.f}, bv = zero4();
+      if (ok) {
+        kv = E::ld4(kh + (size_t)t * qk_t + 4 * kq);
+        qv = E::ld4(qh + (size_t)t * qk_t + 4 * kq);
+        if constexpr (SCA) {
+          const float x = ah[(size_t)t * a_t];
+          av = floatx4{x, x, x, x};
+        } else if constexpr (PRE) {
+          const floatx4 x = E::ld4(ah + (size_t)t * a_t + 4 * kq);
+          av = floatx4{decay_from_pre(x[0]), decay_from_pre(x[1]), decay_from_pre(x[2]), decay_from_pre(x[3])};
+        } else {
+          av = *reinterpret_cast<const floatx4 *>(ah + (size_t)t * a_t + 4 * kq);
+        }
+        if constexpr (CPL) {
+          const float x = bh[(size_t)t * b_t];
+          bv = floatx4{x, x, x, x};
+        } else if constexpr (PRE) {
+          const floatx4 x = E::ld4(bh + (size_t)t * b_t + 4 * kq);
+          bv = floatx4{gate_from_pre(x[0]), gate_from_pre(x[1]), gate_from_pre(x[2]), gate_from_pre(x[3])};
+        } else {
+          bv = *reinterpret_cast<const floatx4 *>(bh + (size_t)t * b_t + 4 * kq);
+        }
+      }
+      r.k[it] = kv;
+      r.q[it] = qv;
+      r.a[it] = av;
+      r.e[it] = bv * kv;
+    }
+    const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+    const int t = bi * LS + tt;
+    r.d = (tid < NCQ && t < T) ? E::ld4(dOh + (size_t)t * vw_t + 4 * cq) : zero4();
+  };
+  auto stash = [&](int buf, const Raw &r) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = tid + it * NT;
+      if (idx < NKQ) {
+        const int tt = idx / (DK / 4), kq = idx % (DK / 4);
+        *reinterpret_cast<floatx4 *>(&sm.kqae[buf][tt][0][4 * kq]) = r.k[it];
+        *reinterpret_cast<floatx4 *>(&sm.kqae[buf][tt][1][4 * kq]) = r.q[it];
+        *reinterpret_cast<floatx4 *>(&sm.kqae[buf][tt][2][4 * kq]) = r.a[it];
+        *reinterpret_cast<floatx4 *>(&sm.kqae[buf][tt][3][4 * kq]) = r.e[it];
+      }
+    }
+    if (tid < NCQ) {
+      const int tt = tid / (CB / 4), cq = tid % (CB / 4);
+      *reinterpret_cast<floatx4 *>(&sm.dO[buf][tt][4 * cq]) = r.d;
+    }
+  };
+  auto lds_row = [&](const float *row, float (&x)[KPL]) {
+#pragma unroll
+    for (int e = 0; e < KPL; e += (KPL >= 4 ? 4 : KPL)) {
+      if constexpr (KPL >= 4) {
+        const floatx4 y = *reinterpret_cast<const floatx4 *>(row + key0 + e);
+        x[e] = y[0]; x[e + 1] = y[1]; x[e + 2] = y[2]; x[e + 3] = y[3];
+      } else if constexpr (KPL == 2) {
+        const floatx2 y = *reinterpret_cast<const floatx2 *>(row + key0 + e);
+        x[e] = y[0]; x[e + 1] = y[1];
+      } else {
+        x[e] = row[key0 + e];
+      }
+    }
+  };
+  auto store_L = [&](int j, const float (&L)[KPL][2]) {
+    float *dst = p.Lout + ((size_t)(n * p.nseg + j) * p.H_v + h) * DK * d_v + col;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+      *reinterpret_cast<floatx2 *>(dst + (size_t)(key0 + e) * d_v) = floatx2{L[e][0], L[e][1]};
+  };
+
+  float L[KPL][2];
+#pragma unroll
+  for (int e = 0; e < KPL; ++e) {
+    if (p.dST) {
+      const floatx2 x =
+          *reinterpret_cast<const floatx2 *>(p.dST + ((size_t)unit * DK + key0 + e) * d_v + col);
+      L[e][0] = x[0];
+      L[e][1] = x[1];
+    } else {
+      L[e][0] = L[e][1] = 0.f;
+    }
+  }
+  store_L(p.nseg - 1, L);
+  const int nb = (T + LS - 1) / LS;
+  Raw r;
+  if (nb > 0) {
+    request(nb - 1, r);
+    stash((nb - 1) & 1, r);
+  }
+  __syncthreads();
+  for (int bi = nb - 1; bi >= 0; --bi) {
+    const int buf = bi & 1;
+    if (bi > 0) request(bi - 1, r);  // in flight during this block
+    const int ntok = min(LS, T - bi * LS);
+    // one token: its rows x (k, q, a, e) and dO of the lane's two columns
+    struct Tok {
+      float k[KPL], q[KPL], a[KPL], e[KPL];
+      floatx2 d;
+    };
+    auto read_tok = [&](int tt, Tok &x) {
+      lds_row(sm.kqae[buf][tt][0], x.k);
+      lds_row(sm.kqae[buf][tt][1], x.q);
+      lds_row(sm.kqae[buf][tt][2], x.a);
+      lds_row(sm.kqae[buf][tt][3], x.e);
+      x.d = *reinterpret_cast<const floatx2 *>(&sm.dO[buf][tt][lcol]);
+    };
+    auto step = [&](const Tok &x) __attribute__((always_inline)) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {  // the output read's adjoint, then the key read e^T L
+        L[e][0] = fmaf(x.q[e], x.d[0], L[e][0]);
+        L[e][1] = fmaf(x.q[e], x.d[1], L[e][1]);
+        s0 = fmaf(x.e[e], L[e][0], s0);
+        s1 = fmaf(x.e[e], L[e][1], s1);
+      }
+      row_sum16x2(s0, s1);
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {  // erase along k, then the decay
+        L[e][0] = x.a[e] * fmaf(-x.k[e], s0, L[e][0]);
+        L[e][1] = x.a[e] * fmaf(-x.k[e], s1, L[e][1]);
+      }
+    };
+    for (int tt = ntok - 1; tt >= 0; --tt) {
+      Tok x;
+      read_tok(tt, x);
+      step(x);
+    }
+    if (bi > 0 && (bi * LS) % p.seg_len == 0) store_L(bi * LS / p.seg_len - 1, L);
+    __syncthreads();
+    if (bi > 0) stash(buf ^ 1, r);
+    __syncthreads();
+  }
+}
+
+template <int DK, int CB, bool BF16>
+hipError_t launch_sweep_cb(const SweepParams &p, int form, hipStream_t st) {
+  const dim3 grid(p.B * p.H_v * (p.d_v / CB)), block(BwdCfg<DK, CB>::NT);
+  switch (form) {
+    case kGatePre: hipLaunchKernelGGL((adjoint_sweep_kernel<DK, CB, BF16, kGatePre>), grid, block, 0, st, p); break;
+    case kGateCoupled:
+      hipLaunchKernelGGL((adjoint_sweep_kernel<DK, CB, BF16, kGateCoupled>), grid, block, 0, st, p);
+      break;
+    case kGateScalar:
+      hipLaunchKernelGGL((adjoint_sweep_kernel<DK, CB, BF16, kGateScalar>), grid, block, 0, st, p);
+      break;
+    default: hipLaunchKernelGGL((adjoint_sweep_kernel<DK, CB, BF16, kGateGeneral>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+// Column blocks as in backward_kernel. Measured at 16 heads x 65536 tokens:
+// narrower blocks (waves alone on their SIMDs) and reading each token's rows
+// during the previous token's step were no faster; the time per token is
+// the chain of one token's instructions in each wave.
+template <int DK, bool BF16>
+hipError_t launch_sweep_dk(const SweepParams &p, int form, hipStream_t st) {
+  switch (bwd_cb(p.d_v)) {
+    case 64: return launch_sweep_cb<DK, 64, BF16>(p, form, st);
+    case 32: return launch_sweep_cb<DK, 32, BF16>(p, form, st);
+  }
+  return launch_sweep_cb<DK, 16, BF16>(p, form, st);
+}
+
 }  // namespace
 
 // This translation unit holds the instances of one dtype (GDN2_BWD_BF16).
@@ -778,7 +1020,180 @@ hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st)
 }
 
 #if GDN2_BWD_BF16
+hipError_t launch_sweep_bf16(const SweepParams &p, int d_k, int form, hipStream_t st) {
+  constexpr bool BF16 = true;
+#else
+hipError_t launch_sweep_f32(const SweepParams &p, int d_k, int form, hipStream_t st) {
+  constexpr bool BF16 = false;
+#endif
+  switch (d_k) {
+    case 16: return launch_sweep_dk<16, BF16>(p, form, st);
+    case 32: return launch_sweep_dk<32, BF16>(p, form, st);
+    case 64: return launch_sweep_dk<64, BF16>(p, form, st);
+    case 128: return launch_sweep_dk<128, BF16>(p, form, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+#if GDN2_BWD_BF16
 hipError_t launch_backward_f32(const BackwardParams &p, int d_k, hipStream_t st);
+hipError_t launch_sweep_f32(const SweepParams &p, int d_k, int form, hipStream_t st);
+
+namespace {
+
+// Segment offsets of the split: packed sequence i = n * nseg + j is tokens
+// n * T + j * seg_len .. (clamped to the sequence).
+__global__ __launch_bounds__(256) void split_cu_kernel(int32_t *cu, int B, int T, int nseg, int seg_len) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int ns = B * nseg;
+  if (i > ns) return;
+  const int n = i / nseg, j = i - n * nseg;
+  cu[i] = i == ns ? B * T : n * T + min(j * seg_len, T);
+}
+
+// Entering state of packed sequence (n, j): S0 of sequence n (zero if null)
+// for j = 0, else the state after segment j - 1 (seg_states, [nseg][B][H_v]).
+__global__ __launch_bounds__(256) void split_states_kernel(float *S_in, const float *S0, const float *seg_states,
+                                                            int B, int H_v, int nseg, int dkdv) {
+  const int blk = blockIdx.x;  // (n * nseg + j) * H_v + h
+  const int h = blk % H_v, i = blk / H_v;
+  const int n = i / nseg, j = i - n * nseg;
+  const size_t unit = (size_t)n * H_v + h;
+  const float *src = j == 0 ? (S0 ? S0 + unit * dkdv : nullptr)
+                            : seg_states + ((size_t)(j - 1) * B * H_v + unit) * dkdv;
+  float *dst = S_in + (size_t)blk * dkdv;
+  for (int x = 4 * threadIdx.x; x < dkdv; x += 4 * 256)
+    *reinterpret_cast<floatx4 *>(dst + x) = src ? *reinterpret_cast<const floatx4 *>(src + x) : zero4();
+}
+
+// dS0 of sequence n is that of its first segment.
+__global__ __launch_bounds__(256) void split_ds0_kernel(float *dS0, const float *dS0_seg, int H_v, int nseg,
+                                                         int dkdv) {
+  const int blk = blockIdx.x;  // n * H_v + h
+  const int n = blk / H_v, h = blk - n * H_v;
+  const float *src = dS0_seg + ((size_t)n * nseg * H_v + h) * dkdv;
+  float *dst = dS0 + (size_t)blk * dkdv;
+  for (int x = 4 * threadIdx.x; x < dkdv; x += 4 * 256)
+    *reinterpret_cast<floatx4 *>(dst + x) = *reinterpret_cast<const floatx4 *>(src + x);
+}
+
+struct BwdSplit {
+  int nseg, seg_len;
+};
+
+// Split plan: with fewer than 128 workgroups (sequences x value heads x
+// column blocks) and long sequences, segments of at least 2048 tokens and
+// up to about 512 workgroups in all; the segments are those the prefill's
+// split would use for the same count (whole chunks). GDN2_BACKWARD_SPLIT=<n>,
+// read at each call, asks for n segments (1: never split).
+BwdSplit backward_split_plan(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
+  const BwdSplit none{1, T};
+  if (B <= 0 || T <= 0 || (long)B * T > 0x7fffffffL) return none;
+  const long wg = (long)B * H_v * (d_v / bwd_cb(d_v));
+  long P = 1;
+  if (const char *env = getenv("GDN2_BACKWARD_SPLIT")) {
+    P = atol(env);
+  } else if (wg < 128) {
+    while (wg * P * 2 <= 512 && T / (P * 2) >= 2048) P *= 2;
+  }
+  if (P < 2) return none;
+  PrefillArgs fa{};
+  fa.B = B; fa.T = T; fa.H_qk = H_qk; fa.H_v = H_v; fa.d_k = d_k; fa.d_v = d_v;
+  fa.chunk = 64;
+  fa.bf16 = bf16;
+  fa.nct = prefill_pick_nct(B, H_v, d_v);
+  fa.force_nseg = (int)(P < 65536 ? P : 65536);
+  const PrefillPlan pl = prefill_plan(fa);
+  if (pl.nseg < 2 || pl.seg_len % kSweepL != 0) return none;
+  return BwdSplit{pl.nseg, pl.seg_len};
+}
+
+struct SplitLayout {
+  size_t inner, states, segst, trans, cu, total;
+};
+
+SplitLayout split_layout(int B, int T, int H_v, int d_k, int d_v, const BwdSplit &sp) {
+  SplitLayout l;
+  const size_t ns = (size_t)B * sp.nseg;
+  l.inner = align256(backward_workspace_bytes((int)ns, (size_t)B * T, H_v, d_k, d_v));
+  l.states = align256(ns * H_v * d_k * d_v * 4);  // entering states, exiting adjoints, dS0 per segment
+  l.segst = align256((size_t)sp.nseg * B * H_v * d_k * d_v * 4);
+  l.trans = align256((size_t)sp.nseg * B * H_v * d_k * d_k * 4);
+  l.cu = align256((ns + 1) * 4);
+  l.total = l.inner + 3 * l.states + l.segst + l.trans + l.cu;
+  return l;
+}
+
+hipError_t launch_backward_split(const BackwardArgs &a, const BwdSplit &sp, hipStream_t st) {
+  const SplitLayout l = split_layout(a.B, a.T, a.H_v, a.d_k, a.d_v, sp);
+  const int ns = a.B * sp.nseg;
+  const int dkdv = a.d_k * a.d_v;
+  char *w = static_cast<char *>(a.workspace);
+  void *inner = w;
+  float *S_in = reinterpret_cast<float *>(w + l.inner);
+  float *Lout = reinterpret_cast<float *>(w + l.inner + l.states);
+  float *dS0_seg = reinterpret_cast<float *>(w + l.inner + 2 * l.states);
+  float *segst = reinterpret_cast<float *>(w + l.inner + 3 * l.states);
+  float *trans = reinterpret_cast<float *>(w + l.inner + 3 * l.states + l.segst);
+  int32_t *cu = reinterpret_cast<int32_t *>(w + l.inner + 3 * l.states + l.segst + l.trans);
+  const bool coupled = a.gate_form == kGateCoupled || a.gate_form == kGateScalar;
+
+  hipLaunchKernelGGL(split_cu_kernel, dim3((ns + 256) / 256), dim3(256), 0, st, cu, a.B, a.T, sp.nseg, sp.seg_len);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // entering states: the prefill's split passes
+  PrefillArgs fa{};
+  fa.B = a.B; fa.T = a.T; fa.H_qk = a.H_qk; fa.H_v = a.H_v; fa.d_k = a.d_k; fa.d_v = a.d_v;
+  fa.chunk = 64;
+  fa.bf16 = a.bf16;
+  fa.nct = prefill_pick_nct(a.B, a.H_v, a.d_v);
+  fa.q = a.q; fa.k = a.k; fa.v = a.v;
+  fa.a = a.a; fa.b = a.b; fa.w = coupled ? a.b : a.w;
+  fa.S0 = a.S0;
+  fa.coupled = coupled;
+  fa.scalar_decay = a.gate_form == kGateScalar;
+  fa.preact = a.gate_form == kGatePre;
+  fa.workspace = trans;
+  fa.workspace_bytes = l.trans;
+  fa.force_nseg = sp.nseg;
+  fa.seg_states = segst;
+  if (prefill_plan(fa).nseg != sp.nseg) return hipErrorInvalidValue;
+  e = launch_prefill(fa, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_states_kernel, dim3(ns * a.H_v), dim3(256), 0, st, S_in, a.S0, segst, a.B, a.H_v,
+                     sp.nseg, dkdv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // exiting adjoints: the adjoint-only sweep
+  SweepParams sw{};
+  sw.q = a.q; sw.k = a.k; sw.a = a.a; sw.b = a.b; sw.dO = a.dO; sw.dST = a.dST;
+  sw.Lout = Lout;
+  sw.B = a.B; sw.T = a.T; sw.H_qk = a.H_qk; sw.H_v = a.H_v; sw.d_v = a.d_v;
+  sw.nseg = sp.nseg; sw.seg_len = sp.seg_len;
+  e = a.bf16 ? launch_sweep_bf16(sw, a.d_k, a.gate_form, st) : launch_sweep_f32(sw, a.d_k, a.gate_form, st);
+  if (e != hipSuccess) return e;
+  // the segments as packed sequences
+  BackwardArgs c = a;
+  c.B = ns;
+  c.T = a.B * a.T;
+  c.cu_seqlens = cu;
+  c.S0 = S_in;
+  c.dST = Lout;
+  c.dS0 = a.dS0 ? dS0_seg : nullptr;
+  c.workspace = inner;
+  e = launch_backward(c, st);
+  if (e != hipSuccess || !a.dS0) return e;
+  hipLaunchKernelGGL(split_ds0_kernel, dim3(a.B * a.H_v), dim3(256), 0, st, a.dS0, dS0_seg, a.H_v, sp.nseg, dkdv);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
+  const BwdSplit sp = backward_split_plan(B, T, H_qk, H_v, d_k, d_v, bf16);
+  if (sp.nseg < 2) return backward_workspace_bytes(B, (size_t)B * T, H_v, d_k, d_v);
+  return split_layout(B, T, H_v, d_k, d_v, sp).total;
+}
 
 // Checkpoints: per (head, column block) BT / kSub + B slots of d_k x CB fp32
 // (each sequence needs at most ceil(T_n / kSub) <= T_n / kSub + 1 of them);
@@ -797,6 +1212,10 @@ size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v) {
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
+  if (!a.cu_seqlens) {
+    const BwdSplit sp = backward_split_plan(a.B, a.T, a.H_qk, a.H_v, a.d_k, a.d_v, a.bf16);
+    if (sp.nseg > 1) return launch_backward_split(a, sp, st);
+  }
   BackwardParams p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.a = a.a; p.b = a.b; p.w = a.w; p.S0 = a.S0;
   p.dO = a.dO; p.dST = a.dST;

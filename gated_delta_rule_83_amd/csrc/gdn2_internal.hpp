@@ -45,6 +45,13 @@ struct PrefillArgs {
   // per-channel gates given as pre-activations in the input dtype (a, b, w
   // point to them), activated in the kernel
   bool preact;
+  // split into this many segments (0: the plan's own choice)
+  int force_nseg;
+  // states only (backward of long sequences): run the split's first two
+  // passes and leave in seg_states[s] ([nseg][B][H_v][d_k][d_v]) the exact
+  // state after segment s for s < nseg - 1; no outputs, no S_T; the
+  // workspace holds the transition matrices (nseg * B * H_v * d_k^2 floats)
+  float *seg_states;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one
@@ -101,6 +108,9 @@ struct BackwardParams {
 
 size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v);
 hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
+// Workspace of the backward of B sequences of T tokens: the split plan's
+// when few long sequences run as segments, else backward_workspace_bytes.
+size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16);
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream);

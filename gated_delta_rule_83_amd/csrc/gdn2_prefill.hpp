@@ -538,7 +538,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // consumer lane's column: a value column, or for an identity block the
   // key channel whose unit vector the column starts from
   const int col = (ident ? cb - p.ncb_val : cb) * Cf::DVB + (consumer ? cw : 0) * 16 + lc;
-  const bool write_o = !ident && !(p.o_first_only && rel > 0);
+  const bool write_o = !ident && p.o && !(p.o_first_only && rel > 0);
 
   // Token strides in bytes, and this (sequence, head)'s token-0 bases. GT:
   // the stored type of the per-channel gates.
@@ -1281,7 +1281,9 @@ PrefillPlan plan_t(const PrefillArgs &a) {
   const int nfull = a.T / C;
   if (a.cu_seqlens || DK % DVB != 0 || nfull < 2) return pl;
   long P = 1;
-  if (const char *env = getenv("GDN2_PREFILL_SPLIT")) {
+  if (a.force_nseg > 0) {
+    P = a.force_nseg;
+  } else if (const char *env = getenv("GDN2_PREFILL_SPLIT")) {
     P = atol(env);
   } else if ((long)a.B * a.H_v * ncb < 128) {
     const long per_seg = (long)a.B * a.H_v * (ncb + DK / DVB);
@@ -1349,10 +1351,18 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
     kernel(units * ncb, p);
     return hipGetLastError();
   }
-  if (!a.workspace || a.workspace_bytes < pl.ws_bytes) return hipErrorInvalidValue;
   const size_t sstate = (size_t)units * DK * a.d_v, strans = (size_t)units * DK * DK;
-  float *state = static_cast<float *>(a.workspace);
-  float *trans = state + (size_t)pl.nseg * sstate;
+  float *state, *trans;
+  if (a.seg_states) {  // states only: the caller's state array, transitions in the workspace
+    if (!a.workspace || a.workspace_bytes < (size_t)pl.nseg * strans * sizeof(float)) return hipErrorInvalidValue;
+    state = a.seg_states;
+    trans = static_cast<float *>(a.workspace);
+    p.o = nullptr;
+  } else {
+    if (!a.workspace || a.workspace_bytes < pl.ws_bytes) return hipErrorInvalidValue;
+    state = static_cast<float *>(a.workspace);
+    trans = state + (size_t)pl.nseg * sstate;
+  }
   // 1.
   p.ncb_id = DK / DVB;
   p.S_T = state; p.sT_stride = sstate;
@@ -1363,7 +1373,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   if (e != hipSuccess) return e;
   // 2.
   e = launch_split_combine(state, trans, pl.nseg, units, DK, a.d_v, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.seg_states) return e;
   // 3.
   p.seg_first = 1;
   p.nseg = pl.nseg - 1;

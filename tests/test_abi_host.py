@@ -269,6 +269,28 @@ def test_backward_workspace_query_and_argument_errors():
     assert bwd(d, p, ws, need) == g.GDN2_ERR_ALIAS
 
 
+def test_backward_split_workspace(monkeypatch):
+    """Few long sequences: the backward runs as segments and its workspace
+    query accounts for the split's buffers (more than the unsplit layout);
+    a workspace of the unsplit size is then rejected before any launch."""
+    d = g.make_desc(1, 8192, 2, 4, 128, 128, 64, g.GDN2_BF16)
+    monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
+    plain = g.gdn2_chunk_backward_workspace_bytes(d)
+    monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "4")
+    split = g.gdn2_chunk_backward_workspace_bytes(d)
+    assert split > plain > 0
+    ws = FAKE + 40 * (1 << 30)
+    assert bwd(d, ws=ws, ws_bytes=plain) == g.GDN2_ERR_WORKSPACE
+    monkeypatch.delenv("GDN2_BACKWARD_SPLIT")
+    # the default plan splits this shape (8 workgroups, 8192 tokens) and not the layer shape
+    assert g.gdn2_chunk_backward_workspace_bytes(d) > plain
+    c1 = g.make_desc(8, 4096, 16, 16, 128, 128, 64, g.GDN2_BF16)
+    monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
+    c1_plain = g.gdn2_chunk_backward_workspace_bytes(c1)
+    monkeypatch.delenv("GDN2_BACKWARD_SPLIT")
+    assert g.gdn2_chunk_backward_workspace_bytes(c1) == c1_plain
+
+
 def test_backward_varlen_workspace_and_errors():
     """Packed sequences: the workspace counts desc.T tokens in all; a null
     cu_seqlens and overlaps with it are rejected before any launch."""
