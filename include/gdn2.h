@@ -257,6 +257,13 @@ gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, cons
  *          per token and value head, plus d_k * d_v * 4 per sequence and value
  *          head), 256-byte aligned; NULL only when that size is 0. Contents
  *          on return are unspecified.
+ * With few sequences x value heads and long sequences the backward runs as
+ * segments in parallel: entering states from the prefill's split passes,
+ * exiting adjoints from one adjoint-only sweep, then each segment as a
+ * packed sequence; the workspace query accounts for it, and the
+ * environment variable GDN2_BACKWARD_SPLIT=<n>, read at each call, forces n
+ * segments (1: never split). Gradients that depend on the forward states
+ * then carry the prefill's rounding (within the stated tolerances).
  * Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums; all
  * arithmetic is fp32. The result is deterministic (no atomics).
  * Errors: as for gdn2_chunk_forward; a missing required pointer is
