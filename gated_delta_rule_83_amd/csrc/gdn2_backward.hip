@@ -145,6 +145,19 @@ __device__ __forceinline__ void row_sum16x2(float &x0, float &x1) {
       "v_add_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf"
       : "+v"(x0), "+v"(x1));
 }
+// One value: the same rotations, two wait states before each (s_nop 1).
+__device__ __forceinline__ void row_sum16x1(float &x) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(x));
+}
 
 // Lane exchange of the column reduce-scatter (gfx950 v_permlane32_swap /
 // v_permlane16_swap), N pairs at once: after swap32(A, B), A holds
@@ -785,19 +798,23 @@ struct SweepSmem {
   alignas(16) float dO[2][kSweepL][CB];
 };
 
-// One workgroup per (sequence, value head, CB columns), lanes as in
-// backward_kernel (2 columns x DK/16 keys, key sums over 16-lane rows). From
+// One workgroup per (sequence, value head, CB columns), a lane holds one
+// column x DK/16 keys (key sums over 16-lane rows: four columns per wave,
+// half the instructions per token of backward_kernel's two). From
 // the last token to the first; after each block that starts a segment j > 0
 // the adjoint of the state entering it, i.e. the exiting adjoint of segment
 // j - 1, goes to Lout[n * nseg + j - 1]; Lout[n * nseg + nseg - 1] gets dS_T
 // (or zero).
+template <int CB>
+constexpr int sweep_threads() { return 16 * CB; }  // CB / 4 waves
+
 template <int DK, int CB, bool BF16, int GF>
-__global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void adjoint_sweep_kernel(SweepParams p) {
+__global__ __launch_bounds__(sweep_threads<CB>()) void adjoint_sweep_kernel(SweepParams p) {
   constexpr bool PRE = GF == kGatePre, CPL = GF == kGateCoupled || GF == kGateScalar, SCA = GF == kGateScalar;
-  using Cf = BwdCfg<DK, CB>;
   using E = Elem<BF16>;
   using ET = typename E::T;
-  constexpr int KPL = Cf::KPL, NT = Cf::NT, LS = kSweepL;
+  constexpr int KPL = DK / 16, NT = sweep_threads<CB>(), LS = kSweepL;
+  static_assert(CB % 4 == 0 && CB <= 64, "four columns per wave");
   constexpr int NKQ = LS * DK / 4;  // key quads per block and array
   constexpr int KIT = (NKQ + NT - 1) / NT;
   constexpr int NCQ = LS * CB / 4;  // dO quads per block
@@ -813,9 +830,11 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void adjoint_sweep_kernel(Swe
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c4 = lane >> 4, kg = lane & 15;
-  const int lcol = wave * 8 + 2 * c4;  // the lane's first column within the block
-  const int col = cb * CB + lcol;      // ... within the head
-  const int key0 = kg * KPL;
+  const int lcol = wave * 4 + c4;  // the lane's column within the block
+  const int col = cb * CB + lcol;  // ... within the head
+  // the lane's keys: quads 4kg .. 4kg+3 of every 64 keys (a row read of 16
+  // lanes then covers 64 banks once), or 2kg, 2kg+1 / kg for DK < 64
+  auto key = [&](int e) { return KPL >= 4 ? (e >> 2) * 64 + 4 * kg + (e & 3) : kg * KPL + e; };
   using GT = typename std::conditional<PRE, ET, float>::type;
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
@@ -890,35 +909,25 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void adjoint_sweep_kernel(Swe
 #pragma unroll
     for (int e = 0; e < KPL; e += (KPL >= 4 ? 4 : KPL)) {
       if constexpr (KPL >= 4) {
-        const floatx4 y = *reinterpret_cast<const floatx4 *>(row + key0 + e);
+        const floatx4 y = *reinterpret_cast<const floatx4 *>(row + key(e));
         x[e] = y[0]; x[e + 1] = y[1]; x[e + 2] = y[2]; x[e + 3] = y[3];
       } else if constexpr (KPL == 2) {
-        const floatx2 y = *reinterpret_cast<const floatx2 *>(row + key0 + e);
+        const floatx2 y = *reinterpret_cast<const floatx2 *>(row + key(e));
         x[e] = y[0]; x[e + 1] = y[1];
       } else {
-        x[e] = row[key0 + e];
+        x[e] = row[key(e)];
       }
     }
   };
-  auto store_L = [&](int j, const float (&L)[KPL][2]) {
+  auto store_L = [&](int j, const float (&L)[KPL]) {
     float *dst = p.Lout + ((size_t)(n * p.nseg + j) * p.H_v + h) * DK * d_v + col;
 #pragma unroll
-    for (int e = 0; e < KPL; ++e)
-      *reinterpret_cast<floatx2 *>(dst + (size_t)(key0 + e) * d_v) = floatx2{L[e][0], L[e][1]};
+    for (int e = 0; e < KPL; ++e) dst[(size_t)key(e) * d_v] = L[e];
   };
 
-  float L[KPL][2];
+  float L[KPL];
 #pragma unroll
-  for (int e = 0; e < KPL; ++e) {
-    if (p.dST) {
-      const floatx2 x =
-          *reinterpret_cast<const floatx2 *>(p.dST + ((size_t)unit * DK + key0 + e) * d_v + col);
-      L[e][0] = x[0];
-      L[e][1] = x[1];
-    } else {
-      L[e][0] = L[e][1] = 0.f;
-    }
-  }
+  for (int e = 0; e < KPL; ++e) L[e] = p.dST ? p.dST[((size_t)unit * DK + key(e)) * d_v + col] : 0.f;
   store_L(p.nseg - 1, L);
   const int nb = (T + LS - 1) / LS;
   Raw r;
@@ -931,39 +940,49 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void adjoint_sweep_kernel(Swe
     const int buf = bi & 1;
     if (bi > 0) request(bi - 1, r);  // in flight during this block
     const int ntok = min(LS, T - bi * LS);
-    // one token: its rows x (k, q, a, e) and dO of the lane's two columns
+    // one token: its rows x (k, q, a, e) and dO of the lane's column
     struct Tok {
       float k[KPL], q[KPL], a[KPL], e[KPL];
-      floatx2 d;
+      float d;
     };
     auto read_tok = [&](int tt, Tok &x) {
       lds_row(sm.kqae[buf][tt][0], x.k);
       lds_row(sm.kqae[buf][tt][1], x.q);
       lds_row(sm.kqae[buf][tt][2], x.a);
       lds_row(sm.kqae[buf][tt][3], x.e);
-      x.d = *reinterpret_cast<const floatx2 *>(&sm.dO[buf][tt][lcol]);
+      x.d = sm.dO[buf][tt][lcol];
     };
     auto step = [&](const Tok &x) __attribute__((always_inline)) {
+      // the output read's adjoint, then the key read e^T L (two partial
+      // sums: a shorter dependent chain)
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) {  // the output read's adjoint, then the key read e^T L
-        L[e][0] = fmaf(x.q[e], x.d[0], L[e][0]);
-        L[e][1] = fmaf(x.q[e], x.d[1], L[e][1]);
-        s0 = fmaf(x.e[e], L[e][0], s0);
-        s1 = fmaf(x.e[e], L[e][1], s1);
+      for (int e = 0; e < KPL; ++e) {
+        L[e] = fmaf(x.q[e], x.d, L[e]);
+        if (e & 1)
+          s1 = fmaf(x.e[e], L[e], s1);
+        else
+          s0 = fmaf(x.e[e], L[e], s0);
       }
-      row_sum16x2(s0, s1);
+      float s = s0 + s1;
+      row_sum16x1(s);
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) {  // erase along k, then the decay
-        L[e][0] = x.a[e] * fmaf(-x.k[e], s0, L[e][0]);
-        L[e][1] = x.a[e] * fmaf(-x.k[e], s1, L[e][1]);
-      }
+      for (int e = 0; e < KPL; ++e) L[e] = x.a[e] * fmaf(-x.k[e], s, L[e]);  // erase along k, then the decay
     };
-    for (int tt = ntok - 1; tt >= 0; --tt) {
-      Tok x;
-      read_tok(tt, x);
-      step(x);
+    // each token's rows are read while the token after it (in time) computes,
+    // into two register sets in turn; the reads are unconditional (the last
+    // one repeats token 0) so that the wait before a step covers only the
+    // reads issued before it
+    Tok xa, xb;
+    read_tok(ntok - 1, xa);
+    int tt = ntok - 1;
+    for (; tt >= 1; tt -= 2) {
+      read_tok(tt - 1, xb);
+      step(xa);
+      read_tok(max(tt - 2, 0), xa);
+      step(xb);
     }
+    if (tt == 0) step(xa);
     if (bi > 0 && (bi * LS) % p.seg_len == 0) store_L(bi * LS / p.seg_len - 1, L);
     __syncthreads();
     if (bi > 0) stash(buf ^ 1, r);
@@ -973,7 +992,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void adjoint_sweep_kernel(Swe
 
 template <int DK, int CB, bool BF16>
 hipError_t launch_sweep_cb(const SweepParams &p, int form, hipStream_t st) {
-  const dim3 grid(p.B * p.H_v * (p.d_v / CB)), block(BwdCfg<DK, CB>::NT);
+  const dim3 grid(p.B * p.H_v * (p.d_v / CB)), block(sweep_threads<CB>());
   switch (form) {
     case kGatePre: hipLaunchKernelGGL((adjoint_sweep_kernel<DK, CB, BF16, kGatePre>), grid, block, 0, st, p); break;
     case kGateCoupled:
@@ -987,16 +1006,12 @@ hipError_t launch_sweep_cb(const SweepParams &p, int form, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Column blocks as in backward_kernel. Measured at 16 heads x 65536 tokens:
-// narrower blocks (waves alone on their SIMDs) and reading each token's rows
-// during the previous token's step were no faster; the time per token is
-// the chain of one token's instructions in each wave.
+// 16-column workgroups (4 waves). Every wave reads each token's rows from
+// LDS, so a CU's LDS bandwidth bounds a token's step: fewer waves per CU
+// (16 columns) measured faster than 32 or 64, and fewer still (8, 4) slower
+// again (each workgroup stages every token's rows).
 template <int DK, bool BF16>
 hipError_t launch_sweep_dk(const SweepParams &p, int form, hipStream_t st) {
-  switch (bwd_cb(p.d_v)) {
-    case 64: return launch_sweep_cb<DK, 64, BF16>(p, form, st);
-    case 32: return launch_sweep_cb<DK, 32, BF16>(p, form, st);
-  }
   return launch_sweep_cb<DK, 16, BF16>(p, form, st);
 }
 
