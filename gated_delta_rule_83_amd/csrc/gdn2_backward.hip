@@ -258,7 +258,11 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   const int c4 = lane >> 4, kg = lane & 15;
   const int lcol = wave * 8 + 2 * c4;  // the lane's first column within the block
   const int col = cb * CB + lcol;      // ... within the head
-  const int key0 = kg * KPL;
+  // the lane's key channels: quads 4kg .. 4kg+3 of every 64 keys, so that a
+  // row read or write of 16 lanes covers the 64 banks once (contiguous
+  // 32-byte pieces per lane would put lanes kg and kg+8 on the same banks);
+  // kg*KPL .. for KPL < 4
+  auto key = [&](int e) { return KPL >= 4 ? (e >> 2) * 64 + 4 * kg + (e & 3) : kg * KPL + e; };
 
   const ET *qh = (const ET *)p.q + tok0 * p.H_qk * DK + (size_t)g * DK;
   const ET *kh = (const ET *)p.k + tok0 * p.H_qk * DK + (size_t)g * DK;
@@ -366,18 +370,18 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       *reinterpret_cast<floatx4 *>(&sm.b.col[tt][4][4 * cq]) = st.r;
     }
   };
-  // x[e] = row[key0 + e]: the lane's key channels of one staged row
+  // x[e] = row[key(e)]: the lane's key channels of one staged row
   auto lds_row = [&](const float *row, float (&x)[KPL]) {
 #pragma unroll
     for (int e = 0; e < KPL; e += (KPL >= 4 ? 4 : KPL)) {
       if constexpr (KPL >= 4) {
-        const floatx4 y = *reinterpret_cast<const floatx4 *>(row + key0 + e);
+        const floatx4 y = *reinterpret_cast<const floatx4 *>(row + key(e));
         x[e] = y[0]; x[e + 1] = y[1]; x[e + 2] = y[2]; x[e + 3] = y[3];
       } else if constexpr (KPL == 2) {
-        const floatx2 y = *reinterpret_cast<const floatx2 *>(row + key0 + e);
+        const floatx2 y = *reinterpret_cast<const floatx2 *>(row + key(e));
         x[e] = y[0]; x[e + 1] = y[1];
       } else {
-        x[e] = row[key0 + e];
+        x[e] = row[key(e)];
       }
     }
   };
@@ -456,7 +460,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
 #pragma unroll
   for (int e = 0; e < KPL; ++e) {
     if (p.S0) {
-      const floatx2 x = *reinterpret_cast<const floatx2 *>(p.S0 + s_off + (size_t)(key0 + e) * d_v + col);
+      const floatx2 x = *reinterpret_cast<const floatx2 *>(p.S0 + s_off + (size_t)key(e) * d_v + col);
       s[e][0] = x[0];
       s[e][1] = x[1];
     } else {
@@ -499,7 +503,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
 #pragma unroll
   for (int e = 0; e < KPL; ++e) {
     if (p.dST) {
-      const floatx2 x = *reinterpret_cast<const floatx2 *>(p.dST + s_off + (size_t)(key0 + e) * d_v + col);
+      const floatx2 x = *reinterpret_cast<const floatx2 *>(p.dST + s_off + (size_t)key(e) * d_v + col);
       lam[e][0] = x[0];
       lam[e][1] = x[1];
     } else {
@@ -606,15 +610,15 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
       swap_sum_n<32, KPL>(x[0], x[2]);
       swap_sum_n<32, KPL>(x[1], x[3]);
       swap_sum_n<16, KPL>(x[0], x[1]);
-      // x[0] now holds the lane group's vector c4 on keys key0 .. key0 + KPL - 1
-      float *dst = &sm.b.red[wave][tt][c4][key0];
+      // x[0] now holds the lane group's vector c4 on the lane's keys
+      float *dst = &sm.b.red[wave][tt][c4][0];
       if constexpr (KPL >= 4) {
 #pragma unroll
         for (int e = 0; e < KPL; e += 4)
-          *reinterpret_cast<floatx4 *>(dst + e) = floatx4{x[0][e], x[0][e + 1], x[0][e + 2], x[0][e + 3]};
+          *reinterpret_cast<floatx4 *>(dst + key(e)) = floatx4{x[0][e], x[0][e + 1], x[0][e + 2], x[0][e + 3]};
       } else {
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) dst[e] = x[0][e];
+        for (int e = 0; e < KPL; ++e) dst[key(e)] = x[0][e];
       }
       if (kg == 0) {
         sm.b.du[tt][lcol] = du0;
@@ -667,7 +671,7 @@ __global__ __launch_bounds__((BwdCfg<DK, CB>::NT)) void backward_kernel(Backward
   if (p.dS0) {
 #pragma unroll
     for (int e = 0; e < KPL; ++e)
-      *reinterpret_cast<floatx2 *>(p.dS0 + s_off + (size_t)(key0 + e) * d_v + col) = floatx2{lam[e][0], lam[e][1]};
+      *reinterpret_cast<floatx2 *>(p.dS0 + s_off + (size_t)key(e) * d_v + col) = floatx2{lam[e][0], lam[e][1]};
   }
 }
 
