@@ -386,14 +386,29 @@ def test_split_backward_matches_unsplit(form, dt, dk, dv, monkeypatch):
     every gradient equals the unsplit backward's within tolerance, for every
     gate form, with a ragged last segment, grouped heads, S0 and dS_T; the
     fp32 per-channel case also against the oracle."""
-    from tests.gate_forms import backward_alone, form_inputs, oracle_backward
     rng = np.random.default_rng(4700 + dk + dv + len(form))
     B, T, Hv = 1, 2000, 2
+    _split_case(rng, form, dt, dk, dv, B, T, Hv, True, monkeypatch)
+
+
+@pytest.mark.parametrize("form,dt,with_state", [("channel", "f32", True), ("scalar", "bf16", False)])
+def test_split_backward_several_sequences(form, dt, with_state, monkeypatch):
+    """The split with two sequences (segment offsets, entering states and
+    exiting adjoints per sequence, each sequence's dS0 from its first
+    segment), with and without S0 and dS_T, against the unsplit backward."""
+    rng = np.random.default_rng(4800 + with_state)
+    _split_case(rng, form, dt, 128, 64, 2, 1500, 2, with_state, monkeypatch)
+
+
+def _split_case(rng, form, dt, dk, dv, B, T, Hv, with_state, monkeypatch):
+    from tests.gate_forms import backward_alone, form_inputs, oracle_backward
     x = form_inputs(rng, form, T, Hv, dk, dv, dt, DEV, B=B)
     tdt = x["q"].dtype
     S0 = torch.from_numpy((rng.standard_normal((B, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
     dO = torch.from_numpy(rng.standard_normal((B, T, Hv, dv)).astype(np.float32)).to(tdt).to(DEV)
     dST = torch.from_numpy(rng.standard_normal((B, Hv, dk, dv)).astype(np.float32)).to(DEV)
+    if not with_state:
+        S0 = dST = None
     desc = g.make_desc(B, T, 1, Hv, dk, dv, 64, g.GDN2_BF16 if dt == "bf16" else g.GDN2_F32)
     monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
     ws1 = g.gdn2_chunk_backward_workspace_bytes(desc)
