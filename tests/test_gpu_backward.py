@@ -430,3 +430,28 @@ def _split_case(rng, form, dt, dk, dv, B, T, Hv, with_state, monkeypatch):
         oerr = {nm: normwise(to_np(got[nm]), oref[nm]) for nm in names}
         print("  vs oracle " + " ".join(f"{k} {v:.2e}" for k, v in oerr.items()), flush=True)
         assert all(v <= TOL[dt] for v in oerr.values()), oerr
+
+
+def test_split_backward_long_context_full_size(monkeypatch):
+    """B1 T65536 H16 d128 bf16 with 1% hard erases (the long-context workload's
+    shape): the default plan's split backward (8 segments) against the
+    unsplit backward of the same inputs, every gradient within tolerance."""
+    monkeypatch.delenv("GDN2_BACKWARD_SPLIT", raising=False)
+    c = gi.config(2)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(4900)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    desc = g.make_desc(c.B, c.T, c.H_qk, c.H_v, c.d_k, c.d_v, 64, g.GDN2_BF16)
+    ws_split = g.gdn2_chunk_backward_workspace_bytes(desc)
+    got = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu() for k, v in got.items()}
+    monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
+    assert g.gdn2_chunk_backward_workspace_bytes(desc) < ws_split  # the default plan did split
+    ref = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    errs = {nm: normwise(got[nm].numpy(), to_np(ref[nm])) for nm in NAMES}
+    print("[split backward long context] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, bad
