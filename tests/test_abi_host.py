@@ -284,6 +284,12 @@ def test_backward_split_workspace(monkeypatch):
     monkeypatch.delenv("GDN2_BACKWARD_SPLIT")
     # the default plan splits this shape (8 workgroups, 8192 tokens) and not the layer shape
     assert g.gdn2_chunk_backward_workspace_bytes(d) > plain
+    # the prefill cannot split d_k = 16 with 32-column workgroups: no split, the plain layout
+    small = g.make_desc(1, 8192, 1, 2, 16, 32, 64, g.GDN2_BF16)
+    monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "4")
+    forced = g.gdn2_chunk_backward_workspace_bytes(small)
+    monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
+    assert forced == g.gdn2_chunk_backward_workspace_bytes(small)
     c1 = g.make_desc(8, 4096, 16, 16, 128, 128, 64, g.GDN2_BF16)
     monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
     c1_plain = g.gdn2_chunk_backward_workspace_bytes(c1)

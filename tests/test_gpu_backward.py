@@ -378,7 +378,8 @@ def test_varlen_autograd_wrapper(form):
 
 @pytest.mark.parametrize("form,dt,dk,dv", [("channel", "f32", 64, 64), ("channel", "bf16", 128, 128),
                                            ("preact", "bf16", 128, 128), ("coupled", "f32", 128, 64),
-                                           ("scalar", "bf16", 128, 128), ("channel", "f32", 128, 16)])
+                                           ("scalar", "bf16", 128, 128), ("channel", "f32", 128, 16),
+                                           ("channel", "f32", 16, 16), ("coupled", "bf16", 32, 16)])
 def test_split_backward_matches_unsplit(form, dt, dk, dv, monkeypatch):
     """Long sequences with few heads run as segments (entering states from the
     prefill's split passes, exiting adjoints from the adjoint-only sweep, then
