@@ -456,3 +456,25 @@ def test_split_backward_long_context_full_size(monkeypatch):
     print("[split backward long context] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("form", ["preact", "coupled", "scalar"])
+def test_varlen_gate_forms_all_empty(form):
+    """Packed batches of empty sequences in every gate form: the forward keeps
+    each state (S_T = S0) and the backward passes the state gradient through
+    (dS0 = dS_T), with no token tensors to touch."""
+    from tests.gate_forms import form_inputs
+    rng = np.random.default_rng(5000 + len(form))
+    N, Hv, dk, dv = 3, 2, 64, 64
+    x = form_inputs(rng, form, 0, Hv, dk, dv, "bf16", DEV)
+    S0 = torch.from_numpy(rng.standard_normal((N, Hv, dk, dv)).astype(np.float32)).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((N, Hv, dk, dv)).astype(np.float32)).to(DEV)
+    cut = torch.zeros(N + 1, dtype=torch.int32, device=DEV)
+    sq = lambda t: None if t is None else t[0]
+    o, ST = g.chunk_forward_varlen(sq(x["q"]), sq(x["k"]), sq(x["v"]), sq(x["a"]), sq(x["b"]), sq(x["w"]), cut, S0,
+                                   gates=form)
+    dO = torch.zeros((1, 0, Hv, dv), dtype=torch.bfloat16, device=DEV)
+    gv = g.chunk_backward_varlen(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], cut, S0, dO, dST, gates=form)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and torch.equal(ST, S0)
+    assert torch.equal(gv["dS0"], dST)
