@@ -137,6 +137,10 @@ def main():
                     help="timed launches of the prefill with gate pre-activations (0: skip)")
     ap.add_argument("--backward-steps", type=int, default=5,
                     help="timed launches of the backward pass over the prefill shape (0: skip)")
+    ap.add_argument("--long-backward", type=int, default=0,
+                    help="also time this many launches of the backward of the long-context shape "
+                         "(B1 T65536 H16 d128 bf16, split into segments), reported under backward_long "
+                         "(default 0: off)")
     ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
     ap.add_argument("--counters", action="store_true",
                     help="for hardware-counter runs: launch the prefill and the decode kernel twice each "
@@ -319,6 +323,40 @@ def main():
             f"{bfl / b_avg / 1e12:.1f} TFLOP/s algorithmic")
         del grads, bws
 
+    # ---------------------------------------------------------------- long-context backward (optional)
+    bwd_long = None
+    if args.long_backward > 0:
+        cl = gi.config(2)
+        tl = gi.to_torch(gi.make_inputs(cl), "bf16", dev)
+        gen = torch.Generator(device=dev).manual_seed(6)
+        dOl = torch.randn(tl["v"].shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        dSTl = torch.randn((cl.B, cl.H_v, cl.d_k, cl.d_v), generator=gen, device=dev, dtype=torch.float32)
+        descl = g.make_desc(cl.B, cl.T, cl.H_qk, cl.H_v, cl.d_k, cl.d_v, cl.chunk, g.GDN2_BF16)
+        wsl = torch.empty(g.gdn2_chunk_backward_workspace_bytes(descl), dtype=torch.uint8, device=dev)
+
+        def backward_long(grads=None):
+            return g.chunk_backward(tl["q"], tl["k"], tl["v"], tl["a"], tl["b"], tl["w"], None, dOl, dSTl,
+                                    grads=grads, workspace=wsl, stream=stream)
+
+        gl = backward_long()
+        torch.cuda.synchronize()
+        lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.long_backward)]
+        for e0, e1 in lev:
+            e0.record(stream)
+            backward_long(gl)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        l_ms = [a.elapsed_time(b) for a, b in lev]
+        l_avg = float(np.mean(l_ms)) / 1e3
+        lfl, _ = backward_algorithmic(cl)
+        bwd_long = {"workload": "backward B1 T65536 H16 d128 bf16 (split into segments)",
+                    "launches": args.long_backward, "ms": l_avg * 1e3, "min_ms": min(l_ms),
+                    "tokens_per_s": cl.B * cl.T / l_avg, "achieved": lfl / l_avg / 1e12,
+                    "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s", "workspace_bytes": wsl.numel()}
+        log(f"[bench] long-context backward: {l_avg * 1e3:.2f} ms per launch (min {min(l_ms):.2f})")
+        del gl, wsl, tl
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -379,6 +417,7 @@ def main():
         },
         "preact": pre_leg,
         "backward": bwd,
+        **({"backward_long": bwd_long} if bwd_long else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
