@@ -802,9 +802,10 @@ struct SweepSmem {
   alignas(16) float dO[2][kSweepL][CB];
 };
 
-// One workgroup per (sequence, value head, CB columns), a lane holds one
-// column x DK/16 keys (key sums over 16-lane rows: four columns per wave,
-// half the instructions per token of backward_kernel's two). From
+// One workgroup per (sequence, value head, CB columns); a lane holds one
+// column x DK/16 keys (backward_kernel's lanes hold two columns: one halves
+// the instructions per token and wave), key sums over 16-lane rows, four
+// columns per wave, keys interleaved as in backward_kernel. From
 // the last token to the first; after each block that starts a segment j > 0
 // the adjoint of the state entering it, i.e. the exiting adjoint of segment
 // j - 1, goes to Lout[n * nseg + j - 1]; Lout[n * nseg + nseg - 1] gets dS_T
