@@ -5,18 +5,29 @@
 
 One step is one pass of the whole hot path over one batch of synthetic
 input: a prefill (gdn2_chunk_forward) over the 1.3B-class layer shape
-(B=8, T=4096, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates and state)
-followed by one decode step (gdn2_decode_step) over the batched-decode shape
-(256 sequences x 16 heads, fp32 128x128 state). Inputs are resident in HBM
-before the timed region. Per-kernel durations come from HIP events recorded
-on the stream the kernels are launched on.
+(B=8, T=4096, H=16, d_k=d_v=128, bf16 q/k/v, fp32 gates and state; the
+workload allows chunks of 64 tokens, the kernel runs the longest that fits,
+reported as chunk_run) followed by one decode step (gdn2_decode_step) over
+the batched-decode shape (256 sequences x 16 heads, fp32 128x128 state).
+Inputs are resident in HBM before any timed region. Kernel durations come
+from HIP events recorded on the stream the kernels are launched on.
 
-After the timed steps, the decode workload as stated (1024 successive decode
-steps from a random state) runs once for the decode bandwidth figure, the
-prefill with the gates as bf16 pre-activations (gdn2_chunk_forward_preact)
-and the backward pass (gdn2_chunk_backward) of the prefill run a few times
-for their own figures, and the fp64 oracle runs on the host over the prefill batch for
-the CPU baseline.
+Legs, in the order they run (each its own figure in the JSON line):
+  series    a cold-start series of prefill launches of the layer shape: the
+            first launches against the settled ones (the GPU's clocks ramp
+            up under load; the JSON reports both);
+  headline  W warm-up steps, then K timed steps (prefill + decode step):
+            `value`, `roofline`, `ms_per_step`;
+  configs   the other prefill workloads: long context (B1 T65536 H16) and
+            grouped heads (B4 T16384 H_qk16 H_v32), each with its roofline;
+  strong_decay  the layer shape with decay pre-activations N(+2, 1)
+            (per-token decay ~0.12): the anchoring's range check at work;
+  decode    the decode workload as stated (1024 successive steps from a
+            random state), plus states of 1 GiB and 4 GiB (beyond the
+            256 MiB Infinity Cache) for the bandwidth attribution;
+  preact, backward   the fused gate activation and the backward pass;
+  cpu_baseline   the fp64 oracle on the host cores over the layer batch, and
+            on one (sequence, head) with one thread.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -24,9 +35,10 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import re
 import json
 import os
+import platform
+import re
 import sys
 import time
 
@@ -38,46 +50,38 @@ MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector ALUs, TFLOP/s
 PREFILL_KERNEL_SOURCES = ["gated_delta_rule_83_amd/csrc/gdn2_prefill.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_device.hpp",
+                          "gated_delta_rule_83_amd/csrc/gdn2_range.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_prefill_inst.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_B8_T4096_H16_d128_bf16_hbm_traffic.txt")
+METRIC = "prefill tokens/s (T=4096,H=16,d=128) + decode HBM GB/s, % of roofline"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill_algorithmic(c):
+def prefill_algorithmic(c, chunk_run, gate_bytes=4):
     """Bytes and flops the method itself must move / compute for one prefill call.
 
-    Bytes: q, k (H_qk heads) and v, o in the input dtype; a, b, w in fp32; the
-    final state S_T in fp32 (S0 is null). Flops per (token, value head):
+    Bytes: q, k (H_qk heads) and v, o in the input dtype; a, b, w at
+    `gate_bytes` each (fp32 activated gates: 4); the final state S_T in fp32
+    (S0 is null). Flops per (token, value head) at the chunk C that runs:
     4*C*d_k (four Gram triangles) + 4*C*d_v (Akk U, T Z, Mqk U, Mqb R) +
     8*d_k*d_v (gamma*K S0, gamma*Q S0, two carry products) + C^2/3 (solve)
     + d_k*d_v/C (carry scaling)."""
     es = 2 if c.dtype == "bf16" else 4
     toks = c.B * c.T
-    by = toks * (c.H_qk * c.d_k * es * 2 + c.H_v * c.d_v * es * 2 + c.H_v * c.d_k * 4 * 2
-                 + c.H_v * c.d_v * 4) + c.B * c.H_v * c.d_k * c.d_v * 4
-    C = c.chunk
+    by = toks * (c.H_qk * c.d_k * es * 2 + c.H_v * c.d_v * es * 2 + c.H_v * c.d_k * gate_bytes * 2
+                 + c.H_v * c.d_v * gate_bytes) + c.B * c.H_v * c.d_k * c.d_v * 4
+    C = chunk_run
     fl_th = 4 * C * c.d_k + 4 * C * c.d_v + 8 * c.d_k * c.d_v + C * C / 3 + c.d_k * c.d_v / C
     return by, fl_th * toks * c.H_v
 
 
-def decode_algorithmic(c):
+def decode_algorithmic(N, H_qk, H_v, d_k, d_v, es=2):
     """Bytes per decode step: state read + write, q, k, v, o, a, b, w."""
-    es = 2 if c.dtype == "bf16" else 4
-    per_head = c.d_k * c.d_v * 4 * 2 + c.d_v * es * 2 + c.d_k * 4 * 2 + c.d_v * 4
-    qk = c.B * c.H_qk * c.d_k * es * 2
-    return c.B * c.H_v * per_head + qk
-
-
-def preact_algorithmic(c):
-    """Bytes of one prefill launch with the gates as pre-activations in the
-    input dtype (a, b, w at es bytes instead of 4)."""
-    es = 2 if c.dtype == "bf16" else 4
-    toks = c.B * c.T
-    return (toks * (c.H_qk * c.d_k * es * 2 + c.H_v * c.d_v * es * 2 + c.H_v * c.d_k * es * 2
-                    + c.H_v * c.d_v * es) + c.B * c.H_v * c.d_k * c.d_v * 4)
+    per_head = d_k * d_v * 4 * 2 + d_v * es * 2 + d_k * 4 * 2 + d_v * 4
+    return N * H_v * per_head + N * H_qk * d_k * es * 2
 
 
 def backward_algorithmic(c):
@@ -108,12 +112,12 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(digest):
-    """HBM bytes per prefill launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
+def read_traffic(path, digest):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -125,11 +129,26 @@ def read_traffic(digest):
         return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--series", type=int, default=300,
+                    help="cold-start prefill launches timed one by one before the headline (0: skip)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed launches of each other prefill workload (0: skip those legs)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="length of the decode workload leg (default: the workload's 1024)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,9 +161,10 @@ def main():
                          "(B1 T65536 H16 d128 bf16, split into segments), reported under backward_long "
                          "(default 0: off)")
     ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
-    ap.add_argument("--counters", action="store_true",
-                    help="for hardware-counter runs: launch the prefill and the decode kernel twice each "
-                         "and a plain 256 MiB device copy twice (counter calibration), then exit")
+    ap.add_argument("--counters", type=int, default=None, metavar="CONFIG",
+                    help="for hardware-counter runs: launch the prefill of workload CONFIG (1, 2 or 3) "
+                         "twice, the decode step twice (with CONFIG 1) and a plain 256 MiB device copy twice "
+                         "(counter calibration), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -163,6 +183,23 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
+    def plan(c):
+        st, crun, nseg = g.gdn2_chunk_forward_plan(
+            g.make_desc(c.B, c.T, c.H_qk, c.H_v, c.d_k, c.d_v, c.chunk, g.GDN2_BF16 if c.dtype == "bf16" else g.GDN2_F32))
+        if st != g.GDN2_OK:
+            raise RuntimeError(f"plan failed for {c.name}: {g.gdn2_status_string(st)}")
+        return crun, nseg
+
+    def time_each(fn, n):
+        """Per-launch milliseconds of n calls of fn, HIP events on `stream`."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
     cp = gi.config(1)
     if args.chunk:
         cp = cp.replace(chunk=args.chunk)
@@ -175,39 +212,75 @@ def main():
     tp = gi.to_torch(dp, cp.dtype, dev)
     o = torch.empty((cp.B, cp.T, cp.H_v, cp.d_v), dtype=tp["q"].dtype, device=dev)
     S_T = torch.empty((cp.B, cp.H_v, cp.d_k, cp.d_v), dtype=torch.float32, device=dev)
-    log(f"[bench] drawing {dec_steps} decode steps {cd.name} ({time.time() - t0:.1f}s so far)")
+    n_dec_inputs = dec_steps if args.counters is None else 2
+    log(f"[bench] drawing {n_dec_inputs} decode steps {cd.name} ({time.time() - t0:.1f}s so far)")
     S_dec0 = torch.from_numpy(gi.make_decode_state(cd)).to(dev)
-    dsteps = [gi.to_torch(gi.make_decode_step(cd, s), cd.dtype, dev) for s in range(dec_steps)]
+    dsteps = [gi.to_torch(gi.make_decode_step(cd, s), cd.dtype, dev) for s in range(n_dec_inputs)]
     o_dec = torch.empty((cd.B, 1, cd.H_v, cd.d_v), dtype=dsteps[0]["q"].dtype, device=dev)
     S_dec = S_dec0.clone()
     torch.cuda.synchronize()
     log(f"[bench] inputs resident ({time.time() - t0:.1f}s)")
+    chunk_run, nseg1 = plan(cp)
 
     def prefill():
         g.chunk_forward(tp["q"], tp["k"], tp["v"], tp["a"], tp["b"], tp["w"], None, chunk=cp.chunk,
                         o=o, S_T=S_T, stream=stream)
 
     def decode(i):
-        x = dsteps[i % dec_steps]
+        x = dsteps[i % len(dsteps)]
         g.decode_step(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], S_dec, o=o_dec, stream=stream)
 
-    if args.counters:
+    if args.counters is not None:
+        ci = args.counters
+        if ci == 1:
+            run = prefill
+        else:
+            cx = gi.config(ci)
+            tx = gi.to_torch(gi.make_inputs(cx), cx.dtype, dev)
+            ox = torch.empty((cx.B, cx.T, cx.H_v, cx.d_v), dtype=tx["q"].dtype, device=dev)
+            sx = torch.empty((cx.B, cx.H_v, cx.d_k, cx.d_v), dtype=torch.float32, device=dev)
+
+            def run():
+                g.chunk_forward(tx["q"], tx["k"], tx["v"], tx["a"], tx["b"], tx["w"], None, chunk=cx.chunk,
+                                o=ox, S_T=sx, stream=stream)
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for i in range(2):
-            prefill()
-            decode(i)
+            run()
+            if ci == 1:
+                decode(i)
             dst.copy_(src)
         torch.cuda.synchronize()
-        log("[bench] counter launches done: 2 x prefill, 2 x decode, 2 x copy of 256 MiB")
+        log(f"[bench] counter launches done: 2 x prefill of workload {ci}"
+            f"{', 2 x decode' if ci == 1 else ''}, 2 x copy of 256 MiB")
         return
 
+    tokens = cp.B * cp.T
+    pbytes, pflops = prefill_algorithmic(cp, chunk_run)
+
+    # ---------------------------------------------------------------- cold-start series
+    series = None
+    if args.series > 0:
+        log(f"[bench] cold-start series: {args.series} prefill launches of {cp.name}")
+        ms = time_each(prefill, args.series)
+        wins = [(0, 1), (1, 5), (5, 25), (25, 50), (50, 100), (100, 200), (200, 300), (300, 500)]
+        series = {"launches": args.series, "windows_us": {}}
+        for a, b in wins:
+            if a < len(ms):
+                seg = ms[a:min(b, len(ms))]
+                series["windows_us"][f"{a}-{min(b, len(ms))}"] = round(float(np.mean(seg)) * 1e3, 1)
+        tail = ms[len(ms) // 2:]
+        series["first_launch_us"] = ms[0] * 1e3
+        series["settled_avg_us"] = float(np.mean(tail)) * 1e3
+        series["settled_min_us"] = float(min(tail)) * 1e3
+        series["settled_frac"] = pbytes / (float(np.mean(tail)) / 1e3) / 1e9 / HBM_PEAK_GBS
+        log(f"[bench] series windows (us): {series['windows_us']}")
+
+    # ---------------------------------------------------------------- headline steps
     for i in range(args.warmup):
         prefill()
         decode(i)
     torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- timed steps
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     if torch.distributed.is_available() and torch.distributed.is_initialized():
@@ -231,19 +304,76 @@ def main():
     pre_avg = float(np.mean(pre_ms)) / 1e3
     log(f"[bench] {K} steps: prefill avg {pre_avg * 1e6:.1f} us (min {min(pre_ms) * 1e3:.1f}), "
         f"decode avg {np.mean(dec_ms) * 1e3:.1f} us; wall {wall * 1e3:.1f} ms")
-
-    tokens = cp.B * cp.T
-    pbytes, pflops = prefill_algorithmic(cp)
     value = tokens / pre_avg
     digest = source_digest(PREFILL_KERNEL_SOURCES)
-    traffic = read_traffic(digest)
+    traffic = read_traffic(TRAFFIC_FILE, digest)
+
+    # ---------------------------------------------------------------- other prefill workloads
+    configs = {}
+    if args.config_steps > 0:
+        for ci in (2, 3):
+            cx = gi.config(ci)
+            if args.chunk:
+                cx = cx.replace(chunk=args.chunk)
+            log(f"[bench] drawing {cx.name}")
+            tx = gi.to_torch(gi.make_inputs(cx), cx.dtype, dev)
+            ox = torch.empty((cx.B, cx.T, cx.H_v, cx.d_v), dtype=tx["q"].dtype, device=dev)
+            sx = torch.empty((cx.B, cx.H_v, cx.d_k, cx.d_v), dtype=torch.float32, device=dev)
+            crun, nseg = plan(cx)
+            desc = g.make_desc(cx.B, cx.T, cx.H_qk, cx.H_v, cx.d_k, cx.d_v, cx.chunk, g.GDN2_BF16)
+            ws = g.gdn2_chunk_forward_workspace_bytes(desc)
+            wsx = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+
+            def run_x():
+                st = g.gdn2_chunk_forward(desc, tx["q"].data_ptr(), tx["k"].data_ptr(), tx["v"].data_ptr(),
+                                          tx["a"].data_ptr(), tx["b"].data_ptr(), tx["w"].data_ptr(), None,
+                                          ox.data_ptr(), sx.data_ptr(), wsx.data_ptr(), ws, stream.cuda_stream)
+                if st != g.GDN2_OK:
+                    raise g.Gdn2Error(st)
+
+            for _ in range(3):
+                run_x()
+            ms = time_each(run_x, args.config_steps)
+            avg = float(np.mean(ms)) / 1e3
+            by, fl = prefill_algorithmic(cx, crun)
+            toks = cx.B * cx.T
+            configs[cx.name] = {
+                "workload": f"prefill B{cx.B} T{cx.T} H_qk{cx.H_qk} H_v{cx.H_v} d{cx.d_k} {cx.dtype}",
+                "chunk_requested": cx.chunk, "chunk_run": crun, "segments": nseg, "launches": args.config_steps,
+                "kernel_us": avg * 1e6, "min_us": min(ms) * 1e3, "tokens_per_s": toks / avg,
+                "bound": "hbm", "achieved": by / avg / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": by / avg / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": by,
+                "mfma_frac_algorithmic": fl / avg / 1e12 / MFMA_BF16_PEAK_TFS}
+            log(f"[bench] {cx.name}: {avg * 1e6:.1f} us per call ({nseg} segments, chunk {crun}) = "
+                f"{by / avg / 1e9:.0f} GB/s, {configs[cx.name]['frac']:.3f} of HBM peak")
+            del tx, ox, sx, wsx
+            torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- strong decay
+    strong = None
+    if args.config_steps > 0:
+        gen = torch.Generator(device=dev).manual_seed(7)
+        a_strong = torch.reciprocal(1.0 + torch.exp(torch.randn(tp["a"].shape, generator=gen, device=dev) + 2.0))
+
+        def run_strong():
+            g.chunk_forward(tp["q"], tp["k"], tp["v"], a_strong, tp["b"], tp["w"], None, chunk=cp.chunk,
+                            o=o, S_T=S_T, stream=stream)
+
+        run_strong()
+        ms = time_each(run_strong, args.config_steps)
+        avg = float(np.mean(ms)) / 1e3
+        strong = {"workload": f"{cp.name} with decay pre-activation N(+2, 1) (per-token decay ~0.12)",
+                  "launches": args.config_steps, "kernel_us": avg * 1e6, "min_us": min(ms) * 1e3,
+                  "vs_headline": avg / pre_avg}
+        log(f"[bench] strong decay: {avg * 1e6:.1f} us per launch ({avg / pre_avg:.2f} x the headline)")
+        del a_strong
 
     # ---------------------------------------------------------------- decode workload leg
     S_dec.copy_(S_dec0)
     torch.cuda.synchronize()
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(dec_steps)]
-    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     l0.record(stream)
     for s in range(dec_steps):
         dev_ev[s][0].record(stream)
@@ -253,11 +383,36 @@ def main():
     torch.cuda.synchronize()
     dk_ms = [a.elapsed_time(b) for a, b in dev_ev]
     loop_ms = l0.elapsed_time(l1)
-    dbytes = decode_algorithmic(cd)
+    dbytes = decode_algorithmic(cd.B, cd.H_qk, cd.H_v, cd.d_k, cd.d_v)
     d_avg = float(np.mean(dk_ms)) / 1e3
     d_gbs = dbytes / d_avg / 1e9
     log(f"[bench] decode workload: {dec_steps} steps in {loop_ms:.1f} ms; kernel avg {d_avg * 1e6:.1f} us "
         f"= {d_gbs:.0f} GB/s algorithmic")
+    decode_leg = {"steps": dec_steps, "kernel_us": d_avg * 1e6, "loop_us_per_step": loop_ms * 1e3 / dec_steps,
+                  "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d_gbs / HBM_PEAK_GBS,
+                  "algorithmic_bytes": dbytes, "state_bytes": cd.B * cd.H_v * cd.d_k * cd.d_v * 4}
+    # larger states (beyond the 256 MiB Infinity Cache): random inputs, same head shape
+    larger = []
+    for N in (1024, 4096):
+        xs = gi.draw_on_device(N, 1, cd.H_qk, cd.H_v, cd.d_k, cd.d_v, "bf16", "channel", dev, seed=40 + N)
+        Sx = torch.randn((N, cd.H_v, cd.d_k, cd.d_v), device=dev) * 0.02
+        ox = torch.empty((N, 1, cd.H_v, cd.d_v), dtype=torch.bfloat16, device=dev)
+
+        def dec_x():
+            g.decode_step(xs["q"], xs["k"], xs["v"], xs["a"], xs["b"], xs["w"], Sx, o=ox, stream=stream)
+
+        for _ in range(5):
+            dec_x()
+        ms = time_each(dec_x, 50)
+        by = decode_algorithmic(N, cd.H_qk, cd.H_v, cd.d_k, cd.d_v)
+        avg = float(np.mean(ms)) / 1e3
+        larger.append({"sequences": N, "state_bytes": N * cd.H_v * cd.d_k * cd.d_v * 4, "steps": 50,
+                       "kernel_us": avg * 1e6, "achieved": by / avg / 1e9, "frac": by / avg / 1e9 / HBM_PEAK_GBS})
+        log(f"[bench] decode N{N} ({N * cd.H_v * cd.d_k * cd.d_v * 4 >> 20} MiB state): {avg * 1e6:.1f} us "
+            f"= {by / avg / 1e9:.0f} GB/s")
+        del xs, Sx, ox
+        torch.cuda.empty_cache()
+    decode_leg["larger_states"] = larger
 
     # ---------------------------------------------------------------- gate pre-activation leg
     pre_leg = None
@@ -268,19 +423,11 @@ def main():
             g.chunk_forward_preact(tpp["q"], tpp["k"], tpp["v"], tpp["a"], tpp["b"], tpp["w"], None, chunk=cp.chunk,
                                    o=o, S_T=S_T, stream=stream)
 
-        for _ in range(100):
+        for _ in range(20):
             prefill_preact()
-        torch.cuda.synchronize()
-        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.preact_steps)]
-        for e0, e1 in pev:
-            e0.record(stream)
-            prefill_preact()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        p_ms = [a.elapsed_time(b) for a, b in pev]
+        p_ms = time_each(prefill_preact, args.preact_steps)
         p_avg = float(np.mean(p_ms)) / 1e3
-        pby = preact_algorithmic(cp)
+        pby, _ = prefill_algorithmic(cp, chunk_run, gate_bytes=2 if cp.dtype == "bf16" else 4)
         pre_leg = {"launches": args.preact_steps, "kernel_us": p_avg * 1e6, "min_us": min(p_ms) * 1e3,
                    "tokens_per_s": tokens / p_avg, "achieved": pby / p_avg / 1e9, "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": pby / p_avg / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": pby}
@@ -304,14 +451,7 @@ def main():
         grads = backward()
         backward(grads)
         torch.cuda.synchronize()
-        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.backward_steps)]
-        for e0, e1 in bev:
-            e0.record(stream)
-            backward(grads)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        b_ms = [a.elapsed_time(b) for a, b in bev]
+        b_ms = time_each(lambda: backward(grads), args.backward_steps)
         b_avg = float(np.mean(b_ms)) / 1e3
         bfl, bby = backward_algorithmic(cp)
         bwd = {"launches": args.backward_steps, "ms": b_avg * 1e3, "min_ms": min(b_ms),
@@ -340,14 +480,7 @@ def main():
 
         gl = backward_long()
         torch.cuda.synchronize()
-        lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.long_backward)]
-        for e0, e1 in lev:
-            e0.record(stream)
-            backward_long(gl)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        l_ms = [a.elapsed_time(b) for a, b in lev]
+        l_ms = time_each(lambda: backward_long(gl), args.long_backward)
         l_avg = float(np.mean(l_ms)) / 1e3
         lfl, _ = backward_algorithmic(cl)
         bwd_long = {"workload": "backward B1 T65536 H16 d128 bf16 (split into segments)",
@@ -361,19 +494,25 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        nthreads = min(16, oracle.cores())
-        log(f"[bench] oracle on the host, {nthreads} threads, full prefill batch")
-        _, _, el = oracle.forward(dp["q"] if cp.dtype == "f32" else tp["q"].cpu(),
-                                  dp["k"] if cp.dtype == "f32" else tp["k"].cpu(),
-                                  dp["v"] if cp.dtype == "f32" else tp["v"].cpu(),
-                                  dp["a"], dp["b"], dp["w"], None, nthreads=nthreads, timing=True)
+        nthreads = oracle.cores()
+        qh = dp["q"] if cp.dtype == "f32" else tp["q"].cpu()
+        kh = dp["k"] if cp.dtype == "f32" else tp["k"].cpu()
+        vh = dp["v"] if cp.dtype == "f32" else tp["v"].cpu()
+        log(f"[bench] oracle on the host, {nthreads} threads, whole prefill batch")
+        _, _, el = oracle.forward(qh, kh, vh, dp["a"], dp["b"], dp["w"], None, nthreads=nthreads, timing=True)
+        one = lambda x: x[:1, :, :1]
+        _, _, el1 = oracle.forward(one(qh), one(kh), one(vh), one(dp["a"]), one(dp["b"]), one(dp["w"]), None,
+                                   nthreads=1, timing=True)
         cpu = {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-               "sample": f"the whole prefill batch once (B={cp.B}, T={cp.T}, {cp.H_v} heads, "
-                         f"d={cp.d_k}), fp64 recurrence, {el:.1f} s"}
-        log(f"[bench] oracle {el:.1f} s -> {tokens / el:.0f} tokens/s")
+               "cpu_model": cpu_model(),
+               "sample": f"the whole prefill batch once (B={cp.B}, T={cp.T}, {cp.H_v} heads, d={cp.d_k}), "
+                         f"fp64 recurrence, threads over (sequence, head), {el:.2f} s",
+               "single_thread": {"value": cp.T / el1, "unit": "tokens/s of one (sequence, head)",
+                                 "seconds": el1, "sample": f"sequence 0, head 0: T={cp.T}, d={cp.d_k}"}}
+        log(f"[bench] oracle {el:.2f} s -> {tokens / el:.0f} tokens/s; one head on one thread {el1:.2f} s")
 
     out = {
-        "metric": "prefill tokens/s (T=4096,H=16,d=128) + decode HBM GB/s, % of roofline",
+        "metric": METRIC,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -387,11 +526,16 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"prefill B{cp.B} T{cp.T} H_qk{cp.H_qk} H_v{cp.H_v} d_k{cp.d_k} d_v{cp.d_v} "
-                         f"chunk{cp.chunk} {cp.dtype} + decode step N{cd.B} H{cd.H_v} d{cd.d_k} fp32 state"),
+                         f"{cp.dtype} (chunk run {chunk_run}) + decode step N{cd.B} H{cd.H_v} d{cd.d_k} "
+                         f"fp32 state"),
+            "chunk_requested": cp.chunk,
+            "chunk_run": chunk_run,
             "prefill_kernel_us": pre_avg * 1e6,
             "prefill_kernel_us_median": float(np.median(pre_ms)) * 1e3,
             "prefill_kernel_us_min": float(min(pre_ms)) * 1e3,
             "decode_kernel_us": float(np.mean(dec_ms)) * 1e3,
+            "before_headline": (f"{args.series} cold-start prefill launches (series) and {args.warmup} "
+                                f"warm-up steps" if series else f"{args.warmup} warm-up steps"),
         },
         "roofline": {
             "kernel": "prefill",
@@ -405,16 +549,10 @@ def main():
             "mfma_frac_algorithmic": pflops / pre_avg / 1e12 / MFMA_BF16_PEAK_TFS,
             "kernel_source_digest": digest,
         },
-        "decode": {
-            "steps": dec_steps,
-            "kernel_us": d_avg * 1e6,
-            "loop_us_per_step": loop_ms * 1e3 / dec_steps,
-            "achieved": d_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": d_gbs / HBM_PEAK_GBS,
-            "algorithmic_bytes": dbytes,
-        },
+        "series": series,
+        "configs": configs,
+        "strong_decay": strong,
+        "decode": decode_leg,
         "preact": pre_leg,
         "backward": bwd,
         **({"backward_long": bwd_long} if bwd_long else {}),

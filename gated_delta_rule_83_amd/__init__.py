@@ -42,7 +42,7 @@ GDN2_BF16 = 1
 EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forward_scalar",
             "gdn2_chunk_forward_preact",
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
-            "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
+            "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_forward_plan", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
             "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes", "gdn2_chunk_backward_preact",
             "gdn2_chunk_backward_coupled", "gdn2_chunk_backward_scalar", "gdn2_chunk_forward_varlen_gates",
             "gdn2_chunk_backward_varlen_gates", "gdn2_decode_step_gates",
@@ -94,6 +94,8 @@ def load(path: Optional[str] = None):
     lib.gdn2_decode_step.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn2_chunk_forward_workspace_bytes.restype = sz
     lib.gdn2_chunk_forward_workspace_bytes.argtypes = [dp]
+    lib.gdn2_chunk_forward_plan.restype = ctypes.c_int
+    lib.gdn2_chunk_forward_plan.argtypes = [dp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.gdn2_chunk_backward.restype = ctypes.c_int
     lib.gdn2_chunk_backward.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
     lib.gdn2_chunk_backward_workspace_bytes.restype = sz
@@ -132,6 +134,14 @@ def gdn2_status_string(status: int) -> str:
 
 def gdn2_chunk_forward_workspace_bytes(desc) -> int:
     return load().gdn2_chunk_forward_workspace_bytes(None if desc is None else ctypes.byref(desc))
+
+
+def gdn2_chunk_forward_plan(desc):
+    """(status, chunk_run, segments): how the prefill would run `desc`."""
+    c, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load().gdn2_chunk_forward_plan(None if desc is None else ctypes.byref(desc), ctypes.byref(c),
+                                        ctypes.byref(n))
+    return st, c.value, n.value
 
 
 def gdn2_chunk_forward(desc, q, k, v, a, b, w, S0, o, S_T, workspace=0, workspace_bytes=0,
@@ -253,6 +263,47 @@ def _check(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _want(t, name, shape, dtype, device):
+    """t (or None) must be a contiguous `dtype` tensor of exactly `shape` on
+    `device`: the kernels index every tensor from the sizes of q and v, so a
+    tensor of another shape would be read or written out of its bounds."""
+    if t is None:
+        return
+    _check(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, but q is on {device}")
+
+
+def _want_rows(t, name, rows, tail, dtype, device):
+    """Like _want for token tensors given as [rows, *tail] with any leading
+    size-1 dimensions (e.g. [1, T, H, d] or [T, H, d])."""
+    if t is None:
+        return
+    _check(t, name, dtype)
+    n = len(tail) + 1
+    lead = tuple(t.shape[:-n])
+    if tuple(t.shape[-n:]) != (rows,) + tuple(tail) or any(x != 1 for x in lead):
+        raise ValueError(f"{name} must have shape [..., {rows}, {', '.join(map(str, tail))}] "
+                         f"(leading dimensions 1), got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, but q is on {device}")
+
+
+def _dims(q, v):
+    """(B, T, H_qk, H_v, d_k, d_v) of a [B, T, H, d] problem from q and v."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"q and v must be [B, T, H, d], got {tuple(q.shape)} and {tuple(v.shape)}")
+    B, T, H_qk, d_k = q.shape
+    if tuple(v.shape[:2]) != (B, T):
+        raise ValueError(f"v must have B={B}, T={T} like q, got {tuple(v.shape)}")
+    H_v, d_v = v.shape[2], v.shape[3]
+    if H_v % H_qk:
+        raise ValueError(f"value heads ({H_v}) must be a multiple of query/key heads ({H_qk})")
+    return B, T, H_qk, H_v, d_k, d_v
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -265,21 +316,24 @@ def chunk_forward(q, k, v, a, b, w, S0=None, chunk: int = 64, o=None, S_T=None,
     """Prefill. q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v]; a, b [B,T,H_v,d_k] fp32;
     w [B,T,H_v,d_v] fp32; S0 [B,H_v,d_k,d_v] fp32 or None. Returns (o, S_T)."""
     import torch
-    B, T, H_qk, d_k = q.shape
-    H_v, d_v = v.shape[2], v.shape[3]
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, nm, q.dtype)
-    for t, nm in ((a, "a"), (b, "b"), (w, "w"), (S0, "S0")):
-        _check(t, nm, torch.float32)
+    B, T, H_qk, H_v, d_k, d_v = _dims(q, v)
+    dev, f32 = q.device, torch.float32
+    _want(q, "q", (B, T, H_qk, d_k), q.dtype, dev)
+    _want(k, "k", (B, T, H_qk, d_k), q.dtype, dev)
+    _want(v, "v", (B, T, H_v, d_v), q.dtype, dev)
+    _want(a, "a", (B, T, H_v, d_k), f32, dev)
+    _want(b, "b", (B, T, H_v, d_k), f32, dev)
+    _want(w, "w", (B, T, H_v, d_v), f32, dev)
+    _want(S0, "S0", (B, H_v, d_k, d_v), f32, dev)
     if o is None:
-        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=dev)
     if S_T is None and want_state:
-        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
-    _check(o, "o", q.dtype)
-    _check(S_T, "S_T", torch.float32)
+        S_T = torch.empty((B, H_v, d_k, d_v), dtype=f32, device=dev)
+    _want(o, "o", (B, T, H_v, d_v), q.dtype, dev)
+    _want(S_T, "S_T", (B, H_v, d_k, d_v), f32, dev)
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
     ws = gdn2_chunk_forward_workspace_bytes(desc)
-    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    work = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
     st = gdn2_chunk_forward(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0),
                             _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
     if st != GDN2_OK:
@@ -338,23 +392,23 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
     import torch
     T, H_qk, d_k = q.shape[-3:]
     H_v, d_v = v.shape[-2], v.shape[-1]
+    dev = q.device
     if cu is None:
-        B = q.shape[0]
+        B, T, H_qk, H_v, d_k, d_v = _dims(q, v)
+        chk = lambda t, nm, tail, dt: _want(t, nm, (B, T) + tuple(tail), dt, dev)
     else:
-        _check(cu, "cu_seqlens", torch.int32)
+        _want(cu, "cu_seqlens", (cu.numel(),), torch.int32, dev)
         B = cu.numel() - 1
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
-        _check(t, nm, q.dtype)
+        if B < 0:
+            raise ValueError("cu_seqlens needs at least one offset")
+        chk = lambda t, nm, tail, dt: _want_rows(t, nm, T, tail, dt, dev)
+    _check_gate_form(chk, q, k, v, a, b, w, form, H_qk, H_v, d_k, d_v)
+    chk(dO, "dO", (H_v, d_v), q.dtype)
     preact, coupled = form == "preact", form in ("coupled", "scalar")
     gdt = q.dtype if preact else torch.float32  # gates (and their gradients)
-    for t, nm in ((a, "a"), (b, "b"), (w, "w")):
-        _check(t, nm, gdt)
-    if coupled and (b.dim() != q.dim() - 1 or (form == "scalar" and a.dim() != q.dim() - 1)):
-        raise ValueError("scalar gates are [.., T, H_v]")
     for t, nm in ((S0, "S0"), (dS_T, "dS_T")):
-        _check(t, nm, torch.float32)
+        _want(t, nm, (B, H_v, d_k, d_v), torch.float32, dev)
     g = dict(grads or {})
-    dev = q.device
     shapes = {"dq": (q.shape, q.dtype), "dk": (k.shape, q.dtype), "dv": (v.shape, q.dtype),
               "da": (a.shape, gdt), "db": (b.shape, gdt)}
     if not coupled:
@@ -364,7 +418,7 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
     for nm, (shape, dt) in shapes.items():
         if g.get(nm) is None:
             g[nm] = torch.empty(shape, dtype=dt, device=dev)
-        _check(g[nm], nm, dt)
+        _want(g[nm], nm, shape, dt, dev)
     g.setdefault("dS0", None)
     g.setdefault("dw", None)
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
@@ -372,6 +426,8 @@ def _backward(q, k, v, a, b, w, S0, dO, dS_T, cu, want_dS0, grads, workspace, st
           else gdn2_chunk_backward_varlen_workspace_bytes(desc))
     if workspace is None and ws:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _want(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
     wbytes = workspace.numel() if workspace is not None else 0
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
@@ -399,20 +455,24 @@ def chunk_forward_preact(q, k, v, a_pre, b_pre, w_pre, S0=None, chunk: int = 64,
     input dtype (decay a = exp(-softplus(a_pre)), b = sigmoid(b_pre),
     w = sigmoid(w_pre)), activated in the kernel. Shapes as chunk_forward."""
     import torch
-    B, T, H_qk, d_k = q.shape
-    H_v, d_v = v.shape[2], v.shape[3]
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (a_pre, "a_pre"), (b_pre, "b_pre"), (w_pre, "w_pre")):
-        _check(t, nm, q.dtype)
-    _check(S0, "S0", torch.float32)
+    B, T, H_qk, H_v, d_k, d_v = _dims(q, v)
+    dev, f32 = q.device, torch.float32
+    _want(q, "q", (B, T, H_qk, d_k), q.dtype, dev)
+    _want(k, "k", (B, T, H_qk, d_k), q.dtype, dev)
+    _want(v, "v", (B, T, H_v, d_v), q.dtype, dev)
+    _want(a_pre, "a_pre", (B, T, H_v, d_k), q.dtype, dev)
+    _want(b_pre, "b_pre", (B, T, H_v, d_k), q.dtype, dev)
+    _want(w_pre, "w_pre", (B, T, H_v, d_v), q.dtype, dev)
+    _want(S0, "S0", (B, H_v, d_k, d_v), f32, dev)
     if o is None:
-        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=dev)
     if S_T is None and want_state:
-        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
-    _check(o, "o", q.dtype)
-    _check(S_T, "S_T", torch.float32)
+        S_T = torch.empty((B, H_v, d_k, d_v), dtype=f32, device=dev)
+    _want(o, "o", (B, T, H_v, d_v), q.dtype, dev)
+    _want(S_T, "S_T", (B, H_v, d_k, d_v), f32, dev)
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
     ws = gdn2_chunk_forward_workspace_bytes(desc)
-    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    work = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
     st = gdn2_chunk_forward_preact(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a_pre), _ptr(b_pre), _ptr(w_pre),
                                    _ptr(S0), _ptr(o), _ptr(S_T), _ptr(work), ws, _stream(stream))
     if st != GDN2_OK:
@@ -425,35 +485,37 @@ def chunk_forward_coupled(q, k, v, a, beta, S0=None, chunk: int = 64, o=None, S_
     """Prefill with coupled gates b = w = beta (one scalar per token and value
     head). q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v]; a [B,T,H_v,d_k] fp32;
     beta [B,T,H_v] fp32; S0 [B,H_v,d_k,d_v] fp32 or None. Returns (o, S_T)."""
-    return _forward_scalar_gates(gdn2_chunk_forward_coupled, q, k, v, a, beta, S0, chunk, o, S_T, want_state,
-                                 stream)
+    return _forward_scalar_gates(gdn2_chunk_forward_coupled, False, q, k, v, a, beta, S0, chunk, o, S_T,
+                                 want_state, stream)
 
 
 def chunk_forward_scalar(q, k, v, alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
                          want_state: bool = True, stream=None):
     """Prefill with scalar gates (Gated DeltaNet form): decay alpha and coupled
     erase/write gate beta, each [B,T,H_v] fp32. Other arguments as chunk_forward."""
-    return _forward_scalar_gates(gdn2_chunk_forward_scalar, q, k, v, alpha, beta, S0, chunk, o, S_T, want_state,
-                                 stream)
+    return _forward_scalar_gates(gdn2_chunk_forward_scalar, True, q, k, v, alpha, beta, S0, chunk, o, S_T,
+                                 want_state, stream)
 
 
-def _forward_scalar_gates(entry, q, k, v, a, beta, S0, chunk, o, S_T, want_state, stream):
+def _forward_scalar_gates(entry, scalar_decay, q, k, v, a, beta, S0, chunk, o, S_T, want_state, stream):
     import torch
-    B, T, H_qk, d_k = q.shape
-    H_v, d_v = v.shape[2], v.shape[3]
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, nm, q.dtype)
-    for t, nm in ((a, "a"), (beta, "beta"), (S0, "S0")):
-        _check(t, nm, torch.float32)
+    B, T, H_qk, H_v, d_k, d_v = _dims(q, v)
+    dev, f32 = q.device, torch.float32
+    _want(q, "q", (B, T, H_qk, d_k), q.dtype, dev)
+    _want(k, "k", (B, T, H_qk, d_k), q.dtype, dev)
+    _want(v, "v", (B, T, H_v, d_v), q.dtype, dev)
+    _want(a, "alpha" if scalar_decay else "a", (B, T, H_v) if scalar_decay else (B, T, H_v, d_k), f32, dev)
+    _want(beta, "beta", (B, T, H_v), f32, dev)
+    _want(S0, "S0", (B, H_v, d_k, d_v), f32, dev)
     if o is None:
-        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=dev)
     if S_T is None and want_state:
-        S_T = torch.empty((B, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
-    _check(o, "o", q.dtype)
-    _check(S_T, "S_T", torch.float32)
+        S_T = torch.empty((B, H_v, d_k, d_v), dtype=f32, device=dev)
+    _want(o, "o", (B, T, H_v, d_v), q.dtype, dev)
+    _want(S_T, "S_T", (B, H_v, d_k, d_v), f32, dev)
     desc = make_desc(B, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
     ws = gdn2_chunk_forward_workspace_bytes(desc)
-    work = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    work = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
     st = entry(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(work), ws,
                _stream(stream))
     if st != GDN2_OK:
@@ -462,6 +524,37 @@ def _forward_scalar_gates(entry, q, k, v, a, beta, S0, chunk, o, S_T, want_state
 
 
 GDN2_GATES = {"channel": 0, "preact": 1, "coupled": 2, "scalar": 3}
+
+
+def _check_gate_form(chk, q, k, v, a, b, w, gates, H_qk, H_v, d_k, d_v):
+    """Token tensors of gate form `gates`; chk(t, name, tail, dtype) checks
+    one tensor against its token dimensions followed by `tail`."""
+    import torch
+    if H_v % H_qk:
+        raise ValueError(f"value heads ({H_v}) must be a multiple of query/key heads ({H_qk})")
+    chk(q, "q", (H_qk, d_k), q.dtype)
+    chk(k, "k", (H_qk, d_k), q.dtype)
+    chk(v, "v", (H_v, d_v), q.dtype)
+    if gates in ("channel", "general", "preact"):
+        gdt = q.dtype if gates == "preact" else torch.float32
+        if a is None or b is None or w is None:
+            raise ValueError(f"a, b and w are required for gates={gates!r}")
+        chk(a, "a", (H_v, d_k), gdt)
+        chk(b, "b", (H_v, d_k), gdt)
+        chk(w, "w", (H_v, d_v), gdt)
+    elif gates in ("coupled", "scalar"):
+        if a is None or b is None:
+            raise ValueError(f"a (alpha) and beta are required for gates={gates!r}")
+        chk(a, "alpha" if gates == "scalar" else "a", (H_v,) if gates == "scalar" else (H_v, d_k), torch.float32)
+        chk(b, "beta", (H_v,), torch.float32)
+    else:
+        raise ValueError(f"unknown gate form {gates}")
+
+
+def _check_packed(q, k, v, a, b, w, gates, T, H_qk, H_v, d_k, d_v, dev):
+    """Token tensors of a packed ([T, H, d], or with leading 1s) problem."""
+    _check_gate_form(lambda t, nm, tail, dt: _want_rows(t, nm, T, tail, dt, dev),
+                     q, k, v, a, b, w, gates, H_qk, H_v, d_k, d_v)
 
 
 def chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64, o=None, S_T=None,
@@ -476,21 +569,22 @@ def chunk_forward_varlen(q, k, v, a, b, w, cu_seqlens, S0=None, chunk: int = 64,
     import torch
     T, H_qk, d_k = q.shape[-3:]
     H_v, d_v = v.shape[-2], v.shape[-1]
-    N = cu_seqlens.numel() - 1
+    if gates not in GDN2_GATES:
+        raise ValueError(f"unknown gate form {gates}")
     form = GDN2_GATES[gates]
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, nm, q.dtype)
-    gdt = q.dtype if gates == "preact" else torch.float32
-    for t, nm in ((a, "a"), (b, "b"), (w, "w")):
-        _check(t, nm, gdt)
-    _check(S0, "S0", torch.float32)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    dev, f32 = q.device, torch.float32
+    _want(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one offset")
+    _check_packed(q, k, v, a, b, w, gates, T, H_qk, H_v, d_k, d_v, dev)
+    _want(S0, "S0", (N, H_v, d_k, d_v), f32, dev)
     if o is None:
-        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+        o = torch.empty(v.shape, dtype=q.dtype, device=dev)
     if S_T is None and want_state:
-        S_T = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=q.device)
-    _check(o, "o", q.dtype)
-    _check(S_T, "S_T", torch.float32)
+        S_T = torch.empty((N, H_v, d_k, d_v), dtype=f32, device=dev)
+    _want(o, "o", v.shape, q.dtype, dev)
+    _want(S_T, "S_T", (N, H_v, d_k, d_v), f32, dev)
     desc = make_desc(N, T, H_qk, H_v, d_k, d_v, chunk, _dtype_code(q))
     st = gdn2_chunk_forward_varlen_gates(desc, _ptr(cu_seqlens), form, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                          _ptr(w), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
@@ -506,18 +600,36 @@ def decode_step(q, k, v, a, b, w, S, o=None, stream=None, gates: str = "channel"
     (a, b, w pre-activations in the input dtype), "coupled" (b = beta
     [N,1,H_v] fp32, w None), "scalar" (a = alpha, b = beta, each [N,1,H_v])."""
     import torch
+    if S.dim() != 4:
+        raise ValueError(f"S must be [N, H_v, d_k, d_v], got {tuple(S.shape)}")
     N, H_v, d_k, d_v = S.shape
     H_qk = q.shape[-2]
+    if gates not in GDN2_GATES:
+        raise ValueError(f"unknown gate form {gates}")
     form = GDN2_GATES[gates]
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+    dev = q.device
+    _want(S, "S", (N, H_v, d_k, d_v), torch.float32, dev)
+    # one token per sequence: [N, 1, H, d] or [N, H, d]
+    one = lambda t, tail: None if t is None else (tuple(t.shape) in ((N, 1) + tail, (N,) + tail))
+    for t, nm, tail in ((q, "q", (H_qk, d_k)), (k, "k", (H_qk, d_k)), (v, "v", (H_v, d_v))):
         _check(t, nm, q.dtype)
+        if not one(t, tail) or t.device != dev:
+            raise ValueError(f"{nm} must be [N, 1, {tail[0]}, {tail[1]}] on {dev}, got {tuple(t.shape)}")
+    gshape = {"a": (H_v,) if gates == "scalar" else (H_v, d_k),
+              "b": (H_v,) if gates in ("coupled", "scalar") else (H_v, d_k), "w": (H_v, d_v)}
     gdt = q.dtype if gates == "preact" else torch.float32
     for t, nm in ((a, "a"), (b, "b"), (w, "w")):
+        if nm == "w" and gates in ("coupled", "scalar"):
+            continue
+        if t is None:
+            raise ValueError(f"{nm} is required for gates={gates!r}")
         _check(t, nm, gdt)
-    _check(S, "S", torch.float32)
+        if not one(t, gshape[nm]) or t.device != dev:
+            raise ValueError(f"{nm} must be [N, 1, {', '.join(map(str, gshape[nm]))}] on {dev}, "
+                             f"got {tuple(t.shape)}")
     if o is None:
-        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
-    _check(o, "o", q.dtype)
+        o = torch.empty(v.shape, dtype=q.dtype, device=dev)
+    _want(o, "o", v.shape, q.dtype, dev)
     desc = make_desc(N, 1, H_qk, H_v, d_k, d_v, 64, _dtype_code(q))
     st = gdn2_decode_step_gates(desc, form, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(w), _ptr(S),
                                 _ptr(o), _stream(stream))

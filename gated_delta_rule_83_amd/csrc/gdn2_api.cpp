@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "gdn2_internal.hpp"
+#include "gdn2_range.hpp"
 
 namespace {
 
@@ -42,6 +43,9 @@ gdn2_status check_desc(const gdn2_desc *d, bool decode) {
   if (decode && d->T != 1) return GDN2_ERR_BAD_SHAPE;
   if (!supported_dim(d->d_k) || !supported_dim(d->d_v)) return GDN2_ERR_UNSUPPORTED;
   if (!decode && !supported_chunk(d->chunk)) return GDN2_ERR_UNSUPPORTED;
+  // the prefill's buffer descriptors span one chunk of token rows: the
+  // widest row times the longest chunk must fit their 31-bit range
+  if (!decode && !gdn2::window_fits(d->H_qk, d->H_v, d->d_k, d->d_v)) return GDN2_ERR_UNSUPPORTED;
   return GDN2_OK;
 }
 
@@ -56,7 +60,7 @@ const char *gdn2_status_string(gdn2_status s) {
     case GDN2_OK: return "ok";
     case GDN2_ERR_NULL_POINTER: return "a required pointer is NULL";
     case GDN2_ERR_BAD_SHAPE: return "invalid shape, or a tensor pointer not 16-byte aligned";
-    case GDN2_ERR_UNSUPPORTED: return "unsupported head dimension or chunk length";
+    case GDN2_ERR_UNSUPPORTED: return "unsupported head dimension or chunk length, or token rows too wide for a chunk's buffer range";
     case GDN2_ERR_BAD_DTYPE: return "unknown dtype";
     case GDN2_ERR_WORKSPACE: return "workspace too small";
     case GDN2_ERR_HIP: return "HIP runtime error at launch";
@@ -94,6 +98,15 @@ size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc) {
   if (check_desc(desc, false) != GDN2_OK) return 0;
   // nonzero only when long sequences are split across workgroups
   return gdn2::prefill_plan(prefill_args(desc)).ws_bytes;
+}
+
+gdn2_status gdn2_chunk_forward_plan(const gdn2_desc *desc, int32_t *chunk_run, int32_t *segments) {
+  const gdn2_status st = check_desc(desc, false);
+  if (st != GDN2_OK) return st;
+  const gdn2::PrefillPlan pl = gdn2::prefill_plan(prefill_args(desc));
+  if (chunk_run) *chunk_run = pl.chunk;
+  if (segments) *segments = pl.nseg;
+  return GDN2_OK;
 }
 
 gdn2_status gdn2_chunk_forward(const gdn2_desc *d, const void *q, const void *k, const void *v,

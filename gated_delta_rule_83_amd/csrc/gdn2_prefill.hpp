@@ -59,6 +59,7 @@
 
 #include "gdn2_device.hpp"
 #include "gdn2_internal.hpp"
+#include "gdn2_range.hpp"
 
 namespace gdn2 {
 
@@ -585,9 +586,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   const float *S0p = (ident || !p.S0 || (rel > 0 && p.s0_stride == 0)) ? nullptr : p.S0 + rel * p.s0_stride;
   float *STp = ident ? p.M_T + rel * p.m_stride
                : (!p.S_T || (p.sT_last_only && rel != p.nseg - 1)) ? nullptr : p.S_T + rel * p.sT_stride;
-  // bytes from token t0 to the end of the segment (0 past the end: a
-  // buffer access beyond the range returns 0 without touching memory)
-  auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return t0 < Tl ? (uint32_t)(Tl - t0) * tb : 0u; };
+  // byte range of a descriptor based at token t0: the C tokens of the chunk
+  // starting there, fewer at the end of the segment, 0 past it (a buffer
+  // access beyond the range returns 0 without touching memory). Every
+  // request and store of a chunk stays inside its own C tokens.
+  auto rows_left = [&](int t0, uint32_t tb) -> uint32_t { return window_bytes(t0, Tl, C, tb); };
 
   // ---------------------------------------------------------------- producer layout
   // Token-major (d_k = 128): producer wave w builds tokens w*C/4 .. +C/4 of

@@ -33,7 +33,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "config", "scaled", "make_inputs", "make_decode_step",
-           "make_decode_state", "to_torch"]
+           "make_decode_state", "to_torch", "draw_on_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -192,4 +192,61 @@ def to_torch(d: dict, dtype: str, device=None):
         if device is not None:
             t = t.to(device)
         out[name] = t
+    return out
+
+
+def draw_on_device(B: int, T: int, H_qk: int, H_v: int, d_k: int, d_v: int, dtype: str, gates: str,
+                   device, seed: int, a_mu: float = -4.0, packed: bool = False,
+                   hard_erase_p: float = 0.0) -> dict:
+    """Inputs drawn on the device with torch's seeded generator, for problems
+    too large to draw on the host (sequences of hundreds of thousands of
+    tokens). Same distributions as the workloads: q, k ~ N(0, 1) then
+    L2-normalised (fp32, before the cast), v ~ N(0, 1); gates by `gates`:
+      "channel": a = 1 / (1 + e^x), x ~ N(a_mu, 1); b, w = sigmoid(N(0, 1)), fp32
+      "preact":  the pre-activations themselves, in `dtype`
+      "coupled": a as "channel"; beta = sigmoid(N(0, 1)) per token and value head
+      "scalar":  alpha = 1 / (1 + e^x), x ~ N(a_mu, 1), and beta, per token and value head
+    With hard_erase_p > 0, Bernoulli(hard_erase_p) (batch, token) positions
+    get erase-gate pre-activation 6 on every head and key channel (per-channel
+    forms). Shapes [B, T, H, d] (gates of the coupled forms [B, T, H_v]);
+    with `packed`, B must be 1 and the leading dimension is dropped."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def normal(shape, mu=0.0):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return x.add_(mu) if mu else x
+
+    def unit(shape):
+        x = normal(shape)
+        x.div_(x.norm(dim=-1, keepdim=True).clamp_min_(1e-30))
+        return x.to(tdt)
+
+    out = {"q": unit((B, T, H_qk, d_k)), "k": unit((B, T, H_qk, d_k)), "v": normal((B, T, H_v, d_v)).to(tdt)}
+    decay = lambda x: torch.reciprocal(1.0 + torch.exp(x))
+    def erase_pre():
+        x = normal((B, T, H_v, d_k))
+        if hard_erase_p > 0.0:
+            hit = torch.rand((B, T), generator=gen, device=device) < hard_erase_p
+            x[hit] = 6.0
+        return x
+
+    if gates == "channel":
+        out["a"] = decay(normal((B, T, H_v, d_k), a_mu))
+        out["b"] = torch.sigmoid(erase_pre())
+        out["w"] = torch.sigmoid(normal((B, T, H_v, d_v)))
+    elif gates == "preact":
+        out["a"] = normal((B, T, H_v, d_k), a_mu).to(tdt)
+        out["b"] = erase_pre().to(tdt)
+        out["w"] = normal((B, T, H_v, d_v)).to(tdt)
+    elif gates in ("coupled", "scalar"):
+        out["a"] = decay(normal((B, T, H_v) if gates == "scalar" else (B, T, H_v, d_k), a_mu))
+        out["b"] = torch.sigmoid(normal((B, T, H_v)))
+        out["w"] = None
+    else:
+        raise ValueError(f"unknown gate form {gates}")
+    if packed:
+        assert B == 1
+        out = {k: (None if x is None else x[0]) for k, x in out.items()}
     return out

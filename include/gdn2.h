@@ -59,7 +59,10 @@ typedef enum {
                                 a tensor pointer not 16-byte aligned (4-byte for the
                                 tensors of one fp32 per token and value head:
                                 beta, alpha and their gradients) */
-  GDN2_ERR_UNSUPPORTED = 3,  /* valid but not built: d_k, d_v not in {16,32,64,128}, chunk not in {16,32,64} */
+  GDN2_ERR_UNSUPPORTED = 3,  /* valid but not built: d_k, d_v not in {16,32,64,128}, chunk not in {16,32,64},
+                                or (prefill and backward) max(H_qk, H_v) * max(d_k, d_v) * 4 * 64 > 2^31 - 1
+                                (one chunk of the widest token rows must fit a buffer range:
+                                H <= 65535 at d = 128) */
   GDN2_ERR_BAD_DTYPE = 4,    /* dtype is neither GDN2_F32 nor GDN2_BF16 */
   GDN2_ERR_WORKSPACE = 5,    /* workspace smaller than gdn2_chunk_forward_workspace_bytes() */
   GDN2_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
@@ -70,8 +73,12 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
 
 /* Problem description. B: sequences; T: tokens per sequence; H_qk / H_v:
  * query-key heads / value heads (H_v % H_qk == 0); d_k, d_v: head dims;
- * chunk: tokens per chunk of the prefill (a performance knob only: results
- * agree at every supported chunk); dtype: a gdn2_dtype for q, k, v, o. */
+ * chunk: the LONGEST chunk of the prefill the caller allows (a performance
+ * knob only: results agree at every supported chunk). The prefill runs the
+ * longest supported chunk not above it whose working set fits one compute
+ * unit: at d_k = 128 in bf16 that is 32 when 64 is asked for (64 does not fit
+ * the 160 KiB of LDS); gdn2_chunk_forward_plan() reports the chunk that runs.
+ * dtype: a gdn2_dtype for q, k, v, o. */
 typedef struct {
   int32_t B, T, H_qk, H_v, d_k, d_v, chunk;
   int32_t dtype;
@@ -88,6 +95,14 @@ typedef struct {
  * Returns 0 for an invalid description as well; the forward call reports
  * the error. */
 size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc);
+
+/* How gdn2_chunk_forward (and its gate forms) would run `desc`: the chunk
+ * length actually used (the longest supported one not above desc->chunk that
+ * fits, see gdn2_desc) into *chunk_run, and the number of segments each
+ * sequence is split into (1: unsplit) into *segments. Either output pointer
+ * may be NULL. Host-only: enqueues nothing, needs no device. Returns the
+ * status gdn2_chunk_forward would return for the description's checks. */
+gdn2_status gdn2_chunk_forward_plan(const gdn2_desc *desc, int32_t *chunk_run, int32_t *segments);
 
 /* Prefill: run T tokens of every (sequence, value head) through the
  * recurrence above, starting from S0, writing every output o_t and the final
