@@ -63,11 +63,14 @@ struct PrefillPlan {
   size_t ws_bytes;
 };
 
-// Threshold on the chunk's total decay per key channel above which the
-// chunk-parallel form is used. Below it the chunk is stepped token by token
-// (exact for any decay). The chunk form scales key-side operands by the
-// inverse cumulative decay, so this bounds every such factor by e^60.
+// Thresholds on the decay per key channel above which the chunk-parallel form
+// is used: of each half of the chunk where the Gram matrices are anchored at
+// the chunk's middle (d_k = 128), of the whole chunk where they are anchored
+// at its start. Below it the chunk is stepped token by token (exact for any
+// decay). The operands carry at most the inverse of that decay, so every
+// scale factor stays below e^60.
 constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
+constexpr float kMinHalfDecay = 8.75651076e-27f;   // e^-60
 
 // Backward pass (gradients of the recurrence); see gdn2_chunk_backward.
 struct BackwardArgs {

@@ -9,22 +9,30 @@
 //
 // Chunk form. Unrolling C tokens from the entering state S0 with
 // gamma_t = prod_{s<=t} a_s (channel-wise), beta_s = b_s * k_s, u_s = w_s * v_s:
-//   Akk[t,s] = sum_i (k_t gamma_t)_i (k_s / gamma_s)_i      s < t
-//   Akb[t,s] = sum_i (k_t gamma_t)_i (beta_s / gamma_s)_i   s < t
-//   Mqk[t,s] = sum_i (q_t gamma_t)_i (k_s / gamma_s)_i      s <= t
-//   Mqb[t,s] = sum_i (q_t gamma_t)_i (beta_s / gamma_s)_i   s <= t
+//   Akk[t,s] = sum_i k_t,i k_s,i gamma_t,i / gamma_s,i      s < t
+//   Akb[t,s] = sum_i k_t,i beta_s,i gamma_t,i / gamma_s,i   s < t
+//   Mqk[t,s] = sum_i q_t,i k_s,i gamma_t,i / gamma_s,i      s <= t
+//   Mqb[t,s] = sum_i q_t,i beta_s,i gamma_t,i / gamma_s,i   s <= t
 //   (I + Akb) R = (gamma * K) S0 + Akk U          (row t of R is the key read r_t)
 //   O  = (gamma * Q) S0 + Mqk U - Mqb R
-//   S_C = diag(gamma_C) (S0 + (K / gamma)^T U - (beta / gamma)^T R)
-// The factor gamma_t / gamma_s <= 1 is split against the chunk start (the
-// anchor), so each MFMA operand carries one factor. Both factors only rescale
-// elements, so bf16/fp32 rounding stays relative; the only risk is range,
-// which is bounded by requiring gamma_C >= e^-60 on every channel. A chunk
-// that fails this test (very strong decay) is stepped token by token, which
-// is exact for any decay. Rescaling cumulative gates against an in-block
-// anchor so that no ratio explodes is the device the FiX analysis on
-// iplexlaw.co.kr describes for its block-wise kernel (section 5); here the
-// blocks are the prefill's chunks.
+//   S_C = diag(gamma_C) S0 + (rho * K)^T U - (rho * beta)^T R,  rho_s = gamma_C / gamma_s
+// Anchors. The ratio gamma_t / gamma_s <= 1 is split between the two MFMA
+// operands against an anchor token: rescaling cumulative gates against an
+// in-block anchor so that ratios cannot explode is the device the FiX
+// analysis on iplexlaw.co.kr describes for its block-wise kernel (section 5).
+// For d_k = 128 the Gram matrices are anchored at the middle of the chunk,
+// m = C/2 - 1: the left operands carry lam_t = gamma_t / gamma_m and the
+// right ones mu_s = gamma_m / gamma_s, so in the off-diagonal block (second
+// half x first half) both factors are <= 1, and elsewhere one factor is
+// bounded by the inverse decay of half a chunk. (gamma * K) S0 is formed as
+// (lam * K)(diag(gamma_m) S0). The carry uses the chunk-end anchor: rho <= 1.
+// Every factor only rescales elements, so bf16 rounding stays relative; the
+// only risk is range, bounded by requiring each half-chunk decay to be at
+// least e^-60 on every channel. A chunk that fails this test (a decay below
+// ~e^-3.75 per token throughout half a chunk) is stepped token by token,
+// which is exact for any decay. (For d_k < 128 the Gram anchor is the chunk
+// start, lam = gamma_t, mu = 1 / gamma_t, and the whole chunk's decay is
+// checked against e^-60.)
 //
 // Everything that does not depend on the entering state (scaled operands,
 // the Gram matrices, the diagonal inverses) is computed one chunk ahead by
@@ -202,6 +210,7 @@ struct ChunkBuf {
   alignas(16) char m[Cf::C * LT::STRIDE];
   alignas(16) typename Op<Cf::BF16>::T dinv[Cf::NCH * 16 * Cf::LDD];  // (I + Akb_rr)^-1 per diagonal block
   alignas(16) float gamc[Cf::DK];                // gamma_C per key channel
+  alignas(16) float gamm[Cf::TOKM ? Cf::DK : 4];  // gamma_m (the Gram anchor) per key channel
   alignas(16) int bad[Cf::NP];                   // per producer wave: chunk must be stepped token by token
 };
 
@@ -714,47 +723,100 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
 
     floatx4 inc = pr, pre;
+    // factors of the operands (see the kernel's header): lam = gamma_t / gamma_m
+    // (left: keys and queries), mu = gamma_m / gamma_t (right: the Gram
+    // matrices' keys and erase keys), rho = gamma_C / gamma_t (the carry),
+    // as lam = gl[r] * cL, mu = sl[r] * cR, rho = sl[r] * post with the
+    // lane's prefix gl and suffix sl of its own tokens' decays
+    floatx4 cL, cR, post;
+    const floatx4 one = {1.f, 1.f, 1.f, 1.f};
+    bool lane_bad = false;
     if constexpr (TOKM) {
-      // earlier waves' totals (LDS, one step ahead), then the lower half's
-      // product for the upper half (lane exchange across the halves)
-      floatx4 pw = {1.f, 1.f, 1.f, 1.f};
+      // all waves' totals of this chunk (LDS, one step ahead) and the other
+      // lane half's product (lane exchange)
+      floatx4 tw[Cf::NP];
 #pragma unroll
-      for (int w2 = 0; w2 < Cf::NP - 1; ++w2)
-        if (w2 < wave) pw *= *reinterpret_cast<const floatx4 *>(&sm.tot[w2][ch0]);
+      for (int w2 = 0; w2 < Cf::NP; ++w2) tw[w2] = *reinterpret_cast<const floatx4 *>(&sm.tot[w2][ch0]);
       const floatx4 lo = shfl4(pr, lane ^ 32);
-      pre = rg ? pw * lo : pw;
-      inc = pre * pr;
-    } else if constexpr (RGE <= 16) {
-      // inclusive prefix product over the row groups (adjacent lanes): DPP
-      // row shifts when a quad's groups fit in one 16-lane row
-
-      static_for<4>([&](auto li) {
-        constexpr int d = 1 << decltype(li)::value;
-        if constexpr (d < RGE) {
-          floatx4 y;
+      constexpr int HW = Cf::NP / 2;  // waves of the first half (tokens 0 .. m)
+      floatx4 before = one, after = one, half_before = one, half_after = one;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = row_shr<d>(inc[e], 1.f);
+      for (int w2 = 0; w2 < Cf::NP; ++w2) {
+        if (w2 < wave) before *= tw[w2];
+        if (w2 > wave) after *= tw[w2];
+        // within the lane's own half of the chunk
+        if (w2 < wave && (w2 >= HW) == (wave >= HW)) half_before *= tw[w2];
+        if (w2 > wave && (w2 >= HW) == (wave >= HW)) half_after *= tw[w2];
+      }
+      pre = rg ? before * lo : before;   // tokens before the lane's first
+      post = rg ? after : lo * after;    // tokens after the lane's last
+      inc = pre * pr;
+      if (wave < HW) {  // t <= m: lam = 1 / (decays t+1 .. m), mu = decays t+1 .. m
+        const floatx4 p1 = rg ? half_after : lo * half_after;  // lane's last token .. m
+        const floatx4 x = pr * p1;
+        cL = floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
+                     __builtin_amdgcn_rcpf(x[3])};
+        cR = p1;
+      } else {  // t > m: lam = decays m+1 .. t, mu = 1 / lam
+        cL = rg ? half_before * lo : half_before;
+        const floatx4 x = pr * cL;
+        cR = floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
+                     __builtin_amdgcn_rcpf(x[3])};
+      }
+      // range of the factors: both half-chunk decays at least kMinHalfDecay
+      // (wave 0's first lane half holds every channel once)
+      if (wave == 0 && rg == 0) {
+        floatx4 h1 = one, h2 = one;
+#pragma unroll
+        for (int w2 = 0; w2 < Cf::NP; ++w2) {
+          if (w2 < HW) h1 *= tw[w2]; else h2 *= tw[w2];
+        }
+        lane_bad = !(h1[0] >= kMinHalfDecay) || !(h1[1] >= kMinHalfDecay) || !(h1[2] >= kMinHalfDecay) ||
+                   !(h1[3] >= kMinHalfDecay) || !(h2[0] >= kMinHalfDecay) || !(h2[1] >= kMinHalfDecay) ||
+                   !(h2[2] >= kMinHalfDecay) || !(h2[3] >= kMinHalfDecay);
+        *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = h1 * h2;
+        *reinterpret_cast<floatx4 *>(&cbuf.gamm[ch0]) = h1;
+      }
+    } else {
+      if constexpr (RGE <= 16) {
+        // inclusive prefix product over the row groups (adjacent lanes): DPP
+        // row shifts when a quad's groups fit in one 16-lane row
+        static_for<4>([&](auto li) {
+          constexpr int d = 1 << decltype(li)::value;
+          if constexpr (d < RGE) {
+            floatx4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = row_shr<d>(inc[e], 1.f);
+            if (rg >= d) inc *= y;
+          }
+        });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pre[e] = row_shr<1>(inc[e], 1.f);
+      } else {
+#pragma unroll
+        for (int d = 1; d < RGE; d <<= 1) {
+          const floatx4 y = shfl4(inc, lane - d);
           if (rg >= d) inc *= y;
         }
-      });
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pre[e] = row_shr<1>(inc[e], 1.f);
-    } else {
-#pragma unroll
-      for (int d = 1; d < RGE; d <<= 1) {
-        const floatx4 y = shfl4(inc, lane - d);
-        if (rg >= d) inc *= y;
+        pre = shfl4(inc, lane - 1);
       }
-      pre = shfl4(inc, lane - 1);
+      if (rg == 0) pre = one;
+      // channel-major build: the anchor of the Gram matrices is the chunk
+      // start (lam = gamma_t, mu = 1 / gamma_t, rho = gamma_C / gamma_t),
+      // which bounds every factor by 1 / gamma_C: the whole chunk's decay is
+      // checked against kMinChunkDecay
+      const floatx4 gC = shfl4(inc, (lane / Cf::RGL) * Cf::RGL + (RGE - 1));  // gamma_C of the lane's quad
+      cL = pre;
+      cR = floatx4{__builtin_amdgcn_rcpf(inc[0]), __builtin_amdgcn_rcpf(inc[1]), __builtin_amdgcn_rcpf(inc[2]),
+                   __builtin_amdgcn_rcpf(inc[3])};
+      post = gC * cR;
+      const bool last = rg == RGE - 1;
+      lane_bad = last && (!(inc[0] >= kMinChunkDecay) || !(inc[1] >= kMinChunkDecay) ||
+                          !(inc[2] >= kMinChunkDecay) || !(inc[3] >= kMinChunkDecay));
+      if (last) *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = inc;
     }
-    if (!TOKM && rg == 0) pre = floatx4{1.f, 1.f, 1.f, 1.f};
-    // the lanes holding the chunk's last token hold gamma_C of their 4 channels
-    const bool last = TOKM ? (wave == Cf::NP - 1 && rg == 1) : rg == RGE - 1;
-    const bool lane_bad = last && (!(inc[0] >= kMinChunkDecay) || !(inc[1] >= kMinChunkDecay) ||
-                                   !(inc[2] >= kMinChunkDecay) || !(inc[3] >= kMinChunkDecay));
     const bool any_bad = __any(lane_bad);
     if (lane == 0) cbuf.bad[wave] = any_bad ? 1 : 0;
-    if (last) *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = inc;
     if constexpr (CPL) {  // beta of the lane's tokens, for the Gram tiles
       if (brow && cq == 0 && (TOKM || wave == 0)) {
 #pragma unroll
@@ -762,32 +824,31 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
     }
     if (brow) {
-      // 1/gamma on the lane's tokens from one reciprocal per channel: the
-      // lane's last cumulative decay (inc) times the decays after each token
-      const floatx4 ginc = {__builtin_amdgcn_rcpf(inc[0]), __builtin_amdgcn_rcpf(inc[1]),
-                            __builtin_amdgcn_rcpf(inc[2]), __builtin_amdgcn_rcpf(inc[3])};
-      floatx4 gis[RPG];
-      gis[RPG - 1] = ginc;
+      // suffix products of the lane's own decays: sl[r] = a_{r+1} ... a_{RPG-1}
+      floatx4 sl[RPG];
+      sl[RPG - 1] = one;
 #pragma unroll
-      for (int r = RPG - 2; r >= 0; --r) gis[r] = gis[r + 1] * ra[P][r + 1];
+      for (int r = RPG - 2; r >= 0; --r) sl[r] = sl[r + 1] * ra[P][r + 1];
       floatx4 kbq[4], bkq[4];
 #pragma unroll
       for (int r = 0; r < RPG; ++r) {
         const int tl = tb0 + r;
-        const floatx4 gm = pre * gl[r];
-        const floatx4 gi = gis[r];
+        const floatx4 lam = gl[r] * cL;
+        const floatx4 mu = sl[r] * cR;
+        const floatx4 rho = sl[r] * post;
         const floatx4 kv = quad_f(rk[P][r]);
         const floatx4 qv = quad_f(rq[P][r]);
-        const floatx4 kb = kv * gi;
-        const floatx4 bk = rb[P][r] * kb;
-        st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * gm);
-        st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * gm);
-        st4<LK, BF16>(sm.kbi, tl, ch0, kb);
-        st4<LK, BF16>(sm.kbi, C + tl, ch0, bk);
-        // transposed copy: 4 (or 2) consecutive tokens per channel at once
+        const floatx4 km = kv * mu;
+        const floatx4 kr = kv * rho;
+        const floatx4 bkr = rb[P][r] * kr;
+        st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * lam);
+        st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * lam);
+        st4<LK, BF16>(sm.kbi, tl, ch0, km);
+        st4<LK, BF16>(sm.kbi, C + tl, ch0, rb[P][r] * km);
+        // transposed carry operands: 4 (or 2) consecutive tokens per channel at once
         if constexpr (RPG % 4 == 0) {
-          kbq[r & 3] = kb;
-          bkq[r & 3] = bk;
+          kbq[r & 3] = kr;
+          bkq[r & 3] = bkr;
           if ((r & 3) == 3) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -799,17 +860,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           if (r & 1) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              st2<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 1, kbq[0][c], kb[c]);
-              st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bk[c]);
+              st2<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 1, kbq[0][c], kr[c]);
+              st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bkr[c]);
             }
           }
-          kbq[0] = kb;
-          bkq[0] = bk;
+          kbq[0] = kr;
+          bkq[0] = bkr;
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            st1<LT, BF16>(cbuf.kbiT, ch0 + c, tl, kb[c]);
-            st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bk[c]);
+            st1<LT, BF16>(cbuf.kbiT, ch0 + c, tl, kr[c]);
+            st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bkr[c]);
           }
         }
       }
@@ -1122,6 +1183,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         qf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, C + 16 * r + lc, pp, lg);
       }
     });
+    // gamma_m of this lane's state rows (the left operands carry gamma_t /
+    // gamma_m, so the state enters X and Y scaled by gamma_m)
+    floatx4 gmr[NRT];
+    if constexpr (Cf::TOKM) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) gmr[rt] = *reinterpret_cast<const floatx4 *>(&cbf.gamm[16 * rt + 4 * lg]);
+    }
     const int flags = cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3];
     __builtin_amdgcn_sched_barrier(0);
     // U of the consumed chunk (requested two steps ago) into the staging rows
@@ -1141,10 +1209,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       // X = (gamma * K) S0, Y = (gamma * Q) S0. Y is formed transposed
       // (operands swapped): lane (lc, lg) holds Y[t = lc] at columns
       // 4lg..4lg+3, the layout of the output store.
+      auto s_in = [&](int rt) { return Cf::TOKM ? S[rt] * gmr[rt] : S[rt]; };
       Pair<BF16> Sp[NKP];
 #pragma unroll
       for (int pp = 0; pp < NKP; ++pp)
-        Sp[pp] = Pair<BF16>{O::from_acc(S[2 * pp]), 2 * pp + 1 < NRT ? O::from_acc(S[(2 * pp + 1) % NRT]) : O::zero()};
+        Sp[pp] = Pair<BF16>{O::from_acc(s_in(2 * pp)),
+                            2 * pp + 1 < NRT ? O::from_acc(s_in((2 * pp + 1) % NRT)) : O::zero()};
 #pragma unroll
       for (int r = 0; r < NCH; ++r) {
         X[r] = zero4();
@@ -1218,16 +1288,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         }
       });
       otc = tc;
-      // S_C = diag(gamma_C) (S0 + (K/gamma)^T U - (beta/gamma)^T R): kbiT
-      // columns are [K part | beta part], K16 block kb pairs with U_kb or
-      // -R_(kb - NCH)
+      // S_C = diag(gamma_C) S0 + (rho K)^T U - (rho beta)^T R with
+      // rho_s = gamma_C / gamma_s <= 1 (the chunk-end anchor): kbiT columns
+      // are [K part | beta part], K16 block kb pairs with U_kb or -R_(kb - NCH)
       auto ub = [&](int kb) { return kb < NCH ? Uf[kb % NCH] : Rn[(kb - NCH) % NCH]; };
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        floatx4 acc = S[rt];
+        floatx4 acc = S[rt] * gc[rt];
 #pragma unroll
         for (int pp = 0; pp < NCH; ++pp) acc = mma<BF16>(acc, tf[rt][pp], Pair<BF16>{ub(2 * pp), ub(2 * pp + 1)});
-        S[rt] = acc * gc[rt];
+        S[rt] = acc;
       }
     }
     GDN2_MARK(5);

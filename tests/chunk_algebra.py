@@ -26,14 +26,28 @@ from __future__ import annotations
 import numpy as np
 
 
-def chunked_head(q, k, v, a, b, w, S0, C: int, anchored: bool = False):
+def bf16_round(x):
+    """Round to the nearest bfloat16 (ties to even), returned as float64."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def chunked_head(q, k, v, a, b, w, S0, C: int, anchored=False, operand_round=None):
     """One head: q, k, a, b [T, d_k]; v, w [T, d_v]; S0 [d_k, d_v] or None.
 
     anchored=False uses the exact per-channel ratio for every (t, s) pair.
-    anchored=True factors the ratio against the chunk start,
-    (k_t gamma_t) . (k_s / gamma_s), which is how the HIP prefill forms its
-    Gram matrices when the chunk's decay range allows it.
+    anchored=True (or "start") factors the ratio against the chunk start,
+    (k_t gamma_t) . (k_s / gamma_s). anchored="mid" factors it against the
+    middle of the chunk, m = C/2 - 1: left operands x_t gamma_t / gamma_m,
+    right operands y_s gamma_m / gamma_s, the state term as
+    (lam K)(diag(gamma_m) S), and the carry's operands rho_s = gamma_C /
+    gamma_s -- the factorisation the HIP prefill uses for d_k = 128.
+    operand_round, if given, is applied to every matrix-product operand
+    (e.g. bf16_round, as the MFMA operands are rounded).
     """
+    rnd = operand_round or (lambda x: x)
     q, k, v, a, b, w = (np.asarray(x, dtype=np.float64) for x in (q, k, v, a, b, w))
     T, dk = k.shape
     dv = v.shape[1]
@@ -49,6 +63,21 @@ def chunked_head(q, k, v, a, b, w, S0, C: int, anchored: bool = False):
         gam = np.exp(G)
         strict = np.tril(np.ones((L, L)), -1)
         incl = np.tril(np.ones((L, L)), 0)
+        if anchored == "mid":
+            m = min(C // 2, L) - 1
+            lam, mu = np.exp(G - G[m]), np.exp(G[m] - G)
+            Kl, Ql, Km, Bm = rnd(lam * K), rnd(lam * Q), rnd(mu * K), rnd(mu * beta)
+            Akk = (Kl @ Km.T) * strict
+            Akb = (Kl @ Bm.T) * strict
+            Mqk = (Ql @ Km.T) * incl
+            Mqb = (Ql @ Bm.T) * incl
+            Sg = rnd(gam[m][:, None] * S)
+            Ur = rnd(U)
+            R = np.linalg.solve(np.eye(L) + Akb, Kl @ Sg + Akk @ Ur)
+            o[sl] = Ql @ Sg + Mqk @ Ur - Mqb @ rnd(R)
+            rho = np.exp(G[-1][None, :] - G)
+            S = gam[-1][:, None] * S + rnd(rho * K).T @ Ur - rnd(rho * beta).T @ rnd(R)
+            continue
         if anchored:
             inv = np.exp(-G)
             Akk = ((gam * K) @ (inv * K).T) * strict
@@ -68,7 +97,7 @@ def chunked_head(q, k, v, a, b, w, S0, C: int, anchored: bool = False):
     return o, S
 
 
-def chunked_forward(q, k, v, a, b, w, S0, C: int, anchored: bool = False):
+def chunked_forward(q, k, v, a, b, w, S0, C: int, anchored=False, operand_round=None):
     """Full layout: q, k [B,T,H_qk,d_k]; v, w [B,T,H_v,d_v]; a, b [B,T,H_v,d_k]."""
     q, k, v, a, b, w = (np.asarray(x, dtype=np.float64) for x in (q, k, v, a, b, w))
     B, T, Hqk, dk = q.shape
@@ -81,5 +110,5 @@ def chunked_forward(q, k, v, a, b, w, S0, C: int, anchored: bool = False):
             g = h // G
             s0 = None if S0 is None else S0[n, h]
             o[n, :, h], ST[n, h] = chunked_head(q[n, :, g], k[n, :, g], v[n, :, h], a[n, :, h],
-                                                b[n, :, h], w[n, :, h], s0, C, anchored)
+                                                b[n, :, h], w[n, :, h], s0, C, anchored, operand_round)
     return o, ST

@@ -48,3 +48,19 @@ def gpu_prefill(td: dict, chunk: int, S_T=True):
     import gated_delta_rule_83_amd as g
     return g.chunk_forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td.get("S0"),
                            chunk=chunk, want_state=S_T)
+
+
+def per_head_normwise(x, ref, head_axes):
+    """Normwise error of every (sequence, head) slice: max|x - ref| / max|ref|
+    over the axes NOT in `head_axes` (e.g. head_axes=(0, 2) for [B, T, H, d]).
+    Returns (worst error, index of the worst slice, array of all errors)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        return float("inf"), None, None
+    red = tuple(i for i in range(x.ndim) if i not in head_axes)
+    num = np.max(np.abs(x - ref), axis=red)
+    den = np.maximum(np.max(np.abs(ref), axis=red), 1e-30)
+    err = num / den
+    idx = np.unravel_index(int(np.argmax(err)), err.shape)
+    return float(err[idx]), tuple(int(i) for i in idx), err

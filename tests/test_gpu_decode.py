@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_83_amd as g
 import oracle
 from gated_delta_rule_83_amd import inputs as gi
-from tests.parity import TOL, normwise, rand_inputs, to_np
+from tests.parity import TOL, normwise, per_head_normwise, rand_inputs, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -51,46 +51,52 @@ def test_config0_as_decode_steps():
     assert normwise(to_np(o), ref_o) <= 1e-4 and normwise(to_np(S), ref_S) <= 1e-4
 
 
-def _decode_workload(c, steps, heads):
-    """Run `steps` decode steps of workload c on the GPU; oracle on sampled (n, h)."""
+def _decode_workload(c, steps, seq_block=32):
+    """Run `steps` decode steps of workload c on the GPU, recording every
+    step's inputs and outputs; the oracle then runs every (sequence, head) as
+    a prefill over the step axis (in blocks of sequences to bound host
+    memory), and each (sequence, head) is held to the tolerance on its own."""
     S0 = gi.make_decode_state(c)
     S = torch.from_numpy(S0).to(DEV)
     rec = {k: [] for k in ("q", "k", "v", "a", "b", "w")}
     outs = []
-    ns = [n for n, _ in heads]
+    print(f"[decode {c.name}] {steps} steps of {c.B} sequences x {c.H_v} heads on the GPU", flush=True)
     for step in range(steps):
-        d = gi.make_decode_step(c, step)
+        td = gi.to_torch(gi.make_decode_step(c, step), c.dtype, DEV)
         for k_ in rec:
-            rec[k_].append(d[k_][ns])
-        td = gi.to_torch(d, c.dtype, DEV)
+            rec[k_].append(td[k_].cpu())
         o = g.decode_step(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], S)
-        outs.append(o[ns].cpu())
+        outs.append(o.cpu())
     torch.cuda.synchronize()
-    # sampled sequences as a prefill over the step axis
-    sub = {k_: np.concatenate(v_, axis=1) for k_, v_ in rec.items()}
-    sub_t = gi.to_torch(sub, c.dtype)
-    sub_t["S0"] = torch.from_numpy(S0[ns])
-    sel = [(i, h) for i, (_, h) in enumerate(heads)]
-    ref_o, ref_S = oracle.forward_heads(sub_t, sel)
-    o_all = torch.cat(outs, dim=1)  # [len(heads), steps, H, d_v]
-    worst = 0.0
-    for i, (n, h) in enumerate(heads):
-        eo = normwise(to_np(o_all[i, :, h]), ref_o[(i, h)])
-        es = normwise(to_np(S[n, h]), ref_S[(i, h)])
-        print(f"[decode {c.name} steps={steps}] (n={n}, h={h}) o err {eo:.3e}  S err {es:.3e}", flush=True)
-        worst = max(worst, eo, es)
-    assert worst <= TOL[c.dtype], worst
+    S_h = to_np(S)
+    o_all = torch.cat(outs, dim=1)  # [B, steps, H, d_v]
+    inp = {k_: torch.cat(v_, dim=1) for k_, v_ in rec.items()}
+    del rec, outs
+    worst_o = worst_s = 0.0
+    where = None
+    for n0 in range(0, c.B, seq_block):
+        n1 = min(c.B, n0 + seq_block)
+        blk = {k_: v_[n0:n1] for k_, v_ in inp.items()}
+        ref_o, ref_S = oracle.forward(blk["q"], blk["k"], blk["v"], blk["a"], blk["b"], blk["w"], S0[n0:n1])
+        eo, io, _ = per_head_normwise(to_np(o_all[n0:n1]), ref_o, (0, 2))
+        es, is_, _ = per_head_normwise(S_h[n0:n1], ref_S, (0, 1))
+        if max(eo, es) > max(worst_o, worst_s):
+            where = (n0 + io[0], io[1]) if eo >= es else (n0 + is_[0], is_[1])
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    print(f"[decode {c.name} steps={steps}] every (sequence, head): worst o err {worst_o:.3e}, "
+          f"worst S err {worst_s:.3e} (at {where})", flush=True)
+    assert max(worst_o, worst_s) <= TOL[c.dtype], (worst_o, worst_s, where)
 
 
 def test_decode_workload_scaled():
     c = gi.scaled(4, B=16)
-    _decode_workload(c, 64, [(0, 0), (5, 9), (15, 15)])
+    _decode_workload(c, 64)
 
 
 def test_decode_workload_full_1024_steps():
-    """Workload c4 as stated: 256 sequences x 16 heads, 1024 steps; sampled heads."""
+    """Workload c4 as stated: 256 sequences x 16 heads, 1024 steps; every head."""
     c = gi.config(4)
-    _decode_workload(c, c.decode_steps, [(0, 0), (100, 7), (255, 15)])
+    _decode_workload(c, c.decode_steps)
 
 
 @pytest.mark.parametrize("form,dtype,dk,dv", [("preact", "bf16", 128, 128), ("preact", "f32", 64, 32),

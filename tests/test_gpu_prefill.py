@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_83_amd as g
 import oracle
 from gated_delta_rule_83_amd import inputs as gi
-from tests.parity import TOL, gpu_prefill, normwise, rand_inputs, to_np
+from tests.parity import TOL, gpu_prefill, normwise, per_head_normwise, rand_inputs, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -331,40 +331,47 @@ def test_decode_steps_equal_prefill():
     assert normwise(to_np(S), to_np(S_pf)) < 1e-5
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled heads
+# ------------------------------------------------------------------ full-size workloads, every head
 
-def _full_size(cfg_index, heads):
+def _full_size(cfg_index):
+    """Workload cfg_index as stated, in the launch configuration the benchmark
+    times; the oracle runs every (sequence, value head) and each slice is
+    held to the tolerance on its own (per-(n, h) normwise), as is each whole
+    tensor."""
     c = gi.config(cfg_index)
     print(f"[full {c.name}] drawing inputs", flush=True)
     d = gi.make_inputs(c)
     td = gi.to_torch(d, c.dtype, DEV)
     del d
+    print(f"[full {c.name}] prefill on the GPU", flush=True)
     o, ST = gpu_prefill(td, c.chunk)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(ST).all()
-    sub = {k: (v if v is None else v[[n for n, _ in heads]].cpu()) for k, v in td.items()}
-    # re-index the sampled sequences 0..len-1 for the oracle
-    sel = [(i, h) for i, (_, h) in enumerate(heads)]
-    ref_o, ref_S = oracle.forward_heads(sub, sel)
-    worst = 0.0
-    for i, (n, h) in enumerate(heads):
-        eo = normwise(to_np(o[n, :, h]), ref_o[(i, h)])
-        es = normwise(to_np(ST[n, h]), ref_S[(i, h)])
-        print(f"[full {c.name}] head (n={n}, h={h}) o err {eo:.3e}  S_T err {es:.3e}", flush=True)
-        worst = max(worst, eo, es)
-    assert worst <= TOL[c.dtype], worst
+    o_h, ST_h = to_np(o), to_np(ST)
+    del o, ST
+    host = {k: (None if v is None else v.cpu()) for k, v in td.items()}
+    del td
+    torch.cuda.empty_cache()
+    print(f"[full {c.name}] oracle on all {c.B * c.H_v} (sequence, head) pairs", flush=True)
+    ref_o, ref_S = oracle.forward(host["q"], host["k"], host["v"], host["a"], host["b"], host["w"], host["S0"])
+    eo_all, es_all = normwise(o_h, ref_o), normwise(ST_h, ref_S)
+    eo, io, _ = per_head_normwise(o_h, ref_o, (0, 2))
+    es, is_, _ = per_head_normwise(ST_h, ref_S, (0, 1))
+    print(f"[full {c.name}] o err {eo_all:.3e} (worst head {io}: {eo:.3e})  "
+          f"S_T err {es_all:.3e} (worst head {is_}: {es:.3e})", flush=True)
+    assert max(eo, es, eo_all, es_all) <= TOL[c.dtype], (eo, io, es, is_)
 
 
-def test_full_config1_sampled_heads():
-    _full_size(1, [(0, 0), (3, 7), (7, 15)])
+def test_full_config1_all_heads():
+    _full_size(1)
 
 
-def test_full_config2_sampled_heads():
-    _full_size(2, [(0, 0), (0, 11)])
+def test_full_config2_all_heads():
+    _full_size(2)
 
 
-def test_full_config3_sampled_heads():
-    _full_size(3, [(0, 0), (1, 1), (3, 30)])
+def test_full_config3_all_heads():
+    _full_size(3)
 
 
 # ------------------------------------------------------------------ gate pre-activations (fused activation)
@@ -421,21 +428,18 @@ def test_preact_split_sequence(monkeypatch):
     _preact_compare(gi.make_preact_inputs(c), "bf16", 64, "split3")
 
 
-def test_preact_full_layer_shape_sampled_heads():
-    """B8 T4096 H16 d128 bf16 with pre-activation gates: two sampled heads."""
+def test_preact_full_layer_shape_all_heads():
+    """B8 T4096 H16 d128 bf16 with pre-activation gates: every (sequence, head)."""
     c = gi.config(1)
     d = gi.make_preact_inputs(c)
     td = gi.to_torch_preact(d, "bf16", DEV)
     o, ST = g.chunk_forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], None, chunk=64)
     torch.cuda.synchronize()
-    for (n, h) in ((0, 0), (5, 11)):
-        sl = lambda x: x[n:n + 1, :, h:h + 1]
-        ref_o, ref_S = oracle.forward_preact(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]),
-                                             sl(td["w"]), None)
-        eo = normwise(to_np(sl(o)), ref_o)
-        es = normwise(to_np(ST[n:n + 1, h:h + 1]), ref_S)
-        print(f"[preact full n{n} h{h}] o err {eo:.3e} S_T err {es:.3e}", flush=True)
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+    ref_o, ref_S = oracle.forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], None)
+    eo, io, _ = per_head_normwise(to_np(o), ref_o, (0, 2))
+    es, is_, _ = per_head_normwise(to_np(ST), ref_S, (0, 1))
+    print(f"[preact full] worst head o err {eo:.3e} at {io}, S_T err {es:.3e} at {is_}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, io, es, is_)
 
 
 @pytest.mark.parametrize("form,dtype", [("preact", "bf16"), ("preact", "f32"), ("coupled", "bf16"),
