@@ -35,6 +35,8 @@ GDN2_ERR_BAD_DTYPE = 4
 GDN2_ERR_WORKSPACE = 5
 GDN2_ERR_HIP = 6
 GDN2_ERR_ALIAS = 7
+GDN2_ERR_SCRATCH = 8
+GDN2_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 GDN2_F32 = 0
 GDN2_BF16 = 1
@@ -42,7 +44,8 @@ GDN2_BF16 = 1
 EXPORTED = ("gdn2_chunk_forward", "gdn2_chunk_forward_coupled", "gdn2_chunk_forward_scalar",
             "gdn2_chunk_forward_preact",
             "gdn2_chunk_forward_varlen", "gdn2_decode_step",
-            "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_forward_plan", "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
+            "gdn2_chunk_forward_workspace_bytes", "gdn2_chunk_forward_plan", "gdn2_chunk_forward_noalloc",
+            "gdn2_chunk_backward", "gdn2_chunk_backward_workspace_bytes",
             "gdn2_chunk_backward_varlen", "gdn2_chunk_backward_varlen_workspace_bytes", "gdn2_chunk_backward_preact",
             "gdn2_chunk_backward_coupled", "gdn2_chunk_backward_scalar", "gdn2_chunk_forward_varlen_gates",
             "gdn2_chunk_backward_varlen_gates", "gdn2_decode_step_gates",
@@ -76,6 +79,8 @@ def load(path: Optional[str] = None):
     vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(gdn2_desc)
     lib.gdn2_chunk_forward.restype = ctypes.c_int
     lib.gdn2_chunk_forward.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
+    lib.gdn2_chunk_forward_noalloc.restype = ctypes.c_int
+    lib.gdn2_chunk_forward_noalloc.argtypes = [dp] + [vp] * 9 + [vp]
     lib.gdn2_chunk_forward_preact.restype = ctypes.c_int
     lib.gdn2_chunk_forward_preact.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
     lib.gdn2_chunk_forward_coupled.restype = ctypes.c_int
@@ -148,6 +153,11 @@ def gdn2_chunk_forward(desc, q, k, v, a, b, w, S0, o, S_T, workspace=0, workspac
                        stream=0) -> int:
     return load().gdn2_chunk_forward(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w,
                                      S0, o, S_T, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_forward_noalloc(desc, q, k, v, a, b, w, S0, o, S_T, stream=0) -> int:
+    return load().gdn2_chunk_forward_noalloc(None if desc is None else ctypes.byref(desc), q, k, v, a, b, w, S0,
+                                             o, S_T, stream)
 
 
 def gdn2_chunk_forward_preact(desc, q, k, v, a_pre, b_pre, w_pre, S0, o, S_T, workspace=0, workspace_bytes=0,

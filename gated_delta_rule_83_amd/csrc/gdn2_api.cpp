@@ -65,6 +65,7 @@ const char *gdn2_status_string(gdn2_status s) {
     case GDN2_ERR_WORKSPACE: return "workspace too small";
     case GDN2_ERR_HIP: return "HIP runtime error at launch";
     case GDN2_ERR_ALIAS: return "output or workspace overlaps an input, the state or each other";
+    case GDN2_ERR_SCRATCH: return "the problem needs more scratch than the allocation-free entry point's static buffer";
   }
   return "unknown status";
 }

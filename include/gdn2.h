@@ -66,7 +66,9 @@ typedef enum {
   GDN2_ERR_BAD_DTYPE = 4,    /* dtype is neither GDN2_F32 nor GDN2_BF16 */
   GDN2_ERR_WORKSPACE = 5,    /* workspace smaller than gdn2_chunk_forward_workspace_bytes() */
   GDN2_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
-  GDN2_ERR_ALIAS = 7         /* o or the workspace overlaps an input, the state or each other */
+  GDN2_ERR_ALIAS = 7,        /* o or the workspace overlaps an input, the state or each other */
+  GDN2_ERR_SCRATCH = 8       /* gdn2_chunk_forward_noalloc: the problem needs more scratch than
+                                GDN2_NOALLOC_SCRATCH_BYTES */
 } gdn2_status;
 
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
@@ -124,6 +126,30 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void 
                                const float *a, const float *b, const float *w, const float *S0,
                                void *o, float *S_T, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* Bytes of the static device scratch of gdn2_chunk_forward_noalloc (64 MiB).
+ * Each device that runs the library holds one such array until the process
+ * ends. */
+#define GDN2_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* gdn2_chunk_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): it allocates nothing and calls no
+ * allocating routine. Same arguments, results and errors as
+ * gdn2_chunk_forward (and bit for bit the same results: the same kernels
+ * and plan); the scratch that a split of long sequences needs
+ * (gdn2_chunk_forward_workspace_bytes(desc)) is taken from a static device
+ * array of GDN2_NOALLOC_SCRATCH_BYTES per device, whose address is looked up
+ * on the first call on each device. Problems that need more scratch than
+ * that (e.g. very many sequence segments forced with GDN2_PREFILL_SPLIT)
+ * return GDN2_ERR_SCRATCH before anything is enqueued; problems that need
+ * none never touch the array. The array is shared by every call on a device
+ * and keeps the last call's contents: calls of this entry point that overlap
+ * in time on one device (other streams, other host threads) race on it and
+ * must be serialised by the caller. Nothing in it needs to start cleared. */
+gdn2_status gdn2_chunk_forward_noalloc(const gdn2_desc *desc, const void *q, const void *k, const void *v,
+                                       const float *a, const float *b, const float *w, const float *S0,
+                                       void *o, float *S_T, void *stream);
 
 /* Prefill with coupled gates: the erase gate and the write gate are one
  * scalar per token and value head, b_t = w_t = beta_t (all channels): the

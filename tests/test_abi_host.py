@@ -29,8 +29,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert g.gdn2_version() == 10000
-    for s in range(8):
-        assert g.gdn2_status_string(s)
+    for s in range(9):
+        assert g.gdn2_status_string(s) != "unknown status", s
     assert g.gdn2_status_string(99) == "unknown status"
 
 
@@ -438,3 +438,18 @@ def test_binding_exposes_every_entry_point_wrapper():
                  "gated_delta_rule_preact", "gated_delta_rule_coupled", "gated_delta_rule_scalar",
                  "gated_delta_rule_varlen", "decode_step"):
         assert callable(getattr(g, name, None)), name
+
+
+def test_noalloc_argument_errors_and_scratch_limit(monkeypatch):
+    """gdn2_chunk_forward_noalloc reports the forward's argument errors, and
+    refuses a problem whose split scratch exceeds its static buffer, before
+    any HIP call (no GPU needed)."""
+    p = _ptrs()
+    noalloc = lambda desc, ptrs=p: g.gdn2_chunk_forward_noalloc(desc, *ptrs[:9], 0)
+    assert noalloc(None) == g.GDN2_ERR_NULL_POINTER
+    assert noalloc(g.make_desc(2, 64, 2, 4, 128, 128, 64, 7)) == g.GDN2_ERR_BAD_DTYPE
+    assert noalloc(g.make_desc(2, 64, 2, 4, 96, 128, 64, 1)) == g.GDN2_ERR_UNSUPPORTED
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "64")
+    big = g.make_desc(1, 64 * 64, 32, 32, 128, 128, 64, g.GDN2_BF16)
+    assert g.gdn2_chunk_forward_workspace_bytes(big) > g.GDN2_NOALLOC_SCRATCH_BYTES
+    assert noalloc(big) == g.GDN2_ERR_SCRATCH
