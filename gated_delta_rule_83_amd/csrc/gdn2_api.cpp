@@ -88,17 +88,24 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
                              int form);
 
 // gdn2_chunk_forward and gdn2_chunk_forward_preact: per-channel gates, fp32
-// activated values or pre-activations in the input dtype.
+// activated values or pre-activations in the input dtype. ws_cap: largest
+// workspace the split may plan for (0: no limit).
 gdn2_status forward_general(const gdn2_desc *d, const void *q, const void *k, const void *v, const void *a,
                             const void *b, const void *w, const float *S0, void *o, float *S_T, void *workspace,
-                            size_t workspace_bytes, void *stream, bool preact);
+                            size_t workspace_bytes, void *stream, bool preact, size_t ws_cap = 0);
+
+size_t workspace_bytes_capped(const gdn2_desc *desc, size_t ws_cap) {
+  if (check_desc(desc, false) != GDN2_OK) return 0;
+  gdn2::PrefillArgs a = prefill_args(desc);
+  a.ws_cap = ws_cap;
+  return gdn2::prefill_plan(a).ws_bytes;
+}
 
 }  // namespace
 
 size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc) {
-  if (check_desc(desc, false) != GDN2_OK) return 0;
   // nonzero only when long sequences are split across workgroups
-  return gdn2::prefill_plan(prefill_args(desc)).ws_bytes;
+  return workspace_bytes_capped(desc, 0);
 }
 
 gdn2_status gdn2_chunk_forward_plan(const gdn2_desc *desc, int32_t *chunk_run, int32_t *segments) {
@@ -130,10 +137,10 @@ namespace {
 
 gdn2_status forward_general(const gdn2_desc *d, const void *q, const void *k, const void *v, const void *a,
                             const void *b, const void *w, const float *S0, void *o, float *S_T, void *workspace,
-                            size_t workspace_bytes, void *stream, bool preact) {
+                            size_t workspace_bytes, void *stream, bool preact, size_t ws_cap) {
   gdn2_status st = check_desc(d, false);
   if (st != GDN2_OK) return st;
-  const size_t ws_need = gdn2_chunk_forward_workspace_bytes(d);
+  const size_t ws_need = workspace_bytes_capped(d, ws_cap);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return GDN2_ERR_WORKSPACE;
   const size_t B = (size_t)d->B, T = (size_t)d->T, Hqk = (size_t)d->H_qk, Hv = (size_t)d->H_v;
   const size_t dk = (size_t)d->d_k, dv = (size_t)d->d_v;
@@ -175,11 +182,28 @@ gdn2_status forward_general(const gdn2_desc *d, const void *q, const void *k, co
   p.preact = preact;
   p.workspace = workspace;
   p.workspace_bytes = workspace_bytes;
+  p.ws_cap = ws_cap;
   const hipError_t e = gdn2::launch_prefill(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
 }  // namespace
+
+namespace gdn2 {
+
+// gdn2_chunk_forward with the split planned within a workspace of at most
+// ws_cap bytes (the allocation-free entry point's static scratch).
+size_t chunk_forward_workspace_capped(const gdn2_desc *desc, size_t ws_cap) {
+  return workspace_bytes_capped(desc, ws_cap);
+}
+
+gdn2_status chunk_forward_capped(const gdn2_desc *d, const void *q, const void *k, const void *v, const float *a,
+                                 const float *b, const float *w, const float *S0, void *o, float *S_T,
+                                 void *workspace, size_t workspace_bytes, size_t ws_cap, void *stream) {
+  return forward_general(d, q, k, v, a, b, w, S0, o, S_T, workspace, workspace_bytes, stream, false, ws_cap);
+}
+
+}  // namespace gdn2
 
 
 namespace {

@@ -134,6 +134,12 @@ template <> struct Op<false> {
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// K32 operand: the fragments of two consecutive K16 blocks.
+template <bool BF16>
+struct Pair {
+  typename Op<BF16>::Frag lo, hi;
+};
+
 // ---------------------------------------------------------------- buffer access
 // Raw buffer loads/stores: a wave-uniform base (the descriptor, in SGPRs), a
 // per-lane 32-bit byte offset (VGPR) and a wave-uniform byte offset (SGPR).

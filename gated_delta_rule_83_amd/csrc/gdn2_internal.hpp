@@ -52,6 +52,9 @@ struct PrefillArgs {
   // state after segment s for s < nseg - 1; no outputs, no S_T; the
   // workspace holds the transition matrices (nseg * B * H_v * d_k^2 floats)
   float *seg_states;
+  // largest workspace the split may use (0: no limit); a split whose
+  // output-correction form needs more runs its segments a second time instead
+  size_t ws_cap;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one
@@ -61,6 +64,10 @@ struct PrefillArgs {
 struct PrefillPlan {
   int chunk, nseg, seg_len;
   size_t ws_bytes;
+  // split form: true = outputs corrected from the identity columns' query
+  // reads (one pass over the segments), false = segments run again from
+  // their exact entering states
+  bool correct;
 };
 
 // Thresholds on the decay per key channel above which the chunk-parallel form
@@ -71,6 +78,10 @@ struct PrefillPlan {
 // scale factor stays below e^60.
 constexpr float kMinChunkDecay = 8.75651076e-27f;  // e^-60
 constexpr float kMinHalfDecay = 8.75651076e-27f;   // e^-60
+// per-chunk path of the prefill (flags of a chunk buffer): the chunk-start
+// anchor (0), the middle-token anchor, or token by token
+constexpr int kChunkSteps = 1;
+constexpr int kChunkMid = 2;
 
 // Backward pass (gradients of the recurrence); see gdn2_chunk_backward.
 struct BackwardArgs {
@@ -118,11 +129,17 @@ size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream);
 PrefillPlan prefill_plan(const PrefillArgs &p);
-// Split-sequence hand-off: for j = 1 .. nseg - 2 in order,
+// Split-sequence hand-off: for j = 1 .. jlast in order,
 // state[j] = trans[j] * state[j - 1] + state[j] per (sequence, head), where
-// state is [nseg][BH][d_k][d_v] and trans [nseg][BH][d_k][d_k], fp32.
-hipError_t launch_split_combine(float *state, const float *trans, int nseg, int BH, int d_k, int d_v,
-                                hipStream_t stream);
+// state is [nseg][BH][d_k][d_v] and trans [nseg][BH][d_k][d_k], fp32; then
+// state[jlast] is also written to S_T ([BH][d_k][d_v]) if S_T is not null.
+hipError_t launch_split_combine(float *state, const float *trans, int jlast, int BH, int d_k, int d_v,
+                                float *S_T, hipStream_t stream);
+// Output correction of split sequences (segments 1 .. nseg - 1 of B
+// sequences of T tokens): o_t += oI_t . state[s - 1] per (sequence, value
+// head), with oI [B*T][H_v][d_k] and o [B*T][H_v][d_v] in the input dtype.
+hipError_t launch_split_correct(void *o, const void *oI, const float *state, int B, int T, int H_v, int d_k,
+                                int d_v, int seg_len, int nseg, bool bf16, hipStream_t stream);
 // Workgroup column width the prefill would use (for tests and tuning).
 int prefill_pick_nct(int B, int H_v, int d_v);
 

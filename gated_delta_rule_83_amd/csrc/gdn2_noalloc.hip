@@ -43,11 +43,21 @@ gdn2_status scratch_on(int dev, void **out) {
 
 }  // namespace
 
+namespace gdn2 {
+size_t chunk_forward_workspace_capped(const gdn2_desc *desc, size_t ws_cap);
+gdn2_status chunk_forward_capped(const gdn2_desc *d, const void *q, const void *k, const void *v, const float *a,
+                                 const float *b, const float *w, const float *S0, void *o, float *S_T,
+                                 void *workspace, size_t workspace_bytes, size_t ws_cap, void *stream);
+}  // namespace gdn2
+
 extern "C" gdn2_status gdn2_chunk_forward_noalloc(const gdn2_desc *d, const void *q, const void *k, const void *v,
                                                   const float *a, const float *b, const float *w, const float *S0,
                                                   void *o, float *S_T, void *stream) {
-  // 0 for an invalid description too: gdn2_chunk_forward then reports it
-  const size_t need = gdn2_chunk_forward_workspace_bytes(d);
+  // The split is planned within the scratch: the form whose workspace fits
+  // (the output correction needs a row of d_k per token, so long problems
+  // run their segments a second time instead). 0 for an invalid
+  // description too: the forward then reports it.
+  const size_t need = gdn2::chunk_forward_workspace_capped(d, kScratchBytes);
   if (need > kScratchBytes) return GDN2_ERR_SCRATCH;
   void *ws = nullptr;
   if (need > 0) {
@@ -62,5 +72,6 @@ extern "C" gdn2_status gdn2_chunk_forward_noalloc(const gdn2_desc *d, const void
   // Every piece of the split's scratch is written before it is read (each
   // segment's state and transition by the first pass), so nothing needs
   // clearing between calls.
-  return gdn2_chunk_forward(d, q, k, v, a, b, w, S0, o, S_T, ws, need > 0 ? kScratchBytes : 0, stream);
+  return gdn2::chunk_forward_capped(d, q, k, v, a, b, w, S0, o, S_T, ws, need > 0 ? kScratchBytes : 0, kScratchBytes,
+                                    stream);
 }

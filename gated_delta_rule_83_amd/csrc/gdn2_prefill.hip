@@ -2,6 +2,7 @@
 // the hand-off kernel of split sequences.
 #include <stdlib.h>
 
+#include "gdn2_device.hpp"
 #include "gdn2_internal.hpp"
 
 namespace gdn2 {
@@ -55,11 +56,12 @@ hipError_t dispatch(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only
 
 // One workgroup per (sequence-head, block of CB state columns); thread
 // (row i = tid / 2, half = tid % 2) owns columns half * CB/2 .. +CB/2 of row i.
-// The running state block stays in LDS; the transition rows are read from
-// memory (each row by two threads).
+// The running state block stays in LDS; each thread holds its row of the
+// next transition matrix in registers, requested one step ahead (16-byte
+// loads), so the sequential steps wait on arithmetic, not on memory.
 template <int CB>
-__global__ __launch_bounds__(256) void split_combine_kernel(float *state, const float *trans, int nseg,
-                                                             int BH, int d_k, int d_v) {
+__global__ __launch_bounds__(256) void split_combine_kernel(float *state, const float *trans, int jlast,
+                                                             int BH, int d_k, int d_v, float *S_T) {
   constexpr int CH = CB / 2;
   __shared__ __attribute__((aligned(16))) float X[128][CB + 4];  // 16-byte rows, 4 banks apart
   const int nblk = d_v / CB;
@@ -70,17 +72,32 @@ __global__ __launch_bounds__(256) void split_combine_kernel(float *state, const 
   const size_t s_row = ((size_t)bh * d_k + i) * d_v + c0 + half * CH;
   if (row)
     for (int c = 0; c < CH; ++c) X[i][half * CH + c] = state[s_row + c];
-  for (int j = 1; j + 1 < nseg; ++j) {
+  const int nk4 = d_k / 4;  // d_k is a multiple of 16
+  floatx4 m[32];
+  auto load_row = [&](int j) {
+    const floatx4 *src = reinterpret_cast<const floatx4 *>(trans + j * strans + ((size_t)bh * d_k + (row ? i : 0)) * d_k);
+#pragma unroll
+    for (int k4 = 0; k4 < 32; ++k4) m[k4] = k4 < nk4 ? src[k4] : zero4();
+  };
+  if (jlast >= 1) load_row(1);
+  for (int j = 1; j <= jlast; ++j) {
     __syncthreads();
     float acc[CH];
-    const float *m = trans + j * strans + ((size_t)bh * d_k + i) * d_k;
-    if (row) {
+    if (row)
       for (int c = 0; c < CH; ++c) acc[c] = state[j * sstate + s_row + c];
-      for (int k = 0; k < d_k; ++k) {
-        const float mk = m[k];
-        for (int c = 0; c < CH; ++c) acc[c] = fmaf(mk, X[k][half * CH + c], acc[c]);
+#pragma unroll
+    for (int k4 = 0; k4 < 32; ++k4) {
+      if (k4 < nk4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float mk = m[k4][e];
+          const float *xr = &X[4 * k4 + e][half * CH];
+#pragma unroll
+          for (int c = 0; c < CH; ++c) acc[c] = fmaf(mk, xr[c], acc[c]);
+        }
       }
     }
+    if (j < jlast) load_row(j + 1);
     __syncthreads();
     if (row)
       for (int c = 0; c < CH; ++c) {
@@ -88,21 +105,187 @@ __global__ __launch_bounds__(256) void split_combine_kernel(float *state, const 
         state[j * sstate + s_row + c] = acc[c];
       }
   }
+  __syncthreads();
+  // the state after segment jlast, [BH][d_k][d_v]
+  if (S_T && row)
+    for (int c = 0; c < CH; ++c) S_T[s_row + c] = X[i][half * CH + c];
+}
+
+// Output correction of split sequences: a segment run from a zero entering
+// state wrote o_zero_t = (S^0_t)^T q_t, and its identity columns the
+// transition's query reads oI_t = (Phi_t)^T q_t; with the segment's exact
+// entering state S_in the output is o_t = o_zero_t + S_in^T oI_t, because
+// the state after t is Phi_t S_in + S^0_t (the recurrence is linear in the
+// state, column by column). Per (segment s >= 1, sequence, value head, slab
+// of tokens), four waves of 16-token tiles: out^T = S_in^T oI^T as MFMA
+// tiles (rows = output columns, columns = tokens), S_in^T held in registers
+// as A fragments, oI rows read as B fragments; then o += out.
+// K slots: slot j of lane group g in K32 step p is key channel 32p + 8g + j
+// for both operands. Output rows: row 4g + j of tile 2q + h is column
+// 32q + 8g + 4h + j, so that lane (token c, g) holds columns 32q + 8g .. +7
+// of its token for q = 0 .. DV/32 - 1 (16 contiguous bytes in bf16) and the
+// four lanes of a token cover 64 contiguous bytes per access.
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(256) void split_correct_kernel(void *o_, const void *oI_, const float *state, int B,
+                                                             int T, int H_v, int seg_len, int nseg, int slab) {
+  using E = Elem<BF16>;
+  using O = Op<BF16>;
+  using ET = typename E::T;
+  typedef typename O::T OT;
+  constexpr int NCT = DV / 16, NKP = (DK + 31) / 32;
+  const int nslab = (seg_len + slab - 1) / slab;
+  int idx = blockIdx.x;
+  const int sl = idx % nslab;
+  idx /= nslab;
+  const int h = idx % H_v;
+  idx /= H_v;
+  const int n = idx % B;
+  const int s = 1 + idx / B;  // segment (>= 1)
+  const int t_beg = s * seg_len + sl * slab;
+  const int t_end = min(min(t_beg + slab, (s + 1) * seg_len), T);
+  if (s >= nseg || t_beg >= t_end) return;
+  const float *Sin = state + (((size_t)(s - 1) * B + n) * H_v + h) * (size_t)(DK * DV);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  auto frag8 = [](const float (&x)[8]) {
+    typename O::Frag lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = O::cvt(x[j]);
+      hi[j] = O::cvt(x[4 + j]);
+    }
+    return Pair<BF16>{lo, hi};
+  };
+  // output column of row r of tile ct
+  auto ocol = [](int ct, int r) { return DV >= 32 ? 32 * (ct >> 1) + 8 * (r >> 2) + 4 * (ct & 1) + (r & 3) : r; };
+  Pair<BF16> sa[NCT][NKP];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = 32 * p + 8 * g + j;
+        x[j] = k < DK ? Sin[(size_t)k * DV + ocol(ct, c)] : 0.f;
+      }
+      sa[ct][p] = frag8(x);
+    }
+  const size_t row0 = (size_t)n * T;  // token index of the sequence's first token
+  const ET *oIh = static_cast<const ET *>(oI_) + (size_t)h * DK;
+  ET *oh = static_cast<ET *>(o_) + (size_t)h * DV;
+  for (int t0 = t_beg + 16 * wave; t0 < t_end; t0 += 64) {
+    const int t = t0 + c;
+    const bool ok = t < t_end;
+    // B fragments: 8 consecutive key channels of token t per K32 step, one
+    // 16-byte (bf16) or two (fp32) loads
+    const ET *src = oIh + (row0 + (ok ? t : t_beg)) * (size_t)H_v * DK;
+    Pair<BF16> b[NKP];
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+      const int k0 = 32 * p + 8 * g;
+      const bool in = ok && k0 < DK;
+      if constexpr (BF16) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 raw = in ? *reinterpret_cast<const u32x4 *>(src + k0) : u32x4{0u, 0u, 0u, 0u};
+        b[p].lo = __builtin_bit_cast(typename O::Frag, uint2{raw.x, raw.y});
+        b[p].hi = __builtin_bit_cast(typename O::Frag, uint2{raw.z, raw.w});
+      } else {
+        b[p].lo = in ? *reinterpret_cast<const floatx4 *>(src + k0) : zero4();
+        b[p].hi = in ? *reinterpret_cast<const floatx4 *>(src + k0 + 4) : zero4();
+      }
+    }
+    ET *dst = oh + (row0 + (ok ? t : t_beg)) * (size_t)H_v * DV;
+    auto tile = [&](int ct) {
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < NKP; ++p) acc = O::mma32(acc, sa[ct][p].lo, sa[ct][p].hi, b[p].lo, b[p].hi);
+      return acc;
+    };
+    if constexpr (DV >= 32) {
+      // columns 32 q + 8 g .. +7: tiles 2q (first four) and 2q + 1
+#pragma unroll
+      for (int q = 0; q < DV / 32; ++q) {
+        floatx4 acc[NCT];
+        acc[2 * q] = tile(2 * q);
+        acc[2 * q + 1] = tile(2 * q + 1);
+        if (ok) {
+          ET *d = dst + 32 * q + 8 * g;
+          if constexpr (BF16) {
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 u = *reinterpret_cast<const u32x4 *>(d);
+            const floatx4 lo = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+            const floatx4 hi = {__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
+                                __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)};
+            const uint2 a = __builtin_bit_cast(uint2, __builtin_convertvector(lo + acc[2 * q], bf16x4));
+            const uint2 b2 = __builtin_bit_cast(uint2, __builtin_convertvector(hi + acc[2 * q + 1], bf16x4));
+            *reinterpret_cast<u32x4 *>(d) = u32x4{a.x, a.y, b2.x, b2.y};
+          } else {
+            floatx4 *df = reinterpret_cast<floatx4 *>(d);
+            df[0] = df[0] + acc[2 * q];
+            df[1] = df[1] + acc[2 * q + 1];
+          }
+        }
+      }
+    } else {  // DV = 16: rows are the columns
+      const floatx4 acc = tile(0);
+      if (ok) {
+        ET *d = dst + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) E::st(d + j, E::ld(d + j) + acc[j]);
+      }
+    }
+  }
+  (void)sizeof(OT);
+}
+
+template <int DK, bool BF16>
+hipError_t launch_correct_dv(void *o, const void *oI, const float *state, int B, int T, int H_v, int d_v,
+                             int seg_len, int nseg, hipStream_t st) {
+  const int slab = 1024;
+  const int nslab = (seg_len + slab - 1) / slab;
+  const dim3 grid((unsigned)((nseg - 1) * B * H_v * nslab));
+  switch (d_v) {
+    case 16: hipLaunchKernelGGL((split_correct_kernel<DK, 16, BF16>), grid, dim3(256), 0, st, o, oI, state, B, T, H_v, seg_len, nseg, slab); break;
+    case 32: hipLaunchKernelGGL((split_correct_kernel<DK, 32, BF16>), grid, dim3(256), 0, st, o, oI, state, B, T, H_v, seg_len, nseg, slab); break;
+    case 64: hipLaunchKernelGGL((split_correct_kernel<DK, 64, BF16>), grid, dim3(256), 0, st, o, oI, state, B, T, H_v, seg_len, nseg, slab); break;
+    case 128: hipLaunchKernelGGL((split_correct_kernel<DK, 128, BF16>), grid, dim3(256), 0, st, o, oI, state, B, T, H_v, seg_len, nseg, slab); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_correct_dk(void *o, const void *oI, const float *state, int B, int T, int H_v, int d_k, int d_v,
+                             int seg_len, int nseg, hipStream_t st) {
+  switch (d_k) {
+    case 16: return launch_correct_dv<16, BF16>(o, oI, state, B, T, H_v, d_v, seg_len, nseg, st);
+    case 32: return launch_correct_dv<32, BF16>(o, oI, state, B, T, H_v, d_v, seg_len, nseg, st);
+    case 64: return launch_correct_dv<64, BF16>(o, oI, state, B, T, H_v, d_v, seg_len, nseg, st);
+    case 128: return launch_correct_dv<128, BF16>(o, oI, state, B, T, H_v, d_v, seg_len, nseg, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_split_combine(float *state, const float *trans, int nseg, int BH, int d_k, int d_v,
-                                hipStream_t st) {
-  if (nseg < 3 || BH == 0) return hipSuccess;
+hipError_t launch_split_combine(float *state, const float *trans, int jlast, int BH, int d_k, int d_v,
+                                float *S_T, hipStream_t st) {
+  if ((jlast < 1 && !S_T) || BH == 0) return hipSuccess;
   if (d_k > 128) return hipErrorInvalidValue;
-  if (d_v % 32 == 0)
-    hipLaunchKernelGGL((split_combine_kernel<32>), dim3(BH * (d_v / 32)), dim3(256), 0, st, state, trans, nseg,
-                       BH, d_k, d_v);
-  else
-    hipLaunchKernelGGL((split_combine_kernel<16>), dim3(BH * (d_v / 16)), dim3(256), 0, st, state, trans, nseg,
-                       BH, d_k, d_v);
+  // narrow column blocks: many workgroups, each step short (the steps are
+  // sequential, the column blocks independent)
+  hipLaunchKernelGGL((split_combine_kernel<8>), dim3(BH * (d_v / 8)), dim3(256), 0, st, state, trans, jlast, BH,
+                     d_k, d_v, S_T);
   return hipGetLastError();
+}
+
+hipError_t launch_split_correct(void *o, const void *oI, const float *state, int B, int T, int H_v, int d_k,
+                                int d_v, int seg_len, int nseg, bool bf16, hipStream_t st) {
+  if (nseg < 2 || B == 0 || H_v == 0) return hipSuccess;
+  return bf16 ? launch_correct_dk<true>(o, oI, state, B, T, H_v, d_k, d_v, seg_len, nseg, st)
+              : launch_correct_dk<false>(o, oI, state, B, T, H_v, d_k, d_v, seg_len, nseg, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
@@ -111,9 +294,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
 }
 
 PrefillPlan prefill_plan(const PrefillArgs &a) {
-  PrefillPlan pl{a.chunk, 1, a.T, 0};
+  PrefillPlan pl{a.chunk, 1, a.T, 0, false};
   if (a.B == 0 || a.H_v == 0) return pl;
-  if (dispatch(a, nullptr, &pl) != hipSuccess) pl = PrefillPlan{a.chunk, 1, a.T, 0};
+  if (dispatch(a, nullptr, &pl) != hipSuccess) pl = PrefillPlan{a.chunk, 1, a.T, 0, false};
   return pl;
 }
 

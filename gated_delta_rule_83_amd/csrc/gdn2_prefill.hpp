@@ -17,22 +17,23 @@
 //   O  = (gamma * Q) S0 + Mqk U - Mqb R
 //   S_C = diag(gamma_C) S0 + (rho * K)^T U - (rho * beta)^T R,  rho_s = gamma_C / gamma_s
 // Anchors. The ratio gamma_t / gamma_s <= 1 is split between the two MFMA
-// operands against an anchor token: rescaling cumulative gates against an
-// in-block anchor so that ratios cannot explode is the device the FiX
-// analysis on iplexlaw.co.kr describes for its block-wise kernel (section 5).
-// For d_k = 128 the Gram matrices are anchored at the middle of the chunk,
-// m = C/2 - 1: the left operands carry lam_t = gamma_t / gamma_m and the
-// right ones mu_s = gamma_m / gamma_s, so in the off-diagonal block (second
-// half x first half) both factors are <= 1, and elsewhere one factor is
-// bounded by the inverse decay of half a chunk. (gamma * K) S0 is formed as
-// (lam * K)(diag(gamma_m) S0). The carry uses the chunk-end anchor: rho <= 1.
-// Every factor only rescales elements, so bf16 rounding stays relative; the
-// only risk is range, bounded by requiring each half-chunk decay to be at
-// least e^-60 on every channel. A chunk that fails this test (a decay below
-// ~e^-3.75 per token throughout half a chunk) is stepped token by token,
-// which is exact for any decay. (For d_k < 128 the Gram anchor is the chunk
-// start, lam = gamma_t, mu = 1 / gamma_t, and the whole chunk's decay is
-// checked against e^-60.)
+// operands against an anchor token with cumulative decay A: the left
+// operands carry lam_t = gamma_t / A, the right ones mu_s = A / gamma_s.
+// Rescaling cumulative gates against an in-block anchor so that ratios
+// cannot explode is the device the FiX analysis on iplexlaw.co.kr describes
+// for its block-wise kernel (section 5). (gamma * K) S0 is formed as
+// (lam * K)(diag(A) S0), and the carry as
+//   S_C = diag(gamma_C / A) (diag(A) S0 + (mu * K)^T U - (mu * beta)^T R).
+// The anchor is chosen per chunk: the chunk start (A = 1, lam = gamma_t <= 1)
+// while the whole chunk's decay is at least e^-60 on every channel (the
+// right factors are then below e^60); for d_k = 128 otherwise the middle
+// token m = C/2 - 1 (A = gamma_m) while each half chunk's decay is at least
+// e^-60: in the off-diagonal block (second half x first half) both factors
+// are then <= 1 and elsewhere one factor is bounded by the inverse decay of
+// half a chunk. Every factor only rescales elements, so bf16 rounding stays
+// relative; the only risk is range. A chunk that fails the test (for
+// d_k = 128 a decay below ~e^-3.75 per token throughout half a chunk) is
+// stepped token by token, which is exact for any decay.
 //
 // Everything that does not depend on the entering state (scaled operands,
 // the Gram matrices, the diagonal inverses) is computed one chunk ahead by
@@ -44,11 +45,11 @@
 // (chunk s produced into LDS buffer s%2, chunk s-1 consumed from buffer
 // (s-1)%2), with one workgroup barrier after each phase:
 //   A. producers: decay scan (wave-local, across lanes), scaled operands
-//      K*gamma | Q*gamma, K/gamma | beta/gamma (also transposed); then the
+//      K*lam | Q*lam, K*mu | beta*mu (also transposed); then the
 //      decay and erase gates of chunk s+2 are requested into registers.
 //      consumers: U = w*v of chunk s-1 (requested two steps earlier) into an
 //      LDS staging array, the previous chunk's outputs stored, v and w of
-//      chunk s+1 requested, X = (gamma*K) S0, Y = (gamma*Q) S0.
+//      chunk s+1 requested, X = (lam*K) diag(A) S0, Y = (lam*Q) diag(A) S0.
 //   B. producers: the Gram tiles (Akk, Akb, Mqk, Mqb, lower tiles) split
 //      over the waves, the inverses of the 16x16 diagonal blocks of I + Akb;
 //      then the keys and queries of chunk s+2 are requested.
@@ -94,12 +95,6 @@ struct RowLayout {
     const int sub = BF16 ? ((((k >> 4) & 1) << 3) | ((k & 3) << 1)) : ((k & 3) << 2);
     return (uint32_t)(row * STRIDE + ((unit ^ ((row >> 2) & SW)) << 4) + sub);
   }
-};
-
-// K32 operand: the fragments of two consecutive K16 blocks.
-template <bool BF16>
-struct Pair {
-  typename Op<BF16>::Frag lo, hi;
 };
 
 // Fragment loads and stores in RowLayout L (O = Op<BF16>).
@@ -209,7 +204,7 @@ struct ChunkBuf {
   alignas(16) char ab[Cf::C * LT::STRIDE];
   alignas(16) char m[Cf::C * LT::STRIDE];
   alignas(16) typename Op<Cf::BF16>::T dinv[Cf::NCH * 16 * Cf::LDD];  // (I + Akb_rr)^-1 per diagonal block
-  alignas(16) float gamc[Cf::DK];                // gamma_C per key channel
+  alignas(16) float gamc[Cf::DK];                // gamma_C / A (A: the anchor's cumulative decay) per key channel
   alignas(16) float gamm[Cf::TOKM ? Cf::DK : 4];  // gamma_m (the Gram anchor) per key channel
   alignas(16) int bad[Cf::NP];                   // per producer wave: chunk must be stepped token by token
 };
@@ -258,9 +253,12 @@ __device__ unsigned long long gdn2_phase_cycles[8][8][8];
     tm_acc[i] += tm_now - tm_prev;                                  \
     tm_prev = tm_now;                                               \
   } while (0)
+#ifndef GDN2_TIMER_BLOCK0
+#define GDN2_TIMER_BLOCK0 0  // first of the 8 workgroups recorded
+#endif
 #define GDN2_TIMER_STORE \
-  if (blockIdx.x < 8 && lane == 0) \
-    for (int i = 0; i < 8; ++i) gdn2_phase_cycles[blockIdx.x][wave][i] = tm_acc[i];
+  if (blockIdx.x >= GDN2_TIMER_BLOCK0 && blockIdx.x < GDN2_TIMER_BLOCK0 + 8 && lane == 0) \
+    for (int i = 0; i < 8; ++i) gdn2_phase_cycles[blockIdx.x - GDN2_TIMER_BLOCK0][wave][i] = tm_acc[i];
 #else
 #define GDN2_TIMER_INIT
 #define GDN2_MARK(i) ((void)0)
@@ -292,6 +290,11 @@ struct PrefillParams {
   // packed sequences: sequence n is tokens cu[n] .. cu[n+1]-1 of T (one
   // segment each); null: sequence n is tokens n*T .. n*T + T-1
   const int32_t *cu;
+  // outputs of the identity column blocks, [B*T][H_v][d_k] in the output
+  // type, d_k == d_v (null: not written): for token t of a segment, the query read of
+  // the segment's transition, (Phi_t)^T q_t, where Phi_t maps the segment's
+  // entering state to the state after t
+  void *oI;
 };
 
 // Lower 16x16 tiles (r, c), c <= r, of the chunk's Gram matrices over the
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // consumer lane's column: a value column, or for an identity block the
   // key channel whose unit vector the column starts from
   const int col = (ident ? cb - p.ncb_val : cb) * Cf::DVB + (consumer ? cw : 0) * 16 + lc;
-  const bool write_o = !ident && p.o && !(p.o_first_only && rel > 0);
+  const bool write_o = ident ? p.oI != nullptr : (p.o && !(p.o_first_only && rel > 0));
 
   // Token strides in bytes, and this (sequence, head)'s token-0 bases. GT:
   // the stored type of the per-channel gates.
@@ -586,7 +589,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   auto gate4 = [](floatx4 x) {
     return floatx4{gate_from_pre(x[0]), gate_from_pre(x[1]), gate_from_pre(x[2]), gate_from_pre(x[3])};
   };
-  ET *oh = (ET *)p.o + tok0 * p.H_v * d_v + (size_t)h * d_v;
+  // outputs: value blocks write o, identity blocks oI (written only when
+  // d_v == d_k: the same token stride)
+  ET *oh = (ET *)(ident ? p.oI : p.o) + tok0 * p.H_v * d_v + (size_t)h * d_v;
+  const int ocb = ident ? cb - p.ncb_val : cb;  // column block within the output row
   // entering and final state of this lane's column: value blocks use S0 /
   // S_T ([B][H_v][d_k][d_v] per segment), identity blocks start from the
   // unit vector and end in M_T ([B][H_v][d_k][d_k] per segment)
@@ -713,6 +719,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // Build chunk operands into buffer cbuf (producer waves; no workgroup sync
   // inside: the decay scan runs across the lanes of one wave).
   auto build = [&](auto P, ChunkBuf<Cf> &cbuf) {
+    // token-major: all waves' totals of this chunk (LDS, one step ahead),
+    // requested first so that they arrive while the gates are awaited
+    floatx4 tw[TOKM ? Cf::NP : 1];
+    if constexpr (TOKM) {
+#pragma unroll
+      for (int w2 = 0; w2 < Cf::NP; ++w2) tw[w2] = *reinterpret_cast<const floatx4 *>(&sm.tot[w2][ch0]);
+    }
     // cumulative decay within the lane's RPG tokens
     floatx4 gl[RPG];
     floatx4 pr = {1.f, 1.f, 1.f, 1.f};
@@ -723,59 +736,68 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
 
     floatx4 inc = pr, pre;
-    // factors of the operands (see the kernel's header): lam = gamma_t / gamma_m
-    // (left: keys and queries), mu = gamma_m / gamma_t (right: the Gram
-    // matrices' keys and erase keys), rho = gamma_C / gamma_t (the carry),
-    // as lam = gl[r] * cL, mu = sl[r] * cR, rho = sl[r] * post with the
-    // lane's prefix gl and suffix sl of its own tokens' decays
-    floatx4 cL, cR, post;
+    // factors of the operands (see the kernel's header): lam (left: keys and
+    // queries) and mu (right: the Gram matrices' and the carry's keys and
+    // erase keys), as lam = gl[r] * cL, mu = sl[r] * cR with the lane's
+    // prefix gl and suffix sl of its own tokens' decays
+    floatx4 cL, cR;
     const floatx4 one = {1.f, 1.f, 1.f, 1.f};
-    bool lane_bad = false;
+    int flag = 0;
     if constexpr (TOKM) {
-      // all waves' totals of this chunk (LDS, one step ahead) and the other
-      // lane half's product (lane exchange)
-      floatx4 tw[Cf::NP];
-#pragma unroll
-      for (int w2 = 0; w2 < Cf::NP; ++w2) tw[w2] = *reinterpret_cast<const floatx4 *>(&sm.tot[w2][ch0]);
+      // the other lane half's product (lane exchange) and the chunk's decay
       const floatx4 lo = shfl4(pr, lane ^ 32);
-      constexpr int HW = Cf::NP / 2;  // waves of the first half (tokens 0 .. m)
-      floatx4 before = one, after = one, half_before = one, half_after = one;
+      const floatx4 gC = (tw[0] * tw[1]) * (tw[2] * tw[3]);
+      floatx4 before = one;  // the waves before this one
 #pragma unroll
-      for (int w2 = 0; w2 < Cf::NP; ++w2) {
+      for (int w2 = 0; w2 < Cf::NP - 1; ++w2)
         if (w2 < wave) before *= tw[w2];
-        if (w2 > wave) after *= tw[w2];
-        // within the lane's own half of the chunk
-        if (w2 < wave && (w2 >= HW) == (wave >= HW)) half_before *= tw[w2];
-        if (w2 > wave && (w2 >= HW) == (wave >= HW)) half_after *= tw[w2];
-      }
-      pre = rg ? before * lo : before;   // tokens before the lane's first
-      post = rg ? after : lo * after;    // tokens after the lane's last
+      pre = rg ? before * lo : before;  // tokens before the lane's first
       inc = pre * pr;
-      if (wave < HW) {  // t <= m: lam = 1 / (decays t+1 .. m), mu = decays t+1 .. m
-        const floatx4 p1 = rg ? half_after : lo * half_after;  // lane's last token .. m
-        const floatx4 x = pr * p1;
-        cL = floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
-                     __builtin_amdgcn_rcpf(x[3])};
-        cR = p1;
-      } else {  // t > m: lam = decays m+1 .. t, mu = 1 / lam
-        cL = rg ? half_before * lo : half_before;
-        const floatx4 x = pr * cL;
-        cR = floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
-                     __builtin_amdgcn_rcpf(x[3])};
-      }
-      // range of the factors: both half-chunk decays at least kMinHalfDecay
-      // (wave 0's first lane half holds every channel once)
-      if (wave == 0 && rg == 0) {
-        floatx4 h1 = one, h2 = one;
+      auto rcp4 = [](floatx4 x) {
+        return floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
+                       __builtin_amdgcn_rcpf(x[3])};
+      };
+      // The anchor, the same on every producer wave (lanes 0..31 hold every
+      // channel once): the chunk start while the whole chunk's decay is at
+      // least kMinChunkDecay on every channel, else the middle token while
+      // both half chunks' are at least kMinHalfDecay, else token by token.
+      // (The test also reads the lane's own product, which is never
+      // negative: the decision then waits for this chunk's gates rather than
+      // holding back the products that use them.)
+      const bool mild = __all(gC[0] >= kMinChunkDecay && gC[1] >= kMinChunkDecay && gC[2] >= kMinChunkDecay &&
+                              gC[3] >= kMinChunkDecay && inc[0] >= 0.f);
+      if (mild) {  // chunk start: lam = gamma_t, mu = 1 / gamma_t
+        cL = pre;
+        cR = rcp4(inc);
+        if (wave == Cf::NP - 1 && rg == 1) *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = inc;  // gamma_C
+      } else {
+        constexpr int HW = Cf::NP / 2;  // waves of the first half (tokens 0 .. m)
+        floatx4 half_before = one, half_after = one;  // within the lane's own half of the chunk
 #pragma unroll
         for (int w2 = 0; w2 < Cf::NP; ++w2) {
-          if (w2 < HW) h1 *= tw[w2]; else h2 *= tw[w2];
+          if (w2 < wave && (w2 >= HW) == (wave >= HW)) half_before *= tw[w2];
+          if (w2 > wave && (w2 >= HW) == (wave >= HW)) half_after *= tw[w2];
         }
-        lane_bad = !(h1[0] >= kMinHalfDecay) || !(h1[1] >= kMinHalfDecay) || !(h1[2] >= kMinHalfDecay) ||
-                   !(h1[3] >= kMinHalfDecay) || !(h2[0] >= kMinHalfDecay) || !(h2[1] >= kMinHalfDecay) ||
-                   !(h2[2] >= kMinHalfDecay) || !(h2[3] >= kMinHalfDecay);
-        *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = h1 * h2;
-        *reinterpret_cast<floatx4 *>(&cbuf.gamm[ch0]) = h1;
+        const floatx4 h1 = tw[0] * tw[1], h2 = tw[2] * tw[3];  // half-chunk decays
+        flag = __all(h1[0] >= kMinHalfDecay && h1[1] >= kMinHalfDecay && h1[2] >= kMinHalfDecay &&
+                     h1[3] >= kMinHalfDecay && h2[0] >= kMinHalfDecay && h2[1] >= kMinHalfDecay &&
+                     h2[2] >= kMinHalfDecay && h2[3] >= kMinHalfDecay)
+                   ? kChunkMid
+                   : kChunkSteps;
+        if (wave < HW) {  // t <= m: lam = 1 / (decays t+1 .. m), mu = decays t+1 .. m
+          const floatx4 p1 = rg ? half_after : lo * half_after;  // lane's last token .. m
+          cL = rcp4(pr * p1);
+          cR = p1;
+        } else {  // t > m: lam = decays m+1 .. t, mu = 1 / lam
+          cL = rg ? half_before * lo : half_before;
+          cR = rcp4(pr * cL);
+        }
+        // the carry's factor on the gamma_m-scaled entering state, and
+        // gamma_m (wave 0's first lane half holds every channel once)
+        if (wave == 0 && rg == 0) {
+          *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = h2;
+          *reinterpret_cast<floatx4 *>(&cbuf.gamm[ch0]) = h1;
+        }
       }
     } else {
       if constexpr (RGE <= 16) {
@@ -801,22 +823,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         pre = shfl4(inc, lane - 1);
       }
       if (rg == 0) pre = one;
-      // channel-major build: the anchor of the Gram matrices is the chunk
-      // start (lam = gamma_t, mu = 1 / gamma_t, rho = gamma_C / gamma_t),
-      // which bounds every factor by 1 / gamma_C: the whole chunk's decay is
-      // checked against kMinChunkDecay
-      const floatx4 gC = shfl4(inc, (lane / Cf::RGL) * Cf::RGL + (RGE - 1));  // gamma_C of the lane's quad
+      // channel-major build: the anchor is the chunk start (lam = gamma_t,
+      // mu = 1 / gamma_t), which bounds every factor by 1 / gamma_C: the
+      // whole chunk's decay is checked against kMinChunkDecay
       cL = pre;
       cR = floatx4{__builtin_amdgcn_rcpf(inc[0]), __builtin_amdgcn_rcpf(inc[1]), __builtin_amdgcn_rcpf(inc[2]),
                    __builtin_amdgcn_rcpf(inc[3])};
-      post = gC * cR;
       const bool last = rg == RGE - 1;
-      lane_bad = last && (!(inc[0] >= kMinChunkDecay) || !(inc[1] >= kMinChunkDecay) ||
-                          !(inc[2] >= kMinChunkDecay) || !(inc[3] >= kMinChunkDecay));
+      const bool lane_bad = last && (!(inc[0] >= kMinChunkDecay) || !(inc[1] >= kMinChunkDecay) ||
+                                     !(inc[2] >= kMinChunkDecay) || !(inc[3] >= kMinChunkDecay));
       if (last) *reinterpret_cast<floatx4 *>(&cbuf.gamc[ch0]) = inc;
+      flag = __any(lane_bad) ? kChunkSteps : 0;
     }
-    const bool any_bad = __any(lane_bad);
-    if (lane == 0) cbuf.bad[wave] = any_bad ? 1 : 0;
+    if (lane == 0) cbuf.bad[wave] = flag;
     if constexpr (CPL) {  // beta of the lane's tokens, for the Gram tiles
       if (brow && cq == 0 && (TOKM || wave == 0)) {
 #pragma unroll
@@ -835,16 +854,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const int tl = tb0 + r;
         const floatx4 lam = gl[r] * cL;
         const floatx4 mu = sl[r] * cR;
-        const floatx4 rho = sl[r] * post;
         const floatx4 kv = quad_f(rk[P][r]);
         const floatx4 qv = quad_f(rq[P][r]);
-        const floatx4 km = kv * mu;
-        const floatx4 kr = kv * rho;
+        const floatx4 kr = kv * mu;
         const floatx4 bkr = rb[P][r] * kr;
         st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * lam);
         st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * lam);
-        st4<LK, BF16>(sm.kbi, tl, ch0, km);
-        st4<LK, BF16>(sm.kbi, C + tl, ch0, rb[P][r] * km);
+        st4<LK, BF16>(sm.kbi, tl, ch0, kr);
+        st4<LK, BF16>(sm.kbi, C + tl, ch0, bkr);
         // transposed carry operands: 4 (or 2) consecutive tokens per channel at once
         if constexpr (RPG % 4 == 0) {
           kbq[r & 3] = kr;
@@ -1135,7 +1152,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   constexpr int OROW = Cf::OROW, OLPR = Cf::OLPR, ORPI = Cf::ORPI, ORPW = Cf::ORPW, ONI = Cf::ONI;
   int otc = -1;  // first token of the staged outputs (-1: none)
   const int orow0 = (consumer ? cw : 0) * ORPW + lane / OLPR;
-  const uint32_t o_off = (uint32_t)orow0 * v_tb + (uint32_t)(cb * Cf::DVB * Cf::OES + 8 * (lane % OLPR));
+  const uint32_t o_off = (uint32_t)orow0 * v_tb + (uint32_t)(ocb * Cf::DVB * Cf::OES + 8 * (lane % OLPR));
   uint2 ox[ONI];
   auto read_o = [&]() {
 #pragma unroll
@@ -1183,13 +1200,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         qf[r][pp] = frag32<LK, BF16, single>(cbf.kqg, C + 16 * r + lc, pp, lg);
       }
     });
-    // gamma_m of this lane's state rows (the left operands carry gamma_t /
-    // gamma_m, so the state enters X and Y scaled by gamma_m)
-    floatx4 gmr[NRT];
-    if constexpr (Cf::TOKM) {
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) gmr[rt] = *reinterpret_cast<const floatx4 *>(&cbf.gamm[16 * rt + 4 * lg]);
-    }
     const int flags = cbf.bad[0] | cbf.bad[1] | cbf.bad[2] | cbf.bad[3];
     __builtin_amdgcn_sched_barrier(0);
     // U of the consumed chunk (requested two steps ago) into the staging rows
@@ -1200,21 +1210,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     load_u(std::integral_constant<int, PP>(), consumer && !ident && s + 1 < nfull ? (s + 1) * C : Tl);
     __builtin_amdgcn_sched_barrier(0);
     // the same flags are read by every wave: the chunk's path is workgroup-uniform
-    const bool chunk_bad = live && flags != 0;
+    const bool chunk_bad = live && (flags & kChunkSteps) != 0;
     const bool cbad = consumer && live && chunk_bad;
     const bool fast = consumer && live && !chunk_bad;
     if (cbad) {
       token_steps(tc, tc + C);
     } else if (fast) {
-      // X = (gamma * K) S0, Y = (gamma * Q) S0. Y is formed transposed
-      // (operands swapped): lane (lc, lg) holds Y[t = lc] at columns
-      // 4lg..4lg+3, the layout of the output store.
-      auto s_in = [&](int rt) { return Cf::TOKM ? S[rt] * gmr[rt] : S[rt]; };
+      // X = (lam * K) diag(A) S0, Y = (lam * Q) diag(A) S0 (the held state
+      // is already diag(A) S0: see the end of the step). Y is formed
+      // transposed (operands swapped): lane (lc, lg) holds Y[t = lc] at
+      // columns 4lg..4lg+3, the layout of the output store.
       Pair<BF16> Sp[NKP];
 #pragma unroll
       for (int pp = 0; pp < NKP; ++pp)
-        Sp[pp] = Pair<BF16>{O::from_acc(s_in(2 * pp)),
-                            2 * pp + 1 < NRT ? O::from_acc(s_in((2 * pp + 1) % NRT)) : O::zero()};
+        Sp[pp] = Pair<BF16>{O::from_acc(S[2 * pp]), 2 * pp + 1 < NRT ? O::from_acc(S[(2 * pp + 1) % NRT]) : O::zero()};
 #pragma unroll
       for (int r = 0; r < NCH; ++r) {
         X[r] = zero4();
@@ -1288,16 +1297,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         }
       });
       otc = tc;
-      // S_C = diag(gamma_C) S0 + (rho K)^T U - (rho beta)^T R with
-      // rho_s = gamma_C / gamma_s <= 1 (the chunk-end anchor): kbiT columns
-      // are [K part | beta part], K16 block kb pairs with U_kb or -R_(kb - NCH)
+      // S_C = diag(gamma_C / A) (diag(A) S0 + (mu K)^T U - (mu beta)^T R)
+      // with the anchor's cumulative decay A (1 at the chunk start, gamma_m
+      // in the middle) and mu_s = A / gamma_s: kbiT columns are
+      // [K part | beta part], K16 block kb pairs with U_kb or -R_(kb - NCH)
       auto ub = [&](int kb) { return kb < NCH ? Uf[kb % NCH] : Rn[(kb - NCH) % NCH]; };
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        floatx4 acc = S[rt] * gc[rt];
+        floatx4 acc = S[rt];
 #pragma unroll
         for (int pp = 0; pp < NCH; ++pp) acc = mma<BF16>(acc, tf[rt][pp], Pair<BF16>{ub(2 * pp), ub(2 * pp + 1)});
-        S[rt] = acc;
+        S[rt] = acc * gc[rt];
+      }
+    }
+    // The state enters a chunk with the middle anchor (built in this step's
+    // first phase, consumed in the next step) as diag(gamma_m) S: scaled
+    // here, after the carry, so that the other chunks need no scaling.
+    if constexpr (Cf::TOKM) {
+      const ChunkBuf<Cf> &nb = sm.buf[s & 1];
+      if (consumer && s < nfull && ((nb.bad[0] | nb.bad[1] | nb.bad[2] | nb.bad[3]) & kChunkMid)) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) S[rt] *= *reinterpret_cast<const floatx4 *>(&nb.gamm[16 * rt + 4 * lg]);
       }
     }
     GDN2_MARK(5);
@@ -1349,7 +1369,7 @@ constexpr int fitting_chunk(int requested) {
 template <int DK, int C, int NCT, bool BF16>
 PrefillPlan plan_t(const PrefillArgs &a) {
   constexpr int DVB = 16 * NCT;
-  PrefillPlan pl{C, 1, a.T, 0};
+  PrefillPlan pl{C, 1, a.T, 0, false};
   const int ncb = a.d_v / DVB;
   const int nfull = a.T / C;
   if (a.cu_seqlens || DK % DVB != 0 || nfull < 2) return pl;
@@ -1371,20 +1391,29 @@ PrefillPlan plan_t(const PrefillArgs &a) {
   if (nseg < 2) return pl;
   pl.nseg = nseg;
   pl.seg_len = seg_len;
-  pl.ws_bytes = (size_t)nseg * a.B * a.H_v * DK * (size_t)(a.d_v + DK) * sizeof(float);
+  // segment states and transitions; with the output correction also the
+  // identity columns' outputs, one row of d_k per token and value head
+  const size_t states = (size_t)nseg * a.B * a.H_v * DK * (size_t)(a.d_v + DK) * sizeof(float);
+  const size_t corr = ((states + 255) & ~(size_t)255) + (size_t)a.B * a.T * a.H_v * DK * (BF16 ? 2 : 4);
+  pl.correct = a.d_v == DK && (a.ws_cap == 0 || corr <= a.ws_cap);
+  pl.ws_bytes = pl.correct ? corr : states;
   return pl;
 }
 
 // Unsplit: one launch over whole sequences. Split (nseg segments):
 //  1. every segment from a zero entering state (the first from S0), value
-//     blocks ending in state[s] and identity blocks in trans[s]: the
-//     segment maps an entering state X to trans[s] X + state[s]; only the
-//     first segment, whose entering state is exact, writes outputs;
+//     blocks ending in state[s] and writing their outputs o_zero, identity
+//     blocks (segments >= 1) ending in trans[s] and writing their query
+//     reads oI to the workspace: the segment maps an entering state X to
+//     trans[s] X + state[s], and its outputs to o_zero + X^T oI;
 //  2. state[s] = trans[s] state[s - 1] + state[s] in order: the exact state
-//     after each segment;
-//  3. segments 1 .. nseg - 1 again from the exact entering states, writing
-//     their outputs and the last one S_T.
-// The chunk boundaries of every segment are those of the unsplit run.
+//     after each segment, the last one also into S_T;
+//  3. o += oI . state[s - 1] on segments 1 .. nseg - 1 (launch_split_correct).
+// When the workspace is capped below what oI needs, the first pass writes
+// only the first segment's outputs, step 2 stops at segment nseg - 2, and
+// segments 1 .. nseg - 1 run again from their exact entering states, the
+// last one writing S_T. The chunk boundaries of every segment are those of
+// the unsplit run.
 template <int DK, int C, int NCT, bool BF16>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   auto kernel = [&](int blocks, const PrefillParams &kp) {
@@ -1419,6 +1448,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.o_first_only = false;
   p.sT_last_only = false;
   p.cu = a.cu_seqlens;
+  p.oI = nullptr;
   const int units = a.B * a.H_v;
   if (pl.nseg <= 1) {
     kernel(units * ncb, p);
@@ -1436,17 +1466,27 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
     state = static_cast<float *>(a.workspace);
     trans = state + (size_t)pl.nseg * sstate;
   }
+  const bool correct = pl.correct && !a.seg_states;
+  void *oI = nullptr;
+  if (correct) {
+    const size_t states = (size_t)pl.nseg * (sstate + strans) * sizeof(float);
+    oI = static_cast<char *>(a.workspace) + ((states + 255) & ~(size_t)255);
+  }
   // 1.
   p.ncb_id = DK / DVB;
   p.S_T = state; p.sT_stride = sstate;
   p.M_T = trans; p.m_stride = strans;
-  p.o_first_only = true;
+  p.o_first_only = !correct;
+  p.oI = oI;
   kernel(pl.nseg * units * (ncb + p.ncb_id), p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 2.
-  e = launch_split_combine(state, trans, pl.nseg, units, DK, a.d_v, st);
+  e = launch_split_combine(state, trans, correct ? pl.nseg - 1 : pl.nseg - 2, units, DK, a.d_v,
+                           correct ? a.S_T : nullptr, st);
   if (e != hipSuccess || a.seg_states) return e;
+  if (correct)  // 3.
+    return launch_split_correct(a.o, oI, state, a.B, a.T, a.H_v, DK, a.d_v, pl.seg_len, pl.nseg, BF16, st);
   // 3.
   p.seg_first = 1;
   p.nseg = pl.nseg - 1;

@@ -93,16 +93,20 @@ def test_workspace_query():
 def test_split_workspace_query_and_errors(monkeypatch):
     """Few heads over a long sequence: the prefill splits the sequence and asks
     for workspace (segments x (d_k x d_v state + d_k x d_k transition) fp32 per
-    head); too little or an overlapping workspace is rejected before any launch."""
+    head, 256-byte aligned, then the identity columns' query reads, one row of
+    d_k per token and value head in the input dtype); too little or an
+    overlapping workspace is rejected before any launch."""
     d2 = g.make_desc(1, 65536, 16, 16, 128, 128, 64, g.GDN2_BF16)
     per_seg = 16 * 128 * (128 + 128) * 4
+    rows = 65536 * 16 * 128 * 2
     monkeypatch.delenv("GDN2_PREFILL_SPLIT", raising=False)
     need = g.gdn2_chunk_forward_workspace_bytes(d2)
-    assert need == 8 * per_seg
+    assert need == 8 * per_seg + rows
+    assert g.gdn2_chunk_forward_plan(d2)[2] == 8
     monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
     assert g.gdn2_chunk_forward_workspace_bytes(d2) == 0
     monkeypatch.setenv("GDN2_PREFILL_SPLIT", "4")
-    assert g.gdn2_chunk_forward_workspace_bytes(d2) == 4 * per_seg
+    assert g.gdn2_chunk_forward_workspace_bytes(d2) == 4 * per_seg + rows
     monkeypatch.delenv("GDN2_PREFILL_SPLIT")
     ws = FAKE + 20 * (1 << 30)
     assert fwd(d2) == g.GDN2_ERR_WORKSPACE
