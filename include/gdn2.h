@@ -91,11 +91,15 @@ typedef struct {
  * parallel: that happens when the unsplit call would occupy few workgroups
  * (few sequences x value heads) and T spans many chunks; the environment
  * variable GDN2_PREFILL_SPLIT=<n>, read at each call, forces n segments
- * (1: never split). The split computes the same recurrence: each segment's
- * entering state is obtained exactly (up to rounding) from the previous
- * segments' states and transition matrices, then the segment is run from it.
- * Returns 0 for an invalid description as well; the forward call reports
- * the error. */
+ * (1: never split). The split computes the same recurrence: every segment
+ * runs from a zero state while identity columns give its transition matrix;
+ * the exact entering states (up to rounding) follow from those in order, and
+ * each segment's outputs are then corrected by its entering state's
+ * contribution (d_k == d_v; otherwise the segments run again from their
+ * entering states). The workspace holds the segments' states and transitions
+ * (fp32) and, for the correction, d_k values of the input dtype per token
+ * and value head. Returns 0 for an invalid description as well; the forward
+ * call reports the error. */
 size_t gdn2_chunk_forward_workspace_bytes(const gdn2_desc *desc);
 
 /* How gdn2_chunk_forward (and its gate forms) would run `desc`: the chunk
@@ -136,14 +140,17 @@ gdn2_status gdn2_chunk_forward(const gdn2_desc *desc, const void *q, const void 
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): it allocates nothing and calls no
  * allocating routine. Same arguments, results and errors as
- * gdn2_chunk_forward (and bit for bit the same results: the same kernels
- * and plan); the scratch that a split of long sequences needs
- * (gdn2_chunk_forward_workspace_bytes(desc)) is taken from a static device
- * array of GDN2_NOALLOC_SCRATCH_BYTES per device, whose address is looked up
- * on the first call on each device. Problems that need more scratch than
- * that (e.g. very many sequence segments forced with GDN2_PREFILL_SPLIT)
- * return GDN2_ERR_SCRATCH before anything is enqueued; problems that need
- * none never touch the array. The array is shared by every call on a device
+ * gdn2_chunk_forward; the scratch that a split of long sequences needs is
+ * taken from a static device array of GDN2_NOALLOC_SCRATCH_BYTES per device,
+ * whose address is looked up on the first call on each device. The split is
+ * planned within that array: where the output correction's scratch
+ * (gdn2_chunk_forward_workspace_bytes(desc)) fits, the results are bit for
+ * bit those of gdn2_chunk_forward (the same kernels and plan); where only
+ * the segment states and transitions fit, the segments run a second time
+ * instead of being corrected (equal up to rounding). Problems whose states
+ * and transitions alone do not fit (e.g. very many segments forced with
+ * GDN2_PREFILL_SPLIT) return GDN2_ERR_SCRATCH before anything is enqueued;
+ * problems that need no scratch never touch the array. The array is shared by every call on a device
  * and keeps the last call's contents: calls of this entry point that overlap
  * in time on one device (other streams, other host threads) race on it and
  * must be serialised by the caller. Nothing in it needs to start cleared. */
