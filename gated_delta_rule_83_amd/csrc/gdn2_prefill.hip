@@ -147,15 +147,19 @@ __global__ __launch_bounds__(256) void split_correct_kernel(void *o_, const void
   const float *Sin = state + (((size_t)(s - 1) * B + n) * H_v + h) * (size_t)(DK * DV);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  auto frag8 = [](const float (&x)[8]) {
-    typename O::Frag lo, hi;
+  // S_in^T in the operand type, staged through LDS: read as whole rows of
+  // S_in (16-byte loads), written transposed ([column][key channel], rows
+  // padded against bank conflicts), then each lane's fragments are runs of 8
+  // key channels of one column.
+  constexpr int SP = DK + (BF16 ? 8 : 4);
+  __shared__ OT sT[DV * SP];
+  for (int e = 4 * (int)threadIdx.x; e < DK * DV; e += 4 * 256) {
+    const int k = e / DV, col = e % DV;
+    const floatx4 v = *reinterpret_cast<const floatx4 *>(Sin + e);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo[j] = O::cvt(x[j]);
-      hi[j] = O::cvt(x[4 + j]);
-    }
-    return Pair<BF16>{lo, hi};
-  };
+    for (int i = 0; i < 4; ++i) sT[(col + i) * SP + k] = O::cvt(v[i]);
+  }
+  __syncthreads();
   // output column of row r of tile ct
   auto ocol = [](int ct, int r) { return DV >= 32 ? 32 * (ct >> 1) + 8 * (r >> 2) + 4 * (ct & 1) + (r & 3) : r; };
   Pair<BF16> sa[NCT][NKP];
@@ -163,13 +167,14 @@ __global__ __launch_bounds__(256) void split_correct_kernel(void *o_, const void
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = 32 * p + 8 * g + j;
-        x[j] = k < DK ? Sin[(size_t)k * DV + ocol(ct, c)] : 0.f;
+      const int k0 = 32 * p + 8 * g;  // a multiple of 8: the run is wholly inside d_k or wholly past it
+      if (k0 < DK) {
+        const OT *src = sT + ocol(ct, c) * SP + k0;
+        sa[ct][p] = Pair<BF16>{*reinterpret_cast<const typename O::Frag *>(src),
+                               *reinterpret_cast<const typename O::Frag *>(src + 4)};
+      } else {
+        sa[ct][p] = Pair<BF16>{O::zero(), O::zero()};
       }
-      sa[ct][p] = frag8(x);
     }
   const size_t row0 = (size_t)n * T;  // token index of the sequence's first token
   const ET *oIh = static_cast<const ET *>(oI_) + (size_t)h * DK;
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) void split_correct_kernel(void *o_, const void
 template <int DK, bool BF16>
 hipError_t launch_correct_dv(void *o, const void *oI, const float *state, int B, int T, int H_v, int d_v,
                              int seg_len, int nseg, hipStream_t st) {
-  const int slab = 1024;
+  const int slab = 2048;
   const int nslab = (seg_len + slab - 1) / slab;
   const dim3 grid((unsigned)((nseg - 1) * B * H_v * nslab));
   switch (d_v) {
