@@ -175,6 +175,10 @@ struct PrefillCfg {
   // w*C/4 .. +C/4 for all key channels, so that every raw request covers
   // whole token rows (see the kernel's producer layout)
   static constexpr bool TOKM = DK == 128;
+  // bf16: the carry's operands (mu K | mu b*K per key channel) are read from
+  // the kbi rows with transposing LDS reads, so kbi is kept per chunk buffer
+  // and no transposed copy is built; fp32 keeps the transposed copy kbiT
+  static constexpr bool TRC = BF16;
   // output staging: rows of DVB output elements plus 8 bytes, so that the
   // 16 rows of one 8-byte column slice written together fall on distinct
   // bank pairs; the stores then write whole rows, 8 bytes per lane
@@ -196,8 +200,12 @@ template <class Cf>
 struct ChunkBuf {
   typedef typename Cf::LK LK;
   typedef typename Cf::LT LT;
-  alignas(16) char kqg[2 * Cf::C * LK::STRIDE];  // rows 0..C-1: k*gamma; rows C..2C-1: q*gamma
-  alignas(16) char kbiT[Cf::DK * LT::STRIDE];    // kbi transposed: [channel][token (K part | beta part)]
+  alignas(16) char kqg[2 * Cf::C * LK::STRIDE];  // rows 0..C-1: k*lam; rows C..2C-1: q*lam
+  // bf16: rows 0..C-1: k*mu; rows C..2C-1: (b*k)*mu (read by this chunk's
+  // Gram tiles and, one step later, by the carry)
+  alignas(16) char kbi[Cf::TRC ? 2 * Cf::C * LK::STRIDE : 16];
+  // fp32: kbi transposed, [channel][token (K part | beta part)], for the carry
+  alignas(16) char kbiT[Cf::TRC ? 16 : Cf::DK * LT::STRIDE];
   // ab: row t, 16-column block 2c = Akk block (t, c) (strictly lower inside
   // diagonal blocks), block 2c + 1 = -Akb block (t, c) (off-diagonal only);
   // m: block 2c = Mqk block, 2c + 1 = Mqb block (lower incl. diagonal)
@@ -212,10 +220,10 @@ struct ChunkBuf {
 template <class Cf>
 struct PrefillSmem {
   ChunkBuf<Cf> buf[2];
-  // rows 0..C-1: k/gamma; rows C..2C-1: (b*k)/gamma of the chunk being
+  // fp32: rows 0..C-1: k*mu; rows C..2C-1: (b*k)*mu of the chunk being
   // produced (written by the build, read by the Gram tiles of the same step:
-  // one buffer)
-  alignas(16) char kbi[2 * Cf::C * Cf::LK::STRIDE];
+  // one buffer; bf16 keeps them per chunk buffer)
+  alignas(16) char kbi[Cf::TRC ? 16 : 2 * Cf::C * Cf::LK::STRIDE];
   // Akb diagonal blocks (fp32, 80-byte rows), Gram -> inverses; row i of a
   // block is stored at position 4 (i % 4) + i / 4 so that the inverse's
   // reads of rows 4qq + j (qq = 0..3) fall on distinct banks
@@ -860,34 +868,38 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const floatx4 bkr = rb[P][r] * kr;
         st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * lam);
         st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * lam);
-        st4<LK, BF16>(sm.kbi, tl, ch0, kr);
-        st4<LK, BF16>(sm.kbi, C + tl, ch0, bkr);
-        // transposed carry operands: 4 (or 2) consecutive tokens per channel at once
-        if constexpr (RPG % 4 == 0) {
-          kbq[r & 3] = kr;
-          bkq[r & 3] = bkr;
-          if ((r & 3) == 3) {
+        char *kbi_b = Cf::TRC ? cbuf.kbi : sm.kbi;
+        st4<LK, BF16>(kbi_b, tl, ch0, kr);
+        st4<LK, BF16>(kbi_b, C + tl, ch0, bkr);
+        // fp32: the carry's operands transposed, 4 (or 2) consecutive tokens
+        // per channel at once
+        if constexpr (!Cf::TRC) {
+          if constexpr (RPG % 4 == 0) {
+            kbq[r & 3] = kr;
+            bkq[r & 3] = bkr;
+            if ((r & 3) == 3) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                st4<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 3, floatx4{kbq[0][c], kbq[1][c], kbq[2][c], kbq[3][c]});
+                st4<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 3, floatx4{bkq[0][c], bkq[1][c], bkq[2][c], bkq[3][c]});
+              }
+            }
+          } else if constexpr (RPG % 2 == 0) {
+            if (r & 1) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                st2<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 1, kbq[0][c], kr[c]);
+                st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bkr[c]);
+              }
+            }
+            kbq[0] = kr;
+            bkq[0] = bkr;
+          } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              st4<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 3, floatx4{kbq[0][c], kbq[1][c], kbq[2][c], kbq[3][c]});
-              st4<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 3, floatx4{bkq[0][c], bkq[1][c], bkq[2][c], bkq[3][c]});
+              st1<LT, BF16>(cbuf.kbiT, ch0 + c, tl, kr[c]);
+              st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bkr[c]);
             }
-          }
-        } else if constexpr (RPG % 2 == 0) {
-          if (r & 1) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              st2<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 1, kbq[0][c], kr[c]);
-              st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bkr[c]);
-            }
-          }
-          kbq[0] = kr;
-          bkq[0] = bkr;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            st1<LT, BF16>(cbuf.kbiT, ch0 + c, tl, kr[c]);
-            st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bkr[c]);
           }
         }
       }
@@ -954,7 +966,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         };
         auto gram_wave = [&](auto wc) {
           constexpr int w = decltype(wc)::value;
-          gram_tiles<Cf, GS::KK[w], GS::KB[w], GS::QK[w], GS::QB[w], CPL>(pb, sm.kbi, sm.akbd, sm.beta[P], lg, lc);
+          gram_tiles<Cf, GS::KK[w], GS::KB[w], GS::QK[w], GS::QB[w], CPL>(pb, Cf::TRC ? pb.kbi : sm.kbi, sm.akbd,
+                                                                          sm.beta[P], lg, lc);
           invert_set(std::integral_constant<unsigned, GS::INV[w]>());
         };
         switch (wave) {
@@ -1126,6 +1139,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       }
     }
   };
+  // The carry's A operand for key-channel tile rt and K32 block pp: rows =
+  // channels 16 rt .. +15, k = the columns [K part (tokens) | beta part] of
+  // the transposed kbi, i.e. kbi row 32 pp + k. bf16: two transposing reads
+  // of the kbi rows (lane j of a 16-lane group addresses kbi row
+  // 32 pp + 16 h + 4 lg + j / 4, channels 16 rt + 4 (j % 4) .. +3, 8 bytes;
+  // lane (lc, lg) then holds rows 4 lg .. 4 lg + 3 (+16 h) of channel
+  // 16 rt + lc); fp32: rows of the transposed copy.
+  auto carry_frag = [&](const ChunkBuf<Cf> &cb, int rt, int pp) -> Pair<BF16> {
+    if constexpr (Cf::TRC) {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      auto rd = [&](int h) {
+        const char *src = cb.kbi + Cf::LK::off(32 * pp + 16 * h + 4 * lg + (lc >> 2), 16 * rt + 4 * (lc & 3));
+        const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(__attribute__((address_space(3))) const char *)src);
+        return __builtin_bit_cast(Frag, r);
+      };
+      return Pair<BF16>{rd(0), rd(1)};
+    } else {
+      return frag32<LT, BF16>(cb.kbiT, 16 * rt + lc, pp, lg);
+    }
+  };
   // this wave's U fragment of 16-token block c: lane (lc, lg) gets tokens
   // 16c + 4lg .. +3 of column lc. bf16: one transposing read per fragment
   // (within a 16-lane group, lane 4a + b receives element b of the 8-byte
@@ -1262,7 +1296,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
-        for (int pp = 0; pp < NCH; ++pp) tf[rt][pp] = frag32<LT, BF16>(cbf.kbiT, 16 * rt + lc, pp, lg);
+        for (int pp = 0; pp < NCH; ++pp) tf[rt][pp] = carry_frag(cbf, rt, pp);
         gc[rt] = *reinterpret_cast<const floatx4 *>(&cbf.gamc[16 * rt + 4 * lg]);
       }
       // Z = X + Akk U, then (I + Akb) R = Z by blocked forward substitution:
