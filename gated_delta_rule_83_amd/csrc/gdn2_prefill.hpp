@@ -977,8 +977,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
           default: gram_wave(std::integral_constant<int, 3>()); break;
         }
       }
+      GDN2_MARK(4);
       activate_ab(std::integral_constant<int, decltype(P)::value ^ 1>());
       wave_totals(std::integral_constant<int, decltype(P)::value ^ 1>());  // chunk s+1
+      GDN2_MARK(6);
       load_kq(P, raw_src(tn));
       GDN2_MARK(2);
       __syncthreads();  // buffer P is now complete for the consumers

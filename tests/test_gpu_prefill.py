@@ -126,6 +126,28 @@ def test_split_sequence_matches_oracle(monkeypatch, dtype, nseg):
     run_and_compare(d, dtype, 64, label=f"split{nseg}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_automatic_split_matches_oracle_and_unsplit(monkeypatch, dtype):
+    """The automatic plan (no forced count): few heads and a long sequence
+    with a ragged tail are split into segments; against the oracle and
+    against the unsplit run."""
+    import gated_delta_rule_83_amd as g
+    monkeypatch.delenv("GDN2_PREFILL_SPLIT", raising=False)
+    B, T, Hqk, Hv = 2, 93 * 32 + 24, 1, 2
+    st, crun, nseg = g.gdn2_chunk_forward_plan(
+        g.make_desc(B, T, Hqk, Hv, 128, 128, 64, g.GDN2_BF16 if dtype == "bf16" else g.GDN2_F32))
+    assert st == g.GDN2_OK and nseg >= 3, (st, crun, nseg)
+    rng = np.random.default_rng(123)
+    d = rand_inputs(rng, B, T, Hqk, Hv, 128, 128)
+    run_and_compare(d, dtype, 64, label="auto split")
+    td = gi.to_torch(d, dtype, DEV)
+    o_s, S_s = gpu_prefill(td, 64)
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
+    o_u, S_u = gpu_prefill(td, 64)
+    torch.cuda.synchronize()
+    assert normwise(to_np(o_s), to_np(o_u)) < TOL[dtype] and normwise(to_np(S_s), to_np(S_u)) < TOL[dtype]
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 32), (16, 16), (32, 128), (128, 16)])
 def test_split_sequence_head_sizes(monkeypatch, dk, dv):
     """Forced split at other head sizes (where the column blocks do not tile
