@@ -32,7 +32,8 @@ CFLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 
 def _units():
     units = [("gdn2_api.cpp", "api", []), ("gdn2_decode.hip", "decode", []),
-             ("gdn2_prefill.hip", "prefill", []), ("gdn2_noalloc.hip", "noalloc", [])]
+             ("gdn2_prefill.hip", "prefill", []), ("gdn2_noalloc.hip", "noalloc", []),
+             ("gdn2_backward_chunk.hip", "backward_chunk", [])]
     for bf in (1, 0):
         units.append(("gdn2_backward.hip", f"backward_{'bf16' if bf else 'f32'}", [f"-DGDN2_BWD_BF16={bf}"]))
     for dt, bf in (("bf16", 1), ("f32", 0)):

@@ -1211,8 +1211,13 @@ hipError_t launch_backward_split(const BackwardArgs &a, const BwdSplit &sp, hipS
 
 size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
   const BwdSplit sp = backward_split_plan(B, T, H_qk, H_v, d_k, d_v, bf16);
-  if (sp.nseg < 2) return backward_workspace_bytes(B, (size_t)B * T, H_v, d_k, d_v);
-  return split_layout(B, T, H_v, d_k, d_v, sp).total;
+  const size_t per_token = sp.nseg < 2 ? backward_workspace_bytes(B, (size_t)B * T, H_v, d_k, d_v)
+                                       : split_layout(B, T, H_v, d_k, d_v, sp).total;
+  // room for the chunk form as well where the shape allows it (any gate form:
+  // the size does not depend on it)
+  const bool chunk_shape = bf16 && d_k == 128 && d_v == 128 && B > 0 && T > 0;
+  const size_t chunked = chunk_shape ? backward_chunked_workspace_bytes(B, T, H_qk, H_v) : 0;
+  return per_token > chunked ? per_token : chunked;
 }
 
 // Checkpoints: per (head, column block) BT / kSub + B slots of d_k x CB fp32
@@ -1232,6 +1237,17 @@ size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v) {
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
+  // GDN2_BACKWARD_CHUNKED, read at each call: 0 never runs the chunk form, 2
+  // requires it (hipErrorNotSupported where it cannot run), else it runs
+  // wherever it applies
+  const char *cenv = getenv("GDN2_BACKWARD_CHUNKED");
+  const int cmode = cenv ? atoi(cenv) : 1;
+  if (cmode != 0 && backward_chunked_eligible(a)) {
+    bool ran = false;
+    const hipError_t e = launch_backward_chunked(a, st, &ran);
+    if (e != hipSuccess || ran) return e;
+  }
+  if (cmode == 2) return hipErrorNotSupported;
   if (!a.cu_seqlens) {
     const BwdSplit sp = backward_split_plan(a.B, a.T, a.H_qk, a.H_v, a.d_k, a.d_v, a.bf16);
     if (sp.nseg > 1) return launch_backward_split(a, sp, st);

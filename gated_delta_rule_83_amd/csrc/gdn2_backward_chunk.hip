@@ -1,0 +1,964 @@
+// gdn2_backward_chunk.hip -- the backward pass in chunk form, on the matrix
+// cores (bf16 inputs, d_k = d_v = 128, per-channel fp32 gates).
+//
+// The forward step of one chunk of C tokens from its entering state S0
+// (Gated DeltaNet-2 post on tilnote.io, GDN-2 design section; the chunk form
+// of the delta rule's WY representation), with cumulative decays
+// gamma_t = a_1 ... a_t per key channel, an anchor A per channel (1, or the
+// decay at the chunk's middle when the chunk decays too far) and
+// lambda_t = gamma_t / A, mu_s = A / gamma_s:
+//   Ql = lambda q, Kl = lambda k, Km = mu k, Bm = mu b k, U = w v,
+//   S0a = diag(A) S0, Akk = stril(Kl Km^T), Akb = stril(Kl Bm^T),
+//   Mqk = tril(Ql Km^T), Mqb = tril(Ql Bm^T), L = I + Akb,
+//   R = L^-1 (Kl S0a + Akk U)            (the erase reads r_t)
+//   O = Ql S0a + Mqk U - Mqb R            (the outputs)
+//   S_C = diag(gamma_C / A) (S0a + Km^T U - Bm^T R).
+// Its adjoint, given dO and dS_C (the gradient of the chunk's exiting
+// state), with dSs = diag(gamma_C / A) dS_C:
+//   dR = -Bm dSs - Mqb^T dO,  dZ = L^-T dR,
+//   dU = Km dSs + Mqk^T dO + Akk^T dZ     (-> dv = w dU, dw = v dU)
+//   dMqk = tril(dO U^T), dMqb = -tril(dO R^T), dAkk = stril(dZ U^T),
+//   dAkb = -stril(dZ R^T),
+//   dQl = dO S0a^T + dMqk Km + dMqb Bm,  dKl = dZ S0a^T + dAkk Km + dAkb Bm,
+//   dKm = U dSs^T + dMqk^T Ql + dAkk^T Kl, dBm = -R dSs^T + dMqb^T Ql + dAkb^T Kl,
+//   dq = lambda dQl, dk = lambda dKl + mu dKm + mu b dBm, db = mu k dBm,
+// the log-decay gradient per token and channel
+//   dg_t = Ql dQl + Kl dKl - Km dKm - Bm dBm  (+ rowsum(dS_C * S_C) at t = C),
+// da_t = (sum over t' >= t of dg_t') / a_t, and the adjoint entering the chunk
+//   dS_prev = diag(gamma_C) dS_C + Kd^T dZ + Qd^T dO  (Kd = gamma k, Qd = gamma q).
+// The anchor cancels in every product; the operands only carry factors up
+// to e^60 (the prefill's chunk classes). Chunks that decay faster than the
+// middle anchor can carry (the prefill steps them token by token) are not
+// handled here: the host then runs the per-token backward instead.
+//
+// Four launches:
+//   1. the prefill, storing the state entering every chunk (bf16);
+//   2. bwd_prep_kernel, per chunk: the operands of the chunk's adjoint step
+//      dS_prev = diag(gamma_C) dS_C - Kd^T (Wt dS_C) + Qe^T dO, with
+//      Wt = L^-T Bc, Qe = Qd - (L^-T Mqb^T)^T Kd, Bc = (gamma_C / gamma) b k,
+//      stored in the order of the MFMA fragments that read them;
+//   3. bwd_dstate_kernel, per (sequence, head, 64 value columns): the
+//      adjoint of the state from the last chunk to the first (three MFMA
+//      products per chunk), storing dS_C of every chunk (bf16) and dS0;
+//   4. bwd_grad_kernel, per (sequence, query/key head, chunk): every
+//      gradient of the chunk from its stored state and adjoint, summing the
+//      value heads that share the query/key head.
+#include <hip/hip_runtime.h>
+
+#include "gdn2_device.hpp"
+#include "gdn2_internal.hpp"
+
+namespace gdn2 {
+namespace {
+
+constexpr int kC = 32;  // chunk length
+using OB = Op<true>;
+using BF = __bf16;
+using Fr = OB::Frag;
+using P2 = Pair<true>;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// e^-60: the smallest decay over a chunk (anchor at its start) or over each
+// half of it (anchor at its middle) whose inverse the operands may carry
+constexpr float kMinDecay = 8.75651076e-27f;
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- LDS fragments
+// Lane l: c = l & 15, g = l >> 4. Conventions of gdn2_device.hpp.
+
+// bf16 arrays in LDS hold rows of W elements (W = 128, 64 or 32) as 8-byte
+// chunks of 4 elements; chunk q of row r sits at q ^ swz<W>(r). The
+// permutations keep the two read patterns below free of bank conflicts (64
+// banks; 16 lanes per pass): a fragment read (16 lanes on 16 consecutive
+// rows, one chunk each) and a transposing read (16 lanes on 4 consecutive
+// rows x 4 consecutive chunks), and row writes of 16 lanes on consecutive
+// chunks.
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(W == 128 || W == 64 || W == 32, "row width");
+  if constexpr (W == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (W == 64) return ((r >> 1) & 1) << 2;
+  else return (r >> 2) & 7;
+}
+// index of element (r, col)
+template <int W>
+__device__ __forceinline__ int sx(int r, int col) {
+  return r * W + (((col >> 2) ^ swz<W>(r)) << 2) + (col & 3);
+}
+
+// lane gets X[k0 + 4g + j][m0 + c], j = 0..3: a transposing LDS read (lane
+// 4a + b of a 16-lane group receives element b of the 8-byte chunks
+// addressed by lanes a, a + 4, a + 8, a + 12)
+template <int W>
+__device__ __forceinline__ Fr tr_frag(const BF *X, int k0, int m0, int c, int g) {
+  const BF *p = X + sx<W>(k0 + 4 * g + (c >> 2), m0 + 4 * (c & 3));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16 *)(__attribute__((address_space(3))) const char *)p);
+  return __builtin_bit_cast(Fr, r);
+}
+// K32 operand whose 16 rows (A: rows m, or B: columns n) are rows of X and
+// whose k runs along X's rows: X[m0 + c][k0 + ...]
+template <int W>
+__device__ __forceinline__ P2 op_rows(const BF *X, int m0, int k0, int c, int g) {
+  const int r = m0 + c;
+  return P2{OB::ld(X + sx<W>(r, k0 + 4 * g)), OB::ld(X + sx<W>(r, k0 + 16 + 4 * g))};
+}
+// K32 operand whose k runs down X's columns: X[k0 + ...][m0 + c]
+template <int W>
+__device__ __forceinline__ P2 op_cols(const BF *X, int m0, int k0, int c, int g) {
+  return P2{tr_frag<W>(X, k0, m0, c, g), tr_frag<W>(X, k0 + 16, m0, c, g)};
+}
+__device__ __forceinline__ floatx4 mma(floatx4 acc, const P2 &a, const P2 &b) {
+  return OB::mma32(acc, a.lo, a.hi, b.lo, b.hi);
+}
+// two accumulator tiles (k rows 0-15 and 16-31 of a K32 block) as an operand
+__device__ __forceinline__ P2 acc_pair(floatx4 x0, floatx4 x1) { return P2{OB::from_acc(x0), OB::from_acc(x1)}; }
+__device__ __forceinline__ floatx4 fr_f32(Fr x) { return __builtin_convertvector(x, floatx4); }
+// reciprocals (v_rcp_f32, 1 ulp): of lambda and of the decays, within [e^-60, e^60]
+__device__ __forceinline__ floatx4 rcp4(floatx4 x) {
+  return floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
+                 __builtin_amdgcn_rcpf(x[3])};
+}
+
+// Per-channel factors of one chunk. mode: 0 = anchor at the chunk start
+// (A = 1), 1 = at the middle token (A = gamma_{C/2-1}), 2 = neither keeps
+// the factors below e^60. h1, h2: the decay over each half.
+__device__ __forceinline__ int chan_mode(const float (&a)[kC], float &h1, float &h2) {
+  h1 = 1.f;
+  h2 = 1.f;
+#pragma unroll
+  for (int t = 0; t < kC / 2; ++t) h1 *= a[t];
+#pragma unroll
+  for (int t = kC / 2; t < kC; ++t) h2 *= a[t];
+  return (h1 * h2 >= kMinDecay) ? 0 : (h1 >= kMinDecay && h2 >= kMinDecay) ? 1 : 2;
+}
+// x: the decays a_t in, lambda_t = gamma_t / A out; the anchor A, gamma_C
+// (may underflow to 0 in mode 1) and gamma_C / A
+__device__ __forceinline__ void chan_lambda(float (&x)[kC], int mode, float h1, float h2, float &A, float &gC,
+                                            float &gCA) {
+  if (mode == 0) {
+    float gm = 1.f;
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      gm *= x[t];
+      x[t] = gm;
+    }
+    A = 1.f;
+    gC = gm;
+    gCA = gm;
+  } else {
+    // prod_{C/2 <= s <= t} a_s from the middle on, 1 / prod_{t < s < C/2} a_s before it
+    float m = 1.f;
+#pragma unroll
+    for (int t = kC / 2; t < kC; ++t) {
+      m *= x[t];
+      x[t] = m;
+    }
+    float y = 1.f;
+#pragma unroll
+    for (int t = kC / 2 - 1; t >= 0; --t) {
+      const float at = x[t];
+      x[t] = 1.f / y;
+      y *= at;
+    }
+    A = h1;
+    gC = h1 * h2;
+    gCA = h2;
+  }
+}
+
+// lambda_t per channel from the chunk's decays staged in LDS (stage: [C][D]
+// fp32, 1 past the end, written and synchronised by the caller) into lam
+// (may be the same array); the anchor, gamma_C and gamma_C / A per channel.
+// Returns the chunk's mode (the same in every thread; mode 2 writes
+// nothing). Every thread of the workgroup calls it; it ends with a barrier.
+template <int D>
+__device__ int lambda_scan(const float *stage, float *lam, float *Ach, float *gCch, float *gCAch, int tid) {
+  float x[kC], h1 = 1.f, h2 = 1.f;
+  int m = 0;
+  if (tid < D) {
+#pragma unroll
+    for (int t = 0; t < kC; ++t) x[t] = stage[t * D + tid];
+    m = chan_mode(x, h1, h2);
+  }
+  const bool any2 = __syncthreads_or(m == 2) != 0;
+  const bool any1 = __syncthreads_or(m == 1) != 0;
+  const int mode = any2 ? 2 : any1 ? 1 : 0;
+  if (mode != 2 && tid < D) {
+    float A, gC, gCA;
+    chan_lambda(x, mode, h1, h2, A, gC, gCA);
+#pragma unroll
+    for (int t = 0; t < kC; ++t) lam[t * D + tid] = x[t];
+    Ach[tid] = A;
+    gCch[tid] = gC;
+    gCAch[tid] = gCA;
+  }
+  __syncthreads();
+  return mode;
+}
+
+// The e-th quad (4 channels) of a chunk's [C][D] rows: token and channel.
+template <int D>
+__device__ __forceinline__ int quad_t(int e) { return e / (D / 4); }
+template <int D>
+__device__ __forceinline__ int quad_i(int e) { return 4 * (e % (D / 4)); }
+
+// (I + N)^-1 for N strictly lower triangular (fp32 [C][C], LDS), written
+// as bf16 into Li ([C][C] row-major); lanes 0..C-1 of one wave, lane j a
+// column: x_t = delta_tj - sum_{u<t} N[t][u] x_u (zero above the diagonal
+// without branches: every x_u with u < j is zero)
+__device__ __forceinline__ void unit_lower_inverse(const float (*N)[kC], BF *Li, int j) {
+  asm volatile("" : "+v"(j));  // keeps the delta_tj selects here (hoisted, they were spilled)
+  float x[kC];
+#pragma unroll
+  for (int t = 0; t < kC; ++t) {
+    float s0 = t == j ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < t; ++u) {
+      if (u & 1)
+        s1 -= N[t][u] * x[u];
+      else
+        s0 -= N[t][u] * x[u];
+    }
+    x[t] = s0 + s1;
+    Li[sx<kC>(t, j)] = (BF)x[t];
+  }
+}
+
+__device__ __forceinline__ void st_bf4(BF *p, floatx4 v) { *reinterpret_cast<Fr *>(p) = __builtin_convertvector(v, Fr); }
+
+// ---------------------------------------------------------------- layouts
+struct ChunkLayout {
+  int B, T, H_qk, H_v, nch;
+  size_t cst, dst, prep, gc, flag, total;  // byte offsets of the workspace regions
+};
+
+template <int D>
+ChunkLayout chunk_layout(int B, int T, int H_qk, int H_v) {
+  ChunkLayout l;
+  l.B = B; l.T = T; l.H_qk = H_qk; l.H_v = H_v;
+  l.nch = (T + kC - 1) / kC;
+  const size_t units = (size_t)B * H_v, mat = (size_t)D * D * 2;
+  l.cst = 0;
+  l.dst = align256(units * (l.nch + 1) * mat);
+  l.prep = l.dst + align256(units * l.nch * mat);
+  l.gc = l.prep + align256(units * l.nch * 3 * kC * D * 2);
+  l.flag = l.gc + align256(units * l.nch * D * 4);
+  l.total = l.flag + 256;
+  return l;
+}
+
+// ---------------------------------------------------------------- 2. chunk operands
+// Per (unit = n * H_v + h, chunk): Wt as A fragments [tb][ib][lane][4]
+// (lane (c, g) of tile (tb, ib): Wt[16tb + c][16ib + 4g + j]), then Kd and
+// Qe as transposed A fragments [ib][tb][lane][4] (Kd[16tb + 4g + j][16ib + c]),
+// and gamma_C per channel. Wt = L^-T Bc and Qe = Qd - Mqb (L^-1 Kd).
+template <int D>
+struct PrepSmem {
+  alignas(16) float lam[kC * D];
+  alignas(16) BF Ql[kC * D], Kl[kC * D], Bm[kC * D], Kd[kC * D], Qd[kC * D], Bc[kC * D];
+  alignas(16) float Akb[kC][kC];
+  alignas(16) BF Mqb[kC * kC], Lb[kC * kC];
+  alignas(16) float A[D], gC[D], gCA[D];
+};
+
+struct PrepParams {
+  const uint16_t *q, *k;
+  const float *a, *b;
+  BF *prep;
+  float *gc;
+  int *flag;
+  int T, H_qk, H_v, nch;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p) {
+  static_assert(D == 128, "d_k = 128");
+  constexpr int NT = 256;
+  __shared__ PrepSmem<D> sm;
+  const int chunk = blockIdx.x % p.nch, unit = blockIdx.x / p.nch;
+  const int n = unit / p.H_v, h = unit - n * p.H_v, gq = h / (p.H_v / p.H_qk);
+  const int t0 = chunk * kC, Tc = min(kC, p.T - t0);
+  const size_t tok0 = (size_t)n * p.T + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+
+  // every request of the chunk first: decays, q, k, b (zero past the end)
+  constexpr int NQ = kC * D / 4 / NT;
+  floatx4 av[NQ], bv[NQ];
+  Fr qv[NQ], kv[NQ];
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+    av[it] = floatx4{1.f, 1.f, 1.f, 1.f};
+    bv[it] = zero4();
+    qv[it] = kv[it] = OB::zero();
+    if (t < Tc) {
+      const size_t row = tok0 + t;
+      av[it] = *reinterpret_cast<const floatx4 *>(p.a + (row * p.H_v + h) * D + i4);
+      bv[it] = *reinterpret_cast<const floatx4 *>(p.b + (row * p.H_v + h) * D + i4);
+      qv[it] = *reinterpret_cast<const Fr *>(p.q + (row * p.H_qk + gq) * D + i4);
+      kv[it] = *reinterpret_cast<const Fr *>(p.k + (row * p.H_qk + gq) * D + i4);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int e = tid + NT * it;
+    *reinterpret_cast<floatx4 *>(&sm.lam[quad_t<D>(e) * D + quad_i<D>(e)]) = av[it];
+  }
+  __syncthreads();
+  const int mode = lambda_scan<D>(sm.lam, sm.lam, sm.A, sm.gC, sm.gCA, tid);
+  if (mode == 2) {  // uniform: some channel decays too far for either anchor
+    if (tid == 0) atomicOr(p.flag, 1);
+    return;
+  }
+  if (tid < D) p.gc[((size_t)unit * p.nch + chunk) * D + tid] = sm.gC[tid];
+  // operands: lambda-scaled q, k; mu-scaled b k; gamma-scaled k, q; the
+  // carry's (gamma_C / gamma) b k
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+    const floatx4 q4 = fr_f32(qv[it]), k4 = fr_f32(kv[it]);
+    const floatx4 lam = *reinterpret_cast<const floatx4 *>(&sm.lam[t * D + i4]);
+    const floatx4 A = *reinterpret_cast<const floatx4 *>(&sm.A[i4]);
+    const floatx4 gCA = *reinterpret_cast<const floatx4 *>(&sm.gCA[i4]);
+    const floatx4 mu = rcp4(lam), bk = bv[it] * k4;
+    st_bf4(&sm.Ql[sx<D>(t, i4)], lam * q4);
+    st_bf4(&sm.Kl[sx<D>(t, i4)], lam * k4);
+    st_bf4(&sm.Bm[sx<D>(t, i4)], mu * bk);
+    st_bf4(&sm.Kd[sx<D>(t, i4)], A * lam * k4);
+    st_bf4(&sm.Qd[sx<D>(t, i4)], A * lam * q4);
+    st_bf4(&sm.Bc[sx<D>(t, i4)], gCA * mu * bk);
+  }
+  __syncthreads();
+  // Gram tiles: Akb = stril(Kl Bm^T) (fp32), Mqb = tril(Ql Bm^T) (bf16);
+  // lower tiles (0,0), (1,0), (1,1) of each
+  for (int tile = wave; tile < 6; tile += NT / 64) {
+    const int mat = tile / 3, tt = tile % 3;
+    const int tb = tt == 0 ? 0 : 1, sb = tt == 2 ? 1 : 0;
+    const BF *L = mat == 0 ? sm.Kl : sm.Ql;
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32)
+      acc = mma(acc, op_rows<D>(L, 16 * tb, k0, c, g), op_rows<D>(sm.Bm, 16 * sb, k0, c, g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 16 * tb + 4 * g + j, s = 16 * sb + c;
+      if (mat == 0) {
+        sm.Akb[t][s] = s < t ? acc[j] : 0.f;
+      } else {
+        sm.Mqb[sx<kC>(t, s)] = (BF)(s <= t ? acc[j] : 0.f);
+        sm.Mqb[sx<kC>(t & 15, 16 + (s & 15))] = (BF)0.f;  // the upper tile
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kC) unit_lower_inverse(sm.Akb, sm.Lb, tid);
+  __syncthreads();
+
+  BF *out = p.prep + ((size_t)unit * p.nch + chunk) * 3 * kC * D;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int ib = 2 * wave + x;
+    // Wt^T = Bc^T L^-1: the accumulator of tile (ib, tb) is Wt's A fragment
+    // Wk = L^-1 Kd, Qe = Qd - Mqb Wk
+    floatx4 Wk[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const floatx4 wt = mma(zero4(), op_cols<D>(sm.Bc, 16 * ib, 0, c, g), op_cols<kC>(sm.Lb, 16 * tb, 0, c, g));
+      *reinterpret_cast<Fr *>(out + ((tb * (D / 16) + ib) * 64 + lane) * 4) = OB::from_acc(wt);
+      Wk[tb] = mma(zero4(), op_rows<kC>(sm.Lb, 16 * tb, 0, c, g), op_cols<D>(sm.Kd, 16 * ib, 0, c, g));
+    }
+    const P2 Wkn = acc_pair(-Wk[0], -Wk[1]);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const Fr kd = tr_frag<D>(sm.Kd, 16 * tb, 16 * ib, c, g);
+      *reinterpret_cast<Fr *>(out + kC * D + ((ib * 2 + tb) * 64 + lane) * 4) = kd;
+      floatx4 qe = fr_f32(tr_frag<D>(sm.Qd, 16 * tb, 16 * ib, c, g));
+      qe = mma(qe, op_rows<kC>(sm.Mqb, 16 * tb, 0, c, g), Wkn);
+      *reinterpret_cast<Fr *>(out + 2 * kC * D + ((ib * 2 + tb) * 64 + lane) * 4) = OB::from_acc(qe);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 3. adjoint of the state
+// One workgroup per (unit, 64 value columns), four waves of 16 columns;
+// lane (c, g) holds dS[16 mt + 4g + j][col] in dS[mt][j]. From the last
+// chunk to the first: dS (the adjoint of chunk c's exiting state) is stored
+// (bf16, [unit][chunk][column][channel]), then
+// dS <- diag(gamma_C) dS - Kd^T (Wt dS) + Qe^T dO.
+// A chunk's operands are requested kPF chunks ahead into one of kPF
+// register sets, and staged in LDS one chunk ahead.
+constexpr int kPF = 2;
+template <int D>
+struct DstSmem {
+  alignas(16) BF ops[2][3 * kC * D];
+  alignas(16) BF dO[2][kC * 64];
+  alignas(16) float gc[2][D];
+};
+
+struct DstParams {
+  const BF *prep;
+  const float *gc;
+  const uint16_t *dO;
+  const float *dST;
+  float *dS0;
+  BF *dst;
+  int T, H_v, nch;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
+  static_assert(D == 128, "d = 128");
+  constexpr int NCB = D / 64, NMT = D / 16;
+  constexpr int OPS16 = 3 * kC * D / 8;  // 16-byte pieces of a chunk's operands
+  static_assert(OPS16 % 256 == 0, "whole pieces per thread");
+  __shared__ DstSmem<D> sm;
+  const int cb = blockIdx.x % NCB, unit = blockIdx.x / NCB;
+  const int n = unit / p.H_v, h = unit - n * p.H_v;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int col = cb * 64 + 16 * wave + c;
+
+  floatx4 dS[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dS[mt][j] = p.dST ? p.dST[((size_t)unit * D + 16 * mt + 4 * g + j) * D + col] : 0.f;
+
+  struct Raw {
+    uint4 o[OPS16 / 256];
+    uint4 d;
+    floatx4 gcv;
+  };
+  // chunk ch's operands into registers; every request is issued on every
+  // call (past the end: a clamped row, zeroed), so that the number of
+  // requests between a request and its use never varies
+  auto fetch = [&](int ch, Raw &r) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.prep + ((size_t)unit * p.nch + ch) * 3 * kC * D);
+#pragma unroll
+    for (int it = 0; it < OPS16 / 256; ++it) r.o[it] = src[tid + 256 * it];
+    const int t = tid >> 3, q8 = tid & 7;  // 32 tokens x 8 pieces of 8 columns
+    const int tok = ch * kC + t;
+    const uint4 d = *reinterpret_cast<const uint4 *>(p.dO + ((size_t)n * p.T + min(tok, p.T - 1)) * p.H_v * D +
+                                                    (size_t)h * D + cb * 64 + 8 * q8);
+    r.d = tok < p.T ? d : uint4{0, 0, 0, 0};
+    r.gcv = *reinterpret_cast<const floatx4 *>(p.gc + ((size_t)unit * p.nch + ch) * D + 4 * (tid % (D / 4)));
+  };
+  auto stash = [&](int buf, const Raw &r) {
+    uint4 *dst = reinterpret_cast<uint4 *>(sm.ops[buf]);
+#pragma unroll
+    for (int it = 0; it < OPS16 / 256; ++it) dst[tid + 256 * it] = r.o[it];
+    *reinterpret_cast<uint4 *>(&sm.dO[buf][sx<64>(tid >> 3, 8 * (tid & 7))]) = r.d;
+    if (tid < D / 4) reinterpret_cast<floatx4 *>(sm.gc[buf])[tid] = r.gcv;
+  };
+
+  Raw r[kPF];
+  // body for the k-th chunk from the last (register set k % kPF = S)
+  auto body = [&](auto S, int k) {
+    constexpr int s = decltype(S)::value;
+    const int ch = p.nch - 1 - k, buf = k & 1;
+    fetch(max(ch - kPF, 0), r[s]);  // set s held chunk ch, staged in the previous step
+    BF *dsto = p.dst + (((size_t)unit * p.nch + ch) * D + col) * D + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<Fr *>(dsto + 16 * mt) = OB::from_acc(dS[mt]);
+    const BF *Wt = sm.ops[buf], *Kd = sm.ops[buf] + kC * D, *Qe = sm.ops[buf] + 2 * kC * D;
+    auto frag = [&](const BF *base, int idx) { return OB::ld(base + (idx * 64 + lane) * 4); };
+    // Y = -Wt dS (tokens x this wave's columns)
+    floatx4 Y[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < NMT / 2; ++kk)
+        acc = mma(acc, P2{frag(Wt, tb * NMT + 2 * kk), frag(Wt, tb * NMT + 2 * kk + 1)},
+                  acc_pair(dS[2 * kk], dS[2 * kk + 1]));
+      Y[tb] = -acc;
+    }
+    const P2 dOf{tr_frag<64>(sm.dO[buf], 0, 16 * wave, c, g), tr_frag<64>(sm.dO[buf], 16, 16 * wave, c, g)};
+    const P2 Yf = acc_pair(Y[0], Y[1]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const floatx4 gcv = *reinterpret_cast<const floatx4 *>(&sm.gc[buf][16 * mt + 4 * g]);
+      floatx4 acc = dS[mt] * gcv;
+      acc = mma(acc, P2{frag(Qe, mt * 2), frag(Qe, mt * 2 + 1)}, dOf);
+      acc = mma(acc, P2{frag(Kd, mt * 2), frag(Kd, mt * 2 + 1)}, Yf);
+      dS[mt] = acc;
+    }
+    // the next chunk (set s + 1, requested two steps ago) into the other
+    // buffer, last read in the previous step
+    if (k + 1 < p.nch) stash(buf ^ 1, r[(s + 1) % kPF]);
+    __syncthreads();
+  };
+
+  static_for<kPF>([&](auto S) { fetch(max(p.nch - 1 - decltype(S)::value, 0), r[decltype(S)::value]); });
+  stash(0, r[0]);
+  __syncthreads();
+  for (int k = 0; k < p.nch; k += kPF) {
+    static_for<kPF>([&](auto S) {
+      if (k + decltype(S)::value < p.nch) body(S, k + decltype(S)::value);
+    });
+  }
+  if (p.dS0) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p.dS0[((size_t)unit * D + 16 * mt + 4 * g + j) * D + col] = dS[mt][j];
+  }
+}
+
+// ---------------------------------------------------------------- 4. gradients of a chunk
+// One workgroup of eight waves per (sequence, query/key head, chunk); wave
+// w owns value columns 16w.. and key channels 16w.. of every product.
+template <int D>
+struct GradSmem {
+  alignas(16) BF Ql[kC * D], Kl[kC * D], Km[kC * D], Bm[kC * D];
+  alignas(16) BF U[kC * D], dO[kC * D], R[kC * D], dZ[kC * D];
+  // S0a^T and dSs^T ([column][channel]); after the key-side products the
+  // log-decay gradients and the carry terms (S0a region), the decays and
+  // lambda again (dSs region). R and dZ hold lambda (fp32 [C][D]) while the
+  // operands are built.
+  alignas(16) BF S0a[D * D], dSs[D * D];
+  alignas(16) BF Akk[kC * kC], Mqk[kC * kC], Mqb[kC * kC], Lb[kC * kC];
+  alignas(16) BF dMqk[kC * kC], dMqb[kC * kC], dAkk[kC * kC], dAkb[kC * kC];
+  alignas(16) float Akb[kC][kC];
+  alignas(16) float A[D], gCA[D], gC[D], rs[8][D];
+};
+
+struct GradParams {
+  const uint16_t *q, *k, *v, *dO;
+  const float *a, *b, *w;
+  const BF *cst, *dst;
+  uint16_t *dq, *dk, *dv;
+  float *da, *db, *dw;
+  int T, H_qk, H_v, nch;
+};
+
+// GRP: several value heads per query/key head (G = H_v / H_qk > 1, looped
+// over); the G = 1 instance has no loop, so nothing is kept across heads.
+template <int D, bool GRP>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
+  static_assert(D == 128, "d = 128");
+  constexpr int NT = 512;
+  static_assert(NT / 64 == D / 16, "one wave per 16 columns");
+  __shared__ GradSmem<D> sm;
+  static_assert(sizeof(GradSmem<D>::R) + sizeof(GradSmem<D>::dZ) == kC * D * 4, "R, dZ hold lambda");
+  float *const lam0 = reinterpret_cast<float *>(sm.R);            // [C][D], over R and dZ
+  float *const dgF = reinterpret_cast<float *>(sm.S0a);           // [C][D]
+  float *const crF = reinterpret_cast<float *>(sm.S0a) + kC * D;  // [C][D]
+  float *const aE = reinterpret_cast<float *>(sm.dSs);            // [C][D]
+  float *const lamE = reinterpret_cast<float *>(sm.dSs) + kC * D;  // [C][D]
+  const int chunk = blockIdx.x % p.nch, ug = blockIdx.x / p.nch;  // ug = n * H_qk + gq
+  const int n = ug / p.H_qk, gq = ug - n * p.H_qk;
+  const int G = GRP ? p.H_v / p.H_qk : 1;
+  const int t0 = chunk * kC, Tc = min(kC, p.T - t0);
+  const size_t tok0 = (size_t)n * p.T + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const size_t qk_row = (size_t)p.H_qk * D, v_row = (size_t)p.H_v * D;
+  const int nb = wave, ib = wave;  // this wave's 16-column blocks
+
+  // dq, dk summed over the group's value heads; tiles (tb, ib)
+  floatx4 dq[2] = {zero4(), zero4()}, dk[2] = {zero4(), zero4()};
+
+  for (int hv = 0; hv < G; ++hv) {
+    const int h = gq * G + hv;
+    const size_t unit = (size_t)n * p.H_v + h;
+    // ---- every request of the chunk first: decays, q, k, b, v, w, dO
+    // (zero past the end), the entering state and the exiting adjoint
+    constexpr int NQ = kC * D / 4 / NT, NS = D * D / 4 / NT;
+    floatx4 av[NQ], bv[NQ], wv[NQ];
+    Fr qv[NQ], kv[NQ], vv[NQ], ov[NQ], s0v[NS], dsv[NS];
+    {
+      const BF *s0 = p.cst + (unit * (p.nch + 1) + chunk) * D * D;
+      const BF *ds = p.dst + (unit * p.nch + chunk) * D * D;
+#pragma unroll
+      for (int it = 0; it < NS; ++it) {
+        const int e = tid + NT * it;
+        s0v[it] = *reinterpret_cast<const Fr *>(s0 + 4 * e);
+        dsv[it] = *reinterpret_cast<const Fr *>(ds + 4 * e);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+      av[it] = floatx4{1.f, 1.f, 1.f, 1.f};
+      bv[it] = wv[it] = zero4();
+      qv[it] = kv[it] = vv[it] = ov[it] = OB::zero();
+      if (t < Tc) {
+        const size_t row = tok0 + t, off = row * v_row + (size_t)h * D + i4;
+        av[it] = *reinterpret_cast<const floatx4 *>(p.a + off);
+        bv[it] = *reinterpret_cast<const floatx4 *>(p.b + off);
+        wv[it] = *reinterpret_cast<const floatx4 *>(p.w + off);
+        qv[it] = *reinterpret_cast<const Fr *>(p.q + row * qk_row + (size_t)gq * D + i4);
+        kv[it] = *reinterpret_cast<const Fr *>(p.k + row * qk_row + (size_t)gq * D + i4);
+        vv[it] = *reinterpret_cast<const Fr *>(p.v + off);
+        ov[it] = *reinterpret_cast<const Fr *>(p.dO + off);
+      }
+    }
+    // ---- lambda (the chunk's anchor: at its start or its middle; chunks
+    // that need neither do not reach this kernel), then the operands
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it;
+      *reinterpret_cast<floatx4 *>(&lam0[quad_t<D>(e) * D + quad_i<D>(e)]) = av[it];
+    }
+    __syncthreads();
+    lambda_scan<D>(lam0, lam0, sm.A, sm.gC, sm.gCA, tid);
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+      const floatx4 lam = *reinterpret_cast<const floatx4 *>(&lam0[t * D + i4]), mu = rcp4(lam);
+      const floatx4 q4 = fr_f32(qv[it]), k4 = fr_f32(kv[it]);
+      st_bf4(&sm.Ql[sx<D>(t, i4)], lam * q4);
+      st_bf4(&sm.Kl[sx<D>(t, i4)], lam * k4);
+      st_bf4(&sm.Km[sx<D>(t, i4)], mu * k4);
+      st_bf4(&sm.Bm[sx<D>(t, i4)], mu * bv[it] * k4);
+      st_bf4(&sm.U[sx<D>(t, i4)], fr_f32(vv[it]) * wv[it]);
+      *reinterpret_cast<Fr *>(&sm.dO[sx<D>(t, i4)]) = ov[it];
+    }
+    // S0a = diag(A) S0 and dSs = diag(gamma_C / A) dS_C, both [column][channel];
+    // rs[i] = sum_j dS_C S0 over this thread's columns (then over the lane
+    // pair 32 apart, whose quads are the same channels)
+    {
+      const int i4 = 4 * (tid % (D / 4));
+      const floatx4 Av = *reinterpret_cast<const floatx4 *>(&sm.A[i4]);
+      const floatx4 Gv = *reinterpret_cast<const floatx4 *>(&sm.gCA[i4]);
+      floatx4 rsum = zero4();
+#pragma unroll
+      for (int it = 0; it < NS; ++it) {
+        const int e = tid + NT * it;
+        const floatx4 sv = fr_f32(s0v[it]), dv = fr_f32(dsv[it]);
+        rsum += sv * dv;
+        st_bf4(&sm.S0a[sx<D>(quad_t<D>(e), i4)], sv * Av);
+        st_bf4(&sm.dSs[sx<D>(quad_t<D>(e), i4)], dv * Gv);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rsum[j] += __shfl_xor(rsum[j], 32);
+      if ((lane & 32) == 0) *reinterpret_cast<floatx4 *>(&sm.rs[tid / (D / 2)][i4]) = rsum;
+    }
+    __syncthreads();
+    // ---- Gram tiles (three lower 16x16 tiles of each; the upper one is zero)
+    for (int tile = wave; tile < 12; tile += NT / 64) {
+      const int mat = tile / 3, tt = tile % 3;
+      const int tb = tt == 0 ? 0 : 1, sb = tt == 2 ? 1 : 0;
+      const BF *L = mat < 2 ? sm.Kl : sm.Ql;  // Akk, Akb | Mqk, Mqb
+      const BF *Rt = (mat & 1) ? sm.Bm : sm.Km;
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32)
+        acc = mma(acc, op_rows<D>(L, 16 * tb, k0, c, g), op_rows<D>(Rt, 16 * sb, k0, c, g));
+      const bool strict = mat < 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * tb + 4 * g + j, s = 16 * sb + c;
+        const float x = (strict ? s < t : s <= t) ? acc[j] : 0.f;
+        if (mat == 1) {
+          sm.Akb[t][s] = x;
+        } else {
+          BF *M = mat == 0 ? sm.Akk : mat == 2 ? sm.Mqk : sm.Mqb;
+          M[sx<kC>(t, s)] = (BF)x;
+          M[sx<kC>(t & 15, 16 + (s & 15))] = (BF)0.f;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < kC) unit_lower_inverse(sm.Akb, sm.Lb, tid);
+    __syncthreads();
+
+    // ---- value side (columns 16 nb ..)
+    {
+      const int jc = 16 * nb + c;
+      float wq[2][4], vq[2][4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * tb + 4 * g + j;
+          const size_t off = (tok0 + min(t, Tc - 1)) * v_row + (size_t)h * D + jc;
+          wq[tb][j] = p.w[off];
+          vq[tb][j] = bf16_to_f32(p.v[off]);
+        }
+      floatx4 Z[2], dR[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        floatx4 z = zero4(), r = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          z = mma(z, op_rows<D>(sm.Kl, 16 * tb, k0, c, g), op_rows<D>(sm.S0a, 16 * nb, k0, c, g));
+          r = mma(r, op_rows<D>(sm.Bm, 16 * tb, k0, c, g), op_rows<D>(sm.dSs, 16 * nb, k0, c, g));
+        }
+        z = mma(z, op_rows<kC>(sm.Akk, 16 * tb, 0, c, g), op_cols<D>(sm.U, 16 * nb, 0, c, g));
+        r = mma(r, op_cols<kC>(sm.Mqb, 16 * tb, 0, c, g), op_cols<D>(sm.dO, 16 * nb, 0, c, g));
+        Z[tb] = z;
+        dR[tb] = -r;
+      }
+      const P2 Zf = acc_pair(Z[0], Z[1]), dRf = acc_pair(dR[0], dR[1]);
+      floatx4 Rr[2], dZr[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        Rr[tb] = mma(zero4(), op_rows<kC>(sm.Lb, 16 * tb, 0, c, g), Zf);
+        dZr[tb] = mma(zero4(), op_cols<kC>(sm.Lb, 16 * tb, 0, c, g), dRf);
+      }
+      const P2 dZf = acc_pair(dZr[0], dZr[1]);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        floatx4 u = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32)
+          u = mma(u, op_rows<D>(sm.Km, 16 * tb, k0, c, g), op_rows<D>(sm.dSs, 16 * nb, k0, c, g));
+        u = mma(u, op_cols<kC>(sm.Mqk, 16 * tb, 0, c, g), op_cols<D>(sm.dO, 16 * nb, 0, c, g));
+        u = mma(u, op_cols<kC>(sm.Akk, 16 * tb, 0, c, g), dZf);
+        // dv = w dU, dw = v dU
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * tb + 4 * g + j;
+          if (t < Tc) {
+            const size_t off = (tok0 + t) * v_row + (size_t)h * D + jc;
+            p.dv[off] = f32_to_bf16(wq[tb][j] * u[j]);
+            p.dw[off] = vq[tb][j] * u[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * tb + 4 * g + j;
+          sm.R[sx<D>(t, jc)] = (BF)Rr[tb][j];
+          sm.dZ[sx<D>(t, jc)] = (BF)dZr[tb][j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- key side (channels 16 ib ..)
+    floatx4 dQl[2], dKl[2], dKm[2], dBm[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      floatx4 a0 = zero4(), a1 = zero4(), a2 = zero4(), a3 = zero4();
+#pragma unroll 1
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        const P2 s0 = op_cols<D>(sm.S0a, 16 * ib, k0, c, g), ds = op_cols<D>(sm.dSs, 16 * ib, k0, c, g);
+        a0 = mma(a0, op_rows<D>(sm.dO, 16 * tb, k0, c, g), s0);
+        a1 = mma(a1, op_rows<D>(sm.dZ, 16 * tb, k0, c, g), s0);
+        a2 = mma(a2, op_rows<D>(sm.U, 16 * tb, k0, c, g), ds);
+        a3 = mma(a3, op_rows<D>(sm.R, 16 * tb, k0, c, g), ds);
+      }
+      dQl[tb] = a0;
+      dKl[tb] = a1;
+      dKm[tb] = a2;
+      dBm[tb] = -a3;
+    }
+    // adjoints of the Gram matrices (lower tiles)
+    for (int tile = wave; tile < 12; tile += NT / 64) {
+      const int mat = tile / 3, tt = tile % 3;
+      const int tb = tt == 0 ? 0 : 1, sb = tt == 2 ? 1 : 0;
+      const BF *L = mat < 2 ? sm.dO : sm.dZ;  // dMqk, dMqb | dAkk, dAkb
+      const BF *Rt = (mat & 1) ? sm.R : sm.U;
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32)
+        acc = mma(acc, op_rows<D>(L, 16 * tb, k0, c, g), op_rows<D>(Rt, 16 * sb, k0, c, g));
+      const bool strict = mat >= 2;
+      const float sg = (mat & 1) ? -1.f : 1.f;
+      BF *M = mat == 0 ? sm.dMqk : mat == 1 ? sm.dMqb : mat == 2 ? sm.dAkk : sm.dAkb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * tb + 4 * g + j, s = 16 * sb + c;
+        M[sx<kC>(t, s)] = (BF)((strict ? s < t : s <= t) ? sg * acc[j] : 0.f);
+        M[sx<kC>(t & 15, 16 + (s & 15))] = (BF)0.f;
+      }
+    }
+    __syncthreads();
+    // Requested first: the decays again (for lambda and da at the end), b
+    // and k at this lane's positions
+    floatx4 av2[NQ];
+    float bq[2][4], kq[2][4];
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+      av2[it] = floatx4{1.f, 1.f, 1.f, 1.f};
+      if (t < Tc) av2[it] = *reinterpret_cast<const floatx4 *>(p.a + (tok0 + t) * v_row + (size_t)h * D + i4);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * tb + 4 * g + j, i = 16 * ib + c;
+        const size_t row = tok0 + min(t, Tc - 1);
+        bq[tb][j] = t < Tc ? p.b[row * v_row + (size_t)h * D + i] : 0.f;
+        kq[tb][j] = t < Tc ? bf16_to_f32(p.k[row * qk_row + (size_t)gq * D + i]) : 0.f;
+      }
+    // carry terms of the log-decay gradient (before the Gram parts are
+    // added), the Gram parts, then the log-decay gradient per token with
+    // the same bf16 operands as the products
+    {
+      const P2 km0 = op_cols<D>(sm.Km, 16 * ib, 0, c, g), bm0 = op_cols<D>(sm.Bm, 16 * ib, 0, c, g);
+      const P2 ql0 = op_cols<D>(sm.Ql, 16 * ib, 0, c, g), kl0 = op_cols<D>(sm.Kl, 16 * ib, 0, c, g);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const floatx4 ql = fr_f32(tr_frag<D>(sm.Ql, 16 * tb, 16 * ib, c, g));
+        const floatx4 kl = fr_f32(tr_frag<D>(sm.Kl, 16 * tb, 16 * ib, c, g));
+        const floatx4 km = fr_f32(tr_frag<D>(sm.Km, 16 * tb, 16 * ib, c, g));
+        const floatx4 bm = fr_f32(tr_frag<D>(sm.Bm, 16 * tb, 16 * ib, c, g));
+        const floatx4 cr = km * dKm[tb] + bm * dBm[tb];
+        dQl[tb] = mma(mma(dQl[tb], op_rows<kC>(sm.dMqk, 16 * tb, 0, c, g), km0),
+                      op_rows<kC>(sm.dMqb, 16 * tb, 0, c, g), bm0);
+        dKl[tb] = mma(mma(dKl[tb], op_rows<kC>(sm.dAkk, 16 * tb, 0, c, g), km0),
+                      op_rows<kC>(sm.dAkb, 16 * tb, 0, c, g), bm0);
+        dKm[tb] = mma(mma(dKm[tb], op_cols<kC>(sm.dMqk, 16 * tb, 0, c, g), ql0),
+                      op_cols<kC>(sm.dAkk, 16 * tb, 0, c, g), kl0);
+        dBm[tb] = mma(mma(dBm[tb], op_cols<kC>(sm.dMqb, 16 * tb, 0, c, g), ql0),
+                      op_cols<kC>(sm.dAkb, 16 * tb, 0, c, g), kl0);
+        const floatx4 dg = ql * dQl[tb] + kl * dKl[tb] - km * dKm[tb] - bm * dBm[tb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int o = (16 * tb + 4 * g + j) * D + 16 * ib + c;
+          crF[o] = cr[j];
+          dgF[o] = dg[j];
+        }
+      }
+    }
+    // lambda again (the dSs region is free), keeping the decays
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it;
+      *reinterpret_cast<floatx4 *>(&aE[quad_t<D>(e) * D + quad_i<D>(e)]) = av2[it];
+    }
+    __syncthreads();
+    lambda_scan<D>(aE, lamE, sm.A, sm.gC, sm.gCA, tid);
+    // dq, dk (summed over the group), db
+    {
+      const int i = 16 * ib + c;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * tb + 4 * g + j;
+          const float lam = lamE[t * D + i], mu = __builtin_amdgcn_rcpf(lam);
+          dq[tb][j] += lam * dQl[tb][j];
+          dk[tb][j] += lam * dKl[tb][j] + mu * (dKm[tb][j] + bq[tb][j] * dBm[tb][j]);
+          if (t < Tc) p.db[(tok0 + t) * v_row + (size_t)h * D + i] = mu * kq[tb][j] * dBm[tb][j];
+        }
+      }
+    }
+    // da: reverse sums of the log-decay gradient over the chunk; the chunk's
+    // end carries the exiting state's term and the carry terms
+    if (tid < D) {
+      const int i = tid;
+      float acc = 0.f;
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) acc += sm.rs[r8][i];
+      acc *= sm.gC[i];
+#pragma unroll 1
+      for (int t = 0; t < kC; ++t) acc += crF[t * D + i];
+#pragma unroll 1
+      for (int t = kC - 1; t >= 0; --t) {
+        acc += dgF[t * D + i];
+        if (t < Tc) p.da[(tok0 + t) * v_row + (size_t)h * D + i] = acc * __builtin_amdgcn_rcpf(aE[t * D + i]);
+      }
+    }
+    __syncthreads();
+  }
+  // dq, dk
+  {
+    const int i = 16 * ib + c;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * tb + 4 * g + j;
+        if (t < Tc) {
+          const size_t off = (tok0 + t) * qk_row + (size_t)gq * D + i;
+          p.dq[off] = f32_to_bf16(dq[tb][j]);
+          p.dk[off] = f32_to_bf16(dk[tb][j]);
+        }
+      }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host
+bool backward_chunked_eligible(const BackwardArgs &a) {
+  if (a.cu_seqlens || a.gate_form != kGateGeneral || !a.bf16 || a.d_k != 128 || a.d_v != 128) return false;
+  if (a.B <= 0 || a.T <= 0 || a.H_v % a.H_qk != 0) return false;
+  PrefillArgs fa{};
+  fa.B = a.B; fa.T = a.T; fa.H_qk = a.H_qk; fa.H_v = a.H_v; fa.d_k = a.d_k; fa.d_v = a.d_v;
+  fa.chunk = 64;
+  fa.bf16 = true;
+  fa.nct = prefill_pick_nct(a.B, a.H_v, a.d_v);
+  fa.force_nseg = 1;
+  return prefill_plan(fa).chunk == kC;
+}
+
+size_t backward_chunked_workspace_bytes(int B, int T, int H_qk, int H_v) {
+  return chunk_layout<128>(B, T, H_qk, H_v).total;
+}
+
+// Runs the chunk-form backward. *ran = false (and nothing written but the
+// workspace) when some chunk decays too fast for its anchors: the caller
+// then runs the per-token backward. Synchronises the stream once (after the
+// chunk operands) to read that flag.
+hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *ran) {
+  constexpr int D = 128;
+  *ran = false;
+  const ChunkLayout l = chunk_layout<D>(a.B, a.T, a.H_qk, a.H_v);
+  char *w = static_cast<char *>(a.workspace);
+  BF *cst = reinterpret_cast<BF *>(w + l.cst);
+  BF *dst = reinterpret_cast<BF *>(w + l.dst);
+  BF *prep = reinterpret_cast<BF *>(w + l.prep);
+  float *gc = reinterpret_cast<float *>(w + l.gc);
+  int *flag = reinterpret_cast<int *>(w + l.flag);
+  const int units = a.B * a.H_v;
+
+  hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
+  if (e != hipSuccess) return e;
+  // 1. the states entering every chunk
+  PrefillArgs fa{};
+  fa.B = a.B; fa.T = a.T; fa.H_qk = a.H_qk; fa.H_v = a.H_v; fa.d_k = a.d_k; fa.d_v = a.d_v;
+  fa.chunk = 64;
+  fa.bf16 = true;
+  fa.nct = prefill_pick_nct(a.B, a.H_v, a.d_v);
+  fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.a = a.a; fa.b = a.b; fa.w = a.w; fa.S0 = a.S0;
+  fa.force_nseg = 1;
+  fa.chunk_states = cst;
+  e = launch_prefill(fa, st);
+  if (e != hipSuccess) return e;
+  // 2. chunk operands of the state's adjoint
+  PrepParams pp{};
+  pp.q = static_cast<const uint16_t *>(a.q); pp.k = static_cast<const uint16_t *>(a.k);
+  pp.a = a.a; pp.b = a.b;
+  pp.prep = prep; pp.gc = gc; pp.flag = flag;
+  pp.T = a.T; pp.H_qk = a.H_qk; pp.H_v = a.H_v; pp.nch = l.nch;
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(units * l.nch), dim3(256), 0, st, pp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int hflag = 0;
+  if ((e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+  if (hflag) return hipSuccess;
+  // 3. the state's adjoint at every chunk boundary, and dS0
+  DstParams dp{};
+  dp.prep = prep; dp.gc = gc;
+  dp.dO = static_cast<const uint16_t *>(a.dO);
+  dp.dST = a.dST; dp.dS0 = a.dS0; dp.dst = dst;
+  dp.T = a.T; dp.H_v = a.H_v; dp.nch = l.nch;
+  hipLaunchKernelGGL(bwd_dstate_kernel<D>, dim3(units * (D / 64)), dim3(256), 0, st, dp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 4. the gradients
+  GradParams gp{};
+  gp.q = static_cast<const uint16_t *>(a.q); gp.k = static_cast<const uint16_t *>(a.k);
+  gp.v = static_cast<const uint16_t *>(a.v); gp.dO = static_cast<const uint16_t *>(a.dO);
+  gp.a = a.a; gp.b = a.b; gp.w = a.w;
+  gp.cst = cst; gp.dst = dst;
+  gp.dq = static_cast<uint16_t *>(a.dq); gp.dk = static_cast<uint16_t *>(a.dk);
+  gp.dv = static_cast<uint16_t *>(a.dv);
+  gp.da = a.da; gp.db = a.db; gp.dw = a.dw;
+  gp.T = a.T; gp.H_qk = a.H_qk; gp.H_v = a.H_v; gp.nch = l.nch;
+  if (a.H_v == a.H_qk)
+    hipLaunchKernelGGL((bwd_grad_kernel<D, false>), dim3(a.B * a.H_qk * l.nch), dim3(512), 0, st, gp);
+  else
+    hipLaunchKernelGGL((bwd_grad_kernel<D, true>), dim3(a.B * a.H_qk * l.nch), dim3(512), 0, st, gp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  *ran = true;
+  return hipSuccess;
+}
+
+}  // namespace gdn2

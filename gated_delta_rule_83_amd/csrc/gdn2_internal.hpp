@@ -55,6 +55,10 @@ struct PrefillArgs {
   // largest workspace the split may use (0: no limit); a split whose
   // output-correction form needs more runs its segments a second time instead
   size_t ws_cap;
+  // the state at every chunk boundary, in the input type (see
+  // PrefillParams::cst); needs an unsplit plan (force_nseg = 1) and no
+  // cu_seqlens
+  void *chunk_states = nullptr;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one
@@ -121,6 +125,13 @@ struct BackwardParams {
 };
 
 size_t backward_workspace_bytes(int B, size_t BT, int H_v, int d_k, int d_v);
+// The chunk-form backward (gdn2_backward_chunk.hip): whether it applies
+// (unpacked bf16 sequences, d_k = d_v = 128, general gates, the prefill's
+// 32-token chunk), its workspace, and the launch (*ran = false when some
+// chunk decays too fast for it: nothing but the workspace written).
+bool backward_chunked_eligible(const BackwardArgs &a);
+size_t backward_chunked_workspace_bytes(int B, int T, int H_qk, int H_v);
+hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *ran);
 hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
 // Workspace of the backward of B sequences of T tokens: the split plan's
 // when few long sequences run as segments, else backward_workspace_bytes.

@@ -303,6 +303,11 @@ struct PrefillParams {
   // the segment's transition, (Phi_t)^T q_t, where Phi_t maps the segment's
   // entering state to the state after t
   void *oI;
+  // state at every chunk boundary (the backward's checkpoints), in the
+  // output type, [B * H_v][ceil(T / C) + 1][d_v][d_k]: entry e of a
+  // (sequence, head) is the state entering chunk e (e = 0: S0; the last
+  // entry: the final state). Unsplit, unpacked launches only; null: none.
+  void *cst;
 };
 
 // Lower 16x16 tiles (r, c), c <= r, of the chunk's Gram matrices over the
@@ -507,7 +512,8 @@ __device__ __forceinline__ void map_block(int L, int B, int H_qk, int H_v, int n
 // gates given as pre-activations x in the input dtype, activated here
 // (decay a = exp(-softplus(x)) = 1 / (1 + e^x), erase and write gates
 // b, w = sigmoid(x)).
-template <int DK, int C, int NCT, bool BF16, bool CPL, bool SCA, bool PRE>
+// CST: store the state at every chunk boundary (PrefillParams::cst)
+template <int DK, int C, int NCT, bool BF16, bool CPL, bool SCA, bool PRE, bool CST = false>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   using Cf = PrefillCfg<DK, C, NCT, BF16>;
   using E = Elem<BF16>;
@@ -1010,6 +1016,26 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // load (including the next chunk's prefetch) at each first use of S.
   __builtin_amdgcn_s_waitcnt(0);
 
+  // Chunk-boundary states (see PrefillParams::cst): this lane's column,
+  // four consecutive key channels per tile.
+  ET *const cstp = (CST && consumer && !ident)
+                       ? (ET *)p.cst + (((size_t)n * p.H_v + h) * (size_t)((Tl + C - 1) / C + 1) * d_v + col) * DK +
+                             4 * lg
+                       : nullptr;
+  auto store_cst = [&](int e) {
+    if constexpr (!CST) return;
+    ET *dst = cstp + (size_t)e * d_v * DK;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      if constexpr (BF16) {
+        *reinterpret_cast<bf16x4 *>(dst + 16 * rt) = __builtin_convertvector(S[rt], bf16x4);
+      } else {
+        *reinterpret_cast<floatx4 *>(dst + 16 * rt) = S[rt];
+      }
+    }
+  };
+  if (CST && cstp) store_cst(0);
+
   // Token-by-token steps on this wave's columns (exact for any decay).
   auto token_steps = [&](int tb, int te) __attribute__((always_inline)) {
     for (int t = tb; t < te; ++t) {
@@ -1346,6 +1372,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         S[rt] = acc * gc[rt];
       }
     }
+    if (CST && cstp && live) store_cst(s);  // the state entering chunk s
     // The state enters a chunk with the middle anchor (built in this step's
     // first phase, consumed in the next step) as diag(gamma_m) S: scaled
     // here, after the carry, so that the other chunks need no scaling.
@@ -1371,7 +1398,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   if (consumer) {
     read_o();
     store_o();
-    if (nfull * C < Tl) token_steps(nfull * C, Tl);
+    if (nfull * C < Tl) {
+      token_steps(nfull * C, Tl);
+      if (CST && cstp) store_cst(nfull + 1);
+    }
     if (STp) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
@@ -1453,6 +1483,13 @@ PrefillPlan plan_t(const PrefillArgs &a) {
 template <int DK, int C, int NCT, bool BF16>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   auto kernel = [&](int blocks, const PrefillParams &kp) {
+    if constexpr (DK == 128 && BF16) {
+      if (kp.cst) {  // general gates only (the chunk-form backward)
+        hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false, false, true>), dim3(blocks), dim3(512), 0,
+                           st, kp);
+        return;
+      }
+    }
     if (a.scalar_decay)  // scalar decay comes with coupled gates (Gated DeltaNet)
       hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, true, false>), dim3(blocks), dim3(512), 0, st, kp);
     else if (a.coupled)
@@ -1485,8 +1522,13 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.sT_last_only = false;
   p.cu = a.cu_seqlens;
   p.oI = nullptr;
+  p.cst = nullptr;
   const int units = a.B * a.H_v;
+  if (a.chunk_states && (pl.nseg > 1 || a.cu_seqlens || DK != 128 || !BF16 || a.coupled || a.scalar_decay ||
+                         a.preact))
+    return hipErrorInvalidValue;
   if (pl.nseg <= 1) {
+    p.cst = a.chunk_states;
     kernel(units * ncb, p);
     return hipGetLastError();
   }

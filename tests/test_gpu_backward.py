@@ -181,11 +181,14 @@ def test_grouped_heads_full_size_sampled():
 
 
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 64, 64), ("bf16", 128, 128), ("f32", 16, 128)])
-def test_varlen_matches_oracle_and_separate_calls(dt, dk, dv):
+def test_varlen_matches_oracle_and_separate_calls(dt, dk, dv, monkeypatch):
     """Packed sequences of lengths 0, 1, 5, 17, 64, 3 (ragged against the
     4-token sub-segments and 16-token stages), grouped heads, per-sequence S0
     and dS_T: each sequence's gradients equal the oracle's and, bit for bit,
-    those of gdn2_chunk_backward on the sequence alone."""
+    those of gdn2_chunk_backward on the sequence alone with the per-token
+    backward (the one packed sequences run; the chunk form is checked against
+    the oracle in test_gpu_backward_chunk.py)."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
     rng = np.random.default_rng(3900 + dk + dv)
     lens = [0, 1, 5, 17, 64, 3]
     N, T = len(lens), sum(lens)

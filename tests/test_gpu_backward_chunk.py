@@ -1,0 +1,89 @@
+"""Parity of the chunk-form backward (bf16 inputs, d_k = d_v = 128,
+per-channel gates: the prefill's states at every chunk boundary, the state's
+adjoint swept over chunks, every gradient of a chunk on the matrix cores)
+with the fp64 oracle's gradients.
+
+GDN2_BACKWARD_CHUNKED=2 makes the library fail instead of falling back to
+the per-token backward, so these tests check the chunk form itself. The
+cases: whole and ragged chunks and sequences shorter than one chunk, grouped
+heads, absent S0 / dS_T, decays that need the middle anchor, and decays too
+fast for either anchor (the library then runs the per-token backward, and
+refuses when the chunk form is required). Tolerance: the bf16 bar, 2e-2
+normwise per gradient tensor."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_83_amd as g
+from gated_delta_rule_83_amd import inputs as gi
+from tests.parity import rand_inputs
+from tests.test_gpu_backward import compare, upstream
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("B,T,Hqk,Hv", [(2, 32, 1, 1), (2, 3 * 32 + 11, 1, 2), (1, 5, 2, 2), (1, 200, 2, 4)])
+def test_chunk_form_matches_oracle(B, T, Hqk, Hv, monkeypatch):
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    rng = np.random.default_rng(5000 + T + 7 * Hv)
+    d = rand_inputs(rng, B, T, Hqk, Hv, 128, 128)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    compare(td, dO, dST, "bf16", f"chunk form B{B} T{T} Hqk{Hqk} Hv{Hv}")
+
+
+def test_chunk_form_without_state(monkeypatch):
+    """S0 and dS_T absent (zero)."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    rng = np.random.default_rng(5100)
+    d = rand_inputs(rng, 2, 70, 1, 1, 128, 128, with_s0=False)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, _ = upstream(rng, d, "bf16", with_dst=False)
+    compare(td, dO, None, "bf16", "chunk form no S0/dS_T")
+
+
+def _decays(rng, shape, lo, hi):
+    return np.exp(-rng.uniform(lo, hi, shape)).astype(np.float32)
+
+
+def test_chunk_form_middle_anchor(monkeypatch):
+    """Some channels decay by about e^-80 over a chunk (e^-40 per half): the
+    chunks take the anchor at their middle token."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    rng = np.random.default_rng(5200)
+    d = rand_inputs(rng, 1, 2 * 32 + 9, 1, 2, 128, 128)
+    d["a"][..., :8] = _decays(rng, d["a"][..., :8].shape, 2.2, 2.8)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    compare(td, dO, dST, "bf16", "chunk form middle anchor")
+
+
+def test_fast_decay_falls_back_to_token_steps(monkeypatch):
+    """One channel decays by about e^-90 within each half chunk: neither
+    anchor keeps the operands below e^60, so the chunk form refuses when
+    required, and the automatic choice runs the per-token backward."""
+    rng = np.random.default_rng(5300)
+    d = rand_inputs(rng, 1, 64, 1, 1, 128, 128)
+    d["a"][..., 3] = _decays(rng, d["a"][..., 3].shape, 5.5, 6.0)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    with pytest.raises(RuntimeError):
+        g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("GDN2_BACKWARD_CHUNKED")
+    compare(td, dO, dST, "bf16", "fast decay, per-token fallback")
+
+
+def test_chunk_form_layer_distributions(monkeypatch):
+    """The 1.3B-class layer's gate distributions (decay pre-activation
+    N(-4, 1)) at B2 H4 T520, against the oracle and against the per-token
+    backward."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    c = gi.scaled(1, B=2, T=520, H_qk=4, H_v=4)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(5400)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    compare(td, dO, dST, "bf16", "chunk form c1-scaled")
