@@ -205,25 +205,60 @@ template <int D>
 __device__ __forceinline__ int quad_i(int e) { return 4 * (e % (D / 4)); }
 
 // (I + N)^-1 for N strictly lower triangular (fp32 [C][C], LDS), written
-// as bf16 into Li ([C][C] row-major); lanes 0..C-1 of one wave, lane j a
-// column: x_t = delta_tj - sum_{u<t} N[t][u] x_u (zero above the diagonal
-// without branches: every x_u with u < j is zero)
-__device__ __forceinline__ void unit_lower_inverse(const float (*N)[kC], BF *Li, int j) {
-  asm volatile("" : "+v"(j));  // keeps the delta_tj selects here (hoisted, they were spilled)
-  float x[kC];
+// as bf16 into Li ([C][C] row-major), by blocks of 16. The diagonal blocks'
+// inverses by substitution (lane j of lanes 0..31 one column, zero above
+// the diagonal without branches: every x_u with u below the column is
+// zero) go into N's diagonal blocks; then X = N10 L00^-1 (into N's upper
+// block) and the lower block -L11^-1 X, one entry per thread of the first
+// 256. Every thread of the workgroup calls it (three barriers).
+__device__ __forceinline__ void unit_lower_inverse(float (*N)[kC], BF *Li, int tid) {
+  constexpr int H = kC / 2;
+  if (tid < kC) {
+    int j = tid & (H - 1);
+    asm volatile("" : "+v"(j));  // keeps the delta_tj selects here (hoisted, they were spilled)
+    const int o = tid < H ? 0 : H;  // the block
+    float x[H];
 #pragma unroll
-  for (int t = 0; t < kC; ++t) {
-    float s0 = t == j ? 1.f : 0.f, s1 = 0.f;
+    for (int t = 0; t < H; ++t) {
+      float s0 = t == j ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < t; ++u) {
-      if (u & 1)
-        s1 -= N[t][u] * x[u];
-      else
-        s0 -= N[t][u] * x[u];
+      for (int u = 0; u < t; ++u) {
+        if (u & 1)
+          s1 -= N[o + t][o + u] * x[u];
+        else
+          s0 -= N[o + t][o + u] * x[u];
+      }
+      x[t] = s0 + s1;
     }
-    x[t] = s0 + s1;
-    Li[sx<kC>(t, j)] = (BF)x[t];
+#pragma unroll
+    for (int t = 0; t < H; ++t) {
+      N[o + t][o + j] = x[t];
+      Li[sx<kC>(o + t, o + j)] = (BF)x[t];
+      Li[sx<kC>(t, H + j)] = (BF)0.f;  // the upper block
+    }
   }
+  __syncthreads();
+  const int t = tid >> 4, j = tid & (H - 1);
+  if (tid < H * H) {  // X[t][j] = sum_u N10[t][u] L00^-1[u][j]
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < H; u += 2) {
+      s0 += N[H + t][u] * N[u][j];
+      s1 += N[H + t][u + 1] * N[u + 1][j];
+    }
+    N[t][H + j] = s0 + s1;
+  }
+  __syncthreads();
+  if (tid < H * H) {  // -sum_u L11^-1[t][u] X[u][j]
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < H; u += 2) {
+      s0 += N[H + t][H + u] * N[u][H + j];
+      s1 += N[H + t][H + u + 1] * N[u + 1][H + j];
+    }
+    Li[sx<kC>(H + t, j)] = (BF)(-(s0 + s1));
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ void st_bf4(BF *p, floatx4 v) { *reinterpret_cast<Fr *>(p) = __builtin_convertvector(v, Fr); }
@@ -353,8 +388,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p) {
     }
   }
   __syncthreads();
-  if (tid < kC) unit_lower_inverse(sm.Akb, sm.Lb, tid);
-  __syncthreads();
+  unit_lower_inverse(sm.Akb, sm.Lb, tid);
 
   BF *out = p.prep + ((size_t)unit * p.nch + chunk) * 3 * kC * D;
 #pragma unroll
@@ -507,6 +541,31 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
   }
 }
 
+// Optional per-phase cycle counters of bwd_grad_kernel for kernel
+// development, compiled only with -DGDN2_BWD_TIMING: 8 workgroups from
+// GDN2_BWD_TIMER_BLOCK0 on store s_memtime deltas per wave and phase into
+// gdn2_bwd_cycles[block][wave][phase] (read by gdn2_bwd_cycles_read).
+#ifdef GDN2_BWD_TIMING
+#ifndef GDN2_BWD_TIMER_BLOCK0
+#define GDN2_BWD_TIMER_BLOCK0 4096
+#endif
+__device__ unsigned long long gdn2_bwd_cycles[8][8][16];
+#define BWD_TIMER_INIT unsigned long long bt_acc[16] = {}, bt_prev = __builtin_amdgcn_s_memtime();
+#define BWD_MARK(i)                                                 \
+  do {                                                              \
+    const unsigned long long bt_now = __builtin_amdgcn_s_memtime(); \
+    bt_acc[i] += bt_now - bt_prev;                                  \
+    bt_prev = bt_now;                                               \
+  } while (0)
+#define BWD_TIMER_STORE                                                                                   \
+  if (blockIdx.x >= GDN2_BWD_TIMER_BLOCK0 && blockIdx.x < GDN2_BWD_TIMER_BLOCK0 + 8 && lane == 0)         \
+    for (int i = 0; i < 16; ++i) gdn2_bwd_cycles[blockIdx.x - GDN2_BWD_TIMER_BLOCK0][wave][i] = bt_acc[i];
+#else
+#define BWD_TIMER_INIT
+#define BWD_MARK(i) ((void)0)
+#define BWD_TIMER_STORE
+#endif
+
 // ---------------------------------------------------------------- 4. gradients of a chunk
 // One workgroup of eight waves per (sequence, query/key head, chunk); wave
 // w owns value columns 16w.. and key channels 16w.. of every product.
@@ -515,9 +574,9 @@ struct GradSmem {
   alignas(16) BF Ql[kC * D], Kl[kC * D], Km[kC * D], Bm[kC * D];
   alignas(16) BF U[kC * D], dO[kC * D], R[kC * D], dZ[kC * D];
   // S0a^T and dSs^T ([column][channel]); after the key-side products the
-  // log-decay gradients and the carry terms (S0a region), the decays and
-  // lambda again (dSs region). R and dZ hold lambda (fp32 [C][D]) while the
-  // operands are built.
+  // log-decay gradients and the carry terms (S0a region) and the decays
+  // (dSs region). R and dZ hold lambda (fp32 [C][D]) while the operands are
+  // built.
   alignas(16) BF S0a[D * D], dSs[D * D];
   alignas(16) BF Akk[kC * kC], Mqk[kC * kC], Mqb[kC * kC], Lb[kC * kC];
   alignas(16) BF dMqk[kC * kC], dMqb[kC * kC], dAkk[kC * kC], dAkb[kC * kC];
@@ -547,7 +606,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
   float *const dgF = reinterpret_cast<float *>(sm.S0a);           // [C][D]
   float *const crF = reinterpret_cast<float *>(sm.S0a) + kC * D;  // [C][D]
   float *const aE = reinterpret_cast<float *>(sm.dSs);            // [C][D]
-  float *const lamE = reinterpret_cast<float *>(sm.dSs) + kC * D;  // [C][D]
   const int chunk = blockIdx.x % p.nch, ug = blockIdx.x / p.nch;  // ug = n * H_qk + gq
   const int n = ug / p.H_qk, gq = ug - n * p.H_qk;
   const int G = GRP ? p.H_v / p.H_qk : 1;
@@ -559,15 +617,35 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
 
   // dq, dk summed over the group's value heads; tiles (tb, ib)
   floatx4 dq[2] = {zero4(), zero4()}, dk[2] = {zero4(), zero4()};
+  BWD_TIMER_INIT
 
   for (int hv = 0; hv < G; ++hv) {
     const int h = gq * G + hv;
     const size_t unit = (size_t)n * p.H_v + h;
-    // ---- every request of the chunk first: decays, q, k, b, v, w, dO
-    // (zero past the end), the entering state and the exiting adjoint
+    // ---- every request of the chunk first, the decays first of all (the
+    // first wait is for them only): decays, q, k, b, v, w, dO (rows past
+    // the end read the last row and are replaced), then the entering state
+    // and the exiting adjoint
     constexpr int NQ = kC * D / 4 / NT, NS = D * D / 4 / NT;
     floatx4 av[NQ], bv[NQ], wv[NQ];
     Fr qv[NQ], kv[NQ], vv[NQ], ov[NQ], s0v[NS], dsv[NS];
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+      const size_t off = (tok0 + min(t, Tc - 1)) * v_row + (size_t)h * D + i4;
+      av[it] = *reinterpret_cast<const floatx4 *>(p.a + off);
+    }
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+      const size_t row = tok0 + min(t, Tc - 1), off = row * v_row + (size_t)h * D + i4;
+      bv[it] = *reinterpret_cast<const floatx4 *>(p.b + off);
+      wv[it] = *reinterpret_cast<const floatx4 *>(p.w + off);
+      qv[it] = *reinterpret_cast<const Fr *>(p.q + row * qk_row + (size_t)gq * D + i4);
+      kv[it] = *reinterpret_cast<const Fr *>(p.k + row * qk_row + (size_t)gq * D + i4);
+      vv[it] = *reinterpret_cast<const Fr *>(p.v + off);
+      ov[it] = *reinterpret_cast<const Fr *>(p.dO + off);
+    }
     {
       const BF *s0 = p.cst + (unit * (p.nch + 1) + chunk) * D * D;
       const BF *ds = p.dst + (unit * p.nch + chunk) * D * D;
@@ -580,19 +658,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
     }
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
-      av[it] = floatx4{1.f, 1.f, 1.f, 1.f};
-      bv[it] = wv[it] = zero4();
-      qv[it] = kv[it] = vv[it] = ov[it] = OB::zero();
-      if (t < Tc) {
-        const size_t row = tok0 + t, off = row * v_row + (size_t)h * D + i4;
-        av[it] = *reinterpret_cast<const floatx4 *>(p.a + off);
-        bv[it] = *reinterpret_cast<const floatx4 *>(p.b + off);
-        wv[it] = *reinterpret_cast<const floatx4 *>(p.w + off);
-        qv[it] = *reinterpret_cast<const Fr *>(p.q + row * qk_row + (size_t)gq * D + i4);
-        kv[it] = *reinterpret_cast<const Fr *>(p.k + row * qk_row + (size_t)gq * D + i4);
-        vv[it] = *reinterpret_cast<const Fr *>(p.v + off);
-        ov[it] = *reinterpret_cast<const Fr *>(p.dO + off);
+      if (quad_t<D>(tid + NT * it) >= Tc) {
+        av[it] = floatx4{1.f, 1.f, 1.f, 1.f};
+        bv[it] = wv[it] = zero4();
+        qv[it] = kv[it] = vv[it] = ov[it] = OB::zero();
       }
     }
     // ---- lambda (the chunk's anchor: at its start or its middle; chunks
@@ -603,7 +672,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
       *reinterpret_cast<floatx4 *>(&lam0[quad_t<D>(e) * D + quad_i<D>(e)]) = av[it];
     }
     __syncthreads();
+    BWD_MARK(0);
     lambda_scan<D>(lam0, lam0, sm.A, sm.gC, sm.gCA, tid);
+    BWD_MARK(1);
+    // lambda at this lane's positions of the key-side tiles (for dq, dk, db)
+    float lq[2][4];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lq[tb][j] = lam0[(16 * tb + 4 * g + j) * D + 16 * ib + c];
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
       const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
@@ -637,6 +714,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
       if ((lane & 32) == 0) *reinterpret_cast<floatx4 *>(&sm.rs[tid / (D / 2)][i4]) = rsum;
     }
     __syncthreads();
+    BWD_MARK(2);
     // ---- Gram tiles (three lower 16x16 tiles of each; the upper one is zero)
     for (int tile = wave; tile < 12; tile += NT / 64) {
       const int mat = tile / 3, tt = tile % 3;
@@ -662,8 +740,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
       }
     }
     __syncthreads();
-    if (tid < kC) unit_lower_inverse(sm.Akb, sm.Lb, tid);
-    __syncthreads();
+    BWD_MARK(3);
+    unit_lower_inverse(sm.Akb, sm.Lb, tid);
+    BWD_MARK(4);
 
     // ---- value side (columns 16 nb ..)
     {
@@ -727,13 +806,32 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
       }
     }
     __syncthreads();
+    BWD_MARK(5);
 
-    // ---- key side (channels 16 ib ..)
+    // ---- key side (channels 16 ib ..). Requested first: the decays again
+    // (for lambda and da at the end), b and k at this lane's positions
+    floatx4 av2[NQ];
+    float bq[2][4], kq[2][4];
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
+      av2[it] = floatx4{1.f, 1.f, 1.f, 1.f};
+      if (t < Tc) av2[it] = *reinterpret_cast<const floatx4 *>(p.a + (tok0 + t) * v_row + (size_t)h * D + i4);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * tb + 4 * g + j, i = 16 * ib + c;
+        const size_t row = tok0 + min(t, Tc - 1);
+        bq[tb][j] = t < Tc ? p.b[row * v_row + (size_t)h * D + i] : 0.f;
+        kq[tb][j] = t < Tc ? bf16_to_f32(p.k[row * qk_row + (size_t)gq * D + i]) : 0.f;
+      }
     floatx4 dQl[2], dKl[2], dKm[2], dBm[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       floatx4 a0 = zero4(), a1 = zero4(), a2 = zero4(), a3 = zero4();
-#pragma unroll 1
+#pragma unroll 2
       for (int k0 = 0; k0 < D; k0 += 32) {
         const P2 s0 = op_cols<D>(sm.S0a, 16 * ib, k0, c, g), ds = op_cols<D>(sm.dSs, 16 * ib, k0, c, g);
         a0 = mma(a0, op_rows<D>(sm.dO, 16 * tb, k0, c, g), s0);
@@ -767,25 +865,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
       }
     }
     __syncthreads();
-    // Requested first: the decays again (for lambda and da at the end), b
-    // and k at this lane's positions
-    floatx4 av2[NQ];
-    float bq[2][4], kq[2][4];
-#pragma unroll
-    for (int it = 0; it < NQ; ++it) {
-      const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
-      av2[it] = floatx4{1.f, 1.f, 1.f, 1.f};
-      if (t < Tc) av2[it] = *reinterpret_cast<const floatx4 *>(p.a + (tok0 + t) * v_row + (size_t)h * D + i4);
-    }
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * tb + 4 * g + j, i = 16 * ib + c;
-        const size_t row = tok0 + min(t, Tc - 1);
-        bq[tb][j] = t < Tc ? p.b[row * v_row + (size_t)h * D + i] : 0.f;
-        kq[tb][j] = t < Tc ? bf16_to_f32(p.k[row * qk_row + (size_t)gq * D + i]) : 0.f;
-      }
+    BWD_MARK(6);
     // carry terms of the log-decay gradient (before the Gram parts are
     // added), the Gram parts, then the log-decay gradient per token with
     // the same bf16 operands as the products
@@ -816,14 +896,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
         }
       }
     }
-    // lambda again (the dSs region is free), keeping the decays
+    // the decays (for da; the dSs region is free)
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
       const int e = tid + NT * it;
       *reinterpret_cast<floatx4 *>(&aE[quad_t<D>(e) * D + quad_i<D>(e)]) = av2[it];
     }
     __syncthreads();
-    lambda_scan<D>(aE, lamE, sm.A, sm.gC, sm.gCA, tid);
+    BWD_MARK(7);
     // dq, dk (summed over the group), db
     {
       const int i = 16 * ib + c;
@@ -832,7 +912,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * tb + 4 * g + j;
-          const float lam = lamE[t * D + i], mu = __builtin_amdgcn_rcpf(lam);
+          const float lam = lq[tb][j], mu = __builtin_amdgcn_rcpf(lam);
           dq[tb][j] += lam * dQl[tb][j];
           dk[tb][j] += lam * dKl[tb][j] + mu * (dKm[tb][j] + bq[tb][j] * dBm[tb][j]);
           if (t < Tc) p.db[(tok0 + t) * v_row + (size_t)h * D + i] = mu * kq[tb][j] * dBm[tb][j];
@@ -847,15 +927,33 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
 #pragma unroll
       for (int r8 = 0; r8 < 8; ++r8) acc += sm.rs[r8][i];
       acc *= sm.gC[i];
+      // in blocks of 8 tokens: the reads of a block are issued together
 #pragma unroll 1
-      for (int t = 0; t < kC; ++t) acc += crF[t * D + i];
+      for (int t0 = 0; t0 < kC; t0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = crF[(t0 + k) * D + i];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += v[k];
+      }
 #pragma unroll 1
-      for (int t = kC - 1; t >= 0; --t) {
-        acc += dgF[t * D + i];
-        if (t < Tc) p.da[(tok0 + t) * v_row + (size_t)h * D + i] = acc * __builtin_amdgcn_rcpf(aE[t * D + i]);
+      for (int t0 = kC - 8; t0 >= 0; t0 -= 8) {
+        float dg8[8], a8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          dg8[k] = dgF[(t0 + k) * D + i];
+          a8[k] = aE[(t0 + k) * D + i];
+        }
+#pragma unroll
+        for (int k = 7; k >= 0; --k) {
+          acc += dg8[k];
+          const int t = t0 + k;
+          if (t < Tc) p.da[(tok0 + t) * v_row + (size_t)h * D + i] = acc * __builtin_amdgcn_rcpf(a8[k]);
+        }
       }
     }
     __syncthreads();
+    BWD_MARK(9);
   }
   // dq, dk
   {
@@ -872,6 +970,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
         }
       }
   }
+  BWD_MARK(10);
+  BWD_TIMER_STORE
 }
 
 }  // namespace
@@ -960,5 +1060,11 @@ hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *
   *ran = true;
   return hipSuccess;
 }
+
+#ifdef GDN2_BWD_TIMING
+extern "C" int gdn2_bwd_cycles_read(unsigned long long *host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn2_bwd_cycles), sizeof(gdn2_bwd_cycles));
+}
+#endif
 
 }  // namespace gdn2

@@ -251,12 +251,13 @@ def test_preact_backward_matches_oracle(dt, dk, dv):
 @pytest.mark.parametrize("form,dt,dk,dv,T", [("coupled", "f32", 64, 64, 37), ("coupled", "bf16", 128, 128, 37),
                                              ("coupled", "f32", 16, 128, 5), ("scalar", "f32", 128, 16, 21),
                                              ("scalar", "bf16", 128, 128, 50), ("scalar", "f32", 32, 32, 1)])
-def test_coupled_scalar_backward_matches_oracle(form, dt, dk, dv, T):
+def test_coupled_scalar_backward_matches_oracle(form, dt, dk, dv, T, monkeypatch):
     """Coupled gate beta (b = w = beta), and the scalar form (decay alpha as
     well): dbeta sums the erase and write gradients, dalpha the decay's, and
     every gradient matches the oracle's chain rule through the broadcasts.
-    dbeta and dalpha also match the general path's gradients on the broadcast
-    gates, summed. Through the autograd wrapper."""
+    dbeta and dalpha also match the general per-token backward's gradients
+    on the broadcast gates, summed (the same arithmetic, so at the fp32 bar).
+    Through the autograd wrapper."""
     rng = np.random.default_rng(4300 + dk + dv + T + (form == "scalar"))
     B, Hv, scalar = 2, 2, form == "scalar"
     d = rand_inputs(rng, B, T, 1, Hv, dk, dv)
@@ -281,6 +282,7 @@ def test_coupled_scalar_backward_matches_oracle(form, dt, dk, dv, T):
     A = leaves["a"].detach()
     A = A[..., None].expand(B, T, Hv, dk).contiguous() if scalar else A
     bt = leaves["b"].detach()
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
     gg = g.chunk_backward(td["q"], td["k"], td["v"], A, bt[..., None].expand(B, T, Hv, dk).contiguous(),
                           bt[..., None].expand(B, T, Hv, dv).contiguous(), td["S0"], dO, dST)
     dbeta = gg["db"].sum(-1) + gg["dw"].sum(-1)
@@ -406,6 +408,7 @@ def test_split_backward_several_sequences(form, dt, with_state, monkeypatch):
 
 def _split_case(rng, form, dt, dk, dv, B, T, Hv, with_state, monkeypatch):
     from tests.gate_forms import backward_alone, form_inputs, oracle_backward
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")  # the per-token backward and its split
     x = form_inputs(rng, form, T, Hv, dk, dv, dt, DEV, B=B)
     tdt = x["q"].dtype
     S0 = torch.from_numpy((rng.standard_normal((B, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
@@ -439,8 +442,11 @@ def _split_case(rng, form, dt, dk, dv, B, T, Hv, with_state, monkeypatch):
 def test_split_backward_long_context_full_size(monkeypatch):
     """B1 T65536 H16 d128 bf16 with 1% hard erases (the long-context workload's
     shape): the default plan's split backward (8 segments) against the
-    unsplit backward of the same inputs, every gradient within tolerance."""
+    unsplit backward of the same inputs, every gradient within tolerance (the
+    per-token backward; the chunk form at this shape is checked in
+    test_gpu_backward_chunk.py)."""
     monkeypatch.delenv("GDN2_BACKWARD_SPLIT", raising=False)
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
     c = gi.config(2)
     d = gi.make_inputs(c)
     rng = np.random.default_rng(4900)

@@ -78,8 +78,7 @@ def test_fast_decay_falls_back_to_token_steps(monkeypatch):
 
 def test_chunk_form_layer_distributions(monkeypatch):
     """The 1.3B-class layer's gate distributions (decay pre-activation
-    N(-4, 1)) at B2 H4 T520, against the oracle and against the per-token
-    backward."""
+    N(-4, 1)) at B2 H4 T520, against the oracle."""
     monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
     c = gi.scaled(1, B=2, T=520, H_qk=4, H_v=4)
     d = gi.make_inputs(c)
@@ -87,3 +86,48 @@ def test_chunk_form_layer_distributions(monkeypatch):
     td = gi.to_torch(d, "bf16", DEV)
     dO, dST = upstream(rng, d, "bf16")
     compare(td, dO, dST, "bf16", "chunk form c1-scaled")
+
+
+def _heads_vs_oracle(td, dO, dST, gg, pairs, label):
+    """Gradients of (sequence n, value head h) against the oracle run on that
+    pair alone (one query/key head per value head)."""
+    import oracle
+    from tests.parity import TOL, normwise, to_np
+    for (n, h) in pairs:
+        sl = lambda x: x[n:n + 1, :, h:h + 1].contiguous()
+        ref = oracle.backward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]),
+                              None if td["S0"] is None else td["S0"][n:n + 1, h:h + 1].contiguous(), sl(dO),
+                              dST[n:n + 1, h:h + 1].contiguous())
+        errs = {nm: normwise(to_np(gg[nm][n:n + 1, :, h:h + 1] if nm != "dS0" else gg[nm][n:n + 1, h:h + 1]),
+                             ref[nm]) for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0")}
+        print(f"[{label} n{n} h{h}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+        bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+        assert not bad, ((n, h), bad)
+
+
+def test_chunk_form_long_context_sampled_heads(monkeypatch):
+    """B1 T65536 H16 d128 bf16 with 1% hard erases (the long-context shape):
+    the chunk form, three heads against the oracle."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    c = gi.config(2)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(5500)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    _heads_vs_oracle(td, dO, dST, gg, ((0, 0), (0, 7), (0, 15)), "chunk form long context")
+
+
+def test_chunk_form_layer_shape_sampled_heads(monkeypatch):
+    """B8 T4096 H16 d128 bf16 (the layer shape): the chunk form, four
+    (sequence, head) pairs against the oracle."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    c = gi.config(1)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(5600)
+    td = gi.to_torch(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    _heads_vs_oracle(td, dO, dST, gg, ((0, 0), (3, 5), (5, 11), (7, 15)), "chunk form layer shape")
