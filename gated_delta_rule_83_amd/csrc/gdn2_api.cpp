@@ -536,6 +536,7 @@ gdn2_status backward_general(const gdn2_desc *d, const int32_t *cu, const void *
   p.dw = static_cast<float *>(dw);
   p.gate_form = form;
   p.workspace = workspace;
+  p.workspace_bytes = ws_need;  // the part checked against the other buffers
   p.cu_seqlens = varlen ? cu : nullptr;
   const hipError_t e = gdn2::launch_backward(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;

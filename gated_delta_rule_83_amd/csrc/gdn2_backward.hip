@@ -1097,8 +1097,11 @@ __global__ __launch_bounds__(256) void split_ds0_kernel(float *dS0, const float 
     *reinterpret_cast<floatx4 *>(dst + x) = *reinterpret_cast<const floatx4 *>(src + x);
 }
 
+// nseg segments of seg_len tokens, from the prefill plan asked for req
+// segments (asking again for nseg can give other segments: 16 chunks asked
+// for 2 give 3 of 8 chunks, asked for 3 give 3 of 6)
 struct BwdSplit {
-  int nseg, seg_len;
+  int nseg, seg_len, req;
 };
 
 // Split plan: with fewer than 128 workgroups (sequences x value heads x
@@ -1107,7 +1110,7 @@ struct BwdSplit {
 // split would use for the same count (whole chunks). GDN2_BACKWARD_SPLIT=<n>,
 // read at each call, asks for n segments (1: never split).
 BwdSplit backward_split_plan(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
-  const BwdSplit none{1, T};
+  const BwdSplit none{1, T, 1};
   if (B <= 0 || T <= 0 || (long)B * T > 0x7fffffffL) return none;
   const long wg = (long)B * H_v * (d_v / bwd_cb(d_v));
   long P = 1;
@@ -1125,7 +1128,7 @@ BwdSplit backward_split_plan(int B, int T, int H_qk, int H_v, int d_k, int d_v, 
   fa.force_nseg = (int)(P < 65536 ? P : 65536);
   const PrefillPlan pl = prefill_plan(fa);
   if (pl.nseg < 2 || pl.seg_len % kSweepL != 0) return none;
-  return BwdSplit{pl.nseg, pl.seg_len};
+  return BwdSplit{pl.nseg, pl.seg_len, fa.force_nseg};
 }
 
 struct SplitLayout {
@@ -1143,6 +1146,8 @@ SplitLayout split_layout(int B, int T, int H_v, int d_k, int d_v, const BwdSplit
   l.total = l.inner + 3 * l.states + l.segst + l.trans + l.cu;
   return l;
 }
+
+hipError_t launch_backward_per_token(const BackwardArgs &a, hipStream_t st);
 
 hipError_t launch_backward_split(const BackwardArgs &a, const BwdSplit &sp, hipStream_t st) {
   const SplitLayout l = split_layout(a.B, a.T, a.H_v, a.d_k, a.d_v, sp);
@@ -1175,9 +1180,10 @@ hipError_t launch_backward_split(const BackwardArgs &a, const BwdSplit &sp, hipS
   fa.preact = a.gate_form == kGatePre;
   fa.workspace = trans;
   fa.workspace_bytes = l.trans;
-  fa.force_nseg = sp.nseg;
+  fa.force_nseg = sp.req;
   fa.seg_states = segst;
-  if (prefill_plan(fa).nseg != sp.nseg) return hipErrorInvalidValue;
+  const PrefillPlan fpl = prefill_plan(fa);
+  if (fpl.nseg != sp.nseg || fpl.seg_len != sp.seg_len) return hipErrorInvalidValue;
   e = launch_prefill(fa, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(split_states_kernel, dim3(ns * a.H_v), dim3(256), 0, st, S_in, a.S0, segst, a.B, a.H_v,
@@ -1201,23 +1207,235 @@ hipError_t launch_backward_split(const BackwardArgs &a, const BwdSplit &sp, hipS
   c.dST = Lout;
   c.dS0 = a.dS0 ? dS0_seg : nullptr;
   c.workspace = inner;
-  e = launch_backward(c, st);
+  e = launch_backward_per_token(c, st);
   if (e != hipSuccess || !a.dS0) return e;
   hipLaunchKernelGGL(split_ds0_kernel, dim3(a.B * a.H_v), dim3(256), 0, st, a.dS0, dS0_seg, a.H_v, sp.nseg, dkdv);
   return hipGetLastError();
 }
 
+hipError_t launch_backward_per_token(const BackwardArgs &a, hipStream_t st) {
+  BackwardParams p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.a = a.a; p.b = a.b; p.w = a.w; p.S0 = a.S0;
+  p.dO = a.dO; p.dST = a.dST;
+  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.da = a.da; p.db = a.db; p.dw = a.dw; p.dS0 = a.dS0;
+  p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
+  p.cu = a.cu_seqlens;
+  p.gate_form = a.gate_form;
+  const size_t BT = a.cu_seqlens ? (size_t)a.T : (size_t)a.B * a.T;
+  const size_t ck = (BT / kSub + a.B) * (size_t)a.H_v * a.d_k * a.d_v * 4;
+  const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * BT * a.H_v * 4 * a.d_k * 4;
+  p.ck = reinterpret_cast<float *>(a.workspace);
+  p.part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck));
+  p.rk = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck) + align256(part));
+  p.wsum = reinterpret_cast<float *>(reinterpret_cast<char *>(p.rk) + align256(BT * a.H_v * a.d_v * 4));
+  return a.bf16 ? launch_backward_bf16(p, a.d_k, st) : launch_backward_f32(p, a.d_k, st);
+}
+
+// ---------------------------------------------------------------- bounded workspace
+// The per-token backward in rounds, for a workspace smaller than it needs at
+// once: sequences cut into segments of about kRoundSeg tokens (whole chunks
+// of the prefill's split), each segment's entering state and exiting
+// adjoint as in launch_backward_split, then the packed-sequence backward over
+// runs of one sequence's consecutive segments, as many per run as the rest of
+// the workspace holds (whole sequences per run when a sequence is one
+// segment). The runs go one after another on the stream.
+constexpr int kRoundSeg = 512;
+
+struct Rounds {
+  int nseg, seg_len, req;  // as BwdSplit
+  size_t trans, segst, states, cu, fixed;  // region bytes; fixed: their sum
+};
+
+Rounds rounds_plan(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
+  Rounds r{};
+  r.nseg = 1;
+  r.seg_len = T;
+  r.req = 1;
+  if (T > kRoundSeg) {
+    PrefillArgs fa{};
+    fa.B = B; fa.T = T; fa.H_qk = H_qk; fa.H_v = H_v; fa.d_k = d_k; fa.d_v = d_v;
+    fa.chunk = 64;
+    fa.bf16 = bf16;
+    fa.nct = prefill_pick_nct(B, H_v, d_v);
+    fa.force_nseg = (T + kRoundSeg - 1) / kRoundSeg;
+    const PrefillPlan pl = prefill_plan(fa);
+    if (pl.nseg >= 2 && pl.seg_len % kSweepL == 0) {
+      r.nseg = pl.nseg;
+      r.seg_len = pl.seg_len;
+      r.req = fa.force_nseg;
+    }
+  }
+  if (r.nseg >= 2) {
+    const size_t mat = (size_t)H_v * d_k * d_v * 4;
+    r.trans = align256((size_t)r.nseg * B * H_v * d_k * d_k * 4);
+    r.segst = align256((size_t)r.nseg * B * mat);
+    r.states = align256((size_t)B * r.nseg * mat);
+    r.cu = align256((size_t)(r.nseg + 1) * 4);
+  }
+  r.fixed = r.trans + r.segst + 3 * r.states + r.cu;
+  return r;
+}
+
+// workspace of one run: k segments of `tokens` tokens in all, or k whole sequences
+size_t run_bytes(const Rounds &, int k, size_t tokens, int H_v, int d_k, int d_v) {
+  return backward_workspace_bytes(k, tokens, H_v, d_k, d_v);
+}
+
+// Bytes per token of each token-major array: q, k (and dq, dk); v, dO (dv);
+// a (da), b (db), w (dw) in the gate form's layout.
+struct TokStrides {
+  size_t qk, v, a, b, w;
+};
+TokStrides tok_strides(const BackwardArgs &a) {
+  const size_t es = a.bf16 ? 2 : 4, gs = a.gate_form == kGatePre ? es : 4;
+  const bool cpl = a.gate_form == kGateCoupled || a.gate_form == kGateScalar, sca = a.gate_form == kGateScalar;
+  TokStrides t;
+  t.qk = (size_t)a.H_qk * a.d_k * es;
+  t.v = (size_t)a.H_v * a.d_v * es;
+  t.a = sca ? (size_t)a.H_v * 4 : (size_t)a.H_v * a.d_k * gs;
+  t.b = cpl ? (size_t)a.H_v * 4 : (size_t)a.H_v * a.d_k * gs;
+  t.w = cpl ? 0 : (size_t)a.H_v * a.d_v * gs;
+  return t;
+}
+
+// a's token arrays moved on by `tok` tokens
+BackwardArgs at_token(const BackwardArgs &a, size_t tok) {
+  const TokStrides t = tok_strides(a);
+  auto in = [&](const void *p, size_t s) -> const void * { return p ? (const char *)p + tok * s : nullptr; };
+  auto out = [&](void *p, size_t s) -> void * { return p ? (char *)p + tok * s : nullptr; };
+  BackwardArgs c = a;
+  c.q = in(a.q, t.qk); c.k = in(a.k, t.qk); c.v = in(a.v, t.v); c.dO = in(a.dO, t.v);
+  c.a = (const float *)in(a.a, t.a); c.b = (const float *)in(a.b, t.b); c.w = (const float *)in(a.w, t.w);
+  c.dq = out(a.dq, t.qk); c.dk = out(a.dk, t.qk); c.dv = out(a.dv, t.v);
+  c.da = (float *)out(a.da, t.a); c.db = (float *)out(a.db, t.b); c.dw = (float *)out(a.dw, t.w);
+  return c;
+}
+
+// Token offsets of a run of k segments of L tokens, the last ending at T_rem.
+__global__ __launch_bounds__(256) void run_cu_kernel(int32_t *cu, int k, int L, int T_rem) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i <= k) cu[i] = min(i * L, T_rem);
+}
+
+hipError_t launch_backward_rounds(const BackwardArgs &a, hipStream_t st) {
+  const Rounds r = rounds_plan(a.B, a.T, a.H_qk, a.H_v, a.d_k, a.d_v, a.bf16);
+  if (a.workspace_bytes < r.fixed) return hipErrorInvalidValue;
+  char *w = static_cast<char *>(a.workspace);
+  char *inner = w + r.fixed;
+  const size_t inner_bytes = a.workspace_bytes - r.fixed;
+  const size_t mat = (size_t)a.H_v * a.d_k * a.d_v;  // floats of one state per sequence
+  hipError_t e = hipSuccess;
+  if (r.nseg < 2) {  // runs of whole sequences
+    for (int n = 0; n < a.B;) {
+      int m = 1;
+      while (n + m < a.B && run_bytes(r, m + 1, (size_t)(m + 1) * a.T, a.H_v, a.d_k, a.d_v) <= inner_bytes) ++m;
+      if (run_bytes(r, m, (size_t)m * a.T, a.H_v, a.d_k, a.d_v) > inner_bytes) return hipErrorInvalidValue;
+      BackwardArgs c = at_token(a, (size_t)n * a.T);
+      c.B = m;
+      c.S0 = a.S0 ? a.S0 + (size_t)n * mat : nullptr;
+      c.dST = a.dST ? a.dST + (size_t)n * mat : nullptr;
+      c.dS0 = a.dS0 ? a.dS0 + (size_t)n * mat : nullptr;
+      c.workspace = inner;
+      c.workspace_bytes = inner_bytes;
+      if ((e = launch_backward_per_token(c, st)) != hipSuccess) return e;
+      n += m;
+    }
+    return hipSuccess;
+  }
+  float *trans = reinterpret_cast<float *>(w);
+  float *segst = reinterpret_cast<float *>(w + r.trans);
+  float *S_in = reinterpret_cast<float *>(w + r.trans + r.segst);
+  float *Lout = reinterpret_cast<float *>(w + r.trans + r.segst + r.states);
+  float *dS0_seg = reinterpret_cast<float *>(w + r.trans + r.segst + 2 * r.states);
+  int32_t *cu = reinterpret_cast<int32_t *>(w + r.trans + r.segst + 3 * r.states);
+  const bool coupled = a.gate_form == kGateCoupled || a.gate_form == kGateScalar;
+  // entering states: the prefill's split passes (states only)
+  PrefillArgs fa{};
+  fa.B = a.B; fa.T = a.T; fa.H_qk = a.H_qk; fa.H_v = a.H_v; fa.d_k = a.d_k; fa.d_v = a.d_v;
+  fa.chunk = 64;
+  fa.bf16 = a.bf16;
+  fa.nct = prefill_pick_nct(a.B, a.H_v, a.d_v);
+  fa.q = a.q; fa.k = a.k; fa.v = a.v;
+  fa.a = a.a; fa.b = a.b; fa.w = coupled ? a.b : a.w;
+  fa.S0 = a.S0;
+  fa.coupled = coupled;
+  fa.scalar_decay = a.gate_form == kGateScalar;
+  fa.preact = a.gate_form == kGatePre;
+  fa.workspace = trans;
+  fa.workspace_bytes = r.trans;
+  fa.force_nseg = r.req;
+  fa.seg_states = segst;
+  const PrefillPlan fpl = prefill_plan(fa);
+  if (fpl.nseg != r.nseg || fpl.seg_len != r.seg_len) return hipErrorInvalidValue;
+  if ((e = launch_prefill(fa, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(split_states_kernel, dim3(a.B * r.nseg * a.H_v), dim3(256), 0, st, S_in, a.S0, segst, a.B,
+                     a.H_v, r.nseg, a.d_k * a.d_v);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // exiting adjoints: the adjoint-only sweep
+  SweepParams sw{};
+  sw.q = a.q; sw.k = a.k; sw.a = a.a; sw.b = a.b; sw.dO = a.dO; sw.dST = a.dST;
+  sw.Lout = Lout;
+  sw.B = a.B; sw.T = a.T; sw.H_qk = a.H_qk; sw.H_v = a.H_v; sw.d_v = a.d_v;
+  sw.nseg = r.nseg; sw.seg_len = r.seg_len;
+  e = a.bf16 ? launch_sweep_bf16(sw, a.d_k, a.gate_form, st) : launch_sweep_f32(sw, a.d_k, a.gate_form, st);
+  if (e != hipSuccess) return e;
+  // runs of consecutive segments of one sequence
+  const int L = r.seg_len;
+  auto seg_tokens = [&](int j0, int j1) { return (size_t)(min(j1 * L, a.T) - j0 * L); };
+  for (int n = 0; n < a.B; ++n) {
+    for (int j = 0; j < r.nseg;) {
+      int j1 = j + 1;
+      while (j1 < r.nseg && run_bytes(r, j1 + 1 - j, seg_tokens(j, j1 + 1), a.H_v, a.d_k, a.d_v) <= inner_bytes) ++j1;
+      if (run_bytes(r, j1 - j, seg_tokens(j, j1), a.H_v, a.d_k, a.d_v) > inner_bytes) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(run_cu_kernel, dim3((j1 - j + 256) / 256), dim3(256), 0, st, cu, j1 - j, L, a.T - j * L);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      BackwardArgs c = at_token(a, (size_t)n * a.T + (size_t)j * L);
+      c.B = j1 - j;
+      c.T = (int)seg_tokens(j, j1);
+      c.cu_seqlens = cu;
+      const size_t s0 = (size_t)n * r.nseg + j;
+      c.S0 = S_in + s0 * mat;
+      c.dST = Lout + s0 * mat;
+      c.dS0 = a.dS0 ? dS0_seg + s0 * mat : nullptr;
+      c.workspace = inner;
+      c.workspace_bytes = inner_bytes;
+      if ((e = launch_backward_per_token(c, st)) != hipSuccess) return e;
+      j = j1;
+    }
+  }
+  if (!a.dS0) return hipSuccess;
+  hipLaunchKernelGGL(split_ds0_kernel, dim3(a.B * a.H_v), dim3(256), 0, st, a.dS0, dS0_seg, a.H_v, r.nseg,
+                     a.d_k * a.d_v);
+  return hipGetLastError();
+}
+
+size_t backward_rounds_min_bytes(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
+  const Rounds r = rounds_plan(B, T, H_qk, H_v, d_k, d_v, bf16);
+  return r.fixed + (r.nseg >= 2 ? run_bytes(r, 1, (size_t)min(r.seg_len, T), H_v, d_k, d_v)
+                                : run_bytes(r, 1, (size_t)T, H_v, d_k, d_v));
+}
+
 }  // namespace
 
-size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
+// The per-token backward all at once: unsplit, or the split plan's.
+size_t per_token_workspace_bytes(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
   const BwdSplit sp = backward_split_plan(B, T, H_qk, H_v, d_k, d_v, bf16);
-  const size_t per_token = sp.nseg < 2 ? backward_workspace_bytes(B, (size_t)B * T, H_v, d_k, d_v)
-                                       : split_layout(B, T, H_v, d_k, d_v, sp).total;
-  // room for the chunk form as well where the shape allows it (any gate form:
-  // the size does not depend on it)
-  const bool chunk_shape = bf16 && d_k == 128 && d_v == 128 && B > 0 && T > 0;
-  const size_t chunked = chunk_shape ? backward_chunked_workspace_bytes(B, T, H_qk, H_v) : 0;
-  return per_token > chunked ? per_token : chunked;
+  return sp.nseg < 2 ? backward_workspace_bytes(B, (size_t)B * T, H_v, d_k, d_v)
+                     : split_layout(B, T, H_v, d_k, d_v, sp).total;
+}
+
+size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
+  // Where the chunk form applies to the shape (bf16, d_k = d_v = 128): its
+  // workspace, and at least the per-token backward's smallest in rounds
+  // (what other gate forms, and chunks that decay too fast for the chunk
+  // form, run in). Elsewhere the per-token backward's.
+  // (GDN2_BACKWARD_CHUNKED=0, read at each call: the per-token backward's)
+  const char *cenv = getenv("GDN2_BACKWARD_CHUNKED");
+  const bool chunk_shape = bf16 && d_k == 128 && d_v == 128 && B > 0 && T > 0 && !(cenv && atoi(cenv) == 0);
+  if (!chunk_shape) return per_token_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, bf16);
+  const size_t chunked = backward_chunked_workspace_bytes(B, T, H_qk, H_v);
+  const size_t rounds = backward_rounds_min_bytes(B, T, H_qk, H_v, d_k, d_v, bf16);
+  return chunked > rounds ? chunked : rounds;
 }
 
 // Checkpoints: per (head, column block) BT / kSub + B slots of d_k x CB fp32
@@ -1248,26 +1466,16 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     if (e != hipSuccess || ran) return e;
   }
   if (cmode == 2) return hipErrorNotSupported;
+  if (!a.cu_seqlens &&
+      a.workspace_bytes < per_token_workspace_bytes(a.B, a.T, a.H_qk, a.H_v, a.d_k, a.d_v, a.bf16))
+    return launch_backward_rounds(a, st);
   if (!a.cu_seqlens) {
     const BwdSplit sp = backward_split_plan(a.B, a.T, a.H_qk, a.H_v, a.d_k, a.d_v, a.bf16);
     if (sp.nseg > 1) return launch_backward_split(a, sp, st);
   }
-  BackwardParams p{};
-  p.q = a.q; p.k = a.k; p.v = a.v; p.a = a.a; p.b = a.b; p.w = a.w; p.S0 = a.S0;
-  p.dO = a.dO; p.dST = a.dST;
-  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.da = a.da; p.db = a.db; p.dw = a.dw; p.dS0 = a.dS0;
-  p.B = a.B; p.T = a.T; p.H_qk = a.H_qk; p.H_v = a.H_v; p.d_v = a.d_v;
-  p.cu = a.cu_seqlens;
-  p.gate_form = a.gate_form;
-  const size_t BT = a.cu_seqlens ? (size_t)a.T : (size_t)a.B * a.T;
-  const size_t ck = (BT / kSub + a.B) * (size_t)a.H_v * a.d_k * a.d_v * 4;
-  const size_t part = ((size_t)a.d_v / bwd_cb(a.d_v)) * BT * a.H_v * 4 * a.d_k * 4;
-  p.ck = reinterpret_cast<float *>(a.workspace);
-  p.part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck));
-  p.rk = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) + align256(ck) + align256(part));
-  p.wsum = reinterpret_cast<float *>(reinterpret_cast<char *>(p.rk) + align256(BT * a.H_v * a.d_v * 4));
-  return a.bf16 ? launch_backward_bf16(p, a.d_k, st) : launch_backward_f32(p, a.d_k, st);
+  return launch_backward_per_token(a, st);
 }
+
 #endif
 
 }  // namespace gdn2

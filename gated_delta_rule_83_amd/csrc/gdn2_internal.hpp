@@ -97,7 +97,8 @@ struct BackwardArgs {
   const float *dST;
   void *dq, *dk, *dv;
   float *da, *db, *dw, *dS0;
-  void *workspace;  // backward_workspace_bytes() bytes, 256-byte aligned
+  void *workspace;  // 256-byte aligned
+  size_t workspace_bytes;  // its size (what the launch may use)
   // packed sequences: B + 1 token offsets (device), or null for B sequences
   // of T tokens each
   const int32_t *cu_seqlens;

@@ -274,9 +274,11 @@ def test_backward_workspace_query_and_argument_errors():
 
 
 def test_backward_split_workspace(monkeypatch):
-    """Few long sequences: the backward runs as segments and its workspace
-    query accounts for the split's buffers (more than the unsplit layout);
-    a workspace of the unsplit size is then rejected before any launch."""
+    """The per-token backward (GDN2_BACKWARD_CHUNKED=0). Few long sequences:
+    it runs as segments and its workspace query accounts for the split's
+    buffers (more than the unsplit layout); a workspace of the unsplit size
+    is then rejected before any launch."""
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
     d = g.make_desc(1, 8192, 2, 4, 128, 128, 64, g.GDN2_BF16)
     monkeypatch.setenv("GDN2_BACKWARD_SPLIT", "1")
     plain = g.gdn2_chunk_backward_workspace_bytes(d)
@@ -299,6 +301,30 @@ def test_backward_split_workspace(monkeypatch):
     c1_plain = g.gdn2_chunk_backward_workspace_bytes(c1)
     monkeypatch.delenv("GDN2_BACKWARD_SPLIT")
     assert g.gdn2_chunk_backward_workspace_bytes(c1) == c1_plain
+
+
+def test_backward_chunk_form_workspace(monkeypatch):
+    """bf16, d_k = d_v = 128: the query returns the chunk form's workspace
+    (with room for the per-token backward in rounds), about 1.5 GB at the
+    layer shape B8 T4096 H16 against 11 GB for the per-token backward at
+    once; a smaller workspace is rejected before any launch. Other shapes
+    keep the per-token backward's size."""
+    monkeypatch.delenv("GDN2_BACKWARD_CHUNKED", raising=False)
+    c1 = g.make_desc(8, 4096, 16, 16, 128, 128, 64, g.GDN2_BF16)
+    chunk = g.gdn2_chunk_backward_workspace_bytes(c1)
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
+    per_token = g.gdn2_chunk_backward_workspace_bytes(c1)
+    monkeypatch.delenv("GDN2_BACKWARD_CHUNKED")
+    assert chunk < 2 * 10**9 < per_token
+    assert 1.3e9 < chunk < 1.6e9
+    ws = FAKE + 40 * (1 << 30)
+    assert bwd(c1, ws=ws, ws_bytes=chunk - 256) == g.GDN2_ERR_WORKSPACE
+    for desc in (g.make_desc(2, 300, 1, 2, 64, 64, 64, g.GDN2_BF16), g.make_desc(2, 300, 1, 2, 128, 128, 64,
+                                                                                g.GDN2_F32)):
+        a = g.gdn2_chunk_backward_workspace_bytes(desc)
+        monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
+        assert g.gdn2_chunk_backward_workspace_bytes(desc) == a
+        monkeypatch.delenv("GDN2_BACKWARD_CHUNKED")
 
 
 def test_backward_varlen_workspace_and_errors():

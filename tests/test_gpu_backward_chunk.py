@@ -131,3 +131,43 @@ def test_chunk_form_layer_shape_sampled_heads(monkeypatch):
     gg = g.chunk_backward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
     torch.cuda.synchronize()
     _heads_vs_oracle(td, dO, dST, gg, ((0, 0), (3, 5), (5, 11), (7, 15)), "chunk form layer shape")
+
+
+@pytest.mark.parametrize("form,T", [("channel", 1100), ("preact", 1100), ("coupled", 1100), ("scalar", 1100),
+                                    ("scalar", 520), ("channel", 520)])
+def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
+    """Where the chunk form's shape applies (bf16, d_k = d_v = 128) the
+    workspace query returns the chunk form's size, smaller than the per-token
+    backward needs at once; the per-token backward (the other gate forms,
+    and per-channel gates with a channel that decays too fast for the chunk
+    form) then runs in rounds of segments within it. B2, T1100 (3 segments
+    of 384 tokens, the last ragged) and T520 (3 of 256, the last shorter than
+    a chunk: asked for 2 segments, which the prefill's plan turns into 3),
+    two value heads per query/key head, S0 and dS_T: against the oracle of
+    the form."""
+    from tests.gate_forms import backward_alone, form_inputs, oracle_backward
+    from tests.parity import TOL, normwise, to_np
+    monkeypatch.delenv("GDN2_BACKWARD_CHUNKED", raising=False)
+    rng = np.random.default_rng(5700 + len(form) + T)
+    B, Hv = 2, 2
+    x = form_inputs(rng, form, T, Hv, 128, 128, "bf16", DEV, B=B)
+    if form == "channel":  # key channel 5 decays by about e^-90 within each half chunk
+        a = x["a"].clone()
+        a[..., 5] = torch.exp(-torch.empty_like(a[..., 5]).uniform_(5.5, 6.0))
+        x["a"] = a
+    desc = g.make_desc(B, T, 1, Hv, 128, 128, 64, g.GDN2_BF16)
+    ws = g.gdn2_chunk_backward_workspace_bytes(desc)
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
+    assert g.gdn2_chunk_backward_workspace_bytes(desc) > ws  # the per-token backward at once needs more
+    monkeypatch.delenv("GDN2_BACKWARD_CHUNKED")
+    S0 = torch.from_numpy((rng.standard_normal((B, Hv, 128, 128)) * 0.5).astype(np.float32)).to(DEV)
+    dO = torch.from_numpy(rng.standard_normal((B, T, Hv, 128)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((B, Hv, 128, 128)).astype(np.float32)).to(DEV)
+    got = backward_alone(form, x, S0, dO, dST)
+    torch.cuda.synchronize()
+    ref = oracle_backward(form, x, S0, dO, dST)
+    names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
+    errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
+    print(f"[per-token rounds {form}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, bad
