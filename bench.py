@@ -25,7 +25,10 @@ Legs, in the order they run (each its own figure in the JSON line):
   decode    the decode workload as stated (1024 successive steps from a
             random state), plus states of 1 GiB and 4 GiB (beyond the
             256 MiB Infinity Cache) for the bandwidth attribution;
-  preact, backward   the fused gate activation and the backward pass;
+  preact    the fused gate activation;
+  backward  the backward pass of the layer shape in chunk form (HBM roofline
+            on the inputs, dO and the gradients), with the per-token
+            backward beside it;
   cpu_baseline   the fp64 oracle on the host cores over the layer batch, and
             on one (sequence, head) with one thread.
 
@@ -461,19 +464,40 @@ def main():
             return g.chunk_backward(tp["q"], tp["k"], tp["v"], tp["a"], tp["b"], tp["w"], None, dO, dST,
                                     grads=grads, workspace=bws, stream=stream)
 
-        grads = backward()
+        # the chunk form (required; the automatic choice if it refuses the inputs)
+        form = "chunk"
+        os.environ["GDN2_BACKWARD_CHUNKED"] = "2"
+        try:
+            grads = backward()
+        except RuntimeError:
+            form = "automatic"
+            os.environ.pop("GDN2_BACKWARD_CHUNKED")
+            grads = backward()
         backward(grads)
         torch.cuda.synchronize()
         b_ms = time_each(lambda: backward(grads), args.backward_steps)
+        os.environ.pop("GDN2_BACKWARD_CHUNKED", None)
         b_avg = float(np.mean(b_ms)) / 1e3
         bfl, bby = backward_algorithmic(cp)
-        bwd = {"launches": args.backward_steps, "ms": b_avg * 1e3, "min_ms": min(b_ms),
-               "tokens_per_s": tokens / b_avg, "bound": "alu",
-               "achieved": bfl / b_avg / 1e12, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
-               "frac": bfl / b_avg / 1e12 / FP32_VECTOR_PEAK_TFS, "algorithmic_flops": bfl,
-               "algorithmic_bytes": bby, "workspace_bytes": bws.numel()}
-        log(f"[bench] backward: {b_avg * 1e3:.2f} ms per launch (min {min(b_ms):.2f}), "
-            f"{bfl / b_avg / 1e12:.1f} TFLOP/s algorithmic")
+        bwd = {"form": form, "launches": args.backward_steps, "ms": b_avg * 1e3, "min_ms": min(b_ms),
+               "tokens_per_s": tokens / b_avg, "bound": "hbm",
+               "achieved": bby / b_avg / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": bby / b_avg / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": bby,
+               "recurrence_flops": bfl, "workspace_bytes": bws.numel()}
+        log(f"[bench] backward ({form}): {b_avg * 1e3:.2f} ms per launch (min {min(b_ms):.2f}), "
+            f"workspace {bws.numel() / 1e9:.2f} GB")
+        del grads, bws
+        # the per-token backward beside it (its own, larger workspace)
+        os.environ["GDN2_BACKWARD_CHUNKED"] = "0"
+        bws = torch.empty(g.gdn2_chunk_backward_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        grads = backward()
+        torch.cuda.synchronize()
+        t_ms = time_each(lambda: backward(grads), max(2, args.backward_steps // 2))
+        os.environ.pop("GDN2_BACKWARD_CHUNKED")
+        bwd["per_token"] = {"ms": float(np.mean(t_ms)), "min_ms": min(t_ms), "workspace_bytes": bws.numel(),
+                            "achieved": bfl / (float(np.mean(t_ms)) / 1e3) / 1e12, "unit": "TFLOP/s",
+                            "peak": FP32_VECTOR_PEAK_TFS}
+        log(f"[bench] backward (per-token): {np.mean(t_ms):.2f} ms per launch, workspace {bws.numel() / 1e9:.2f} GB")
         del grads, bws
 
     # ---------------------------------------------------------------- long-context backward (optional)
@@ -496,7 +520,7 @@ def main():
         l_ms = time_each(lambda: backward_long(gl), args.long_backward)
         l_avg = float(np.mean(l_ms)) / 1e3
         lfl, _ = backward_algorithmic(cl)
-        bwd_long = {"workload": "backward B1 T65536 H16 d128 bf16 (split into segments)",
+        bwd_long = {"workload": "backward B1 T65536 H16 d128 bf16",
                     "launches": args.long_backward, "ms": l_avg * 1e3, "min_ms": min(l_ms),
                     "tokens_per_s": cl.B * cl.T / l_avg, "achieved": lfl / l_avg / 1e12,
                     "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s", "workspace_bytes": wsl.numel()}

@@ -263,6 +263,59 @@ __device__ __forceinline__ void unit_lower_inverse(float (*N)[kC], BF *Li, int t
 
 __device__ __forceinline__ void st_bf4(BF *p, floatx4 v) { *reinterpret_cast<Fr *>(p) = __builtin_convertvector(v, Fr); }
 
+// The gates in each stored form (GF, kGate*): per-channel fp32 values;
+// pre-activations in bf16, activated here (decay 1 / (1 + e^x), erase and
+// write gates sigmoid(x)); coupled: b = w = beta, one fp32 value per token
+// and value head; scalar: also a = alpha per token and value head. th is
+// the (token, value head) index, i4 / i a channel (or value column).
+template <int GF, int D>
+__device__ __forceinline__ floatx4 gate_a4(const void *a, size_t th, int i4) {
+  if constexpr (GF == kGateScalar) {
+    const float x = static_cast<const float *>(a)[th];
+    return floatx4{x, x, x, x};
+  } else if constexpr (GF == kGatePre) {
+    const floatx4 x = fr_f32(*reinterpret_cast<const Fr *>(static_cast<const BF *>(a) + th * D + i4));
+    return floatx4{decay_from_pre(x[0]), decay_from_pre(x[1]), decay_from_pre(x[2]), decay_from_pre(x[3])};
+  } else {
+    return *reinterpret_cast<const floatx4 *>(static_cast<const float *>(a) + th * D + i4);
+  }
+}
+// erase gate (b) or write gate (w, from `w`; the coupled forms read beta from `b`)
+template <int GF, int D>
+__device__ __forceinline__ floatx4 gate_bw4(const void *bw, const void *b, size_t th, int i4) {
+  if constexpr (GF == kGateCoupled || GF == kGateScalar) {
+    const float x = static_cast<const float *>(b)[th];
+    return floatx4{x, x, x, x};
+  } else if constexpr (GF == kGatePre) {
+    const floatx4 x = fr_f32(*reinterpret_cast<const Fr *>(static_cast<const BF *>(bw) + th * D + i4));
+    return floatx4{gate_from_pre(x[0]), gate_from_pre(x[1]), gate_from_pre(x[2]), gate_from_pre(x[3])};
+  } else {
+    return *reinterpret_cast<const floatx4 *>(static_cast<const float *>(bw) + th * D + i4);
+  }
+}
+template <int GF, int D>
+__device__ __forceinline__ float gate_bw1(const void *bw, const void *b, size_t th, int i) {
+  if constexpr (GF == kGateCoupled || GF == kGateScalar) {
+    return static_cast<const float *>(b)[th];
+  } else if constexpr (GF == kGatePre) {
+    return gate_from_pre(bf16_to_f32(static_cast<const uint16_t *>(bw)[th * D + i]));
+  } else {
+    return static_cast<const float *>(bw)[th * D + i];
+  }
+}
+// a gate gradient dx of a per-channel gate x (activated value) in the stored
+// form: fp32 as is, or for pre-activations dx dx/dpre in bf16 (dpre = dx *
+// (-x (1 - x)) for the decay, dx * x (1 - x) for the erase and write gates)
+template <int GF>
+__device__ __forceinline__ void put_gate_grad(void *out, size_t idx, float dx, float x, bool decay) {
+  if constexpr (GF == kGatePre) {
+    const float s = x * (1.f - x);
+    static_cast<uint16_t *>(out)[idx] = f32_to_bf16(dx * (decay ? -s : s));
+  } else {
+    static_cast<float *>(out)[idx] = dx;
+  }
+}
+
 // ---------------------------------------------------------------- layouts
 struct ChunkLayout {
   int B, T, H_qk, H_v, nch;
@@ -300,14 +353,14 @@ struct PrepSmem {
 
 struct PrepParams {
   const uint16_t *q, *k;
-  const float *a, *b;
+  const void *a, *b;  // in the gate form's layout
   BF *prep;
   float *gc;
   int *flag;
   int T, H_qk, H_v, nch;
 };
 
-template <int D>
+template <int D, int GF>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p) {
   static_assert(D == 128, "d_k = 128");
   constexpr int NT = 256;
@@ -330,8 +383,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p) {
     qv[it] = kv[it] = OB::zero();
     if (t < Tc) {
       const size_t row = tok0 + t;
-      av[it] = *reinterpret_cast<const floatx4 *>(p.a + (row * p.H_v + h) * D + i4);
-      bv[it] = *reinterpret_cast<const floatx4 *>(p.b + (row * p.H_v + h) * D + i4);
+      av[it] = gate_a4<GF, D>(p.a, row * p.H_v + h, i4);
+      bv[it] = gate_bw4<GF, D>(p.b, p.b, row * p.H_v + h, i4);
       qv[it] = *reinterpret_cast<const Fr *>(p.q + (row * p.H_qk + gq) * D + i4);
       kv[it] = *reinterpret_cast<const Fr *>(p.k + (row * p.H_qk + gq) * D + i4);
     }
@@ -582,22 +635,25 @@ struct GradSmem {
   alignas(16) BF dMqk[kC * kC], dMqb[kC * kC], dAkk[kC * kC], dAkb[kC * kC];
   alignas(16) float Akb[kC][kC];
   alignas(16) float A[D], gCA[D], gC[D], rs[8][D];
+  float beta8[8][kC];  // coupled forms: d(beta) per wave and token
 };
 
 struct GradParams {
   const uint16_t *q, *k, *v, *dO;
-  const float *a, *b, *w;
+  const void *a, *b, *w;  // in the gate form's layout
   const BF *cst, *dst;
   uint16_t *dq, *dk, *dv;
-  float *da, *db, *dw;
+  void *da, *db, *dw;  // likewise (coupled forms: db is d(beta); scalar: da is d(alpha))
   int T, H_qk, H_v, nch;
 };
 
 // GRP: several value heads per query/key head (G = H_v / H_qk > 1, looped
 // over); the G = 1 instance has no loop, so nothing is kept across heads.
-template <int D, bool GRP>
+// GF: the gate form (kGate*).
+template <int D, bool GRP, int GF>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
   static_assert(D == 128, "d = 128");
+  constexpr bool CPL = GF == kGateCoupled || GF == kGateScalar, SCA = GF == kGateScalar;
   constexpr int NT = 512;
   static_assert(NT / 64 == D / 16, "one wave per 16 columns");
   __shared__ GradSmem<D> sm;
@@ -606,6 +662,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
   float *const dgF = reinterpret_cast<float *>(sm.S0a);           // [C][D]
   float *const crF = reinterpret_cast<float *>(sm.S0a) + kC * D;  // [C][D]
   float *const aE = reinterpret_cast<float *>(sm.dSs);            // [C][D]
+  float *const daS = reinterpret_cast<float *>(sm.dSs) + kC * D;  // [C][D], scalar decay: da per channel
   const int chunk = blockIdx.x % p.nch, ug = blockIdx.x / p.nch;  // ug = n * H_qk + gq
   const int n = ug / p.H_qk, gq = ug - n * p.H_qk;
   const int G = GRP ? p.H_v / p.H_qk : 1;
@@ -619,7 +676,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
   floatx4 dq[2] = {zero4(), zero4()}, dk[2] = {zero4(), zero4()};
   BWD_TIMER_INIT
 
-  for (int hv = 0; hv < G; ++hv) {
+  // One value head: a lambda so that, with several heads, the thread's
+  // indices can be made opaque per head (otherwise the addresses derived
+  // from them are hoisted out of the loop and held across it, in scratch).
+  auto head = [&](const int hv, const int tid, const int c, const int g) __attribute__((always_inline)) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nb = wave, ib = wave;
     const int h = gq * G + hv;
     const size_t unit = (size_t)n * p.H_v + h;
     // ---- every request of the chunk first, the decays first of all (the
@@ -632,15 +694,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
       const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
-      const size_t off = (tok0 + min(t, Tc - 1)) * v_row + (size_t)h * D + i4;
-      av[it] = *reinterpret_cast<const floatx4 *>(p.a + off);
+      av[it] = gate_a4<GF, D>(p.a, (tok0 + min(t, Tc - 1)) * p.H_v + h, i4);
     }
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
       const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
       const size_t row = tok0 + min(t, Tc - 1), off = row * v_row + (size_t)h * D + i4;
-      bv[it] = *reinterpret_cast<const floatx4 *>(p.b + off);
-      wv[it] = *reinterpret_cast<const floatx4 *>(p.w + off);
+      bv[it] = gate_bw4<GF, D>(p.b, p.b, row * p.H_v + h, i4);
+      wv[it] = gate_bw4<GF, D>(p.w, p.b, row * p.H_v + h, i4);
       qv[it] = *reinterpret_cast<const Fr *>(p.q + row * qk_row + (size_t)gq * D + i4);
       kv[it] = *reinterpret_cast<const Fr *>(p.k + row * qk_row + (size_t)gq * D + i4);
       vv[it] = *reinterpret_cast<const Fr *>(p.v + off);
@@ -744,6 +805,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
     unit_lower_inverse(sm.Akb, sm.Lb, tid);
     BWD_MARK(4);
 
+    // coupled forms: this lane's part of d(beta) for its 8 tokens
+    float bsum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     // ---- value side (columns 16 nb ..)
     {
       const int jc = 16 * nb + c;
@@ -753,9 +816,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * tb + 4 * g + j;
-          const size_t off = (tok0 + min(t, Tc - 1)) * v_row + (size_t)h * D + jc;
-          wq[tb][j] = p.w[off];
-          vq[tb][j] = bf16_to_f32(p.v[off]);
+          const size_t row = tok0 + min(t, Tc - 1);
+          wq[tb][j] = gate_bw1<GF, D>(p.w, p.b, row * p.H_v + h, jc);
+          vq[tb][j] = bf16_to_f32(p.v[row * v_row + (size_t)h * D + jc]);
         }
       floatx4 Z[2], dR[2];
 #pragma unroll
@@ -794,7 +857,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
           if (t < Tc) {
             const size_t off = (tok0 + t) * v_row + (size_t)h * D + jc;
             p.dv[off] = f32_to_bf16(wq[tb][j] * u[j]);
-            p.dw[off] = vq[tb][j] * u[j];
+            if constexpr (CPL)
+              bsum[tb][j] = vq[tb][j] * u[j];
+            else
+              put_gate_grad<GF>(p.dw, off, vq[tb][j] * u[j], wq[tb][j], false);
           }
         }
 #pragma unroll
@@ -816,7 +882,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
     for (int it = 0; it < NQ; ++it) {
       const int e = tid + NT * it, t = quad_t<D>(e), i4 = quad_i<D>(e);
       av2[it] = floatx4{1.f, 1.f, 1.f, 1.f};
-      if (t < Tc) av2[it] = *reinterpret_cast<const floatx4 *>(p.a + (tok0 + t) * v_row + (size_t)h * D + i4);
+      if (t < Tc) av2[it] = gate_a4<GF, D>(p.a, (tok0 + t) * p.H_v + h, i4);
     }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -824,7 +890,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * tb + 4 * g + j, i = 16 * ib + c;
         const size_t row = tok0 + min(t, Tc - 1);
-        bq[tb][j] = t < Tc ? p.b[row * v_row + (size_t)h * D + i] : 0.f;
+        bq[tb][j] = t < Tc ? gate_bw1<GF, D>(p.b, p.b, row * p.H_v + h, i) : 0.f;
         kq[tb][j] = t < Tc ? bf16_to_f32(p.k[row * qk_row + (size_t)gq * D + i]) : 0.f;
       }
     floatx4 dQl[2], dKl[2], dKm[2], dBm[2];
@@ -915,7 +981,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
           const float lam = lq[tb][j], mu = __builtin_amdgcn_rcpf(lam);
           dq[tb][j] += lam * dQl[tb][j];
           dk[tb][j] += lam * dKl[tb][j] + mu * (dKm[tb][j] + bq[tb][j] * dBm[tb][j]);
-          if (t < Tc) p.db[(tok0 + t) * v_row + (size_t)h * D + i] = mu * kq[tb][j] * dBm[tb][j];
+          if (t < Tc) {
+            const float dbv = mu * kq[tb][j] * dBm[tb][j];
+            if constexpr (CPL)
+              bsum[tb][j] += dbv;
+            else
+              put_gate_grad<GF>(p.db, (tok0 + t) * v_row + (size_t)h * D + i, dbv, bq[tb][j], false);
+          }
         }
       }
     }
@@ -948,27 +1020,71 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
         for (int k = 7; k >= 0; --k) {
           acc += dg8[k];
           const int t = t0 + k;
-          if (t < Tc) p.da[(tok0 + t) * v_row + (size_t)h * D + i] = acc * __builtin_amdgcn_rcpf(a8[k]);
+          if (t < Tc) {
+            const float dav = acc * __builtin_amdgcn_rcpf(a8[k]);
+            if constexpr (SCA)
+              daS[t * D + i] = dav;  // summed over the channels below
+            else
+              put_gate_grad<GF>(p.da, (tok0 + t) * v_row + (size_t)h * D + i, dav, a8[k], true);
+          }
         }
       }
     }
-    __syncthreads();
-    BWD_MARK(9);
-  }
-  // dq, dk
-  {
-    const int i = 16 * ib + c;
+    // coupled forms: d(beta) of this lane's tokens summed over the wave's 16
+    // columns (write side) and 16 channels (erase side), then over the waves
+    if constexpr (CPL) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * tb + 4 * g + j;
-        if (t < Tc) {
-          const size_t off = (tok0 + t) * qk_row + (size_t)gq * D + i;
-          p.dq[off] = f32_to_bf16(dq[tb][j]);
-          p.dk[off] = f32_to_bf16(dk[tb][j]);
+        for (int j = 0; j < 4; ++j) {
+          float x = bsum[tb][j];
+          x += __shfl_xor(x, 8, 16);
+          x += __shfl_xor(x, 4, 16);
+          x += __shfl_xor(x, 2, 16);
+          x += __shfl_xor(x, 1, 16);
+          if (c == 0) sm.beta8[wave][16 * tb + 4 * g + j] = x;
         }
+    }
+    __syncthreads();
+    if constexpr (CPL) {
+      if (tid < Tc) {
+        float sb = 0.f;
+#pragma unroll
+        for (int w8 = 0; w8 < 8; ++w8) sb += sm.beta8[w8][tid];
+        static_cast<float *>(p.db)[(tok0 + tid) * p.H_v + h] = sb;
       }
+    }
+    if constexpr (SCA) {  // d(alpha): da summed over the channels
+      if (tid < Tc) {
+        float sa = 0.f;
+        for (int i = 0; i < D; ++i) sa += daS[tid * D + i];
+        static_cast<float *>(p.da)[(tok0 + tid) * p.H_v + h] = sa;
+      }
+    }
+    BWD_MARK(9);
+    if (hv == G - 1) {  // dq, dk
+      const int i = 16 * ib + c;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * tb + 4 * g + j;
+          if (t < Tc) {
+            const size_t off = (tok0 + t) * qk_row + (size_t)gq * D + i;
+            p.dq[off] = f32_to_bf16(dq[tb][j]);
+            p.dk[off] = f32_to_bf16(dk[tb][j]);
+          }
+        }
+    }
+  };
+  if constexpr (GRP) {
+    for (int hv = 0; hv < G; ++hv) {
+      int tid_h = tid, c_h = c, g_h = g;
+      asm volatile("" : "+v"(tid_h), "+v"(c_h), "+v"(g_h));
+      head(hv, tid_h, c_h, g_h);
+    }
+  } else {
+    head(0, tid, c, g);
   }
   BWD_MARK(10);
   BWD_TIMER_STORE
@@ -978,7 +1094,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(GradParams p) {
 
 // ---------------------------------------------------------------- host
 bool backward_chunked_eligible(const BackwardArgs &a) {
-  if (a.cu_seqlens || a.gate_form != kGateGeneral || !a.bf16 || a.d_k != 128 || a.d_v != 128) return false;
+  if (a.cu_seqlens || !a.bf16 || a.d_k != 128 || a.d_v != 128) return false;
   if (a.B <= 0 || a.T <= 0 || a.H_v % a.H_qk != 0) return false;
   PrefillArgs fa{};
   fa.B = a.B; fa.T = a.T; fa.H_qk = a.H_qk; fa.H_v = a.H_v; fa.d_k = a.d_k; fa.d_v = a.d_v;
@@ -1017,7 +1133,11 @@ hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *
   fa.chunk = 64;
   fa.bf16 = true;
   fa.nct = prefill_pick_nct(a.B, a.H_v, a.d_v);
-  fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.a = a.a; fa.b = a.b; fa.w = a.w; fa.S0 = a.S0;
+  const bool coupled = a.gate_form == kGateCoupled || a.gate_form == kGateScalar;
+  fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.a = a.a; fa.b = a.b; fa.w = coupled ? a.b : a.w; fa.S0 = a.S0;
+  fa.coupled = coupled;
+  fa.scalar_decay = a.gate_form == kGateScalar;
+  fa.preact = a.gate_form == kGatePre;
   fa.force_nseg = 1;
   fa.chunk_states = cst;
   e = launch_prefill(fa, st);
@@ -1028,7 +1148,16 @@ hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *
   pp.a = a.a; pp.b = a.b;
   pp.prep = prep; pp.gc = gc; pp.flag = flag;
   pp.T = a.T; pp.H_qk = a.H_qk; pp.H_v = a.H_v; pp.nch = l.nch;
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(units * l.nch), dim3(256), 0, st, pp);
+  switch (a.gate_form) {
+    case kGatePre: hipLaunchKernelGGL((bwd_prep_kernel<D, kGatePre>), dim3(units * l.nch), dim3(256), 0, st, pp); break;
+    case kGateCoupled:
+      hipLaunchKernelGGL((bwd_prep_kernel<D, kGateCoupled>), dim3(units * l.nch), dim3(256), 0, st, pp);
+      break;
+    case kGateScalar:
+      hipLaunchKernelGGL((bwd_prep_kernel<D, kGateScalar>), dim3(units * l.nch), dim3(256), 0, st, pp);
+      break;
+    default: hipLaunchKernelGGL((bwd_prep_kernel<D, kGateGeneral>), dim3(units * l.nch), dim3(256), 0, st, pp);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   int hflag = 0;
   if ((e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
@@ -1052,10 +1181,25 @@ hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *
   gp.dv = static_cast<uint16_t *>(a.dv);
   gp.da = a.da; gp.db = a.db; gp.dw = a.dw;
   gp.T = a.T; gp.H_qk = a.H_qk; gp.H_v = a.H_v; gp.nch = l.nch;
-  if (a.H_v == a.H_qk)
-    hipLaunchKernelGGL((bwd_grad_kernel<D, false>), dim3(a.B * a.H_qk * l.nch), dim3(512), 0, st, gp);
-  else
-    hipLaunchKernelGGL((bwd_grad_kernel<D, true>), dim3(a.B * a.H_qk * l.nch), dim3(512), 0, st, gp);
+  const dim3 ggrid(a.B * a.H_qk * l.nch), gblock(512);
+  const bool grp = a.H_v != a.H_qk;
+  switch (a.gate_form) {
+    case kGatePre:
+      if (grp) hipLaunchKernelGGL((bwd_grad_kernel<D, true, kGatePre>), ggrid, gblock, 0, st, gp);
+      else hipLaunchKernelGGL((bwd_grad_kernel<D, false, kGatePre>), ggrid, gblock, 0, st, gp);
+      break;
+    case kGateCoupled:
+      if (grp) hipLaunchKernelGGL((bwd_grad_kernel<D, true, kGateCoupled>), ggrid, gblock, 0, st, gp);
+      else hipLaunchKernelGGL((bwd_grad_kernel<D, false, kGateCoupled>), ggrid, gblock, 0, st, gp);
+      break;
+    case kGateScalar:
+      if (grp) hipLaunchKernelGGL((bwd_grad_kernel<D, true, kGateScalar>), ggrid, gblock, 0, st, gp);
+      else hipLaunchKernelGGL((bwd_grad_kernel<D, false, kGateScalar>), ggrid, gblock, 0, st, gp);
+      break;
+    default:
+      if (grp) hipLaunchKernelGGL((bwd_grad_kernel<D, true, kGateGeneral>), ggrid, gblock, 0, st, gp);
+      else hipLaunchKernelGGL((bwd_grad_kernel<D, false, kGateGeneral>), ggrid, gblock, 0, st, gp);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   *ran = true;
   return hipSuccess;

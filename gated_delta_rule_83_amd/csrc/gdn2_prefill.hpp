@@ -1484,9 +1484,19 @@ template <int DK, int C, int NCT, bool BF16>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *plan_only) {
   auto kernel = [&](int blocks, const PrefillParams &kp) {
     if constexpr (DK == 128 && BF16) {
-      if (kp.cst) {  // general gates only (the chunk-form backward)
-        hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false, false, true>), dim3(blocks), dim3(512), 0,
-                           st, kp);
+      if (kp.cst) {  // the chunk-form backward's states
+        if (a.scalar_decay)
+          hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, true, false, true>), dim3(blocks), dim3(512), 0,
+                             st, kp);
+        else if (a.coupled)
+          hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, true, false, false, true>), dim3(blocks), dim3(512), 0,
+                             st, kp);
+        else if (a.preact)
+          hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false, true, true>), dim3(blocks), dim3(512), 0,
+                             st, kp);
+        else
+          hipLaunchKernelGGL((prefill_kernel<DK, C, NCT, BF16, false, false, false, true>), dim3(blocks), dim3(512), 0,
+                             st, kp);
         return;
       }
     }
@@ -1524,9 +1534,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.oI = nullptr;
   p.cst = nullptr;
   const int units = a.B * a.H_v;
-  if (a.chunk_states && (pl.nseg > 1 || a.cu_seqlens || DK != 128 || !BF16 || a.coupled || a.scalar_decay ||
-                         a.preact))
-    return hipErrorInvalidValue;
+  if (a.chunk_states && (pl.nseg > 1 || a.cu_seqlens || DK != 128 || !BF16)) return hipErrorInvalidValue;
   if (pl.nseg <= 1) {
     p.cst = a.chunk_states;
     kernel(units * ncb, p);

@@ -138,9 +138,10 @@ def test_chunk_form_layer_shape_sampled_heads(monkeypatch):
 def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
     """Where the chunk form's shape applies (bf16, d_k = d_v = 128) the
     workspace query returns the chunk form's size, smaller than the per-token
-    backward needs at once; the per-token backward (the other gate forms,
-    and per-channel gates with a channel that decays too fast for the chunk
-    form) then runs in rounds of segments within it. B2, T1100 (3 segments
+    backward needs at once; the per-token backward (for decays too fast for
+    the chunk form: here key channel 5 decays by about e^-90 within each half
+    chunk, or every channel in the scalar form) then runs in rounds of
+    segments within it. B2, T1100 (3 segments
     of 384 tokens, the last ragged) and T520 (3 of 256, the last shorter than
     a chunk: asked for 2 segments, which the prefill's plan turns into 3),
     two value heads per query/key head, S0 and dS_T: against the oracle of
@@ -151,10 +152,15 @@ def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
     rng = np.random.default_rng(5700 + len(form) + T)
     B, Hv = 2, 2
     x = form_inputs(rng, form, T, Hv, 128, 128, "bf16", DEV, B=B)
-    if form == "channel":  # key channel 5 decays by about e^-90 within each half chunk
-        a = x["a"].clone()
-        a[..., 5] = torch.exp(-torch.empty_like(a[..., 5]).uniform_(5.5, 6.0))
-        x["a"] = a
+    a = x["a"].clone()
+    fast = lambda y: torch.empty_like(y, dtype=torch.float32).uniform_(5.5, 6.0)
+    if form == "preact":  # a = 1 / (1 + e^x): x in [5.5, 6]
+        a[..., 5] = fast(a[..., 5]).to(a.dtype)
+    elif form == "scalar":
+        a = torch.exp(-fast(a))
+    else:
+        a[..., 5] = torch.exp(-fast(a[..., 5]))
+    x["a"] = a
     desc = g.make_desc(B, T, 1, Hv, 128, 128, 64, g.GDN2_BF16)
     ws = g.gdn2_chunk_backward_workspace_bytes(desc)
     monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
@@ -169,5 +175,33 @@ def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
     names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
     errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
     print(f"[per-token rounds {form}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("form,B,T,Hqk,Hv", [("preact", 2, 107, 1, 2), ("coupled", 2, 107, 1, 2),
+                                            ("scalar", 2, 107, 1, 2), ("preact", 1, 200, 2, 2),
+                                            ("coupled", 1, 200, 2, 2), ("scalar", 1, 200, 2, 2)])
+def test_chunk_form_gate_forms(form, B, T, Hqk, Hv, monkeypatch):
+    """The chunk form for the other gate forms: pre-activations in bf16
+    (activated as read, gradients through the activations), coupled beta
+    (d(beta) summed over the erase side's channels and the write side's
+    columns) and scalar alpha (d(alpha) summed over the channels); ragged
+    chunks, grouped heads, S0 and dS_T: against the oracle of the form."""
+    from tests.gate_forms import backward_alone, form_inputs, oracle_backward
+    from tests.parity import TOL, normwise, to_np
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    rng = np.random.default_rng(5800 + len(form) + T + Hqk)
+    x = form_inputs(rng, form, T, Hv, 128, 128, "bf16", DEV, B=B, Hqk=Hqk)
+    S0 = torch.from_numpy((rng.standard_normal((B, Hv, 128, 128)) * 0.5).astype(np.float32)).to(DEV)
+    dO = torch.from_numpy(rng.standard_normal((B, T, Hv, 128)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((B, Hv, 128, 128)).astype(np.float32)).to(DEV)
+    got = backward_alone(form, x, S0, dO, dST)
+    torch.cuda.synchronize()
+    ref = oracle_backward(form, x, S0, dO, dST)
+    names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
+    errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
+    print(f"[chunk form {form} B{B} T{T} Hqk{Hqk} Hv{Hv}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()),
+          flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
     assert not bad, bad
