@@ -57,6 +57,7 @@ using BF = __bf16;
 using Fr = OB::Frag;
 using P2 = Pair<true>;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes (a plain vector: kept in registers)
 
 // e^-60: the smallest decay over a chunk (anchor at its start) or over each
 // half of it (anchor at its middle) whose inverse the operands may carry
@@ -474,9 +475,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p) {
 // chunk to the first: dS (the adjoint of chunk c's exiting state) is stored
 // (bf16, [unit][chunk][column][channel]), then
 // dS <- diag(gamma_C) dS - Kd^T (Wt dS) + Qe^T dO.
-// A chunk's operands are requested kPF chunks ahead into one of kPF
-// register sets, and staged in LDS one chunk ahead.
-constexpr int kPF = 2;
+// A chunk's operands are requested two chunks ahead into one of two
+// register sets (plain vector types: arrays of HIP's uint4 struct were kept
+// in scratch), and staged in LDS one chunk ahead.
 template <int D>
 struct DstSmem {
   alignas(16) BF ops[2][3 * kC * D];
@@ -514,38 +515,37 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
       dS[mt][j] = p.dST ? p.dST[((size_t)unit * D + 16 * mt + 4 * g + j) * D + col] : 0.f;
 
   struct Raw {
-    uint4 o[OPS16 / 256];
-    uint4 d;
+    u32x4 o[OPS16 / 256];
+    u32x4 d;
     floatx4 gcv;
   };
   // chunk ch's operands into registers; every request is issued on every
   // call (past the end: a clamped row, zeroed), so that the number of
   // requests between a request and its use never varies
-  auto fetch = [&](int ch, Raw &r) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.prep + ((size_t)unit * p.nch + ch) * 3 * kC * D);
+  auto fetch = [&](int ch, Raw &r) __attribute__((always_inline)) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(p.prep + ((size_t)unit * p.nch + ch) * 3 * kC * D);
 #pragma unroll
     for (int it = 0; it < OPS16 / 256; ++it) r.o[it] = src[tid + 256 * it];
     const int t = tid >> 3, q8 = tid & 7;  // 32 tokens x 8 pieces of 8 columns
     const int tok = ch * kC + t;
-    const uint4 d = *reinterpret_cast<const uint4 *>(p.dO + ((size_t)n * p.T + min(tok, p.T - 1)) * p.H_v * D +
+    const u32x4 d = *reinterpret_cast<const u32x4 *>(p.dO + ((size_t)n * p.T + min(tok, p.T - 1)) * p.H_v * D +
                                                     (size_t)h * D + cb * 64 + 8 * q8);
-    r.d = tok < p.T ? d : uint4{0, 0, 0, 0};
+    r.d = tok < p.T ? d : u32x4{0u, 0u, 0u, 0u};
     r.gcv = *reinterpret_cast<const floatx4 *>(p.gc + ((size_t)unit * p.nch + ch) * D + 4 * (tid % (D / 4)));
   };
-  auto stash = [&](int buf, const Raw &r) {
-    uint4 *dst = reinterpret_cast<uint4 *>(sm.ops[buf]);
+  auto stash = [&](int buf, const Raw &r) __attribute__((always_inline)) {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sm.ops[buf]);
 #pragma unroll
     for (int it = 0; it < OPS16 / 256; ++it) dst[tid + 256 * it] = r.o[it];
-    *reinterpret_cast<uint4 *>(&sm.dO[buf][sx<64>(tid >> 3, 8 * (tid & 7))]) = r.d;
+    *reinterpret_cast<u32x4 *>(&sm.dO[buf][sx<64>(tid >> 3, 8 * (tid & 7))]) = r.d;
     if (tid < D / 4) reinterpret_cast<floatx4 *>(sm.gc[buf])[tid] = r.gcv;
   };
 
-  Raw r[kPF];
-  // body for the k-th chunk from the last (register set k % kPF = S)
-  auto body = [&](auto S, int k) {
-    constexpr int s = decltype(S)::value;
+  Raw r0, r1;  // chunk k (from the last) is requested into set k % 2, two chunks ahead
+  auto body = [&](Raw &cur, Raw &nxt, int k) __attribute__((always_inline)) {
     const int ch = p.nch - 1 - k, buf = k & 1;
-    fetch(max(ch - kPF, 0), r[s]);  // set s held chunk ch, staged in the previous step
+    fetch(max(ch - 2, 0), cur);  // cur held chunk ch, staged in the previous step (chunk 0 again at the end)
+    // the adjoint of this chunk's exiting state
     BF *dsto = p.dst + (((size_t)unit * p.nch + ch) * D + col) * D + 4 * g;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<Fr *>(dsto + 16 * mt) = OB::from_acc(dS[mt]);
@@ -572,19 +572,18 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
       acc = mma(acc, P2{frag(Kd, mt * 2), frag(Kd, mt * 2 + 1)}, Yf);
       dS[mt] = acc;
     }
-    // the next chunk (set s + 1, requested two steps ago) into the other
-    // buffer, last read in the previous step
-    if (k + 1 < p.nch) stash(buf ^ 1, r[(s + 1) % kPF]);
+    // the next chunk (requested a step ago) into the other buffer, last
+    // read in the previous step, before its barrier
+    if (k + 1 < p.nch) stash(buf ^ 1, nxt);
     __syncthreads();
   };
-
-  static_for<kPF>([&](auto S) { fetch(max(p.nch - 1 - decltype(S)::value, 0), r[decltype(S)::value]); });
-  stash(0, r[0]);
+  fetch(p.nch - 1, r0);
+  fetch(max(p.nch - 2, 0), r1);
+  stash(0, r0);
   __syncthreads();
-  for (int k = 0; k < p.nch; k += kPF) {
-    static_for<kPF>([&](auto S) {
-      if (k + decltype(S)::value < p.nch) body(S, k + decltype(S)::value);
-    });
+  for (int k = 0; k < p.nch; k += 2) {
+    body(r0, r1, k);
+    if (k + 1 < p.nch) body(r1, r0, k + 1);
   }
   if (p.dS0) {
 #pragma unroll

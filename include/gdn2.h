@@ -284,7 +284,8 @@ gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, cons
  * The pages define no backward pass; training the layer (the Gated
  * DeltaNet-2 post on tilnote.io reports a 1.3B-parameter model trained on
  * 100B tokens) needs the exact derivative of the forward map above, which
- * is what this computes (reverse mode through the per-token recurrence).
+ * is what this computes (in chunk form or through the per-token recurrence:
+ * see "How it runs" below).
  *
  * Arguments (all device pointers, caller-owned, contiguous row-major):
  *   desc : as for gdn2_chunk_forward. The chunk length is checked as there
@@ -298,22 +299,46 @@ gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, cons
  *   da, db : [B, T, H_v, d_k] fp32.   dw : [B, T, H_v, d_v] fp32.
  *   dS0  : [B, H_v, d_k, d_v] fp32, or NULL (not written). It may be the
  *          same pointer as dS_T (in place), but not a partial overlap.
- *   workspace : gdn2_chunk_backward_workspace_bytes(desc) bytes (fp32 state
- *          checkpoints every 4 tokens, per 64-column block key-side partial
- *          sums and every token's k-read: about
- *          (d_k * d_v / 4 + (4 * d_k + 1) * ceil(d_v / 64) + d_v) * 4 bytes
- *          per token and value head, plus d_k * d_v * 4 per sequence and value
- *          head), 256-byte aligned; NULL only when that size is 0. Contents
- *          on return are unspecified.
- * With few sequences x value heads and long sequences the backward runs as
- * segments in parallel: entering states from the prefill's split passes,
+ *   workspace : gdn2_chunk_backward_workspace_bytes(desc) bytes, 256-byte
+ *          aligned; NULL only when that size is 0. Contents on return are
+ *          unspecified. Its size:
+ *          - bf16 inputs with d_k = d_v = 128 (the chunk form below): per
+ *            32-token chunk and value head the state entering it and the
+ *            adjoint of the state leaving it (bf16, d_k * d_v each), the
+ *            chunk's adjoint operands (3 * 32 * d_k bf16) and its decay
+ *            (d_k fp32), plus one more state per sequence and value head:
+ *            about 2.8 KB per token and value head, 1.49 GB at B8 T4096 H16
+ *            (and at least what the per-token backward needs in rounds);
+ *          - otherwise (the per-token backward): fp32 state checkpoints
+ *            every 4 tokens, per 64-column block key-side partial sums and
+ *            every token's k-read, about
+ *            (d_k * d_v / 4 + (4 * d_k + 1) * ceil(d_v / 64) + d_v) * 4 bytes
+ *            per token and value head, plus d_k * d_v * 4 per sequence and
+ *            value head (more with the segment split below).
+ * How it runs. bf16 inputs with d_k = d_v = 128, every gate form: in chunk
+ * form on the matrix cores (the prefill run again storing the state at every
+ * 32-token chunk boundary; per chunk the operands of the state adjoint's
+ * chunk step; the adjoint swept from the last chunk to the first; every
+ * gradient of a chunk from its entering state and exiting adjoint). Its
+ * products take bf16 operands with fp32 accumulation, the states and
+ * adjoints at chunk boundaries rounded to bf16 (the prefill's own rounding
+ * of its chunk products), within the bf16 tolerance. A chunk in which some
+ * key channel decays by less than e^-60 over each half (the prefill steps
+ * such chunks token by token) is beyond its operands' range: then (the
+ * stream is synchronised once to find out) the per-token backward runs
+ * instead, in rounds of 512-token segments that fit this workspace.
+ * Otherwise the per-token backward: reverse mode through the recurrence,
+ * fp32 arithmetic; with few sequences x value heads and long sequences as
+ * segments in parallel (entering states from the prefill's split passes,
  * exiting adjoints from one adjoint-only sweep, then each segment as a
- * packed sequence; the workspace query accounts for it, and the
- * environment variable GDN2_BACKWARD_SPLIT=<n>, read at each call, forces n
- * segments (1: never split). Gradients that depend on the forward states
- * then carry the prefill's rounding (within the stated tolerances).
- * Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums; all
- * arithmetic is fp32. The result is deterministic (no atomics).
+ * packed sequence), which the workspace query accounts for; gradients that
+ * depend on the forward states then carry the prefill's rounding. The
+ * environment variables GDN2_BACKWARD_CHUNKED (0: never the chunk form,
+ * and the query returns the per-token size; 2: only the chunk form, failing
+ * with GDN2_ERR_HIP where it cannot run) and GDN2_BACKWARD_SPLIT=<n> (n
+ * segments for the per-token backward; 1: never split) are read at each
+ * call. Gradients of bf16 inputs are rounded to bf16 (RNE) from fp32 sums.
+ * The result is deterministic (no atomics).
  * Errors: as for gdn2_chunk_forward; a missing required pointer is
  * GDN2_ERR_NULL_POINTER, a small or misaligned workspace GDN2_ERR_WORKSPACE /
  * GDN2_ERR_BAD_SHAPE, and an output or the workspace overlapping an input,
@@ -366,10 +391,11 @@ gdn2_status gdn2_chunk_backward_scalar(const gdn2_desc *desc, const void *q, con
  * (cu_seqlens: B + 1 non-decreasing int32 device offsets; offsets outside
  * [0, T] are clamped). The token tensors (q, k, v, a, b, w, dO and the token
  * gradients) hold desc->T tokens; S0, dS_T and dS0 hold one state per
- * sequence. Each sequence's gradients are computed exactly as
- * gdn2_chunk_backward computes them for that sequence alone. The workspace
- * is gdn2_chunk_backward_varlen_workspace_bytes(desc) bytes (the same
- * regions as gdn2_chunk_backward's, over T tokens in all). Errors as for
+ * sequence. Packed sequences run the per-token backward: each sequence's
+ * gradients are those of gdn2_chunk_backward's per-token backward on that
+ * sequence alone, bit for bit (equal to its chunk form up to rounding). The
+ * workspace is gdn2_chunk_backward_varlen_workspace_bytes(desc) bytes (the
+ * per-token backward's regions over T tokens in all). Errors as for
  * gdn2_chunk_backward, plus GDN2_ERR_NULL_POINTER for a null cu_seqlens when
  * B > 0. */
 size_t gdn2_chunk_backward_varlen_workspace_bytes(const gdn2_desc *desc);
@@ -385,7 +411,8 @@ gdn2_status gdn2_chunk_backward_varlen(const gdn2_desc *desc, const int32_t *cu_
  * (CHANNEL, fp32; PREACT, input dtype, gradients of the pre-activations);
  * da and db = dbeta (COUPLED; SCALAR: da = dalpha [T, H_v]), dw unused (may
  * be NULL). Workspace: gdn2_chunk_backward_varlen_workspace_bytes(desc);
- * each sequence's gradients are those of the unpacked call on it alone.
+ * each sequence's gradients are those of the unpacked call's per-token
+ * backward on it alone.
  * Errors as for gdn2_chunk_backward_varlen. */
 gdn2_status gdn2_chunk_backward_varlen_gates(const gdn2_desc *desc, const int32_t *cu_seqlens, gdn2_gates gates,
                                              const void *q, const void *k, const void *v, const void *a,
