@@ -161,7 +161,7 @@ def main():
                     help="timed launches of the backward pass over the prefill shape (0: skip)")
     ap.add_argument("--long-backward", type=int, default=0,
                     help="also time this many launches of the backward of the long-context shape "
-                         "(B1 T65536 H16 d128 bf16, split into segments), reported under backward_long "
+                         "(B1 T65536 H16 d128 bf16, in chunk form where it applies), reported under backward_long "
                          "(default 0: off)")
     ap.add_argument("--chunk", type=int, default=None, help="override the prefill chunk length")
     ap.add_argument("--counters", type=int, default=None, metavar="CONFIG",
@@ -515,16 +515,25 @@ def main():
             return g.chunk_backward(tl["q"], tl["k"], tl["v"], tl["a"], tl["b"], tl["w"], None, dOl, dSTl,
                                     grads=grads, workspace=wsl, stream=stream)
 
-        gl = backward_long()
+        lform = "chunk"
+        os.environ["GDN2_BACKWARD_CHUNKED"] = "2"
+        try:
+            gl = backward_long()
+        except RuntimeError:
+            lform = "automatic"
+            os.environ.pop("GDN2_BACKWARD_CHUNKED")
+            gl = backward_long()
         torch.cuda.synchronize()
         l_ms = time_each(lambda: backward_long(gl), args.long_backward)
+        os.environ.pop("GDN2_BACKWARD_CHUNKED", None)
         l_avg = float(np.mean(l_ms)) / 1e3
-        lfl, _ = backward_algorithmic(cl)
-        bwd_long = {"workload": "backward B1 T65536 H16 d128 bf16",
+        lfl, lby = backward_algorithmic(cl)
+        bwd_long = {"workload": "backward B1 T65536 H16 d128 bf16", "form": lform,
                     "launches": args.long_backward, "ms": l_avg * 1e3, "min_ms": min(l_ms),
-                    "tokens_per_s": cl.B * cl.T / l_avg, "achieved": lfl / l_avg / 1e12,
-                    "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s", "workspace_bytes": wsl.numel()}
-        log(f"[bench] long-context backward: {l_avg * 1e3:.2f} ms per launch (min {min(l_ms):.2f})")
+                    "tokens_per_s": cl.B * cl.T / l_avg, "bound": "hbm", "achieved": lby / l_avg / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lby / l_avg / 1e9 / HBM_PEAK_GBS,
+                    "algorithmic_bytes": lby, "recurrence_flops": lfl, "workspace_bytes": wsl.numel()}
+        log(f"[bench] long-context backward ({lform}): {l_avg * 1e3:.2f} ms per launch (min {min(l_ms):.2f})")
         del gl, wsl, tl
 
     # ---------------------------------------------------------------- CPU baseline (oracle)

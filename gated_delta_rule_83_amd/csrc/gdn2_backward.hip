@@ -1417,6 +1417,13 @@ size_t backward_rounds_min_bytes(int B, int T, int H_qk, int H_v, int d_k, int d
 
 }  // namespace
 
+hipError_t launch_split_states(float *S_in, const float *S0, const float *seg_states, int B, int H_v, int nseg,
+                               int dkdv, hipStream_t st) {
+  hipLaunchKernelGGL(split_states_kernel, dim3(B * nseg * H_v), dim3(256), 0, st, S_in, S0, seg_states, B, H_v, nseg,
+                     dkdv);
+  return hipGetLastError();
+}
+
 // The per-token backward all at once: unsplit, or the split plan's.
 size_t per_token_workspace_bytes(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16) {
   const BwdSplit sp = backward_split_plan(B, T, H_qk, H_v, d_k, d_v, bf16);

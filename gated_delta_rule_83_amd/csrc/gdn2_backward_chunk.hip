@@ -318,9 +318,40 @@ __device__ __forceinline__ void put_gate_grad(void *out, size_t idx, float dx, f
 }
 
 // ---------------------------------------------------------------- layouts
+// The chunk-boundary states of few long sequences come from segments run in
+// parallel (PrefillArgs::cst_segs) when the prefill's own split plan would cut
+// the sequences into segments of equal length: its first two passes give the
+// state entering every segment (seg_states), then one launch runs all
+// segments from those states, storing the states at their chunk boundaries.
+// seg.nseg = 1: one launch over whole sequences.
+struct CstSplit {
+  int nseg, seg_len, req;  // req: the force_nseg that yields this plan
+};
+
+PrefillArgs cst_prefill_args(int B, int T, int H_qk, int H_v) {
+  PrefillArgs fa{};
+  fa.B = B; fa.T = T; fa.H_qk = H_qk; fa.H_v = H_v; fa.d_k = 128; fa.d_v = 128;
+  fa.chunk = 64;
+  fa.bf16 = true;
+  fa.nct = prefill_pick_nct(B, H_v, 128);
+  return fa;
+}
+
+CstSplit cst_split_plan(int B, int T, int H_qk, int H_v) {
+  const CstSplit none{1, T, 1};
+  PrefillArgs fa = cst_prefill_args(B, T, H_qk, H_v);
+  const PrefillPlan def = prefill_plan(fa);  // the prefill's own choice
+  if (def.nseg < 2) return none;
+  fa.force_nseg = def.nseg;
+  const PrefillPlan pl = prefill_plan(fa);
+  if (pl.nseg < 2 || pl.chunk != kC || (long)pl.nseg * pl.seg_len != T || pl.seg_len % kC != 0) return none;
+  return CstSplit{pl.nseg, pl.seg_len, def.nseg};
+}
+
 struct ChunkLayout {
   int B, T, H_qk, H_v, nch;
-  size_t cst, dst, prep, gc, flag, total;  // byte offsets of the workspace regions
+  CstSplit seg;
+  size_t cst, dst, prep, gc, flag, trans, segst, sin, total;  // byte offsets of the workspace regions
 };
 
 template <int D>
@@ -328,13 +359,19 @@ ChunkLayout chunk_layout(int B, int T, int H_qk, int H_v) {
   ChunkLayout l;
   l.B = B; l.T = T; l.H_qk = H_qk; l.H_v = H_v;
   l.nch = (T + kC - 1) / kC;
+  l.seg = cst_split_plan(B, T, H_qk, H_v);
   const size_t units = (size_t)B * H_v, mat = (size_t)D * D * 2;
   l.cst = 0;
   l.dst = align256(units * (l.nch + 1) * mat);
   l.prep = l.dst + align256(units * l.nch * mat);
   l.gc = l.prep + align256(units * l.nch * 3 * kC * D * 2);
   l.flag = l.gc + align256(units * l.nch * D * 4);
-  l.total = l.flag + 256;
+  // segments: transitions, exiting states, entering states (fp32)
+  const size_t segm = l.seg.nseg > 1 ? align256((size_t)l.seg.nseg * units * D * D * 4) : 0;
+  l.trans = l.flag + 256;
+  l.segst = l.trans + segm;
+  l.sin = l.segst + segm;
+  l.total = l.sin + segm;
   return l;
 }
 
@@ -1127,16 +1164,35 @@ hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *
   hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
   if (e != hipSuccess) return e;
   // 1. the states entering every chunk
-  PrefillArgs fa{};
-  fa.B = a.B; fa.T = a.T; fa.H_qk = a.H_qk; fa.H_v = a.H_v; fa.d_k = a.d_k; fa.d_v = a.d_v;
-  fa.chunk = 64;
-  fa.bf16 = true;
-  fa.nct = prefill_pick_nct(a.B, a.H_v, a.d_v);
+  PrefillArgs fa = cst_prefill_args(a.B, a.T, a.H_qk, a.H_v);
   const bool coupled = a.gate_form == kGateCoupled || a.gate_form == kGateScalar;
   fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.a = a.a; fa.b = a.b; fa.w = coupled ? a.b : a.w; fa.S0 = a.S0;
   fa.coupled = coupled;
   fa.scalar_decay = a.gate_form == kGateScalar;
   fa.preact = a.gate_form == kGatePre;
+  if (l.seg.nseg > 1) {
+    // the state entering every segment (the prefill split's first two passes)
+    float *trans = reinterpret_cast<float *>(w + l.trans);
+    float *segst = reinterpret_cast<float *>(w + l.segst);
+    float *sin = reinterpret_cast<float *>(w + l.sin);
+    fa.force_nseg = l.seg.req;
+    fa.seg_states = segst;
+    fa.workspace = trans;
+    fa.workspace_bytes = l.segst - l.trans;
+    const PrefillPlan pl = prefill_plan(fa);
+    if (pl.nseg != l.seg.nseg || pl.seg_len != l.seg.seg_len) return hipErrorInvalidValue;
+    if ((e = launch_prefill(fa, st)) != hipSuccess) return e;
+    if ((e = launch_split_states(sin, a.S0, segst, a.B, a.H_v, l.seg.nseg, D * D, st)) != hipSuccess) return e;
+    // every segment from its entering state, as B * nseg sequences
+    fa.B = a.B * l.seg.nseg;
+    fa.T = l.seg.seg_len;
+    fa.nct = prefill_pick_nct(fa.B, a.H_v, a.d_v);
+    fa.S0 = sin;
+    fa.seg_states = nullptr;
+    fa.workspace = nullptr;
+    fa.workspace_bytes = 0;
+    fa.cst_segs = l.seg.nseg;
+  }
   fa.force_nseg = 1;
   fa.chunk_states = cst;
   e = launch_prefill(fa, st);

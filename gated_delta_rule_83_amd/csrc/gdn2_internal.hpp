@@ -59,6 +59,9 @@ struct PrefillArgs {
   // PrefillParams::cst); needs an unsplit plan (force_nseg = 1) and no
   // cu_seqlens
   void *chunk_states = nullptr;
+  // chunk_states of B / cst_segs sequences, each given as cst_segs consecutive
+  // segments of T tokens (PrefillParams::cst_segs); 1: whole sequences
+  int cst_segs = 1;
 };
 
 // How a prefill call runs: the chunk length used (the largest supported one
@@ -134,6 +137,11 @@ bool backward_chunked_eligible(const BackwardArgs &a);
 size_t backward_chunked_workspace_bytes(int B, int T, int H_qk, int H_v);
 hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *ran);
 hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
+// Entering state of every segment of B sequences cut into nseg segments:
+// S_in[(n * nseg + j) * H_v + h] = S0[n * H_v + h] (zero if S0 is null) for
+// j = 0, else seg_states[j - 1] (PrefillArgs::seg_states); d_k x d_v fp32.
+hipError_t launch_split_states(float *S_in, const float *S0, const float *seg_states, int B, int H_v, int nseg,
+                               int dkdv, hipStream_t stream);
 // Workspace of the backward of B sequences of T tokens: the split plan's
 // when few long sequences run as segments, else backward_workspace_bytes.
 size_t backward_workspace_bytes_split(int B, int T, int H_qk, int H_v, int d_k, int d_v, bool bf16);

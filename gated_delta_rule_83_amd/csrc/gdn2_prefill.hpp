@@ -307,7 +307,13 @@ struct PrefillParams {
   // output type, [B * H_v][ceil(T / C) + 1][d_v][d_k]: entry e of a
   // (sequence, head) is the state entering chunk e (e = 0: S0; the last
   // entry: the final state). Unsplit, unpacked launches only; null: none.
+  // With cst_segs > 1 the launch's sequences are consecutive segments of
+  // equal length, cst_segs to a sequence of the layout (n = m * cst_segs + j:
+  // segment j of sequence m), and segment j writes that sequence's entries
+  // j * nc .. j * nc + nc - 1 (nc chunks per segment), the last segment also
+  // the final entry.
   void *cst;
+  int cst_segs;
 };
 
 // Lower 16x16 tiles (r, c), c <= r, of the chunk's Gram matrices over the
@@ -1018,12 +1024,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 
   // Chunk-boundary states (see PrefillParams::cst): this lane's column,
   // four consecutive key channels per tile.
-  ET *const cstp = (CST && consumer && !ident)
-                       ? (ET *)p.cst + (((size_t)n * p.H_v + h) * (size_t)((Tl + C - 1) / C + 1) * d_v + col) * DK +
-                             4 * lg
-                       : nullptr;
+  const int cst_nc = (Tl + C - 1) / C;           // entries of this segment: 0 .. cst_nc
+  const int cst_j = CST ? n % p.cst_segs : 0;     // segment within its sequence
+  const bool cst_last = cst_j == p.cst_segs - 1;  // writes the final entry
+  ET *const cstp =
+      (CST && consumer && !ident)
+          ? (ET *)p.cst + ((((size_t)(n / p.cst_segs) * p.H_v + h) * (size_t)(cst_nc * p.cst_segs + 1) +
+                            (size_t)cst_j * cst_nc) * d_v + col) * DK + 4 * lg
+          : nullptr;
   auto store_cst = [&](int e) {
     if constexpr (!CST) return;
+    if (e == cst_nc && !cst_last) return;  // the next segment's entry 0
     ET *dst = cstp + (size_t)e * d_v * DK;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -1533,8 +1544,10 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, PrefillPlan *p
   p.cu = a.cu_seqlens;
   p.oI = nullptr;
   p.cst = nullptr;
+  p.cst_segs = a.cst_segs > 1 ? a.cst_segs : 1;
   const int units = a.B * a.H_v;
-  if (a.chunk_states && (pl.nseg > 1 || a.cu_seqlens || DK != 128 || !BF16)) return hipErrorInvalidValue;
+  if (a.chunk_states && (pl.nseg > 1 || a.cu_seqlens || DK != 128 || !BF16 || a.B % p.cst_segs != 0))
+    return hipErrorInvalidValue;
   if (pl.nseg <= 1) {
     p.cst = a.chunk_states;
     kernel(units * ncb, p);

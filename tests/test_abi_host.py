@@ -327,6 +327,22 @@ def test_backward_chunk_form_workspace(monkeypatch):
         monkeypatch.delenv("GDN2_BACKWARD_CHUNKED")
 
 
+def test_backward_chunk_form_workspace_long_context(monkeypatch):
+    """The long-context shape B1 T65536 H16 (bf16, d128): the chunk form's
+    workspace (about 3 GB) adds, to what one launch over the whole sequence
+    would need (GDN2_PREFILL_SPLIT=1), the prefill split's 8 segments: their
+    transitions, exiting and entering states (3 x 8 x 16 fp32 128 x 128)."""
+    monkeypatch.delenv("GDN2_BACKWARD_CHUNKED", raising=False)
+    monkeypatch.delenv("GDN2_PREFILL_SPLIT", raising=False)
+    c2 = g.make_desc(1, 65536, 16, 16, 128, 128, 64, g.GDN2_BF16)
+    seg = g.gdn2_chunk_backward_workspace_bytes(c2)
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
+    whole = g.gdn2_chunk_backward_workspace_bytes(c2)
+    monkeypatch.delenv("GDN2_PREFILL_SPLIT")
+    assert seg - whole == 3 * 8 * 16 * 128 * 128 * 4
+    assert 2.9e9 < seg < 3.1e9
+
+
 def test_backward_varlen_workspace_and_errors():
     """Packed sequences: the workspace counts desc.T tokens in all; a null
     cu_seqlens and overlaps with it are rejected before any launch."""

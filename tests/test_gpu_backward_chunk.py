@@ -205,3 +205,44 @@ def test_chunk_form_gate_forms(form, B, T, Hqk, Hv, monkeypatch):
           flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("form,B,T,Hqk,split", [("channel", 1, 8192, 1, None), ("channel", 1, 8192, 1, "1"),
+                                                ("channel", 2, 2048, 1, None), ("coupled", 2, 2048, 1, None),
+                                                ("preact", 1, 2048, 2, None), ("scalar", 1, 2048, 2, None)])
+def test_chunk_states_from_segments(form, B, T, Hqk, split, monkeypatch):
+    """Few long sequences (B1-2, two value heads): the prefill's split plan
+    cuts them into segments of 512 tokens (16 at T8192, 4 at T2048), so the
+    chunk-boundary states come from all segments at once, each run from its
+    entering state (GDN2_PREFILL_SPLIT=1: one launch over whole sequences
+    instead); S0 and dS_T present, against the oracle of the form. At T8192
+    the workspace shows the plan: the segments' transitions, exiting and
+    entering states (3 x 16 x 2 fp32 states) on top of the whole-sequence
+    form's."""
+    from tests.gate_forms import backward_alone, form_inputs, oracle_backward
+    from tests.parity import TOL, normwise, to_np
+    Hv = 2
+    if T == 8192:
+        desc = g.make_desc(B, T, Hqk, Hv, 128, 128, 64, g.GDN2_BF16)
+        monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
+        whole = g.gdn2_chunk_backward_workspace_bytes(desc)
+        monkeypatch.delenv("GDN2_PREFILL_SPLIT")
+        seg = g.gdn2_chunk_backward_workspace_bytes(desc)
+        assert seg - whole == 3 * 16 * B * Hv * 128 * 128 * 4
+    if split is not None:
+        monkeypatch.setenv("GDN2_PREFILL_SPLIT", split)
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    rng = np.random.default_rng(5900 + len(form) + B + 3 * Hqk + T)
+    x = form_inputs(rng, form, T, Hv, 128, 128, "bf16", DEV, B=B, Hqk=Hqk)
+    S0 = torch.from_numpy((rng.standard_normal((B, Hv, 128, 128)) * 0.5).astype(np.float32)).to(DEV)
+    dO = torch.from_numpy(rng.standard_normal((B, T, Hv, 128)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    dST = torch.from_numpy(rng.standard_normal((B, Hv, 128, 128)).astype(np.float32)).to(DEV)
+    got = backward_alone(form, x, S0, dO, dST)
+    torch.cuda.synchronize()
+    ref = oracle_backward(form, x, S0, dO, dST)
+    names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
+    errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
+    print(f"[chunk states from segments {form} B{B} T{T} Hqk{Hqk} split {split}] "
+          + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, bad
