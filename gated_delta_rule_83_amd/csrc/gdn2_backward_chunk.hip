@@ -522,6 +522,16 @@ struct DstSmem {
   alignas(16) float gc[2][D];
 };
 
+// The sweep over segments of seg_chunks chunks (the last may be shorter),
+// segments seg_first .. seg_first + nseg - 1 in one launch, per (segment,
+// unit) NCB value column blocks and ncb_id identity column blocks. A value
+// block starts from dS_in[in_base - s] (null: dS_T for the sequence's last
+// segment, zero for the others) and ends in L_out[out_base - s] (null: dS0
+// for segment 0); it stores the chunks' exiting adjoints when dst_all or its
+// segment is the sequence's last. An identity block runs the homogeneous
+// part (no dO term) on the columns of the identity and ends in
+// M_out[out_base - s], the segment's map of its exiting adjoint to its
+// entering one; none for the last segment. Per (slot, unit) d x d fp32.
 struct DstParams {
   const BF *prep;
   const float *gc;
@@ -529,7 +539,11 @@ struct DstParams {
   const float *dST;
   float *dS0;
   BF *dst;
-  int T, H_v, nch;
+  int T, H_v, nch, units;
+  int seg_chunks, seg_first, ncb_id, in_base, out_base;
+  bool dst_all;
+  const float *dS_in;
+  float *L_out, *M_out;
 };
 
 template <int D>
@@ -539,17 +553,29 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
   constexpr int OPS16 = 3 * kC * D / 8;  // 16-byte pieces of a chunk's operands
   static_assert(OPS16 % 256 == 0, "whole pieces per thread");
   __shared__ DstSmem<D> sm;
-  const int cb = blockIdx.x % NCB, unit = blockIdx.x / NCB;
+  const int ncbt = NCB + p.ncb_id;
+  const int cbt = blockIdx.x % ncbt, su = blockIdx.x / ncbt;  // su = (s - seg_first) * units + unit
+  const int unit = su % p.units, s = p.seg_first + su / p.units;
+  const int c_lo = s * p.seg_chunks, c_hi = min(c_lo + p.seg_chunks, p.nch), nloc = c_hi - c_lo;
+  const bool last = c_hi == p.nch, ident = cbt >= NCB;
+  if (nloc <= 0 || (ident && last)) return;
+  const int cb = ident ? cbt - NCB : cbt;
   const int n = unit / p.H_v, h = unit - n * p.H_v;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int col = cb * 64 + 16 * wave + c;
 
   floatx4 dS[NMT];
+  const float *din = p.dS_in ? p.dS_in + ((size_t)(p.in_base - s) * p.units + unit) * D * D
+                     : (last && p.dST) ? p.dST + (size_t)unit * D * D
+                                       : nullptr;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dS[mt][j] = p.dST ? p.dST[((size_t)unit * D + 16 * mt + 4 * g + j) * D + col] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * mt + 4 * g + j;
+      dS[mt][j] = ident ? (row == col ? 1.f : 0.f) : din ? din[(size_t)row * D + col] : 0.f;
+    }
+  const bool store = !ident && (p.dst_all || last);
 
   struct Raw {
     u32x4 o[OPS16 / 256];
@@ -567,7 +593,7 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
     const int tok = ch * kC + t;
     const u32x4 d = *reinterpret_cast<const u32x4 *>(p.dO + ((size_t)n * p.T + min(tok, p.T - 1)) * p.H_v * D +
                                                     (size_t)h * D + cb * 64 + 8 * q8);
-    r.d = tok < p.T ? d : u32x4{0u, 0u, 0u, 0u};
+    r.d = tok < p.T && !ident ? d : u32x4{0u, 0u, 0u, 0u};
     r.gcv = *reinterpret_cast<const floatx4 *>(p.gc + ((size_t)unit * p.nch + ch) * D + 4 * (tid % (D / 4)));
   };
   auto stash = [&](int buf, const Raw &r) __attribute__((always_inline)) {
@@ -578,14 +604,16 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
     if (tid < D / 4) reinterpret_cast<floatx4 *>(sm.gc[buf])[tid] = r.gcv;
   };
 
-  Raw r0, r1;  // chunk k (from the last) is requested into set k % 2, two chunks ahead
+  Raw r0, r1;  // chunk k (from the segment's last) is requested into set k % 2, two chunks ahead
   auto body = [&](Raw &cur, Raw &nxt, int k) __attribute__((always_inline)) {
-    const int ch = p.nch - 1 - k, buf = k & 1;
-    fetch(max(ch - 2, 0), cur);  // cur held chunk ch, staged in the previous step (chunk 0 again at the end)
+    const int ch = c_hi - 1 - k, buf = k & 1;
+    fetch(max(ch - 2, c_lo), cur);  // cur held chunk ch, staged in the previous step (c_lo again at the end)
     // the adjoint of this chunk's exiting state
-    BF *dsto = p.dst + (((size_t)unit * p.nch + ch) * D + col) * D + 4 * g;
+    if (store) {
+      BF *dsto = p.dst + (((size_t)unit * p.nch + ch) * D + col) * D + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<Fr *>(dsto + 16 * mt) = OB::from_acc(dS[mt]);
+      for (int mt = 0; mt < NMT; ++mt) *reinterpret_cast<Fr *>(dsto + 16 * mt) = OB::from_acc(dS[mt]);
+    }
     const BF *Wt = sm.ops[buf], *Kd = sm.ops[buf] + kC * D, *Qe = sm.ops[buf] + 2 * kC * D;
     auto frag = [&](const BF *base, int idx) { return OB::ld(base + (idx * 64 + lane) * 4); };
     // Y = -Wt dS (tokens x this wave's columns)
@@ -611,22 +639,26 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(DstParams p) {
     }
     // the next chunk (requested a step ago) into the other buffer, last
     // read in the previous step, before its barrier
-    if (k + 1 < p.nch) stash(buf ^ 1, nxt);
+    if (k + 1 < nloc) stash(buf ^ 1, nxt);
     __syncthreads();
   };
-  fetch(p.nch - 1, r0);
-  fetch(max(p.nch - 2, 0), r1);
+  fetch(c_hi - 1, r0);
+  fetch(max(c_hi - 2, c_lo), r1);
   stash(0, r0);
   __syncthreads();
-  for (int k = 0; k < p.nch; k += 2) {
+  for (int k = 0; k < nloc; k += 2) {
     body(r0, r1, k);
-    if (k + 1 < p.nch) body(r1, r0, k + 1);
+    if (k + 1 < nloc) body(r1, r0, k + 1);
   }
-  if (p.dS0) {
+  float *out = ident ? p.M_out + ((size_t)(p.out_base - s) * p.units + unit) * D * D
+               : p.L_out ? p.L_out + ((size_t)(p.out_base - s) * p.units + unit) * D * D
+               : s == 0 && p.dS0 ? p.dS0 + (size_t)unit * D * D
+                                 : nullptr;
+  if (out) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p.dS0[((size_t)unit * D + 16 * mt + 4 * g + j) * D + col] = dS[mt][j];
+      for (int j = 0; j < 4; ++j) out[(size_t)(16 * mt + 4 * g + j) * D + col] = dS[mt][j];
   }
 }
 
@@ -1223,8 +1255,39 @@ hipError_t launch_backward_chunked(const BackwardArgs &a, hipStream_t st, bool *
   dp.prep = prep; dp.gc = gc;
   dp.dO = static_cast<const uint16_t *>(a.dO);
   dp.dST = a.dST; dp.dS0 = a.dS0; dp.dst = dst;
-  dp.T = a.T; dp.H_v = a.H_v; dp.nch = l.nch;
-  hipLaunchKernelGGL(bwd_dstate_kernel<D>, dim3(units * (D / 64)), dim3(256), 0, st, dp);
+  dp.T = a.T; dp.H_v = a.H_v; dp.nch = l.nch; dp.units = units;
+  dp.seg_chunks = l.nch;
+  dp.dst_all = true;
+  constexpr int NCB = D / 64;
+  if (l.seg.nseg > 1) {
+    // segments swept at once in reverse (the states' regions are free now):
+    // 1. segments 1 .. nseg - 1 from a zero exiting adjoint (the last from
+    //    dS_T, storing its chunks' adjoints), ending in L[nseg - 1 - s], and
+    //    the maps M[nseg - 1 - s] of segments 1 .. nseg - 2;
+    // 2. L[j] = M[j] L[j - 1] + L[j] for j = 1 .. nseg - 2: L[nseg - 2 - s]
+    //    is then the exact adjoint leaving segment s;
+    // 3. segments 0 .. nseg - 2 from those, storing their chunks' adjoints
+    //    (segment 0 also dS0).
+    const int ns = l.seg.nseg;
+    float *M = reinterpret_cast<float *>(w + l.trans), *L = reinterpret_cast<float *>(w + l.segst);
+    dp.seg_chunks = l.seg.seg_len / kC;
+    dp.seg_first = 1;
+    dp.ncb_id = NCB;
+    dp.out_base = ns - 1;
+    dp.dst_all = false;
+    dp.L_out = L; dp.M_out = M;
+    hipLaunchKernelGGL(bwd_dstate_kernel<D>, dim3((ns - 1) * units * 2 * NCB), dim3(256), 0, st, dp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ns > 2 && (e = launch_split_combine(L, M, ns - 2, units, D, D, nullptr, st)) != hipSuccess) return e;
+    dp.seg_first = 0;
+    dp.ncb_id = 0;
+    dp.dS_in = L; dp.in_base = ns - 2;
+    dp.dst_all = true;
+    dp.L_out = nullptr; dp.M_out = nullptr;
+    hipLaunchKernelGGL(bwd_dstate_kernel<D>, dim3((ns - 1) * units * NCB), dim3(256), 0, st, dp);
+  } else {
+    hipLaunchKernelGGL(bwd_dstate_kernel<D>, dim3(units * NCB), dim3(256), 0, st, dp);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 4. the gradients
   GradParams gp{};
