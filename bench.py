@@ -51,6 +51,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector ALUs, TFLOP/s
+# GDN2_BACKWARD_CHUNKED as the caller set it: the long-context backward leg
+# runs that choice (the legs below set the variable for their own runs)
+USER_BACKWARD_CHUNKED = os.environ.get("GDN2_BACKWARD_CHUNKED")
 PREFILL_KERNEL_SOURCES = ["gated_delta_rule_83_amd/csrc/gdn2_prefill.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_device.hpp",
                           "gated_delta_rule_83_amd/csrc/gdn2_range.hpp",
@@ -515,14 +518,19 @@ def main():
             return g.chunk_backward(tl["q"], tl["k"], tl["v"], tl["a"], tl["b"], tl["w"], None, dOl, dSTl,
                                     grads=grads, workspace=wsl, stream=stream)
 
-        lform = "chunk"
-        os.environ["GDN2_BACKWARD_CHUNKED"] = "2"
-        try:
+        if USER_BACKWARD_CHUNKED is not None:  # the caller's choice (0: the per-token backward)
+            os.environ["GDN2_BACKWARD_CHUNKED"] = USER_BACKWARD_CHUNKED
+            lform = {"0": "per-token", "2": "chunk"}.get(USER_BACKWARD_CHUNKED, "automatic")
             gl = backward_long()
-        except RuntimeError:
-            lform = "automatic"
-            os.environ.pop("GDN2_BACKWARD_CHUNKED")
-            gl = backward_long()
+        else:
+            lform = "chunk"
+            os.environ["GDN2_BACKWARD_CHUNKED"] = "2"
+            try:
+                gl = backward_long()
+            except RuntimeError:
+                lform = "automatic"
+                os.environ.pop("GDN2_BACKWARD_CHUNKED")
+                gl = backward_long()
         torch.cuda.synchronize()
         l_ms = time_each(lambda: backward_long(gl), args.long_backward)
         os.environ.pop("GDN2_BACKWARD_CHUNKED", None)

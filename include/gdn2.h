@@ -307,8 +307,11 @@ gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, cons
  *            adjoint of the state leaving it (bf16, d_k * d_v each), the
  *            chunk's adjoint operands (3 * 32 * d_k bf16) and its decay
  *            (d_k fp32), plus one more state per sequence and value head:
- *            about 2.8 KB per token and value head, 1.49 GB at B8 T4096 H16
- *            (and at least what the per-token backward needs in rounds);
+ *            about 2.8 KB per token and value head, 1.49 GB at B8 T4096 H16;
+ *            with few long sequences (segments below) also three fp32
+ *            d_k * d_v states per segment and value head (2.97 GB at B1
+ *            T65536 H16, 8 segments); and at least what the per-token
+ *            backward needs in rounds;
  *          - otherwise (the per-token backward): fp32 state checkpoints
  *            every 4 tokens, per 64-column block key-side partial sums and
  *            every token's k-read, about
@@ -319,7 +322,14 @@ gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, cons
  * form on the matrix cores (the prefill run again storing the state at every
  * 32-token chunk boundary; per chunk the operands of the state adjoint's
  * chunk step; the adjoint swept from the last chunk to the first; every
- * gradient of a chunk from its entering state and exiting adjoint). Its
+ * gradient of a chunk from its entering state and exiting adjoint). Few long
+ * sequences (where the prefill would cut them into segments of equal length,
+ * GDN2_PREFILL_SPLIT included) run both sequential parts over the segments at
+ * once: the chunk states from every segment's exact entering state (the
+ * prefill's split passes), and the adjoint sweep as the prefill's split in
+ * reverse (each segment from a zero exiting adjoint and on the identity's
+ * columns, the exact exiting adjoints handed from segment to segment, then
+ * every segment again from its own). Its
  * products take bf16 operands with fp32 accumulation, the states and
  * adjoints at chunk boundaries rounded to bf16 (the prefill's own rounding
  * of its chunk products), within the bf16 tolerance. A chunk in which some
