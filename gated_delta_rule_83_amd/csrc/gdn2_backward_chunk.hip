@@ -334,6 +334,9 @@ PrefillArgs cst_prefill_args(int B, int T, int H_qk, int H_v) {
   fa.chunk = 64;
   fa.bf16 = true;
   fa.nct = prefill_pick_nct(B, H_v, 128);
+  // up to two rounds of the compute units in the split's first pass: the
+  // segments' state launch (no identity blocks) then fills one round
+  fa.split_wgs = 2 * kNumCU;
   return fa;
 }
 

@@ -13,6 +13,10 @@ namespace gdn2 {
 // scalar, also a = alpha (one fp32 per token and value head).
 enum { kGateGeneral = 0, kGatePre = 1, kGateCoupled = 2, kGateScalar = 3 };
 
+// Compute units of one MI355X (gfx950): one prefill workgroup each (its LDS
+// working set admits one per unit), so this many make one round of a launch.
+constexpr int kNumCU = 256;
+
 struct DecodeArgs {
   int B, H_qk, H_v, d_k, d_v;
   bool bf16;
@@ -47,6 +51,9 @@ struct PrefillArgs {
   bool preact;
   // split into this many segments (0: the plan's own choice)
   int force_nseg;
+  // the plan's own choice: at most this many workgroups in the split's first
+  // pass (0: kNumCU, one round of the compute units)
+  int split_wgs = 0;
   // states only (backward of long sequences): run the split's first two
   // passes and leave in seg_states[s] ([nseg][B][H_v][d_k][d_v]) the exact
   // state after segment s for s < nseg - 1; no outputs, no S_T; the

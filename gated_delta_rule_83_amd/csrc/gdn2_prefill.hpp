@@ -1441,8 +1441,13 @@ constexpr int fitting_chunk(int requested) {
 
 // Split plan. Sequences are cut into segments when an unsplit launch would
 // occupy few workgroups (few sequences and heads) and the sequence is long:
-// segments of at least 16 chunks, about two rounds of 256 workgroups in the
-// first pass. GDN2_PREFILL_SPLIT=<n> forces n segments (1: never split).
+// segments of at least 16 chunks, the largest power of two of them that
+// keeps the first pass (value blocks of every segment, identity blocks of
+// all but the first) within PrefillArgs::split_wgs workgroups (default: one
+// per compute unit, i.e. one round). Every round of the first pass is as
+// deep as its segments, so more segments than one round holds only add
+// identity work and a longer combine and correction. GDN2_PREFILL_SPLIT=<n>
+// forces n segments (1: never split).
 template <int DK, int C, int NCT, bool BF16>
 PrefillPlan plan_t(const PrefillArgs &a) {
   constexpr int DVB = 16 * NCT;
@@ -1456,8 +1461,11 @@ PrefillPlan plan_t(const PrefillArgs &a) {
   } else if (const char *env = getenv("GDN2_PREFILL_SPLIT")) {
     P = atol(env);
   } else if ((long)a.B * a.H_v * ncb < 128) {
-    const long per_seg = (long)a.B * a.H_v * (ncb + DK / DVB);
-    while (P * 2 * per_seg <= 512) P *= 2;
+    const long val = (long)a.B * a.H_v * ncb, idb = (long)a.B * a.H_v * (DK / DVB);
+    const long cap = a.split_wgs > 0 ? a.split_wgs : kNumCU;
+    // the largest power of two with val P + idb (P - 1) <= cap (powers of two
+    // give equal segments of the usual power-of-two lengths)
+    while (val * (2 * P) + idb * (2 * P - 1) <= cap) P *= 2;
     P = P < nfull / 16 ? P : nfull / 16;
   }
   P = P < nfull ? P : nfull;

@@ -101,12 +101,14 @@ def test_split_workspace_query_and_errors(monkeypatch):
     rows = 65536 * 16 * 128 * 2
     monkeypatch.delenv("GDN2_PREFILL_SPLIT", raising=False)
     need = g.gdn2_chunk_forward_workspace_bytes(d2)
-    assert need == 8 * per_seg + rows
-    assert g.gdn2_chunk_forward_plan(d2)[2] == 8
+    # the largest power of two of segments whose first pass fits one round of
+    # the 256 compute units: 32 value + 32 identity blocks per later segment
+    assert need == 4 * per_seg + rows
+    assert g.gdn2_chunk_forward_plan(d2)[2] == 4
     monkeypatch.setenv("GDN2_PREFILL_SPLIT", "1")
     assert g.gdn2_chunk_forward_workspace_bytes(d2) == 0
-    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "4")
-    assert g.gdn2_chunk_forward_workspace_bytes(d2) == 4 * per_seg + rows
+    monkeypatch.setenv("GDN2_PREFILL_SPLIT", "8")
+    assert g.gdn2_chunk_forward_workspace_bytes(d2) == 8 * per_seg + rows
     monkeypatch.delenv("GDN2_PREFILL_SPLIT")
     ws = FAKE + 20 * (1 << 30)
     assert fwd(d2) == g.GDN2_ERR_WORKSPACE
