@@ -179,68 +179,100 @@ __global__ __launch_bounds__(256) void split_correct_kernel(void *o_, const void
   const size_t row0 = (size_t)n * T;  // token index of the sequence's first token
   const ET *oIh = static_cast<const ET *>(oI_) + (size_t)h * DK;
   ET *oh = static_cast<ET *>(o_) + (size_t)h * DV;
-  for (int t0 = t_beg + 16 * wave; t0 < t_end; t0 += 64) {
+  // One 16-token tile of this wave per step: its oI rows (B fragments: 8
+  // consecutive key channels of token t per K32 step, one 16-byte load in
+  // bf16, two in fp32) and the o pieces it updates are requested together,
+  // one step ahead (the next step's requests are issued before this step's
+  // products), so a step waits on one memory round trip at most. Tokens
+  // past the slab's end read the slab's first row and store nothing.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NQ = DV >= 32 ? DV / 32 : 1;  // 8-column groups of a lane
+  struct Step {
+    Pair<BF16> b[NKP];
+    floatx4 od[NQ][BF16 ? 1 : 2];  // the o pieces (bf16: raw 16-byte words)
+  };
+  auto request = [&](int t0, Step &L) {
     const int t = t0 + c;
     const bool ok = t < t_end;
-    // B fragments: 8 consecutive key channels of token t per K32 step, one
-    // 16-byte (bf16) or two (fp32) loads
     const ET *src = oIh + (row0 + (ok ? t : t_beg)) * (size_t)H_v * DK;
-    Pair<BF16> b[NKP];
 #pragma unroll
     for (int p = 0; p < NKP; ++p) {
       const int k0 = 32 * p + 8 * g;
-      const bool in = ok && k0 < DK;
+      const bool in = k0 < DK;  // compile-time per p and lane group's run
       if constexpr (BF16) {
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 raw = in ? *reinterpret_cast<const u32x4 *>(src + k0) : u32x4{0u, 0u, 0u, 0u};
-        b[p].lo = __builtin_bit_cast(typename O::Frag, uint2{raw.x, raw.y});
-        b[p].hi = __builtin_bit_cast(typename O::Frag, uint2{raw.z, raw.w});
+        L.b[p].lo = __builtin_bit_cast(typename O::Frag, uint2{raw.x, raw.y});
+        L.b[p].hi = __builtin_bit_cast(typename O::Frag, uint2{raw.z, raw.w});
       } else {
-        b[p].lo = in ? *reinterpret_cast<const floatx4 *>(src + k0) : zero4();
-        b[p].hi = in ? *reinterpret_cast<const floatx4 *>(src + k0 + 4) : zero4();
+        L.b[p].lo = in ? *reinterpret_cast<const floatx4 *>(src + k0) : zero4();
+        L.b[p].hi = in ? *reinterpret_cast<const floatx4 *>(src + k0 + 4) : zero4();
       }
     }
-    ET *dst = oh + (row0 + (ok ? t : t_beg)) * (size_t)H_v * DV;
-    auto tile = [&](int ct) {
-      floatx4 acc = zero4();
+    if constexpr (DV >= 32) {
+      const ET *d = oh + (row0 + (ok ? t : t_beg)) * (size_t)H_v * DV + 8 * g;
 #pragma unroll
-      for (int p = 0; p < NKP; ++p) acc = O::mma32(acc, sa[ct][p].lo, sa[ct][p].hi, b[p].lo, b[p].hi);
-      return acc;
-    };
+      for (int q = 0; q < NQ; ++q) {
+        if constexpr (BF16) {
+          L.od[q][0] = __builtin_bit_cast(floatx4, *reinterpret_cast<const u32x4 *>(d + 32 * q));
+        } else {
+          L.od[q][0] = *reinterpret_cast<const floatx4 *>(d + 32 * q);
+          L.od[q][1] = *reinterpret_cast<const floatx4 *>(d + 32 * q + 4);
+        }
+      }
+    }
+  };
+  auto tile = [&](const Step &L, int ct) {
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) acc = O::mma32(acc, sa[ct][p].lo, sa[ct][p].hi, L.b[p].lo, L.b[p].hi);
+    return acc;
+  };
+  auto finish = [&](int t0, const Step &L) {
+    const int t = t0 + c;
+    const bool ok = t < t_end;
+    ET *dst = oh + (row0 + (ok ? t : t_beg)) * (size_t)H_v * DV;
     if constexpr (DV >= 32) {
       // columns 32 q + 8 g .. +7: tiles 2q (first four) and 2q + 1
 #pragma unroll
-      for (int q = 0; q < DV / 32; ++q) {
-        floatx4 acc[NCT];
-        acc[2 * q] = tile(2 * q);
-        acc[2 * q + 1] = tile(2 * q + 1);
+      for (int q = 0; q < NQ; ++q) {
+        const floatx4 a0 = tile(L, 2 * q), a1 = tile(L, 2 * q + 1);
         if (ok) {
           ET *d = dst + 32 * q + 8 * g;
           if constexpr (BF16) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 u = *reinterpret_cast<const u32x4 *>(d);
+            const u32x4 u = __builtin_bit_cast(u32x4, L.od[q][0]);
             const floatx4 lo = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
             const floatx4 hi = {__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
                                 __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)};
-            const uint2 a = __builtin_bit_cast(uint2, __builtin_convertvector(lo + acc[2 * q], bf16x4));
-            const uint2 b2 = __builtin_bit_cast(uint2, __builtin_convertvector(hi + acc[2 * q + 1], bf16x4));
-            *reinterpret_cast<u32x4 *>(d) = u32x4{a.x, a.y, b2.x, b2.y};
+            const uint2 x = __builtin_bit_cast(uint2, __builtin_convertvector(lo + a0, bf16x4));
+            const uint2 y = __builtin_bit_cast(uint2, __builtin_convertvector(hi + a1, bf16x4));
+            *reinterpret_cast<u32x4 *>(d) = u32x4{x.x, x.y, y.x, y.y};
           } else {
             floatx4 *df = reinterpret_cast<floatx4 *>(d);
-            df[0] = df[0] + acc[2 * q];
-            df[1] = df[1] + acc[2 * q + 1];
+            df[0] = L.od[q][0] + a0;
+            df[1] = L.od[q][1] + a1;
           }
         }
       }
     } else {  // DV = 16: rows are the columns
-      const floatx4 acc = tile(0);
+      const floatx4 acc = tile(L, 0);
       if (ok) {
         ET *d = dst + 4 * g;
 #pragma unroll
         for (int j = 0; j < 4; ++j) E::st(d + j, E::ld(d + j) + acc[j]);
       }
     }
+  };
+  // two register sets in turn (no copies between them)
+  Step s0, s1;
+  int t0 = t_beg + 16 * wave;
+  if (t0 < t_end) request(t0, s0);
+  for (; t0 < t_end; t0 += 128) {
+    request(t0 + 64, s1);
+    finish(t0, s0);
+    if (t0 + 64 >= t_end) break;
+    request(t0 + 128, s0);
+    finish(t0 + 64, s1);
   }
   (void)sizeof(OT);
 }
@@ -248,7 +280,11 @@ __global__ __launch_bounds__(256) void split_correct_kernel(void *o_, const void
 template <int DK, bool BF16>
 hipError_t launch_correct_dv(void *o, const void *oI, const float *state, int B, int T, int H_v, int d_v,
                              int seg_len, int nseg, hipStream_t st) {
-  const int slab = 2048;
+  // tokens per workgroup: each stages its segment's entering state once, so
+  // shorter slabs repeat that; longer ones leave few workgroups per compute
+  // unit (2048 and 4096 tokens measured 25% and 12% slower at B1 T65536 H16,
+  // 256 tokens 12%)
+  const int slab = 512;
   const int nslab = (seg_len + slab - 1) / slab;
   const dim3 grid((unsigned)((nseg - 1) * B * H_v * nslab));
   switch (d_v) {
