@@ -533,6 +533,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   using LT = typename Cf::LT;
   constexpr int NRT = Cf::NRT, NCH = Cf::NCH, NKP = Cf::NKP, LDD = Cf::LDD, RPG = Cf::RPG,
                 RGE = Cf::RGE;
+  // Coupled gates (b = beta per token): the carry's erase term is
+  // (mu beta K)^T R = (mu K)^T diag(beta) R, so the carry contracts the
+  // mu K rows once with U - diag(beta) R (half the products) and the
+  // mu beta K rows are not built (the Gram tiles derive Akb, Mqb from Akk,
+  // Mqk). With an odd number of 16-token blocks a K32 step would pair the
+  // two halves, so that case keeps both; so does the launch that stores the
+  // chunk-boundary states for the backward, whose states are then those of
+  // the per-channel form on the broadcast gates.
+  constexpr bool HCARRY = CPL && NCH % 2 == 0 && !CST;
   static_assert(sizeof(PrefillSmem<Cf>) <= 160 * 1024, "LDS working set exceeds one CU");
 
   __shared__ PrefillSmem<Cf> sm;
@@ -882,7 +891,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * lam);
         char *kbi_b = Cf::TRC ? cbuf.kbi : sm.kbi;
         st4<LK, BF16>(kbi_b, tl, ch0, kr);
-        st4<LK, BF16>(kbi_b, C + tl, ch0, bkr);
+        if constexpr (!HCARRY) st4<LK, BF16>(kbi_b, C + tl, ch0, bkr);
         // fp32: the carry's operands transposed, 4 (or 2) consecutive tokens
         // per channel at once
         if constexpr (!Cf::TRC) {
@@ -893,7 +902,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 st4<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 3, floatx4{kbq[0][c], kbq[1][c], kbq[2][c], kbq[3][c]});
-                st4<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 3, floatx4{bkq[0][c], bkq[1][c], bkq[2][c], bkq[3][c]});
+                if constexpr (!HCARRY)
+                  st4<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 3, floatx4{bkq[0][c], bkq[1][c], bkq[2][c], bkq[3][c]});
               }
             }
           } else if constexpr (RPG % 2 == 0) {
@@ -901,7 +911,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 st2<LT, BF16>(cbuf.kbiT, ch0 + c, tl - 1, kbq[0][c], kr[c]);
-                st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bkr[c]);
+                if constexpr (!HCARRY) st2<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl - 1, bkq[0][c], bkr[c]);
               }
             }
             kbq[0] = kr;
@@ -910,7 +920,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               st1<LT, BF16>(cbuf.kbiT, ch0 + c, tl, kr[c]);
-              st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bkr[c]);
+              if constexpr (!HCARRY) st1<LT, BF16>(cbuf.kbiT, ch0 + c, C + tl, bkr[c]);
             }
           }
         }
@@ -1246,7 +1256,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   };
 
   // consumer registers carried across the phases of one step
-  Frag Uf[NCH], Rf[NCH], Rn[NCH];
+  Frag Uf[NCH], Rf[NCH], Rn[NCH], Wf[HCARRY ? NCH : 1];
   floatx4 X[NCH], Y[NCH];
   // One pipeline step (chunk s-1 consumed from set PP, which then receives
   // chunk s+1); the loop runs two steps per iteration so that both U
@@ -1335,7 +1345,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
-        for (int pp = 0; pp < NCH; ++pp) tf[rt][pp] = carry_frag(cbf, rt, pp);
+        for (int pp = 0; pp < (HCARRY ? NCH / 2 : NCH); ++pp) tf[rt][pp] = carry_frag(cbf, rt, pp);
         gc[rt] = *reinterpret_cast<const floatx4 *>(&cbf.gamc[16 * rt + 4 * lg]);
       }
       // Z = X + Akk U, then (I + Akb) R = Z by blocked forward substitution:
@@ -1350,6 +1360,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const floatx4 R = mma<BF16, true>(zero4(), Pair<BF16>{df[r], O::zero()}, Pair<BF16>{O::from_acc(acc), O::zero()});
         Rf[r] = O::from_acc(R);
         Rn[r] = O::from_acc(-R);
+        if constexpr (HCARRY) {  // U - diag(beta) R of this lane's tokens 16 r + 4 lg ..
+          const floatx4 b4 = *reinterpret_cast<const floatx4 *>(&sm.beta[PP][16 * r + 4 * lg]);
+          Wf[r] = O::from_acc(__builtin_convertvector(Uf[r], floatx4) - b4 * R);
+        }
       });
       GDN2_MARK(3);
       // O^T = Y^T + U^T Mqk^T - R^T Mqb^T, one chain over the pairs
@@ -1374,12 +1388,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
       // with the anchor's cumulative decay A (1 at the chunk start, gamma_m
       // in the middle) and mu_s = A / gamma_s: kbiT columns are
       // [K part | beta part], K16 block kb pairs with U_kb or -R_(kb - NCH)
+      // (coupled gates: only the K part, paired with U - diag(beta) R)
       auto ub = [&](int kb) { return kb < NCH ? Uf[kb % NCH] : Rn[(kb - NCH) % NCH]; };
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         floatx4 acc = S[rt];
+        if constexpr (HCARRY) {
 #pragma unroll
-        for (int pp = 0; pp < NCH; ++pp) acc = mma<BF16>(acc, tf[rt][pp], Pair<BF16>{ub(2 * pp), ub(2 * pp + 1)});
+          for (int pp = 0; pp < NCH / 2; ++pp) acc = mma<BF16>(acc, tf[rt][pp], Pair<BF16>{Wf[2 * pp], Wf[2 * pp + 1]});
+        } else {
+#pragma unroll
+          for (int pp = 0; pp < NCH; ++pp) acc = mma<BF16>(acc, tf[rt][pp], Pair<BF16>{ub(2 * pp), ub(2 * pp + 1)});
+        }
         S[rt] = acc * gc[rt];
       }
     }
