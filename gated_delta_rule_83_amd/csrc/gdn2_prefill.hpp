@@ -542,9 +542,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
   // chunk-boundary states for the backward, whose states are then those of
   // the per-channel form on the broadcast gates.
   constexpr bool HCARRY = CPL && NCH % 2 == 0 && !CST;
+  // Pre-activations with the token-major build: the erase gates are
+  // activated by the column waves (idle while the producers build) and handed
+  // to the producers in LDS, fp32, double-buffered by chunk parity; the
+  // producers activate only the decays.
+  constexpr bool CBG = PRE && Cf::TOKM;
   static_assert(sizeof(PrefillSmem<Cf>) <= 160 * 1024, "LDS working set exceeds one CU");
 
   __shared__ PrefillSmem<Cf> sm;
+  // CBG: activated erase gates of the chunks with parity 0 and 1, [token][channel]
+  __shared__ __attribute__((aligned(16))) float bgl[CBG ? 2 * C * DK : 4];
+  static_assert(sizeof(PrefillSmem<Cf>) + sizeof(bgl) <= 160 * 1024, "LDS working set exceeds one CU");
   GDN2_TIMER_INIT
 
   // workgroup -> (segment, sequence, value head, column block)
@@ -686,7 +694,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         } else {
           ra[P][r] = bload<floatx4>(src.a, ab_off, r * ab_tb);
         }
-        if constexpr (CPL) {
+        if constexpr (CBG) {
+          // erase gates come from LDS (activated by the column waves)
+        } else if constexpr (CPL) {
           const float bb = bload<float>(src.b, (uint32_t)tb0 * bt_tb, r * bt_tb);
           rb[P][r] = floatx4{bb, bb, bb, bb};
         } else if constexpr (PRE && BF16) {
@@ -727,7 +737,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
           ra[P][r] = decay4(gate_unpack(ra[P][r]));
-          rb[P][r] = gate4(gate_unpack(rb[P][r]));
+          if constexpr (!CBG) rb[P][r] = gate4(gate_unpack(rb[P][r]));
         }
       }
     }
@@ -886,7 +896,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const floatx4 kv = quad_f(rk[P][r]);
         const floatx4 qv = quad_f(rq[P][r]);
         const floatx4 kr = kv * mu;
-        const floatx4 bkr = rb[P][r] * kr;
+        const floatx4 bg = CBG ? *reinterpret_cast<const floatx4 *>(&bgl[((int)decltype(P)::value * C + tl) * DK + ch0])
+                               : rb[P][r];
+        const floatx4 bkr = bg * kr;
         st4<LK, BF16>(cbuf.kqg, tl, ch0, kv * lam);
         st4<LK, BF16>(cbuf.kqg, C + tl, ch0, qv * lam);
         char *kbi_b = Cf::TRC ? cbuf.kbi : sm.kbi;
@@ -1255,6 +1267,48 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     otc = -1;
   };
 
+  // CBG: erase-gate pre-activations. Column wave cw (all four, consumers or
+  // not) requests tokens cw C/4 + 4 i + lane/16 (i < C/16), channels
+  // 8 (lane % 16) .. +7 (one 16-byte load in bf16, two in fp32), into
+  // register set c % 2 for chunk c, two steps before the set is activated and
+  // written to LDS buffer c % 2 (at the end of step c - 1, or before the loop
+  // for c = 0).
+  constexpr int BGI = CBG ? C / 16 : 1, BGL = BF16 ? 1 : 2;
+  floatx4 rbg[2][BGI][BGL];
+  const int bg_tok = (cw & 3) * (C / 4) + (lane >> 4), bg_ch = 8 * (lane & 15);
+  const uint32_t bg_off = (uint32_t)bg_tok * bt_tb + (uint32_t)bg_ch * GS;
+  auto load_bg = [&](auto S, int t0) {
+    if constexpr (CBG) {
+      const rsrc_t rs = make_rsrc((const char *)bh + (size_t)t0 * bt_tb, rows_left(t0, bt_tb));
+#pragma unroll
+      for (int i = 0; i < BGI; ++i)
+#pragma unroll
+        for (int e = 0; e < BGL; ++e)
+          rbg[decltype(S)::value][i][e] = bload<floatx4>(rs, bg_off + 16u * e, (uint32_t)(4 * i) * bt_tb);
+    }
+  };
+  auto stage_bg = [&](auto S) {
+    if constexpr (CBG) {
+      constexpr int b = decltype(S)::value;
+#pragma unroll
+      for (int i = 0; i < BGI; ++i) {
+        floatx4 g8[2];
+        if constexpr (BF16) {
+          const floatx4 raw = rbg[b][i][0];
+          g8[0] = gate4(gate_unpack(floatx4{raw[0], raw[1], 0.f, 0.f}));
+          g8[1] = gate4(gate_unpack(floatx4{raw[2], raw[3], 0.f, 0.f}));
+        } else {
+          g8[0] = gate4(rbg[b][i][0]);
+          g8[1] = gate4(rbg[b][i][BGL - 1]);
+        }
+        float *dst = &bgl[(b * C + bg_tok + 4 * i) * DK + bg_ch];
+        *reinterpret_cast<floatx4 *>(dst) = g8[0];
+        *reinterpret_cast<floatx4 *>(dst + 4) = g8[1];
+      }
+    }
+  };
+  if constexpr (CBG) load_bg(std::integral_constant<int, 0>(), nfull > 0 ? 0 : Tl);
+
   // consumer registers carried across the phases of one step
   Frag Uf[NCH], Rf[NCH], Rn[NCH], Wf[HCARRY ? NCH : 1];
   floatx4 X[NCH], Y[NCH];
@@ -1414,11 +1468,24 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         for (int rt = 0; rt < NRT; ++rt) S[rt] *= *reinterpret_cast<const floatx4 *>(&nb.gamm[16 * rt + 4 * lg]);
       }
     }
+    // chunk s+1's erase gates into LDS buffer PP (the producers build from it
+    // in the next step), then chunk s+3's requested: in the second phase,
+    // which the column waves finish before the producers (they activate the
+    // write gates in the first)
+    if constexpr (CBG) {
+      stage_bg(std::integral_constant<int, PP>());
+      load_bg(std::integral_constant<int, PP>(), s + 3 < nfull ? (s + 3) * C : Tl);
+    }
     GDN2_MARK(5);
     __syncthreads();  // buffer (s+1)&1 may now be rebuilt by the producers
     GDN2_MARK(7);
   };
   load_u(std::integral_constant<int, 0>(), consumer && !ident && nfull > 0 ? 0 : Tl);
+  if constexpr (CBG) {  // erase gates of chunks 0 and 1 requested, chunk 0's staged, chunk 2's requested
+    load_bg(std::integral_constant<int, 1>(), nfull > 1 ? C : Tl);
+    stage_bg(std::integral_constant<int, 0>());
+    load_bg(std::integral_constant<int, 0>(), nfull > 2 ? 2 * C : Tl);
+  }
   if constexpr (Cf::TOKM) __syncthreads();  // matches the producers' barrier before their loop
   for (int s = 0; s < nsteps; s += 2) {
     cstep(std::integral_constant<int, 0>(), s);
