@@ -119,6 +119,29 @@ def test_split_workspace_query_and_errors(monkeypatch):
         assert fwd(d2, p, ws=p[i] + 256, ws_bytes=need) == g.GDN2_ERR_ALIAS, i
 
 
+def test_split_plan_fills_one_round(monkeypatch):
+    """The prefill's own split plan: the largest power of two of segments whose
+    first pass (every segment's value column blocks, all but the first
+    segment's identity blocks; 64-column blocks at d = 128) stays within one
+    round of the 256 compute units, at most one segment per 16 chunks; shapes
+    with enough workgroups unsplit run whole."""
+    monkeypatch.delenv("GDN2_PREFILL_SPLIT", raising=False)
+
+    def nseg(B, T, Hqk, Hv):
+        st, crun, n = g.gdn2_chunk_forward_plan(g.make_desc(B, T, Hqk, Hv, 128, 128, 64, g.GDN2_BF16))
+        assert st == g.GDN2_OK and crun == 32
+        return n
+
+    # B1 H16: 32 value + 32 identity blocks per segment: 4 segments = 224 workgroups (8 would be 480)
+    assert nseg(1, 65536, 16, 16) == 4
+    assert nseg(2, 65536, 16, 16) == 2      # 64 + 64 per segment: 2 segments = 192
+    assert nseg(1, 65536, 8, 8) == 8        # 16 + 16: 8 segments = 240
+    assert nseg(1, 65536, 1, 1) == 64       # 2 + 2: 64 segments = 254 (one per 16 chunks: 128 allowed)
+    assert nseg(1, 16 * 32 * 3, 1, 1) == 3  # capped at one segment per 16 chunks (48 chunks)
+    assert nseg(1, 65536, 64, 64) == 1      # 128 value blocks: enough workgroups unsplit
+    assert nseg(8, 4096, 16, 16) == 1       # the layer shape
+
+
 def test_coupled_argument_errors():
     def fc(desc, p=None, ws=0, ws_bytes=0):
         p = p or _ptrs()[:8]  # q, k, v, a, beta, S0, o, S_T
