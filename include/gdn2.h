@@ -323,7 +323,8 @@ gdn2_status gdn2_decode_step_gates(const gdn2_desc *desc, gdn2_gates gates, cons
  * 32-token chunk boundary; per chunk the operands of the state adjoint's
  * chunk step; the adjoint swept from the last chunk to the first; every
  * gradient of a chunk from its entering state and exiting adjoint). Few long
- * sequences (where the prefill would cut them into segments of equal length,
+ * sequences (where the prefill's split plan, allowed up to two rounds of
+ * first-pass workgroups, would cut them into segments of equal length;
  * GDN2_PREFILL_SPLIT included) run both sequential parts over the segments at
  * once: the chunk states from every segment's exact entering state (the
  * prefill's split passes), and the adjoint sweep as the prefill's split in
