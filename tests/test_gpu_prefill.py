@@ -242,12 +242,14 @@ def test_varlen_null_state_and_in_place():
 
 
 @pytest.mark.parametrize("dtype,dk,dv,chunk,T", [("f32", 128, 128, 64, 200), ("bf16", 128, 128, 64, 300),
-                                                  ("f32", 32, 64, 32, 133), ("bf16", 64, 16, 16, 70)])
+                                                  ("f32", 32, 64, 32, 133), ("bf16", 64, 16, 16, 70),
+                                                  ("bf16", 16, 16, 64, 200), ("bf16", 16, 64, 64, 141)])
 def test_coupled_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
     """b = w = beta (one scalar per token and value head): the oracle within
     tolerance, and the general path fed the expanded gates up to rounding (the
     coupled path scales the key Gram products by beta instead of forming
-    separate erase-side products)."""
+    separate erase-side products, and contracts the carry's keys once with
+    U - diag(beta) R: two and, at chunk 64 with d_k 16, four 16-token blocks)."""
     import gated_delta_rule_83_amd as g
     rng = np.random.default_rng(130 + dk + dv)
     d = rand_inputs(rng, 2, T, 1, 2, dk, dv)
@@ -269,7 +271,7 @@ def test_coupled_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
 
 
 @pytest.mark.parametrize("dtype,dk,dv,chunk,T", [("f32", 128, 128, 64, 150), ("bf16", 128, 128, 64, 330),
-                                                  ("bf16", 32, 32, 32, 97)])
+                                                  ("bf16", 32, 32, 32, 97), ("bf16", 16, 16, 64, 130)])
 def test_scalar_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
     """Gated DeltaNet form (scalar decay alpha, coupled gate beta, one scalar
     each per token and value head): the oracle within tolerance, and the
@@ -418,7 +420,7 @@ def _rand_preact(rng, B, T, Hqk, Hv, dk, dv, a_mu=0.0):
 
 
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 32), ("f32", 128, 128), ("bf16", 32, 64),
-                                      ("bf16", 128, 128)])
+                                      ("bf16", 128, 128), ("bf16", 128, 16), ("f32", 128, 32)])
 def test_preact_gates_match_oracle(dt, dk, dv):
     """Pre-activation gates in the input dtype, activated in the kernel: several
     chunks plus a ragged tail, grouped heads, random S0."""
