@@ -18,10 +18,21 @@ def run_and_compare(d, dtype, chunk, tol=None, label=""):
     torch.cuda.synchronize()
     ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
     eo, es = normwise(to_np(o), ref_o), normwise(to_np(ST), ref_S)
+    ho, hs = _per_head(to_np(o), ref_o, to_np(ST), ref_S)
     tol = TOL[dtype] if tol is None else tol
-    print(f"[prefill {label} {dtype} C={chunk}] o err {eo:.3e}  S_T err {es:.3e}  tol {tol:g}", flush=True)
+    print(f"[prefill {label} {dtype} C={chunk}] o err {eo:.3e}  S_T err {es:.3e}  per (sequence, head) "
+          f"{ho:.3e} {hs:.3e}  tol {tol:g}", flush=True)
     assert eo <= tol and es <= tol, (eo, es)
+    assert ho <= tol and hs <= tol, (ho, hs)
     return eo, es
+
+
+def _per_head(o, ref_o, S, ref_S):
+    """Worst normwise error over the (sequence, head) slices of o [B, T, H, d]
+    and S_T [B, H, d_k, d_v], each slice against its own scale."""
+    if ref_o.size == 0:
+        return 0.0, per_head_normwise(S, ref_S, (0, 1))[0]
+    return per_head_normwise(o, ref_o, (0, 2))[0], per_head_normwise(S, ref_S, (0, 1))[0]
 
 
 def test_config0_tiny_fp32():
@@ -264,6 +275,8 @@ def test_coupled_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
     go, gs = normwise(to_np(oc), to_np(og)), normwise(to_np(Sc), to_np(Sg))
     ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
     eo, es = normwise(to_np(oc), ref_o), normwise(to_np(Sc), ref_S)
+    ho, hs = _per_head(to_np(oc), ref_o, to_np(Sc), ref_S)
+    assert ho <= TOL[dtype] and hs <= TOL[dtype], ("per (sequence, head)", ho, hs)
     print(f"[coupled {dtype} dk{dk} dv{dv}] o err {eo:.3e} S_T err {es:.3e}; vs general {go:.1e} {gs:.1e}",
           flush=True)
     assert go <= TOL[dtype] and gs <= TOL[dtype]
@@ -292,6 +305,8 @@ def test_scalar_gates_equal_general_path_and_oracle(dtype, dk, dv, chunk, T):
     go, gs = normwise(to_np(os_), to_np(og)), normwise(to_np(Ss), to_np(Sg))
     ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
     eo, es = normwise(to_np(os_), ref_o), normwise(to_np(Ss), ref_S)
+    ho, hs = _per_head(to_np(os_), ref_o, to_np(Ss), ref_S)
+    assert ho <= TOL[dtype] and hs <= TOL[dtype], ("per (sequence, head)", ho, hs)
     print(f"[scalar {dtype} dk{dk} dv{dv}] o err {eo:.3e} S_T err {es:.3e}; vs general {go:.1e} {gs:.1e}",
           flush=True)
     assert go <= TOL[dtype] and gs <= TOL[dtype]
@@ -405,9 +420,12 @@ def _preact_compare(d, dtype, chunk, label, tol=None):
     torch.cuda.synchronize()
     ref_o, ref_S = oracle.forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
     eo, es = normwise(to_np(o), ref_o), normwise(to_np(ST), ref_S)
+    ho, hs = _per_head(to_np(o), ref_o, to_np(ST), ref_S)
     tol = TOL[dtype] if tol is None else tol
-    print(f"[preact {label} {dtype} C={chunk}] o err {eo:.3e}  S_T err {es:.3e}  tol {tol:g}", flush=True)
+    print(f"[preact {label} {dtype} C={chunk}] o err {eo:.3e}  S_T err {es:.3e}  per (sequence, head) "
+          f"{ho:.3e} {hs:.3e}  tol {tol:g}", flush=True)
     assert eo <= tol and es <= tol, (eo, es)
+    assert ho <= tol and hs <= tol, (ho, hs)
 
 
 def _rand_preact(rng, B, T, Hqk, Hv, dk, dv, a_mu=0.0):
