@@ -9,7 +9,7 @@ cases: whole and ragged chunks and sequences shorter than one chunk, grouped
 heads, absent S0 / dS_T, decays that need the middle anchor, and decays too
 fast for either anchor (the library then runs the per-token backward, and
 refuses when the chunk form is required). Tolerance: the bf16 bar, 2e-2
-normwise per gradient tensor."""
+normwise per gradient tensor, and per (sequence, head) slice."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +17,7 @@ import torch
 import gated_delta_rule_83_amd as g
 from gated_delta_rule_83_amd import inputs as gi
 from tests.parity import rand_inputs
-from tests.test_gpu_backward import compare, upstream
+from tests.test_gpu_backward import compare, per_head_error, upstream
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -174,6 +174,8 @@ def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
     ref = oracle_backward(form, x, S0, dO, dST)
     names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
     errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
+    errs.update({nm + " per head": per_head_error(to_np(got[nm]), ref[nm], (0, 1) if nm == "dS0" else (0, 2))
+                 for nm in names})
     print(f"[per-token rounds {form}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
     assert not bad, bad
@@ -201,6 +203,8 @@ def test_chunk_form_gate_forms(form, B, T, Hqk, Hv, monkeypatch):
     ref = oracle_backward(form, x, S0, dO, dST)
     names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
     errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
+    errs.update({nm + " per head": per_head_error(to_np(got[nm]), ref[nm], (0, 1) if nm == "dS0" else (0, 2))
+                 for nm in names})
     print(f"[chunk form {form} B{B} T{T} Hqk{Hqk} Hv{Hv}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()),
           flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
@@ -242,6 +246,8 @@ def test_chunk_states_from_segments(form, B, T, Hqk, split, monkeypatch):
     ref = oracle_backward(form, x, S0, dO, dST)
     names = [nm for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0") if got.get(nm) is not None]
     errs = {nm: normwise(to_np(got[nm]), ref[nm]) for nm in names}
+    errs.update({nm + " per head": per_head_error(to_np(got[nm]), ref[nm], (0, 1) if nm == "dS0" else (0, 2))
+                 for nm in names})
     print(f"[chunk states from segments {form} B{B} T{T} Hqk{Hqk} split {split}] "
           + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
