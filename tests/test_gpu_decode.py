@@ -35,8 +35,11 @@ def test_decode_shapes(dk, dv, dtype):
     torch.cuda.synchronize()
     ref_o, ref_S = oracle.forward(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"])
     eo, es = normwise(to_np(o), ref_o), normwise(to_np(S), ref_S)
-    print(f"[decode dk{dk} dv{dv} {dtype}] o err {eo:.3e}  S err {es:.3e}", flush=True)
+    ho, hs = per_head_normwise(to_np(o), ref_o, (0, 2))[0], per_head_normwise(to_np(S), ref_S, (0, 1))[0]
+    print(f"[decode dk{dk} dv{dv} {dtype}] o err {eo:.3e}  S err {es:.3e}  per (sequence, head) {ho:.3e} {hs:.3e}",
+          flush=True)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
+    assert ho <= TOL[dtype] and hs <= TOL[dtype]
 
 
 def test_config0_as_decode_steps():
@@ -128,5 +131,8 @@ def test_decode_gate_forms(form, dtype, dk, dv):
     o = torch.cat(outs, dim=1)
     ref_o, ref_S = oracle_forward(form, x, S0)
     eo, es = normwise(to_np(o), ref_o), normwise(to_np(S), ref_S)
-    print(f"[decode {form} {dtype} dk{dk} dv{dv}] o err {eo:.3e} S err {es:.3e}", flush=True)
+    ho, hs = per_head_normwise(to_np(o), ref_o, (0, 2))[0], per_head_normwise(to_np(S), ref_S, (0, 1))[0]
+    print(f"[decode {form} {dtype} dk{dk} dv{dv}] o err {eo:.3e} S err {es:.3e} per (sequence, head) "
+          f"{ho:.3e} {hs:.3e}", flush=True)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
+    assert ho <= TOL[dtype] and hs <= TOL[dtype]
