@@ -401,6 +401,57 @@ def _full_size(cfg_index):
     assert max(eo, es, eo_all, es_all) <= TOL[c.dtype], (eo, io, es, is_)
 
 
+def _full_size_coupled(cfg_index, scalar=False):
+    """Workload cfg_index as stated with coupled gates: beta = the drawn erase
+    gate's first channel per token and value head (so the long context keeps
+    its hard erases), b = w = beta; the scalar form also takes alpha = the
+    decay's first channel. Every (sequence, value head) against the oracle on
+    the broadcast gates, each slice on its own scale: the coupled carry
+    contracts U - diag(beta) R, rounded to bf16 once per chunk, over every
+    chunk of the sequence (through the split at the long context)."""
+    import gated_delta_rule_83_amd as g
+    c = gi.config(cfg_index)
+    print(f"[full coupled {c.name} scalar={scalar}] drawing inputs", flush=True)
+    d = gi.make_inputs(c)
+    beta = np.ascontiguousarray(d["b"][..., 0])
+    alpha = np.ascontiguousarray(d["a"][..., 0]) if scalar else None
+    td = gi.to_torch(d, c.dtype, DEV)
+    del d
+    bt = torch.from_numpy(beta).to(DEV)
+    if scalar:
+        o, ST = g.chunk_forward_scalar(td["q"], td["k"], td["v"], torch.from_numpy(alpha).to(DEV), bt, None,
+                                       chunk=c.chunk)
+    else:
+        o, ST = g.chunk_forward_coupled(td["q"], td["k"], td["v"], td["a"], bt, None, chunk=c.chunk)
+    torch.cuda.synchronize()
+    o_h, ST_h = to_np(o), to_np(ST)
+    q, k, v = (td[n].cpu() for n in ("q", "k", "v"))
+    a = np.broadcast_to(alpha[..., None], alpha.shape + (c.d_k,)) if scalar else td["a"].cpu().numpy()
+    del o, ST, td
+    torch.cuda.empty_cache()
+    bb = np.broadcast_to(beta[..., None], beta.shape + (c.d_k,))
+    bw = np.broadcast_to(beta[..., None], beta.shape + (c.d_v,))
+    print(f"[full coupled {c.name}] oracle on all {c.B * c.H_v} (sequence, head) pairs", flush=True)
+    ref_o, ref_S = oracle.forward(q, k, v, np.ascontiguousarray(a), np.ascontiguousarray(bb),
+                                  np.ascontiguousarray(bw), None)
+    eo, io, _ = per_head_normwise(o_h, ref_o, (0, 2))
+    es, is_, _ = per_head_normwise(ST_h, ref_S, (0, 1))
+    print(f"[full coupled {c.name} scalar={scalar}] worst head o {io}: {eo:.3e}  S_T {is_}: {es:.3e}", flush=True)
+    assert max(eo, es) <= TOL[c.dtype], (eo, io, es, is_)
+
+
+def test_full_config1_coupled_all_heads():
+    _full_size_coupled(1)
+
+
+def test_full_config1_scalar_all_heads():
+    _full_size_coupled(1, scalar=True)
+
+
+def test_full_config2_coupled_all_heads():
+    _full_size_coupled(2)
+
+
 def test_full_config1_all_heads():
     _full_size(1)
 
