@@ -521,9 +521,12 @@ def test_preact_split_sequence(monkeypatch):
     _preact_compare(gi.make_preact_inputs(c), "bf16", 64, "split3")
 
 
-def test_preact_full_layer_shape_all_heads():
-    """B8 T4096 H16 d128 bf16 with pre-activation gates: every (sequence, head)."""
-    c = gi.config(1)
+@pytest.mark.parametrize("cfg_index", [1, 2])
+def test_preact_full_layer_shape_all_heads(cfg_index):
+    """The layer shape (B8 T4096 H16 d128 bf16) and the long context (B1
+    T65536 H16, through the split, hard erases) with pre-activation gates:
+    every (sequence, head)."""
+    c = gi.config(cfg_index)
     d = gi.make_preact_inputs(c)
     td = gi.to_torch_preact(d, "bf16", DEV)
     o, ST = g.chunk_forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], None, chunk=64)
@@ -531,7 +534,7 @@ def test_preact_full_layer_shape_all_heads():
     ref_o, ref_S = oracle.forward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], None)
     eo, io, _ = per_head_normwise(to_np(o), ref_o, (0, 2))
     es, is_, _ = per_head_normwise(to_np(ST), ref_S, (0, 1))
-    print(f"[preact full] worst head o err {eo:.3e} at {io}, S_T err {es:.3e} at {is_}", flush=True)
+    print(f"[preact full {c.name}] worst head o err {eo:.3e} at {io}, S_T err {es:.3e} at {is_}", flush=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, io, es, is_)
 
 
