@@ -133,6 +133,38 @@ def test_chunk_form_layer_shape_sampled_heads(monkeypatch):
     _heads_vs_oracle(td, dO, dST, gg, ((0, 0), (3, 5), (5, 11), (7, 15)), "chunk form layer shape")
 
 
+@pytest.mark.parametrize("scalar", [False, True])
+def test_chunk_form_coupled_layer_shape_sampled_heads(scalar, monkeypatch):
+    """The layer shape (B8 T4096 H16 d128 bf16) in the coupled and scalar gate
+    forms (beta, and alpha, = the drawn gates' first channel per token and
+    value head): the chunk form, four (sequence, head) pairs against the
+    oracle's gradients through the broadcasts, dbeta (and dalpha) included."""
+    import oracle
+    from tests.parity import TOL, normwise, to_np
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    c = gi.config(1)
+    d = gi.make_inputs(c)
+    rng = np.random.default_rng(5700 + scalar)
+    beta = torch.from_numpy(np.ascontiguousarray(d["b"][..., 0])).to(DEV)
+    td = gi.to_torch(d, "bf16", DEV)
+    a = torch.from_numpy(np.ascontiguousarray(d["a"][..., 0])).to(DEV) if scalar else td["a"]
+    dO, dST = upstream(rng, d, "bf16")
+    fn = g.chunk_backward_scalar if scalar else g.chunk_backward_coupled
+    gg = fn(td["q"], td["k"], td["v"], a, beta, td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    for (n, h) in ((0, 0), (3, 5), (5, 11), (7, 15)):
+        sl = lambda x: x[n:n + 1, :, h:h + 1].contiguous()
+        ref = oracle.backward_coupled(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(a), sl(beta),
+                                      None if td["S0"] is None else td["S0"][n:n + 1, h:h + 1].contiguous(),
+                                      sl(dO), dST[n:n + 1, h:h + 1].contiguous(), scalar_decay=scalar)
+        errs = {nm: normwise(to_np(gg[nm][n:n + 1, :, h:h + 1] if nm != "dS0" else gg[nm][n:n + 1, h:h + 1]),
+                             ref[nm]) for nm in ("dq", "dk", "dv", "da", "db", "dS0")}
+        print(f"[chunk form {'scalar' if scalar else 'coupled'} layer shape n{n} h{h}] "
+              + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+        bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+        assert not bad, ((n, h), bad)
+
+
 @pytest.mark.parametrize("form,T", [("channel", 1100), ("preact", 1100), ("coupled", 1100), ("scalar", 1100),
                                     ("scalar", 520), ("channel", 520)])
 def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
