@@ -165,6 +165,34 @@ def test_chunk_form_coupled_layer_shape_sampled_heads(scalar, monkeypatch):
         assert not bad, ((n, h), bad)
 
 
+def test_chunk_form_preact_layer_shape_sampled_heads(monkeypatch):
+    """The layer shape (B8 T4096 H16 d128 bf16) with bf16 gate pre-activations:
+    the chunk form (its chunk states from the prefill whose column waves
+    activate the erase gates), four (sequence, head) pairs against the
+    oracle's gradients through the activations."""
+    import oracle
+    from tests.parity import TOL, normwise, to_np
+    monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "2")
+    c = gi.config(1)
+    d = gi.make_preact_inputs(c)
+    rng = np.random.default_rng(5800)
+    td = gi.to_torch_preact(d, "bf16", DEV)
+    dO, dST = upstream(rng, d, "bf16")
+    gg = g.chunk_backward_preact(td["q"], td["k"], td["v"], td["a"], td["b"], td["w"], td["S0"], dO, dST)
+    torch.cuda.synchronize()
+    for (n, h) in ((0, 0), (3, 5), (5, 11), (7, 15)):
+        sl = lambda x: x[n:n + 1, :, h:h + 1].contiguous()
+        ref = oracle.backward_preact(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]),
+                                     None if td["S0"] is None else td["S0"][n:n + 1, h:h + 1].contiguous(),
+                                     sl(dO), dST[n:n + 1, h:h + 1].contiguous())
+        errs = {nm: normwise(to_np(gg[nm][n:n + 1, :, h:h + 1] if nm != "dS0" else gg[nm][n:n + 1, h:h + 1]),
+                             ref[nm]) for nm in ("dq", "dk", "dv", "da", "db", "dw", "dS0")}
+        print(f"[chunk form preact layer shape n{n} h{h}] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()),
+              flush=True)
+        bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+        assert not bad, ((n, h), bad)
+
+
 @pytest.mark.parametrize("form,T", [("channel", 1100), ("preact", 1100), ("coupled", 1100), ("scalar", 1100),
                                     ("scalar", 520), ("channel", 520)])
 def test_per_token_rounds_in_chunk_workspace(form, T, monkeypatch):
