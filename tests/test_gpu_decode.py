@@ -136,3 +136,32 @@ def test_decode_gate_forms(form, dtype, dk, dv):
           f"{ho:.3e} {hs:.3e}", flush=True)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
     assert ho <= TOL[dtype] and hs <= TOL[dtype]
+
+
+@pytest.mark.parametrize("form", ["channel", "preact", "coupled", "scalar"])
+def test_decode_empty_batch(form):
+    """A decode step over no sequences (N = 0) returns an empty output and
+    launches nothing; a one-sequence step right after it on the same stream
+    still equals the oracle's single token."""
+    Hqk, Hv, dk, dv = 2, 4, 64, 32
+    z = lambda *s: torch.zeros(s, device=DEV, dtype=torch.bfloat16)
+    gshape = {"channel": ((dk,), (dk,), (dv,)), "preact": ((dk,), (dk,), (dv,)),
+              "coupled": ((dk,), (), None), "scalar": ((), (), None)}[form]
+    gdt = torch.bfloat16 if form == "preact" else torch.float32
+    ga = lambda N, tail: None if tail is None else torch.zeros((N, 1, Hv) + tail, device=DEV, dtype=gdt)
+    S = torch.zeros((0, Hv, dk, dv), device=DEV)
+    o = g.decode_step(z(0, 1, Hqk, dk), z(0, 1, Hqk, dk), z(0, 1, Hv, dv), ga(0, gshape[0]),
+                      ga(0, gshape[1]), ga(0, gshape[2]), S, gates=form)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 1, Hv, dv)
+    from tests.gate_forms import form_inputs, oracle_forward
+    rng = np.random.default_rng(77)
+    x = form_inputs(rng, form, 1, Hv, dk, dv, "bf16", DEV, B=1, Hqk=Hqk)
+    S0 = torch.from_numpy((rng.standard_normal((1, Hv, dk, dv)) * 0.5).astype(np.float32)).to(DEV)
+    S1 = S0.clone()
+    o1 = g.decode_step(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], S1, gates=form)
+    torch.cuda.synchronize()
+    ref_o, ref_S = oracle_forward(form, x, S0)
+    eo, es = normwise(to_np(o1), ref_o), normwise(to_np(S1), ref_S)
+    print(f"[decode empty batch, {form}] then one token: o err {eo:.3e} S err {es:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
