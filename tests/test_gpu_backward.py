@@ -461,9 +461,10 @@ def _split_case(rng, form, dt, dk, dv, B, T, Hv, with_state, monkeypatch):
 
 def test_split_backward_long_context_full_size(monkeypatch):
     """B1 T65536 H16 d128 bf16 with 1% hard erases (the long-context workload's
-    shape): the default plan's split backward (8 segments) against the
-    unsplit backward of the same inputs, every gradient within tolerance (the
-    per-token backward; the chunk form at this shape is checked in
+    shape): the default plan's split backward (16 segments) against the
+    unsplit backward of the same inputs, every gradient within tolerance, and
+    two heads of the split result against the oracle run on that head alone
+    (the per-token backward; the chunk form at this shape is checked in
     test_gpu_backward_chunk.py)."""
     monkeypatch.delenv("GDN2_BACKWARD_SPLIT", raising=False)
     monkeypatch.setenv("GDN2_BACKWARD_CHUNKED", "0")
@@ -485,6 +486,17 @@ def test_split_backward_long_context_full_size(monkeypatch):
     print("[split backward long context] " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
     assert not bad, bad
+    for h in (0, 9):  # one query/key head per value head at this shape
+        sl = lambda x: x[:, :, h:h + 1].contiguous()
+        oref = oracle.backward(sl(td["q"]), sl(td["k"]), sl(td["v"]), sl(td["a"]), sl(td["b"]), sl(td["w"]),
+                               None if td["S0"] is None else td["S0"][:, h:h + 1].contiguous(), sl(dO),
+                               dST[:, h:h + 1].contiguous())
+        herr = {nm: normwise((got[nm][:, h:h + 1] if nm == "dS0" else got[nm][:, :, h:h + 1]).numpy(), oref[nm])
+                for nm in NAMES}
+        print(f"[split backward long context h{h} vs oracle] " + " ".join(f"{k} {v:.2e}" for k, v in herr.items()),
+              flush=True)
+        bad = {k: v for k, v in herr.items() if not v <= TOL["bf16"]}
+        assert not bad, (h, bad)
 
 
 @pytest.mark.parametrize("form", ["preact", "coupled", "scalar"])
