@@ -482,6 +482,8 @@ def test_decode_gate_forms_errors():
     base = [FAKE + i * (1 << 30) for i in range(9)]  # q, k, v, a, b, w, S, o (stream last)
     dec = lambda form, p: g.gdn2_decode_step_gates(d, form, *p[:8], 0)
     assert dec(9, base) == g.GDN2_ERR_UNSUPPORTED
+    for form in range(4):  # an empty batch returns before the pointers are looked at
+        assert g.gdn2_decode_step_gates(g.make_desc(0, 1, 2, 2, 64, 64, 64, 1), form, *[0] * 8, 0) == g.GDN2_OK
     assert g.gdn2_decode_step_gates(g.make_desc(4, 2, 2, 2, 64, 64, 64, 1), 2, *base[:8], 0) == g.GDN2_ERR_BAD_SHAPE
     for form in (0, 1):
         p = list(base)
