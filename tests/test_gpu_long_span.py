@@ -1,4 +1,5 @@
-"""Prefill parity at sequence spans beyond 4 GiB per tensor.
+"""Parity at buffer spans beyond 4 GiB per tensor: prefill sequences, and a
+decode step over a state larger than 2^32 bytes.
 
 A sequence whose rows of one tensor span 4 GiB or more (e.g. bf16 values of
 32 value heads at T >= 524,288, or bf16 gate pre-activations of 64 value
@@ -95,3 +96,30 @@ def test_packed_preact_gates_span_over_4gib():
         print(f"[long span] preact h={h} o err {eo:.3e} (first 256 tokens {e0:.3e}) S_T err {es:.3e}",
               flush=True)
         assert eo <= TOL["bf16"] and es <= TOL["bf16"] and e0 <= TOL["bf16"], (h, eo, es, e0)
+
+
+def test_decode_state_over_4gib():
+    """One decode step of N4200 H16 d128 (bf16 q/k/v, fp32 gates): the fp32
+    state is 4200 * 16 * 64 KiB = 4.1 GiB, so the last 104 sequences' states
+    lie past byte 2^32 of the allocation. Sampled sequences on both sides of
+    that boundary against the oracle's single token from the same state."""
+    N, H, d = 4200, 16, 128
+    print(f"[long span] decode N{N} H{H} d{d} bf16: drawing on the GPU", flush=True)
+    x = gi.draw_on_device(N, 1, H, H, d, d, "bf16", "channel", DEV, seed=4200)
+    gen = torch.Generator(device=DEV).manual_seed(4201)
+    S = torch.randn((N, H, d, d), generator=gen, device=DEV).mul_(0.5)
+    pairs = [(0, 3), (2047, 11), (4095, 15), (4096, 0), (4150, 7), (4199, 15)]
+    S0 = {p: S[p[0], p[1]].cpu() for p in pairs}
+    o = torch.full((N, 1, H, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    print("[long span] launching the decode step (in place)", flush=True)
+    g.decode_step(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], S, o=o)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()), "outputs left unwritten (NaN)"
+    for n, h in pairs:
+        sl = lambda t: t[n:n + 1, :, h:h + 1].cpu()
+        ref_o, ref_S = oracle.forward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["a"]), sl(x["b"]), sl(x["w"]),
+                                      S0[(n, h)][None, None])
+        eo = normwise(to_np(o[n, :, h]), ref_o[0, :, 0])
+        es = normwise(to_np(S[n, h]), ref_S[0, 0])
+        print(f"[long span] decode (n={n}, h={h}) o err {eo:.3e} S err {es:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (n, h, eo, es)
